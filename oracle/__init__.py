@@ -1,0 +1,138 @@
+"""fp64 CPU oracle for the (gated) delta-rule forward -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never calls it and it
+shares no code with that library: the arithmetic lives in ``gdn_oracle.c``
+(token-by-token recurrence, see that file's header for the passages it follows)
+and ``chunked_ref.py`` (the chunkwise form, used only to pin the chunk
+equations).  This module only converts arrays to fp64 and calls the C code.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(closed forms, invariants, an autograd-derived gradient step, exact rational
+fixtures under ``tests/golden/`` and planted-mistake checks).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+GATES = {"none": 0, "head": 1, "key": 2}
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the C oracle with gcc (OpenMP, -O2) into a shared library."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                               "-o", tmp, src, "-lm"])
+        os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building first if needed) the oracle library; returns the ctypes handle."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        _lib = _declare(ctypes.CDLL(build()))
+    return _lib
+
+
+def _declare(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_fwd.restype = ctypes.c_int
+    lib.oracle_fwd.argtypes = [ctypes.c_int, ip, ip, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_step.restype = ctypes.c_int
+    lib.oracle_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, dp, dp, dp, dp, dp, dp, dp]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor (CPU); upcast exactly, as the GPU sees the same bits
+        x = x.detach().cpu().double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def infer_gate(log_alpha, token_ndim: int) -> str:
+    if log_alpha is None:
+        return "none"
+    return "head" if np.ndim(log_alpha) == token_ndim else "key"
+
+
+def fwd(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None, gate=None,
+        nthreads: int = 0, lib=None):
+    """Run the recurrence over whole sequences.
+
+    Batch mode: q,k [B,T,H,d_k], v [B,T,H,d_v], beta [B,T,H], log_alpha None |
+    [B,T,H] | [B,T,H,d_k]; varlen mode: B == 1 and ``cu_seqlens`` (N+1 offsets).
+    ``initial_state`` None (zeros) or [N,H,d_k,d_v] with M = S^T.
+    Returns (o [B,T,H,d_v], final_state [N,H,d_k,d_v]) as fp64 numpy arrays.
+    """
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    log_alpha, initial_state = _f64(log_alpha), _f64(initial_state)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if gate is None:
+        gate = infer_gate(log_alpha, 3)
+    if cu_seqlens is not None:
+        cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64)
+        assert B == 1 and cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+        start, lens = cu[:-1].copy(), np.diff(cu)
+    else:
+        start = np.arange(B, dtype=np.int64) * T
+        lens = np.full(B, T, dtype=np.int64)
+    N = len(start)
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    fs = np.zeros((N, H, dk, dv), dtype=np.float64)
+    lib = lib or load()
+    rc = lib.oracle_fwd(N, start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                        lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
+                        GATES[gate], _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                        _ptr(initial_state), _ptr(o), _ptr(fs), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_fwd failed (%d)" % rc)
+    return o, fs
+
+
+def step(q, k, v, beta, log_alpha, state, gate=None, lib=None):
+    """One token per stream: q,k [N,H,d_k], v [N,H,d_v], beta [N,H], log_alpha None |
+    [N,H] | [N,H,d_k], state [N,H,d_k,d_v].  Returns (o [N,H,d_v], new_state)."""
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    log_alpha = _f64(log_alpha)
+    st = _f64(state).copy()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if gate is None:
+        gate = infer_gate(log_alpha, 2)
+    o = np.zeros((N, H, dv), dtype=np.float64)
+    lib = lib or load()
+    rc = lib.oracle_step(N, H, dk, dv, GATES[gate], _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                         _ptr(log_alpha), _ptr(st), _ptr(o))
+    if rc != 0:
+        raise RuntimeError("oracle_step failed (%d)" % rc)
+    return o, st
+
+
+def max_threads() -> int:
+    return load().oracle_max_threads()

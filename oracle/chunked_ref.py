@@ -1,0 +1,112 @@
+"""fp64 chunkwise form of the (gated) delta rule -- TEST INFRASTRUCTURE.
+
+Used only by the tests, to pin the chunk equations that the GPU kernels
+implement against the token-by-token oracle (``gdn_oracle.c``).  It shares no
+code with the GPU library.  Plain NumPy, small sizes only.
+
+The chunkwise-parallel algorithm is the one of "Decoding Hybrid Linear Attention
+Architectures", sec. 5 (inter-chunk state recursion and intra-chunk output), with
+the WY / UT representation of "Linear Attention Variants (RetNet, GLA, DeltaNet,
+Based)", section "DeltaNet: Error-Correcting Writes".  The printed formulas are
+garbled; the reading used here (derived from the recurrence, and checked against
+it by the tests) is, for one chunk of C positions entering with state M0 = S^T:
+
+  G         chunk-local inclusive cumulative sum of log alpha (sec. 5: gate
+            products accumulated in log space)
+  Gamma     Gamma[r,i,c] = exp(G[r,c] - G[i,c]) for i <= r  (decay from i to r)
+  A         A[r,i] = beta_r * sum_c K[r,c] K[i,c] Gamma[r,i,c] for i < r, else 0
+  T         (I + A)^-1, unit lower triangular, by forward substitution
+  W, U      W = T diag(beta) (K * e^G),  U = T diag(beta) V
+  Delta     U - W M0          (the "net correction" U - W S of sec. 5)
+  P         P[r,i] = sum_c Q[r,c] K[i,c] Gamma[r,i,c] for i <= r (inclusive)
+  O         (Q * e^G) M0 + P Delta
+  M_C       diag(e^{G_C}) M0 + (K * e^{G_C - G})^T Delta
+
+e^G is the decay from the chunk start to position r, e^{G_C - G} the decay from
+position i to the chunk end (the Gamma^{i->C} of sec. 5), e^{G_C} the whole-chunk
+decay (gamma^C of sec. 5).  The causal mask is strict for A (a token's write does
+not see itself) and inclusive for P (the read at t happens after the write at t).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def chunk_cumsum(log_alpha_chunk):
+    """G: inclusive cumulative sum over the chunk positions (axis 0)."""
+    return np.cumsum(log_alpha_chunk, axis=0)
+
+
+def forward_substitution_inverse(A):
+    """T = (I + A)^-1 for strictly lower triangular A, one row at a time:
+    row r of T is e_r minus the A[r, i]-weighted sum of the earlier rows."""
+    C = A.shape[0]
+    T = np.zeros_like(A)
+    for r in range(C):
+        T[r, r] = 1.0
+        for i in range(r):
+            T[r] -= A[r, i] * T[i]
+    return T
+
+
+def chunk_step(q, k, v, beta, G, M0):
+    """One chunk.  q,k [C,dk], v [C,dv], beta [C], G [C,dk] (already expanded to
+    every key channel: zeros without a gate), M0 [dk,dv].  Returns a dict of the
+    intermediates and the results O [C,dv], M_C [dk,dv]."""
+    C = q.shape[0]
+    causal_strict = np.tril(np.ones((C, C), dtype=bool), -1)
+    causal_incl = np.tril(np.ones((C, C), dtype=bool), 0)
+    # Gamma[r, i, c] = exp(G[r, c] - G[i, c]); only used where i <= r (exponent <= 0
+    # when the gates are decays), the rest is masked before exponentiation.
+    diff = G[:, None, :] - G[None, :, :]
+    Gamma = np.exp(np.where(causal_incl[:, :, None], diff, 0.0)) * causal_incl[:, :, None]
+    A = beta[:, None] * np.einsum("rc,ic,ric->ri", k, k, Gamma) * causal_strict
+    T = forward_substitution_inverse(A)
+    eG = np.exp(G)
+    W = T @ (beta[:, None] * (k * eG))
+    U = T @ (beta[:, None] * v)
+    Delta = U - W @ M0
+    P = np.einsum("rc,ic,ric->ri", q, k, Gamma) * causal_incl
+    O = (q * eG) @ M0 + P @ Delta
+    gC = G[-1]
+    MC = np.exp(gC)[:, None] * M0 + (k * np.exp(gC[None, :] - G)).T @ Delta
+    return dict(A=A, T=T, W=W, U=U, Delta=Delta, P=P, O=O, M=MC)
+
+
+def fwd_sequence(q, k, v, beta, log_alpha, M0, chunk: int):
+    """One sequence, one head.  q,k [T,dk], v [T,dv], beta [T], log_alpha None |
+    [T] | [T,dk], M0 [dk,dv] or None.  The last chunk may be partial (it is simply
+    shorter).  Returns (O [T,dv], M_T [dk,dv])."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    M = np.zeros((dk, dv)) if M0 is None else np.array(M0, dtype=np.float64)
+    if log_alpha is None:
+        la = np.zeros((T, dk))
+    elif np.ndim(log_alpha) == 1:
+        la = np.repeat(np.asarray(log_alpha, dtype=np.float64)[:, None], dk, axis=1)
+    else:
+        la = np.asarray(log_alpha, dtype=np.float64)
+    O = np.zeros((T, dv))
+    for s in range(0, T, chunk):
+        e = min(T, s + chunk)
+        G = chunk_cumsum(la[s:e])
+        res = chunk_step(q[s:e], k[s:e], v[s:e], beta[s:e], G, M)
+        O[s:e] = res["O"]
+        M = res["M"]
+    return O, M
+
+
+def fwd(q, k, v, beta, log_alpha=None, initial_state=None, chunk: int = 64):
+    """Batch mode over [B,T,H,*] arrays (fp64 numpy).  Returns (o, final_state)."""
+    q, k, v, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    fs = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            la = None if log_alpha is None else np.asarray(log_alpha, dtype=np.float64)[b, :, h]
+            m0 = None if initial_state is None else np.asarray(initial_state)[b, h]
+            o[b, :, h], fs[b, h] = fwd_sequence(q[b, :, h], k[b, :, h], v[b, :, h], beta[b, :, h],
+                                                la, m0, chunk)
+    return o, fs
