@@ -1,0 +1,174 @@
+"""MI355X (gfx950) chunked gated delta-rule forward -- Python binding.
+
+Thin ctypes marshalling over the C ABI of ``include/gdn.h`` (``libgdn.so``, built
+in-tree by ``gated_delta_rule_20_amd/build.py``).  Every step of the computation
+runs in the library's HIP kernels; PyTorch only supplies device memory and the
+current stream.  There is no fallback: if the library is missing this module
+raises on import.
+
+The names follow the C ABI: ``fwd_chunked`` wraps ``gdn_fwd_chunked`` and
+``recurrent_step`` wraps ``gdn_fwd_recurrent_step``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gdn.h")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 0, -1, -2, -3, -4
+GDN_F32, GDN_BF16 = 0, 1
+GDN_GATE_NONE, GDN_GATE_HEAD, GDN_GATE_KEY = 0, 1, 2
+CHUNK = 64
+
+
+class FwdArgs(ctypes.Structure):
+    """Mirror of ``gdn_fwd_args``."""
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("d_k", ctypes.c_int), ("d_v", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("N", ctypes.c_int), ("dtype", ctypes.c_int), ("gate", ctypes.c_int),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
+                ("initial_state", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class StepArgs(ctypes.Structure):
+    """Mirror of ``gdn_step_args``."""
+    _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("d_k", ctypes.c_int),
+                ("d_v", ctypes.c_int), ("dtype", ctypes.c_int), ("gate", ctypes.c_int),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
+                ("state", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
+def load_library(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError("libgdn.so is not built (%s); run `python __graft_entry__.py build` "
+                          "or gated_delta_rule_20_amd/build.py" % path)
+    lib = ctypes.CDLL(path)
+    lib.gdn_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs)]
+    lib.gdn_fwd_chunked.restype = ctypes.c_int
+    lib.gdn_fwd_chunked.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+    lib.gdn_fwd_recurrent_step.restype = ctypes.c_int
+    lib.gdn_fwd_recurrent_step.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_void_p]
+    lib.gdn_status_str.restype = ctypes.c_char_p
+    lib.gdn_status_str.argtypes = [ctypes.c_int]
+    lib.gdn_version.restype = ctypes.c_int
+    return lib
+
+
+_lib = load_library()
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions declared in include/gdn.h."""
+    text = open(path).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, re.M)))
+
+
+def status_str(status: int) -> str:
+    return _lib.gdn_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != GDN_OK:
+        raise RuntimeError("%s failed: %s (%d)" % (what, status_str(status), status))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def gate_code(log_alpha, token_ndim: int) -> int:
+    if log_alpha is None:
+        return GDN_GATE_NONE
+    return GDN_GATE_HEAD if log_alpha.dim() == token_ndim else GDN_GATE_KEY
+
+
+def make_fwd_args(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None, o=None,
+                  final_state=None, chunk: int = CHUNK) -> FwdArgs:
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    return FwdArgs(B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=chunk, N=N, dtype=_dtype_code(q),
+                   gate=gate_code(log_alpha, 3), q=_ptr(q), k=_ptr(k), v=_ptr(v), beta=_ptr(beta),
+                   log_alpha=_ptr(log_alpha), initial_state=_ptr(initial_state),
+                   cu_seqlens=_ptr(cu_seqlens), o=_ptr(o), final_state=_ptr(final_state),
+                   workspace=None, workspace_bytes=0)
+
+
+def fwd_workspace_size(args: FwdArgs) -> int:
+    return int(_lib.gdn_fwd_workspace_size(ctypes.byref(args)))
+
+
+def fwd_chunked(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None,
+                output_final_state: bool = True, chunk: int = CHUNK, out=None, final_state=None,
+                workspace=None, stream=None):
+    """Chunked forward (gdn_fwd_chunked).
+
+    q, k [B,T,H,d_k] and v [B,T,H,d_v] (bf16 or fp32, CUDA, contiguous); beta [B,T,H]
+    fp32; log_alpha None | [B,T,H] | [B,T,H,d_k] fp32; initial_state None |
+    [N,H,d_k,d_v] fp32 (M = S^T); cu_seqlens None | int32 [N+1] (then B == 1).
+    Returns (o [B,T,H,d_v], final_state [N,H,d_k,d_v] or None).  Asynchronous on the
+    current (or given) stream.
+    """
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    args = make_fwd_args(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out,
+                         final_state if output_final_state else None, chunk)
+    need = fwd_workspace_size(args)
+    if need:
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        args.workspace, args.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    _check(_lib.gdn_fwd_chunked(ctypes.byref(args), _stream(stream)), "gdn_fwd_chunked")
+    return out, (final_state if output_final_state else None)
+
+
+def recurrent_step(q, k, v, beta, log_alpha, state, out=None, stream=None):
+    """One decode token per stream (gdn_fwd_recurrent_step).
+
+    q, k [N,H,d_k], v [N,H,d_v] (bf16 or fp32); beta [N,H]; log_alpha None | [N,H] |
+    [N,H,d_k]; state [N,H,d_k,d_v] fp32, updated in place.  Returns o [N,H,d_v].
+    """
+    import torch
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    args = StepArgs(N=N, H=H, d_k=dk, d_v=dv, dtype=_dtype_code(q), gate=gate_code(log_alpha, 2),
+                    q=_ptr(q), k=_ptr(k), v=_ptr(v), beta=_ptr(beta), log_alpha=_ptr(log_alpha),
+                    state=_ptr(state), o=_ptr(out))
+    _check(_lib.gdn_fwd_recurrent_step(ctypes.byref(args), _stream(stream)), "gdn_fwd_recurrent_step")
+    return out
+
+
+def version() -> int:
+    return int(_lib.gdn_version())

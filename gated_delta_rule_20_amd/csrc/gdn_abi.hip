@@ -1,0 +1,150 @@
+// gdn_abi.hip -- host side of the C ABI declared in include/gdn.h.
+//
+// Validates every argument on the host, chooses the kernel configuration, carves
+// the caller's workspace and launches on the caller's stream.  Nothing here
+// allocates, copies or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+#include "gdn_kernels.h"
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// Value columns per workgroup: 64, or 32 when there are too few (sequence, head)
+// streams to give every compute unit a workgroup.
+int choose_dvb(int N, int H, int dv) {
+  const long wg64 = (long)N * H * (dv / 64);
+  return wg64 >= 256 ? 64 : 32;
+}
+
+int check_fwd(const gdn_fwd_args *a) {
+  if (!a) return GDN_ERR_INVALID_ARG;
+  if (a->B < 0 || a->T < 0 || a->H <= 0 || a->N < 0) return GDN_ERR_INVALID_ARG;
+  if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD && a->gate != GDN_GATE_KEY)
+    return GDN_ERR_INVALID_ARG;
+  if (a->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
+  if (a->dtype == GDN_F32 && a->d_k != 64) return GDN_ERR_UNSUPPORTED;
+  if (a->gate == GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
+  if (a->cu_seqlens) {
+    if (a->B != 1 || a->N < 1) return GDN_ERR_INVALID_ARG;
+  } else if (a->N != a->B) {
+    return GDN_ERR_INVALID_ARG;
+  }
+  if ((long)a->B * a->T > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+  const bool tokens = (long)a->B * a->T > 0;
+  if (tokens && (!a->q || !a->k || !a->v || !a->beta || !a->o)) return GDN_ERR_INVALID_ARG;
+  if ((a->gate == GDN_GATE_NONE) != (a->log_alpha == nullptr) && tokens) return GDN_ERR_INVALID_ARG;
+  if (a->gate == GDN_GATE_NONE && a->log_alpha) return GDN_ERR_INVALID_ARG;
+  const void *p16[] = {a->q, a->k, a->v, a->o, a->initial_state, a->final_state};
+  for (const void *p : p16)
+    if (p && !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+  if ((a->beta && !aligned(a->beta, 4)) || (a->log_alpha && !aligned(a->log_alpha, 4)) ||
+      (a->cu_seqlens && !aligned(a->cu_seqlens, 4)))
+    return GDN_ERR_INVALID_ARG;
+  return GDN_OK;
+}
+
+size_t order_bytes(const gdn_fwd_args *a) {
+  if (!a->cu_seqlens || a->N > 8192) return 0;
+  return ((size_t)a->N * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+int check_step(const gdn_step_args *a) {
+  if (!a) return GDN_ERR_INVALID_ARG;
+  if (a->N < 0 || a->H <= 0) return GDN_ERR_INVALID_ARG;
+  if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD && a->gate != GDN_GATE_KEY)
+    return GDN_ERR_INVALID_ARG;
+  if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
+  if (a->N == 0) return GDN_OK;
+  if (!a->q || !a->k || !a->v || !a->beta || !a->state || !a->o) return GDN_ERR_INVALID_ARG;
+  if ((a->gate == GDN_GATE_NONE) != (a->log_alpha == nullptr)) return GDN_ERR_INVALID_ARG;
+  if (!aligned(a->state, 16) || !aligned(a->q, 4) || !aligned(a->k, 4) || !aligned(a->v, 4) ||
+      !aligned(a->o, 4) || !aligned(a->beta, 4) || (a->log_alpha && !aligned(a->log_alpha, 4)))
+    return GDN_ERR_INVALID_ARG;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_fwd_workspace_size(const gdn_fwd_args *a) {
+  if (check_fwd(a) != GDN_OK) return 0;
+  return order_bytes(a);
+}
+
+int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
+  const int st = check_fwd(a);
+  if (st != GDN_OK) return st;
+  const size_t need = order_bytes(a);
+  if (need && (!a->workspace || a->workspace_bytes < need || !aligned(a->workspace, 256)))
+    return GDN_ERR_WORKSPACE;
+  if (a->N == 0) return GDN_OK;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  gdn::FwdParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.beta = a->beta;
+  p.log_alpha = a->log_alpha;
+  p.init_state = a->initial_state;
+  p.final_state = a->final_state;
+  p.o = a->o;
+  p.cu_seqlens = a->cu_seqlens;
+  p.order = need ? (const int32_t *)a->workspace : nullptr;
+  p.N = a->N;
+  p.H = a->H;
+  p.T = a->T;
+  p.dv = a->d_v;
+  const int dvb = choose_dvb(a->N, a->H, a->d_v);
+  p.nb = a->d_v / dvb;
+  if (need) {
+    if (gdn::launch_seq_order(a->cu_seqlens, a->N, (int32_t *)a->workspace, stream) != hipSuccess)
+      return GDN_ERR_HIP;
+  }
+  if (gdn::launch_fwd_fused(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, (int)a->gate, stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+int gdn_fwd_recurrent_step(const gdn_step_args *a, void *hip_stream) {
+  const int st = check_step(a);
+  if (st != GDN_OK) return st;
+  if (a->N == 0) return GDN_OK;
+  gdn::StepParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.beta = a->beta;
+  p.log_alpha = a->log_alpha;
+  p.state = a->state;
+  p.o = a->o;
+  p.N = a->N;
+  p.H = a->H;
+  if (gdn::launch_recurrent_step(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->d_v, (int)a->gate,
+                                 (hipStream_t)hip_stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+const char *gdn_status_str(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_INVALID_ARG: return "invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "unsupported shape or mode";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int gdn_version(void) { return 100; }
+
+}  // extern "C"

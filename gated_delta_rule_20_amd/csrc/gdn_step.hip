@@ -1,0 +1,121 @@
+// gdn_step.hip -- one decode token per stream, state updated in place.
+//
+// The recurrent mode of the (gated) delta rule ("Decoding Hybrid Linear Attention
+// Architectures", sec. 6: constant-cost update of the fixed-size state per decoded
+// token; sec. 3 item 6 for the order decay -> erase -> write).  With the state kept
+// as M = S^T (d_k x d_v) and a = exp(log alpha):
+//   r = (Diag(a) M)^T k,   w = beta (v - r),   M' = Diag(a) M + k w^T,
+//   o = M'^T q = (Diag(a) M)^T q + w (q . k)
+// so one read of M gives both reductions r and (Diag(a) M)^T q, and one write stores
+// M'.  The kernel is bound by HBM traffic (2 * 4 * d_k * d_v bytes per stream).
+//
+// One workgroup (256 threads) per (stream, head).  Thread (row group rg, column
+// quad cq) holds d_k / RG rows x 4 columns of M in registers: 16-byte coalesced
+// loads and stores, partial reductions combined in LDS in a fixed order.
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+namespace {
+
+template <typename E, int DK, int DV, int GATE>
+__global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
+  constexpr int CQ = DV / 4;    // column quads
+  constexpr int RG = 256 / CQ;  // row groups
+  constexpr int RP = DK / RG;   // rows per thread
+  static_assert(RP >= 1 && RG * RP == DK, "step geometry");
+  __shared__ float qs[DK], ks[DK], as_[DK];
+  __shared__ f32x4 red_r[RG][CQ], red_s[RG][CQ];
+  __shared__ float qk_s;
+
+  const int pair = blockIdx.x;  // stream * H + head
+  const int tid = threadIdx.x, cq = tid % CQ, rg = tid / CQ;
+  const E *q = (const E *)p.q + (size_t)pair * DK;
+  const E *k = (const E *)p.k + (size_t)pair * DK;
+  if (tid < DK) {
+    qs[tid] = to_f(q[tid]);
+    ks[tid] = to_f(k[tid]);
+    float a = 1.f;
+    if (GATE == GATE_HEAD) a = __expf(p.log_alpha[pair]);
+    if (GATE == GATE_KEY) a = __expf(p.log_alpha[(size_t)pair * DK + tid]);
+    as_[tid] = a;
+  }
+  float *st = p.state + (size_t)pair * DK * DV;
+  f32x4 m[RP];
+#pragma unroll
+  for (int u = 0; u < RP; ++u) m[u] = *(const f32x4 *)(st + (size_t)(rg * RP + u) * DV + 4 * cq);
+  __syncthreads();
+
+  f32x4 r = zero4(), s = zero4();
+#pragma unroll
+  for (int u = 0; u < RP; ++u) {
+    const int row = rg * RP + u;
+    m[u] *= as_[row];
+    r += m[u] * ks[row];
+    s += m[u] * qs[row];
+  }
+  red_r[rg][cq] = r;
+  red_s[rg][cq] = s;
+  if (tid < 64) {
+    float d = 0.f;
+    for (int i = tid; i < DK; i += 64) d += qs[i] * ks[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+    if (tid == 0) qk_s = d;
+  }
+  __syncthreads();
+
+  f32x4 R = zero4(), S = zero4();
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    R += red_r[g][cq];
+    S += red_s[g][cq];
+  }
+  const E *v = (const E *)p.v + (size_t)pair * DV + 4 * cq;
+  const float beta = p.beta[pair];
+  f32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = beta * (to_f(v[e]) - R[e]);
+#pragma unroll
+  for (int u = 0; u < RP; ++u) {
+    const int row = rg * RP + u;
+    *(f32x4 *)(st + (size_t)row * DV + 4 * cq) = m[u] + ks[row] * w;
+  }
+  if (rg == 0) {
+    E *o = (E *)p.o + (size_t)pair * DV + 4 * cq;
+    const float qk = qk_s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = to_e<E>(S[e] + w[e] * qk);
+  }
+}
+
+template <typename E, int DK, int DV>
+hipError_t launch_g(const StepParams &p, int gate, hipStream_t stream) {
+  const int blocks = p.N * p.H;
+  if (blocks == 0) return hipSuccess;
+  switch (gate) {
+    case GATE_NONE: hipLaunchKernelGGL((recurrent_step_kernel<E, DK, DV, GATE_NONE>), dim3(blocks), dim3(256), 0, stream, p); break;
+    case GATE_HEAD: hipLaunchKernelGGL((recurrent_step_kernel<E, DK, DV, GATE_HEAD>), dim3(blocks), dim3(256), 0, stream, p); break;
+    case GATE_KEY: hipLaunchKernelGGL((recurrent_step_kernel<E, DK, DV, GATE_KEY>), dim3(blocks), dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_e(const StepParams &p, int dk, int dv, int gate, hipStream_t stream) {
+  if (dk == 128 && dv == 128) return launch_g<E, 128, 128>(p, gate, stream);
+  if (dk == 128 && dv == 64) return launch_g<E, 128, 64>(p, gate, stream);
+  if (dk == 64 && dv == 128) return launch_g<E, 64, 128>(p, gate, stream);
+  if (dk == 64 && dv == 64) return launch_g<E, 64, 64>(p, gate, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream) {
+  return dtype == 1 ? launch_e<bf16>(p, dk, dv, gate, stream) : launch_e<float>(p, dk, dv, gate, stream);
+}
+
+}  // namespace gdn

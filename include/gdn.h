@@ -1,0 +1,143 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) chunked gated delta-rule forward.
+ *
+ * The method: a linear-attention layer keeps one fixed-size matrix state per
+ * (sequence, head) ("Decoding Hybrid Linear Attention Architectures", sec. 1: a
+ * state of size d_k x d_v, updated and read once per token).  Per token t, with
+ * query q_t, key k_t, value v_t, write strength beta_t and decay alpha_t:
+ *
+ *   S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t
+ *
+ * with S in R^{d_v x d_k}.  alpha_t = 1 is the delta rule (same page, sec. 3 item 2;
+ * "Linear Attention Variants (RetNet, GLA, DeltaNet, Based)", DeltaNet section),
+ * one scalar per (token, head) is the gated delta rule (sec. 3 item 3) and one
+ * value per key channel is the channel-wise gated delta rule (sec. 3 item 6).  The
+ * decay acts first, then the erase along k_t, then the write (sec. 3 item 6 and its
+ * single-step pseudocode).  The read uses the state after the write.
+ *
+ * The library computes this with the chunkwise-parallel algorithm of "Decoding
+ * Hybrid Linear Attention Architectures", sec. 5 (chunks of C = 64 tokens; within
+ * a chunk, matrix products; across chunks, a serial state recursion), with the
+ * WY/UT representation of the chunk's erase-and-write products ("Linear Attention
+ * Variants", DeltaNet section).  The result equals the token-by-token recurrence up
+ * to rounding.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA memory),
+ *    dense, row-major, 16-byte aligned.  The caller owns all memory; the library
+ *    allocates and frees nothing and keeps no pointer after returning.
+ *  - The state is stored transposed, M = S^T, as [.., d_k, d_v] fp32:
+ *    M[i][j] maps key channel i to value channel j.
+ *  - beta and log_alpha are fp32 in every mode; alpha = exp(log_alpha).  Gate
+ *    products are accumulated in log space (sec. 5 of the first page).
+ *  - q, k, v, o share one I/O dtype (fp32 or bf16).  Arithmetic: fp32 state and
+ *    accumulation; bf16 mode rounds matrix-core operands to bf16; o is rounded
+ *    once (round-to-nearest-even) to the I/O dtype.
+ *  - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the default
+ *    stream).  Buffers must stay valid until the stream has finished the work.
+ *  - Arguments are validated on the host before anything is launched.  A negative
+ *    return means nothing was launched and nothing was written.  Launch failures
+ *    return GDN_ERR_HIP.  No C++ exception crosses this boundary.
+ *  - Results are deterministic: no atomics, fixed reduction order.
+ *  - Thread safety: the library holds no mutable global state; concurrent calls
+ *    on different streams are independent.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad offsets, misalignment */
+  GDN_ERR_UNSUPPORTED = -2, /* a shape or mode outside the supported set        */
+  GDN_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required       */
+  GDN_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed        */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype; /* dtype of q, k, v, o */
+
+typedef enum {
+  GDN_GATE_NONE = 0, /* alpha = 1 (delta rule); log_alpha must be NULL      */
+  GDN_GATE_HEAD = 1, /* one log_alpha per (token, head) (gated delta rule)  */
+  GDN_GATE_KEY = 2   /* one log_alpha per (token, head, key channel)        */
+} gdn_gate;
+
+/*
+ * Chunked forward over whole sequences ("Decoding Hybrid Linear Attention
+ * Architectures", sec. 5: inter-chunk state recursion and intra-chunk output).
+ *
+ * Batch mode (cu_seqlens == NULL): N = B sequences of T tokens each.
+ * Varlen mode (cu_seqlens != NULL): B must be 1; the T packed tokens hold
+ *   N = number of sequences; sequence n is tokens [cu_seqlens[n], cu_seqlens[n+1]).
+ *   cu_seqlens is int32 on the device, N+1 non-decreasing entries, cu_seqlens[0]
+ *   = 0 and cu_seqlens[N] = T (checked by the kernel: a bad table leaves o and
+ *   final_state of the affected sequences unwritten rather than reading out of
+ *   bounds).  Empty sequences are allowed (their final state = initial state).
+ * A sequence whose length is not a multiple of 64 ends in a partial chunk; the
+ * result is the recurrence's, as if padded with beta = 0 and log_alpha = 0.
+ */
+typedef struct {
+  int B, T, H;        /* batch, tokens per batch row (packed total in varlen), heads */
+  int d_k, d_v;       /* head dims: each 64 or 128                                   */
+  int chunk;          /* chunk length: must be 64                                    */
+  int N;              /* number of sequences: B, or len(cu_seqlens) - 1              */
+  gdn_dtype dtype;    /* dtype of q, k, v, o                                         */
+  gdn_gate gate;      /* gate mode                                                   */
+  const void *q;      /* [B, T, H, d_k]                                              */
+  const void *k;      /* [B, T, H, d_k]                                              */
+  const void *v;      /* [B, T, H, d_v]                                              */
+  const float *beta;  /* [B, T, H] fp32                                              */
+  const float *log_alpha;     /* NONE: NULL; HEAD: [B,T,H]; KEY: [B,T,H,d_k] fp32   */
+  const float *initial_state; /* NULL (zeros) or [N, H, d_k, d_v] fp32 (M = S^T)     */
+  const int32_t *cu_seqlens;  /* NULL or [N + 1] int32 (device)                      */
+  void *o;                    /* out: [B, T, H, d_v], dtype                          */
+  float *final_state;         /* out: NULL or [N, H, d_k, d_v] fp32; may alias
+                                 initial_state (each block is read before written)  */
+  void *workspace;            /* device scratch of gdn_fwd_workspace_size() bytes    */
+  size_t workspace_bytes;     /* (NULL / 0 allowed when that size is 0)             */
+} gdn_fwd_args;
+
+/* One token per stream, state updated in place (the constant-cost decode update of
+ * "Decoding Hybrid Linear Attention Architectures", sec. 6; the recurrent mode of
+ * "Linear Attention Variants", RetNet section). */
+typedef struct {
+  int N, H, d_k, d_v; /* streams, heads, head dims (each 64 or 128)                  */
+  gdn_dtype dtype;    /* dtype of q, k, v, o                                         */
+  gdn_gate gate;
+  const void *q;          /* [N, H, d_k]                                             */
+  const void *k;          /* [N, H, d_k]                                             */
+  const void *v;          /* [N, H, d_v]                                             */
+  const float *beta;      /* [N, H]                                                  */
+  const float *log_alpha; /* NONE: NULL; HEAD: [N,H]; KEY: [N,H,d_k]                 */
+  float *state;           /* in/out: [N, H, d_k, d_v] fp32, read then overwritten   */
+  void *o;                /* out: [N, H, d_v], dtype                                 */
+} gdn_step_args;
+
+/* Bytes of device workspace gdn_fwd_chunked needs for these arguments (depends on
+ * N, H and whether cu_seqlens is given; 0 means none).  Returns 0 for arguments
+ * that gdn_fwd_chunked would reject. */
+size_t gdn_fwd_workspace_size(const gdn_fwd_args *args);
+
+/* Chunked forward: writes o (and final_state when non-NULL). */
+int gdn_fwd_chunked(const gdn_fwd_args *args, void *hip_stream);
+
+/* One decode token per stream: writes o and updates state in place. */
+int gdn_fwd_recurrent_step(const gdn_step_args *args, void *hip_stream);
+
+/* Static description of a status code (never NULL). */
+const char *gdn_status_str(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

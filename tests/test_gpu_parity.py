@@ -1,0 +1,211 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Metric: max |x - x_ref| / max |x_ref| per output tensor.  Tolerances: 2e-2 for
+bf16 inputs with fp32 accumulation, 1e-4 for the fp32 mode.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_20_amd as g
+    return g
+
+
+def relerr(x, ref):
+    x = x.detach().double().cpu().numpy() if hasattr(x, "detach") else np.asarray(x, dtype=np.float64)
+    den = np.abs(ref).max()
+    return float(np.abs(x - ref).max() / (den if den > 0 else 1.0))
+
+
+def to_dev(inp):
+    return {k: (v.cuda() if hasattr(v, "cuda") else v) for k, v in inp.items()}
+
+
+def run_gpu(gdn, inp, output_final_state=True):
+    d = to_dev(inp)
+    o, fs = gdn.fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"],
+                            d["cu_seqlens"], output_final_state=output_final_state)
+    torch.cuda.synchronize()
+    return o.cpu(), (fs.cpu() if fs is not None else None)
+
+
+def run_oracle(inp):
+    return oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                      inp["initial_state"], inp["cu_seqlens"], gate=inp["gate"])
+
+
+def check(gdn, inp, tol=None):
+    tol = tol or TOL[inp["dtype"]]
+    o, fs = run_gpu(gdn, inp)
+    o_ref, fs_ref = run_oracle(inp)
+    eo, ef = relerr(o, o_ref), relerr(fs, fs_ref)
+    assert np.isfinite(o.float().numpy()).all() and np.isfinite(fs.numpy()).all()
+    assert eo <= tol and ef <= tol, "o err %.3e, state err %.3e (tol %.1e)" % (eo, ef, tol)
+    return eo, ef
+
+
+# ---------------------------------------------------------------- small shapes
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+@pytest.mark.parametrize("gate", ["none", "head"])
+def test_bf16_ragged_lengths(gdn, T, gate):
+    inp = synth.random_inputs(2, T, 3, 128, 128, gate, "bf16", seed=T, state_std=0.05)
+    check(gdn, inp)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_bf16_head_dims(gdn, dk, dv, with_state):
+    inp = synth.random_inputs(2, 130, 2, dk, dv, "head", "bf16", seed=dk + dv,
+                              state_std=0.05 if with_state else None)
+    check(gdn, inp)
+
+
+@pytest.mark.parametrize("dv", [64, 128])
+@pytest.mark.parametrize("gate", ["none", "head"])
+def test_fp32_mode(gdn, dv, gate):
+    inp = synth.random_inputs(2, 190, 2, 64, dv, gate, "f32", seed=dv, state_std=0.1)
+    check(gdn, inp)
+
+
+def test_varlen_small(gdn):
+    lengths = [1, 64, 65, 130, 7, 0, 300]
+    inp = synth.random_inputs(1, None, 2, 128, 128, "head", "bf16", seed=3, state_std=0.05,
+                              lengths=lengths)
+    check(gdn, inp)
+
+
+def test_varlen_equals_separate_runs(gdn):
+    lengths = [70, 5, 129]
+    inp = synth.random_inputs(1, None, 2, 128, 128, "head", "bf16", seed=8, state_std=0.05,
+                              lengths=lengths)
+    o, fs = run_gpu(gdn, inp)
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(len(lengths)):
+        sl = slice(cu[n], cu[n + 1])
+        sub = dict(inp, q=inp["q"][:, sl].contiguous(), k=inp["k"][:, sl].contiguous(),
+                   v=inp["v"][:, sl].contiguous(), beta=inp["beta"][:, sl].contiguous(),
+                   log_alpha=inp["log_alpha"][:, sl].contiguous(),
+                   initial_state=inp["initial_state"][n:n + 1].contiguous(), cu_seqlens=None)
+        o1, f1 = run_gpu(gdn, sub)
+        assert torch.equal(o1, o[:, sl]), n
+        assert torch.equal(f1[0], fs[n]), n
+
+
+def test_replace_invariant_gpu(gdn):
+    """beta = 1, q = k (unit norm): the read returns the value just written."""
+    inp = synth.random_inputs(1, 256, 2, 128, 128, "head", "bf16", seed=5)
+    inp["beta"] = torch.ones_like(inp["beta"])
+    inp["q"] = inp["k"].clone()
+    o, _ = run_gpu(gdn, inp)
+    v = inp["v"].double().numpy()
+    assert relerr(o, v) <= 2e-2
+
+
+def test_beta_zero_keeps_decayed_state(gdn):
+    inp = synth.random_inputs(2, 100, 2, 128, 128, "head", "bf16", seed=6, state_std=0.1)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    o, fs = run_gpu(gdn, inp)
+    d = torch.exp(inp["log_alpha"].double().sum(dim=1))  # [B, H]
+    expect = d[:, :, None, None] * inp["initial_state"].double()
+    assert relerr(fs, expect.numpy()) <= 1e-5
+
+
+def test_deterministic_and_aliased_state(gdn):
+    inp = synth.random_inputs(2, 300, 4, 128, 128, "head", "bf16", seed=9, state_std=0.05)
+    o1, f1 = run_gpu(gdn, inp)
+    o2, f2 = run_gpu(gdn, inp)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    d = to_dev(inp)
+    st = d["initial_state"].clone()
+    o3, f3 = gdn.fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], st, None,
+                             final_state=st)
+    torch.cuda.synchronize()
+    assert f3.data_ptr() == st.data_ptr()
+    assert torch.equal(o3.cpu(), o1) and torch.equal(st.cpu(), f1)
+
+
+def test_no_final_state_output(gdn):
+    inp = synth.random_inputs(1, 100, 2, 128, 128, "head", "bf16", seed=10)
+    o, fs = run_gpu(gdn, inp, output_final_state=False)
+    assert fs is None
+    o_ref, _ = run_oracle(inp)
+    assert relerr(o, o_ref) <= 2e-2
+
+
+# ---------------------------------------------------------------- workloads
+def test_workload_deltanet_fp32(gdn):
+    check(gdn, synth.workload_inputs("deltanet-fp32-B1-T256-H2-d64"))
+
+
+def test_workload_gdn_bf16_B4(gdn):
+    check(gdn, synth.workload_inputs("gdn-bf16-B4-T2048-H8-d128"))
+
+
+def test_workload_gdn_350m(gdn):
+    check(gdn, synth.workload_inputs("gdn-350m-bf16-B16-T2048-H8-d128"))
+
+
+def test_workload_varlen_sampled(gdn):
+    """Full packed workload on the GPU; the oracle recomputes sampled sequences
+    (shortest, longest, one more) on two heads."""
+    name = "gdn-varlen-bf16-N32-H16-d128"
+    inp = synth.workload_inputs(name)
+    o, fs = run_gpu(gdn, inp)
+    lengths = inp["lengths"]
+    cu = inp["cu_seqlens"].tolist()
+    picks = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), 5})
+    heads = [0, 15]
+    for n in picks:
+        sl = slice(cu[n], cu[n + 1])
+        o_ref, f_ref = oracle.fwd(inp["q"][:, sl][:, :, heads], inp["k"][:, sl][:, :, heads],
+                                  inp["v"][:, sl][:, :, heads], inp["beta"][:, sl][:, :, heads],
+                                  inp["log_alpha"][:, sl][:, :, heads], None)
+        assert relerr(o[:, sl][:, :, heads], o_ref) <= 2e-2, n
+        assert relerr(fs[n, heads], f_ref[0]) <= 2e-2, n
+
+
+# ---------------------------------------------------------------- decode step
+@pytest.mark.parametrize("gate", ["none", "head", "key"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_recurrent_step_matches_oracle(gdn, gate, dtype):
+    N, H, dk, dv, steps = 5, 3, 128, 64, 6
+    dec = synth.decode_inputs(N, H, dk, dv, steps, gate, dtype, seed=11)
+    state0 = torch.randn(N, H, dk, dv, generator=torch.Generator().manual_seed(1)) * 0.1
+    st = state0.cuda()
+    ref = state0.double().numpy()
+    for s in range(steps):
+        la = None if dec["log_alpha"] is None else dec["log_alpha"][s]
+        o = gdn.recurrent_step(dec["q"][s].cuda(), dec["k"][s].cuda(), dec["v"][s].cuda(),
+                               dec["beta"][s].cuda(), None if la is None else la.cuda(), st)
+        torch.cuda.synchronize()
+        o_ref, ref = oracle.step(dec["q"][s], dec["k"][s], dec["v"][s], dec["beta"][s], la, ref, gate=gate)
+        tol = TOL[dtype] if dtype == "bf16" else 1e-5
+        assert relerr(o.cpu(), o_ref) <= tol, s
+        assert relerr(st.cpu(), ref) <= 1e-5, s
+
+
+def test_forward_then_step_equals_longer_forward(gdn):
+    inp = synth.random_inputs(2, 129, 2, 128, 128, "head", "bf16", seed=12, state_std=0.05)
+    head = {k: (v[:, :128].contiguous() if k in ("q", "k", "v", "beta", "log_alpha") else v)
+            for k, v in inp.items()}
+    _, fs = run_gpu(gdn, head)
+    st = fs.cuda()
+    o = gdn.recurrent_step(inp["q"][:, 128].contiguous().cuda(), inp["k"][:, 128].contiguous().cuda(),
+                           inp["v"][:, 128].contiguous().cuda(), inp["beta"][:, 128].contiguous().cuda(),
+                           inp["log_alpha"][:, 128].contiguous().cuda(), st)
+    torch.cuda.synchronize()
+    o_ref, f_ref = run_oracle(inp)
+    assert relerr(o.cpu(), o_ref[:, 128]) <= 2e-2
+    assert relerr(st.cpu(), f_ref) <= 2e-2
