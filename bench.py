@@ -1,0 +1,263 @@
+"""Benchmark of the chunked gated delta-rule forward on one MI355X.
+
+One step = one gdn_fwd_chunked call over one batch of the 350M-class layer shape
+(B=16, T=2048, H=8, d_k=d_v=128, bf16 q/k/v/o, fp32 beta/log alpha/state, chunk 64,
+random fp32 initial state): every step of the chunked method runs in that call.
+Inputs are synthetic (seeded), resident in HBM before timing, and rotated over
+four copies so that no step finds its inputs in the 256 MB last-level cache.
+
+Prints ONE JSON line.  `roofline` relates the fused kernel's algorithmic bytes
+(q, k, v read and o written in bf16, beta and log alpha in fp32, initial and final
+fp32 state) to its average launch duration, measured with HIP events on the stream
+the kernel runs on.  `cpu_baseline` times the fp64 oracle on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gated-delta-rule fwd tokens/sec and % MFMA peak, 1×MI355X"
+HEADLINE = "gdn-350m-bf16-B16-T2048-H8-d128"
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA = {"bf16": 2516.6, "f32": 157.3}  # dense TFLOP/s
+KERNEL_SOURCES = ["gated_delta_rule_20_amd/csrc/gdn_fwd_fused.hip", "gated_delta_rule_20_amd/csrc/gdn_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_fused_gdn-350m.txt")
+ROTATE = 4
+CHUNK = 64
+
+
+def alg_counts(tokens, H, dk, dv, nseq, gate, esize, has_init, has_final=True):
+    """Algorithmic flops and bytes of the chunked method (chunk 64).
+
+    flops per token-head: 2C(3 d_k + 2 d_v) + 6 d_k d_v + C^2/3 (Gram tiles, UT inverse,
+    W and U, W M, K^T Delta, Q M, Q K^T, P Delta; multiply-add = 2).
+    bytes: q, k, v read and o written in the I/O dtype, beta and log alpha in fp32,
+    the fp32 initial state read (if given) and final state written.
+    """
+    C = CHUNK
+    f_th = 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv + C * C / 3.0
+    b_th = esize * (2 * dk + 2 * dv) + 4 + (4 if gate == "head" else 4 * dk if gate == "key" else 0)
+    state = 4 * dk * dv * nseq * H * ((1 if has_init else 0) + (1 if has_final else 0))
+    return f_th * tokens * H, b_th * tokens * H + state
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if
+    the summary is missing or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sha") != kernel_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_device_inputs(inp, copies):
+    import torch
+    sets = []
+    for _ in range(copies):
+        d = {}
+        for k, v in inp.items():
+            d[k] = v.cuda().clone() if isinstance(v, torch.Tensor) else v
+        sets.append(d)
+    return sets
+
+
+def time_chunked(gdn, sets, steps, warmup):
+    """Whole-job time of `steps` calls (barrier + synchronize on both sides) and the
+    average per-launch duration from HIP events on the launch stream."""
+    import torch
+    s0 = sets[0]
+    B, T, H, dk = s0["q"].shape
+    dv = s0["v"].shape[-1]
+    N = s0["N"]
+    outs = [torch.empty((B, T, H, dv), dtype=s0["q"].dtype, device="cuda") for _ in sets]
+    fstates = [torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda") for _ in sets]
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        d = sets[i % len(sets)]
+        gdn.fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"],
+                        d["cu_seqlens"], out=outs[i % len(sets)], final_state=fstates[i % len(sets)],
+                        workspace=ws)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall, sum(launch_ms) / len(launch_ms), launch_ms
+
+
+def time_decode(gdn, spec, final_states, steps=64):
+    import torch
+    import synth
+    batch = spec["decode_batch"]
+    dec = synth.decode_inputs(batch, spec["H"], spec["dk"], spec["dv"], steps, spec["gate"],
+                              spec["dtype"], seed=spec["seed"] + 1)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in dec.items()}
+    st = synth.decode_initial_states(final_states.cpu(), batch).cuda()
+    out = torch.empty((batch, spec["H"], spec["dv"]), dtype=d["q"].dtype, device="cuda")
+    for s in range(4):
+        gdn.recurrent_step(d["q"][s], d["k"][s], d["v"][s], d["beta"][s], d["log_alpha"][s], st, out=out)
+    st = synth.decode_initial_states(final_states.cpu(), batch).cuda()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        gdn.recurrent_step(d["q"][s], d["k"][s], d["v"][s], d["beta"][s], d["log_alpha"][s], st, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    bytes_step = batch * spec["H"] * (2 * 4 * spec["dk"] * spec["dv"] + 2 * (2 * spec["dk"] + 2 * spec["dv"]) + 8)
+    return {"workload": "gdn-decode-bf16-N%d-H%d-d%d" % (batch, spec["H"], spec["dk"]),
+            "ms_per_step": ms, "tokens_per_s": batch / (ms / 1e3),
+            "hbm_gbs": bytes_step / (ms / 1e3) / 1e9, "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+
+
+def cpu_baseline(inp, H):
+    """The fp64 oracle on the host cores, on the whole workload (bounded: a few
+    seconds), best of two runs."""
+    import oracle
+    threads = oracle.max_threads()
+    best = None
+    for _ in range(2):
+        t0 = time.perf_counter()
+        oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], inp["initial_state"],
+                   inp["cu_seqlens"], nthreads=threads)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    tokens = inp["q"].shape[0] * inp["q"].shape[1]
+    return {"value": tokens / best, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "whole workload (%d tokens x %d heads), fp64 token-by-token recurrence, "
+                      "OpenMP over (sequence, head), best of 2 runs (%.2f s)" % (tokens, H, best)}
+
+
+def bench_workload(gdn, name, steps, warmup):
+    import synth
+    spec = synth.WORKLOADS[name]
+    inp = synth.workload_inputs(name)
+    B, T, H, dk = inp["q"].shape
+    dv = inp["v"].shape[-1]
+    sets = make_device_inputs(inp, ROTATE)
+    wall, launch_ms, _ = time_chunked(gdn, sets, steps, warmup)
+    tokens = B * T
+    esize = 2 if spec["dtype"] == "bf16" else 4
+    flops, nbytes = alg_counts(tokens, H, dk, dv, inp["N"], spec["gate"], esize,
+                               inp["initial_state"] is not None)
+    res = {"workload": name, "ms_per_step": wall / steps * 1e3, "launch_ms": launch_ms,
+           "tokens_per_s": tokens / (wall / steps), "alg_flops": flops, "alg_bytes": nbytes,
+           "tflops": flops / (launch_ms / 1e3) / 1e12,
+           "mfma_frac": flops / (launch_ms / 1e3) / 1e12 / PEAK_MFMA[spec["dtype"]],
+           "hbm_gbs": nbytes / (launch_ms / 1e3) / 1e9,
+           "hbm_frac": nbytes / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+    return res, inp, sets
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--all", action="store_true", help="also report every workload (extra lines on stderr)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_20_amd as gdn
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    res, inp, sets = bench_workload(gdn, HEADLINE, args.steps, args.warmup)
+    spec = synth.WORKLOADS[HEADLINE]
+    B, T, H, dk = inp["q"].shape
+    achieved = res["alg_bytes"] / (res["launch_ms"] / 1e3) / 1e9
+    traffic = read_traffic()
+    line = {
+        "metric": METRIC,
+        "value": res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k L2-normalised, v; sigmoid beta; -softplus*exp(U) "
+                "log decay; N(0,0.02^2) initial state)",
+        "config": {"workload": HEADLINE, "B": B, "T": T, "H": H, "d_k": dk, "d_v": inp["v"].shape[-1],
+                   "chunk": CHUNK, "gate": spec["gate"], "initial_state": True,
+                   "rotated_input_copies": ROTATE},
+        "tflops": res["tflops"],
+        "mfma_peak_frac": res["mfma_frac"],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(inp, H)
+    if args.all:
+        extra = []
+        del sets
+        torch.cuda.empty_cache()
+        for name in ["gdn-bf16-B4-T2048-H8-d128", "kda-bf16-B2-T16384-H16-d128",
+                     "gdn-varlen-bf16-N32-H16-d128", "deltanet-fp32-B1-T256-H2-d64"]:
+            try:
+                r, winp, wsets = bench_workload(gdn, name, max(5, args.steps // 5), 2)
+            except RuntimeError as e:
+                extra.append({"workload": name, "error": str(e)})
+                continue
+            if name.startswith("gdn-varlen"):
+                d = wsets[0]
+                _, fs = gdn.fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], None,
+                                        d["cu_seqlens"])
+                torch.cuda.synchronize()
+                extra.append(time_decode(gdn, synth.WORKLOADS[name], fs))
+            del wsets
+            torch.cuda.empty_cache()
+            extra.append(r)
+        for e in extra:
+            print(json.dumps(e), file=sys.stderr)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

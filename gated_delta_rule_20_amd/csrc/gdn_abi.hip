@@ -103,12 +103,18 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
   p.H = a->H;
   p.T = a->T;
   p.dv = a->d_v;
-  const int dvb = choose_dvb(a->N, a->H, a->d_v);
-  p.nb = a->d_v / dvb;
   if (need) {
     if (gdn::launch_seq_order(a->cu_seqlens, a->N, (int32_t *)a->workspace, stream) != hipSuccess)
       return GDN_ERR_HIP;
   }
+  const bool pipe = a->dtype == GDN_BF16 && a->d_k == 128 && a->gate != GDN_GATE_KEY;
+  if (pipe) {
+    p.nb = a->d_v / 64;
+    if (gdn::launch_fwd_pipe(p, (int)a->gate, stream) != hipSuccess) return GDN_ERR_HIP;
+    return GDN_OK;
+  }
+  const int dvb = choose_dvb(a->N, a->H, a->d_v);
+  p.nb = a->d_v / dvb;
   if (gdn::launch_fwd_fused(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, (int)a->gate, stream) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;

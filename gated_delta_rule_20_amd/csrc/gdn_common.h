@@ -25,6 +25,7 @@ typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename E> struct Frag;
 template <> struct Frag<bf16> { typedef bf16x8 type; };
@@ -100,5 +101,12 @@ __device__ __forceinline__ typename Frag<E>::type frag_from_c_half(const f32x4 &
 }
 
 __device__ __forceinline__ f32x4 zero4() { return (f32x4){0.f, 0.f, 0.f, 0.f}; }
+
+// Empty asm that "reads and writes" a register: the compiler must have the value
+// (waiting for its load here, not earlier) and cannot hoist later arithmetic on it
+// above this point.  Used to keep prefetched tiles in flight until they are stored.
+__device__ __forceinline__ void opaque(u32x4 &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void opaque(float &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void opaque(f32x4 &x) { asm volatile("" : "+v"(x)); }
 
 }  // namespace gdn

@@ -164,6 +164,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       M[t][j] = (sw && p.init_state) ? p.init_state[sbase + (size_t)(16 * t + 4 * lg + j) * dv] : 0.f;
+  // complete the state loads here, so no wait inside the chunk loop refers to them
+#pragma unroll
+  for (int t = 0; t < CF::MT; ++t) opaque(M[t]);
 
   // ---- zero the matrices whose upper blocks are read as zeros
   for (int i = tid; i < (3 * C * ST * CF::ES) / 16; i += NT) ((uint4 *)(smem + CF::OFF_T))[i] = make_uint4(0, 0, 0, 0);
@@ -171,38 +174,50 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   // ---- loader: chunk tiles -> registers -> LDS
   const int cc = tid % CF::CH, rg = tid / CF::CH;
   const int cv = tid % CF::CHV, rgv = tid / CF::CHV;
-  uint4 rk[CF::RPT], rq[CF::RPT], rv[CF::RPTV];
+  u32x4 rk[CF::RPT], rq[CF::RPT], rv[CF::RPTV];
   float rbeta = 0.f, rla = 0.f;
+  // Loads are unconditional (rows past the sequence end re-read its last row) so
+  // that no branch ties the unpacking of a prefetched tile to its load; rows past
+  // the end are zeroed when the tile is stored to LDS.
   auto gload = [&](int c) {
     const int base = c * C;
-    const int nv = min(C, len - base);
+    const int last = min(C, len - base) - 1;
 #pragma unroll
     for (int u = 0; u < CF::RPT; ++u) {
-      const int row = rg * CF::RPT + u;
-      if (row < nv) {
-        rk[u] = *(const uint4 *)(kb + (size_t)(base + row) * sqk + cc * VEC);
-        rq[u] = *(const uint4 *)(qb + (size_t)(base + row) * sqk + cc * VEC);
-      } else {
-        rk[u] = make_uint4(0, 0, 0, 0);
-        rq[u] = make_uint4(0, 0, 0, 0);
-      }
+      const int row = min(rg * CF::RPT + u, last);
+      rk[u] = *(const u32x4 *)(kb + (size_t)(base + row) * sqk + cc * VEC);
+      rq[u] = *(const u32x4 *)(qb + (size_t)(base + row) * sqk + cc * VEC);
     }
 #pragma unroll
     for (int u = 0; u < CF::RPTV; ++u) {
-      const int row = rgv * CF::RPTV + u;
-      rv[u] = (row < nv) ? *(const uint4 *)(vb + (size_t)(base + row) * sv + cv * VEC)
-                         : make_uint4(0, 0, 0, 0);
+      const int row = min(rgv * CF::RPTV + u, last);
+      rv[u] = *(const u32x4 *)(vb + (size_t)(base + row) * sv + cv * VEC);
     }
-    if (tid < C) rbeta = (tid < nv) ? bb[(size_t)(base + tid) * H] : 0.f;
-    if (GATE == GATE_HEAD && tid >= C && tid < 2 * C)
-      rla = (tid - C < nv) ? lab[(size_t)(base + tid - C) * H] : 0.f;
+    if (tid < C) rbeta = bb[(size_t)(base + min(tid, last)) * H];
+    if (GATE == GATE_HEAD && tid >= C && tid < 2 * C) rla = lab[(size_t)(base + min(tid - C, last)) * H];
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int nv) {
+    // the prefetched registers are consumed only from here on
+#pragma unroll
+    for (int u = 0; u < CF::RPT; ++u) {
+      opaque(rk[u]);
+      opaque(rq[u]);
+      if (rg * CF::RPT + u >= nv) rk[u] = rq[u] = (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < CF::RPTV; ++u) {
+      opaque(rv[u]);
+      if (rgv * CF::RPTV + u >= nv) rv[u] = (u32x4){0u, 0u, 0u, 0u};
+    }
+    opaque(rbeta);
+    opaque(rla);
+    if (tid >= nv) rbeta = 0.f;
+    if (tid - C >= nv) rla = 0.f;
 #pragma unroll
     for (int u = 0; u < CF::RPT; ++u) {
       const int row = rg * CF::RPT + u;
-      *(uint4 *)(Ks + row * SK + cc * VEC) = rk[u];
-      *(uint4 *)(Qs + row * SK + cc * VEC) = rq[u];
+      *(u32x4 *)(Ks + row * SK + cc * VEC) = rk[u];
+      *(u32x4 *)(Qs + row * SK + cc * VEC) = rq[u];
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -225,7 +240,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   const int nchunks = (len + C - 1) / C;
   if (nchunks > 0) {
     gload(0);
-    lstore();
+    lstore(min(C, len));
   }
   __syncthreads();
 
@@ -409,7 +424,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       if (row < nv)
         *(uint4 *)(ob + (size_t)(c * C + row) * sv + cq * VEC) = *(const uint4 *)(Os + row * SO + cq * VEC);
     }
-    if (c + 1 < nchunks) lstore();
+    if (c + 1 < nchunks) lstore(min(C, len - (c + 1) * C));
     __syncthreads();
   }
 

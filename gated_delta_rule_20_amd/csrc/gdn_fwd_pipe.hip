@@ -1,0 +1,562 @@
+// gdn_fwd_pipe.hip -- chunked (gated) delta-rule forward, software-pipelined kernel
+// for bf16 I/O, d_k = 128 and 64-column value blocks (the shape of the 350M-class
+// layer and of the other bf16 workloads).
+//
+// Per chunk of C = 64 tokens (the chunkwise form of "Decoding Hybrid Linear
+// Attention Architectures", sec. 5, with the WY/UT representation of "Linear
+// Attention Variants (RetNet, GLA, DeltaNet, Based)", DeltaNet section):
+//   A     = strictly lower (beta_r (K K^T)[r,i] Gamma[r,i]),  Gamma[r,i] = exp(g_r - g_i)
+//   T     = (I + A)^-1
+//   P     = lower-inclusive (Q K^T * Gamma)
+//   Delta = T diag(beta) (V - diag(e^g) K M0)
+//   O     = diag(e^g) Q M0 + P Delta
+//   M_C   = e^{g_C} M0 + K^T diag(e^{g_C - g}) Delta
+//
+// One workgroup = one (sequence, head, 64 value columns); 4 waves with roles:
+//   waves 0, 1  state waves: 32 value columns each.  The fp32 state lives in MFMA
+//               accumulators; per chunk they compute X = K M0, O^T = M0^T Q^T,
+//               Delta = T X, O^T += Delta^T P^T and M += K^T Delta (the state's own
+//               C tiles feed back as operands, "B/A from C").  O is produced
+//               transposed so each lane stores 4 consecutive bf16 of one row.
+//   wave 2      T builder for the NEXT chunk: decay prefix, Gram tiles K K^T ->
+//               A, 16x16 diagonal inverses by forward substitution (one row per
+//               lane, DPP row broadcasts), off-diagonal blocks on MFMA.
+//   wave 3      P builder for the next chunk (Q K^T tiles, decay vectors) and the
+//               loader: buffer loads write the chunk after next straight into LDS
+//               (zero-filled past the sequence end by the buffer range check).
+// K and Q are triple-buffered, V and the precomputed T/P double-buffered, so one
+// barrier per chunk separates producer and consumer stages.
+//
+// LDS layouts are XOR-swizzled instead of padded: K/Q rows of 256 B in 16-byte
+// chunks (chunk ^ (row & 15)), V rows of 128 B (chunk ^ (row & 7)), T/P rows of
+// 128 B in 8-byte units (unit ^ (row & 15)).  K^T and V fragments are read with
+// ds_read_b64_tr_b16 (gfx950 transposing LDS read), so no transposed copies exist.
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int C = 64, DK = 128, DVB = 64, NT = 256;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ---- LDS map (bytes)
+constexpr int KQ_BYTES = 2 * C * DK * 2;  // K then Q
+constexpr int OFF_KQ = 0;                 // x3
+constexpr int V_BYTES = C * DVB * 2;
+constexpr int OFF_V = OFF_KQ + 3 * KQ_BYTES;  // x2
+constexpr int BL_BYTES = 2 * C * 4;           // beta, log alpha
+constexpr int OFF_BL = OFF_V + 2 * V_BYTES;   // x3
+constexpr int PRE_P = C * C * 2;              // T at 0, P at PRE_P
+constexpr int PRE_VEC = 2 * C * C * 2;        // eg[64] egc[64] beta[64] gamma
+constexpr int PRE_BYTES = PRE_VEC + 1024;
+constexpr int OFF_PRE = OFF_BL + 3 * BL_BYTES;  // x2
+constexpr int OFF_AD = OFF_PRE + 2 * PRE_BYTES;  // diagonal blocks of A, fp32 [4][16][16]
+constexpr int AO_STRIDE = 24;                     // off-diagonal blocks, bf16 6 x [16][24]
+constexpr int OFF_AO = OFF_AD + 4 * 16 * 16 * 4;
+constexpr int GS_BYTES = 1088;                    // per producer wave: Ehead, Ehinv, Etail, beta, F
+constexpr int OFF_GS = OFF_AO + 6 * 16 * AO_STRIDE * 2;
+constexpr int LDS_TOTAL = OFF_GS + 2 * GS_BYTES;
+static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ int kq_off(int r, int c) {  // K/Q [64][128] bf16
+  return r * 256 + ((((c >> 3) ^ (r & 15))) << 4) + ((c & 7) << 1);
+}
+__device__ __forceinline__ int v_off(int r, int c) {  // V [64][64] bf16
+  return r * 128 + ((((c >> 3) ^ (r & 7))) << 4) + ((c & 7) << 1);
+}
+__device__ __forceinline__ int tp_off(int r, int c) {  // T/P [64][64] bf16, 8-byte units
+  return r * 128 + ((((c >> 2) ^ (r & 15))) << 3) + ((c & 3) << 1);
+}
+// off-diagonal A block index: (1,0)->0 (2,0)->1 (2,1)->2 (3,0)->3 (3,1)->4 (3,2)->5
+__device__ __forceinline__ int ao_idx(int a, int b) { return a * (a - 1) / 2 + b; }
+
+__device__ __forceinline__ bf16x4 lds_ld4(const char *base, int off) { return *(const bf16x4 *)(base + off); }
+__device__ __forceinline__ bf16x8 cat44(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x4 tr16(const char *p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+  return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
+  return (bf16x4){(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+// broadcast lane `src` of each row of 16 lanes (DPP row_newbcast)
+template <int SRC>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_amdgcn_update_dpp(0.f, x, 0x150 + SRC, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+struct Res {
+  __amdgpu_buffer_rsrc_t k, q, v, beta, la;
+  uint32_t row_qk, row_v, row_s;  // bytes between consecutive tokens
+};
+
+// ---- loader (wave 3): chunk tiles straight into LDS
+__device__ __forceinline__ void load_kq(const Res &rs, char *dst, int chunk, int lane) {
+  const uint32_t soff = (uint32_t)chunk * C * rs.row_qk;
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const int r = 4 * n + (lane >> 4);
+    const int ch = (lane & 15) ^ (r & 15);
+    const uint32_t vo = r * rs.row_qk + ch * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k, (lds_void_t *)(dst + n * 1024), 16, vo, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.q, (lds_void_t *)(dst + C * DK * 2 + n * 1024), 16, vo, soff, 0, 0);
+  }
+}
+__device__ __forceinline__ void load_v(const Res &rs, char *dst, int chunk, int lane) {
+  const uint32_t soff = (uint32_t)chunk * C * rs.row_v;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int r = 8 * n + (lane >> 3);
+    const int ch = (lane & 7) ^ (r & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (lds_void_t *)(dst + n * 1024), 16, r * rs.row_v + ch * 16, soff, 0, 0);
+  }
+}
+template <int GATE>
+__device__ __forceinline__ void load_bl(const Res &rs, char *dst, int chunk, int lane) {
+  const uint32_t soff = (uint32_t)chunk * C * rs.row_s;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.beta, (lds_void_t *)dst, 4, lane * rs.row_s, soff, 0, 0);
+  if (GATE == GATE_HEAD)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.la, (lds_void_t *)(dst + 256), 4, lane * rs.row_s, soff, 0, 0);
+}
+
+// ---- producers: decay prefix and the per-position factors of Gamma.
+// Ehead[r] = e^{g_r - g_{s-1}}, Ehinv[r] = e^{g_{s-1} - g_r}, Etail[r] = e^{g_e - g_r}
+// where s-1 / e are the positions before / at the end of r's 16-block (g_{-1} = 0);
+// F[a][b] = e^{g_{16a-1} - g_{16b+15}} (a > b).  Then Gamma[r,i] = Ehead[r] F Etail[i]
+// across blocks and Ehead[r] Ehinv[i] within a block; every factor except Ehinv is
+// <= 1 and Ehinv spans one block only.  Returns g (this lane's position).
+template <int GATE>
+__device__ __forceinline__ float gate_vectors(const char *bl, char *gs, int lane, float &beta_out) {
+  const float beta = ((const float *)bl)[lane];
+  beta_out = beta;
+  float *Eh = (float *)gs, *Ehi = Eh + 64, *Et = Eh + 128, *bs = Eh + 192, *F = Eh + 256;
+  bs[lane] = beta;
+  if (GATE == GATE_NONE) {
+    Eh[lane] = 1.f;
+    Ehi[lane] = 1.f;
+    Et[lane] = 1.f;
+    if (lane < 16) F[lane] = 1.f;
+    return 0.f;
+  }
+  float g = ((const float *)bl)[64 + lane];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(g, off);
+    if (lane >= off) g += y;
+  }
+  const int blk = lane >> 4;
+  // shuffles run on all lanes (a lane masked off in a bpermute provides no data)
+  const float gp = __shfl(g, blk ? 16 * blk - 1 : 0);
+  const float gprev = blk ? gp : 0.f;
+  const float gend = __shfl(g, 16 * blk + 15);
+  Eh[lane] = __expf(g - gprev);
+  Ehi[lane] = __expf(gprev - g);
+  Et[lane] = __expf(gend - g);
+  // F[a*4+b] for a > b
+  const float gE0 = __shfl(g, 15), gE1 = __shfl(g, 31), gE2 = __shfl(g, 47);
+  if (lane < 16) {
+    const int a = lane >> 2, b = lane & 3;
+    const float ga = a == 1 ? gE0 : a == 2 ? gE1 : gE2;  // g_{16a-1}
+    const float gb = b == 0 ? gE0 : b == 1 ? gE1 : gE2;  // g_{16b+15}
+    F[lane] = (a > b) ? __expf(ga - gb) : 0.f;
+  }
+  return g;
+}
+
+// Gamma-weighted tile entries for tile (a, b), row r = 16a + lm, columns i = 16b + 4lg + j.
+// Returns the mask/decay factor per j (0 where i > r, or i >= r when strict).
+template <int GATE, bool STRICT>
+__device__ __forceinline__ f32x4 gamma_row(const char *gs, int a, int b, int lm, int lg) {
+  const float *Eh = (const float *)gs, *Ehi = Eh + 64, *Et = Eh + 128, *F = Eh + 256;
+  const int r = 16 * a + lm;
+  f32x4 out;
+  if (a > b) {
+    const float h = Eh[r] * F[4 * a + b];
+    const f32x4 et = *(const f32x4 *)(Et + 16 * b + 4 * lg);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = (GATE == GATE_NONE) ? 1.f : h * et[j];
+  } else {
+    const float h = Eh[r];
+    const f32x4 ehi = *(const f32x4 *)(Ehi + 16 * b + 4 * lg);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 16 * b + 4 * lg + j;
+      const bool keep = STRICT ? (i < r) : (i <= r);
+      out[j] = keep ? ((GATE == GATE_NONE) ? 1.f : h * ehi[j]) : 0.f;
+    }
+  }
+  return out;
+}
+
+template <int GATE>
+__global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
+  __shared__ __align__(16) char smem[LDS_TOTAL];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lg = lane >> 4, lm = lane & 15;
+
+  // ---- workgroup -> (sequence, head, value block); blocks of one (sequence,
+  // head) get ids equal mod 8 (same XCD, shared L2 for K and Q).
+  const int nb = p.nb;
+  const int total = p.N * p.H * nb;
+  const int bid = blockIdx.x;
+  const int grp = 8 * nb;
+  const int full = (total / grp) * grp;
+  int pair, jb;
+  if (bid < full) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    pair = (slot / nb) * 8 + xcd;
+    jb = slot % nb;
+  } else {
+    pair = bid / nb;
+    jb = bid % nb;
+  }
+  const int sidx = pair / p.H, h = pair % p.H;
+  const int n = p.order ? p.order[sidx] : sidx;
+  long tok0;
+  int len;
+  if (p.cu_seqlens) {
+    const int a = p.cu_seqlens[n], b = p.cu_seqlens[n + 1];
+    if (a < 0 || b < a || b > p.T) return;  // malformed offsets: leave untouched
+    tok0 = a;
+    len = b - a;
+  } else {
+    tok0 = (long)n * p.T;
+    len = p.T;
+  }
+  const int H = p.H, dv = p.dv, col0 = jb * DVB;
+  const int nchunks = (len + C - 1) / C;
+
+  Res rs;
+  rs.row_qk = (uint32_t)H * DK * 2;
+  rs.row_v = (uint32_t)H * dv * 2;
+  rs.row_s = (uint32_t)H * 4;
+  {
+    const int lm1 = len > 0 ? len - 1 : 0;
+    const uint32_t nk = len > 0 ? (uint32_t)lm1 * rs.row_qk + DK * 2 : 0;
+    const uint32_t nvb = len > 0 ? (uint32_t)lm1 * rs.row_v + DVB * 2 : 0;
+    const uint32_t ns = len > 0 ? (uint32_t)lm1 * rs.row_s + 4 : 0;
+    rs.k = __builtin_amdgcn_make_buffer_rsrc((void *)((const bf16 *)p.k + ((size_t)tok0 * H + h) * DK), 0, nk, 0x00020000);
+    rs.q = __builtin_amdgcn_make_buffer_rsrc((void *)((const bf16 *)p.q + ((size_t)tok0 * H + h) * DK), 0, nk, 0x00020000);
+    rs.v = __builtin_amdgcn_make_buffer_rsrc((void *)((const bf16 *)p.v + ((size_t)tok0 * H + h) * dv + col0), 0, nvb, 0x00020000);
+    rs.beta = __builtin_amdgcn_make_buffer_rsrc((void *)(p.beta + (size_t)tok0 * H + h), 0, ns, 0x00020000);
+    rs.la = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(GATE == GATE_HEAD ? p.log_alpha + (size_t)tok0 * H + h : p.beta), 0, GATE == GATE_HEAD ? ns : 0, 0x00020000);
+  }
+
+  auto KQ = [&](int i) { return smem + OFF_KQ + i * KQ_BYTES; };
+  auto VB = [&](int i) { return smem + OFF_V + i * V_BYTES; };
+  auto BL = [&](int i) { return smem + OFF_BL + i * BL_BYTES; };
+  auto PRE = [&](int i) { return smem + OFF_PRE + i * PRE_BYTES; };
+  char *AD = smem + OFF_AD, *AO = smem + OFF_AO;
+
+  // ---- prologue: zero T and P of both stages (their upper blocks stay zero)
+  for (int i = tid; i < 2 * (PRE_VEC / 16); i += NT) {
+    const int s = i / (PRE_VEC / 16), w = i % (PRE_VEC / 16);
+    ((uint4 *)PRE(s))[w] = make_uint4(0, 0, 0, 0);
+  }
+  if (wave == 3 && nchunks > 0) {
+    load_kq(rs, KQ(0), 0, lane);
+    load_bl<GATE>(rs, BL(0), 0, lane);
+    load_v(rs, VB(0), 0, lane);
+    if (nchunks > 1) {
+      load_kq(rs, KQ(1), 1, lane);
+      load_bl<GATE>(rs, BL(1), 1, lane);
+    }
+    wait_vm0();
+  }
+
+  // ---- state (waves 0, 1): 2 column tiles x 8 row tiles of fp32 C tiles
+  const int n0 = 32 * wave;  // first value column of this wave inside the block
+  f32x4 M[2][8];
+  const size_t sbase = ((size_t)n * H + h) * DK * dv + col0 + n0 + lm;
+  if (wave < 2) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          M[ct][t][j] = p.init_state ? p.init_state[sbase + 16 * ct + (size_t)(16 * t + 4 * lg + j) * dv] : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) opaque(M[ct][t]);
+  }
+  __syncthreads();
+
+  // ---- producer stage: everything of chunk `cc` that does not depend on the state
+  auto produce = [&](int cc) {
+    const char *kq = KQ(cc % 3);
+    const char *bl = BL(cc % 3);
+    char *pre = PRE(cc & 1);
+    char *gs = smem + OFF_GS + (wave - 2) * GS_BYTES;
+    float beta;
+    const float g = gate_vectors<GATE>(bl, gs, lane, beta);
+    const char *Ks = kq, *Qs = kq + C * DK * 2;
+    if (wave == 3) {
+      // decay vectors for the state waves
+      float *vec = (float *)(pre + PRE_VEC);
+      const float gC = __shfl(g, 63);
+      vec[lane] = (GATE == GATE_HEAD) ? __expf(g) : 1.f;
+      vec[64 + lane] = (GATE == GATE_HEAD) ? __expf(gC - g) : 1.f;
+      vec[128 + lane] = beta;
+      if (lane == 0) vec[192] = (GATE == GATE_HEAD) ? __expf(gC) : 1.f;
+      // P = lower-inclusive(Q K^T * Gamma): tile (a, b) computed as K_b Q_a^T so the
+      // lane holds row 16a+lm, columns 16b+4lg..+3 (the A-operand fragment layout)
+      bf16x8 kf[4][4], qf[4][4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          kf[b][s] = *(const bf16x8 *)(Ks + kq_off(16 * b + lm, 32 * s + 8 * lg));
+          qf[b][s] = *(const bf16x8 *)(Qs + kq_off(16 * b + lm, 32 * s + 8 * lg));
+        }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b <= a; ++b) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc = mma(kf[b][s], qf[a][s], acc);
+          const f32x4 gm = gamma_row<GATE, false>(gs, a, b, lm, lg);
+          *(bf16x4 *)(pre + PRE_P + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(acc * gm);
+        }
+    } else {
+      // A = strictly lower(beta_r K K^T * Gamma): tile (a, b) computed as K_b K_a^T
+      // (K K^T is symmetric), lane holds row 16a+lm, columns 16b+4lg..+3
+      bf16x8 kf[4][4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[b][s] = *(const bf16x8 *)(Ks + kq_off(16 * b + lm, 32 * s + 8 * lg));
+      const float *bs = (const float *)gs + 192;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float br = bs[16 * a + lm];
+#pragma unroll
+        for (int b = 0; b <= a; ++b) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc = mma(kf[b][s], kf[a][s], acc);
+          const f32x4 av = acc * gamma_row<GATE, true>(gs, a, b, lm, lg) * br;
+          if (a == b)
+            *(f32x4 *)(AD + ((16 * a + lm) * 16 + 4 * lg) * 4) = av;
+          else
+            *(bf16x4 *)(AO + (ao_idx(a, b) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) = to_bf4(av);
+        }
+      }
+      // diagonal 16x16 blocks of T = (I + A)^-1: lane (lg, lm) owns row lm of block lg;
+      // t_r = e_r - sum_{i<r} A[r][i] t_i with rows broadcast along the 16-lane DPP row
+      float ar[16], t[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v4 = *(const f32x4 *)(AD + ((16 * lg + lm) * 16 + 4 * q4) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ar[4 * q4 + j] = v4[j];
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) t[c] = (c == lm) ? 1.f : 0.f;
+#define GDN_T1_STEP(I)                                                    \
+  _Pragma("unroll") for (int c = 0; c <= I; ++c) t[c] -= ar[I] * row_bcast<I>(t[c]);
+      GDN_T1_STEP(0) GDN_T1_STEP(1) GDN_T1_STEP(2) GDN_T1_STEP(3) GDN_T1_STEP(4)
+      GDN_T1_STEP(5) GDN_T1_STEP(6) GDN_T1_STEP(7) GDN_T1_STEP(8) GDN_T1_STEP(9)
+      GDN_T1_STEP(10) GDN_T1_STEP(11) GDN_T1_STEP(12) GDN_T1_STEP(13) GDN_T1_STEP(14)
+#undef GDN_T1_STEP
+      char *Tm = pre;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(bf16x4 *)(Tm + tp_off(16 * lg + lm, 16 * lg + 4 * q4)) =
+            to_bf4((f32x4){t[4 * q4], t[4 * q4 + 1], t[4 * q4 + 2], t[4 * q4 + 3]});
+      // off-diagonal blocks, level by level: T[a][b] = -T[a][a] sum_{k=b}^{a-1} A[a][k] T[k][b],
+      // computed transposed (Z = T[a][b]^T = -Y^T T[a][a]^T) so the lane holds a row
+#pragma unroll
+      for (int lev = 1; lev < 4; ++lev) {
+#pragma unroll
+        for (int b = 0; b + lev < 4; ++b) {
+          const int a = b + lev;
+          f32x4 y = zero4();
+#pragma unroll
+          for (int k0 = 0; k0 < 4; k0 += 2) {
+            const bool in0 = (k0 >= b && k0 < a), in1 = (k0 + 1 >= b && k0 + 1 < a);
+            if (in0 || in1) {
+              const bf16x4 z4 = {};
+              const bf16x4 a0 = in0 ? lds_ld4(AO, (ao_idx(a, k0) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) : z4;
+              const bf16x4 a1 = in1 ? lds_ld4(AO, (ao_idx(a, k0 + 1) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) : z4;
+              // B = T[k][b] column-distributed: transposing reads of row-major T
+              const bf16x4 b0 = in0 ? tr16(Tm + tp_off(16 * k0 + 4 * lg + (lm >> 2), 16 * b + 4 * (lm & 3))) : z4;
+              const bf16x4 b1 = in1 ? tr16(Tm + tp_off(16 * (k0 + 1) + 4 * lg + (lm >> 2), 16 * b + 4 * (lm & 3))) : z4;
+              y = mma(cat44(a0, a1), cat44(b0, b1), y);
+            }
+          }
+          const bf16x4 z4 = {};
+          const bf16x8 yA = cat44(to_bf4(y), z4);
+          const bf16x8 taa = cat44(lds_ld4(Tm, tp_off(16 * a + lm, 16 * a + 4 * lg)), z4);
+          const f32x4 zt = mma(yA, taa, zero4());
+          *(bf16x4 *)(Tm + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(-zt);
+        }
+      }
+    }
+  };
+
+  if (wave >= 2 && nchunks > 0) produce(0);
+  __syncthreads();
+
+  const int H_ = H;
+  bf16 *og = (bf16 *)p.o + ((size_t)tok0 * H_ + h) * dv + col0 + n0;
+  for (int c = 0; c < nchunks; ++c) {
+    if (wave >= 2) {
+      if (wave == 3) {
+        if (c + 2 < nchunks) {
+          load_kq(rs, KQ((c + 2) % 3), c + 2, lane);
+          load_bl<GATE>(rs, BL((c + 2) % 3), c + 2, lane);
+        }
+        if (c + 1 < nchunks) load_v(rs, VB((c + 1) & 1), c + 1, lane);
+      }
+      if (c + 1 < nchunks) produce(c + 1);
+      if (wave == 3) wait_vm0();
+    } else {
+      const char *Ks = KQ(c % 3), *Qs = KQ(c % 3) + C * DK * 2;
+      const char *Vs = VB(c & 1);
+      const char *pre = PRE(c & 1);
+      const float *vec = (const float *)(pre + PRE_VEC);
+      // state as operands: the same fragments serve as B (for K M) and A (for M^T Q^T)
+      bf16x8 MB[2][4];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) MB[ct][s] = frag_from_c<bf16>(M[ct][2 * s], M[ct][2 * s + 1]);
+      f32x4 X[2][4], OT[2][4];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[ct][i] = OT[ct][i] = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * i + lm, cA = 32 * s + 4 * lg;
+          const bf16x8 kf = cat44(lds_ld4(Ks, kq_off(r, cA)), lds_ld4(Ks, kq_off(r, cA + 16)));
+          const bf16x8 qf = cat44(lds_ld4(Qs, kq_off(r, cA)), lds_ld4(Qs, kq_off(r, cA + 16)));
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            X[ct][i] = mma(kf, MB[ct][s], X[ct][i]);
+            OT[ct][i] = mma(MB[ct][s], qf, OT[ct][i]);
+          }
+        }
+      // X <- beta (V - e^g X);  O^T columns (positions) scaled by e^g
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 eg4 = *(const f32x4 *)(vec + 16 * i + 4 * lg);
+        const f32x4 be4 = *(const f32x4 *)(vec + 128 + 16 * i + 4 * lg);
+        const float egl = vec[16 * i + lm];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const bf16x4 v4 = tr16(Vs + v_off(16 * i + 4 * lg + (lm >> 2), n0 + 16 * ct + 4 * (lm & 3)));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) X[ct][i][j] = be4[j] * ((float)v4[j] - eg4[j] * X[ct][i][j]);
+          OT[ct][i] *= egl;
+        }
+      }
+      // Delta = T X
+      f32x4 D[2][4];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) D[ct][i] = zero4();
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 XB[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) XB[ct] = frag_from_c<bf16>(X[ct][2 * s2], X[ct][2 * s2 + 1]);
+#pragma unroll
+        for (int i = 2 * s2; i < 4; ++i) {
+          const int r = 16 * i + lm, cA = 32 * s2 + 4 * lg;
+          const char *Tm = pre;
+          const bf16x8 tf = cat44(lds_ld4(Tm, tp_off(r, cA)), lds_ld4(Tm, tp_off(r, cA + 16)));
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) D[ct][i] = mma(tf, XB[ct], D[ct][i]);
+        }
+      }
+      // O^T += Delta^T P^T ;  M <- e^{g_C} M + K^T diag(e^{g_C - g}) Delta
+      bf16x8 DA[2][2], DT[2][2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const f32x4 ec0 = *(const f32x4 *)(vec + 64 + 32 * s2 + 4 * lg);
+        const f32x4 ec1 = *(const f32x4 *)(vec + 64 + 32 * s2 + 16 + 4 * lg);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          DA[ct][s2] = frag_from_c<bf16>(D[ct][2 * s2], D[ct][2 * s2 + 1]);
+          DT[ct][s2] = frag_from_c<bf16>(D[ct][2 * s2] * ec0, D[ct][2 * s2 + 1] * ec1);
+        }
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 2 * s2; i < 4; ++i) {
+          const int r = 16 * i + lm, cA = 32 * s2 + 4 * lg;
+          const char *Pm = pre + PRE_P;
+          const bf16x8 pf = cat44(lds_ld4(Pm, tp_off(r, cA)), lds_ld4(Pm, tp_off(r, cA + 16)));
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) OT[ct][i] = mma(DA[ct][s2], pf, OT[ct][i]);
+        }
+      const float gam = vec[192];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) M[ct][t] *= gam;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int rr = 32 * s2 + 4 * lg + (lm >> 2), cc = 16 * t + 4 * (lm & 3);
+          const bf16x8 ktf = cat44(tr16(Ks + kq_off(rr, cc)), tr16(Ks + kq_off(rr + 16, cc)));
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) M[ct][t] = mma(ktf, DT[ct][s2], M[ct][t]);
+        }
+      }
+      // O rows -> HBM: lane holds O[16i+lm][n0 + 16ct + 4lg .. +3]
+      const int nv = min(C, len - c * C);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * i + lm;
+        if (row < nv) {
+          bf16 *dst = og + ((size_t)(c * C + row) * H_) * dv + 4 * lg;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) *(bf16x4 *)(dst + 16 * ct) = to_bf4(OT[ct][i]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (wave < 2 && p.final_state) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p.final_state[sbase + 16 * ct + (size_t)(16 * t + 4 * lg + j) * dv] = M[ct][t][j];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_pipe(const FwdParams &p, int gate, hipStream_t stream) {
+  const int blocks = p.N * p.H * p.nb;
+  if (blocks == 0) return hipSuccess;
+  switch (gate) {
+    case GATE_NONE: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_NONE>), dim3(blocks), dim3(NT), 0, stream, p); break;
+    case GATE_HEAD: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_HEAD>), dim3(blocks), dim3(NT), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

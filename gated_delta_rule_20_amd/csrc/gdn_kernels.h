@@ -34,6 +34,9 @@ struct StepParams {
 // dvb: columns of d_v per workgroup (32 or 64).
 hipError_t launch_fwd_fused(const FwdParams &p, int dtype, int dk, int dvb, int gate,
                             hipStream_t stream);
+// Software-pipelined forward for bf16, d_k = 128, 64-column value blocks (nb = d_v / 64),
+// gate NONE or HEAD.
+hipError_t launch_fwd_pipe(const FwdParams &p, int gate, hipStream_t stream);
 hipError_t launch_seq_order(const int32_t *cu_seqlens, int N, int32_t *order, hipStream_t stream);
 hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate,
                                  hipStream_t stream);
