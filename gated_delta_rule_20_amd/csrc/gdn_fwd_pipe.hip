@@ -71,6 +71,9 @@ __device__ __forceinline__ int v_off(int r, int c) {  // V [64][64] bf16
 __device__ __forceinline__ int tp_off(int r, int c) {  // T/P [64][64] bf16, 8-byte units
   return r * 128 + ((((c >> 2) ^ (r & 15))) << 3) + ((c & 3) << 1);
 }
+// the ten lower 16x16 tiles (a >= b) of a 64x64 chunk matrix
+constexpr int TA[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+constexpr int TB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 // off-diagonal A block index: (1,0)->0 (2,0)->1 (2,1)->2 (3,0)->3 (3,1)->4 (3,2)->5
 __device__ __forceinline__ int ao_idx(int a, int b) { return a * (a - 1) / 2 + b; }
 
@@ -88,7 +91,15 @@ __device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
 // broadcast lane `src` of each row of 16 lanes (DPP row_newbcast)
 template <int SRC>
 __device__ __forceinline__ float row_bcast(float x) {
-  return __builtin_amdgcn_update_dpp(0.f, x, 0x150 + SRC, 0xF, 0xF, false);
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + SRC, 0xF, 0xF, false));
+}
+// x from lane - N of the same 16-lane row, 0 for the first N lanes of a row (DPP row_shr)
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float readlane(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -147,21 +158,22 @@ __device__ __forceinline__ float gate_vectors(const char *bl, char *gs, int lane
     return 0.f;
   }
   float g = ((const float *)bl)[64 + lane];
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(g, off);
-    if (lane >= off) g += y;
-  }
+  // inclusive prefix sum: within rows of 16 lanes by DPP shifts, then row totals
+  g += row_shr<1>(g);
+  g += row_shr<2>(g);
+  g += row_shr<4>(g);
+  g += row_shr<8>(g);
   const int blk = lane >> 4;
-  // shuffles run on all lanes (a lane masked off in a bpermute provides no data)
-  const float gp = __shfl(g, blk ? 16 * blk - 1 : 0);
-  const float gprev = blk ? gp : 0.f;
-  const float gend = __shfl(g, 16 * blk + 15);
+  const float t0 = readlane(g, 15), t1 = readlane(g, 31), t2 = readlane(g, 47);
+  const float gE0 = t0, gE1 = t0 + t1, gE2 = t0 + t1 + t2;  // g at positions 15, 31, 47
+  const float gprev = blk == 0 ? 0.f : blk == 1 ? gE0 : blk == 2 ? gE1 : gE2;
+  g += gprev;
+  const float gE3 = readlane(g, 63);
+  const float gend = blk == 0 ? gE0 : blk == 1 ? gE1 : blk == 2 ? gE2 : gE3;
   Eh[lane] = __expf(g - gprev);
   Ehi[lane] = __expf(gprev - g);
   Et[lane] = __expf(gend - g);
   // F[a*4+b] for a > b
-  const float gE0 = __shfl(g, 15), gE1 = __shfl(g, 31), gE2 = __shfl(g, 47);
   if (lane < 16) {
     const int a = lane >> 2, b = lane & 3;
     const float ga = a == 1 ? gE0 : a == 2 ? gE1 : gE2;  // g_{16a-1}
@@ -263,36 +275,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     const int s = i / (PRE_VEC / 16), w = i % (PRE_VEC / 16);
     ((uint4 *)PRE(s))[w] = make_uint4(0, 0, 0, 0);
   }
-  if (wave == 3 && nchunks > 0) {
-    load_kq(rs, KQ(0), 0, lane);
-    load_bl<GATE>(rs, BL(0), 0, lane);
-    load_v(rs, VB(0), 0, lane);
-    if (nchunks > 1) {
-      load_kq(rs, KQ(1), 1, lane);
-      load_bl<GATE>(rs, BL(1), 1, lane);
-    }
-    wait_vm0();
-  }
-
-  // ---- state (waves 0, 1): 2 column tiles x 8 row tiles of fp32 C tiles
-  const int n0 = 32 * wave;  // first value column of this wave inside the block
-  f32x4 M[2][8];
-  const size_t sbase = ((size_t)n * H + h) * DK * dv + col0 + n0 + lm;
-  if (wave < 2) {
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          M[ct][t][j] = p.init_state ? p.init_state[sbase + 16 * ct + (size_t)(16 * t + 4 * lg + j) * dv] : 0.f;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) opaque(M[ct][t]);
-  }
-  __syncthreads();
-
   // ---- producer stage: everything of chunk `cc` that does not depend on the state
   auto produce = [&](int cc) {
     const char *kq = KQ(cc % 3);
@@ -302,71 +284,73 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     float beta;
     const float g = gate_vectors<GATE>(bl, gs, lane, beta);
     const char *Ks = kq, *Qs = kq + C * DK * 2;
+    // K rows as fragments: row 16b+lm, natural columns 32s+8lg..+7
+    bf16x8 kf[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kf[b][s] = *(const bf16x8 *)(Ks + kq_off(16 * b + lm, 32 * s + 8 * lg));
     if (wave == 3) {
       // decay vectors for the state waves
       float *vec = (float *)(pre + PRE_VEC);
-      const float gC = __shfl(g, 63);
+      const float gC = readlane(g, 63);
       vec[lane] = (GATE == GATE_HEAD) ? __expf(g) : 1.f;
       vec[64 + lane] = (GATE == GATE_HEAD) ? __expf(gC - g) : 1.f;
       vec[128 + lane] = beta;
       if (lane == 0) vec[192] = (GATE == GATE_HEAD) ? __expf(gC) : 1.f;
       // P = lower-inclusive(Q K^T * Gamma): tile (a, b) computed as K_b Q_a^T so the
-      // lane holds row 16a+lm, columns 16b+4lg..+3 (the A-operand fragment layout)
-      bf16x8 kf[4][4], qf[4][4];
+      // lane holds row 16a+lm, columns 16b+4lg..+3 (the A-operand fragment layout);
+      // the ten accumulation chains are interleaved
+      f32x4 acc[10];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int t = 0; t < 10; ++t) acc[t] = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          kf[b][s] = *(const bf16x8 *)(Ks + kq_off(16 * b + lm, 32 * s + 8 * lg));
-          qf[b][s] = *(const bf16x8 *)(Qs + kq_off(16 * b + lm, 32 * s + 8 * lg));
-        }
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 qf[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) qf[a] = *(const bf16x8 *)(Qs + kq_off(16 * a + lm, 32 * s + 8 * lg));
 #pragma unroll
-        for (int b = 0; b <= a; ++b) {
-          f32x4 acc = zero4();
+        for (int t = 0; t < 10; ++t) acc[t] = mma(kf[TB[t]][s], qf[TA[t]], acc[t]);
+      }
 #pragma unroll
-          for (int s = 0; s < 4; ++s) acc = mma(kf[b][s], qf[a][s], acc);
-          const f32x4 gm = gamma_row<GATE, false>(gs, a, b, lm, lg);
-          *(bf16x4 *)(pre + PRE_P + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(acc * gm);
-        }
+      for (int t = 0; t < 10; ++t) {
+        const int a = TA[t], b = TB[t];
+        const f32x4 gm = gamma_row<GATE, false>(gs, a, b, lm, lg);
+        *(bf16x4 *)(pre + PRE_P + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(acc[t] * gm);
+      }
     } else {
       // A = strictly lower(beta_r K K^T * Gamma): tile (a, b) computed as K_b K_a^T
       // (K K^T is symmetric), lane holds row 16a+lm, columns 16b+4lg..+3
-      bf16x8 kf[4][4];
+      f32x4 acc[10];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int t = 0; t < 10; ++t) acc[t] = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kf[b][s] = *(const bf16x8 *)(Ks + kq_off(16 * b + lm, 32 * s + 8 * lg));
-      const float *bs = (const float *)gs + 192;
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float br = bs[16 * a + lm];
+        for (int t = 0; t < 10; ++t) acc[t] = mma(kf[TB[t]][s], kf[TA[t]][s], acc[t]);
+      const float *bsa = (const float *)gs + 192;
 #pragma unroll
-        for (int b = 0; b <= a; ++b) {
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int s = 0; s < 4; ++s) acc = mma(kf[b][s], kf[a][s], acc);
-          const f32x4 av = acc * gamma_row<GATE, true>(gs, a, b, lm, lg) * br;
-          if (a == b)
-            *(f32x4 *)(AD + ((16 * a + lm) * 16 + 4 * lg) * 4) = av;
-          else
-            *(bf16x4 *)(AO + (ao_idx(a, b) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) = to_bf4(av);
-        }
+      for (int t = 0; t < 10; ++t) {
+        const int a = TA[t], b = TB[t];
+        const f32x4 av = acc[t] * gamma_row<GATE, true>(gs, a, b, lm, lg) * bsa[16 * a + lm];
+        if (a == b)
+          *(f32x4 *)(AD + ((16 * a + lm) * 16 + 4 * lg) * 4) = av;
+        else
+          *(bf16x4 *)(AO + (ao_idx(a, b) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) = to_bf4(av);
       }
       // diagonal 16x16 blocks of T = (I + A)^-1: lane (lg, lm) owns row lm of block lg;
       // t_r = e_r - sum_{i<r} A[r][i] t_i with rows broadcast along the 16-lane DPP row
-      float ar[16], t[16];
+      float nar[16], t[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 v4 = *(const f32x4 *)(AD + ((16 * lg + lm) * 16 + 4 * q4) * 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ar[4 * q4 + j] = v4[j];
+        for (int j = 0; j < 4; ++j) nar[4 * q4 + j] = -v4[j];
       }
 #pragma unroll
       for (int c = 0; c < 16; ++c) t[c] = (c == lm) ? 1.f : 0.f;
 #define GDN_T1_STEP(I)                                                    \
-  _Pragma("unroll") for (int c = 0; c <= I; ++c) t[c] -= ar[I] * row_bcast<I>(t[c]);
+  _Pragma("unroll") for (int c = 0; c <= I; ++c) t[c] = __builtin_fmaf(row_bcast<I>(t[c]), nar[I], t[c]);
       GDN_T1_STEP(0) GDN_T1_STEP(1) GDN_T1_STEP(2) GDN_T1_STEP(3) GDN_T1_STEP(4)
       GDN_T1_STEP(5) GDN_T1_STEP(6) GDN_T1_STEP(7) GDN_T1_STEP(8) GDN_T1_STEP(9)
       GDN_T1_STEP(10) GDN_T1_STEP(11) GDN_T1_STEP(12) GDN_T1_STEP(13) GDN_T1_STEP(14)
@@ -376,8 +360,27 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       for (int q4 = 0; q4 < 4; ++q4)
         *(bf16x4 *)(Tm + tp_off(16 * lg + lm, 16 * lg + 4 * q4)) =
             to_bf4((f32x4){t[4 * q4], t[4 * q4 + 1], t[4 * q4 + 2], t[4 * q4 + 3]});
-      // off-diagonal blocks, level by level: T[a][b] = -T[a][a] sum_{k=b}^{a-1} A[a][k] T[k][b],
-      // computed transposed (Z = T[a][b]^T = -Y^T T[a][a]^T) so the lane holds a row
+      const float *bs = (const float *)gs + 192;
+      // off-diagonal blocks, level by level: Y = sum_{k=b}^{a-1} A[a][k] T[k][b],
+      // T[a][b] = -T[a][a] Y.  T[k][b] stay in registers as C tiles (column-distributed);
+      // the transposed product -Y^T T[a][a]^T gives the row-distributed copy for LDS.
+      f32x4 Tc[4][4];  // [k][b], C layout
+#pragma unroll
+      for (int b = 0; b < 4; ++b)  // diagonal blocks, column-distributed, via transposing reads
+        Tc[b][b] = [&] {
+          const bf16x4 v = tr16(Tm + tp_off(16 * b + 4 * lg + (lm >> 2), 16 * b + 4 * (lm & 3)));
+          return (f32x4){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+        }();
+      bf16x8 taa[4];  // T[a][a] rows: lane holds T[a][a][lm][4lg..4lg+3], zero-padded to 32-deep
+#pragma unroll
+      for (int a = 1; a < 4; ++a) taa[a] = cat44(lds_ld4(Tm, tp_off(16 * a + lm, 16 * a + 4 * lg)), (bf16x4){});
+      // the unscaled diagonal blocks are in registers now: store them as T diag(beta)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 b4 = *(const f32x4 *)(bs + 16 * lg + 4 * q4);
+        *(bf16x4 *)(Tm + tp_off(16 * lg + lm, 16 * lg + 4 * q4)) =
+            to_bf4((f32x4){t[4 * q4], t[4 * q4 + 1], t[4 * q4 + 2], t[4 * q4 + 3]} * b4);
+      }
 #pragma unroll
       for (int lev = 1; lev < 4; ++lev) {
 #pragma unroll
@@ -391,39 +394,86 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
               const bf16x4 z4 = {};
               const bf16x4 a0 = in0 ? lds_ld4(AO, (ao_idx(a, k0) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) : z4;
               const bf16x4 a1 = in1 ? lds_ld4(AO, (ao_idx(a, k0 + 1) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) : z4;
-              // B = T[k][b] column-distributed: transposing reads of row-major T
-              const bf16x4 b0 = in0 ? tr16(Tm + tp_off(16 * k0 + 4 * lg + (lm >> 2), 16 * b + 4 * (lm & 3))) : z4;
-              const bf16x4 b1 = in1 ? tr16(Tm + tp_off(16 * (k0 + 1) + 4 * lg + (lm >> 2), 16 * b + 4 * (lm & 3))) : z4;
-              y = mma(cat44(a0, a1), cat44(b0, b1), y);
+              const bf16x8 bfr = frag_from_c<bf16>(in0 ? Tc[k0][b] : zero4(), in1 ? Tc[k0 + 1][b] : zero4());
+              y = mma(cat44(a0, a1), bfr, y);
             }
           }
-          const bf16x4 z4 = {};
-          const bf16x8 yA = cat44(to_bf4(y), z4);
-          const bf16x8 taa = cat44(lds_ld4(Tm, tp_off(16 * a + lm, 16 * a + 4 * lg)), z4);
-          const f32x4 zt = mma(yA, taa, zero4());
-          *(bf16x4 *)(Tm + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(-zt);
+          const bf16x8 yf = frag_from_c_half<bf16>(y);
+          Tc[a][b] = -mma(taa[a], yf, zero4());           // T[a][b], column-distributed
+          const f32x4 zt = mma(yf, taa[a], zero4());       // (T[a][a] Y)^T: row-distributed
+          const f32x4 b4 = *(const f32x4 *)(bs + 16 * b + 4 * lg);
+          *(bf16x4 *)(Tm + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(-zt * b4);
         }
       }
     }
   };
 
-  if (wave >= 2 && nchunks > 0) produce(0);
-  __syncthreads();
-
-  const int H_ = H;
-  bf16 *og = (bf16 *)p.o + ((size_t)tok0 * H_ + h) * dv + col0 + n0;
-  for (int c = 0; c < nchunks; ++c) {
-    if (wave >= 2) {
-      if (wave == 3) {
-        if (c + 2 < nchunks) {
-          load_kq(rs, KQ((c + 2) % 3), c + 2, lane);
-          load_bl<GATE>(rs, BL((c + 2) % 3), c + 2, lane);
-        }
-        if (c + 1 < nchunks) load_v(rs, VB((c + 1) & 1), c + 1, lane);
+  if (wave >= 2) {
+    // ===================== producer waves: T/P builders and loader =====================
+    if (wave == 3 && nchunks > 0) {
+      load_kq(rs, KQ(0), 0, lane);
+      load_bl<GATE>(rs, BL(0), 0, lane);
+      load_v(rs, VB(0), 0, lane);
+      if (nchunks > 1) {
+        load_kq(rs, KQ(1), 1, lane);
+        load_bl<GATE>(rs, BL(1), 1, lane);
       }
-      if (c + 1 < nchunks) produce(c + 1);
-      if (wave == 3) wait_vm0();
-    } else {
+      wait_vm0();
+    }
+
+    __syncthreads();
+    if (nchunks > 0) produce(0);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        if (wave == 3) {
+          if (c + 2 < nchunks) {
+            load_kq(rs, KQ((c + 2) % 3), c + 2, lane);
+            load_bl<GATE>(rs, BL((c + 2) % 3), c + 2, lane);
+          }
+          if (c + 1 < nchunks) load_v(rs, VB((c + 1) & 1), c + 1, lane);
+        }
+        if (c + 1 < nchunks) produce(c + 1);
+        if (wave == 3) wait_vm0();
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ===================== state waves (0, 1) =====================
+  // ---- state (waves 0, 1): 2 column tiles x 8 row tiles of fp32 C tiles.
+  // C tile (ct, t), lane (lg, lm), register j holds M[key][value] with
+  //   key   = 32 (t/2) + 8 lg + 4 (t%2) + j   (two row tiles form a natural 32-deep operand)
+  //   value = n0 + 8 (lm/4) + 4 ct + (lm%4)  (the lane's O^T values are 8 contiguous columns)
+  const int n0 = 32 * wave;  // first value column of this wave inside the block
+  f32x4 M[2][8];
+  const size_t sbase = ((size_t)n * H + h) * DK * dv + col0 + n0 + 8 * (lm >> 2) + (lm & 3);
+  {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          M[ct][t][j] = p.init_state
+                            ? p.init_state[sbase + 4 * ct + (size_t)(32 * (t >> 1) + 8 * lg + 4 * (t & 1) + j) * dv]
+                            : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) opaque(M[ct][t]);
+  }
+  __syncthreads();
+  __syncthreads();
+  const int H_ = H;
+  const size_t orow = (size_t)H_ * dv;  // elements between output rows
+  bf16 *olane = (bf16 *)p.o + ((size_t)tok0 * H_ + h) * dv + col0 + n0 + (size_t)lm * orow + 8 * lg;
+  // The state waves keep M_hat = M / Gam with a running scalar Gam (the product of the
+  // whole-chunk decays since the last renormalisation): the decay then costs one scalar
+  // multiply per chunk instead of one per state element.  Gam is folded into the row
+  // scalings of K M and Q M and into the write scale e^{g_C-g}/Gam; when Gam would drop
+  // below 2^-100 the state is renormalised (M_hat *= Gam) and that chunk decays eagerly.
+  float Gam = 1.f;
+  for (int c = 0; c < nchunks; ++c) {
       const char *Ks = KQ(c % 3), *Qs = KQ(c % 3) + C * DK * 2;
       const char *Vs = VB(c & 1);
       const char *pre = PRE(c & 1);
@@ -443,26 +493,28 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * i + lm, cA = 32 * s + 4 * lg;
-          const bf16x8 kf = cat44(lds_ld4(Ks, kq_off(r, cA)), lds_ld4(Ks, kq_off(r, cA + 16)));
-          const bf16x8 qf = cat44(lds_ld4(Qs, kq_off(r, cA)), lds_ld4(Qs, kq_off(r, cA + 16)));
+          const int r = 16 * i + lm, cA = 32 * s + 8 * lg;
+          const bf16x8 kf = *(const bf16x8 *)(Ks + kq_off(r, cA));
+          const bf16x8 qf = *(const bf16x8 *)(Qs + kq_off(r, cA));
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
             X[ct][i] = mma(kf, MB[ct][s], X[ct][i]);
             OT[ct][i] = mma(MB[ct][s], qf, OT[ct][i]);
           }
         }
-      // X <- beta (V - e^g X);  O^T columns (positions) scaled by e^g
+      // X <- V - Gam e^g X (beta is folded into T);  O^T columns (positions) scaled by Gam e^g
+      const float gam = vec[192];
+      const float Gn = Gam * gam;
+      const bool eager = (GATE == GATE_HEAD) && !(Gn >= 0x1p-100f);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 eg4 = *(const f32x4 *)(vec + 16 * i + 4 * lg);
-        const f32x4 be4 = *(const f32x4 *)(vec + 128 + 16 * i + 4 * lg);
-        const float egl = vec[16 * i + lm];
+        const f32x4 eg4 = *(const f32x4 *)(vec + 16 * i + 4 * lg) * Gam;
+        const float egl = vec[16 * i + lm] * Gam;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const bf16x4 v4 = tr16(Vs + v_off(16 * i + 4 * lg + (lm >> 2), n0 + 16 * ct + 4 * (lm & 3)));
+          const bf16x4 v4 = tr16(Vs + v_off(16 * i + 4 * lg + (lm >> 2), n0 + 8 * (lm & 3) + 4 * ct));
 #pragma unroll
-          for (int j = 0; j < 4; ++j) X[ct][i][j] = be4[j] * ((float)v4[j] - eg4[j] * X[ct][i][j]);
+          for (int j = 0; j < 4; ++j) X[ct][i][j] = (float)v4[j] - eg4[j] * X[ct][i][j];
           OT[ct][i] *= egl;
         }
       }
@@ -488,10 +540,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       }
       // O^T += Delta^T P^T ;  M <- e^{g_C} M + K^T diag(e^{g_C - g}) Delta
       bf16x8 DA[2][2], DT[2][2];
+      const float winv = eager ? 1.f : 1.f / Gn;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const f32x4 ec0 = *(const f32x4 *)(vec + 64 + 32 * s2 + 4 * lg);
-        const f32x4 ec1 = *(const f32x4 *)(vec + 64 + 32 * s2 + 16 + 4 * lg);
+        const f32x4 ec0 = *(const f32x4 *)(vec + 64 + 32 * s2 + 4 * lg) * winv;
+        const f32x4 ec1 = *(const f32x4 *)(vec + 64 + 32 * s2 + 16 + 4 * lg) * winv;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           DA[ct][s2] = frag_from_c<bf16>(D[ct][2 * s2], D[ct][2 * s2 + 1]);
@@ -508,41 +561,46 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) OT[ct][i] = mma(DA[ct][s2], pf, OT[ct][i]);
         }
-      const float gam = vec[192];
+      if (eager) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) M[ct][t] *= Gn;
+      }
+      Gam = eager ? 1.f : Gn;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) M[ct][t] *= gam;
-#pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const int rr = 32 * s2 + 4 * lg + (lm >> 2), cc = 16 * t + 4 * (lm & 3);
+          const int rr = 32 * s2 + 4 * lg + (lm >> 2), cc = 32 * (t >> 1) + 8 * (lm & 3) + 4 * (t & 1);
           const bf16x8 ktf = cat44(tr16(Ks + kq_off(rr, cc)), tr16(Ks + kq_off(rr + 16, cc)));
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) M[ct][t] = mma(ktf, DT[ct][s2], M[ct][t]);
         }
       }
-      // O rows -> HBM: lane holds O[16i+lm][n0 + 16ct + 4lg .. +3]
+      // O rows -> HBM: lane holds O[16i+lm][n0 + 8lg .. 8lg+7] (one 16-byte store)
       const int nv = min(C, len - c * C);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * i + lm;
-        if (row < nv) {
-          bf16 *dst = og + ((size_t)(c * C + row) * H_) * dv + 4 * lg;
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) *(bf16x4 *)(dst + 16 * ct) = to_bf4(OT[ct][i]);
-        }
+        if (row < nv)
+          *(bf16x8 *)(olane + (size_t)(c * C + 16 * i) * orow) = cat44(to_bf4(OT[0][i]), to_bf4(OT[1][i]));
       }
-    }
     __syncthreads();
   }
 
-  if (wave < 2 && p.final_state) {
+  if (p.final_state) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) M[ct][t] *= Gam;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p.final_state[sbase + 16 * ct + (size_t)(16 * t + 4 * lg + j) * dv] = M[ct][t][j];
+        for (int j = 0; j < 4; ++j)
+          p.final_state[sbase + 4 * ct + (size_t)(32 * (t >> 1) + 8 * lg + 4 * (t & 1) + j) * dv] = M[ct][t][j];
   }
 }
 
