@@ -183,26 +183,42 @@ __device__ __forceinline__ float gate_vectors(const char *bl, char *gs, int lane
   return g;
 }
 
-// Gamma-weighted tile entries for tile (a, b), row r = 16a + lm, columns i = 16b + 4lg + j.
-// Returns the mask/decay factor per j (0 where i > r, or i >= r when strict).
+// The Gamma factors one lane needs for its tiles, read from LDS once per chunk:
+// rows r = 16a + lm (a = 0..3) and column groups 16b + 4lg .. +3 (b = 0..3).
+struct GammaRegs {
+  float eh[4], be[4];  // Ehead[16a+lm], beta[16a+lm]
+  f32x4 et[4], ehi[4]; // Etail / Ehinv[16b+4lg ..+3]
+  float f[4][4];       // F[a][b], a > b
+};
+template <int GATE>
+__device__ __forceinline__ void load_gamma(GammaRegs &G, const char *gs, int lm, int lg) {
+  const float *Eh = (const float *)gs, *Ehi = Eh + 64, *Et = Eh + 128, *bs = Eh + 192, *F = Eh + 256;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    G.eh[a] = Eh[16 * a + lm];
+    G.be[a] = bs[16 * a + lm];
+    G.et[a] = *(const f32x4 *)(Et + 16 * a + 4 * lg);
+    G.ehi[a] = *(const f32x4 *)(Ehi + 16 * a + 4 * lg);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) G.f[a][b] = (a > b) ? F[4 * a + b] : 0.f;
+  }
+}
+// Gamma (times the causal mask) for tile (a, b): row r = 16a + lm, columns
+// i = 16b + 4lg + j.  Across blocks Gamma = Ehead[r] F[a][b] Etail[i]; within a block
+// Gamma = Ehead[r] Ehinv[i]; masked entries are 0 (i > r, or i >= r when strict).
 template <int GATE, bool STRICT>
-__device__ __forceinline__ f32x4 gamma_row(const char *gs, int a, int b, int lm, int lg) {
-  const float *Eh = (const float *)gs, *Ehi = Eh + 64, *Et = Eh + 128, *F = Eh + 256;
-  const int r = 16 * a + lm;
+__device__ __forceinline__ f32x4 gamma_tile(const GammaRegs &G, int a, int b, int lm, int lg) {
   f32x4 out;
   if (a > b) {
-    const float h = Eh[r] * F[4 * a + b];
-    const f32x4 et = *(const f32x4 *)(Et + 16 * b + 4 * lg);
+    const float h = G.eh[a] * G.f[a][b];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = (GATE == GATE_NONE) ? 1.f : h * et[j];
+    for (int j = 0; j < 4; ++j) out[j] = (GATE == GATE_NONE) ? 1.f : h * G.et[b][j];
   } else {
-    const float h = Eh[r];
-    const f32x4 ehi = *(const f32x4 *)(Ehi + 16 * b + 4 * lg);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i = 16 * b + 4 * lg + j;
-      const bool keep = STRICT ? (i < r) : (i <= r);
-      out[j] = keep ? ((GATE == GATE_NONE) ? 1.f : h * ehi[j]) : 0.f;
+      const int i = 4 * lg + j;
+      const bool keep = STRICT ? (i < lm) : (i <= lm);
+      out[j] = keep ? ((GATE == GATE_NONE) ? 1.f : G.eh[a] * G.ehi[b][j]) : 0.f;
     }
   }
   return out;
@@ -290,6 +306,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int s = 0; s < 4; ++s) kf[b][s] = *(const bf16x8 *)(Ks + kq_off(16 * b + lm, 32 * s + 8 * lg));
+    GammaRegs G;
+    load_gamma<GATE>(G, gs, lm, lg);
     if (wave == 3) {
       // decay vectors for the state waves
       float *vec = (float *)(pre + PRE_VEC);
@@ -301,22 +319,22 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       // P = lower-inclusive(Q K^T * Gamma): tile (a, b) computed as K_b Q_a^T so the
       // lane holds row 16a+lm, columns 16b+4lg..+3 (the A-operand fragment layout);
       // the ten accumulation chains are interleaved
+      bf16x8 qf[4][4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[a][s] = *(const bf16x8 *)(Qs + kq_off(16 * a + lm, 32 * s + 8 * lg));
       f32x4 acc[10];
 #pragma unroll
       for (int t = 0; t < 10; ++t) acc[t] = zero4();
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 qf[4];
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) qf[a] = *(const bf16x8 *)(Qs + kq_off(16 * a + lm, 32 * s + 8 * lg));
-#pragma unroll
-        for (int t = 0; t < 10; ++t) acc[t] = mma(kf[TB[t]][s], qf[TA[t]], acc[t]);
-      }
+        for (int t = 0; t < 10; ++t) acc[t] = mma(kf[TB[t]][s], qf[TA[t]][s], acc[t]);
 #pragma unroll
       for (int t = 0; t < 10; ++t) {
         const int a = TA[t], b = TB[t];
-        const f32x4 gm = gamma_row<GATE, false>(gs, a, b, lm, lg);
-        *(bf16x4 *)(pre + PRE_P + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(acc[t] * gm);
+        *(bf16x4 *)(pre + PRE_P + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(acc[t] * gamma_tile<GATE, false>(G, a, b, lm, lg));
       }
     } else {
       // A = strictly lower(beta_r K K^T * Gamma): tile (a, b) computed as K_b K_a^T
@@ -328,16 +346,25 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int t = 0; t < 10; ++t) acc[t] = mma(kf[TB[t]][s], kf[TA[t]][s], acc[t]);
-      const float *bsa = (const float *)gs + 192;
+      // diagonal tiles first (they feed the substitution), then the off-diagonal ones
 #pragma unroll
       for (int t = 0; t < 10; ++t) {
         const int a = TA[t], b = TB[t];
-        const f32x4 av = acc[t] * gamma_row<GATE, true>(gs, a, b, lm, lg) * bsa[16 * a + lm];
         if (a == b)
-          *(f32x4 *)(AD + ((16 * a + lm) * 16 + 4 * lg) * 4) = av;
-        else
-          *(bf16x4 *)(AO + (ao_idx(a, b) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) = to_bf4(av);
+          *(f32x4 *)(AD + ((16 * a + lm) * 16 + 4 * lg) * 4) = acc[t] * gamma_tile<GATE, true>(G, a, b, lm, lg) * G.be[a];
       }
+#pragma unroll
+      for (int t = 0; t < 10; ++t) {
+        const int a = TA[t], b = TB[t];
+        if (a != b)
+          *(bf16x4 *)(AO + (ao_idx(a, b) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) =
+              to_bf4(acc[t] * gamma_tile<GATE, true>(G, a, b, lm, lg) * G.be[a]);
+      }
+      // operands of the off-diagonal recursion, read before the substitution so their
+      // latency overlaps it: A[a][k] half-fragments (row lm, columns 4lg..+3)
+      bf16x4 aof[6];
+#pragma unroll
+      for (int q = 0; q < 6; ++q) aof[q] = lds_ld4(AO, (q * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2);
       // diagonal 16x16 blocks of T = (I + A)^-1: lane (lg, lm) owns row lm of block lg;
       // t_r = e_r - sum_{i<r} A[r][i] t_i with rows broadcast along the 16-lane DPP row
       float nar[16], t[16];
@@ -392,8 +419,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
             const bool in0 = (k0 >= b && k0 < a), in1 = (k0 + 1 >= b && k0 + 1 < a);
             if (in0 || in1) {
               const bf16x4 z4 = {};
-              const bf16x4 a0 = in0 ? lds_ld4(AO, (ao_idx(a, k0) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) : z4;
-              const bf16x4 a1 = in1 ? lds_ld4(AO, (ao_idx(a, k0 + 1) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) : z4;
+              const bf16x4 a0 = in0 ? aof[ao_idx(a, k0)] : z4;
+              const bf16x4 a1 = in1 ? aof[ao_idx(a, k0 + 1)] : z4;
               const bf16x8 bfr = frag_from_c<bf16>(in0 ? Tc[k0][b] : zero4(), in1 ? Tc[k0 + 1][b] : zero4());
               y = mma(cat44(a0, a1), bfr, y);
             }
@@ -478,6 +505,32 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       const char *Vs = VB(c & 1);
       const char *pre = PRE(c & 1);
       const float *vec = (const float *)(pre + PRE_VEC);
+      // ---- issue every LDS read of this chunk's later stages up front, so their
+      // latency hides behind the K M / M^T Q^T products: K^T fragments for the state
+      // update (transposing reads), T and P fragments, V in C layout
+      bf16x8 ktf[8][2];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int rr = 32 * s2 + 4 * lg + (lm >> 2), cc = 32 * (t >> 1) + 8 * (lm & 3) + 4 * (t & 1);
+          ktf[t][s2] = cat44(tr16(Ks + kq_off(rr, cc)), tr16(Ks + kq_off(rr + 16, cc)));
+        }
+      bf16x8 tf[4][2], pf[4][2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 2 * s2; i < 4; ++i) {
+          const int r = 16 * i + lm, cA = 32 * s2 + 4 * lg;
+          tf[i][s2] = cat44(lds_ld4(pre, tp_off(r, cA)), lds_ld4(pre, tp_off(r, cA + 16)));
+          pf[i][s2] = cat44(lds_ld4(pre + PRE_P, tp_off(r, cA)), lds_ld4(pre + PRE_P, tp_off(r, cA + 16)));
+        }
+      bf16x4 vv[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          vv[i][ct] = tr16(Vs + v_off(16 * i + 4 * lg + (lm >> 2), n0 + 8 * (lm & 3) + 4 * ct));
       // state as operands: the same fragments serve as B (for K M) and A (for M^T Q^T)
       bf16x8 MB[2][4];
 #pragma unroll
@@ -512,9 +565,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
         const float egl = vec[16 * i + lm] * Gam;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const bf16x4 v4 = tr16(Vs + v_off(16 * i + 4 * lg + (lm >> 2), n0 + 8 * (lm & 3) + 4 * ct));
 #pragma unroll
-          for (int j = 0; j < 4; ++j) X[ct][i][j] = (float)v4[j] - eg4[j] * X[ct][i][j];
+          for (int j = 0; j < 4; ++j) X[ct][i][j] = (float)vv[i][ct][j] - eg4[j] * X[ct][i][j];
           OT[ct][i] *= egl;
         }
       }
@@ -531,11 +583,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
         for (int ct = 0; ct < 2; ++ct) XB[ct] = frag_from_c<bf16>(X[ct][2 * s2], X[ct][2 * s2 + 1]);
 #pragma unroll
         for (int i = 2 * s2; i < 4; ++i) {
-          const int r = 16 * i + lm, cA = 32 * s2 + 4 * lg;
-          const char *Tm = pre;
-          const bf16x8 tf = cat44(lds_ld4(Tm, tp_off(r, cA)), lds_ld4(Tm, tp_off(r, cA + 16)));
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) D[ct][i] = mma(tf, XB[ct], D[ct][i]);
+          for (int ct = 0; ct < 2; ++ct) D[ct][i] = mma(tf[i][s2], XB[ct], D[ct][i]);
         }
       }
       // O^T += Delta^T P^T ;  M <- e^{g_C} M + K^T diag(e^{g_C - g}) Delta
@@ -555,11 +604,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int i = 2 * s2; i < 4; ++i) {
-          const int r = 16 * i + lm, cA = 32 * s2 + 4 * lg;
-          const char *Pm = pre + PRE_P;
-          const bf16x8 pf = cat44(lds_ld4(Pm, tp_off(r, cA)), lds_ld4(Pm, tp_off(r, cA + 16)));
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) OT[ct][i] = mma(DA[ct][s2], pf, OT[ct][i]);
+          for (int ct = 0; ct < 2; ++ct) OT[ct][i] = mma(DA[ct][s2], pf[i][s2], OT[ct][i]);
         }
       if (eager) {
 #pragma unroll
@@ -571,12 +617,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int rr = 32 * s2 + 4 * lg + (lm >> 2), cc = 32 * (t >> 1) + 8 * (lm & 3) + 4 * (t & 1);
-          const bf16x8 ktf = cat44(tr16(Ks + kq_off(rr, cc)), tr16(Ks + kq_off(rr + 16, cc)));
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) M[ct][t] = mma(ktf, DT[ct][s2], M[ct][t]);
-        }
+          for (int ct = 0; ct < 2; ++ct) M[ct][t] = mma(ktf[t][s2], DT[ct][s2], M[ct][t]);
       }
       // O rows -> HBM: lane holds O[16i+lm][n0 + 8lg .. 8lg+7] (one 16-byte store)
       const int nv = min(C, len - c * C);
