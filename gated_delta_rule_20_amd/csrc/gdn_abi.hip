@@ -30,7 +30,6 @@ int check_fwd(const gdn_fwd_args *a) {
   if (a->chunk != 64) return GDN_ERR_UNSUPPORTED;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   if (a->dtype == GDN_F32 && a->d_k != 64) return GDN_ERR_UNSUPPORTED;
-  if (a->gate == GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
   if (a->cu_seqlens) {
     if (a->B != 1 || a->N < 1) return GDN_ERR_INVALID_ARG;
   } else if (a->N != a->B) {
@@ -44,7 +43,8 @@ int check_fwd(const gdn_fwd_args *a) {
   const void *p16[] = {a->q, a->k, a->v, a->o, a->initial_state, a->final_state};
   for (const void *p : p16)
     if (p && !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
-  if ((a->beta && !aligned(a->beta, 4)) || (a->log_alpha && !aligned(a->log_alpha, 4)) ||
+  const size_t la_align = a->gate == GDN_GATE_KEY ? 16 : 4;
+  if ((a->beta && !aligned(a->beta, 4)) || (a->log_alpha && !aligned(a->log_alpha, la_align)) ||
       (a->cu_seqlens && !aligned(a->cu_seqlens, 4)))
     return GDN_ERR_INVALID_ARG;
   return GDN_OK;

@@ -12,6 +12,12 @@
 //   M_C   = e^{g_C} M0 + K^T diag(e^{g_C - g}) Delta                         (state)
 // The strict mask makes a token's write blind to itself; the inclusive mask lets
 // the read at t see the write at t.
+// With one decay per key channel (sec. 3, the per-channel gate of the diagonal
+// family) every exp(g_r - g_i) is per channel and moves inside the contractions:
+// K and Q rows carry e^{g_r}, K^T carries e^{g_C - g_i}, the state rows decay by
+// e^{g_C} and the pairwise factor of the Gram tiles is split at a reference row in
+// the middle of each 16-row block (exp(g_r - m) * exp(m - g_i)), so that no single
+// factor exceeds the decay accumulated over eight tokens.
 //
 // Mapping onto gfx950 (one workgroup = one (sequence, head, d_v block), 4 waves):
 //  * The workgroup walks its sequence chunk by chunk.  The fp32 state never leaves
@@ -54,7 +60,7 @@ __device__ __forceinline__ void st_pack(E *dst, const E (&v)[R]) {
   *(T *)dst = u.t;
 }
 
-template <typename E, int DK, int DVB>
+template <typename E, int DK, int DVB, bool KG>
 struct Cfg {
   static constexpr int ES = sizeof(E);
   static constexpr int VEC = 16 / ES;       // elements per 16-byte access
@@ -68,6 +74,9 @@ struct Cfg {
   static constexpr int NWS = DVB / 16;      // waves holding state columns
   static constexpr int KB = DK / 32;        // 32-deep blocks over d_k
   static constexpr int MT = DK / 16;        // 16-row tiles of the state
+  static constexpr int SG = DK + 4;         // row stride of the per-channel log-decay tile
+  static constexpr int CHG = DK / 4;        // 16-byte chunks per log-decay row
+  static constexpr int RPTG = KG ? C * CHG / NT : 1;  // log-decay rows per loader thread
   static constexpr int OFF_K = 0;
   static constexpr int OFF_Q = OFF_K + C * SK * ES;
   static constexpr int OFF_KT = OFF_Q + C * SK * ES;
@@ -78,8 +87,10 @@ struct Cfg {
   static constexpr int OFF_O = OFF_A + C * ST * ES;
   static constexpr int OFF_AD = OFF_O + C * SO * ES;
   static constexpr int OFF_VEC = OFF_AD + 4 * 16 * 16 * 4;
-  static constexpr int BYTES = OFF_VEC + (5 * C + 8) * 4;
+  static constexpr int OFF_G = OFF_VEC + (5 * C + 8) * 4;  // per-channel gate: g [C][SG], e^{g_C} [DK]
+  static constexpr int BYTES = OFF_G + (KG ? (C * SG + DK) * 4 : 0);
   static_assert(RPT >= 1 && C * CH == RPT * NT, "K loader geometry");
+  static_assert(!KG || C * CHG == RPTG * NT, "log-decay loader geometry");
   static_assert(RPTV >= 1 && C * CHV == RPTV * NT, "V loader geometry");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
@@ -92,9 +103,10 @@ constexpr int GT_W[10] = {0, 0, 0, 1, 1, 1, 2, 2, 3, 3};
 
 template <typename E, int DK, int DVB, int GATE>
 __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
-  typedef Cfg<E, DK, DVB> CF;
+  constexpr bool KG = GATE == GATE_KEY;
+  typedef Cfg<E, DK, DVB, KG> CF;
   typedef typename Frag<E>::type F;
-  constexpr int SK = CF::SK, ST = CF::ST, SO = CF::SO, VEC = CF::VEC;
+  constexpr int SK = CF::SK, ST = CF::ST, SO = CF::SO, VEC = CF::VEC, SG = CF::SG;
   __shared__ __align__(16) char smem[CF::BYTES];
   E *Ks = (E *)(smem + CF::OFF_K);
   E *Qs = (E *)(smem + CF::OFF_Q);
@@ -111,6 +123,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   float *egs = gs + C;
   float *egcs = egs + C;
   float *misc = egcs + C;
+  float *Gs = (float *)(smem + CF::OFF_G);  // KEY: chunk-local log-decay prefix per channel
+  float *egck = Gs + C * SG;                 // KEY: e^{g_C} per channel
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
@@ -153,6 +167,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   E *ob = (E *)p.o + ((size_t)tok0 * H + h) * dv + col0;
   const float *bb = p.beta + (size_t)tok0 * H + h;
   const float *lab = (GATE == GATE_HEAD) ? p.log_alpha + (size_t)tok0 * H + h : nullptr;
+  const float *lak = KG ? p.log_alpha + ((size_t)tok0 * H + h) * DK : nullptr;
 
   // ---- state: wave w < NWS owns value columns col0 + 16w .. +15 (C-tile layout)
   const bool sw = wave < CF::NWS;
@@ -174,7 +189,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   // ---- loader: chunk tiles -> registers -> LDS
   const int cc = tid % CF::CH, rg = tid / CF::CH;
   const int cv = tid % CF::CHV, rgv = tid / CF::CHV;
-  u32x4 rk[CF::RPT], rq[CF::RPT], rv[CF::RPTV];
+  const int cg = tid % CF::CHG, rgg = tid / CF::CHG;
+  u32x4 rk[CF::RPT], rq[CF::RPT], rv[CF::RPTV], rg4[CF::RPTG];
   float rbeta = 0.f, rla = 0.f;
   // Loads are unconditional (rows past the sequence end re-read its last row) so
   // that no branch ties the unpacking of a prefetched tile to its load; rows past
@@ -195,6 +211,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
     }
     if (tid < C) rbeta = bb[(size_t)(base + min(tid, last)) * H];
     if (GATE == GATE_HEAD && tid >= C && tid < 2 * C) rla = lab[(size_t)(base + min(tid - C, last)) * H];
+    if (KG) {
+#pragma unroll
+      for (int u = 0; u < CF::RPTG; ++u) {
+        const int row = min(rgg * CF::RPTG + u, last);
+        rg4[u] = *(const u32x4 *)(lak + (size_t)(base + row) * H * DK + cg * 4);
+      }
+    }
   };
   auto lstore = [&](int nv) {
     // the prefetched registers are consumed only from here on
@@ -208,6 +231,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
     for (int u = 0; u < CF::RPTV; ++u) {
       opaque(rv[u]);
       if (rgv * CF::RPTV + u >= nv) rv[u] = (u32x4){0u, 0u, 0u, 0u};
+    }
+    if (KG) {
+#pragma unroll
+      for (int u = 0; u < CF::RPTG; ++u) {
+        opaque(rg4[u]);
+        const int row = rgg * CF::RPTG + u;
+        if (row >= nv) rg4[u] = (u32x4){0u, 0u, 0u, 0u};  // log alpha = 0: identity decay
+        *(u32x4 *)(Gs + row * SG + cg * 4) = rg4[u];
+      }
     }
     opaque(rbeta);
     opaque(rla);
@@ -262,6 +294,19 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       egcs[lane] = __expf(gC - g);
       if (lane == 0) misc[0] = __expf(gC);
     }
+    if (KG && tid < DK) {
+      // per channel: inclusive prefix over the chunk's rows, in place
+      float x[C];
+#pragma unroll
+      for (int r = 0; r < C; ++r) x[r] = Gs[r * SG + tid];
+      float g = 0.f;
+#pragma unroll
+      for (int r = 0; r < C; ++r) {
+        g += x[r];
+        Gs[r * SG + tid] = g;
+      }
+      egck[tid] = __expf(g);
+    }
     __syncthreads();
 
     // (2) Gram tiles -> A (strictly lower, beta- and decay-weighted) and P
@@ -272,9 +317,22 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       f32x4 kk = zero4(), qk = zero4();
 #pragma unroll
       for (int s = 0; s < CF::KB; ++s) {
-        const F bk = ld8(Ks + (16 * b + lm) * SK + 32 * s + 8 * lg);
-        const F ak = ld8(Ks + (16 * a + lm) * SK + 32 * s + 8 * lg);
-        const F aq = ld8(Qs + (16 * a + lm) * SK + 32 * s + 8 * lg);
+        F bk = ld8(Ks + (16 * b + lm) * SK + 32 * s + 8 * lg);
+        F ak = ld8(Ks + (16 * a + lm) * SK + 32 * s + 8 * lg);
+        F aq = ld8(Qs + (16 * a + lm) * SK + 32 * s + 8 * lg);
+        if (KG) {
+          // exp(g_r - g_i) per channel = exp(g_r - m_a) * exp(m_a - g_i), m_a = g at row 16a+7
+          const float *gr = Gs + (16 * a + lm) * SG + 32 * s + 8 * lg;
+          const float *gi = Gs + (16 * b + lm) * SG + 32 * s + 8 * lg;
+          const float *gm = Gs + (16 * a + 7) * SG + 32 * s + 8 * lg;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float ea = __expf(gr[j] - gm[j]), eb = __expf(gm[j] - gi[j]);
+            ak[j] = to_e<E>(to_f(ak[j]) * ea);
+            aq[j] = to_e<E>(to_f(aq[j]) * ea);
+            bk[j] = to_e<E>(to_f(bk[j]) * eb);
+          }
+        }
         kk = mma(ak, bk, kk);
         qk = mma(aq, bk, qk);
       }
@@ -309,6 +367,29 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) Ts[(16 * lg + r) * ST + 16 * lg + lm] = to_e<E>(x[r]);
+    } else if (KG) {
+      // per-channel decay folded into the state-phase operands (waves 1-3, while
+      // wave 0 solves): K, Q rows times e^{g_r}; K^T entries times e^{g_C - g_i}
+      const int t3 = tid - 64;
+      for (int idx = t3; idx < C * CF::CHG; idx += NT - 64) {
+        const int r = idx / CF::CHG, c4 = (idx % CF::CHG) * 4;
+        const f32x4 g = *(const f32x4 *)(Gs + r * SG + c4);
+        E *kp = Ks + r * SK + c4;
+        E *qp = Qs + r * SK + c4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float e = __expf(g[j]);
+          kp[j] = to_e<E>(to_f(kp[j]) * e);
+          qp[j] = to_e<E>(to_f(qp[j]) * e);
+        }
+      }
+      for (int idx = t3; idx < DK * (C / 4); idx += NT - 64) {
+        const int ch = idx / (C / 4), i4 = (idx % (C / 4)) * 4;
+        const float gc = Gs[(C - 1) * SG + ch];
+        E *kt = KTs + ch * ST + i4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kt[j] = to_e<E>(to_f(kt[j]) * __expf(gc - Gs[(i4 + j) * SG + ch]));
+      }
     }
     __syncthreads();
 
@@ -407,6 +488,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
 #pragma unroll
       for (int t = 0; t < CF::MT; ++t) {
         if (GATE == GATE_HEAD) M[t] *= gam;
+        if (KG)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) M[t][j] *= egck[16 * t + 4 * lg + j];
         const E *kt = KTs + (16 * t + lm) * ST + 4 * lg;
         M[t] = mma(ld4x2(kt, kt + 16), DT0, M[t]);
         M[t] = mma(ld4x2(kt + 32, kt + 48), DT1, M[t]);
@@ -463,6 +547,7 @@ hipError_t launch_g(const FwdParams &p, int gate, hipStream_t stream) {
   switch (gate) {
     case GATE_NONE: return launch_t<E, DK, DVB, GATE_NONE>(p, stream);
     case GATE_HEAD: return launch_t<E, DK, DVB, GATE_HEAD>(p, stream);
+    case GATE_KEY: return launch_t<E, DK, DVB, GATE_KEY>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

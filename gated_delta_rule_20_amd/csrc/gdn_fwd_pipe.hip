@@ -139,11 +139,11 @@ __device__ __forceinline__ void load_bl(const Res &rs, char *dst, int chunk, int
 }
 
 // ---- producers: decay prefix and the per-position factors of Gamma.
-// Ehead[r] = e^{g_r - g_{s-1}}, Ehinv[r] = e^{g_{s-1} - g_r}, Etail[r] = e^{g_e - g_r}
-// where s-1 / e are the positions before / at the end of r's 16-block (g_{-1} = 0);
-// F[a][b] = e^{g_{16a-1} - g_{16b+15}} (a > b).  Then Gamma[r,i] = Ehead[r] F Etail[i]
-// across blocks and Ehead[r] Ehinv[i] within a block; every factor except Ehinv is
-// <= 1 and Ehinv spans one block only.  Returns g (this lane's position).
+// Ehead[r] = e^{g_r - g_m}, Ehinv[r] = e^{g_m - g_r}, Etail[r] = e^{g_e - g_r}
+// where m / e are row 7 / the last row of r's 16-block;
+// F[a][b] = e^{g_{16a+7} - g_{16b+15}} (a > b).  Then Gamma[r,i] = Ehead[r] F Etail[i]
+// across blocks and Ehead[r] Ehinv[i] within a block; F and Etail are <= 1, Ehead
+// and Ehinv at most the decay over eight tokens.  Returns g (this lane's position).
 template <int GATE>
 __device__ __forceinline__ float gate_vectors(const char *bl, char *gs, int lane, float &beta_out) {
   const float beta = ((const float *)bl)[lane];
@@ -170,14 +170,18 @@ __device__ __forceinline__ float gate_vectors(const char *bl, char *gs, int lane
   g += gprev;
   const float gE3 = readlane(g, 63);
   const float gend = blk == 0 ? gE0 : blk == 1 ? gE1 : blk == 2 ? gE2 : gE3;
-  Eh[lane] = __expf(g - gprev);
-  Ehi[lane] = __expf(gprev - g);
+  // reference point of each 16-row block: its row 7, so that neither Ehead nor
+  // Ehinv exceeds the decay accumulated over eight tokens
+  const float m0 = readlane(g, 7), m1 = readlane(g, 23), m2 = readlane(g, 39), m3 = readlane(g, 55);
+  const float gmid = blk == 0 ? m0 : blk == 1 ? m1 : blk == 2 ? m2 : m3;
+  Eh[lane] = __expf(g - gmid);
+  Ehi[lane] = __expf(gmid - g);
   Et[lane] = __expf(gend - g);
-  // F[a*4+b] for a > b
+  // F[a*4+b] = exp(g_{16a+7} - g_{16b+15}) for a > b
   if (lane < 16) {
     const int a = lane >> 2, b = lane & 3;
-    const float ga = a == 1 ? gE0 : a == 2 ? gE1 : gE2;  // g_{16a-1}
-    const float gb = b == 0 ? gE0 : b == 1 ? gE1 : gE2;  // g_{16b+15}
+    const float ga = a == 1 ? m1 : a == 2 ? m2 : m3;
+    const float gb = b == 0 ? gE0 : b == 1 ? gE1 : gE2;
     F[lane] = (a > b) ? __expf(ga - gb) : 0.f;
   }
   return g;

@@ -58,7 +58,7 @@ def check(gdn, inp, tol=None):
 
 # ---------------------------------------------------------------- small shapes
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
-@pytest.mark.parametrize("gate", ["none", "head"])
+@pytest.mark.parametrize("gate", ["none", "head", "key"])
 def test_bf16_ragged_lengths(gdn, T, gate):
     inp = synth.random_inputs(2, T, 3, 128, 128, gate, "bf16", seed=T, state_std=0.05)
     check(gdn, inp)
@@ -66,29 +66,43 @@ def test_bf16_ragged_lengths(gdn, T, gate):
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("with_state", [False, True])
-def test_bf16_head_dims(gdn, dk, dv, with_state):
-    inp = synth.random_inputs(2, 130, 2, dk, dv, "head", "bf16", seed=dk + dv,
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_bf16_head_dims(gdn, dk, dv, with_state, gate):
+    inp = synth.random_inputs(2, 130, 2, dk, dv, gate, "bf16", seed=dk + dv,
                               state_std=0.05 if with_state else None)
     check(gdn, inp)
 
 
 @pytest.mark.parametrize("dv", [64, 128])
-@pytest.mark.parametrize("gate", ["none", "head"])
+@pytest.mark.parametrize("gate", ["none", "head", "key"])
 def test_fp32_mode(gdn, dv, gate):
     inp = synth.random_inputs(2, 190, 2, 64, dv, gate, "f32", seed=dv, state_std=0.1)
     check(gdn, inp)
 
 
-def test_varlen_small(gdn):
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_varlen_small(gdn, gate):
     lengths = [1, 64, 65, 130, 7, 0, 300]
-    inp = synth.random_inputs(1, None, 2, 128, 128, "head", "bf16", seed=3, state_std=0.05,
+    inp = synth.random_inputs(1, None, 2, 128, 128, gate, "bf16", seed=3, state_std=0.05,
                               lengths=lengths)
     check(gdn, inp)
 
 
-def test_varlen_equals_separate_runs(gdn):
+@pytest.mark.parametrize("gate", ["head", "key"])
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_strong_decay(gdn, gate, dtype, dk):
+    """Log decay of -5 per token (-320 per chunk): the per-position factors of every
+    decay product must stay finite and the result match the recurrence."""
+    inp = synth.random_inputs(2, 200, 2, dk, 128, gate, dtype, seed=21, state_std=0.05)
+    la = inp["log_alpha"]
+    inp["log_alpha"] = torch.full_like(la, -5.0) + 0.5 * torch.rand(la.shape, generator=torch.Generator().manual_seed(2))
+    check(gdn, inp)
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_varlen_equals_separate_runs(gdn, gate):
     lengths = [70, 5, 129]
-    inp = synth.random_inputs(1, None, 2, 128, 128, "head", "bf16", seed=8, state_std=0.05,
+    inp = synth.random_inputs(1, None, 2, 128, 128, gate, "bf16", seed=8, state_std=0.05,
                               lengths=lengths)
     o, fs = run_gpu(gdn, inp)
     cu = inp["cu_seqlens"].tolist()
@@ -113,12 +127,14 @@ def test_replace_invariant_gpu(gdn):
     assert relerr(o, v) <= 2e-2
 
 
-def test_beta_zero_keeps_decayed_state(gdn):
-    inp = synth.random_inputs(2, 100, 2, 128, 128, "head", "bf16", seed=6, state_std=0.1)
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_beta_zero_keeps_decayed_state(gdn, gate):
+    inp = synth.random_inputs(2, 100, 2, 128, 128, gate, "bf16", seed=6, state_std=0.1)
     inp["beta"] = torch.zeros_like(inp["beta"])
     o, fs = run_gpu(gdn, inp)
-    d = torch.exp(inp["log_alpha"].double().sum(dim=1))  # [B, H]
-    expect = d[:, :, None, None] * inp["initial_state"].double()
+    d = torch.exp(inp["log_alpha"].double().sum(dim=1))  # [B, H] or [B, H, d_k]
+    d = d[:, :, None, None] if gate == "head" else d[:, :, :, None]
+    expect = d * inp["initial_state"].double()
     assert relerr(fs, expect.numpy()) <= 1e-5
 
 
@@ -155,6 +171,10 @@ def test_workload_gdn_bf16_B4(gdn):
 
 def test_workload_gdn_350m(gdn):
     check(gdn, synth.workload_inputs("gdn-350m-bf16-B16-T2048-H8-d128"))
+
+
+def test_workload_kda_long(gdn):
+    check(gdn, synth.workload_inputs("kda-bf16-B2-T16384-H16-d128"))
 
 
 def test_workload_varlen_sampled(gdn):
