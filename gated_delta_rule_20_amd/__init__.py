@@ -100,6 +100,87 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _require(cond, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _same_device(tensors, ref):
+    for name, t in tensors:
+        if t is not None:
+            _require(t.is_cuda and t.device == ref.device,
+                      "%s must be on the GPU device of q (%s), got %s" % (name, ref.device, t.device))
+
+
+def check_fwd_tensors(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None,
+                      out=None, final_state=None):
+    """Host-side shape, dtype and layout checks for fwd_chunked.
+
+    The C ABI receives bare pointers and sizes, so the shapes it is told must be
+    the shapes of the buffers; this raises ValueError on any mismatch before a
+    pointer is handed over.  Device placement is checked last."""
+    import torch
+    named = [("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
+             ("initial_state", initial_state), ("cu_seqlens", cu_seqlens), ("out", out),
+             ("final_state", final_state)]
+    _require(q.dim() == 4, "q must be [B, T, H, d_k], got shape %s" % (tuple(q.shape),))
+    B, T, H, dk = q.shape
+    _require(q.dtype in (torch.bfloat16, torch.float32), "q must be bfloat16 or float32")
+    _require(tuple(k.shape) == (B, T, H, dk), "k must have the shape of q")
+    _require(v.dim() == 4 and tuple(v.shape[:3]) == (B, T, H), "v must be [B, T, H, d_v]")
+    dv = v.shape[3]
+    _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share one dtype")
+    _require(tuple(beta.shape) == (B, T, H) and beta.dtype == torch.float32,
+             "beta must be float32 [B, T, H]")
+    if log_alpha is not None:
+        _require(log_alpha.dtype == torch.float32, "log_alpha must be float32")
+        _require(tuple(log_alpha.shape) in ((B, T, H), (B, T, H, dk)),
+                 "log_alpha must be [B, T, H] (one decay per head) or [B, T, H, d_k]")
+    if cu_seqlens is not None:
+        _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2,
+                 "cu_seqlens must be int32 [N + 1] with N >= 1")
+        _require(B == 1, "packed sequences (cu_seqlens) need B == 1")
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None:
+            _require(tuple(t.shape) == (N, H, dk, dv) and t.dtype == torch.float32,
+                     "%s must be float32 [N, H, d_k, d_v] = %s" % (name, (N, H, dk, dv)))
+    if out is not None:
+        _require(tuple(out.shape) == (B, T, H, dv) and out.dtype == q.dtype,
+                 "out must be [B, T, H, d_v] in the dtype of q")
+    for name, t in named:
+        if t is not None:
+            _require(t.is_contiguous(), "%s must be contiguous" % name)
+    _same_device(named, q)
+    return N
+
+
+def check_step_tensors(q, k, v, beta, log_alpha, state, out=None):
+    """Host-side checks for recurrent_step (see check_fwd_tensors)."""
+    import torch
+    named = [("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
+             ("state", state), ("out", out)]
+    _require(q.dim() == 3, "q must be [N, H, d_k]")
+    N, H, dk = q.shape
+    _require(q.dtype in (torch.bfloat16, torch.float32), "q must be bfloat16 or float32")
+    _require(tuple(k.shape) == (N, H, dk), "k must have the shape of q")
+    _require(v.dim() == 3 and tuple(v.shape[:2]) == (N, H), "v must be [N, H, d_v]")
+    dv = v.shape[2]
+    _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share one dtype")
+    _require(tuple(beta.shape) == (N, H) and beta.dtype == torch.float32, "beta must be float32 [N, H]")
+    if log_alpha is not None:
+        _require(log_alpha.dtype == torch.float32 and tuple(log_alpha.shape) in ((N, H), (N, H, dk)),
+                 "log_alpha must be float32 [N, H] or [N, H, d_k]")
+    _require(tuple(state.shape) == (N, H, dk, dv) and state.dtype == torch.float32,
+             "state must be float32 [N, H, d_k, d_v]")
+    if out is not None:
+        _require(tuple(out.shape) == (N, H, dv) and out.dtype == q.dtype, "out must be [N, H, d_v]")
+    for name, t in named:
+        if t is not None:
+            _require(t.is_contiguous(), "%s must be contiguous" % name)
+    _same_device(named, q)
+
+
 def gate_code(log_alpha, token_ndim: int) -> int:
     if log_alpha is None:
         return GDN_GATE_NONE
@@ -134,9 +215,10 @@ def fwd_chunked(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=No
     current (or given) stream.
     """
     import torch
+    N = check_fwd_tensors(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out,
+                          final_state if output_final_state else None)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     if output_final_state and final_state is None:
@@ -159,6 +241,7 @@ def recurrent_step(q, k, v, beta, log_alpha, state, out=None, stream=None):
     [N,H,d_k]; state [N,H,d_k,d_v] fp32, updated in place.  Returns o [N,H,d_v].
     """
     import torch
+    check_step_tensors(q, k, v, beta, log_alpha, state, out)
     N, H, dk = q.shape
     dv = v.shape[-1]
     if out is None:

@@ -1,0 +1,181 @@
+"""Host side of the C ABI, no GPU needed.
+
+The library loads, exports every function include/gdn.h declares, and rejects bad
+arguments on the host with the documented status before anything is launched.
+The pointers handed over here are fake (never dereferenced on the host); only
+calls that the host validation ends are made, so no kernel is ever launched.
+"""
+import ctypes
+import glob
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "gated_delta_rule_20_amd", "libgdn.so")
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not os.path.exists(LIB):
+        subprocess.run([sys.executable, os.path.join(ROOT, "gated_delta_rule_20_amd", "build.py")],
+                       check=True, cwd=ROOT)
+    import gated_delta_rule_20_amd as mod
+    return mod
+
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def fake(i, misalign=0):
+    return ctypes.c_void_p(0x1000000 * (i + 1) + misalign)
+
+
+def base_args(g, **kw):
+    a = g.FwdArgs(B=2, T=128, H=4, d_k=128, d_v=128, chunk=64, N=2, dtype=g.GDN_BF16,
+                  gate=g.GDN_GATE_HEAD)
+    a.q, a.k, a.v, a.beta, a.log_alpha = fake(0), fake(1), fake(2), fake(3), fake(4)
+    a.o, a.final_state = fake(5), fake(6)
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+def fwd(g, a):
+    return g._lib.gdn_fwd_chunked(ctypes.byref(a) if a is not None else None, None)
+
+
+def test_header_declares_the_boundary(g):
+    assert g.header_functions() == ["gdn_fwd_chunked", "gdn_fwd_recurrent_step",
+                                    "gdn_fwd_workspace_size", "gdn_status_str", "gdn_version"]
+
+
+def test_library_exports_every_header_function(g):
+    lib = ctypes.CDLL(LIB)
+    for name in g.header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(g):
+    texts = {c: g.status_str(c) for c in (OK, INVALID, UNSUPPORTED, WORKSPACE, g.GDN_ERR_HIP)}
+    assert len(set(texts.values())) == 5 and all(texts.values())
+    assert g.status_str(12345) == "unknown status"
+    assert g.version() >= 100
+
+
+def test_missing_library_fails_loudly(g):
+    with pytest.raises(ImportError):
+        g.load_library("/nonexistent/libgdn.so")
+
+
+def test_package_has_no_cpu_path():
+    """The product package never reaches the CPU oracle."""
+    pkg = os.path.join(ROOT, "gated_delta_rule_20_amd")
+    for path in glob.glob(os.path.join(pkg, "*.py")):
+        text = open(path).read()
+        assert "import oracle" not in text and "from oracle" not in text, path
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(d_k=96), UNSUPPORTED),
+    (dict(d_v=256), UNSUPPORTED),
+    (dict(dtype=0), UNSUPPORTED),          # fp32 I/O needs d_k = 64
+    (dict(dtype=7), INVALID),
+    (dict(gate=3), INVALID),
+    (dict(log_alpha=None), INVALID),       # scalar gate without its decays
+    (dict(gate=0), INVALID),               # no gate but decays given
+    (dict(q=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(q=fake(0, 2)), INVALID),         # misaligned
+    (dict(final_state=fake(6, 8)), INVALID),
+    (dict(gate=2, log_alpha=fake(4, 4)), INVALID),  # per-channel decays need 16-byte rows
+    (dict(N=3), INVALID),                  # N must equal B without cu_seqlens
+    (dict(cu_seqlens=fake(7)), INVALID),   # packed sequences need B == 1
+    (dict(H=0), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(B=65536, T=65536, N=65536), UNSUPPORTED),  # more than 2^31 - 1 tokens
+    (dict(B=1, N=3, cu_seqlens=fake(7)), WORKSPACE),  # varlen needs its order table
+    (dict(B=1, N=3, cu_seqlens=fake(7), workspace=fake(8, 16), workspace_bytes=4096), WORKSPACE),
+    (dict(B=1, N=3, cu_seqlens=fake(7), workspace=fake(8), workspace_bytes=8), WORKSPACE),
+    (dict(B=0, N=0), OK),                  # nothing to do: nothing launched
+])
+def test_fwd_host_validation(g, change, status):
+    assert fwd(g, base_args(g, **change)) == status
+
+
+def test_fwd_null_args(g):
+    assert fwd(g, None) == INVALID
+    assert g._lib.gdn_fwd_workspace_size(None) == 0
+
+
+def test_workspace_size(g):
+    assert g.fwd_workspace_size(base_args(g)) == 0
+    for n, need in [(1, 256), (64, 256), (65, 512), (100, 512), (8192, 32768), (8193, 0)]:
+        assert g.fwd_workspace_size(base_args(g, B=1, N=n, cu_seqlens=fake(7))) == need, n
+    assert g.fwd_workspace_size(base_args(g, chunk=128)) == 0
+
+
+def step_args(g, **kw):
+    a = g.StepArgs(N=4, H=2, d_k=128, d_v=64, dtype=g.GDN_BF16, gate=g.GDN_GATE_KEY)
+    a.q, a.k, a.v, a.beta, a.log_alpha, a.state, a.o = (fake(i) for i in range(7))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(N=0), OK),
+    (dict(d_k=32), UNSUPPORTED),
+    (dict(d_v=96), UNSUPPORTED),
+    (dict(state=None), INVALID),
+    (dict(state=fake(5, 4)), INVALID),
+    (dict(log_alpha=None), INVALID),
+    (dict(gate=0), INVALID),
+    (dict(dtype=5), INVALID),
+    (dict(H=0), INVALID),
+])
+def test_step_host_validation(g, change, status):
+    assert g._lib.gdn_fwd_recurrent_step(ctypes.byref(step_args(g, **change)), None) == status
+
+
+# ------------------------------------------------------------ binding checks
+def fwd_tensors(B=2, T=5, H=3, dk=64, dv=64, dtype=torch.bfloat16):
+    return dict(q=torch.zeros(B, T, H, dk, dtype=dtype), k=torch.zeros(B, T, H, dk, dtype=dtype),
+                v=torch.zeros(B, T, H, dv, dtype=dtype), beta=torch.zeros(B, T, H),
+                log_alpha=torch.zeros(B, T, H))
+
+
+@pytest.mark.parametrize("mutate,msg", [
+    (lambda t: t.update(k=t["k"][:, :4]), "k must"),
+    (lambda t: t.update(v=t["v"][:1]), "v must"),
+    (lambda t: t.update(beta=t["beta"].double()), "beta must"),
+    (lambda t: t.update(log_alpha=torch.zeros(2, 5, 3, 7)), "log_alpha must"),
+    (lambda t: t.update(q=t["q"].float()), "share one dtype"),
+    (lambda t: t.update(initial_state=torch.zeros(2, 3, 64, 32)), "initial_state must"),
+    (lambda t: t.update(q=torch.zeros(2, 5, 64, 3, dtype=torch.bfloat16).transpose(2, 3)), "contiguous"),
+    (lambda t: t.update(cu_seqlens=torch.tensor([0, 5], dtype=torch.int64)), "cu_seqlens must"),
+    (lambda t: t.update(cu_seqlens=torch.tensor([0, 5], dtype=torch.int32)), "B == 1"),
+    (lambda t: None, "GPU device"),  # well-formed, but host tensors
+])
+def test_binding_rejects_bad_tensors(g, mutate, msg):
+    t = fwd_tensors()
+    mutate(t)
+    with pytest.raises(ValueError, match=msg):
+        g.fwd_chunked(**t)
+
+
+def test_binding_rejects_bad_step_tensors(g):
+    N, H, dk, dv = 3, 2, 64, 64
+    q = torch.zeros(N, H, dk, dtype=torch.bfloat16)
+    ok = dict(q=q, k=q.clone(), v=torch.zeros(N, H, dv, dtype=torch.bfloat16), beta=torch.zeros(N, H),
+              log_alpha=None, state=torch.zeros(N, H, dk, dv))
+    with pytest.raises(ValueError, match="state must"):
+        g.recurrent_step(**dict(ok, state=torch.zeros(N, H, dv, dk + 1)))
+    with pytest.raises(ValueError, match="log_alpha must"):
+        g.recurrent_step(**dict(ok, log_alpha=torch.zeros(N, H, 5)))
+    with pytest.raises(ValueError, match="GPU device"):
+        g.recurrent_step(**ok)
