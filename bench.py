@@ -12,6 +12,7 @@ fp32 state) to its average launch duration, measured with HIP events on the stre
 the kernel runs on.  `cpu_baseline` times the fp64 oracle on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
+                       [--calibrate-copy MIB]
 """
 from __future__ import annotations
 
@@ -29,8 +30,9 @@ METRIC = "gated-delta-rule fwd tokens/sec and % MFMA peak, 1×MI355X"
 HEADLINE = "gdn-350m-bf16-B16-T2048-H8-d128"
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA = {"bf16": 2516.6, "f32": 157.3}  # dense TFLOP/s
-KERNEL_SOURCES = ["gated_delta_rule_20_amd/csrc/gdn_fwd_fused.hip", "gated_delta_rule_20_amd/csrc/gdn_common.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_fused_gdn-350m.txt")
+# sources of the kernel that runs the headline workload (bf16, d_k = 128, scalar gate)
+KERNEL_SOURCES = ["gated_delta_rule_20_amd/csrc/gdn_fwd_pipe.hip", "gated_delta_rule_20_amd/csrc/gdn_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_pipe_gdn-350m.txt")
 ROTATE = 4
 CHUNK = 64
 
@@ -90,35 +92,29 @@ def time_chunked(gdn, sets, steps, warmup):
     """Whole-job time of `steps` calls (barrier + synchronize on both sides) and the
     average per-launch duration from HIP events on the launch stream."""
     import torch
-    s0 = sets[0]
-    B, T, H, dk = s0["q"].shape
-    dv = s0["v"].shape[-1]
-    N = s0["N"]
-    outs = [torch.empty((B, T, H, dv), dtype=s0["q"].dtype, device="cuda") for _ in sets]
-    fstates = [torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda") for _ in sets]
-    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    # one validated call per input copy: each timed step is a single library call
+    stream = torch.cuda.current_stream()
+    calls = [gdn.PreparedFwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"],
+                             d["cu_seqlens"]) for d in sets]
 
     def call(i):
-        d = sets[i % len(sets)]
-        gdn.fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"],
-                        d["cu_seqlens"], out=outs[i % len(sets)], final_state=fstates[i % len(sets)],
-                        workspace=ws)
+        calls[i % len(calls)].launch(stream)
 
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # HIP events on the launch stream around the whole timed region: the launches
+    # run back to back, so (end - start) / steps is the average launch duration
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         call(i)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    return wall, sum(launch_ms) / len(launch_ms), launch_ms
+    return wall, e0.elapsed_time(e1) / steps
 
 
 def time_decode(gdn, spec, final_states, steps=64):
@@ -172,7 +168,7 @@ def bench_workload(gdn, name, steps, warmup):
     B, T, H, dk = inp["q"].shape
     dv = inp["v"].shape[-1]
     sets = make_device_inputs(inp, ROTATE)
-    wall, launch_ms, _ = time_chunked(gdn, sets, steps, warmup)
+    wall, launch_ms = time_chunked(gdn, sets, steps, warmup)
     tokens = B * T
     esize = 2 if spec["dtype"] == "bf16" else 4
     flops, nbytes = alg_counts(tokens, H, dk, dv, inp["N"], spec["gate"], esize,
@@ -193,6 +189,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--all", action="store_true", help="also report every workload (extra lines on stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run twice a plain elementwise kernel that reads MIB MiB once "
+                         "and writes them once: the known-size reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -232,6 +231,13 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic},
     }
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(inp, H)
     if args.all:

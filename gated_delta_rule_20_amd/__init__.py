@@ -234,6 +234,43 @@ def fwd_chunked(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=No
     return out, (final_state if output_final_state else None)
 
 
+class PreparedFwd:
+    """A validated gdn_fwd_chunked call on fixed buffers, for repeated launches.
+
+    Checks the tensors once and keeps the marshalled argument struct, so that each
+    ``launch`` is a single call into the library (no per-call Python checks).  The
+    tensors are held by reference and must keep their storage; ``o`` and
+    ``final_state`` are overwritten by every launch."""
+
+    def __init__(self, q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None,
+                 out=None, final_state=None, output_final_state: bool = True, workspace=None,
+                 chunk: int = CHUNK):
+        import torch
+        if output_final_state and final_state is None:
+            B, T, H, dk = q.shape
+            N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+            final_state = torch.empty((N, H, dk, v.shape[-1]), dtype=torch.float32, device=q.device)
+        if out is None:
+            out = torch.empty(tuple(v.shape), dtype=q.dtype, device=q.device)
+        check_fwd_tensors(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out,
+                          final_state if output_final_state else None)
+        self.args = make_fwd_args(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out,
+                                  final_state if output_final_state else None, chunk)
+        need = fwd_workspace_size(self.args)
+        if need and (workspace is None or workspace.numel() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if need:
+            self.args.workspace, self.args.workspace_bytes = workspace.data_ptr(), workspace.numel()
+        self._keep = (q, k, v, beta, log_alpha, initial_state, cu_seqlens, workspace)
+        self.out, self.final_state = out, (final_state if output_final_state else None)
+        self._ref = ctypes.byref(self.args)
+
+    def launch(self, stream=None):
+        """Enqueue the forward on `stream` (default: torch's current stream)."""
+        _check(_lib.gdn_fwd_chunked(self._ref, _stream(stream)), "gdn_fwd_chunked")
+        return self.out, self.final_state
+
+
 def recurrent_step(q, k, v, beta, log_alpha, state, out=None, stream=None):
     """One decode token per stream (gdn_fwd_recurrent_step).
 

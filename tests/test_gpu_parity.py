@@ -229,3 +229,14 @@ def test_forward_then_step_equals_longer_forward(gdn):
     o_ref, f_ref = run_oracle(inp)
     assert relerr(o.cpu(), o_ref[:, 128]) <= 2e-2
     assert relerr(st.cpu(), f_ref) <= 2e-2
+
+
+def test_prepared_call_matches_direct_call(gdn):
+    inp = synth.random_inputs(2, 150, 2, 128, 128, "head", "bf16", seed=13, state_std=0.05)
+    o_ref, f_ref = run_gpu(gdn, inp)
+    d = to_dev(inp)
+    call = gdn.PreparedFwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"], None)
+    for _ in range(2):
+        o, fs = call.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(o.cpu(), o_ref) and torch.equal(fs.cpu(), f_ref)
