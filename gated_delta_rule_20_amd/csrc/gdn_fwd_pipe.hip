@@ -31,6 +31,8 @@
 // chunks (chunk ^ (row & 15)), V rows of 128 B (chunk ^ (row & 7)), T/P rows of
 // 128 B in 8-byte units (unit ^ (row & 15)).  K^T and V fragments are read with
 // ds_read_b64_tr_b16 (gfx950 transposing LDS read), so no transposed copies exist.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -38,7 +40,12 @@ namespace gdn {
 
 namespace {
 
-constexpr int C = 64, DK = 128, DVB = 64, NT = 256;
+constexpr int C = 64, DK = 128, DVB = 64, NT = 512;
+// wave roles (wave w runs on SIMD w % 4): 0, 1 state waves; producers of the next
+// chunk: TA, TB (T), PA, PB (P); loaders LKQ (K, Q, V) and LBL (beta, log alpha, decay
+// vectors).  Each state wave shares its SIMD with a T builder, whose instructions fill
+// the state wave's dependency stalls; the P builders share theirs with the loaders.
+constexpr int W_LKQ = 2, W_LBL = 3, W_TA = 4, W_TB = 5, W_PA = 6, W_PB = 7;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -72,14 +79,22 @@ __device__ __forceinline__ int kq_off(int r, int c) {  // K/Q [64][128] bf16
 __device__ __forceinline__ int v_off(int r, int c) {  // V [64][64] bf16
   return r * 128 + ((((c >> 3) ^ (r & 7))) << 4) + ((c & 7) << 1);
 }
-__device__ __forceinline__ int tp_off(int r, int c) {  // T/P [64][64] bf16, 8-byte units
-  return r * 128 + ((((c >> 2) ^ (r & 15))) << 3) + ((c & 3) << 1);
+// T/P [64][64] bf16.  Columns are stored permuted, c -> 32(c/32) + 8((c/4)%4) + 4((c/16)%2)
+// + c%4, so the two 4-column halves of an MFMA fragment (columns 32s+4q.. and
+// 32s+16+4q..) are one 16-byte unit; units are XOR-swizzled by (row & 7).
+__device__ __forceinline__ int tp_off(int r, int c) {
+  const int pc = 32 * (c >> 5) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3);
+  return r * 128 + (((pc >> 3) ^ (r & 7)) << 4) + ((pc & 7) << 1);
 }
 // the ten lower 16x16 tiles (a >= b) of a 64x64 chunk matrix
 constexpr int TA[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 constexpr int TB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 // off-diagonal A block index: (1,0)->0 (2,0)->1 (2,1)->2 (3,0)->3 (3,1)->4 (3,2)->5
 __device__ __forceinline__ int ao_idx(int a, int b) { return a * (a - 1) / 2 + b; }
+constexpr int OA[6] = {1, 2, 2, 3, 3, 3};
+constexpr int OB[6] = {0, 0, 1, 0, 1, 2};
+// unscaled diagonal blocks of T, bf16 [64][16] (row r of block r/16)
+__device__ __forceinline__ int td_off(int r, int c) { return r * 32 + c * 2; }
 
 __device__ __forceinline__ bf16x4 lds_ld4(const char *base, int off) { return *(const bf16x4 *)(base + off); }
 __device__ __forceinline__ bf16x8 cat44(bf16x4 a, bf16x4 b) {
@@ -297,81 +312,98 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   auto PRE = [&](int i) { return smem + OFF_PRE + i * PRE_BYTES; };
   auto GV = [&](int i) { return (float *)(smem + OFF_GV + i * GV_BYTES); };
   char *AD = smem + OFF_AD, *AO = smem + OFF_AO;
+  char *TD = AD;  // unscaled diagonal blocks of T (bf16 [64][16]) overwrite A's diagonal blocks
 
   // ---- prologue: zero T and P of both stages (their upper blocks stay zero)
   for (int i = tid; i < 2 * (PRE_BYTES / 16); i += NT) ((uint4 *)PRE(0))[i] = make_uint4(0, 0, 0, 0);
-  // ---- producer stage: everything of chunk `cc` that does not depend on the state
-  auto produce = [&](int cc) {
-    const char *kq = KQ(cc % 3);
-    char *pre = PRE(cc & 1);
-    const float *gv = GV(cc % 3);
-    const char *Ks = kq, *Qs = kq + C * DK * 2;
-    // K rows as fragments: row 16b+lm, natural columns 32s+8lg..+7
-    bf16x8 kf[4][4];
+
+  if (wave >= 2) {
+    // ===================== producer waves: everything of the next chunk that does
+    // not depend on the state, in two phases separated by the mid-chunk barrier
+    auto kfrag = [&](const char *base, int b, int s) {
+      return *(const bf16x8 *)(base + kq_off(16 * b + lm, 32 * s + 8 * lg));
+    };
+    // phase 1: Gram tiles, diagonal inverses (wave TA), P tiles (waves PA, PB)
+    // r3 = chunk % 3 (K/Q, decay vectors), r2 = chunk % 2 (T/P)
+    auto phase1 = [&](int r3, int r2) {
+      if (wave == W_LKQ || wave == W_LBL) return;
+      const char *Ks = KQ(r3), *Qs = KQ(r3) + C * DK * 2;
+      char *pre = PRE(r2);
+      const float *gv = GV(r3);
+      GammaRegs G;
+      load_gamma<GATE>(G, gv, lm, lg);
+      if (wave == W_PA || wave == W_PB) {
+        // P = lower-inclusive(Q K^T * Gamma): tile (a, b) as K_b Q_a^T, so the lane
+        // holds row 16a+lm, columns 16b+4lg..+3 (the A-operand fragment layout)
+        auto ptiles = [&](auto t0c, auto t1c) {
+          constexpr int t0 = decltype(t0c)::value, t1 = decltype(t1c)::value;
+          bf16x8 kf[4][4], qf[4][4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+          for (int t = t0; t < t1; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) kf[b][s] = *(const bf16x8 *)(Ks + kq_off(16 * b + lm, 32 * s + 8 * lg));
-    GammaRegs G;
-    load_gamma<GATE>(G, gv, lm, lg);
-    if (wave == 3) {
-      // P = lower-inclusive(Q K^T * Gamma): tile (a, b) computed as K_b Q_a^T so the
-      // lane holds row 16a+lm, columns 16b+4lg..+3 (the A-operand fragment layout);
-      // the ten accumulation chains are interleaved
-      bf16x8 qf[4][4];
+            for (int s = 0; s < 4; ++s) {
+              kf[TB[t]][s] = kfrag(Ks, TB[t], s);
+              qf[TA[t]][s] = kfrag(Qs, TA[t], s);
+            }
+          f32x4 acc[10];
+#pragma unroll
+          for (int t = t0; t < t1; ++t) acc[t] = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = t0; t < t1; ++t) acc[t] = mma(kf[TB[t]][s], qf[TA[t]][s], acc[t]);
+#pragma unroll
+          for (int t = t0; t < t1; ++t) {
+            const int a = TA[t], b = TB[t];
+            *(bf16x4 *)(pre + PRE_P + tp_off(16 * a + lm, 16 * b + 4 * lg)) =
+                to_bf4(acc[t] * gamma_tile<GATE, false>(G, a, b, lm, lg));
+          }
+        };
+        if (wave == W_PA)
+          ptiles(std::integral_constant<int, 0>(), std::integral_constant<int, 5>());
+        else
+          ptiles(std::integral_constant<int, 5>(), std::integral_constant<int, 10>());
+        return;
+      }
+      bf16x8 kf[4][4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[b][s] = kfrag(Ks, b, s);
+      if (wave == W_TB) {
+        // off-diagonal tiles of A = strictly lower(beta_r K K^T * Gamma), bf16, as the
+        // A operands of the block recursion (row lm, columns 4lg..+3)
+        f32x4 acc[6];
+#pragma unroll
+        for (int q = 0; q < 6; ++q) acc[q] = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int q = 0; q < 6; ++q) acc[q] = mma(kf[OB[q]][s], kf[OA[q]][s], acc[q]);
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+          const int a = OA[q], b = OB[q];
+          *(bf16x4 *)(AO + (ao_idx(a, b) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) =
+              to_bf4(acc[q] * gamma_tile<GATE, true>(G, a, b, lm, lg) * G.be[a]);
+        }
+        return;
+      }
+      // wave TA: diagonal tiles of A (fp32), then their inverses by forward substitution
+      f32x4 acc[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc[a] = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) acc[a] = mma(kf[a][s], kf[a][s], acc[a]);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) qf[a][s] = *(const bf16x8 *)(Qs + kq_off(16 * a + lm, 32 * s + 8 * lg));
-      f32x4 acc[10];
-#pragma unroll
-      for (int t = 0; t < 10; ++t) acc[t] = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int t = 0; t < 10; ++t) acc[t] = mma(kf[TB[t]][s], qf[TA[t]][s], acc[t]);
-#pragma unroll
-      for (int t = 0; t < 10; ++t) {
-        const int a = TA[t], b = TB[t];
-        *(bf16x4 *)(pre + PRE_P + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(acc[t] * gamma_tile<GATE, false>(G, a, b, lm, lg));
-      }
-    } else {
-      // A = strictly lower(beta_r K K^T * Gamma): tile (a, b) computed as K_b K_a^T
-      // (K K^T is symmetric), lane holds row 16a+lm, columns 16b+4lg..+3
-      f32x4 acc[10];
-#pragma unroll
-      for (int t = 0; t < 10; ++t) acc[t] = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int t = 0; t < 10; ++t) acc[t] = mma(kf[TB[t]][s], kf[TA[t]][s], acc[t]);
-      // diagonal tiles first (they feed the substitution), then the off-diagonal ones
-#pragma unroll
-      for (int t = 0; t < 10; ++t) {
-        const int a = TA[t], b = TB[t];
-        if (a == b)
-          *(f32x4 *)(AD + ((16 * a + lm) * 16 + 4 * lg) * 4) = acc[t] * gamma_tile<GATE, true>(G, a, b, lm, lg) * G.be[a];
-      }
-#pragma unroll
-      for (int t = 0; t < 10; ++t) {
-        const int a = TA[t], b = TB[t];
-        if (a != b)
-          *(bf16x4 *)(AO + (ao_idx(a, b) * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2) =
-              to_bf4(acc[t] * gamma_tile<GATE, true>(G, a, b, lm, lg) * G.be[a]);
-      }
-      // operands of the off-diagonal recursion, read before the substitution so their
-      // latency overlaps it: A[a][k] half-fragments (row lm, columns 4lg..+3) and the
-      // beta columns that scale T: 16lg..16lg+15 (diagonal rows), 16b+4lg..+3 (blocks)
-      bf16x4 aof[6];
-#pragma unroll
-      for (int q = 0; q < 6; ++q) aof[q] = lds_ld4(AO, (q * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2);
-      f32x4 bdg[4], bcol[3];
+        *(f32x4 *)(AD + ((16 * a + lm) * 16 + 4 * lg) * 4) = acc[a] * gamma_tile<GATE, true>(G, a, a, lm, lg) * G.be[a];
+      f32x4 bdg[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) bdg[q4] = *(const f32x4 *)(gv + GV_BETA + 16 * lg + 4 * q4);
-#pragma unroll
-      for (int b = 0; b < 3; ++b) bcol[b] = *(const f32x4 *)(gv + GV_BETA + 16 * b + 4 * lg);
-      // diagonal 16x16 blocks of T = (I + A)^-1: lane (lg, lm) owns row lm of block lg;
-      // t_r = e_r - sum_{i<r} A[r][i] t_i with rows broadcast along the 16-lane DPP row
+      // lane (lg, lm) owns row lm of diagonal block lg:
+      // t_r = e_r - sum_{i<r} A[r][i] t_i, rows broadcast along the 16-lane DPP row
       float nar[16], t[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -421,34 +453,39 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
                               GDN_FM(14, 11) GDN_FM(14, 12) GDN_FM(14, 13) GDN_FM(14, 14));
 #undef GDN_T1_STEP
 #undef GDN_FM
-      char *Tm = pre;
+      // T's diagonal blocks: unscaled into TD (read by both T waves after the barrier),
+      // times diag(beta) into T
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *(bf16x4 *)(Tm + tp_off(16 * lg + lm, 16 * lg + 4 * q4)) =
-            to_bf4((f32x4){t[4 * q4], t[4 * q4 + 1], t[4 * q4 + 2], t[4 * q4 + 3]});
-      // off-diagonal blocks, level by level: Y = sum_{k=b}^{a-1} A[a][k] T[k][b],
-      // T[a][b] = -T[a][a] Y.  T[k][b] stay in registers as C tiles (column-distributed);
-      // the transposed product -Y^T T[a][a]^T gives the row-distributed copy for LDS.
-      f32x4 Tc[4][4];  // [k][b], C layout
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 t4 = {t[4 * q4], t[4 * q4 + 1], t[4 * q4 + 2], t[4 * q4 + 3]};
+        *(bf16x4 *)(TD + td_off(16 * lg + lm, 4 * q4)) = to_bf4(t4);
+        *(bf16x4 *)(pre + tp_off(16 * lg + lm, 16 * lg + 4 * q4)) = to_bf4(t4 * bdg[q4]);
+      }
+    };
+    // phase 2: off-diagonal blocks of T by columns, Y = sum_{k=b}^{a-1} A[a][k] T[k][b],
+    // T[a][b] = -T[a][a] Y (columns are independent): wave TA column 0, wave TB
+    // columns 1 and 2.  T[k][b] stay in registers as C tiles (column-distributed); the
+    // transposed product -Y^T T[a][a]^T gives the row-distributed copy for LDS.
+    auto phase2 = [&](int r3, int r2) {
+      if (wave != W_TA && wave != W_TB) return;
+      char *Tm = PRE(r2);
+      const float *gv = GV(r3);
+      bf16x4 aof[6];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)  // diagonal blocks, column-distributed, via transposing reads
-        Tc[b][b] = [&] {
-          const bf16x4 v = tr16(Tm + tp_off(16 * b + 4 * lg + (lm >> 2), 16 * b + 4 * (lm & 3)));
-          return (f32x4){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-        }();
+      for (int q = 0; q < 6; ++q) aof[q] = lds_ld4(AO, (q * 16 * AO_STRIDE + lm * AO_STRIDE + 4 * lg) * 2);
       bf16x8 taa[4];  // T[a][a] rows: lane holds T[a][a][lm][4lg..4lg+3], zero-padded to 32-deep
 #pragma unroll
-      for (int a = 1; a < 4; ++a) taa[a] = cat44(lds_ld4(Tm, tp_off(16 * a + lm, 16 * a + 4 * lg)), (bf16x4){});
-      // the unscaled diagonal blocks are in registers now: store them as T diag(beta)
+      for (int a = 1; a < 4; ++a) taa[a] = cat44(lds_ld4(TD, td_off(16 * a + lm, 4 * lg)), (bf16x4){});
+      auto column = [&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+        const f32x4 bcol = *(const f32x4 *)(gv + GV_BETA + 16 * b + 4 * lg);
+        f32x4 Tc[4];  // [k], C layout
+        {
+          const bf16x4 v = tr16(TD + td_off(16 * b + 4 * lg + (lm >> 2), 4 * (lm & 3)));
+          Tc[b] = (f32x4){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+        }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *(bf16x4 *)(Tm + tp_off(16 * lg + lm, 16 * lg + 4 * q4)) =
-            to_bf4((f32x4){t[4 * q4], t[4 * q4 + 1], t[4 * q4 + 2], t[4 * q4 + 3]} * bdg[q4]);
-#pragma unroll
-      for (int lev = 1; lev < 4; ++lev) {
-#pragma unroll
-        for (int b = 0; b + lev < 4; ++b) {
-          const int a = b + lev;
+        for (int a = b + 1; a < 4; ++a) {
           f32x4 y = zero4();
 #pragma unroll
           for (int k0 = 0; k0 < 4; k0 += 2) {
@@ -457,57 +494,70 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
               const bf16x4 z4 = {};
               const bf16x4 a0 = in0 ? aof[ao_idx(a, k0)] : z4;
               const bf16x4 a1 = in1 ? aof[ao_idx(a, k0 + 1)] : z4;
-              const bf16x8 bfr = frag_from_c<bf16>(in0 ? Tc[k0][b] : zero4(), in1 ? Tc[k0 + 1][b] : zero4());
+              const bf16x8 bfr = frag_from_c<bf16>(in0 ? Tc[k0] : zero4(), in1 ? Tc[k0 + 1] : zero4());
               y = mma(cat44(a0, a1), bfr, y);
             }
           }
           const bf16x8 yf = frag_from_c_half<bf16>(y);
-          Tc[a][b] = -mma(taa[a], yf, zero4());           // T[a][b], column-distributed
-          const f32x4 zt = mma(yf, taa[a], zero4());       // (T[a][a] Y)^T: row-distributed
-          *(bf16x4 *)(Tm + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(-zt * bcol[b]);
+          if (a + 1 < 4) Tc[a] = -mma(taa[a], yf, zero4());  // T[a][b], column-distributed
+          const f32x4 zt = mma(yf, taa[a], zero4());          // (T[a][a] Y)^T: row-distributed
+          *(bf16x4 *)(Tm + tp_off(16 * a + lm, 16 * b + 4 * lg)) = to_bf4(-zt * bcol);
         }
+      };
+      if (wave == W_TA) {
+        column(std::integral_constant<int, 0>());
+      } else {
+        column(std::integral_constant<int, 1>());
+        column(std::integral_constant<int, 2>());
+      }
+    };
+
+    if (nchunks > 0) {
+      if (wave == W_LKQ) {
+        load_kq(rs, KQ(0), 0, lane);
+        load_v(rs, VB(0), 0, lane);
+        if (nchunks > 1) load_kq(rs, KQ(1), 1, lane);
+        wait_vm0();
+      } else if (wave == W_LBL) {
+        load_bl<GATE>(rs, BL(0), 0, lane);
+        if (nchunks > 1) load_bl<GATE>(rs, BL(1), 1, lane);
+        wait_vm0();
+        gate_vectors<GATE>(BL(0), GV(0), lane);
+        if (nchunks > 1) gate_vectors<GATE>(BL(1), GV(1), lane);
       }
     }
-  };
-
-  if (wave >= 2) {
-    // ===================== producer waves: T/P builders and loader =====================
-    if (wave == 3 && nchunks > 0) {
-      load_kq(rs, KQ(0), 0, lane);
-      load_bl<GATE>(rs, BL(0), 0, lane);
-      load_v(rs, VB(0), 0, lane);
-      if (nchunks > 1) {
-        load_kq(rs, KQ(1), 1, lane);
-        load_bl<GATE>(rs, BL(1), 1, lane);
-      }
-      wait_vm0();
-      gate_vectors<GATE>(BL(0), GV(0), lane);
-      if (nchunks > 1) gate_vectors<GATE>(BL(1), GV(1), lane);
-    }
-
     __syncthreads();
-    if (nchunks > 0) produce(0);
+    if (nchunks > 0) phase1(0, 0);
     __syncthreads();
+    if (nchunks > 0) phase2(0, 0);
+    __syncthreads();
+    int n3 = 1, n2 = 1, l3 = 2;  // (c + 1) % 3, (c + 1) % 2, (c + 2) % 3
     for (int c = 0; c < nchunks; ++c) {
-        if (wave == 3) {
-          if (c + 2 < nchunks) {
-            load_kq(rs, KQ((c + 2) % 3), c + 2, lane);
-            load_bl<GATE>(rs, BL((c + 2) % 3), c + 2, lane);
-          }
-          if (c + 1 < nchunks) load_v(rs, VB((c + 1) & 1), c + 1, lane);
-        }
-        if (c + 1 < nchunks) produce(c + 1);
-        if (wave == 3) {
-          wait_vm0();
-          if (c + 2 < nchunks) gate_vectors<GATE>(BL((c + 2) % 3), GV((c + 2) % 3), lane);
-        }
+      if (wave == W_LKQ) {
+        if (c + 2 < nchunks) load_kq(rs, KQ(l3), c + 2, lane);
+        if (c + 1 < nchunks) load_v(rs, VB(n2), c + 1, lane);
+      } else if (wave == W_LBL) {
+        if (c + 2 < nchunks) load_bl<GATE>(rs, BL(l3), c + 2, lane);
+      }
+      if (c + 1 < nchunks) phase1(n3, n2);
+      __syncthreads();
+      if (c + 1 < nchunks) phase2(n3, n2);
+      if (wave == W_LKQ) {
+        wait_vm0();
+      } else if (wave == W_LBL) {
+        wait_vm0();
+        if (c + 2 < nchunks) gate_vectors<GATE>(BL(l3), GV(l3), lane);
+      }
+      n3 = l3;
+      l3 = l3 == 2 ? 0 : l3 + 1;
+      n2 ^= 1;
       __syncthreads();
     }
     return;
   }
 
   // ===================== state waves (0, 1) =====================
-  // ---- state (waves 0, 1): 2 column tiles x 8 row tiles of fp32 C tiles.
+  // Each holds 32 value columns of the state as 2 x 8 fp32 C tiles.
   // C tile (ct, t), lane (lg, lm), register j holds M[key][value] with
   //   key   = 32 (t/2) + 8 lg + 4 (t%2) + j   (two row tiles form a natural 32-deep operand)
   //   value = n0 + 8 (lm/4) + 4 ct + (lm%4)  (the lane's O^T values are 8 contiguous columns)
@@ -531,144 +581,212 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   }
   __syncthreads();
   __syncthreads();
-  const int H_ = H;
-  const size_t orow = (size_t)H_ * dv;  // elements between output rows
-  bf16 *olane = (bf16 *)p.o + ((size_t)tok0 * H_ + h) * dv + col0 + n0 + (size_t)lm * orow + 8 * lg;
+  __syncthreads();
+  const size_t orow = (size_t)H * dv;  // elements between output rows
+  bf16 *olane = (bf16 *)p.o + ((size_t)tok0 * H + h) * dv + col0 + n0 + (size_t)lm * orow + 8 * lg;
+  // Lane-dependent parts of the swizzled LDS offsets; the rest of each offset is a
+  // compile-time constant (row blocks, column halves, tiles):
+  //   kq_off(16i + lm, 32s + 8lg)                   = kql[s] + 4096 i
+  //   kq_off(32s2 + 16h + r0, 32tp + 8(lm&3) + 4u)  = ktl[tp] + 8192 s2 + 4096 h + 8u
+  //   tp_off(16i + lm, fragment (s2, lg))           = tpl[s2] + 2048 i
+  //   v_off(16i + r0, n0 + 8(lm&3) + 4ct)           = vl + 2048 i + 8 ct
+  // with r0 = 4lg + lm/4 (all follow from the XOR layouts' bit fields).
+  const int r0 = 4 * lg + (lm >> 2);
+  int kql[4], ktl[4], tpl[2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    kql[q] = lm * 256 + 16 * ((4 * q + lg) ^ lm);
+    ktl[q] = r0 * 256 + 16 * ((4 * q + (lm & 3)) ^ r0);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) tpl[q] = 128 * lm + 16 * ((4 * q + lg) ^ (lm & 7));
+  const int vl = r0 * 128 + 16 * (((n0 >> 3) + (lm & 3)) ^ (r0 & 7));
   // The state waves keep M_hat = M / Gam with a running scalar Gam (the product of the
   // whole-chunk decays since the last renormalisation): the decay then costs one scalar
   // multiply per chunk instead of one per state element.  Gam is folded into the row
   // scalings of K M and Q M and into the write scale e^{g_C-g}/Gam; when Gam would drop
   // below 2^-100 the state is renormalised (M_hat *= Gam) and that chunk decays eagerly.
+  //
+  // Per chunk the critical chain is X = K M_hat -> Delta = T (V - X) -> M_hat update;
+  // O^T = M_hat^T Q^T and P Delta are issued in its gaps.  LDS fragments are read one
+  // step ahead; scheduling fences keep each group where it is written.
   float Gam = 1.f;
+  // ring-buffer offsets carried across chunks (K/Q and decay vectors: 3 stages, V and
+  // T/P: 2), so every LDS address is a lane base plus a uniform offset plus a constant
+  int ring3 = 0, ring2 = 0;
   for (int c = 0; c < nchunks; ++c) {
-      const char *Ks = KQ(c % 3), *Qs = KQ(c % 3) + C * DK * 2;
-      const char *Vs = VB(c & 1);
-      const char *pre = PRE(c & 1);
-      const float *gv = GV(c % 3);
-      // ---- issue every LDS read of this chunk's later stages up front, so their
-      // latency hides behind the K M / M^T Q^T products: K^T fragments for the state
-      // update (transposing reads), T and P fragments, V in C layout
-      bf16x8 ktf[8][2];
+    const char *Ks = smem + OFF_KQ + ring3 * KQ_BYTES;
+    const char *Vs = smem + OFF_V + ring2 * V_BYTES + vl;
+    const char *pre = smem + OFF_PRE + ring2 * PRE_BYTES;
+    const float *gv = (const float *)(smem + OFF_GV + ring3 * GV_BYTES);
+    ring3 = ring3 == 2 ? 0 : ring3 + 1;
+    ring2 ^= 1;
+    const char *kqb[4], *ktb[4], *tb[2];
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+    for (int q = 0; q < 4; ++q) {
+      kqb[q] = Ks + kql[q];
+      ktb[q] = Ks + ktl[q];
+    }
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int rr = 32 * s2 + 4 * lg + (lm >> 2), cc = 32 * (t >> 1) + 8 * (lm & 3) + 4 * (t & 1);
-          ktf[t][s2] = cat44(tr16(Ks + kq_off(rr, cc)), tr16(Ks + kq_off(rr + 16, cc)));
-        }
-      bf16x8 tf[4][2], pf[4][2];
+    for (int q = 0; q < 2; ++q) tb[q] = pre + tpl[q];
+    bf16x8 MB[4][2];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int i = 2 * s2; i < 4; ++i) {
-          const int r = 16 * i + lm, cA = 32 * s2 + 4 * lg;
-          tf[i][s2] = cat44(lds_ld4(pre, tp_off(r, cA)), lds_ld4(pre, tp_off(r, cA + 16)));
-          pf[i][s2] = cat44(lds_ld4(pre + PRE_P, tp_off(r, cA)), lds_ld4(pre + PRE_P, tp_off(r, cA + 16)));
-        }
-      bf16x4 vv[4][2];
+      for (int ct = 0; ct < 2; ++ct) MB[st][ct] = frag_from_c<bf16>(M[ct][2 * st], M[ct][2 * st + 1]);
+    // ---- X = K M_hat (K fragments of step st+1 read during step st)
+    f32x4 X[2][4];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[ct][i] = zero4();
+    bf16x8 kf[2][4], qf[2][4];
+    bf16x4 vv[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kf[0][i] = *(const bf16x8 *)(kqb[0] + 4096 * i);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (st + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[(st + 1) & 1][i] = *(const bf16x8 *)(kqb[st + 1] + 4096 * i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qf[0][i] = *(const bf16x8 *)(kqb[0] + C * DK * 2 + 4096 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) vv[i][ct] = tr16(Vs + 2048 * i + 8 * ct);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          vv[i][ct] = tr16(Vs + v_off(16 * i + 4 * lg + (lm >> 2), n0 + 8 * (lm & 3) + 4 * ct));
-      // state as operands: the same fragments serve as B (for K M) and A (for M^T Q^T)
-      bf16x8 MB[2][4];
+        for (int ct = 0; ct < 2; ++ct) X[ct][i] = mma(kf[st & 1][i], MB[st][ct], X[ct][i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- O^T = M_hat^T Q^T, with the V / decay scaling of X and its B fragments in
+    // the MFMA gaps: X <- V - Gam e^g X (beta is folded into T)
+    const float gam = gv[GV_GAMMA];
+    const float Gn = Gam * gam;
+    const bool eager = (GATE == GATE_HEAD) && !(Gn >= 0x1p-100f);
+    f32x4 OT[2][4];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) MB[ct][s] = frag_from_c<bf16>(M[ct][2 * s], M[ct][2 * s + 1]);
-      f32x4 X[2][4], OT[2][4];
+      for (int i = 0; i < 4; ++i) OT[ct][i] = zero4();
+    bf16x8 tf[4][2], XB[2][2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+    for (int st = 0; st < 4; ++st) {
+      if (st + 1 < 4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[ct][i] = OT[ct][i] = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * i + lm, cA = 32 * s + 8 * lg;
-          const bf16x8 kf = *(const bf16x8 *)(Ks + kq_off(r, cA));
-          const bf16x8 qf = *(const bf16x8 *)(Qs + kq_off(r, cA));
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            X[ct][i] = mma(kf, MB[ct][s], X[ct][i]);
-            OT[ct][i] = mma(MB[ct][s], qf, OT[ct][i]);
-          }
-        }
-      // X <- V - Gam e^g X (beta is folded into T);  O^T columns (positions) scaled by Gam e^g
-      const float gam = gv[GV_GAMMA];
-      const float Gn = Gam * gam;
-      const bool eager = (GATE == GATE_HEAD) && !(Gn >= 0x1p-100f);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 eg4 = *(const f32x4 *)(gv + GV_EG + 16 * i + 4 * lg) * Gam;
-        const float egl = gv[GV_EG + 16 * i + lm] * Gam;
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) X[ct][i][j] = (float)vv[i][ct][j] - eg4[j] * X[ct][i][j];
-          OT[ct][i] *= egl;
-        }
-      }
-      // Delta = T X
-      f32x4 D[2][4];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) D[ct][i] = zero4();
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        bf16x8 XB[2];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) XB[ct] = frag_from_c<bf16>(X[ct][2 * s2], X[ct][2 * s2 + 1]);
-#pragma unroll
-        for (int i = 2 * s2; i < 4; ++i) {
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) D[ct][i] = mma(tf[i][s2], XB[ct], D[ct][i]);
-        }
-      }
-      // O^T += Delta^T P^T ;  M <- e^{g_C} M + K^T diag(e^{g_C - g}) Delta
-      bf16x8 DA[2][2], DT[2][2];
-      const float winv = eager ? 1.f : 1.f / Gn;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const f32x4 ec0 = *(const f32x4 *)(gv + GV_EGC + 32 * s2 + 4 * lg) * winv;
-        const f32x4 ec1 = *(const f32x4 *)(gv + GV_EGC + 32 * s2 + 16 + 4 * lg) * winv;
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          DA[ct][s2] = frag_from_c<bf16>(D[ct][2 * s2], D[ct][2 * s2 + 1]);
-          DT[ct][s2] = frag_from_c<bf16>(D[ct][2 * s2] * ec0, D[ct][2 * s2 + 1] * ec1);
-        }
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int i = 2 * s2; i < 4; ++i) {
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) OT[ct][i] = mma(DA[ct][s2], pf[i][s2], OT[ct][i]);
-        }
-      if (eager) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) M[ct][t] *= Gn;
-      }
-      Gam = eager ? 1.f : Gn;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
+        for (int i = 0; i < 4; ++i) qf[(st + 1) & 1][i] = *(const bf16x8 *)(kqb[st + 1] + C * DK * 2 + 4096 * i);
+      } else {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) M[ct][t] = mma(ktf[t][s2], DT[ct][s2], M[ct][t]);
+          for (int i = 2 * s2; i < 4; ++i) tf[i][s2] = *(const bf16x8 *)(tb[s2] + 2048 * i);
       }
-      // O rows -> HBM: lane holds O[16i+lm][n0 + 8lg .. 8lg+7] (one 16-byte store)
-      const int nv = min(C, len - c * C);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * i + lm;
-        if (row < nv)
-          *(bf16x8 *)(olane + (size_t)(c * C + 16 * i) * orow) = cat44(to_bf4(OT[0][i]), to_bf4(OT[1][i]));
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) OT[ct][i] = mma(MB[st][ct], qf[st & 1][i], OT[ct][i]);
+      if (st < 2) {
+#pragma unroll
+        for (int i = 2 * st; i < 2 * st + 2; ++i) {
+          const f32x4 eg4 = *(const f32x4 *)(gv + GV_EG + 16 * i + 4 * lg) * Gam;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) X[ct][i][j] = (float)vv[i][ct][j] - eg4[j] * X[ct][i][j];
+        }
+      } else if (st == 2) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) XB[ct][s2] = frag_from_c<bf16>(X[ct][2 * s2], X[ct][2 * s2 + 1]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- Delta = T X  (T lower triangular: row blocks 0, 1 need the first 32 columns only)
+    f32x4 D[2][4];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) D[ct][i] = zero4();
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 2 * s2; i < 4; ++i)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) D[ct][i] = mma(tf[i][s2], XB[ct][s2], D[ct][i]);
+    // P fragments and the first K^T fragments in flight; O^T scaled by Gam e^g meanwhile
+    bf16x8 pf[4][2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 2 * s2; i < 4; ++i) pf[i][s2] = *(const bf16x8 *)(tb[s2] + PRE_P + 2048 * i);
+    bf16x8 ktf[2][2][2];  // [buffer][t & 1][s2]
+    auto ld_kt = [&](int tp, int buf) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const char *kt = ktb[tp] + 8192 * s2 + 8 * u;
+          ktf[buf][u][s2] = cat44(tr16(kt), tr16(kt + 4096));
+        }
+    };
+    ld_kt(0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) OT[0][i] *= gv[GV_EG + 16 * i + lm] * Gam, OT[1][i] *= gv[GV_EG + 16 * i + lm] * Gam;
+    __builtin_amdgcn_sched_barrier(0);
+    // DA: Delta as the A operand of O^T += Delta^T P^T;  DT: diag(e^{g_C - g}) Delta / Gam
+    bf16x8 DA[2][2], DT[2][2];
+    const float winv = eager ? 1.f : __builtin_amdgcn_rcpf(Gn);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const f32x4 ec0 = *(const f32x4 *)(gv + GV_EGC + 32 * s2 + 4 * lg) * winv;
+      const f32x4 ec1 = *(const f32x4 *)(gv + GV_EGC + 32 * s2 + 16 + 4 * lg) * winv;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        DA[ct][s2] = frag_from_c<bf16>(D[ct][2 * s2], D[ct][2 * s2 + 1]);
+        DT[ct][s2] = frag_from_c<bf16>(D[ct][2 * s2] * ec0, D[ct][2 * s2 + 1] * ec1);
+      }
+    }
+    __syncthreads();  // mid-chunk barrier (the producers' phases)
+    if (eager) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) M[ct][t] *= Gn;
+    }
+    Gam = eager ? 1.f : Gn;
+    // ---- M_hat += K^T DT (two state tiles per step), with O^T += Delta^T P^T in its gaps
+#pragma unroll
+    for (int tp = 0; tp < 4; ++tp) {
+      if (tp + 1 < 4) ld_kt(tp + 1, (tp + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+            M[ct][2 * tp + u] = mma(ktf[tp & 1][u][s2], DT[ct][s2], M[ct][2 * tp + u]);
+      // three of the twelve P Delta products
+#pragma unroll
+      for (int k = 3 * tp; k < 3 * tp + 3; ++k) {
+        const int s2 = k < 8 ? 0 : 1, i = k < 8 ? (k >> 1) : 2 + ((k - 8) >> 1), ct = k & 1;
+        OT[ct][i] = mma(DA[ct][s2], pf[i][s2], OT[ct][i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // O rows -> HBM: lane holds O[16i+lm][n0 + 8lg .. 8lg+7] (one 16-byte store)
+    const int nv = min(C, len - c * C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (nv == C || 16 * i + lm < nv)
+        *(bf16x8 *)(olane + (size_t)(c * C + 16 * i) * orow) = cat44(to_bf4(OT[0][i]), to_bf4(OT[1][i]));
     __syncthreads();
   }
 
