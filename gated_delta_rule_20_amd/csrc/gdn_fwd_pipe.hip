@@ -12,25 +12,30 @@
 //   O     = diag(e^g) Q M0 + P Delta
 //   M_C   = e^{g_C} M0 + K^T diag(e^{g_C - g}) Delta
 //
-// One workgroup = one (sequence, head, 64 value columns); 4 waves with roles:
-//   waves 0, 1  state waves: 32 value columns each.  The fp32 state lives in MFMA
-//               accumulators; per chunk they compute X = K M0, O^T = M0^T Q^T,
-//               Delta = T X, O^T += Delta^T P^T and M += K^T Delta (the state's own
-//               C tiles feed back as operands, "B/A from C").  O is produced
-//               transposed so each lane stores 4 consecutive bf16 of one row.
-//   wave 2      T builder for the NEXT chunk: decay prefix, Gram tiles K K^T ->
-//               A, 16x16 diagonal inverses by forward substitution (one row per
-//               lane, DPP row broadcasts), off-diagonal blocks on MFMA.
-//   wave 3      P builder for the next chunk (Q K^T tiles, decay vectors) and the
-//               loader: buffer loads write the chunk after next straight into LDS
-//               (zero-filled past the sequence end by the buffer range check).
-// K and Q are triple-buffered, V and the precomputed T/P double-buffered, so one
-// barrier per chunk separates producer and consumer stages.
+// One workgroup = one (sequence, head, 64 value columns); 8 waves (2 per SIMD) with
+// fixed roles:
+//   waves 0, 1  state waves: 32 value columns each.  The fp32 state stays in
+//               registers for the whole sequence; per chunk they compute X = K M0,
+//               O^T = M0^T Q^T, Delta = T X, O^T += Delta^T P^T and M += K^T Delta
+//               (the state's own C tiles feed back as operands, "B/A from C").  O is
+//               produced transposed so each lane stores 8 consecutive bf16 of a row.
+//   TA, TB      T builders for the NEXT chunk: Gram tiles K K^T (TA the diagonal
+//               blocks, in fp32, then their inverses by forward substitution, one row
+//               per lane with DPP row broadcasts; TB the off-diagonal blocks); after
+//               the mid-chunk barrier the off-diagonal blocks of T, by block columns.
+//   PA, PB      P builders for the next chunk (five Q K^T tiles each).
+//   LKQ, LBL    loaders: direct-to-LDS buffer loads of the chunk after next (zero-
+//               filled past the sequence end by the buffer range check); LBL also
+//               turns beta and log alpha into the decay vectors one chunk ahead.
+// Each state wave shares its SIMD with a T builder, whose instructions fill the state
+// wave's dependency stalls.  K, Q and the decay vectors are triple-buffered, V and T/P
+// double-buffered; two barriers per chunk separate the producer phases.
 //
-// LDS layouts are XOR-swizzled instead of padded: K/Q rows of 256 B in 16-byte
-// chunks (chunk ^ (row & 15)), V rows of 128 B (chunk ^ (row & 7)), T/P rows of
-// 128 B in 8-byte units (unit ^ (row & 15)).  K^T and V fragments are read with
-// ds_read_b64_tr_b16 (gfx950 transposing LDS read), so no transposed copies exist.
+// LDS layouts are XOR-swizzled instead of padded: K/Q rows of 256 B in 16-byte units
+// (unit ^ kq_swz(row)), V rows of 128 B (unit ^ (row & 7)), T/P rows of 128 B with
+// permuted columns so each MFMA fragment is one 16-byte unit.  K^T and V fragments
+// are read with ds_read_b64_tr_b16 (gfx950 transposing LDS read), so no transposed
+// copies exist.
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -73,8 +78,16 @@ constexpr int LDS_TOTAL = OFF_GV + 3 * GV_BYTES;
 static_assert(4 * (GV_GAMMA + 1) <= GV_BYTES && GV_BYTES % 16 == 0, "decay vector layout");
 static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
 
-__device__ __forceinline__ int kq_off(int r, int c) {  // K/Q [64][128] bf16
-  return r * 256 + ((((c >> 3) ^ (r & 15))) << 4) + ((c & 7) << 1);
+// K/Q [64][128] bf16: the 16-byte units of a row are XOR-permuted by kq_swz(row & 15),
+// a linear bit map (images 7, 12, 14, 3 of the four row bits) chosen by timing the two
+// access patterns on gfx950: 16-byte row reads (16 rows, one unit each) and the
+// transposing 8-byte reads of K^T (4 rows x 4 units per 16 lanes) are both free of
+// bank conflicts with it (the plain row XOR makes the latter 2-way).
+__device__ __forceinline__ int kq_swz(int r) {
+  return ((r & 1) ? 7 : 0) ^ ((r & 2) ? 12 : 0) ^ ((r & 4) ? 14 : 0) ^ ((r & 8) ? 3 : 0);
+}
+__device__ __forceinline__ int kq_off(int r, int c) {
+  return r * 256 + (((c >> 3) ^ kq_swz(r & 15)) << 4) + ((c & 7) << 1);
 }
 __device__ __forceinline__ int v_off(int r, int c) {  // V [64][64] bf16
   return r * 128 + ((((c >> 3) ^ (r & 7))) << 4) + ((c & 7) << 1);
@@ -134,7 +147,7 @@ __device__ __forceinline__ void load_kq(const Res &rs, char *dst, int chunk, int
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
     const int r = 4 * n + (lane >> 4);
-    const int ch = (lane & 15) ^ (r & 15);
+    const int ch = (lane & 15) ^ kq_swz(r & 15);
     const uint32_t vo = r * rs.row_qk + ch * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k, (lds_void_t *)(dst + n * 1024), 16, vo, soff, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.q, (lds_void_t *)(dst + C * DK * 2 + n * 1024), 16, vo, soff, 0, 0);
@@ -595,8 +608,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   int kql[4], ktl[4], tpl[2];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    kql[q] = lm * 256 + 16 * ((4 * q + lg) ^ lm);
-    ktl[q] = r0 * 256 + 16 * ((4 * q + (lm & 3)) ^ r0);
+    kql[q] = lm * 256 + 16 * ((4 * q + lg) ^ kq_swz(lm));
+    ktl[q] = r0 * 256 + 16 * ((4 * q + (lm & 3)) ^ kq_swz(r0));
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) tpl[q] = 128 * lm + 16 * ((4 * q + lg) ^ (lm & 7));
