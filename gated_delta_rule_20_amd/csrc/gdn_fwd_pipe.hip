@@ -50,7 +50,8 @@ constexpr int C = 64, DK = 128, DVB = 64, NT = 512;
 // chunk: TA, TB (T), PA, PB (P); loaders LKQ (K, Q, V) and LBL (beta, log alpha, decay
 // vectors).  Each state wave shares its SIMD with a T builder, whose instructions fill
 // the state wave's dependency stalls; the P builders share theirs with the loaders.
-constexpr int W_LKQ = 2, W_LBL = 3, W_TA = 4, W_TB = 5, W_PA = 6, W_PB = 7;
+constexpr int W_TA = 2, W_TB = 3, W_PA = 6, W_PB = 7;
+constexpr int W_LKQ = W_PA, W_LBL = W_PB;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   // ---- prologue: zero T and P of both stages (their upper blocks stay zero)
   for (int i = tid; i < 2 * (PRE_BYTES / 16); i += NT) ((uint4 *)PRE(0))[i] = make_uint4(0, 0, 0, 0);
 
-  if (wave >= 2) {
+  if ((wave & 3) >= 2) {
     // ===================== producer waves: everything of the next chunk that does
     // not depend on the state, in two phases separated by the mid-chunk barrier
     auto kfrag = [&](const char *base, int b, int s) {
@@ -339,7 +340,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     // phase 1: Gram tiles, diagonal inverses (wave TA), P tiles (waves PA, PB)
     // r3 = chunk % 3 (K/Q, decay vectors), r2 = chunk % 2 (T/P)
     auto phase1 = [&](int r3, int r2) {
-      if (wave == W_LKQ || wave == W_LBL) return;
       const char *Ks = KQ(r3), *Qs = KQ(r3) + C * DK * 2;
       char *pre = PRE(r2);
       const float *gv = GV(r3);
@@ -569,40 +569,34 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     return;
   }
 
-  // ===================== state waves (0, 1) =====================
-  // Each holds 32 value columns of the state as 2 x 8 fp32 C tiles.
-  // C tile (ct, t), lane (lg, lm), register j holds M[key][value] with
-  //   key   = 32 (t/2) + 8 lg + 4 (t%2) + j   (two row tiles form a natural 32-deep operand)
-  //   value = n0 + 8 (lm/4) + 4 ct + (lm%4)  (the lane's O^T values are 8 contiguous columns)
-  const int n0 = 32 * wave;  // first value column of this wave inside the block
-  f32x4 M[2][8];
-  const size_t sbase = ((size_t)n * H + h) * DK * dv + col0 + n0 + 8 * (lm >> 2) + (lm & 3);
+  // ===================== state waves (0, 1, 4, 5) =====================
+  // Each holds 16 value columns of the state as 8 fp32 C tiles (one per 16 keys).
+  // C tile t, lane (lg, lm), register j holds M[key][value] with
+  //   key   = 32 (t/2) + 8 lg + 4 (t%2) + j   (two tiles form a natural 32-deep operand)
+  //   value = n0 + lm
+  const int n0 = 16 * ((wave & 1) + 2 * (wave >> 2));  // first value column inside the block
+  f32x4 M[8];
+  const size_t sbase = ((size_t)n * H + h) * DK * dv + col0 + n0 + lm;
   {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int j = 0; j < 4; ++j)
+        M[t][j] = p.init_state ? p.init_state[sbase + (size_t)(32 * (t >> 1) + 8 * lg + 4 * (t & 1) + j) * dv] : 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          M[ct][t][j] = p.init_state
-                            ? p.init_state[sbase + 4 * ct + (size_t)(32 * (t >> 1) + 8 * lg + 4 * (t & 1) + j) * dv]
-                            : 0.f;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) opaque(M[ct][t]);
+    for (int t = 0; t < 8; ++t) opaque(M[t]);
   }
   __syncthreads();
   __syncthreads();
   __syncthreads();
   const size_t orow = (size_t)H * dv;  // elements between output rows
-  bf16 *olane = (bf16 *)p.o + ((size_t)tok0 * H + h) * dv + col0 + n0 + (size_t)lm * orow + 8 * lg;
+  bf16 *olane = (bf16 *)p.o + ((size_t)tok0 * H + h) * dv + col0 + n0 + (size_t)lm * orow + 4 * lg;
   // Lane-dependent parts of the swizzled LDS offsets; the rest of each offset is a
   // compile-time constant (row blocks, column halves, tiles):
   //   kq_off(16i + lm, 32s + 8lg)                   = kql[s] + 4096 i
   //   kq_off(32s2 + 16h + r0, 32tp + 8(lm&3) + 4u)  = ktl[tp] + 8192 s2 + 4096 h + 8u
   //   tp_off(16i + lm, fragment (s2, lg))           = tpl[s2] + 2048 i
-  //   v_off(16i + r0, n0 + 8(lm&3) + 4ct)           = vl + 2048 i + 8 ct
+  //   v_off(16i + r0, n0 + 4(lm&3))                 = vl + 2048 i
   // with r0 = 4lg + lm/4 (all follow from the XOR layouts' bit fields).
   const int r0 = 4 * lg + (lm >> 2);
   int kql[4], ktl[4], tpl[2];
@@ -613,7 +607,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) tpl[q] = 128 * lm + 16 * ((4 * q + lg) ^ (lm & 7));
-  const int vl = r0 * 128 + 16 * (((n0 >> 3) + (lm & 3)) ^ (r0 & 7));
+  const int vl = r0 * 128 + 16 * (((n0 >> 3) + ((lm & 3) >> 1)) ^ (r0 & 7)) + 8 * (lm & 1);
   // The state waves keep M_hat = M / Gam with a running scalar Gam (the product of the
   // whole-chunk decays since the last renormalisation): the decay then costs one scalar
   // multiply per chunk instead of one per state element.  Gam is folded into the row
@@ -642,19 +636,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) tb[q] = pre + tpl[q];
-    bf16x8 MB[4][2];
+    bf16x8 MB[4];
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) MB[st][ct] = frag_from_c<bf16>(M[ct][2 * st], M[ct][2 * st + 1]);
+    for (int st = 0; st < 4; ++st) MB[st] = frag_from_c<bf16>(M[2 * st], M[2 * st + 1]);
     // ---- X = K M_hat (K fragments of step st+1 read during step st)
-    f32x4 X[2][4];
+    f32x4 X[4];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) X[ct][i] = zero4();
+    for (int i = 0; i < 4; ++i) X[i] = zero4();
     bf16x8 kf[2][4], qf[2][4];
-    bf16x4 vv[4][2];
+    bf16x4 vv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) kf[0][i] = *(const bf16x8 *)(kqb[0] + 4096 * i);
 #pragma unroll
@@ -666,15 +656,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) qf[0][i] = *(const bf16x8 *)(kqb[0] + C * DK * 2 + 4096 * i);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) vv[i][ct] = tr16(Vs + 2048 * i + 8 * ct);
+        for (int i = 0; i < 4; ++i) vv[i] = tr16(Vs + 2048 * i);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) X[ct][i] = mma(kf[st & 1][i], MB[st][ct], X[ct][i]);
+      for (int i = 0; i < 4; ++i) X[i] = mma(kf[st & 1][i], MB[st], X[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // ---- O^T = M_hat^T Q^T, with the V / decay scaling of X and its B fragments in
@@ -682,12 +668,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     const float gam = gv[GV_GAMMA];
     const float Gn = Gam * gam;
     const bool eager = (GATE == GATE_HEAD) && !(Gn >= 0x1p-100f);
-    f32x4 OT[2][4];
+    f32x4 OT[4];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) OT[ct][i] = zero4();
-    bf16x8 tf[4][2], XB[2][2];
+    for (int i = 0; i < 4; ++i) OT[i] = zero4();
+    bf16x8 tf[4][2], XB[2];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       if (st + 1 < 4) {
@@ -701,38 +685,28 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) OT[ct][i] = mma(MB[st][ct], qf[st & 1][i], OT[ct][i]);
+      for (int i = 0; i < 4; ++i) OT[i] = mma(MB[st], qf[st & 1][i], OT[i]);
       if (st < 2) {
 #pragma unroll
         for (int i = 2 * st; i < 2 * st + 2; ++i) {
           const f32x4 eg4 = *(const f32x4 *)(gv + GV_EG + 16 * i + 4 * lg) * Gam;
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) X[ct][i][j] = (float)vv[i][ct][j] - eg4[j] * X[ct][i][j];
+          for (int j = 0; j < 4; ++j) X[i][j] = (float)vv[i][j] - eg4[j] * X[i][j];
         }
       } else if (st == 2) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) XB[ct][s2] = frag_from_c<bf16>(X[ct][2 * s2], X[ct][2 * s2 + 1]);
+        for (int s2 = 0; s2 < 2; ++s2) XB[s2] = frag_from_c<bf16>(X[2 * s2], X[2 * s2 + 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // ---- Delta = T X  (T lower triangular: row blocks 0, 1 need the first 32 columns only)
-    f32x4 D[2][4];
+    f32x4 D[4];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) D[ct][i] = zero4();
+    for (int i = 0; i < 4; ++i) D[i] = zero4();
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int i = 2 * s2; i < 4; ++i)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) D[ct][i] = mma(tf[i][s2], XB[ct][s2], D[ct][i]);
+      for (int i = 2 * s2; i < 4; ++i) D[i] = mma(tf[i][s2], XB[s2], D[i]);
     // P fragments and the first K^T fragments in flight; O^T scaled by Gam e^g meanwhile
     bf16x8 pf[4][2];
 #pragma unroll
@@ -751,27 +725,22 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     };
     ld_kt(0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) OT[0][i] *= gv[GV_EG + 16 * i + lm] * Gam, OT[1][i] *= gv[GV_EG + 16 * i + lm] * Gam;
+    for (int i = 0; i < 4; ++i) OT[i] *= gv[GV_EG + 16 * i + lm] * Gam;
     __builtin_amdgcn_sched_barrier(0);
     // DA: Delta as the A operand of O^T += Delta^T P^T;  DT: diag(e^{g_C - g}) Delta / Gam
-    bf16x8 DA[2][2], DT[2][2];
+    bf16x8 DA[2], DT[2];
     const float winv = eager ? 1.f : __builtin_amdgcn_rcpf(Gn);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const f32x4 ec0 = *(const f32x4 *)(gv + GV_EGC + 32 * s2 + 4 * lg) * winv;
       const f32x4 ec1 = *(const f32x4 *)(gv + GV_EGC + 32 * s2 + 16 + 4 * lg) * winv;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        DA[ct][s2] = frag_from_c<bf16>(D[ct][2 * s2], D[ct][2 * s2 + 1]);
-        DT[ct][s2] = frag_from_c<bf16>(D[ct][2 * s2] * ec0, D[ct][2 * s2 + 1] * ec1);
-      }
+      DA[s2] = frag_from_c<bf16>(D[2 * s2], D[2 * s2 + 1]);
+      DT[s2] = frag_from_c<bf16>(D[2 * s2] * ec0, D[2 * s2 + 1] * ec1);
     }
     __syncthreads();  // mid-chunk barrier (the producers' phases)
     if (eager) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) M[ct][t] *= Gn;
+      for (int t = 0; t < 8; ++t) M[t] *= Gn;
     }
     Gam = eager ? 1.f : Gn;
     // ---- M_hat += K^T DT (two state tiles per step), with O^T += Delta^T P^T in its gaps
@@ -782,39 +751,31 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u) M[2 * tp + u] = mma(ktf[tp & 1][u][s2], DT[s2], M[2 * tp + u]);
+      // the six P Delta products, spread over the steps
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-            M[ct][2 * tp + u] = mma(ktf[tp & 1][u][s2], DT[ct][s2], M[ct][2 * tp + u]);
-      // three of the twelve P Delta products
-#pragma unroll
-      for (int k = 3 * tp; k < 3 * tp + 3; ++k) {
-        const int s2 = k < 8 ? 0 : 1, i = k < 8 ? (k >> 1) : 2 + ((k - 8) >> 1), ct = k & 1;
-        OT[ct][i] = mma(DA[ct][s2], pf[i][s2], OT[ct][i]);
+      for (int k = (6 * tp) / 4; k < (6 * (tp + 1)) / 4; ++k) {
+        const int s2 = k < 4 ? 0 : 1, i = k < 4 ? k : k - 2;
+        OT[i] = mma(DA[s2], pf[i][s2], OT[i]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // O rows -> HBM: lane holds O[16i+lm][n0 + 8lg .. 8lg+7] (one 16-byte store)
+    // O rows -> HBM: lane holds O[16i+lm][n0 + 4lg .. 4lg+3] (one 8-byte store)
     const int nv = min(C, len - c * C);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (nv == C || 16 * i + lm < nv)
-        *(bf16x8 *)(olane + (size_t)(c * C + 16 * i) * orow) = cat44(to_bf4(OT[0][i]), to_bf4(OT[1][i]));
+      if (nv == C || 16 * i + lm < nv) *(bf16x4 *)(olane + (size_t)(c * C + 16 * i) * orow) = to_bf4(OT[i]);
     __syncthreads();
   }
 
   if (p.final_state) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int t = 0; t < 8; ++t) M[t] *= Gam;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) M[ct][t] *= Gam;
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          p.final_state[sbase + 4 * ct + (size_t)(32 * (t >> 1) + 8 * lg + 4 * (t & 1) + j) * dv] = M[ct][t][j];
+      for (int j = 0; j < 4; ++j)
+        p.final_state[sbase + (size_t)(32 * (t >> 1) + 8 * lg + 4 * (t & 1) + j) * dv] = M[t][j];
   }
 }
 
