@@ -14,22 +14,24 @@
 //
 // One workgroup = one (sequence, head, 64 value columns); 8 waves (2 per SIMD) with
 // fixed roles:
-//   waves 0, 1  state waves: 32 value columns each.  The fp32 state stays in
+//   waves 0, 1, 4, 5  state waves: 16 value columns each.  The fp32 state stays in
 //               registers for the whole sequence; per chunk they compute X = K M0,
 //               O^T = M0^T Q^T, Delta = T X, O^T += Delta^T P^T and M += K^T Delta
 //               (the state's own C tiles feed back as operands, "B/A from C").  O is
-//               produced transposed so each lane stores 8 consecutive bf16 of a row.
+//               produced transposed so each lane stores 4 consecutive bf16 of a row.
 //   TA, TB      T builders for the NEXT chunk: Gram tiles K K^T (TA the diagonal
 //               blocks, in fp32, then their inverses by forward substitution, one row
-//               per lane with DPP row broadcasts; TB the off-diagonal blocks); after
-//               the mid-chunk barrier the off-diagonal blocks of T, by block columns.
-//   PA, PB      P builders for the next chunk (five Q K^T tiles each).
-//   LKQ, LBL    loaders: direct-to-LDS buffer loads of the chunk after next (zero-
-//               filled past the sequence end by the buffer range check); LBL also
-//               turns beta and log alpha into the decay vectors one chunk ahead.
-// Each state wave shares its SIMD with a T builder, whose instructions fill the state
-// wave's dependency stalls.  K, Q and the decay vectors are triple-buffered, V and T/P
-// double-buffered; two barriers per chunk separate the producer phases.
+//               per lane with DPP row broadcasts; TB the off-diagonal blocks); then,
+//               after handing these to each other through LDS flags, the off-diagonal
+//               blocks of T, by block columns.
+//   PA, PB      P builders for the next chunk (five Q K^T tiles each) and loaders:
+//               direct-to-LDS buffer loads of the chunk after next (zero-filled past
+//               the sequence end by the buffer range check); PB also turns beta and
+//               log alpha into the decay vectors one chunk ahead.
+// Two state waves share each of SIMDs 0 and 1 (each fills the other's dependency
+// stalls); a T and a P builder share each of SIMDs 2 and 3.  K, Q and the decay vectors
+// are triple-buffered, V and T/P double-buffered; one workgroup barrier per chunk
+// separates producers and consumers.
 //
 // LDS layouts are XOR-swizzled instead of padded: K/Q rows of 256 B in 16-byte units
 // (unit ^ kq_swz(row)), V rows of 128 B (unit ^ (row & 7)), T/P rows of 128 B with
@@ -46,10 +48,9 @@ namespace gdn {
 namespace {
 
 constexpr int C = 64, DK = 128, DVB = 64, NT = 512;
-// wave roles (wave w runs on SIMD w % 4): 0, 1 state waves; producers of the next
-// chunk: TA, TB (T), PA, PB (P); loaders LKQ (K, Q, V) and LBL (beta, log alpha, decay
-// vectors).  Each state wave shares its SIMD with a T builder, whose instructions fill
-// the state wave's dependency stalls; the P builders share theirs with the loaders.
+// wave roles (wave w runs on SIMD w % 4): 0, 1, 4, 5 state waves; producers of the
+// next chunk: TA, TB (T) and PA, PB (P), which also load (LKQ: K, Q, V; LBL: beta,
+// log alpha and the decay vectors)
 constexpr int W_TA = 2, W_TB = 3, W_PA = 6, W_PB = 7;
 constexpr int W_LKQ = W_PA, W_LBL = W_PB;
 
@@ -75,7 +76,8 @@ constexpr int GV_EH = 0, GV_EHI = 64, GV_ET = 128, GV_BETA = 192, GV_F = 256, GV
               GV_EGC = 336, GV_GAMMA = 400;
 constexpr int GV_BYTES = 1664;
 constexpr int OFF_GV = OFF_AO + 6 * 16 * AO_STRIDE * 2;
-constexpr int LDS_TOTAL = OFF_GV + 3 * GV_BYTES;
+constexpr int OFF_FLAGS = OFF_GV + 3 * GV_BYTES;  // two int flags between the T builders
+constexpr int LDS_TOTAL = OFF_FLAGS + 16;
 static_assert(4 * (GV_GAMMA + 1) <= GV_BYTES && GV_BYTES % 16 == 0, "decay vector layout");
 static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
 
@@ -328,12 +330,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   char *AD = smem + OFF_AD, *AO = smem + OFF_AO;
   char *TD = AD;  // unscaled diagonal blocks of T (bf16 [64][16]) overwrite A's diagonal blocks
 
-  // ---- prologue: zero T and P of both stages (their upper blocks stay zero)
+  // ---- prologue: zero T and P of both stages (their upper blocks stay zero) and the
+  // T builders' flags
   for (int i = tid; i < 2 * (PRE_BYTES / 16); i += NT) ((uint4 *)PRE(0))[i] = make_uint4(0, 0, 0, 0);
+  if (tid < 4) ((int *)(smem + OFF_FLAGS))[tid] = 0;
 
   if ((wave & 3) >= 2) {
     // ===================== producer waves: everything of the next chunk that does
-    // not depend on the state, in two phases separated by the mid-chunk barrier
+    // not depend on the state, in two phases around the T builders' hand-off
     auto kfrag = [&](const char *base, int b, int s) {
       return *(const bf16x8 *)(base + kq_off(16 * b + lm, 32 * s + 8 * lg));
     };
@@ -540,9 +544,24 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       }
     }
     __syncthreads();
-    if (nchunks > 0) phase1(0, 0);
-    __syncthreads();
-    if (nchunks > 0) phase2(0, 0);
+    // The two T builders hand data to each other inside a chunk (TA: T's unscaled
+    // diagonal blocks; TB: A's off-diagonal blocks) through LDS flags that count
+    // chunks, so that only one workgroup barrier per chunk is needed.  Each signals
+    // its own data before it waits for the other's, so neither wait can block.
+    volatile int *flags = (volatile int *)(smem + OFF_FLAGS);
+    auto handoff = [&](int cc) {
+      if (wave != W_TA && wave != W_TB) return;
+      const int mine = wave == W_TA ? 0 : 1;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own LDS writes done
+      if (lane == 0) flags[mine] = cc + 1;
+      while (flags[mine ^ 1] < cc + 1) __builtin_amdgcn_s_sleep(1);
+      asm volatile("" ::: "memory");
+    };
+    if (nchunks > 0) {
+      phase1(0, 0);
+      handoff(0);
+      phase2(0, 0);
+    }
     __syncthreads();
     int n3 = 1, n2 = 1, l3 = 2;  // (c + 1) % 3, (c + 1) % 2, (c + 2) % 3
     for (int c = 0; c < nchunks; ++c) {
@@ -552,9 +571,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       } else if (wave == W_LBL) {
         if (c + 2 < nchunks) load_bl<GATE>(rs, BL(l3), c + 2, lane);
       }
-      if (c + 1 < nchunks) phase1(n3, n2);
-      __syncthreads();
-      if (c + 1 < nchunks) phase2(n3, n2);
+      if (c + 1 < nchunks) {
+        phase1(n3, n2);
+        handoff(c + 1);
+        phase2(n3, n2);
+      }
       if (wave == W_LKQ) {
         wait_vm0();
       } else if (wave == W_LBL) {
@@ -586,7 +607,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) opaque(M[t]);
   }
-  __syncthreads();
   __syncthreads();
   __syncthreads();
   const size_t orow = (size_t)H * dv;  // elements between output rows
@@ -737,7 +757,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       DA[s2] = frag_from_c<bf16>(D[2 * s2], D[2 * s2 + 1]);
       DT[s2] = frag_from_c<bf16>(D[2 * s2] * ec0, D[2 * s2 + 1] * ec1);
     }
-    __syncthreads();  // mid-chunk barrier (the producers' phases)
     if (eager) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) M[t] *= Gn;
