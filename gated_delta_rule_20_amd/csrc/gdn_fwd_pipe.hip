@@ -145,15 +145,16 @@ struct Res {
 };
 
 // ---- loader (wave 3): chunk tiles straight into LDS
-__device__ __forceinline__ void load_kq(const Res &rs, char *dst, int chunk, int lane) {
+// one [64][128] tile of K (q = false) or Q (q = true) of a chunk
+__device__ __forceinline__ void load_kq(const Res &rs, char *dst, int chunk, int lane, bool q) {
   const uint32_t soff = (uint32_t)chunk * C * rs.row_qk;
+  char *d = dst + (q ? C * DK * 2 : 0);
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
     const int r = 4 * n + (lane >> 4);
     const int ch = (lane & 15) ^ kq_swz(r & 15);
     const uint32_t vo = r * rs.row_qk + ch * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.k, (lds_void_t *)(dst + n * 1024), 16, vo, soff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.q, (lds_void_t *)(dst + C * DK * 2 + n * 1024), 16, vo, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(q ? rs.q : rs.k, (lds_void_t *)(d + n * 1024), 16, vo, soff, 0, 0);
   }
 }
 __device__ __forceinline__ void load_v(const Res &rs, char *dst, int chunk, int lane) {
@@ -529,18 +530,37 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       }
     };
 
+    // Prologue loads: chunk 0 first, then chunk 1 (and beta / log alpha of chunk 2).
+    // Vector-memory loads of a wave complete in issue order, so a partial wait for
+    // chunk 0 lets T and P of chunk 0 be built while chunk 1 is still in flight.
     if (nchunks > 0) {
       if (wave == W_LKQ) {
-        load_kq(rs, KQ(0), 0, lane);
+        load_kq(rs, KQ(0), 0, lane, false);
         load_v(rs, VB(0), 0, lane);
-        if (nchunks > 1) load_kq(rs, KQ(1), 1, lane);
-        wait_vm0();
+        if (nchunks > 1) {
+          load_kq(rs, KQ(1), 1, lane, false);  // 16 loads
+          asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        } else {
+          wait_vm0();
+        }
       } else if (wave == W_LBL) {
+        load_kq(rs, KQ(0), 0, lane, true);
         load_bl<GATE>(rs, BL(0), 0, lane);
-        if (nchunks > 1) load_bl<GATE>(rs, BL(1), 1, lane);
-        wait_vm0();
+        if (nchunks > 2) {
+          load_kq(rs, KQ(1), 1, lane, true);  // 16 + 2 + 2 loads
+          load_bl<GATE>(rs, BL(1), 1, lane);
+          load_bl<GATE>(rs, BL(2), 2, lane);
+          if (GATE == GATE_HEAD) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+          else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        } else if (nchunks > 1) {
+          load_kq(rs, KQ(1), 1, lane, true);  // 16 + 2 loads
+          load_bl<GATE>(rs, BL(1), 1, lane);
+          if (GATE == GATE_HEAD) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+          else asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
+        } else {
+          wait_vm0();
+        }
         gate_vectors<GATE>(BL(0), GV(0), lane);
-        if (nchunks > 1) gate_vectors<GATE>(BL(1), GV(1), lane);
       }
     }
     __syncthreads();
@@ -548,13 +568,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     // diagonal blocks; TB: A's off-diagonal blocks) through LDS flags that count
     // chunks, so that only one workgroup barrier per chunk is needed.  Each signals
     // its own data before it waits for the other's, so neither wait can block.
-    volatile int *flags = (volatile int *)(smem + OFF_FLAGS);
+    // (relaxed workgroup-scope atomics: a volatile access would make the compiler
+    // wait for every outstanding memory operation of the wave first)
+    int *flags = (int *)(smem + OFF_FLAGS);
     auto handoff = [&](int cc) {
       if (wave != W_TA && wave != W_TB) return;
       const int mine = wave == W_TA ? 0 : 1;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own LDS writes done
-      if (lane == 0) flags[mine] = cc + 1;
-      while (flags[mine ^ 1] < cc + 1) __builtin_amdgcn_s_sleep(1);
+      if (lane == 0) __hip_atomic_store(flags + mine, cc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      while (__hip_atomic_load(flags + (mine ^ 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < cc + 1)
+        __builtin_amdgcn_s_sleep(1);
       asm volatile("" ::: "memory");
     };
     if (nchunks > 0) {
@@ -562,14 +585,24 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       handoff(0);
       phase2(0, 0);
     }
+    if (wave == W_LKQ) {
+      wait_vm0();
+    } else if (wave == W_LBL) {
+      wait_vm0();
+      if (nchunks > 1) gate_vectors<GATE>(BL(1), GV(1), lane);
+    }
     __syncthreads();
     int n3 = 1, n2 = 1, l3 = 2;  // (c + 1) % 3, (c + 1) % 2, (c + 2) % 3
     for (int c = 0; c < nchunks; ++c) {
       if (wave == W_LKQ) {
-        if (c + 2 < nchunks) load_kq(rs, KQ(l3), c + 2, lane);
+        if (c + 2 < nchunks) load_kq(rs, KQ(l3), c + 2, lane, false);
         if (c + 1 < nchunks) load_v(rs, VB(n2), c + 1, lane);
       } else if (wave == W_LBL) {
-        if (c + 2 < nchunks) load_bl<GATE>(rs, BL(l3), c + 2, lane);
+        // beta / log alpha run three chunks ahead, so the decay vectors of chunk c + 2
+        // are computed here, off the path that waits for this chunk's loads
+        if (c + 2 < nchunks) load_kq(rs, KQ(l3), c + 2, lane, true);
+        if (c + 3 < nchunks) load_bl<GATE>(rs, BL(3 - n3 - l3), c + 3, lane);
+        if (c + 2 < nchunks) gate_vectors<GATE>(BL(l3), GV(l3), lane);
       }
       if (c + 1 < nchunks) {
         phase1(n3, n2);
@@ -580,7 +613,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
         wait_vm0();
       } else if (wave == W_LBL) {
         wait_vm0();
-        if (c + 2 < nchunks) gate_vectors<GATE>(BL(l3), GV(l3), lane);
       }
       n3 = l3;
       l3 = l3 == 2 ? 0 : l3 + 1;
