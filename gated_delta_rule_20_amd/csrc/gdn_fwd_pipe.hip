@@ -25,9 +25,10 @@
 //               after handing these to each other through LDS flags, the off-diagonal
 //               blocks of T, by block columns.
 //   PA, PB      P builders for the next chunk (five Q K^T tiles each) and loaders:
-//               direct-to-LDS buffer loads of the chunk after next (zero-filled past
-//               the sequence end by the buffer range check); PB also turns beta and
-//               log alpha into the decay vectors one chunk ahead.
+//               direct-to-LDS buffer loads (zero-filled past the sequence end by the
+//               buffer range check), PA of K two chunks ahead and V one chunk ahead,
+//               PB of Q two chunks ahead and beta / log alpha three chunks ahead; PB
+//               also turns beta and log alpha into the decay vectors two chunks ahead.
 // Two state waves share each of SIMDs 0 and 1 (each fills the other's dependency
 // stalls); a T and a P builder share each of SIMDs 2 and 3.  K, Q and the decay vectors
 // are triple-buffered, V and T/P double-buffered; one workgroup barrier per chunk
@@ -49,8 +50,8 @@ namespace {
 
 constexpr int C = 64, DK = 128, DVB = 64, NT = 512;
 // wave roles (wave w runs on SIMD w % 4): 0, 1, 4, 5 state waves; producers of the
-// next chunk: TA, TB (T) and PA, PB (P), which also load (LKQ: K, Q, V; LBL: beta,
-// log alpha and the decay vectors)
+// next chunk: TA, TB (T) and PA, PB (P), which also load (LKQ: K and V; LBL: Q, beta,
+// log alpha, and the decay vectors)
 constexpr int W_TA = 2, W_TB = 3, W_PA = 6, W_PB = 7;
 constexpr int W_LKQ = W_PA, W_LBL = W_PB;
 
@@ -144,7 +145,7 @@ struct Res {
   uint32_t row_qk, row_v, row_s;  // bytes between consecutive tokens
 };
 
-// ---- loader (wave 3): chunk tiles straight into LDS
+// ---- loaders: chunk tiles straight into LDS
 // one [64][128] tile of K (q = false) or Q (q = true) of a chunk
 __device__ __forceinline__ void load_kq(const Res &rs, char *dst, int chunk, int lane, bool q) {
   const uint32_t soff = (uint32_t)chunk * C * rs.row_qk;
@@ -174,7 +175,7 @@ __device__ __forceinline__ void load_bl(const Res &rs, char *dst, int chunk, int
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.la, (lds_void_t *)(dst + 256), 4, lane * rs.row_s, soff, 0, 0);
 }
 
-// ---- decay prefix and the per-position factors of Gamma (loader wave, one chunk ahead).
+// ---- decay prefix and the per-position factors of Gamma (loader wave, two chunks ahead).
 // Ehead[r] = e^{g_r - g_m}, Ehinv[r] = e^{g_m - g_r}, Etail[r] = e^{g_e - g_r}
 // where m / e are row 7 / the last row of r's 16-block;
 // F[a][b] = e^{g_{16a+7} - g_{16b+15}} (a > b).  Then Gamma[r,i] = Ehead[r] F Etail[i]
