@@ -72,14 +72,15 @@ constexpr int OFF_AD = OFF_PRE + 2 * PRE_BYTES;  // diagonal blocks of A, fp32 [
 constexpr int AO_STRIDE = 24;                     // off-diagonal blocks, bf16 6 x [16][24]
 constexpr int OFF_AO = OFF_AD + 4 * 16 * 16 * 4;
 // per-chunk decay vectors (fp32), x3 by chunk: Ehead, Ehinv, Etail, beta, F[4][4],
-// e^g, e^{g_C - g}, e^{g_C}
-constexpr int GV_EH = 0, GV_EHI = 64, GV_ET = 128, GV_BETA = 192, GV_F = 256, GV_EG = 272,
-              GV_EGC = 336, GV_GAMMA = 400;
+// e^g Gam, e^{g_C - g} / Gam', Gam', eager flag (Gam: the state's running decay scalar
+// entering the chunk, Gam' the one leaving it; see the state waves)
+constexpr int GV_EH = 0, GV_EHI = 64, GV_ET = 128, GV_BETA = 192, GV_F = 256, GV_EGS = 272,
+              GV_EGCW = 336, GV_GN = 400, GV_EAGER = 401;
 constexpr int GV_BYTES = 1664;
 constexpr int OFF_GV = OFF_AO + 6 * 16 * AO_STRIDE * 2;
 constexpr int OFF_FLAGS = OFF_GV + 3 * GV_BYTES;  // two int flags between the T builders
 constexpr int LDS_TOTAL = OFF_FLAGS + 16;
-static_assert(4 * (GV_GAMMA + 1) <= GV_BYTES && GV_BYTES % 16 == 0, "decay vector layout");
+static_assert(4 * (GV_EAGER + 1) <= GV_BYTES && GV_BYTES % 16 == 0, "decay vector layout");
 static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
 
 // K/Q [64][128] bf16: the 16-byte units of a row are XOR-permuted by kq_swz(row & 15),
@@ -181,18 +182,24 @@ __device__ __forceinline__ void load_bl(const Res &rs, char *dst, int chunk, int
 // F[a][b] = e^{g_{16a+7} - g_{16b+15}} (a > b).  Then Gamma[r,i] = Ehead[r] F Etail[i]
 // across blocks and Ehead[r] Ehinv[i] within a block; F and Etail are <= 1, Ehead
 // and Ehinv at most the decay over eight tokens.  Also stores beta and the
-// state-phase vectors e^g, e^{g_C - g} and e^{g_C}.
+// state-phase vectors with the state waves' running decay scalar folded in.
+// `gam` is that scalar entering this chunk (uniform); it is advanced to the value
+// entering the next chunk with exactly the state waves' rule, so the chunks must be
+// prepared in order.
 template <int GATE>
-__device__ __forceinline__ void gate_vectors(const char *bl, float *gv, int lane) {
+__device__ __forceinline__ void gate_vectors(const char *bl, float *gv, int lane, float &gam) {
   gv[GV_BETA + lane] = ((const float *)bl)[lane];
   if (GATE == GATE_NONE) {
     gv[GV_EH + lane] = 1.f;
     gv[GV_EHI + lane] = 1.f;
     gv[GV_ET + lane] = 1.f;
-    gv[GV_EG + lane] = 1.f;
-    gv[GV_EGC + lane] = 1.f;
+    gv[GV_EGS + lane] = 1.f;
+    gv[GV_EGCW + lane] = 1.f;
     if (lane < 16) gv[GV_F + lane] = 1.f;
-    if (lane == 0) gv[GV_GAMMA] = 1.f;
+    if (lane == 0) {
+      gv[GV_GN] = 1.f;
+      gv[GV_EAGER] = 0.f;
+    }
     return;
   }
   float g = ((const float *)bl)[64 + lane];
@@ -215,9 +222,17 @@ __device__ __forceinline__ void gate_vectors(const char *bl, float *gv, int lane
   gv[GV_EH + lane] = __expf(g - gmid);
   gv[GV_EHI + lane] = __expf(gmid - g);
   gv[GV_ET + lane] = __expf(gend - g);
-  gv[GV_EG + lane] = __expf(g);
-  gv[GV_EGC + lane] = __expf(gE3 - g);
-  if (lane == 0) gv[GV_GAMMA] = __expf(gE3);
+  // Gn = Gam * e^{g_C}; below 2^-100 the state waves renormalise (eager chunk)
+  const float Gn = gam * __expf(gE3);
+  const bool eager = GATE == GATE_HEAD && !(Gn >= 0x1p-100f);
+  const float winv = eager ? 1.f : __builtin_amdgcn_rcpf(Gn);
+  gv[GV_EGS + lane] = __expf(g) * gam;
+  gv[GV_EGCW + lane] = __expf(gE3 - g) * winv;
+  if (lane == 0) {
+    gv[GV_GN] = Gn;
+    gv[GV_EAGER] = eager ? 1.f : 0.f;
+  }
+  gam = eager ? 1.f : Gn;
   // F[a*4+b] = exp(g_{16a+7} - g_{16b+15}) for a > b
   if (lane < 16) {
     const int a = lane >> 2, b = lane & 3;
@@ -531,6 +546,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       }
     };
 
+    float gam_run = 1.f;  // PB: the state's decay scalar entering the next chunk to prepare
     // Prologue loads: chunk 0 first, then chunk 1 (and beta / log alpha of chunk 2).
     // Vector-memory loads of a wave complete in issue order, so a partial wait for
     // chunk 0 lets T and P of chunk 0 be built while chunk 1 is still in flight.
@@ -561,7 +577,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
         } else {
           wait_vm0();
         }
-        gate_vectors<GATE>(BL(0), GV(0), lane);
+        gate_vectors<GATE>(BL(0), GV(0), lane, gam_run);
       }
     }
     __syncthreads();
@@ -590,7 +606,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       wait_vm0();
     } else if (wave == W_LBL) {
       wait_vm0();
-      if (nchunks > 1) gate_vectors<GATE>(BL(1), GV(1), lane);
+      if (nchunks > 1) gate_vectors<GATE>(BL(1), GV(1), lane, gam_run);
     }
     __syncthreads();
     int n3 = 1, n2 = 1, l3 = 2;  // (c + 1) % 3, (c + 1) % 2, (c + 2) % 3
@@ -603,7 +619,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
         // are computed here, off the path that waits for this chunk's loads
         if (c + 2 < nchunks) load_kq(rs, KQ(l3), c + 2, lane, true);
         if (c + 3 < nchunks) load_bl<GATE>(rs, BL(3 - n3 - l3), c + 3, lane);
-        if (c + 2 < nchunks) gate_vectors<GATE>(BL(l3), GV(l3), lane);
+        if (c + 2 < nchunks) gate_vectors<GATE>(BL(l3), GV(l3), lane, gam_run);
       }
       if (c + 1 < nchunks) {
         phase1(n3, n2);
@@ -666,6 +682,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   // multiply per chunk instead of one per state element.  Gam is folded into the row
   // scalings of K M and Q M and into the write scale e^{g_C-g}/Gam; when Gam would drop
   // below 2^-100 the state is renormalised (M_hat *= Gam) and that chunk decays eagerly.
+  // The loader that prepares the decay vectors runs the same scalar recursion and
+  // stores the vectors with Gam already folded in (and the renormalisation flag), so
+  // here Gam is only tracked for the final state.
   //
   // Per chunk the critical chain is X = K M_hat -> Delta = T (V - X) -> M_hat update;
   // O^T = M_hat^T Q^T and P Delta are issued in its gaps.  LDS fragments are read one
@@ -718,9 +737,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     }
     // ---- O^T = M_hat^T Q^T, with the V / decay scaling of X and its B fragments in
     // the MFMA gaps: X <- V - Gam e^g X (beta is folded into T)
-    const float gam = gv[GV_GAMMA];
-    const float Gn = Gam * gam;
-    const bool eager = (GATE == GATE_HEAD) && !(Gn >= 0x1p-100f);
+    const float Gn = gv[GV_GN];
+    const bool eager = (GATE == GATE_HEAD) && gv[GV_EAGER] != 0.f;
     f32x4 OT[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) OT[i] = zero4();
@@ -742,7 +760,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       if (st < 2) {
 #pragma unroll
         for (int i = 2 * st; i < 2 * st + 2; ++i) {
-          const f32x4 eg4 = *(const f32x4 *)(gv + GV_EG + 16 * i + 4 * lg) * Gam;
+          const f32x4 eg4 = *(const f32x4 *)(gv + GV_EGS + 16 * i + 4 * lg);
 #pragma unroll
           for (int j = 0; j < 4; ++j) X[i][j] = (float)vv[i][j] - eg4[j] * X[i][j];
         }
@@ -778,15 +796,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     };
     ld_kt(0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) OT[i] *= gv[GV_EG + 16 * i + lm] * Gam;
+    for (int i = 0; i < 4; ++i) OT[i] *= gv[GV_EGS + 16 * i + lm];
     __builtin_amdgcn_sched_barrier(0);
     // DA: Delta as the A operand of O^T += Delta^T P^T;  DT: diag(e^{g_C - g}) Delta / Gam
     bf16x8 DA[2], DT[2];
-    const float winv = eager ? 1.f : __builtin_amdgcn_rcpf(Gn);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const f32x4 ec0 = *(const f32x4 *)(gv + GV_EGC + 32 * s2 + 4 * lg) * winv;
-      const f32x4 ec1 = *(const f32x4 *)(gv + GV_EGC + 32 * s2 + 16 + 4 * lg) * winv;
+      const f32x4 ec0 = *(const f32x4 *)(gv + GV_EGCW + 32 * s2 + 4 * lg);
+      const f32x4 ec1 = *(const f32x4 *)(gv + GV_EGCW + 32 * s2 + 16 + 4 * lg);
       DA[s2] = frag_from_c<bf16>(D[2 * s2], D[2 * s2 + 1]);
       DT[s2] = frag_from_c<bf16>(D[2 * s2] * ec0, D[2 * s2 + 1] * ec1);
     }
