@@ -50,9 +50,32 @@ int check_fwd(const gdn_fwd_args *a) {
   return GDN_OK;
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 size_t order_bytes(const gdn_fwd_args *a) {
   if (!a->cu_seqlens || a->N > 8192) return 0;
-  return ((size_t)a->N * sizeof(int32_t) + 255) & ~(size_t)255;
+  return align256((size_t)a->N * sizeof(int32_t));
+}
+
+// The per-key-channel gate on the pipelined kernel (bf16, d_k = 128): a first pass
+// prepares every chunk's operands in the workspace.
+bool key_pipe(const gdn_fwd_args *a) {
+  return a->gate == GDN_GATE_KEY && a->dtype == GDN_BF16 && a->d_k == 128;
+}
+struct KeyLayout {
+  long slots;
+  size_t kq, tp, eg;  // bytes of one pre-scaled K/Q array, the T/P images, e^{g_C}
+  size_t total() const { return 3 * kq + tp + eg; }
+};
+KeyLayout key_layout(const gdn_fwd_args *a) {
+  KeyLayout L{0, 0, 0, 0};
+  if (!key_pipe(a)) return L;
+  const long tokens = (long)a->B * a->T;
+  L.slots = gdn::key_slots(tokens, a->N);
+  L.kq = align256((size_t)tokens * a->H * 128 * 2);
+  L.tp = align256((size_t)L.slots * a->H * 16384);
+  L.eg = align256((size_t)L.slots * a->H * 128 * 4);
+  return L;
 }
 
 int check_step(const gdn_step_args *a) {
@@ -77,13 +100,15 @@ extern "C" {
 
 size_t gdn_fwd_workspace_size(const gdn_fwd_args *a) {
   if (check_fwd(a) != GDN_OK) return 0;
-  return order_bytes(a);
+  return order_bytes(a) + key_layout(a).total();
 }
 
 int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
   const int st = check_fwd(a);
   if (st != GDN_OK) return st;
-  const size_t need = order_bytes(a);
+  const size_t obytes = order_bytes(a);
+  const KeyLayout L = key_layout(a);
+  const size_t need = obytes + L.total();
   if (need && (!a->workspace || a->workspace_bytes < need || !aligned(a->workspace, 256)))
     return GDN_ERR_WORKSPACE;
   if (a->N == 0) return GDN_OK;
@@ -98,16 +123,42 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
   p.final_state = a->final_state;
   p.o = a->o;
   p.cu_seqlens = a->cu_seqlens;
-  p.order = need ? (const int32_t *)a->workspace : nullptr;
+  p.order = obytes ? (const int32_t *)a->workspace : nullptr;
+  p.k_hat = nullptr;
+  p.tp_img = nullptr;
+  p.egc = nullptr;
   p.N = a->N;
   p.H = a->H;
   p.T = a->T;
   p.dv = a->d_v;
-  if (need) {
+  if (obytes) {
     if (gdn::launch_seq_order(a->cu_seqlens, a->N, (int32_t *)a->workspace, stream) != hipSuccess)
       return GDN_ERR_HIP;
   }
-  const bool pipe = a->dtype == GDN_BF16 && a->d_k == 128 && a->gate != GDN_GATE_KEY;
+  if (L.slots) {
+    char *ws = (char *)a->workspace + obytes;
+    gdn::KeyPrepParams kp;
+    kp.q = a->q;
+    kp.k = a->k;
+    kp.beta = a->beta;
+    kp.log_alpha = a->log_alpha;
+    kp.cu_seqlens = a->cu_seqlens;
+    kp.k_g = ws;
+    kp.q_g = ws + L.kq;
+    kp.k_hat = ws + 2 * L.kq;
+    kp.tp_img = ws + 3 * L.kq;
+    kp.egc = (float *)(ws + 3 * L.kq + L.tp);
+    kp.N = a->N;
+    kp.H = a->H;
+    kp.T = a->T;
+    if (gdn::launch_key_prep(kp, L.slots, stream) != hipSuccess) return GDN_ERR_HIP;
+    p.k = kp.k_g;  // the pipelined kernel then reads the pre-scaled operands
+    p.q = kp.q_g;
+    p.k_hat = kp.k_hat;
+    p.tp_img = kp.tp_img;
+    p.egc = kp.egc;
+  }
+  const bool pipe = a->dtype == GDN_BF16 && a->d_k == 128;
   if (pipe) {
     p.nb = a->d_v / 64;
     if (gdn::launch_fwd_pipe(p, (int)a->gate, stream) != hipSuccess) return GDN_ERR_HIP;

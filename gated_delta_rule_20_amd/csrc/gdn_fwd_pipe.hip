@@ -142,7 +142,7 @@ __device__ __forceinline__ float readlane(float x, int l) {
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 struct Res {
-  __amdgpu_buffer_rsrc_t k, q, v, beta, la;
+  __amdgpu_buffer_rsrc_t k, q, v, beta, la, kh;
   uint32_t row_qk, row_v, row_s;  // bytes between consecutive tokens
 };
 
@@ -158,6 +158,30 @@ __device__ __forceinline__ void load_kq(const Res &rs, char *dst, int chunk, int
     const uint32_t vo = r * rs.row_qk + ch * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(q ? rs.q : rs.k, (lds_void_t *)(d + n * 1024), 16, vo, soff, 0, 0);
   }
+}
+// K e^{g_C - G} of a chunk (per-key-channel gate), in the layout of K
+__device__ __forceinline__ void load_kh(const Res &rs, char *dst, int chunk, int lane) {
+  const uint32_t soff = (uint32_t)chunk * C * rs.row_qk;
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const int r = 4 * n + (lane >> 4);
+    const int ch = (lane & 15) ^ kq_swz(r & 15);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.kh, (lds_void_t *)(dst + n * 1024), 16, r * rs.row_qk + ch * 16, soff, 0, 0);
+  }
+}
+// `bytes` (a multiple of 1 KiB) copied verbatim from `src` into LDS
+template <int BYTES>
+__device__ __forceinline__ void load_linear(const void *src, char *dst, int lane) {
+  static_assert(BYTES % 1024 == 0, "whole 1 KiB rows");
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, BYTES, 0x00020000);
+#pragma unroll
+  for (int n = 0; n < BYTES / 1024; ++n)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + n * 1024), 16, n * 1024 + lane * 16, 0, 0, 0);
+}
+__device__ __forceinline__ void load_egc(const float *src, float *dst, int lane) {  // 128 floats
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, 512, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 4, lane * 4, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + 64), 4, 256 + lane * 4, 0, 0, 0);
 }
 __device__ __forceinline__ void load_v(const Res &rs, char *dst, int chunk, int lane) {
   const uint32_t soff = (uint32_t)chunk * C * rs.row_v;
@@ -337,6 +361,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     rs.beta = __builtin_amdgcn_make_buffer_rsrc((void *)(p.beta + (size_t)tok0 * H + h), 0, ns, 0x00020000);
     rs.la = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(GATE == GATE_HEAD ? p.log_alpha + (size_t)tok0 * H + h : p.beta), 0, GATE == GATE_HEAD ? ns : 0, 0x00020000);
+    rs.kh = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(GATE == GATE_KEY ? (const bf16 *)p.k_hat + ((size_t)tok0 * H + h) * DK : (const bf16 *)p.k), 0,
+        GATE == GATE_KEY ? nk : 0, 0x00020000);
   }
 
   auto KQ = [&](int i) { return smem + OFF_KQ + i * KQ_BYTES; };
@@ -344,13 +371,47 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   auto BL = [&](int i) { return smem + OFF_BL + i * BL_BYTES; };
   auto PRE = [&](int i) { return smem + OFF_PRE + i * PRE_BYTES; };
   auto GV = [&](int i) { return (float *)(smem + OFF_GV + i * GV_BYTES); };
+  // per-key-channel gate: K e^{g_C - G} in the third K/Q stage (two 16 KiB halves)
+  auto KH = [&](int i) { return smem + OFF_KQ + 2 * KQ_BYTES + i * (C * DK * 2); };
   char *AD = smem + OFF_AD, *AO = smem + OFF_AO;
   char *TD = AD;  // unscaled diagonal blocks of T (bf16 [64][16]) overwrite A's diagonal blocks
 
   // ---- prologue: zero T and P of both stages (their upper blocks stay zero) and the
   // T builders' flags
-  for (int i = tid; i < 2 * (PRE_BYTES / 16); i += NT) ((uint4 *)PRE(0))[i] = make_uint4(0, 0, 0, 0);
+  if (GATE != GATE_KEY)
+    for (int i = tid; i < 2 * (PRE_BYTES / 16); i += NT) ((uint4 *)PRE(0))[i] = make_uint4(0, 0, 0, 0);
   if (tid < 4) ((int *)(smem + OFF_FLAGS))[tid] = 0;
+
+  if (GATE == GATE_KEY && (wave & 3) >= 2) {
+    // ===================== per-key-channel gate: the chunk operands were prepared
+    // in HBM (launch_key_prep), so the four producer waves only load chunk c + 1
+    // while the state waves work on chunk c (every buffer two stages deep)
+    const long slot0 = (tok0 >> 6) + n;  // slot of this sequence's chunk 0
+    auto ld_chunk = [&](int cc, int st) {
+      if (wave == W_TA) {
+        load_kq(rs, KQ(st), cc, lane, false);  // K e^G
+      } else if (wave == W_TB) {
+        load_kq(rs, KQ(st), cc, lane, true);   // Q e^G
+      } else if (wave == W_PA) {
+        load_kh(rs, KH(st), cc, lane);         // K e^{g_C - G}
+      } else {
+        const size_t sl = (size_t)(slot0 + cc) * H + h;
+        load_v(rs, VB(st), cc, lane);
+        load_linear<PRE_BYTES>((const char *)p.tp_img + sl * PRE_BYTES, PRE(st), lane);
+        load_egc(p.egc + sl * DK, GV(st), lane);
+      }
+    };
+    if (nchunks > 0) ld_chunk(0, 0);
+    wait_vm0();
+    __syncthreads();
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      if (c + 1 < nchunks) ld_chunk(c + 1, (c + 1) & 1);
+      wait_vm0();
+      __syncthreads();
+    }
+    return;
+  }
 
   if ((wave & 3) >= 2) {
     // ===================== producer waves: everything of the next chunk that does
@@ -694,17 +755,21 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   // T/P: 2), so every LDS address is a lane base plus a uniform offset plus a constant
   int ring3 = 0, ring2 = 0;
   for (int c = 0; c < nchunks; ++c) {
-    const char *Ks = smem + OFF_KQ + ring3 * KQ_BYTES;
+    // (per-key-channel gate: two stages of everything; K holds K e^G, Q holds Q e^G
+    // and the update reads K e^{g_C - G}; gv holds e^{g_C} per key channel)
+    constexpr bool KP = GATE == GATE_KEY;
+    const char *Ks = smem + OFF_KQ + (KP ? ring2 : ring3) * KQ_BYTES;
+    const char *Kh = KP ? smem + OFF_KQ + 2 * KQ_BYTES + ring2 * (C * DK * 2) : Ks;
     const char *Vs = smem + OFF_V + ring2 * V_BYTES + vl;
     const char *pre = smem + OFF_PRE + ring2 * PRE_BYTES;
-    const float *gv = (const float *)(smem + OFF_GV + ring3 * GV_BYTES);
+    const float *gv = (const float *)(smem + OFF_GV + (KP ? ring2 : ring3) * GV_BYTES);
     ring3 = ring3 == 2 ? 0 : ring3 + 1;
     ring2 ^= 1;
     const char *kqb[4], *ktb[4], *tb[2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       kqb[q] = Ks + kql[q];
-      ktb[q] = Ks + ktl[q];
+      ktb[q] = Kh + ktl[q];
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) tb[q] = pre + tpl[q];
@@ -737,7 +802,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     }
     // ---- O^T = M_hat^T Q^T, with the V / decay scaling of X and its B fragments in
     // the MFMA gaps: X <- V - Gam e^g X (beta is folded into T)
-    const float Gn = gv[GV_GN];
+    const float Gn = KP ? 1.f : gv[GV_GN];
     const bool eager = (GATE == GATE_HEAD) && gv[GV_EAGER] != 0.f;
     f32x4 OT[4];
 #pragma unroll
@@ -760,9 +825,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       if (st < 2) {
 #pragma unroll
         for (int i = 2 * st; i < 2 * st + 2; ++i) {
-          const f32x4 eg4 = *(const f32x4 *)(gv + GV_EGS + 16 * i + 4 * lg);
+          if (KP) {  // K e^G already carries the row decay
 #pragma unroll
-          for (int j = 0; j < 4; ++j) X[i][j] = (float)vv[i][j] - eg4[j] * X[i][j];
+            for (int j = 0; j < 4; ++j) X[i][j] = (float)vv[i][j] - X[i][j];
+          } else {
+            const f32x4 eg4 = *(const f32x4 *)(gv + GV_EGS + 16 * i + 4 * lg);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) X[i][j] = (float)vv[i][j] - eg4[j] * X[i][j];
+          }
         }
       } else if (st == 2) {
 #pragma unroll
@@ -796,16 +866,25 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     };
     ld_kt(0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) OT[i] *= gv[GV_EGS + 16 * i + lm];
+    for (int i = 0; i < 4; ++i)
+      if (!KP) OT[i] *= gv[GV_EGS + 16 * i + lm];
     __builtin_amdgcn_sched_barrier(0);
     // DA: Delta as the A operand of O^T += Delta^T P^T;  DT: diag(e^{g_C - g}) Delta / Gam
     bf16x8 DA[2], DT[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const f32x4 ec0 = *(const f32x4 *)(gv + GV_EGCW + 32 * s2 + 4 * lg);
-      const f32x4 ec1 = *(const f32x4 *)(gv + GV_EGCW + 32 * s2 + 16 + 4 * lg);
       DA[s2] = frag_from_c<bf16>(D[2 * s2], D[2 * s2 + 1]);
-      DT[s2] = frag_from_c<bf16>(D[2 * s2] * ec0, D[2 * s2 + 1] * ec1);
+      if (KP) {  // K e^{g_C - G} already carries the write decay
+        DT[s2] = DA[s2];
+      } else {
+        const f32x4 ec0 = *(const f32x4 *)(gv + GV_EGCW + 32 * s2 + 4 * lg);
+        const f32x4 ec1 = *(const f32x4 *)(gv + GV_EGCW + 32 * s2 + 16 + 4 * lg);
+        DT[s2] = frag_from_c<bf16>(D[2 * s2] * ec0, D[2 * s2 + 1] * ec1);
+      }
+    }
+    if (KP) {  // per-key-channel decay of the state rows: M <- diag(e^{g_C}) M
+#pragma unroll
+      for (int t = 0; t < 8; ++t) M[t] *= *(const f32x4 *)(gv + 32 * (t >> 1) + 8 * lg + 4 * (t & 1));
     }
     if (eager) {
 #pragma unroll
@@ -848,6 +927,232 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   }
 }
 
+// ===================== per-key-channel gate: chunk preparation =====================
+// One workgroup (4 waves) per (chunk slot, head); every chunk independently.  With the
+// chunk-local per-channel prefix G[r][d] = sum_{i <= r} log alpha[i][d] (the gate of
+// "Decoding Hybrid Linear Attention Architectures", sec. 3, one decay per key channel,
+// accumulated in log space):
+//   outputs K e^G, Q e^G, K e^{g_C - G} (bf16, token-major like K) and e^{g_C};
+//   A[r][i] = beta_r sum_d K[r][d] K[i][d] e^{G[r][d] - G[i][d]}  (i < r),
+//   P[r][i] =        sum_d Q[r][d] K[i][d] e^{G[r][d] - G[i][d]}  (i <= r),
+// with the pairwise factor split at row m = 16a + 7 of the row block a (e^{G[r] - G[m]}
+// on the row operand, e^{G[m] - G[i]} on the column operand, so neither exceeds the
+// decay over the rows between them); T = (I + A)^-1 by forward substitution of the
+// diagonal blocks in fp32 and block substitution on MFMA; T diag(beta) and P leave as
+// the 16 KiB LDS images the pipelined kernel loads (tp_off layout).
+constexpr int KP_NT = 256;
+constexpr int KP_SG = 132;  // row stride of G (floats)
+constexpr int KP_SK = 136;  // row stride of K, Q (bf16)
+constexpr int KP_ST = 72;   // row stride of the 64-wide bf16 matrices A, T
+constexpr int KP_OFF_G = 0;                              // G [64][132] fp32, later T [64][72]
+constexpr int KP_OFF_K = KP_OFF_G + C * KP_SG * 4;
+constexpr int KP_OFF_Q = KP_OFF_K + C * KP_SK * 2;
+constexpr int KP_OFF_A = KP_OFF_Q + C * KP_SK * 2;       // off-diagonal blocks of A
+constexpr int KP_OFF_AD = KP_OFF_A + C * KP_ST * 2;      // diagonal blocks of A, fp32
+constexpr int KP_OFF_IMG = KP_OFF_AD + 4 * 16 * 16 * 4;  // T diag(beta) at 0, P at PRE_P
+constexpr int KP_OFF_BETA = KP_OFF_IMG + PRE_BYTES;
+constexpr int KP_BYTES = KP_OFF_BETA + C * 4;
+static_assert(C * KP_ST * 2 <= C * KP_SG * 4, "T reuses the space of G");
+// the ten lower 16x16 tiles and the wave that builds each
+constexpr int KT_A[10] = {0, 3, 3, 1, 1, 3, 2, 2, 2, 3};
+constexpr int KT_B[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+constexpr int KT_W[10] = {0, 0, 0, 1, 1, 1, 2, 2, 3, 3};
+
+__global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p) {
+  __shared__ __align__(16) char smem[KP_BYTES];
+  float *Gs = (float *)(smem + KP_OFF_G);
+  bf16 *Ks = (bf16 *)(smem + KP_OFF_K), *Qs = (bf16 *)(smem + KP_OFF_Q);
+  bf16 *As = (bf16 *)(smem + KP_OFF_A);
+  float *AD = (float *)(smem + KP_OFF_AD);
+  char *img = smem + KP_OFF_IMG;
+  float *bs = (float *)(smem + KP_OFF_BETA);
+  bf16 *Ts = (bf16 *)(smem + KP_OFF_G);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lm = lane & 15;
+  const long slot = blockIdx.x;
+  const int h = blockIdx.y, H = p.H;
+
+  // the sequence owning this slot: the last one whose first slot is <= slot
+  auto tok_start = [&](int sq) -> long { return p.cu_seqlens ? (long)p.cu_seqlens[sq] : (long)sq * p.T; };
+  int lo = 0, hi = p.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((tok_start(mid) >> 6) + mid <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  const int n = lo;
+  const long tok0 = tok_start(n);
+  const long tend = p.cu_seqlens ? (long)p.cu_seqlens[n + 1] : tok0 + p.T;
+  if (tok0 < 0 || tend < tok0 || (p.cu_seqlens && tend > p.T)) return;  // malformed offsets
+  const long c = slot - ((tok0 >> 6) + n);
+  if (c < 0 || 64 * c >= tend - tok0) return;  // a slot that no chunk owns
+  const int nv = (int)min(64L, tend - tok0 - 64 * c);
+  const long t0 = tok0 + 64 * c;
+
+  // ---- loads: log alpha -> per-channel prefix (two halves of 32 rows), K, Q, beta;
+  // rows past the sequence end are zero (log alpha = 0 keeps the prefix)
+  {
+    const int d = tid & 127, half = tid >> 7;
+    const float *la = p.log_alpha + ((size_t)t0 * H + h) * DK + d;
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int r = 32 * half + i;
+      x[i] = r < nv ? la[(size_t)r * H * DK] : 0.f;
+    }
+#pragma unroll
+    for (int i = 1; i < 32; ++i) x[i] += x[i - 1];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) Gs[(32 * half + i) * KP_SG + d] = x[i];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = (tid >> 4) + 16 * u, g = tid & 15;
+    u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+    if (r < nv) {
+      const size_t o = ((size_t)(t0 + r) * H + h) * DK + 8 * g;
+      kv = *(const u32x4 *)((const bf16 *)p.k + o);
+      qv = *(const u32x4 *)((const bf16 *)p.q + o);
+    }
+    *(u32x4 *)(Ks + r * KP_SK + 8 * g) = kv;
+    *(u32x4 *)(Qs + r * KP_SK + 8 * g) = qv;
+  }
+  if (tid < C) bs[tid] = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
+  for (int i = tid; i < PRE_BYTES / 16; i += KP_NT) ((uint4 *)img)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < C * KP_ST * 2 / 16; i += KP_NT) ((uint4 *)As)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  if (tid >= 128) {
+    const int d = tid & 127;
+    const float base = Gs[31 * KP_SG + d];
+#pragma unroll
+    for (int i = 32; i < 64; ++i) Gs[i * KP_SG + d] += base;
+  }
+  __syncthreads();
+
+  // ---- pre-scaled operands of the state phase, and e^{g_C}
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = (tid >> 4) + 16 * u, g = tid & 15;
+    if (r < nv) {
+      const float *gr = Gs + r * KP_SG + 8 * g, *gc = Gs + 63 * KP_SG + 8 * g;
+      const bf16x8 kv = *(const bf16x8 *)(Ks + r * KP_SK + 8 * g);
+      const bf16x8 qv = *(const bf16x8 *)(Qs + r * KP_SK + 8 * g);
+      bf16x8 kg, qg, kh;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float e = __expf(gr[j]), w = __expf(gc[j] - gr[j]);
+        kg[j] = (bf16)((float)kv[j] * e);
+        qg[j] = (bf16)((float)qv[j] * e);
+        kh[j] = (bf16)((float)kv[j] * w);
+      }
+      const size_t o = ((size_t)(t0 + r) * H + h) * DK + 8 * g;
+      *(bf16x8 *)((bf16 *)p.k_g + o) = kg;
+      *(bf16x8 *)((bf16 *)p.q_g + o) = qg;
+      *(bf16x8 *)((bf16 *)p.k_hat + o) = kh;
+    }
+  }
+  if (tid < DK) p.egc[((size_t)slot * H + h) * DK + tid] = __expf(Gs[63 * KP_SG + tid]);
+
+  // ---- Gram tiles of A and P (reads G, K, Q only, so no barrier before it)
+#pragma unroll
+  for (int ti = 0; ti < 10; ++ti) {
+    if (wave != KT_W[ti]) continue;
+    const int a = KT_A[ti], b = KT_B[ti];
+    const int ra = 16 * a + lm, rb = 16 * b + lm, m = 16 * a + 7;
+    f32x4 kk = zero4(), qk = zero4();
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int ch = 32 * s4 + 8 * lg;
+      const bf16x8 kav = *(const bf16x8 *)(Ks + ra * KP_SK + ch);
+      const bf16x8 qav = *(const bf16x8 *)(Qs + ra * KP_SK + ch);
+      const bf16x8 kbv = *(const bf16x8 *)(Ks + rb * KP_SK + ch);
+      const float *gr = Gs + ra * KP_SG + ch, *gm = Gs + m * KP_SG + ch, *gi = Gs + rb * KP_SG + ch;
+      bf16x8 ak, aq, bk;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ea = __expf(gr[j] - gm[j]), eb = __expf(gm[j] - gi[j]);
+        ak[j] = (bf16)((float)kav[j] * ea);
+        aq[j] = (bf16)((float)qav[j] * ea);
+        bk[j] = (bf16)((float)kbv[j] * eb);
+      }
+      kk = mma(ak, bk, kk);
+      qk = mma(aq, bk, qk);
+    }
+    // lane: column i = 16b + lm, rows r = 16a + 4lg + j
+    const int i = 16 * b + lm;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * a + 4 * lg + j;
+      const float av = i < r ? bs[r] * kk[j] : 0.f;
+      if (a == b) AD[(16 * a + 4 * lg + j) * 16 + lm] = av;
+      else As[r * KP_ST + i] = (bf16)av;
+      *(bf16 *)(img + PRE_P + tp_off(r, i)) = (bf16)(i <= r ? qk[j] : 0.f);
+    }
+  }
+  __syncthreads();
+
+  // ---- diagonal blocks of T: lane (lg, lm) solves column lm of block lg in fp32
+  if (wave == 0) {
+    const float *ad = AD + lg * 256;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = r == lm ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc -= ad[r * 16 + i] * x[i];
+      x[r] = acc;
+    }
+    const int col = 16 * lg + lm;
+    const float bc = bs[col];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 16 * lg + r;
+      Ts[row * KP_ST + col] = (bf16)x[r];
+      *(bf16 *)(img + tp_off(row, col)) = (bf16)(x[r] * bc);
+    }
+  }
+  __syncthreads();
+  // ---- off-diagonal blocks: T[a][b] = -T[a][a] sum_{k=b}^{a-1} A[a][k] T[k][b];
+  // wave b walks block column b downwards with T[k][b] kept as C tiles
+  if (wave < 3) {
+    const int b = wave;
+    const float bc = bs[16 * b + lm];
+    f32x4 Tc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      Tc[k] = zero4();
+      if (k == b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Tc[k][j] = (float)Ts[(16 * k + 4 * lg + j) * KP_ST + 16 * k + lm];
+    }
+#pragma unroll
+    for (int a = 1; a < 4; ++a) {
+      if (a > b) {
+        f32x4 y = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < 4; k0 += 2) {
+          const bool in0 = (k0 >= b && k0 < a), in1 = (k0 + 1 >= b && k0 + 1 < a);
+          if (in0 || in1) {
+            const bf16x8 bf = frag_from_c<bf16>(in0 ? Tc[k0] : zero4(), in1 ? Tc[k0 + 1] : zero4());
+            const bf16 *ar = As + (16 * a + lm) * KP_ST + 16 * k0 + 4 * lg;
+            y = mma(ld4x2(ar, ar + 16), bf, y);
+          }
+        }
+        const bf16x8 tf = ld4z(Ts + (16 * a + lm) * KP_ST + 16 * a + 4 * lg);
+        const f32x4 z = mma(tf, frag_from_c_half<bf16>(y), zero4());
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Tc[a][j] = -z[j];
+          *(bf16 *)(img + tp_off(16 * a + 4 * lg + j, 16 * b + lm)) = (bf16)(-z[j] * bc);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  char *dst = (char *)p.tp_img + ((size_t)slot * H + h) * PRE_BYTES;
+  for (int i = tid; i < PRE_BYTES / 16; i += KP_NT) ((uint4 *)dst)[i] = ((const uint4 *)img)[i];
+}
+
 }  // namespace
 
 hipError_t launch_fwd_pipe(const FwdParams &p, int gate, hipStream_t stream) {
@@ -856,8 +1161,15 @@ hipError_t launch_fwd_pipe(const FwdParams &p, int gate, hipStream_t stream) {
   switch (gate) {
     case GATE_NONE: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_NONE>), dim3(blocks), dim3(NT), 0, stream, p); break;
     case GATE_HEAD: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_HEAD>), dim3(blocks), dim3(NT), 0, stream, p); break;
+    case GATE_KEY: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_KEY>), dim3(blocks), dim3(NT), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_key_prep(const KeyPrepParams &p, long slots, hipStream_t stream) {
+  if (slots <= 0 || p.N <= 0 || p.H <= 0) return hipSuccess;
+  hipLaunchKernelGGL(key_prep_kernel, dim3((unsigned)slots, (unsigned)p.H), dim3(KP_NT), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -20,7 +20,16 @@ struct FwdParams {
   int T;                         // tokens per batch row, or packed total (varlen)
   int dv;                        // full d_v
   int nb;                        // number of d_v blocks per (sequence, head)
+  // Per-key-channel gate on the pipelined kernel: operands prepared per chunk by
+  // launch_key_prep (q and k then point at the pre-scaled Q e^G and K e^G).
+  const void *k_hat;             // [tokens, H, d_k] K e^{g_C - G}
+  const void *tp_img;            // [slots, H] 16 KiB LDS images of T diag(beta) and P
+  const float *egc;              // [slots, H, d_k] e^{g_C} per key channel
 };
+
+// Chunk slots of the per-key-channel preparation: chunk c of sequence n (first token
+// t0) is slot floor(t0 / 64) + c + n, unique and below floor(total / 64) + N.
+inline long key_slots(long total_tokens, int N) { return total_tokens / 64 + N; }
 
 struct StepParams {
   const void *q, *k, *v;
@@ -34,9 +43,23 @@ struct StepParams {
 // dvb: columns of d_v per workgroup (32 or 64).
 hipError_t launch_fwd_fused(const FwdParams &p, int dtype, int dk, int dvb, int gate,
                             hipStream_t stream);
-// Software-pipelined forward for bf16, d_k = 128, 64-column value blocks (nb = d_v / 64),
-// gate NONE or HEAD.
+// Software-pipelined forward for bf16, d_k = 128, 64-column value blocks (nb = d_v / 64).
+// Gate NONE or HEAD; gate KEY after launch_key_prep, with the k_hat, tp_img, egc fields.
 hipError_t launch_fwd_pipe(const FwdParams &p, int gate, hipStream_t stream);
+// Per-key-channel gate, bf16, d_k = 128: for every chunk (all in parallel) the
+// pre-scaled operands K e^G, Q e^G, K e^{g_C - G}, e^{g_C}, and T diag(beta) and P as
+// the LDS images the pipelined kernel loads.
+struct KeyPrepParams {
+  const void *q, *k;             // [tokens, H, 128] bf16
+  const float *beta;             // [tokens, H]
+  const float *log_alpha;        // [tokens, H, 128]
+  const int32_t *cu_seqlens;     // NULL | [N + 1]
+  void *q_g, *k_g, *k_hat;       // [tokens, H, 128] bf16 outputs
+  void *tp_img;                  // [slots, H, 16384 B]
+  float *egc;                    // [slots, H, 128]
+  int N, H, T;
+};
+hipError_t launch_key_prep(const KeyPrepParams &p, long slots, hipStream_t stream);
 hipError_t launch_seq_order(const int32_t *cu_seqlens, int N, int32_t *order, hipStream_t stream);
 hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate,
                                  hipStream_t stream);

@@ -119,9 +119,15 @@ typedef struct {
   void *o;                /* out: [N, H, d_v], dtype                                 */
 } gdn_step_args;
 
-/* Bytes of device workspace gdn_fwd_chunked needs for these arguments (depends on
- * N, H and whether cu_seqlens is given; 0 means none).  Returns 0 for arguments
- * that gdn_fwd_chunked would reject. */
+/* Bytes of device workspace gdn_fwd_chunked needs for these arguments; 0 means none.
+ * Returns 0 for arguments that gdn_fwd_chunked would reject.
+ *   - with cu_seqlens (N <= 8192): a processing-order table, 4 N bytes rounded up to 256;
+ *   - bf16 with d_k = 128 and the per-key-channel gate: the chunk operands prepared in
+ *     a first, fully parallel pass (K e^G, Q e^G and K e^{g_C - G}: 3 x 256 bytes per
+ *     token and head; T diag(beta) and P: 16 KiB, e^{g_C}: 512 bytes per chunk slot and
+ *     head, with floor(B T / 64) + N slots), each part rounded up to 256 bytes.
+ * The workspace is owned by the caller; its contents need no initialisation and are
+ * meaningless after the call. */
 size_t gdn_fwd_workspace_size(const gdn_fwd_args *args);
 
 /* Chunked forward: writes o (and final_state when non-NULL). */
