@@ -34,6 +34,12 @@
 // are triple-buffered, V and T/P double-buffered; one workgroup barrier per chunk
 // separates producers and consumers.
 //
+// Per-key-channel gate (one decay per key channel): key_prep_kernel (at the end of
+// this file) first prepares every chunk in parallel -- K e^G, Q e^G, K e^{g_C - G},
+// e^{g_C}, and T diag(beta) and P as LDS images -- and fwd_pipe_kernel<GATE_KEY> then
+// runs the same state waves on them, its four producer waves only loading (two
+// stages of every buffer), and the state rows decaying by e^{g_C} per channel.
+//
 // LDS layouts are XOR-swizzled instead of padded: K/Q rows of 256 B in 16-byte units
 // (unit ^ kq_swz(row)), V rows of 128 B (unit ^ (row & 7)), T/P rows of 128 B with
 // permuted columns so each MFMA fragment is one 16-byte unit.  K^T and V fragments
@@ -941,27 +947,41 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
 // diagonal blocks in fp32 and block substitution on MFMA; T diag(beta) and P leave as
 // the 16 KiB LDS images the pipelined kernel loads (tp_off layout).
 constexpr int KP_NT = 256;
-constexpr int KP_SG = 132;  // row stride of G (floats)
-constexpr int KP_SK = 136;  // row stride of K, Q (bf16)
+constexpr int KP_SG = 132;  // row stride of the fp32 [64][128] tables (floats)
+constexpr int KP_SK = 136;  // row stride of the bf16 [64][128] operands
 constexpr int KP_ST = 72;   // row stride of the 64-wide bf16 matrices A, T
-constexpr int KP_OFF_G = 0;                              // G [64][132] fp32, later T [64][72]
-constexpr int KP_OFF_K = KP_OFF_G + C * KP_SG * 4;
-constexpr int KP_OFF_Q = KP_OFF_K + C * KP_SK * 2;
-constexpr int KP_OFF_A = KP_OFF_Q + C * KP_SK * 2;       // off-diagonal blocks of A
-constexpr int KP_OFF_AD = KP_OFF_A + C * KP_ST * 2;      // diagonal blocks of A, fp32
+constexpr int KP_OP = C * KP_SK * 2;
+constexpr int KP_OFF_G = 0;                         // G, then e^{G[e] - G}, then T [64][72]
+constexpr int KP_OFF_K = KP_OFF_G + C * KP_SG * 4;  // K
+constexpr int KP_OFF_QA = KP_OFF_K + KP_OP;         // Q, then Q e^{G - G[m]} in place
+constexpr int KP_OFF_KA = KP_OFF_QA + KP_OP;        // K e^{G - G[m]}   (row operands)
+constexpr int KP_OFF_KD = KP_OFF_KA + KP_OP;        // K e^{G[m] - G}   (diagonal column operands)
+constexpr int KP_OFF_F = KP_OFF_KD + KP_OP;         // F[ab][d] = e^{G[m_a] - G[e_b]}, a > b
+constexpr int KP_OFF_BC = KP_OFF_F + 6 * DK * 4;    // e^{G[m_a]} [4][128], e^{g_C - G[e_a]} [4][128]
+constexpr int KP_OFF_A = KP_OFF_BC + 8 * DK * 4;    // off-diagonal blocks of A
+constexpr int KP_OFF_AD = KP_OFF_A + C * KP_ST * 2; // diagonal blocks of A, fp32
 constexpr int KP_OFF_IMG = KP_OFF_AD + 4 * 16 * 16 * 4;  // T diag(beta) at 0, P at PRE_P
 constexpr int KP_OFF_BETA = KP_OFF_IMG + PRE_BYTES;
 constexpr int KP_BYTES = KP_OFF_BETA + C * 4;
 static_assert(C * KP_ST * 2 <= C * KP_SG * 4, "T reuses the space of G");
+static_assert(KP_BYTES <= 160 * 1024, "LDS budget");
 // the ten lower 16x16 tiles and the wave that builds each
 constexpr int KT_A[10] = {0, 3, 3, 1, 1, 3, 2, 2, 2, 3};
 constexpr int KT_B[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 constexpr int KT_W[10] = {0, 0, 0, 1, 1, 1, 2, 2, 3, 3};
 
+// Every factor is an exponential of a difference of prefixes over at most one 16-row
+// block, or a product of such factors formed in fp32 (so each operand is rounded to
+// bf16 once):  with m = 16a + 7 and e = 16a + 15 of row r's block a,
+//   e^{G[r]}         = e^{G[m]} e^{G[r] - G[m]},  e^{g_C - G[r]} = e^{g_C - G[e]} e^{G[e] - G[r]},
+//   e^{G[m_a] - G[i]} = F[a][b] e^{G[e_b] - G[i]}  for a column row i of a block b < a.
 __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p) {
   __shared__ __align__(16) char smem[KP_BYTES];
   float *Gs = (float *)(smem + KP_OFF_G);
-  bf16 *Ks = (bf16 *)(smem + KP_OFF_K), *Qs = (bf16 *)(smem + KP_OFF_Q);
+  float *Et = Gs;  // e^{G[e] - G}, after the prefix is no longer read
+  bf16 *Ks = (bf16 *)(smem + KP_OFF_K), *QA = (bf16 *)(smem + KP_OFF_QA);
+  bf16 *KA = (bf16 *)(smem + KP_OFF_KA), *KD = (bf16 *)(smem + KP_OFF_KD);
+  float *Fs = (float *)(smem + KP_OFF_F), *Bc = (float *)(smem + KP_OFF_BC);
   bf16 *As = (bf16 *)(smem + KP_OFF_A);
   float *AD = (float *)(smem + KP_OFF_AD);
   char *img = smem + KP_OFF_IMG;
@@ -1015,7 +1035,7 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p) {
       qv = *(const u32x4 *)((const bf16 *)p.q + o);
     }
     *(u32x4 *)(Ks + r * KP_SK + 8 * g) = kv;
-    *(u32x4 *)(Qs + r * KP_SK + 8 * g) = qv;
+    *(u32x4 *)(QA + r * KP_SK + 8 * g) = qv;
   }
   if (tid < C) bs[tid] = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
   for (int i = tid; i < PRE_BYTES / 16; i += KP_NT) ((uint4 *)img)[i] = make_uint4(0, 0, 0, 0);
@@ -1029,51 +1049,86 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p) {
   }
   __syncthreads();
 
-  // ---- pre-scaled operands of the state phase, and e^{g_C}
+  // ---- per-block constants, the cross-block factors F, and e^{g_C}
+  for (int i = tid; i < 8 * DK + 6 * DK; i += KP_NT) {
+    const int d = i & (DK - 1), k = i >> 7;
+    const float gC = Gs[63 * KP_SG + d];
+    if (k < 4) {
+      Bc[k * DK + d] = __expf(Gs[(16 * k + 7) * KP_SG + d]);
+    } else if (k < 8) {
+      Bc[k * DK + d] = __expf(gC - Gs[(16 * (k - 4) + 15) * KP_SG + d]);
+    } else {
+      const int ab = k - 8, a = OA[ab], b = OB[ab];
+      Fs[ab * DK + d] = __expf(Gs[(16 * a + 7) * KP_SG + d] - Gs[(16 * b + 15) * KP_SG + d]);
+    }
+  }
+  if (tid < DK) p.egc[((size_t)slot * H + h) * DK + tid] = __expf(Gs[63 * KP_SG + tid]);
+  __syncthreads();
+
+  // ---- operands: row operands K e^{G - G[m]}, Q e^{G - G[m]}, diagonal column operand
+  // K e^{G[m] - G}, the tail factors e^{G[e] - G}, and the state-phase outputs
+  f32x4 etk[4][2];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int r = (tid >> 4) + 16 * u, g = tid & 15;
-    if (r < nv) {
-      const float *gr = Gs + r * KP_SG + 8 * g, *gc = Gs + 63 * KP_SG + 8 * g;
-      const bf16x8 kv = *(const bf16x8 *)(Ks + r * KP_SK + 8 * g);
-      const bf16x8 qv = *(const bf16x8 *)(Qs + r * KP_SK + 8 * g);
-      bf16x8 kg, qg, kh;
+    const int r = (tid >> 4) + 16 * u, g = tid & 15, blk = r >> 4;
+    const float *gr = Gs + r * KP_SG + 8 * g, *gm = Gs + (16 * blk + 7) * KP_SG + 8 * g;
+    const float *ge = Gs + (16 * blk + 15) * KP_SG + 8 * g;
+    const float *bm = Bc + blk * DK + 8 * g, *bt = Bc + (4 + blk) * DK + 8 * g;
+    const bf16x8 kv = *(const bf16x8 *)(Ks + r * KP_SK + 8 * g);
+    const bf16x8 qv = *(const bf16x8 *)(QA + r * KP_SK + 8 * g);
+    bf16x8 ka, qa, kd, kg, qg, kh;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float e = __expf(gr[j]), w = __expf(gc[j] - gr[j]);
-        kg[j] = (bf16)((float)kv[j] * e);
-        qg[j] = (bf16)((float)qv[j] * e);
-        kh[j] = (bf16)((float)kv[j] * w);
-      }
+    for (int j = 0; j < 8; ++j) {
+      const float eh = __expf(gr[j] - gm[j]), ehi = __expf(gm[j] - gr[j]), et = __expf(ge[j] - gr[j]);
+      etk[u][j >> 2][j & 3] = et;
+      const float kf = (float)kv[j], qf = (float)qv[j];
+      ka[j] = (bf16)(kf * eh);
+      qa[j] = (bf16)(qf * eh);
+      kd[j] = (bf16)(kf * ehi);
+      const float eg = bm[j] * eh, ew = bt[j] * et;
+      kg[j] = (bf16)(kf * eg);
+      qg[j] = (bf16)(qf * eg);
+      kh[j] = (bf16)(kf * ew);
+    }
+    *(bf16x8 *)(KA + r * KP_SK + 8 * g) = ka;
+    *(bf16x8 *)(QA + r * KP_SK + 8 * g) = qa;  // each thread rewrites only its own Q entries
+    *(bf16x8 *)(KD + r * KP_SK + 8 * g) = kd;
+    if (r < nv) {
       const size_t o = ((size_t)(t0 + r) * H + h) * DK + 8 * g;
       *(bf16x8 *)((bf16 *)p.k_g + o) = kg;
       *(bf16x8 *)((bf16 *)p.q_g + o) = qg;
       *(bf16x8 *)((bf16 *)p.k_hat + o) = kh;
     }
   }
-  if (tid < DK) p.egc[((size_t)slot * H + h) * DK + tid] = __expf(Gs[63 * KP_SG + tid]);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = (tid >> 4) + 16 * u, g = tid & 15;
+    *(f32x4 *)(Et + r * KP_SG + 8 * g) = etk[u][0];
+    *(f32x4 *)(Et + r * KP_SG + 8 * g + 4) = etk[u][1];
+  }
+  __syncthreads();
 
-  // ---- Gram tiles of A and P (reads G, K, Q only, so no barrier before it)
+  // ---- Gram tiles of A and P
 #pragma unroll
   for (int ti = 0; ti < 10; ++ti) {
     if (wave != KT_W[ti]) continue;
     const int a = KT_A[ti], b = KT_B[ti];
-    const int ra = 16 * a + lm, rb = 16 * b + lm, m = 16 * a + 7;
+    const int ra = 16 * a + lm, rb = 16 * b + lm;
     f32x4 kk = zero4(), qk = zero4();
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int ch = 32 * s4 + 8 * lg;
-      const bf16x8 kav = *(const bf16x8 *)(Ks + ra * KP_SK + ch);
-      const bf16x8 qav = *(const bf16x8 *)(Qs + ra * KP_SK + ch);
-      const bf16x8 kbv = *(const bf16x8 *)(Ks + rb * KP_SK + ch);
-      const float *gr = Gs + ra * KP_SG + ch, *gm = Gs + m * KP_SG + ch, *gi = Gs + rb * KP_SG + ch;
-      bf16x8 ak, aq, bk;
+      const bf16x8 ak = *(const bf16x8 *)(KA + ra * KP_SK + ch);
+      const bf16x8 aq = *(const bf16x8 *)(QA + ra * KP_SK + ch);
+      bf16x8 bk;
+      if (a == b) {
+        bk = *(const bf16x8 *)(KD + rb * KP_SK + ch);
+      } else {
+        const bf16x8 kbv = *(const bf16x8 *)(Ks + rb * KP_SK + ch);
+        const float *et = Et + rb * KP_SG + ch, *f = Fs + ao_idx(a, b) * DK + ch;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float ea = __expf(gr[j] - gm[j]), eb = __expf(gm[j] - gi[j]);
-        ak[j] = (bf16)((float)kav[j] * ea);
-        aq[j] = (bf16)((float)qav[j] * ea);
-        bk[j] = (bf16)((float)kbv[j] * eb);
+        for (int j = 0; j < 8; ++j) bk[j] = (bf16)((float)kbv[j] * (f[j] * et[j]));
       }
       kk = mma(ak, bk, kk);
       qk = mma(aq, bk, qk);

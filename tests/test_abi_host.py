@@ -119,6 +119,26 @@ def test_workspace_size(g):
     assert g.fwd_workspace_size(base_args(g, chunk=128)) == 0
 
 
+def test_workspace_size_key_gate(g):
+    """bf16, d_k = 128 and the per-key-channel gate: three pre-scaled [tokens, H, 128]
+    bf16 arrays, then 16 KiB of T/P images and 512 B of e^{g_C} per chunk slot and head
+    (floor(B T / 64) + N slots), each part rounded up to 256 bytes."""
+    def expect(tokens, H, N, order=0):
+        up = lambda x: (x + 255) // 256 * 256
+        slots = tokens // 64 + N
+        return order + 3 * up(tokens * H * 256) + up(slots * H * 16384) + up(slots * H * 512)
+    a = base_args(g, gate=g.GDN_GATE_KEY)
+    assert g.fwd_workspace_size(a) == expect(2 * 128, 4, 2)
+    a = base_args(g, gate=g.GDN_GATE_KEY, B=3, T=100, N=3, H=1)
+    assert g.fwd_workspace_size(a) == expect(300, 1, 3)
+    a = base_args(g, gate=g.GDN_GATE_KEY, B=1, T=1000, N=7, cu_seqlens=fake(7))
+    assert g.fwd_workspace_size(a) == expect(1000, 4, 7, order=256)
+    # the other modes that take the per-key-channel gate need no prepared operands
+    assert g.fwd_workspace_size(base_args(g, gate=g.GDN_GATE_KEY, d_k=64)) == 0
+    # and the pass needs that workspace: without it the call is rejected, nothing launched
+    assert fwd(g, base_args(g, gate=g.GDN_GATE_KEY)) == WORKSPACE
+
+
 def step_args(g, **kw):
     a = g.StepArgs(N=4, H=2, d_k=128, d_v=64, dtype=g.GDN_BF16, gate=g.GDN_GATE_KEY)
     a.q, a.k, a.v, a.beta, a.log_alpha, a.state, a.o = (fake(i) for i in range(7))

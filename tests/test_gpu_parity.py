@@ -88,6 +88,31 @@ def test_varlen_small(gdn, gate):
     check(gdn, inp)
 
 
+def test_varlen_key_many_short(gdn):
+    """Per-key-channel gate on packed sequences whose lengths straddle chunk
+    boundaries (1..130 tokens, including empty ones): every chunk slot of the
+    preparation pass is owned by exactly one (sequence, chunk)."""
+    lengths = [1, 63, 64, 65, 0, 127, 128, 129, 2, 70, 0, 130, 5, 64, 33, 97]
+    inp = synth.random_inputs(1, None, 3, 128, 128, "key", "bf16", seed=17, state_std=0.05,
+                              lengths=lengths)
+    check(gdn, inp)
+
+
+def test_key_prepared_call_repeats(gdn):
+    """The per-key-channel gate through PreparedFwd: the workspace holding the
+    prepared chunk operands is reused across launches with identical results."""
+    inp = synth.random_inputs(2, 300, 2, 128, 64, "key", "bf16", seed=23, state_std=0.05)
+    d = to_dev(inp)
+    call = gdn.PreparedFwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"])
+    o1, f1 = call.launch()
+    o1, f1 = o1.clone(), f1.clone()
+    o2, f2 = call.launch()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    o_ref, fs_ref = run_oracle(inp)
+    assert relerr(o2.cpu(), o_ref) <= TOL["bf16"] and relerr(f2.cpu(), fs_ref) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("gate", ["head", "key"])
 @pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("bf16", 64), ("f32", 64)])
 def test_strong_decay(gdn, gate, dtype, dk):
