@@ -946,7 +946,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
 // decay over the rows between them); T = (I + A)^-1 by forward substitution of the
 // diagonal blocks in fp32 and block substitution on MFMA; T diag(beta) and P leave as
 // the 16 KiB LDS images the pipelined kernel loads (tp_off layout).
-constexpr int KP_NT = 256;
+constexpr int KP_NT = 512;  // 8 waves
 constexpr int KP_SG = 132;  // row stride of the fp32 [64][128] tables (floats)
 constexpr int KP_SK = 136;  // row stride of the bf16 [64][128] operands
 constexpr int KP_ST = 72;   // row stride of the 64-wide bf16 matrices A, T
@@ -955,33 +955,43 @@ constexpr int KP_OFF_G = 0;                         // G, then e^{G[e] - G}, the
 constexpr int KP_OFF_K = KP_OFF_G + C * KP_SG * 4;  // K
 constexpr int KP_OFF_QA = KP_OFF_K + KP_OP;         // Q, then Q e^{G - G[m]} in place
 constexpr int KP_OFF_KA = KP_OFF_QA + KP_OP;        // K e^{G - G[m]}   (row operands)
-constexpr int KP_OFF_KD = KP_OFF_KA + KP_OP;        // K e^{G[m] - G}   (diagonal column operands)
-constexpr int KP_OFF_F = KP_OFF_KD + KP_OP;         // F[ab][d] = e^{G[m_a] - G[e_b]}, a > b
-constexpr int KP_OFF_BC = KP_OFF_F + 6 * DK * 4;    // e^{G[m_a]} [4][128], e^{g_C - G[e_a]} [4][128]
+constexpr int KP_OFF_F = KP_OFF_KA + KP_OP;         // F[ab][d] = e^{G[m_a] - G[e_b]}, a >= b
+constexpr int KP_OFF_BC = KP_OFF_F + 10 * DK * 4;   // e^{G[m_a]} [4][128], e^{g_C - G[e_a]} [4][128]
 constexpr int KP_OFF_A = KP_OFF_BC + 8 * DK * 4;    // off-diagonal blocks of A
 constexpr int KP_OFF_AD = KP_OFF_A + C * KP_ST * 2; // diagonal blocks of A, fp32
 constexpr int KP_OFF_IMG = KP_OFF_AD + 4 * 16 * 16 * 4;  // T diag(beta) at 0, P at PRE_P
 constexpr int KP_OFF_BETA = KP_OFF_IMG + PRE_BYTES;
 constexpr int KP_BYTES = KP_OFF_BETA + C * 4;
 static_assert(C * KP_ST * 2 <= C * KP_SG * 4, "T reuses the space of G");
+static_assert(4 * DK * 4 <= 10 * DK * 4, "the quarter totals of the prefix fit in F's space");
 static_assert(KP_BYTES <= 160 * 1024, "LDS budget");
-// the ten lower 16x16 tiles and the wave that builds each
-constexpr int KT_A[10] = {0, 3, 3, 1, 1, 3, 2, 2, 2, 3};
+// the ten lower 16x16 tiles (row block a >= column block b), and the factor F index of
+// each: ao_idx(a, b) below the diagonal, 6 + a on it
+constexpr int KT_A[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 constexpr int KT_B[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-constexpr int KT_W[10] = {0, 0, 0, 1, 1, 1, 2, 2, 3, 3};
+// tiles per wave: waves 0 and 1 take two tiles, waves 2..7 one
+constexpr int KT_W0[8] = {6, 8, 0, 1, 2, 3, 4, 5};
+constexpr int KT_W1[8] = {7, 9, -1, -1, -1, -1, -1, -1};
 
 // Every factor is an exponential of a difference of prefixes over at most one 16-row
-// block, or a product of such factors formed in fp32 (so each operand is rounded to
-// bf16 once):  with m = 16a + 7 and e = 16a + 15 of row r's block a,
-//   e^{G[r]}         = e^{G[m]} e^{G[r] - G[m]},  e^{g_C - G[r]} = e^{g_C - G[e]} e^{G[e] - G[r]},
-//   e^{G[m_a] - G[i]} = F[a][b] e^{G[e_b] - G[i]}  for a column row i of a block b < a.
-__global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p) {
+// block, or a product of such factors formed in fp32, so each operand is rounded to
+// bf16 once.  With m = 16a + 7 and e = 16a + 15 of a row's block a:
+//   e^{G[r]}          = e^{G[m]} e^{G[r] - G[m]},  e^{g_C - G[r]} = e^{g_C - G[e]} e^{G[e] - G[r]},
+//   e^{G[m_a] - G[i]}  = F[a][b] e^{G[e_b] - G[i]}  for a column row i of a block b <= a.
+// The grid is persistent (one workgroup per CU walks the (slot, head) items), and the
+// next item's inputs are loaded into registers while the current one is computed.
+__device__ __forceinline__ void kp_barrier() {  // LDS-only barrier: loads stay in flight
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, long items) {
   __shared__ __align__(16) char smem[KP_BYTES];
   float *Gs = (float *)(smem + KP_OFF_G);
   float *Et = Gs;  // e^{G[e] - G}, after the prefix is no longer read
   bf16 *Ks = (bf16 *)(smem + KP_OFF_K), *QA = (bf16 *)(smem + KP_OFF_QA);
-  bf16 *KA = (bf16 *)(smem + KP_OFF_KA), *KD = (bf16 *)(smem + KP_OFF_KD);
+  bf16 *KA = (bf16 *)(smem + KP_OFF_KA);
   float *Fs = (float *)(smem + KP_OFF_F), *Bc = (float *)(smem + KP_OFF_BC);
+  float *tot = Fs;  // quarter totals of the prefix, before F is formed
   bf16 *As = (bf16 *)(smem + KP_OFF_A);
   float *AD = (float *)(smem + KP_OFF_AD);
   char *img = smem + KP_OFF_IMG;
@@ -989,223 +999,289 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p) {
   bf16 *Ts = (bf16 *)(smem + KP_OFF_G);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
-  const long slot = blockIdx.x;
-  const int h = blockIdx.y, H = p.H;
+  const int H = p.H;
+  const int d = tid & 127, qtr = tid >> 7;  // prefix: channel d, rows 16 qtr .. +15
 
-  // the sequence owning this slot: the last one whose first slot is <= slot
-  auto tok_start = [&](int sq) -> long { return p.cu_seqlens ? (long)p.cu_seqlens[sq] : (long)sq * p.T; };
-  int lo = 0, hi = p.N - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((tok_start(mid) >> 6) + mid <= slot) lo = mid;
-    else hi = mid - 1;
-  }
-  const int n = lo;
-  const long tok0 = tok_start(n);
-  const long tend = p.cu_seqlens ? (long)p.cu_seqlens[n + 1] : tok0 + p.T;
-  if (tok0 < 0 || tend < tok0 || (p.cu_seqlens && tend > p.T)) return;  // malformed offsets
-  const long c = slot - ((tok0 >> 6) + n);
-  if (c < 0 || 64 * c >= tend - tok0) return;  // a slot that no chunk owns
-  const int nv = (int)min(64L, tend - tok0 - 64 * c);
-  const long t0 = tok0 + 64 * c;
-
-  // ---- loads: log alpha -> per-channel prefix (two halves of 32 rows), K, Q, beta;
-  // rows past the sequence end are zero (log alpha = 0 keeps the prefix)
-  {
-    const int d = tid & 127, half = tid >> 7;
-    const float *la = p.log_alpha + ((size_t)t0 * H + h) * DK + d;
-    float x[32];
+  struct Item {
+    bool ok;
+    int h, nv;
+    long slot, t0;
+  };
+  // (slot, head) of item w; ok = false when no chunk owns the slot
+  auto decode = [&](long w) {
+    Item it{false, 0, 0, 0, 0};
+    if (w >= items) return it;
+    it.slot = w / H;
+    it.h = (int)(w % H);
+    auto tok_start = [&](int sq) -> long { return p.cu_seqlens ? (long)p.cu_seqlens[sq] : (long)sq * p.T; };
+    int lo = 0, hi = p.N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((tok_start(mid) >> 6) + mid <= it.slot) lo = mid;
+      else hi = mid - 1;
+    }
+    const long tok0 = tok_start(lo);
+    const long tend = p.cu_seqlens ? (long)p.cu_seqlens[lo + 1] : tok0 + p.T;
+    if (tok0 < 0 || tend < tok0 || (p.cu_seqlens && tend > p.T)) return it;  // malformed offsets
+    const long c = it.slot - ((tok0 >> 6) + lo);
+    if (c < 0 || 64 * c >= tend - tok0) return it;
+    it.ok = true;
+    it.nv = (int)min(64L, tend - tok0 - 64 * c);
+    it.t0 = tok0 + 64 * c;
+    return it;
+  };
+  // inputs of one item in registers; rows past the sequence end are zero
+  float la_r[16], b_r;
+  u32x4 k_r[2], q_r[2];
+  auto prefetch = [&](const Item &it) {
+    const float *la = p.log_alpha + ((size_t)it.t0 * H + it.h) * DK + d;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int r = 32 * half + i;
-      x[i] = r < nv ? la[(size_t)r * H * DK] : 0.f;
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * qtr + i;
+      la_r[i] = (it.ok && r < it.nv) ? la[(size_t)r * H * DK] : 0.f;
     }
 #pragma unroll
-    for (int i = 1; i < 32; ++i) x[i] += x[i - 1];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) Gs[(32 * half + i) * KP_SG + d] = x[i];
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = (tid >> 4) + 16 * u, g = tid & 15;
-    u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-    if (r < nv) {
-      const size_t o = ((size_t)(t0 + r) * H + h) * DK + 8 * g;
-      kv = *(const u32x4 *)((const bf16 *)p.k + o);
-      qv = *(const u32x4 *)((const bf16 *)p.q + o);
+    for (int u = 0; u < 2; ++u) {
+      const int r = (tid >> 4) + 32 * u, g = tid & 15;
+      k_r[u] = q_r[u] = (u32x4){0u, 0u, 0u, 0u};
+      if (it.ok && r < it.nv) {
+        const size_t o = ((size_t)(it.t0 + r) * H + it.h) * DK + 8 * g;
+        k_r[u] = *(const u32x4 *)((const bf16 *)p.k + o);
+        q_r[u] = *(const u32x4 *)((const bf16 *)p.q + o);
+      }
     }
-    *(u32x4 *)(Ks + r * KP_SK + 8 * g) = kv;
-    *(u32x4 *)(QA + r * KP_SK + 8 * g) = qv;
-  }
-  if (tid < C) bs[tid] = tid < nv ? p.beta[(size_t)(t0 + tid) * H + h] : 0.f;
-  for (int i = tid; i < PRE_BYTES / 16; i += KP_NT) ((uint4 *)img)[i] = make_uint4(0, 0, 0, 0);
-  for (int i = tid; i < C * KP_ST * 2 / 16; i += KP_NT) ((uint4 *)As)[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
-  if (tid >= 128) {
-    const int d = tid & 127;
-    const float base = Gs[31 * KP_SG + d];
-#pragma unroll
-    for (int i = 32; i < 64; ++i) Gs[i * KP_SG + d] += base;
-  }
-  __syncthreads();
+    b_r = (it.ok && tid < it.nv) ? p.beta[(size_t)(it.t0 + tid) * H + it.h] : 0.f;
+  };
 
-  // ---- per-block constants, the cross-block factors F, and e^{g_C}
-  for (int i = tid; i < 8 * DK + 6 * DK; i += KP_NT) {
-    const int d = i & (DK - 1), k = i >> 7;
-    const float gC = Gs[63 * KP_SG + d];
-    if (k < 4) {
-      Bc[k * DK + d] = __expf(Gs[(16 * k + 7) * KP_SG + d]);
-    } else if (k < 8) {
-      Bc[k * DK + d] = __expf(gC - Gs[(16 * (k - 4) + 15) * KP_SG + d]);
-    } else {
-      const int ab = k - 8, a = OA[ab], b = OB[ab];
-      Fs[ab * DK + d] = __expf(Gs[(16 * a + 7) * KP_SG + d] - Gs[(16 * b + 15) * KP_SG + d]);
+  long w = blockIdx.x;
+  Item cur = decode(w);
+  prefetch(cur);
+  for (; w < items; w += gridDim.x) {
+    const Item it = cur;
+    const int nv = it.nv, h = it.h;
+    const long t0 = it.t0, slot = it.slot;
+    // ---- stage the prefetched inputs: quarter prefixes, K, Q, beta
+    if (it.ok) {
+      float x = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x += la_r[i];
+        Gs[(16 * qtr + i) * KP_SG + d] = x;
+      }
+      tot[qtr * DK + d] = x;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = (tid >> 4) + 32 * u, g = tid & 15;
+        *(u32x4 *)(Ks + r * KP_SK + 8 * g) = k_r[u];
+        *(u32x4 *)(QA + r * KP_SK + 8 * g) = q_r[u];
+      }
+      if (tid < C) bs[tid] = b_r;
+      for (int i = tid; i < PRE_BYTES / 16; i += KP_NT) ((uint4 *)img)[i] = make_uint4(0, 0, 0, 0);
+      for (int i = tid; i < C * KP_ST * 2 / 16; i += KP_NT) ((uint4 *)As)[i] = make_uint4(0, 0, 0, 0);
     }
-  }
-  if (tid < DK) p.egc[((size_t)slot * H + h) * DK + tid] = __expf(Gs[63 * KP_SG + tid]);
-  __syncthreads();
+    cur = decode(w + gridDim.x);
+    prefetch(cur);  // in flight while this item is computed
+    if (!it.ok) continue;  // uniform over the workgroup
+    kp_barrier();
+    if (qtr > 0) {  // each thread adds the totals of the earlier quarters to its own rows
+      float base = 0.f;
+      for (int q = 0; q < qtr; ++q) base += tot[q * DK + d];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Gs[(16 * qtr + i) * KP_SG + d] += base;
+    }
+    kp_barrier();
 
-  // ---- operands: row operands K e^{G - G[m]}, Q e^{G - G[m]}, diagonal column operand
-  // K e^{G[m] - G}, the tail factors e^{G[e] - G}, and the state-phase outputs
-  f32x4 etk[4][2];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = (tid >> 4) + 16 * u, g = tid & 15, blk = r >> 4;
-    const float *gr = Gs + r * KP_SG + 8 * g, *gm = Gs + (16 * blk + 7) * KP_SG + 8 * g;
-    const float *ge = Gs + (16 * blk + 15) * KP_SG + 8 * g;
-    const float *bm = Bc + blk * DK + 8 * g, *bt = Bc + (4 + blk) * DK + 8 * g;
-    const bf16x8 kv = *(const bf16x8 *)(Ks + r * KP_SK + 8 * g);
-    const bf16x8 qv = *(const bf16x8 *)(QA + r * KP_SK + 8 * g);
-    bf16x8 ka, qa, kd, kg, qg, kh;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float eh = __expf(gr[j] - gm[j]), ehi = __expf(gm[j] - gr[j]), et = __expf(ge[j] - gr[j]);
-      etk[u][j >> 2][j & 3] = et;
-      const float kf = (float)kv[j], qf = (float)qv[j];
-      ka[j] = (bf16)(kf * eh);
-      qa[j] = (bf16)(qf * eh);
-      kd[j] = (bf16)(kf * ehi);
-      const float eg = bm[j] * eh, ew = bt[j] * et;
-      kg[j] = (bf16)(kf * eg);
-      qg[j] = (bf16)(qf * eg);
-      kh[j] = (bf16)(kf * ew);
-    }
-    *(bf16x8 *)(KA + r * KP_SK + 8 * g) = ka;
-    *(bf16x8 *)(QA + r * KP_SK + 8 * g) = qa;  // each thread rewrites only its own Q entries
-    *(bf16x8 *)(KD + r * KP_SK + 8 * g) = kd;
-    if (r < nv) {
-      const size_t o = ((size_t)(t0 + r) * H + h) * DK + 8 * g;
-      *(bf16x8 *)((bf16 *)p.k_g + o) = kg;
-      *(bf16x8 *)((bf16 *)p.q_g + o) = qg;
-      *(bf16x8 *)((bf16 *)p.k_hat + o) = kh;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = (tid >> 4) + 16 * u, g = tid & 15;
-    *(f32x4 *)(Et + r * KP_SG + 8 * g) = etk[u][0];
-    *(f32x4 *)(Et + r * KP_SG + 8 * g + 4) = etk[u][1];
-  }
-  __syncthreads();
-
-  // ---- Gram tiles of A and P
-#pragma unroll
-  for (int ti = 0; ti < 10; ++ti) {
-    if (wave != KT_W[ti]) continue;
-    const int a = KT_A[ti], b = KT_B[ti];
-    const int ra = 16 * a + lm, rb = 16 * b + lm;
-    f32x4 kk = zero4(), qk = zero4();
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int ch = 32 * s4 + 8 * lg;
-      const bf16x8 ak = *(const bf16x8 *)(KA + ra * KP_SK + ch);
-      const bf16x8 aq = *(const bf16x8 *)(QA + ra * KP_SK + ch);
-      bf16x8 bk;
-      if (a == b) {
-        bk = *(const bf16x8 *)(KD + rb * KP_SK + ch);
+    // ---- per-block constants, the factors F, and e^{g_C}
+    for (int i = tid; i < 8 * DK + 10 * DK; i += KP_NT) {
+      const int dd = i & (DK - 1), k = i >> 7;
+      if (k < 4) {
+        Bc[k * DK + dd] = __expf(Gs[(16 * k + 7) * KP_SG + dd]);
+      } else if (k < 8) {
+        Bc[k * DK + dd] = __expf(Gs[63 * KP_SG + dd] - Gs[(16 * (k - 4) + 15) * KP_SG + dd]);
       } else {
+        const int ab = k - 8, a = ab < 6 ? OA[ab] : ab - 6, b = ab < 6 ? OB[ab] : ab - 6;
+        Fs[ab * DK + dd] = __expf(Gs[(16 * a + 7) * KP_SG + dd] - Gs[(16 * b + 15) * KP_SG + dd]);
+      }
+    }
+    if (tid < DK) p.egc[((size_t)slot * H + h) * DK + tid] = __expf(Gs[63 * KP_SG + tid]);
+    kp_barrier();
+
+    // ---- row operands K e^{G - G[m]}, Q e^{G - G[m]}, the tail factors e^{G[e] - G},
+    // and the state-phase outputs
+    f32x4 etk[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = (tid >> 4) + 32 * u, g = tid & 15, blk = r >> 4;
+      const float *gr = Gs + r * KP_SG + 8 * g, *gm = Gs + (16 * blk + 7) * KP_SG + 8 * g;
+      const float *ge = Gs + (16 * blk + 15) * KP_SG + 8 * g;
+      const float *bm = Bc + blk * DK + 8 * g, *bt = Bc + (4 + blk) * DK + 8 * g;
+      const bf16x8 kv = *(const bf16x8 *)(Ks + r * KP_SK + 8 * g);
+      const bf16x8 qv = *(const bf16x8 *)(QA + r * KP_SK + 8 * g);
+      bf16x8 ka, qa, kg, qg, kh;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float eh = __expf(gr[j] - gm[j]), et = __expf(ge[j] - gr[j]);
+        etk[u][j >> 2][j & 3] = et;
+        const float kf = (float)kv[j], qf = (float)qv[j];
+        ka[j] = (bf16)(kf * eh);
+        qa[j] = (bf16)(qf * eh);
+        const float eg = bm[j] * eh, ew = bt[j] * et;
+        kg[j] = (bf16)(kf * eg);
+        qg[j] = (bf16)(qf * eg);
+        kh[j] = (bf16)(kf * ew);
+      }
+      *(bf16x8 *)(KA + r * KP_SK + 8 * g) = ka;
+      *(bf16x8 *)(QA + r * KP_SK + 8 * g) = qa;  // each thread rewrites only its own Q entries
+      if (r < nv) {
+        const size_t o = ((size_t)(t0 + r) * H + h) * DK + 8 * g;
+        *(bf16x8 *)((bf16 *)p.k_g + o) = kg;
+        *(bf16x8 *)((bf16 *)p.q_g + o) = qg;
+        *(bf16x8 *)((bf16 *)p.k_hat + o) = kh;
+      }
+    }
+    kp_barrier();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = (tid >> 4) + 32 * u, g = tid & 15;
+      *(f32x4 *)(Et + r * KP_SG + 8 * g) = etk[u][0];
+      *(f32x4 *)(Et + r * KP_SG + 8 * g + 4) = etk[u][1];
+    }
+    kp_barrier();
+
+    // ---- Gram tiles of A and P
+    auto gram_tile = [&](int ti) {
+      const int a = KT_A[ti], b = KT_B[ti];
+      const int ra = 16 * a + lm, rb = 16 * b + lm;
+      const float *fab = Fs + (a > b ? ao_idx(a, b) : 6 + a) * DK;
+      f32x4 kk = zero4(), qk = zero4();
+#pragma unroll 2
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int ch = 32 * s4 + 8 * lg;
+        const bf16x8 ak = *(const bf16x8 *)(KA + ra * KP_SK + ch);
+        const bf16x8 aq = *(const bf16x8 *)(QA + ra * KP_SK + ch);
         const bf16x8 kbv = *(const bf16x8 *)(Ks + rb * KP_SK + ch);
-        const float *et = Et + rb * KP_SG + ch, *f = Fs + ao_idx(a, b) * DK + ch;
+        const float *et = Et + rb * KP_SG + ch, *f = fab + ch;
+        bf16x8 bk;
 #pragma unroll
         for (int j = 0; j < 8; ++j) bk[j] = (bf16)((float)kbv[j] * (f[j] * et[j]));
+        kk = mma(ak, bk, kk);
+        qk = mma(aq, bk, qk);
       }
-      kk = mma(ak, bk, kk);
-      qk = mma(aq, bk, qk);
-    }
-    // lane: column i = 16b + lm, rows r = 16a + 4lg + j
-    const int i = 16 * b + lm;
+      // lane: column i = 16b + lm, rows r = 16a + 4lg + j
+      const int i = 16 * b + lm;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 16 * a + 4 * lg + j;
-      const float av = i < r ? bs[r] * kk[j] : 0.f;
-      if (a == b) AD[(16 * a + 4 * lg + j) * 16 + lm] = av;
-      else As[r * KP_ST + i] = (bf16)av;
-      *(bf16 *)(img + PRE_P + tp_off(r, i)) = (bf16)(i <= r ? qk[j] : 0.f);
-    }
-  }
-  __syncthreads();
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * a + 4 * lg + j;
+        const float av = i < r ? bs[r] * kk[j] : 0.f;
+        if (a == b) AD[(16 * a + 4 * lg + j) * 16 + lm] = av;
+        else As[r * KP_ST + i] = (bf16)av;
+        *(bf16 *)(img + PRE_P + tp_off(r, i)) = (bf16)(i <= r ? qk[j] : 0.f);
+      }
+    };
+    gram_tile(KT_W0[wave]);
+    if (KT_W1[wave] >= 0) gram_tile(KT_W1[wave]);
+    kp_barrier();
 
-  // ---- diagonal blocks of T: lane (lg, lm) solves column lm of block lg in fp32
-  if (wave == 0) {
-    const float *ad = AD + lg * 256;
-    float x[16];
+    // ---- diagonal blocks of T in fp32: lane (lg, lm) owns row lm of block lg,
+    // t_r = e_r - sum_{i<r} A[r][i] t_i with rows broadcast along the 16-lane DPP row
+    if (wave == 0) {
+      float nar[16], t[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = r == lm ? 1.f : 0.f;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v4 = *(const f32x4 *)(AD + (16 * lg + lm) * 16 + 4 * q4);
 #pragma unroll
-      for (int i = 0; i < r; ++i) acc -= ad[r * 16 + i] * x[i];
-      x[r] = acc;
+        for (int j = 0; j < 4; ++j) nar[4 * q4 + j] = -v4[j];
+      }
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc) t[cc] = (cc == lm) ? 1.f : 0.f;
+#define GDN_FM(I, C) "v_fmac_f32_dpp %" #C ", %" #C ", %16 row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n"
+#define GDN_T1_STEP(I, BODY)                                                                         \
+  asm volatile("s_nop 1\n" BODY                                                                    \
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), \
+                 "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]),           \
+                 "+v"(t[13]), "+v"(t[14]), "+v"(t[15])                                               \
+               : "v"(nar[I]))
+      GDN_T1_STEP(0, GDN_FM(0, 0));
+      GDN_T1_STEP(1, GDN_FM(1, 0) GDN_FM(1, 1));
+      GDN_T1_STEP(2, GDN_FM(2, 0) GDN_FM(2, 1) GDN_FM(2, 2));
+      GDN_T1_STEP(3, GDN_FM(3, 0) GDN_FM(3, 1) GDN_FM(3, 2) GDN_FM(3, 3));
+      GDN_T1_STEP(4, GDN_FM(4, 0) GDN_FM(4, 1) GDN_FM(4, 2) GDN_FM(4, 3) GDN_FM(4, 4));
+      GDN_T1_STEP(5, GDN_FM(5, 0) GDN_FM(5, 1) GDN_FM(5, 2) GDN_FM(5, 3) GDN_FM(5, 4) GDN_FM(5, 5));
+      GDN_T1_STEP(6, GDN_FM(6, 0) GDN_FM(6, 1) GDN_FM(6, 2) GDN_FM(6, 3) GDN_FM(6, 4) GDN_FM(6, 5)
+                         GDN_FM(6, 6));
+      GDN_T1_STEP(7, GDN_FM(7, 0) GDN_FM(7, 1) GDN_FM(7, 2) GDN_FM(7, 3) GDN_FM(7, 4) GDN_FM(7, 5)
+                         GDN_FM(7, 6) GDN_FM(7, 7));
+      GDN_T1_STEP(8, GDN_FM(8, 0) GDN_FM(8, 1) GDN_FM(8, 2) GDN_FM(8, 3) GDN_FM(8, 4) GDN_FM(8, 5)
+                         GDN_FM(8, 6) GDN_FM(8, 7) GDN_FM(8, 8));
+      GDN_T1_STEP(9, GDN_FM(9, 0) GDN_FM(9, 1) GDN_FM(9, 2) GDN_FM(9, 3) GDN_FM(9, 4) GDN_FM(9, 5)
+                         GDN_FM(9, 6) GDN_FM(9, 7) GDN_FM(9, 8) GDN_FM(9, 9));
+      GDN_T1_STEP(10, GDN_FM(10, 0) GDN_FM(10, 1) GDN_FM(10, 2) GDN_FM(10, 3) GDN_FM(10, 4) GDN_FM(10, 5)
+                          GDN_FM(10, 6) GDN_FM(10, 7) GDN_FM(10, 8) GDN_FM(10, 9) GDN_FM(10, 10));
+      GDN_T1_STEP(11, GDN_FM(11, 0) GDN_FM(11, 1) GDN_FM(11, 2) GDN_FM(11, 3) GDN_FM(11, 4) GDN_FM(11, 5)
+                          GDN_FM(11, 6) GDN_FM(11, 7) GDN_FM(11, 8) GDN_FM(11, 9) GDN_FM(11, 10)
+                              GDN_FM(11, 11));
+      GDN_T1_STEP(12, GDN_FM(12, 0) GDN_FM(12, 1) GDN_FM(12, 2) GDN_FM(12, 3) GDN_FM(12, 4) GDN_FM(12, 5)
+                          GDN_FM(12, 6) GDN_FM(12, 7) GDN_FM(12, 8) GDN_FM(12, 9) GDN_FM(12, 10)
+                              GDN_FM(12, 11) GDN_FM(12, 12));
+      GDN_T1_STEP(13, GDN_FM(13, 0) GDN_FM(13, 1) GDN_FM(13, 2) GDN_FM(13, 3) GDN_FM(13, 4) GDN_FM(13, 5)
+                          GDN_FM(13, 6) GDN_FM(13, 7) GDN_FM(13, 8) GDN_FM(13, 9) GDN_FM(13, 10)
+                              GDN_FM(13, 11) GDN_FM(13, 12) GDN_FM(13, 13));
+      GDN_T1_STEP(14, GDN_FM(14, 0) GDN_FM(14, 1) GDN_FM(14, 2) GDN_FM(14, 3) GDN_FM(14, 4) GDN_FM(14, 5)
+                          GDN_FM(14, 6) GDN_FM(14, 7) GDN_FM(14, 8) GDN_FM(14, 9) GDN_FM(14, 10)
+                              GDN_FM(14, 11) GDN_FM(14, 12) GDN_FM(14, 13) GDN_FM(14, 14));
+#undef GDN_T1_STEP
+#undef GDN_FM
+      const int row = 16 * lg + lm;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 t4 = {t[4 * q4], t[4 * q4 + 1], t[4 * q4 + 2], t[4 * q4 + 3]};
+        const f32x4 b4 = *(const f32x4 *)(bs + 16 * lg + 4 * q4);
+        *(bf16x4 *)(Ts + row * KP_ST + 16 * lg + 4 * q4) = to_bf4(t4);
+        *(bf16x4 *)(img + tp_off(row, 16 * lg + 4 * q4)) = to_bf4(t4 * b4);
+      }
     }
-    const int col = 16 * lg + lm;
-    const float bc = bs[col];
+    kp_barrier();
+    // ---- off-diagonal blocks: T[a][b] = -T[a][a] sum_{k=b}^{a-1} A[a][k] T[k][b];
+    // wave b walks block column b downwards with T[k][b] kept as C tiles
+    if (wave < 3) {
+      const int b = wave;
+      const float bc = bs[16 * b + lm];
+      f32x4 Tc[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 16 * lg + r;
-      Ts[row * KP_ST + col] = (bf16)x[r];
-      *(bf16 *)(img + tp_off(row, col)) = (bf16)(x[r] * bc);
-    }
-  }
-  __syncthreads();
-  // ---- off-diagonal blocks: T[a][b] = -T[a][a] sum_{k=b}^{a-1} A[a][k] T[k][b];
-  // wave b walks block column b downwards with T[k][b] kept as C tiles
-  if (wave < 3) {
-    const int b = wave;
-    const float bc = bs[16 * b + lm];
-    f32x4 Tc[4];
+      for (int k = 0; k < 4; ++k) {
+        Tc[k] = zero4();
+        if (k == b)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      Tc[k] = zero4();
-      if (k == b)
+          for (int j = 0; j < 4; ++j) Tc[k][j] = (float)Ts[(16 * k + 4 * lg + j) * KP_ST + 16 * k + lm];
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Tc[k][j] = (float)Ts[(16 * k + 4 * lg + j) * KP_ST + 16 * k + lm];
-    }
+      for (int a = 1; a < 4; ++a) {
+        if (a > b) {
+          f32x4 y = zero4();
 #pragma unroll
-    for (int a = 1; a < 4; ++a) {
-      if (a > b) {
-        f32x4 y = zero4();
+          for (int k0 = 0; k0 < 4; k0 += 2) {
+            const bool in0 = (k0 >= b && k0 < a), in1 = (k0 + 1 >= b && k0 + 1 < a);
+            if (in0 || in1) {
+              const bf16x8 bf = frag_from_c<bf16>(in0 ? Tc[k0] : zero4(), in1 ? Tc[k0 + 1] : zero4());
+              const bf16 *ar = As + (16 * a + lm) * KP_ST + 16 * k0 + 4 * lg;
+              y = mma(ld4x2(ar, ar + 16), bf, y);
+            }
+          }
+          const bf16x8 tf = ld4z(Ts + (16 * a + lm) * KP_ST + 16 * a + 4 * lg);
+          const f32x4 z = mma(tf, frag_from_c_half<bf16>(y), zero4());
 #pragma unroll
-        for (int k0 = 0; k0 < 4; k0 += 2) {
-          const bool in0 = (k0 >= b && k0 < a), in1 = (k0 + 1 >= b && k0 + 1 < a);
-          if (in0 || in1) {
-            const bf16x8 bf = frag_from_c<bf16>(in0 ? Tc[k0] : zero4(), in1 ? Tc[k0 + 1] : zero4());
-            const bf16 *ar = As + (16 * a + lm) * KP_ST + 16 * k0 + 4 * lg;
-            y = mma(ld4x2(ar, ar + 16), bf, y);
+          for (int j = 0; j < 4; ++j) {
+            Tc[a][j] = -z[j];
+            *(bf16 *)(img + tp_off(16 * a + 4 * lg + j, 16 * b + lm)) = (bf16)(-z[j] * bc);
           }
         }
-        const bf16x8 tf = ld4z(Ts + (16 * a + lm) * KP_ST + 16 * a + 4 * lg);
-        const f32x4 z = mma(tf, frag_from_c_half<bf16>(y), zero4());
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          Tc[a][j] = -z[j];
-          *(bf16 *)(img + tp_off(16 * a + 4 * lg + j, 16 * b + lm)) = (bf16)(-z[j] * bc);
-        }
       }
     }
+    kp_barrier();
+    char *dst = (char *)p.tp_img + ((size_t)slot * H + h) * PRE_BYTES;
+    for (int i = tid; i < PRE_BYTES / 16; i += KP_NT) ((uint4 *)dst)[i] = ((const uint4 *)img)[i];
+    kp_barrier();  // LDS is restaged by the next item
   }
-  __syncthreads();
-  char *dst = (char *)p.tp_img + ((size_t)slot * H + h) * PRE_BYTES;
-  for (int i = tid; i < PRE_BYTES / 16; i += KP_NT) ((uint4 *)dst)[i] = ((const uint4 *)img)[i];
 }
 
 }  // namespace
@@ -1224,7 +1300,11 @@ hipError_t launch_fwd_pipe(const FwdParams &p, int gate, hipStream_t stream) {
 
 hipError_t launch_key_prep(const KeyPrepParams &p, long slots, hipStream_t stream) {
   if (slots <= 0 || p.N <= 0 || p.H <= 0) return hipSuccess;
-  hipLaunchKernelGGL(key_prep_kernel, dim3((unsigned)slots, (unsigned)p.H), dim3(KP_NT), 0, stream, p);
+  const long items = slots * p.H;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const long grid = items < cus ? items : cus;  // persistent: one workgroup per CU
+  hipLaunchKernelGGL(key_prep_kernel, dim3((unsigned)grid), dim3(KP_NT), 0, stream, p, items);
   return hipGetLastError();
 }
 
