@@ -1302,7 +1302,9 @@ hipError_t launch_key_prep(const KeyPrepParams &p, long slots, hipStream_t strea
   if (slots <= 0 || p.N <= 0 || p.H <= 0) return hipSuccess;
   const long items = slots * p.H;
   int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
   const long grid = items < cus ? items : cus;  // persistent: one workgroup per CU
   hipLaunchKernelGGL(key_prep_kernel, dim3((unsigned)grid), dim3(KP_NT), 0, stream, p, items);
   return hipGetLastError();
