@@ -74,9 +74,10 @@ constexpr int OFF_BL = OFF_V + 2 * V_BYTES;   // x3
 constexpr int PRE_P = C * C * 2;              // T at 0, P at PRE_P
 constexpr int PRE_BYTES = 2 * C * C * 2;
 constexpr int OFF_PRE = OFF_BL + 3 * BL_BYTES;  // x2
-constexpr int OFF_AD = OFF_PRE + 2 * PRE_BYTES;  // diagonal blocks of A, fp32 [4][16][16]
+constexpr int AD_STRIDE = 20;                    // fp32 row pitch of the diagonal blocks of A
+constexpr int OFF_AD = OFF_PRE + 2 * PRE_BYTES;  // diagonal blocks of A, fp32 [4][16][20]
 constexpr int AO_STRIDE = 24;                     // off-diagonal blocks, bf16 6 x [16][24]
-constexpr int OFF_AO = OFF_AD + 4 * 16 * 16 * 4;
+constexpr int OFF_AO = OFF_AD + 4 * 16 * AD_STRIDE * 4;
 // per-chunk decay vectors (fp32), x3 by chunk: Ehead, Ehinv, Etail, beta, F[4][4],
 // e^g Gam, e^{g_C - g} / Gam', Gam', eager flag (Gam: the state's running decay scalar
 // entering the chunk, Gam' the one leaving it; see the state waves)
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
         for (int a = 0; a < 4; ++a) acc[a] = mma(kf[a][s], kf[a][s], acc[a]);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
-        *(f32x4 *)(AD + ((16 * a + lm) * 16 + 4 * lg) * 4) = acc[a] * gamma_tile<GATE, true>(G, a, a, lm, lg) * G.be[a];
+        *(f32x4 *)(AD + ((16 * a + lm) * AD_STRIDE + 4 * lg) * 4) = acc[a] * gamma_tile<GATE, true>(G, a, a, lm, lg) * G.be[a];
       f32x4 bdg[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) bdg[q4] = *(const f32x4 *)(gv + GV_BETA + 16 * lg + 4 * q4);
@@ -508,7 +509,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       float nar[16], t[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v4 = *(const f32x4 *)(AD + ((16 * lg + lm) * 16 + 4 * q4) * 4);
+        const f32x4 v4 = *(const f32x4 *)(AD + ((16 * lg + lm) * AD_STRIDE + 4 * q4) * 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) nar[4 * q4 + j] = -v4[j];
       }
@@ -959,7 +960,7 @@ constexpr int KP_OFF_F = KP_OFF_KA + KP_OP;         // F[ab][d] = e^{G[m_a] - G[
 constexpr int KP_OFF_BC = KP_OFF_F + 10 * DK * 4;   // e^{G[m_a]} [4][128], e^{g_C - G[e_a]} [4][128]
 constexpr int KP_OFF_A = KP_OFF_BC + 8 * DK * 4;    // off-diagonal blocks of A
 constexpr int KP_OFF_AD = KP_OFF_A + C * KP_ST * 2; // diagonal blocks of A, fp32
-constexpr int KP_OFF_IMG = KP_OFF_AD + 4 * 16 * 16 * 4;  // T diag(beta) at 0, P at PRE_P
+constexpr int KP_OFF_IMG = KP_OFF_AD + 4 * 16 * AD_STRIDE * 4;  // T diag(beta) at 0, P at PRE_P
 constexpr int KP_OFF_BETA = KP_OFF_IMG + PRE_BYTES;
 constexpr int KP_BYTES = KP_OFF_BETA + C * 4;
 static_assert(C * KP_ST * 2 <= C * KP_SG * 4, "T reuses the space of G");
@@ -1173,7 +1174,7 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * a + 4 * lg + j;
         const float av = i < r ? bs[r] * kk[j] : 0.f;
-        if (a == b) AD[(16 * a + 4 * lg + j) * 16 + lm] = av;
+        if (a == b) AD[(16 * a + 4 * lg + j) * AD_STRIDE + lm] = av;
         else As[r * KP_ST + i] = (bf16)av;
         *(bf16 *)(img + PRE_P + tp_off(r, i)) = (bf16)(i <= r ? qk[j] : 0.f);
       }
@@ -1188,7 +1189,7 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
       float nar[16], t[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v4 = *(const f32x4 *)(AD + (16 * lg + lm) * 16 + 4 * q4);
+        const f32x4 v4 = *(const f32x4 *)(AD + (16 * lg + lm) * AD_STRIDE + 4 * q4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) nar[4 * q4 + j] = -v4[j];
       }
