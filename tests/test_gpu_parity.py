@@ -98,6 +98,18 @@ def test_varlen_key_many_short(gdn):
     check(gdn, inp)
 
 
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_varlen_many_sequences(gdn, gate):
+    """More than 8192 packed sequences: no processing-order table, and for the
+    per-key-channel gate the chunk slots are searched over all of them."""
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(0, 4, size=8200)]
+    lengths[100] = 70  # one sequence longer than a chunk
+    inp = synth.random_inputs(1, None, 1, 128, 64, gate, "bf16", seed=33, state_std=0.05,
+                              lengths=lengths)
+    check(gdn, inp)
+
+
 def test_key_prepared_call_repeats(gdn):
     """The per-key-channel gate through PreparedFwd: the workspace holding the
     prepared chunk operands is reused across launches with identical results."""
