@@ -175,8 +175,9 @@ def test_beta_zero_keeps_decayed_state(gdn, gate):
     assert relerr(fs, expect.numpy()) <= 1e-5
 
 
-def test_deterministic_and_aliased_state(gdn):
-    inp = synth.random_inputs(2, 300, 4, 128, 128, "head", "bf16", seed=9, state_std=0.05)
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_deterministic_and_aliased_state(gdn, gate):
+    inp = synth.random_inputs(2, 300, 4, 128, 128, gate, "bf16", seed=9, state_std=0.05)
     o1, f1 = run_gpu(gdn, inp)
     o2, f2 = run_gpu(gdn, inp)
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
