@@ -40,9 +40,10 @@
 // runs the same state waves on them, its four producer waves only loading (two
 // stages of every buffer), and the state rows decaying by e^{g_C} per channel.
 //
-// LDS layouts are XOR-swizzled instead of padded: K/Q rows of 256 B in 16-byte units
-// (unit ^ kq_swz(row)), V rows of 128 B (unit ^ (row & 7)), T/P rows of 128 B with
-// permuted columns so each MFMA fragment is one 16-byte unit.  K^T and V fragments
+// The large LDS layouts are XOR-swizzled instead of padded: K/Q rows of 256 B in
+// 16-byte units (unit ^ kq_swz(row)), V rows of 128 B (unit ^ (row & 7)), T/P rows of
+// 128 B with permuted columns so each MFMA fragment is one 16-byte unit; the small
+// fp32 diagonal blocks of A are padded to an 80-byte row pitch.  K^T and V fragments
 // are read with ds_read_b64_tr_b16 (gfx950 transposing LDS read), so no transposed
 // copies exist.
 #include <type_traits>
