@@ -622,7 +622,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     if (nchunks > 0) {
       if (wave == W_LKQ) {
         load_kq(rs, KQ(0), 0, lane, false);
-        load_v(rs, VB(0), 0, lane);
         if (nchunks > 1) {
           load_kq(rs, KQ(1), 1, lane, false);  // 16 loads
           asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -666,6 +665,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
         __builtin_amdgcn_s_sleep(1);
       asm volatile("" ::: "memory");
     };
+    if (nchunks > 0 && wave == W_LKQ) load_v(rs, VB(0), 0, lane);  // needed from the second barrier on
     if (nchunks > 0) {
       phase1(0, 0);
       handoff(0);
@@ -716,6 +716,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   const int n0 = 16 * ((wave & 1) + 2 * (wave >> 2));  // first value column inside the block
   f32x4 M[8];
   const size_t sbase = ((size_t)n * H + h) * DK * dv + col0 + n0 + lm;
+  // the initial state is read after the first barrier: at launch every workgroup's
+  // chunk-0 loads, which the first T depends on, get the memory system to themselves
+  __syncthreads();
   {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
@@ -725,7 +728,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) opaque(M[t]);
   }
-  __syncthreads();
   __syncthreads();
   const size_t orow = (size_t)H * dv;  // elements between output rows
   bf16 *olane = (bf16 *)p.o + ((size_t)tok0 * H + h) * dv + col0 + n0 + (size_t)lm * orow + 4 * lg;
