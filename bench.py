@@ -6,6 +6,12 @@ random fp32 initial state): every step of the chunked method runs in that call.
 Inputs are synthetic (seeded), resident in HBM before timing, and rotated over
 four copies so that no step finds its inputs in the 256 MB last-level cache.
 
+Warm-up: from idle, the GPU's power controller needs about 25-30 ms of continuous
+load to settle (launch durations first dip well below and then recover to the
+sustained rate, with socket power at its 1400 W limit). The default warm-up of 600
+headline launches (about 50 ms) covers that transient, so the timed steps measure
+the sustained rate a continuously running layer sees.
+
 Prints ONE JSON line.  `roofline` relates the fused kernel's algorithmic bytes
 (q, k, v read and o written in bf16, beta and log alpha in fp32, initial and final
 fp32 state) to its average launch duration, measured with HIP events on the stream
@@ -35,6 +41,7 @@ KERNEL_SOURCES = ["gated_delta_rule_20_amd/csrc/gdn_fwd_pipe.hip", "gated_delta_
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_pipe_gdn-350m.txt")
 ROTATE = 4
 CHUNK = 64
+SETTLE_MS = 50.0  # continuous load before timing the workloads other than the headline
 
 
 def alg_counts(tokens, H, dk, dv, nseq, gate, esize, has_init, has_final=True):
@@ -89,8 +96,9 @@ def make_device_inputs(inp, copies):
 
 
 def time_chunked(gdn, sets, steps, warmup):
-    """Whole-job time of `steps` calls (barrier + synchronize on both sides) and the
-    average per-launch duration from HIP events on the launch stream."""
+    """Whole-job time of `steps` calls (barrier + synchronize on both sides) after
+    `warmup` untimed calls (None: as many as fill SETTLE_MS), and the average
+    per-launch duration from HIP events on the launch stream."""
     import torch
     # one validated call per input copy: each timed step is a single library call
     stream = torch.cuda.current_stream()
@@ -100,6 +108,14 @@ def time_chunked(gdn, sets, steps, warmup):
     def call(i):
         calls[i % len(calls)].launch(stream)
 
+    if warmup is None:
+        # enough launches for SETTLE_MS of continuous load, from one timed call
+        call(0)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        call(1)
+        torch.cuda.synchronize()
+        warmup = max(2, int(SETTLE_MS / 1e3 / (time.perf_counter() - t)) + 1)
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
@@ -126,7 +142,13 @@ def time_decode(gdn, spec, final_states, steps=64):
     d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in dec.items()}
     st = synth.decode_initial_states(final_states.cpu(), batch).cuda()
     out = torch.empty((batch, spec["H"], spec["dv"]), dtype=d["q"].dtype, device="cuda")
-    for s in range(4):
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    gdn.recurrent_step(d["q"][0], d["k"][0], d["v"][0], d["beta"][0], d["log_alpha"][0], st, out=out)
+    torch.cuda.synchronize()
+    warm = max(4, int(SETTLE_MS / 1e3 / (time.perf_counter() - t)) + 1)
+    for i in range(warm):
+        s = i % steps
         gdn.recurrent_step(d["q"][s], d["k"][s], d["v"][s], d["beta"][s], d["log_alpha"][s], st, out=out)
     st = synth.decode_initial_states(final_states.cpu(), batch).cuda()
     torch.cuda.synchronize()
@@ -185,8 +207,9 @@ def bench_workload(gdn, name, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=600,
+                    help="untimed launches first; the default covers the power controller's settling")
     ap.add_argument("--all", action="store_true", help="also report every workload (extra lines on stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -247,7 +270,7 @@ def main():
         for name in ["gdn-bf16-B4-T2048-H8-d128", "kda-bf16-B2-T16384-H16-d128",
                      "gdn-varlen-bf16-N32-H16-d128", "deltanet-fp32-B1-T256-H2-d64"]:
             try:
-                r, winp, wsets = bench_workload(gdn, name, max(5, args.steps // 5), 2)
+                r, winp, wsets = bench_workload(gdn, name, max(5, args.steps // 5), None)
             except RuntimeError as e:
                 extra.append({"workload": name, "error": str(e)})
                 continue
