@@ -7,9 +7,11 @@ shares no code with that library: the arithmetic lives in ``gdn_oracle.c``
 and ``chunked_ref.py`` (the chunkwise form, used only to pin the chunk
 equations).  This module only converts arrays to fp64 and calls the C code.
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-(closed forms, invariants, an autograd-derived gradient step, exact rational
-fixtures under ``tests/golden/`` and planted-mistake checks).
+Parity status: every function here is pinned.  ``fwd`` and ``step`` by
+``tests/test_oracle_pins.py`` (closed forms, invariants, an autograd-derived
+gradient step, exact rational fixtures under ``tests/golden/`` and planted-mistake
+checks); ``decode_pool`` by ``tests/test_oracle_decode.py`` (against ``fwd`` over
+the same tokens and over every stored prefix, chained and speculative calls).
 """
 from __future__ import annotations
 
@@ -132,6 +134,43 @@ def step(q, k, v, beta, log_alpha, state, gate=None, lib=None):
     if rc != 0:
         raise RuntimeError("oracle_step failed (%d)" % rc)
     return o, st
+
+
+def decode_pool(q, k, v, beta, log_alpha, pool, src_slots, dst_slots, gate=None, lib=None):
+    """L decode tokens per stream against a pool of states, by repeated ``step``.
+
+    q,k [N,L,H,d_k], v [N,L,H,d_v], beta [N,L,H], log_alpha None | [N,L,H] |
+    [N,L,H,d_k]; pool [P,H,d_k,d_v] (M = S^T); src_slots [N] and dst_slots [N,L]
+    integers.  Stream n is active when 0 <= src_slots[n] < P: its state is read from
+    that slot (all reads happen before any write), its L tokens run through the
+    recurrence in order, and the state after token t is stored into slot
+    dst_slots[n, t] when that is in [0, P).  Inactive streams read and write nothing.
+    Returns (o [N,L,H,d_v] with NaN rows for inactive streams, the pool afterwards),
+    both fp64.  Writes land in (stream, token) order.
+    """
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    log_alpha, pool = _f64(log_alpha), _f64(pool)
+    src = np.asarray(src_slots.cpu() if hasattr(src_slots, "cpu") else src_slots, dtype=np.int64)
+    dst = np.asarray(dst_slots.cpu() if hasattr(dst_slots, "cpu") else dst_slots, dtype=np.int64)
+    N, L, H, dk = q.shape
+    dv = v.shape[-1]
+    P = pool.shape[0]
+    if gate is None:
+        gate = infer_gate(log_alpha, 3)
+    o = np.full((N, L, H, dv), np.nan)
+    out = pool.copy()
+    act = np.nonzero((src >= 0) & (src < P))[0]
+    if len(act) == 0:
+        return o, out
+    states = pool[src[act]].copy()  # every read before any write
+    for t in range(L):
+        la = None if log_alpha is None else log_alpha[act, t]
+        o_t, states = step(q[act, t], k[act, t], v[act, t], beta[act, t], la, states, gate=gate, lib=lib)
+        o[act, t] = o_t
+        for j, n in enumerate(act):
+            if 0 <= dst[n, t] < P:
+                out[dst[n, t]] = states[j]
+    return o, out
 
 
 def max_threads() -> int:
