@@ -6,8 +6,9 @@ runs in the library's HIP kernels; PyTorch only supplies device memory and the
 current stream.  There is no fallback: if the library is missing this module
 raises on import.
 
-The names follow the C ABI: ``fwd_chunked`` wraps ``gdn_fwd_chunked`` and
-``recurrent_step`` wraps ``gdn_fwd_recurrent_step``.
+The names follow the C ABI: ``fwd_chunked`` wraps ``gdn_fwd_chunked``,
+``recurrent_step`` wraps ``gdn_fwd_recurrent_step`` and ``decode`` wraps
+``gdn_fwd_decode``.
 """
 from __future__ import annotations
 
@@ -46,6 +47,16 @@ class StepArgs(ctypes.Structure):
                 ("state", ctypes.c_void_p), ("o", ctypes.c_void_p)]
 
 
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``gdn_decode_args``."""
+    _fields_ = [("N", ctypes.c_int), ("L", ctypes.c_int), ("H", ctypes.c_int),
+                ("d_k", ctypes.c_int), ("d_v", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("gate", ctypes.c_int), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
+                ("state_pool", ctypes.c_void_p), ("pool_size", ctypes.c_int),
+                ("src_slots", ctypes.c_void_p), ("dst_slots", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
 def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError("libgdn.so is not built (%s); run `python __graft_entry__.py build` "
@@ -57,6 +68,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_fwd_chunked.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
     lib.gdn_fwd_recurrent_step.restype = ctypes.c_int
     lib.gdn_fwd_recurrent_step.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_void_p]
+    lib.gdn_fwd_decode.restype = ctypes.c_int
+    lib.gdn_fwd_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
     lib.gdn_status_str.restype = ctypes.c_char_p
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_version.restype = ctypes.c_int
@@ -181,6 +194,39 @@ def check_step_tensors(q, k, v, beta, log_alpha, state, out=None):
     _same_device(named, q)
 
 
+def check_decode_tensors(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out=None):
+    """Host-side checks for decode (see check_fwd_tensors).  Slot values live on the
+    device and are not inspected here."""
+    import torch
+    named = [("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
+             ("state_pool", state_pool), ("src_slots", src_slots), ("dst_slots", dst_slots), ("out", out)]
+    _require(q.dim() == 4, "q must be [N, L, H, d_k]")
+    N, L, H, dk = q.shape
+    _require(L >= 1, "q must hold at least one token per stream")
+    _require(q.dtype in (torch.bfloat16, torch.float32), "q must be bfloat16 or float32")
+    _require(tuple(k.shape) == (N, L, H, dk), "k must have the shape of q")
+    _require(v.dim() == 4 and tuple(v.shape[:3]) == (N, L, H), "v must be [N, L, H, d_v]")
+    dv = v.shape[3]
+    _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share one dtype")
+    _require(tuple(beta.shape) == (N, L, H) and beta.dtype == torch.float32,
+             "beta must be float32 [N, L, H]")
+    if log_alpha is not None:
+        _require(log_alpha.dtype == torch.float32 and tuple(log_alpha.shape) in ((N, L, H), (N, L, H, dk)),
+                 "log_alpha must be float32 [N, L, H] or [N, L, H, d_k]")
+    _require(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (H, dk, dv) and
+             state_pool.shape[0] >= 1 and state_pool.dtype == torch.float32,
+             "state_pool must be float32 [P, H, d_k, d_v] with P >= 1")
+    _require(tuple(src_slots.shape) == (N,) and src_slots.dtype == torch.int32, "src_slots must be int32 [N]")
+    _require(tuple(dst_slots.shape) == (N, L) and dst_slots.dtype == torch.int32,
+             "dst_slots must be int32 [N, L]")
+    if out is not None:
+        _require(tuple(out.shape) == (N, L, H, dv) and out.dtype == q.dtype, "out must be [N, L, H, d_v]")
+    for name, t in named:
+        if t is not None:
+            _require(t.is_contiguous(), "%s must be contiguous" % name)
+    _same_device(named, q)
+
+
 def gate_code(log_alpha, token_ndim: int) -> int:
     if log_alpha is None:
         return GDN_GATE_NONE
@@ -287,6 +333,30 @@ def recurrent_step(q, k, v, beta, log_alpha, state, out=None, stream=None):
                     q=_ptr(q), k=_ptr(k), v=_ptr(v), beta=_ptr(beta), log_alpha=_ptr(log_alpha),
                     state=_ptr(state), o=_ptr(out))
     _check(_lib.gdn_fwd_recurrent_step(ctypes.byref(args), _stream(stream)), "gdn_fwd_recurrent_step")
+    return out
+
+
+def decode(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out=None, stream=None):
+    """Serving decode (gdn_fwd_decode): L tokens per stream against a pool of states.
+
+    q, k [N,L,H,d_k], v [N,L,H,d_v] (bf16 or fp32); beta [N,L,H]; log_alpha None |
+    [N,L,H] | [N,L,H,d_k]; state_pool [P,H,d_k,d_v] fp32; src_slots int32 [N] (slot
+    each stream starts from; outside [0, P): padding stream, skipped); dst_slots int32
+    [N,L] (slot receiving the state after each token; outside [0, P): not stored).
+    Returns o [N,L,H,d_v]; rows of padding streams are left as they were in ``out``
+    (uninitialised if ``out`` is None).
+    """
+    import torch
+    check_decode_tensors(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out)
+    N, L, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((N, L, H, dv), dtype=q.dtype, device=q.device)
+    args = DecodeArgs(N=N, L=L, H=H, d_k=dk, d_v=dv, dtype=_dtype_code(q), gate=gate_code(log_alpha, 3),
+                      q=_ptr(q), k=_ptr(k), v=_ptr(v), beta=_ptr(beta), log_alpha=_ptr(log_alpha),
+                      state_pool=_ptr(state_pool), pool_size=state_pool.shape[0],
+                      src_slots=_ptr(src_slots), dst_slots=_ptr(dst_slots), o=_ptr(out))
+    _check(_lib.gdn_fwd_decode(ctypes.byref(args), _stream(stream)), "gdn_fwd_decode")
     return out
 
 

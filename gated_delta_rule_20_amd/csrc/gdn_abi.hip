@@ -94,6 +94,25 @@ int check_step(const gdn_step_args *a) {
   return GDN_OK;
 }
 
+int check_decode(const gdn_decode_args *a) {
+  if (!a) return GDN_ERR_INVALID_ARG;
+  if (a->N < 0 || a->L < 1 || a->H <= 0 || a->pool_size < 1) return GDN_ERR_INVALID_ARG;
+  if ((long long)a->N * a->H > INT32_MAX || (long long)a->N * a->L > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+  if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD && a->gate != GDN_GATE_KEY)
+    return GDN_ERR_INVALID_ARG;
+  if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
+  if (a->N == 0) return GDN_OK;
+  if (!a->q || !a->k || !a->v || !a->beta || !a->state_pool || !a->src_slots || !a->dst_slots || !a->o)
+    return GDN_ERR_INVALID_ARG;
+  if ((a->gate == GDN_GATE_NONE) != (a->log_alpha == nullptr)) return GDN_ERR_INVALID_ARG;
+  if (!aligned(a->state_pool, 16) || !aligned(a->q, 4) || !aligned(a->k, 4) || !aligned(a->v, 4) ||
+      !aligned(a->o, 4) || !aligned(a->beta, 4) || (a->log_alpha && !aligned(a->log_alpha, 4)) ||
+      !aligned(a->src_slots, 4) || !aligned(a->dst_slots, 4))
+    return GDN_ERR_INVALID_ARG;
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,6 +206,30 @@ int gdn_fwd_recurrent_step(const gdn_step_args *a, void *hip_stream) {
   p.H = a->H;
   if (gdn::launch_recurrent_step(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->d_v, (int)a->gate,
                                  (hipStream_t)hip_stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+int gdn_fwd_decode(const gdn_decode_args *a, void *hip_stream) {
+  const int st = check_decode(a);
+  if (st != GDN_OK) return st;
+  if (a->N == 0) return GDN_OK;
+  gdn::DecodeParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.beta = a->beta;
+  p.log_alpha = a->log_alpha;
+  p.pool = a->state_pool;
+  p.src = a->src_slots;
+  p.dst = a->dst_slots;
+  p.o = a->o;
+  p.N = a->N;
+  p.L = a->L;
+  p.H = a->H;
+  p.P = a->pool_size;
+  if (gdn::launch_decode(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->d_v, (int)a->gate,
+                         (hipStream_t)hip_stream) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
 }

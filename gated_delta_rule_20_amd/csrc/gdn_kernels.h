@@ -39,6 +39,17 @@ struct StepParams {
   int N, H;
 };
 
+// L decode tokens per stream against a pool of states: slot src[n] is read, the
+// state after token t is stored into slot dst[n * L + t] when that is in [0, P).
+struct DecodeParams {
+  const void *q, *k, *v;
+  const float *beta, *log_alpha;
+  float *pool;
+  const int *src, *dst;
+  void *o;
+  int N, L, H, P;
+};
+
 // dtype: 0 fp32, 1 bf16.  Each launcher returns hipSuccess or the launch error.
 // dvb: columns of d_v per workgroup (32 or 64).
 hipError_t launch_fwd_fused(const FwdParams &p, int dtype, int dk, int dvb, int gate,
@@ -63,5 +74,6 @@ hipError_t launch_key_prep(const KeyPrepParams &p, long slots, hipStream_t strea
 hipError_t launch_seq_order(const int32_t *cu_seqlens, int N, int32_t *order, hipStream_t stream);
 hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate,
                                  hipStream_t stream);
+hipError_t launch_decode(const DecodeParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream);
 
 }  // namespace gdn

@@ -90,6 +90,107 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
   }
 }
 
+// Serving decode: L tokens per stream in one launch, the state read once from its
+// pool slot, kept in registers across the tokens, and stored only where a slot is
+// given (every token for speculative drafts, the last one for plain decoding).  The
+// per-token body is the one above; the token's q, k, decay, v and beta are fetched
+// into registers one token ahead, and q, k and the decay alternate between two LDS
+// buffers, so two barriers per token suffice.
+template <typename E, int DK, int DV, int GATE>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  constexpr int CQ = DV / 4;
+  constexpr int RG = 256 / CQ;
+  constexpr int RP = DK / RG;
+  static_assert(RP >= 1 && RG * RP == DK, "decode geometry");
+  __shared__ float qs[2][DK], ks[2][DK], as_[2][DK];
+  __shared__ f32x4 red_r[RG][CQ], red_s[RG][CQ];
+  __shared__ float qk_s;
+
+  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int src = p.src[n];
+  if (src < 0 || src >= p.P) return;  // padding stream: nothing read or written
+  const int tid = threadIdx.x, cq = tid % CQ, rg = tid / CQ;
+  const size_t slot = (size_t)p.H * DK * DV, head = (size_t)h * DK * DV;
+  const float *st = p.pool + (size_t)src * slot + head;
+  f32x4 m[RP];
+#pragma unroll
+  for (int u = 0; u < RP; ++u) m[u] = *(const f32x4 *)(st + (size_t)(rg * RP + u) * DV + 4 * cq);
+
+  float qn = 0.f, kn = 0.f, an = 1.f, bn = 0.f;
+  f32x4 vn;
+  auto fetch = [&](int t) {
+    const size_t i = ((size_t)n * p.L + t) * p.H + h;  // (stream, token, head)
+    if (tid < DK) {
+      qn = to_f(((const E *)p.q)[i * DK + tid]);
+      kn = to_f(((const E *)p.k)[i * DK + tid]);
+      if (GATE == GATE_HEAD) an = __expf(p.log_alpha[i]);
+      if (GATE == GATE_KEY) an = __expf(p.log_alpha[i * DK + tid]);
+    }
+    const E *vp = (const E *)p.v + i * DV + 4 * cq;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vn[e] = to_f(vp[e]);
+    bn = p.beta[i];
+  };
+  fetch(0);
+
+  for (int t = 0; t < p.L; ++t) {
+    const int b = t & 1;
+    if (tid < DK) {
+      qs[b][tid] = qn;
+      ks[b][tid] = kn;
+      as_[b][tid] = an;
+    }
+    const f32x4 vv = vn;
+    const float beta = bn;
+    const size_t it = ((size_t)n * p.L + t) * p.H + h;
+    if (t + 1 < p.L) fetch(t + 1);
+    __syncthreads();
+
+    f32x4 r = zero4(), s = zero4();
+#pragma unroll
+    for (int u = 0; u < RP; ++u) {
+      const int row = rg * RP + u;
+      m[u] *= as_[b][row];
+      r += m[u] * ks[b][row];
+      s += m[u] * qs[b][row];
+    }
+    red_r[rg][cq] = r;
+    red_s[rg][cq] = s;
+    if (tid < 64) {
+      float d = 0.f;
+      for (int i = tid; i < DK; i += 64) d += qs[b][i] * ks[b][i];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      if (tid == 0) qk_s = d;
+    }
+    __syncthreads();
+
+    f32x4 R = zero4(), S = zero4();
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      R += red_r[g][cq];
+      S += red_s[g][cq];
+    }
+    f32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = beta * (vv[e] - R[e]);
+#pragma unroll
+    for (int u = 0; u < RP; ++u) m[u] += ks[b][rg * RP + u] * w;
+    if (rg == 0) {
+      E *o = (E *)p.o + it * DV + 4 * cq;
+      const float qk = qk_s;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = to_e<E>(S[e] + w[e] * qk);
+    }
+    const int dst = p.dst[(size_t)n * p.L + t];
+    if (dst >= 0 && dst < p.P) {
+      float *out = p.pool + (size_t)dst * slot + head;
+#pragma unroll
+      for (int u = 0; u < RP; ++u) *(f32x4 *)(out + (size_t)(rg * RP + u) * DV + 4 * cq) = m[u];
+    }
+  }
+}
+
 template <typename E, int DK, int DV>
 hipError_t launch_g(const StepParams &p, int gate, hipStream_t stream) {
   const int blocks = p.N * p.H;
@@ -112,7 +213,33 @@ hipError_t launch_e(const StepParams &p, int dk, int dv, int gate, hipStream_t s
   return hipErrorInvalidValue;
 }
 
+template <typename E, int DK, int DV>
+hipError_t launch_dg(const DecodeParams &p, int gate, hipStream_t stream) {
+  const int blocks = p.N * p.H;
+  if (blocks == 0) return hipSuccess;
+  switch (gate) {
+    case GATE_NONE: hipLaunchKernelGGL((decode_kernel<E, DK, DV, GATE_NONE>), dim3(blocks), dim3(256), 0, stream, p); break;
+    case GATE_HEAD: hipLaunchKernelGGL((decode_kernel<E, DK, DV, GATE_HEAD>), dim3(blocks), dim3(256), 0, stream, p); break;
+    case GATE_KEY: hipLaunchKernelGGL((decode_kernel<E, DK, DV, GATE_KEY>), dim3(blocks), dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_de(const DecodeParams &p, int dk, int dv, int gate, hipStream_t stream) {
+  if (dk == 128 && dv == 128) return launch_dg<E, 128, 128>(p, gate, stream);
+  if (dk == 128 && dv == 64) return launch_dg<E, 128, 64>(p, gate, stream);
+  if (dk == 64 && dv == 128) return launch_dg<E, 64, 128>(p, gate, stream);
+  if (dk == 64 && dv == 64) return launch_dg<E, 64, 64>(p, gate, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_decode(const DecodeParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream) {
+  return dtype == 1 ? launch_de<bf16>(p, dk, dv, gate, stream) : launch_de<float>(p, dk, dv, gate, stream);
+}
 
 hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream) {
   return dtype == 1 ? launch_e<bf16>(p, dk, dv, gate, stream) : launch_e<float>(p, dk, dv, gate, stream);

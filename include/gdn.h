@@ -119,6 +119,38 @@ typedef struct {
   void *o;                /* out: [N, H, d_v], dtype                                 */
 } gdn_step_args;
 
+/* Serving decode: L tokens per stream against a pool of states, in one call.  The
+ * per-token update is the one of gdn_fwd_recurrent_step (the constant-cost decode
+ * update of "Decoding Hybrid Linear Attention Architectures", sec. 6); the pages fix
+ * no layout for the states of many streams, so the pool and slot convention here is
+ * this library's own.  Each stream's state is read once from its slot, carried
+ * through its L tokens on the GPU, and written only where a slot is given:
+ *   - plain decoding: dst_slots[n, L-1] = src_slots[n], the other entries -1;
+ *   - speculative drafts: one spare slot per draft token; after verification the
+ *     slot of the last accepted token is the next call's src slot (no copy).
+ * Slots are indices into state_pool.  A stream whose src slot is outside
+ * [0, pool_size) is padding: nothing is read or written for it (its o rows are left
+ * as they are).  A dst entry outside [0, pool_size) stores nothing.  The dst slots of
+ * one call must differ from each other and from the other streams' src slots (a
+ * stream's own src slot may be reused); otherwise the pool's contents are undefined.
+ * Slots are device data, so out-of-range values cannot be reported: they are
+ * skipped as described. */
+typedef struct {
+  int N, L, H, d_k, d_v;  /* streams, tokens per stream (>= 1), heads, head dims (64/128) */
+  gdn_dtype dtype;        /* dtype of q, k, v, o                                      */
+  gdn_gate gate;
+  const void *q;          /* [N, L, H, d_k]                                           */
+  const void *k;          /* [N, L, H, d_k]                                           */
+  const void *v;          /* [N, L, H, d_v]                                           */
+  const float *beta;      /* [N, L, H]                                                */
+  const float *log_alpha; /* NONE: NULL; HEAD: [N,L,H]; KEY: [N,L,H,d_k]              */
+  float *state_pool;      /* in/out: [pool_size, H, d_k, d_v] fp32 (M = S^T), device  */
+  int pool_size;          /* number of slots (>= 1)                                   */
+  const int32_t *src_slots; /* [N] device: slot each stream's state is read from     */
+  const int32_t *dst_slots; /* [N, L] device: slot receiving the state after token t */
+  void *o;                /* out: [N, L, H, d_v], dtype                               */
+} gdn_decode_args;
+
 /* Bytes of device workspace gdn_fwd_chunked needs for these arguments; 0 means none.
  * Returns 0 for arguments that gdn_fwd_chunked would reject.
  *   - with cu_seqlens (N <= 8192): a processing-order table, 4 N bytes rounded up to 256;
@@ -135,6 +167,10 @@ int gdn_fwd_chunked(const gdn_fwd_args *args, void *hip_stream);
 
 /* One decode token per stream: writes o and updates state in place. */
 int gdn_fwd_recurrent_step(const gdn_step_args *args, void *hip_stream);
+
+/* Serving decode (see gdn_decode_args): writes o for the active streams and the
+ * requested pool slots; allocates nothing. */
+int gdn_fwd_decode(const gdn_decode_args *args, void *hip_stream);
 
 /* Static description of a status code (never NULL). */
 const char *gdn_status_str(int status);

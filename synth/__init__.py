@@ -115,6 +115,33 @@ def decode_inputs(N, H, dk, dv, steps, gate="head", dtype="bf16", seed=0):
     return dict(q=q, k=k, v=v, beta=beta, log_alpha=la, gate=gate, dtype=dtype)
 
 
+def pool_decode_inputs(N, L, H, dk, dv, pool_size, gate="head", dtype="bf16", seed=0,
+                       store="last", padding=0, state_std=0.05):
+    """Inputs of one pooled decode call: tokens q,k [N,L,H,dk], v [N,L,H,dv], beta
+    [N,L,H], log_alpha; a pool [P,H,dk,dv] of N(0, state_std^2) states; src_slots
+    int32 [N] drawn without replacement from a random permutation of the slots, the
+    first ``padding`` streams set to -1 (padding); dst_slots int32 [N,L]:
+    ``store="last"`` writes the last state back to the stream's own slot (plain
+    decoding), ``"all"`` gives every token a spare slot of its own (speculative
+    drafts), ``"none"`` stores nothing."""
+    g = torch.Generator().manual_seed(int(seed))
+    q, k, v, beta, la = _draw_tokens(g, (N, L), H, dk, dv, gate, _DTYPES[dtype])
+    pool = torch.randn(pool_size, H, dk, dv, generator=g) * float(state_std)
+    need = N + (N * L if store == "all" else 0)
+    assert pool_size >= need, "pool too small for the requested slots"
+    perm = torch.randperm(pool_size, generator=g).to(torch.int32)
+    src = perm[:N].clone()
+    src[:padding] = -1
+    dst = torch.full((N, L), -1, dtype=torch.int32)
+    if store == "last":
+        dst[:, -1] = src
+    elif store == "all":
+        dst = perm[N:N + N * L].reshape(N, L).clone()
+        dst[:padding] = -1
+    return dict(q=q, k=k, v=v, beta=beta, log_alpha=la, state_pool=pool, src_slots=src,
+                dst_slots=dst, gate=gate, dtype=dtype)
+
+
 def decode_initial_states(final_states: torch.Tensor, batch: int) -> torch.Tensor:
     """Decode streams start from the prefill's final states, tiled: stream s takes
     sequence s mod N_prefill."""

@@ -49,7 +49,7 @@ def fwd(g, a):
 
 
 def test_header_declares_the_boundary(g):
-    assert g.header_functions() == ["gdn_fwd_chunked", "gdn_fwd_recurrent_step",
+    assert g.header_functions() == ["gdn_fwd_chunked", "gdn_fwd_decode", "gdn_fwd_recurrent_step",
                                     "gdn_fwd_workspace_size", "gdn_status_str", "gdn_version"]
 
 
@@ -162,6 +162,43 @@ def test_step_host_validation(g, change, status):
     assert g._lib.gdn_fwd_recurrent_step(ctypes.byref(step_args(g, **change)), None) == status
 
 
+def decode_args(g, **kw):
+    a = g.DecodeArgs(N=4, L=3, H=2, d_k=128, d_v=64, dtype=g.GDN_BF16, gate=g.GDN_GATE_HEAD, pool_size=8)
+    a.q, a.k, a.v, a.beta, a.log_alpha, a.state_pool, a.src_slots, a.dst_slots, a.o = (fake(i) for i in range(9))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(N=0), OK),
+    (dict(N=0, q=None), OK),
+    (dict(L=0), INVALID),
+    (dict(pool_size=0), INVALID),
+    (dict(H=0), INVALID),
+    (dict(N=-1), INVALID),
+    (dict(d_k=32), UNSUPPORTED),
+    (dict(d_v=256), UNSUPPORTED),
+    (dict(N=1 << 20, H=1 << 12), UNSUPPORTED),
+    (dict(state_pool=None), INVALID),
+    (dict(src_slots=None), INVALID),
+    (dict(dst_slots=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(log_alpha=None), INVALID),
+    (dict(gate=0), INVALID),
+    (dict(gate=3), INVALID),
+    (dict(dtype=2), INVALID),
+    (dict(state_pool=fake(5, 8)), INVALID),
+    (dict(src_slots=fake(6, 2)), INVALID),
+])
+def test_decode_host_validation(g, change, status):
+    assert g._lib.gdn_fwd_decode(ctypes.byref(decode_args(g, **change)), None) == status
+
+
+def test_decode_null_args(g):
+    assert g._lib.gdn_fwd_decode(None, None) == INVALID
+
+
 # ------------------------------------------------------------ binding checks
 def fwd_tensors(B=2, T=5, H=3, dk=64, dv=64, dtype=torch.bfloat16):
     return dict(q=torch.zeros(B, T, H, dk, dtype=dtype), k=torch.zeros(B, T, H, dk, dtype=dtype),
@@ -199,3 +236,21 @@ def test_binding_rejects_bad_step_tensors(g):
         g.recurrent_step(**dict(ok, log_alpha=torch.zeros(N, H, 5)))
     with pytest.raises(ValueError, match="GPU device"):
         g.recurrent_step(**ok)
+
+
+def test_binding_rejects_bad_decode_tensors(g):
+    N, L, H, dk, dv, P = 3, 2, 2, 64, 64, 5
+    q = torch.zeros(N, L, H, dk, dtype=torch.bfloat16)
+    ok = dict(q=q, k=q.clone(), v=torch.zeros(N, L, H, dv, dtype=torch.bfloat16), beta=torch.zeros(N, L, H),
+              log_alpha=torch.zeros(N, L, H), state_pool=torch.zeros(P, H, dk, dv),
+              src_slots=torch.zeros(N, dtype=torch.int32), dst_slots=torch.zeros(N, L, dtype=torch.int32))
+    for change, msg in [(dict(state_pool=torch.zeros(P, H, dv, dk + 1)), "state_pool must"),
+                        (dict(state_pool=torch.zeros(0, H, dk, dv)), "state_pool must"),
+                        (dict(src_slots=torch.zeros(N, dtype=torch.int64)), "src_slots must"),
+                        (dict(dst_slots=torch.zeros(N, L + 1, dtype=torch.int32)), "dst_slots must"),
+                        (dict(log_alpha=torch.zeros(N, L, H, 5)), "log_alpha must"),
+                        (dict(beta=torch.zeros(N, H)), "beta must"),
+                        (dict(q=torch.zeros(N, 0, H, dk, dtype=torch.bfloat16)), "at least one token"),
+                        (dict(), "GPU device")]:
+        with pytest.raises(ValueError, match=msg):
+            g.decode(**dict(ok, **change))
