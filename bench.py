@@ -165,6 +165,41 @@ def time_decode(gdn, spec, final_states, steps=64):
             "hbm_gbs": bytes_step / (ms / 1e3) / 1e9, "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
 
 
+def time_pool_decode(gdn, N, L, H, dk, dv, store, steps=64):
+    """gdn_fwd_decode: L tokens for each of N streams per call, states in a pool.
+    ``store="last"`` writes each stream's state back in place; ``"all"`` stores the
+    state after every token into slots of its own (speculative drafts)."""
+    import torch
+    import synth
+    P = N + (N * L if store == "all" else 0)
+    inp = synth.pool_decode_inputs(N, L, H, dk, dv, P, "head", "bf16", seed=97, store=store)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    out = torch.empty((N, L, H, dv), dtype=d["q"].dtype, device="cuda")
+    args = (d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["state_pool"], d["src_slots"], d["dst_slots"])
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    gdn.decode(*args, out=out)
+    torch.cuda.synchronize()
+    warm = max(4, int(SETTLE_MS / 1e3 / (time.perf_counter() - t)) + 1)
+    for _ in range(warm):
+        gdn.decode(*args, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        gdn.decode(*args, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    state = 4 * dk * dv
+    writes = 1 if store == "last" else L
+    tok = 2 * (2 * dk + 2 * dv) + 8  # q, k, v, o in bf16; beta and log alpha in fp32
+    nbytes = N * H * (state * (1 + writes) + L * tok)
+    return {"workload": "gdn-decode-pool-bf16-N%d-L%d-H%d-d%d-store-%s" % (N, L, H, dk, store),
+            "ms_per_step": ms, "tokens_per_s": N * L / (ms / 1e3), "alg_bytes": nbytes,
+            "hbm_gbs": nbytes / (ms / 1e3) / 1e9, "hbm_frac": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+
+
 def cpu_baseline(inp, H):
     """The fp64 oracle on the host cores, on the whole workload (bounded: a few
     seconds), best of two runs."""
@@ -280,6 +315,9 @@ def main():
                                         d["cu_seqlens"])
                 torch.cuda.synchronize()
                 extra.append(time_decode(gdn, synth.WORKLOADS[name], fs))
+                del fs
+                for store in ("last", "all"):
+                    extra.append(time_pool_decode(gdn, 256, 4, 16, 128, 128, store))
             del wsets
             torch.cuda.empty_cache()
             extra.append(r)

@@ -1,4 +1,4 @@
-// gdn_step.hip -- one decode token per stream, state updated in place.
+// gdn_step.hip -- decode: one token per stream in place, and L tokens per stream against a state pool.
 //
 // The recurrent mode of the (gated) delta rule ("Decoding Hybrid Linear Attention
 // Architectures", sec. 6: constant-cost update of the fixed-size state per decoded
@@ -11,7 +11,9 @@
 //
 // One workgroup (256 threads) per (stream, head).  Thread (row group rg, column
 // quad cq) holds d_k / RG rows x 4 columns of M in registers: 16-byte coalesced
-// loads and stores, partial reductions combined in LDS in a fixed order.
+// loads and stores, partial reductions combined in LDS in a fixed order.  The same
+// body serves the pooled decode below (states addressed by slot, one or more tokens
+// per stream).
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -45,6 +47,11 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
   f32x4 m[RP];
 #pragma unroll
   for (int u = 0; u < RP; ++u) m[u] = *(const f32x4 *)(st + (size_t)(rg * RP + u) * DV + 4 * cq);
+  const E *vp = (const E *)p.v + (size_t)pair * DV + 4 * cq;  // needed only after the reduction
+  f32x4 vv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vv[e] = to_f(vp[e]);
+  const float beta = p.beta[pair];
   __syncthreads();
 
   f32x4 r = zero4(), s = zero4();
@@ -72,11 +79,9 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
     R += red_r[g][cq];
     S += red_s[g][cq];
   }
-  const E *v = (const E *)p.v + (size_t)pair * DV + 4 * cq;
-  const float beta = p.beta[pair];
   f32x4 w;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = beta * (to_f(v[e]) - R[e]);
+  for (int e = 0; e < 4; ++e) w[e] = beta * (vv[e] - R[e]);
 #pragma unroll
   for (int u = 0; u < RP; ++u) {
     const int row = rg * RP + u;
@@ -90,21 +95,103 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
   }
 }
 
+// Serving decode with one token per stream (L = 1): the body of recurrent_step_kernel
+// with the state read from and written to pool slots.
+template <typename E, int DK, int DV, int GATE>
+__global__ __launch_bounds__(256) void decode_one_kernel(DecodeParams p) {
+  constexpr int CQ = DV / 4;
+  constexpr int RG = 256 / CQ;
+  constexpr int RP = DK / RG;
+  static_assert(RP >= 1 && RG * RP == DK, "decode geometry");
+  __shared__ float qs[DK], ks[DK], as_[DK];
+  __shared__ f32x4 red_r[RG][CQ], red_s[RG][CQ];
+  __shared__ float qk_s;
+
+  const int pair = blockIdx.x, n = pair / p.H, h = pair % p.H;  // token index == pair (L = 1)
+  const int src = p.src[n];
+  if (src < 0 || src >= p.P) return;  // padding stream: nothing read or written
+  const int tid = threadIdx.x, cq = tid % CQ, rg = tid / CQ;
+  if (tid < DK) {
+    qs[tid] = to_f(((const E *)p.q)[(size_t)pair * DK + tid]);
+    ks[tid] = to_f(((const E *)p.k)[(size_t)pair * DK + tid]);
+    float a = 1.f;
+    if (GATE == GATE_HEAD) a = __expf(p.log_alpha[pair]);
+    if (GATE == GATE_KEY) a = __expf(p.log_alpha[(size_t)pair * DK + tid]);
+    as_[tid] = a;
+  }
+  const size_t slot = (size_t)p.H * DK * DV, head = (size_t)h * DK * DV;
+  const float *st = p.pool + (size_t)src * slot + head;
+  f32x4 m[RP];
+#pragma unroll
+  for (int u = 0; u < RP; ++u) m[u] = *(const f32x4 *)(st + (size_t)(rg * RP + u) * DV + 4 * cq);
+  const E *vp = (const E *)p.v + (size_t)pair * DV + 4 * cq;  // needed only after the reduction
+  f32x4 vv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vv[e] = to_f(vp[e]);
+  const float beta = p.beta[pair];
+  __syncthreads();
+
+  f32x4 r = zero4(), s = zero4();
+#pragma unroll
+  for (int u = 0; u < RP; ++u) {
+    const int row = rg * RP + u;
+    m[u] *= as_[row];
+    r += m[u] * ks[row];
+    s += m[u] * qs[row];
+  }
+  red_r[rg][cq] = r;
+  red_s[rg][cq] = s;
+  if (tid < 64) {
+    float d = 0.f;
+    for (int i = tid; i < DK; i += 64) d += qs[i] * ks[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+    if (tid == 0) qk_s = d;
+  }
+  __syncthreads();
+
+  f32x4 R = zero4(), S = zero4();
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    R += red_r[g][cq];
+    S += red_s[g][cq];
+  }
+  f32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = beta * (vv[e] - R[e]);
+#pragma unroll
+  for (int u = 0; u < RP; ++u) m[u] += ks[rg * RP + u] * w;
+  if (rg == 0) {
+    E *o = (E *)p.o + (size_t)pair * DV + 4 * cq;
+    const float qk = qk_s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = to_e<E>(S[e] + w[e] * qk);
+  }
+  const int dst = p.dst[n];
+  if (dst >= 0 && dst < p.P) {
+    float *out = p.pool + (size_t)dst * slot + head;
+#pragma unroll
+    for (int u = 0; u < RP; ++u) *(f32x4 *)(out + (size_t)(rg * RP + u) * DV + 4 * cq) = m[u];
+  }
+}
+
 // Serving decode: L tokens per stream in one launch, the state read once from its
 // pool slot, kept in registers across the tokens, and stored only where a slot is
 // given (every token for speculative drafts, the last one for plain decoding).  The
-// per-token body is the one above; the token's q, k, decay, v and beta are fetched
-// into registers one token ahead, and q, k and the decay alternate between two LDS
-// buffers, so two barriers per token suffice.
+// per-token body is the one above.  The inputs of up to TB tokens are staged in LDS
+// together, issued with the state load, so one memory latency covers them; q . k of
+// every staged token is formed once per batch, and the partial sums alternate
+// between two LDS buffers, so each token needs a single barrier.
 template <typename E, int DK, int DV, int GATE>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int CQ = DV / 4;
   constexpr int RG = 256 / CQ;
   constexpr int RP = DK / RG;
+  constexpr int TB = 8;  // tokens staged in LDS at a time
   static_assert(RP >= 1 && RG * RP == DK, "decode geometry");
-  __shared__ float qs[2][DK], ks[2][DK], as_[2][DK];
-  __shared__ f32x4 red_r[RG][CQ], red_s[RG][CQ];
-  __shared__ float qk_s;
+  __shared__ float qs[TB][DK], ks[TB][DK], as_[GATE == GATE_KEY ? TB : 1][DK], vs[TB][DV];
+  __shared__ float bs[TB], ah[TB], qk_s[TB];
+  __shared__ f32x4 red_r[2][RG][CQ], red_s[2][RG][CQ];
 
   const int n = blockIdx.x / p.H, h = blockIdx.x % p.H;
   const int src = p.src[n];
@@ -116,77 +203,76 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int u = 0; u < RP; ++u) m[u] = *(const f32x4 *)(st + (size_t)(rg * RP + u) * DV + 4 * cq);
 
-  float qn = 0.f, kn = 0.f, an = 1.f, bn = 0.f;
-  f32x4 vn;
-  auto fetch = [&](int t) {
-    const size_t i = ((size_t)n * p.L + t) * p.H + h;  // (stream, token, head)
-    if (tid < DK) {
-      qn = to_f(((const E *)p.q)[i * DK + tid]);
-      kn = to_f(((const E *)p.k)[i * DK + tid]);
-      if (GATE == GATE_HEAD) an = __expf(p.log_alpha[i]);
-      if (GATE == GATE_KEY) an = __expf(p.log_alpha[i * DK + tid]);
+  for (int t0 = 0; t0 < p.L; t0 += TB) {
+    const int nt = p.L - t0 < TB ? p.L - t0 : TB;
+    if (t0 > 0) __syncthreads();  // the previous batch is done with the staged inputs
+    const size_t i0 = ((size_t)n * p.L + t0) * p.H + h;  // (stream, token t0, head)
+    for (int x = tid; x < nt * DK; x += 256) {
+      const int tt = x / DK, c = x % DK;
+      const size_t i = i0 + (size_t)tt * p.H;
+      qs[tt][c] = to_f(((const E *)p.q)[i * DK + c]);
+      ks[tt][c] = to_f(((const E *)p.k)[i * DK + c]);
+      if (GATE == GATE_KEY) as_[tt][c] = __expf(p.log_alpha[i * DK + c]);
     }
-    const E *vp = (const E *)p.v + i * DV + 4 * cq;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vn[e] = to_f(vp[e]);
-    bn = p.beta[i];
-  };
-  fetch(0);
-
-  for (int t = 0; t < p.L; ++t) {
-    const int b = t & 1;
-    if (tid < DK) {
-      qs[b][tid] = qn;
-      ks[b][tid] = kn;
-      as_[b][tid] = an;
+    for (int x = tid; x < nt * DV; x += 256) {
+      const int tt = x / DV, c = x % DV;
+      vs[tt][c] = to_f(((const E *)p.v)[(i0 + (size_t)tt * p.H) * DV + c]);
     }
-    const f32x4 vv = vn;
-    const float beta = bn;
-    const size_t it = ((size_t)n * p.L + t) * p.H + h;
-    if (t + 1 < p.L) fetch(t + 1);
+    if (tid < nt) {
+      const size_t i = i0 + (size_t)tid * p.H;
+      bs[tid] = p.beta[i];
+      ah[tid] = GATE == GATE_HEAD ? __expf(p.log_alpha[i]) : 1.f;
+    }
     __syncthreads();
-
-    f32x4 r = zero4(), s = zero4();
-#pragma unroll
-    for (int u = 0; u < RP; ++u) {
-      const int row = rg * RP + u;
-      m[u] *= as_[b][row];
-      r += m[u] * ks[b][row];
-      s += m[u] * qs[b][row];
-    }
-    red_r[rg][cq] = r;
-    red_s[rg][cq] = s;
-    if (tid < 64) {
+    // q . k of each staged token: wave w takes tokens w, w + 4
+    for (int tt = tid >> 6; tt < nt; tt += 4) {
       float d = 0.f;
-      for (int i = tid; i < DK; i += 64) d += qs[b][i] * ks[b][i];
+      for (int c = tid & 63; c < DK; c += 64) d += qs[tt][c] * ks[tt][c];
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
-      if (tid == 0) qk_s = d;
+      if ((tid & 63) == 0) qk_s[tt] = d;
     }
-    __syncthreads();
 
-    f32x4 R = zero4(), S = zero4();
+    for (int tt = 0; tt < nt; ++tt) {
+      const int t = t0 + tt, b = t & 1;
+      f32x4 r = zero4(), s = zero4();
 #pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      R += red_r[g][cq];
-      S += red_s[g][cq];
-    }
-    f32x4 w;
+      for (int u = 0; u < RP; ++u) {
+        const int row = rg * RP + u;
+        if (GATE == GATE_KEY) m[u] *= as_[tt][row];
+        if (GATE == GATE_HEAD) m[u] *= ah[tt];
+        r += m[u] * ks[tt][row];
+        s += m[u] * qs[tt][row];
+      }
+      red_r[b][rg][cq] = r;
+      red_s[b][rg][cq] = s;
+      __syncthreads();
+
+      f32x4 R = zero4(), S = zero4();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = beta * (vv[e] - R[e]);
+      for (int g = 0; g < RG; ++g) {
+        R += red_r[b][g][cq];
+        S += red_s[b][g][cq];
+      }
+      const float beta = bs[tt];
+      const f32x4 vv = *(const f32x4 *)&vs[tt][4 * cq];
+      f32x4 w;
 #pragma unroll
-    for (int u = 0; u < RP; ++u) m[u] += ks[b][rg * RP + u] * w;
-    if (rg == 0) {
-      E *o = (E *)p.o + it * DV + 4 * cq;
-      const float qk = qk_s;
+      for (int e = 0; e < 4; ++e) w[e] = beta * (vv[e] - R[e]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = to_e<E>(S[e] + w[e] * qk);
-    }
-    const int dst = p.dst[(size_t)n * p.L + t];
-    if (dst >= 0 && dst < p.P) {
-      float *out = p.pool + (size_t)dst * slot + head;
+      for (int u = 0; u < RP; ++u) m[u] += ks[tt][rg * RP + u] * w;
+      if (rg == 0) {
+        E *o = (E *)p.o + (i0 + (size_t)tt * p.H) * DV + 4 * cq;
+        const float qk = qk_s[tt];
 #pragma unroll
-      for (int u = 0; u < RP; ++u) *(f32x4 *)(out + (size_t)(rg * RP + u) * DV + 4 * cq) = m[u];
+        for (int e = 0; e < 4; ++e) o[e] = to_e<E>(S[e] + w[e] * qk);
+      }
+      const int dst = p.dst[(size_t)n * p.L + t];
+      if (dst >= 0 && dst < p.P) {
+        float *out = p.pool + (size_t)dst * slot + head;
+#pragma unroll
+        for (int u = 0; u < RP; ++u) *(f32x4 *)(out + (size_t)(rg * RP + u) * DV + 4 * cq) = m[u];
+      }
     }
   }
 }
@@ -217,6 +303,15 @@ template <typename E, int DK, int DV>
 hipError_t launch_dg(const DecodeParams &p, int gate, hipStream_t stream) {
   const int blocks = p.N * p.H;
   if (blocks == 0) return hipSuccess;
+  if (p.L == 1) {
+    switch (gate) {
+      case GATE_NONE: hipLaunchKernelGGL((decode_one_kernel<E, DK, DV, GATE_NONE>), dim3(blocks), dim3(256), 0, stream, p); break;
+      case GATE_HEAD: hipLaunchKernelGGL((decode_one_kernel<E, DK, DV, GATE_HEAD>), dim3(blocks), dim3(256), 0, stream, p); break;
+      case GATE_KEY: hipLaunchKernelGGL((decode_one_kernel<E, DK, DV, GATE_KEY>), dim3(blocks), dim3(256), 0, stream, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (gate) {
     case GATE_NONE: hipLaunchKernelGGL((decode_kernel<E, DK, DV, GATE_NONE>), dim3(blocks), dim3(256), 0, stream, p); break;
     case GATE_HEAD: hipLaunchKernelGGL((decode_kernel<E, DK, DV, GATE_HEAD>), dim3(blocks), dim3(256), 0, stream, p); break;

@@ -70,7 +70,7 @@ def check(gdn, inp):
 
 
 @pytest.mark.parametrize("store", ["last", "all"])
-@pytest.mark.parametrize("L", [1, 3, 8])
+@pytest.mark.parametrize("L", [1, 3, 8, 13])
 @pytest.mark.parametrize("gate", ["none", "head", "key"])
 def test_decode_bf16(gdn, gate, L, store):
     inp = synth.pool_decode_inputs(6, L, 3, 128, 128, 6 + 6 * L + 5, gate, "bf16", seed=L, store=store,
