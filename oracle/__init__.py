@@ -11,7 +11,11 @@ Parity status: every function here is pinned.  ``fwd`` and ``step`` by
 ``tests/test_oracle_pins.py`` (closed forms, invariants, an autograd-derived
 gradient step, exact rational fixtures under ``tests/golden/`` and planted-mistake
 checks); ``decode_pool`` by ``tests/test_oracle_decode.py`` (against ``fwd`` over
-the same tokens and over every stored prefix, chained and speculative calls).
+the same tokens and over every stored prefix, chained and speculative calls); the
+additive write (``write="add"``) and the constant per-head gate by
+``tests/test_oracle_additive.py`` (RetNet's decay-mask parallel form, the
+gated-linear-attention brute-force sum, the plain linear-transformer sum, agreement
+with the delta rule on orthonormal keys, linearity and a planted mutant).
 """
 from __future__ import annotations
 
@@ -27,6 +31,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 GATES = {"none": 0, "head": 1, "key": 2}
+WRITES = {"delta": 0, "add": 1}
 
 
 def build(force: bool = False, src: str = _SRC, out: str = _LIB) -> str:
@@ -54,10 +59,10 @@ def _declare(lib):
     ip = ctypes.POINTER(ctypes.c_int64)
     lib.oracle_fwd.restype = ctypes.c_int
     lib.oracle_fwd.argtypes = [ctypes.c_int, ip, ip, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                               ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+                               ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
     lib.oracle_step.restype = ctypes.c_int
     lib.oracle_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                ctypes.c_int, dp, dp, dp, dp, dp, dp, dp]
+                                ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -79,16 +84,26 @@ def _ptr(a):
 def infer_gate(log_alpha, token_ndim: int) -> str:
     if log_alpha is None:
         return "none"
+    if np.ndim(log_alpha) == 1:
+        return "const"
     return "head" if np.ndim(log_alpha) == token_ndim else "key"
 
 
+def _per_token(log_alpha, lead):
+    """A constant per-head log decay [H] as the same value at every token position
+    [*lead, H] (a layout change only)."""
+    return np.ascontiguousarray(np.broadcast_to(log_alpha, tuple(lead) + log_alpha.shape))
+
+
 def fwd(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None, gate=None,
-        nthreads: int = 0, lib=None):
+        nthreads: int = 0, lib=None, write: str = "delta"):
     """Run the recurrence over whole sequences.
 
-    Batch mode: q,k [B,T,H,d_k], v [B,T,H,d_v], beta [B,T,H], log_alpha None |
-    [B,T,H] | [B,T,H,d_k]; varlen mode: B == 1 and ``cu_seqlens`` (N+1 offsets).
-    ``initial_state`` None (zeros) or [N,H,d_k,d_v] with M = S^T.
+    Batch mode: q,k [B,T,H,d_k], v [B,T,H,d_v], beta [B,T,H] (None with the additive
+    write), log_alpha None | [H] (one constant decay per head) | [B,T,H] | [B,T,H,d_k];
+    varlen mode: B == 1 and ``cu_seqlens`` (N+1 offsets).  ``initial_state`` None
+    (zeros) or [N,H,d_k,d_v] with M = S^T.  ``write``: "delta" (erase, then write) or
+    "add" (M += k v^T).
     Returns (o [B,T,H,d_v], final_state [N,H,d_k,d_v]) as fp64 numpy arrays.
     """
     q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
@@ -97,6 +112,8 @@ def fwd(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None, gate
     dv = v.shape[-1]
     if gate is None:
         gate = infer_gate(log_alpha, 3)
+    if gate == "const":
+        log_alpha, gate = _per_token(log_alpha, (B, T)), "head"
     if cu_seqlens is not None:
         cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64)
         assert B == 1 and cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
@@ -110,16 +127,17 @@ def fwd(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None, gate
     lib = lib or load()
     rc = lib.oracle_fwd(N, start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                         lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
-                        GATES[gate], _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                        GATES[gate], WRITES[write], _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
                         _ptr(initial_state), _ptr(o), _ptr(fs), int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_fwd failed (%d)" % rc)
     return o, fs
 
 
-def step(q, k, v, beta, log_alpha, state, gate=None, lib=None):
-    """One token per stream: q,k [N,H,d_k], v [N,H,d_v], beta [N,H], log_alpha None |
-    [N,H] | [N,H,d_k], state [N,H,d_k,d_v].  Returns (o [N,H,d_v], new_state)."""
+def step(q, k, v, beta, log_alpha, state, gate=None, lib=None, write: str = "delta"):
+    """One token per stream: q,k [N,H,d_k], v [N,H,d_v], beta [N,H] (None with the
+    additive write), log_alpha None | [H] | [N,H] | [N,H,d_k], state [N,H,d_k,d_v].
+    Returns (o [N,H,d_v], new_state)."""
     q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
     log_alpha = _f64(log_alpha)
     st = _f64(state).copy()
@@ -127,20 +145,24 @@ def step(q, k, v, beta, log_alpha, state, gate=None, lib=None):
     dv = v.shape[-1]
     if gate is None:
         gate = infer_gate(log_alpha, 2)
+    if gate == "const":
+        log_alpha, gate = _per_token(log_alpha, (N,)), "head"
     o = np.zeros((N, H, dv), dtype=np.float64)
     lib = lib or load()
-    rc = lib.oracle_step(N, H, dk, dv, GATES[gate], _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+    rc = lib.oracle_step(N, H, dk, dv, GATES[gate], WRITES[write], _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                          _ptr(log_alpha), _ptr(st), _ptr(o))
     if rc != 0:
         raise RuntimeError("oracle_step failed (%d)" % rc)
     return o, st
 
 
-def decode_pool(q, k, v, beta, log_alpha, pool, src_slots, dst_slots, gate=None, lib=None):
+def decode_pool(q, k, v, beta, log_alpha, pool, src_slots, dst_slots, gate=None, lib=None,
+                write: str = "delta"):
     """L decode tokens per stream against a pool of states, by repeated ``step``.
 
-    q,k [N,L,H,d_k], v [N,L,H,d_v], beta [N,L,H], log_alpha None | [N,L,H] |
-    [N,L,H,d_k]; pool [P,H,d_k,d_v] (M = S^T); src_slots [N] and dst_slots [N,L]
+    q,k [N,L,H,d_k], v [N,L,H,d_v], beta [N,L,H] (None with the additive write),
+    log_alpha None | [H] | [N,L,H] | [N,L,H,d_k]; pool [P,H,d_k,d_v] (M = S^T);
+    src_slots [N] and dst_slots [N,L]
     integers.  Stream n is active when 0 <= src_slots[n] < P: its state is read from
     that slot (all reads happen before any write), its L tokens run through the
     recurrence in order, and the state after token t is stored into slot
@@ -157,6 +179,8 @@ def decode_pool(q, k, v, beta, log_alpha, pool, src_slots, dst_slots, gate=None,
     P = pool.shape[0]
     if gate is None:
         gate = infer_gate(log_alpha, 3)
+    if gate == "const":
+        log_alpha, gate = _per_token(log_alpha, (N, L)), "head"
     o = np.full((N, L, H, dv), np.nan)
     out = pool.copy()
     act = np.nonzero((src >= 0) & (src < P))[0]
@@ -165,7 +189,8 @@ def decode_pool(q, k, v, beta, log_alpha, pool, src_slots, dst_slots, gate=None,
     states = pool[src[act]].copy()  # every read before any write
     for t in range(L):
         la = None if log_alpha is None else log_alpha[act, t]
-        o_t, states = step(q[act, t], k[act, t], v[act, t], beta[act, t], la, states, gate=gate, lib=lib)
+        bt = None if beta is None else beta[act, t]
+        o_t, states = step(q[act, t], k[act, t], v[act, t], bt, la, states, gate=gate, lib=lib, write=write)
         o[act, t] = o_t
         for j, n in enumerate(act):
             if 0 <= dst[n, t] < P:

@@ -20,6 +20,15 @@
  *     3. write:    M += beta * k (v - r)^T
  *     4. read:     o = M^T q        (the read uses the state after the write)
  *
+ *   With the additive write (write = ORACLE_WRITE_ADD) steps 2-3 are replaced by
+ *
+ *     2'. write:   M += k v^T       (no erase, no beta)
+ *
+ *   which is the gated-linear-attention update of the same sec. 3, item 4
+ *   (channel-wise forgetting without overwriting), RetNet's retention with a fixed
+ *   per-head decay ("Linear Attention Variants", RetNet section) and, without a
+ *   gate, the plain linear-transformer sum of that page's "The Shared Machinery".
+ *
  *   Steps 1-3 are the single-step update of "Decoding Hybrid Linear Attention
  *   Architectures", sec. 3 item 6 (decay, directional erase, overwriting write),
  *   which for a scalar gate is item 3 (gated delta rule) and without a gate is
@@ -31,7 +40,8 @@
  *
  * Layout: tokens of all sequences are packed; sequence n covers packed tokens
  * [start[n], start[n] + len[n]).  q,k: [tokens][H][d_k], v,o: [tokens][H][d_v],
- * beta: [tokens][H], log_alpha: NULL | [tokens][H] | [tokens][H][d_k],
+ * beta: [tokens][H] (NULL with the additive write), log_alpha: NULL | [tokens][H] |
+ * [tokens][H][d_k],
  * states: [N][H][d_k][d_v].  All arrays are fp64 and contiguous.
  */
 #include <math.h>
@@ -43,9 +53,10 @@
 #endif
 
 enum { ORACLE_GATE_NONE = 0, ORACLE_GATE_HEAD = 1, ORACLE_GATE_KEY = 2 };
+enum { ORACLE_WRITE_DELTA = 0, ORACLE_WRITE_ADD = 1 };
 
 /* One token of the recurrence on one head's state M (d_k x d_v, row-major). */
-static void oracle_token(int dk, int dv, int gate, const double *q, const double *k,
+static void oracle_token(int dk, int dv, int gate, int write, const double *q, const double *k,
                          const double *v, double beta, const double *log_alpha,
                          double *M, double *r, double *o) {
   int i, j;
@@ -59,6 +70,11 @@ static void oracle_token(int dk, int dv, int gate, const double *q, const double
       for (j = 0; j < dv; ++j) M[i * dv + j] *= a;
     }
   }
+  if (write == ORACLE_WRITE_ADD) {
+    /* 2'. additive write M += k v^T */
+    for (i = 0; i < dk; ++i)
+      for (j = 0; j < dv; ++j) M[i * dv + j] += k[i] * v[j];
+  } else {
   /* 2. retrieve r = M^T k */
   for (j = 0; j < dv; ++j) r[j] = 0.0;
   for (i = 0; i < dk; ++i)
@@ -68,6 +84,7 @@ static void oracle_token(int dk, int dv, int gate, const double *q, const double
     double bk = beta * k[i];
     for (j = 0; j < dv; ++j) M[i * dv + j] += bk * (v[j] - r[j]);
   }
+  }
   /* 4. read o = M^T q */
   for (j = 0; j < dv; ++j) o[j] = 0.0;
   for (i = 0; i < dk; ++i)
@@ -76,13 +93,14 @@ static void oracle_token(int dk, int dv, int gate, const double *q, const double
 
 /* Whole sequences.  Returns 0, or -1 on a bad argument / allocation failure. */
 int oracle_fwd(int N, const int64_t *start, const int64_t *len, int H, int dk, int dv,
-               int gate, const double *q, const double *k, const double *v,
+               int gate, int write, const double *q, const double *k, const double *v,
                const double *beta, const double *log_alpha, const double *initial_state,
                double *o, double *final_state, int nthreads) {
   int64_t pair;
   int failed = 0;
   if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   if (gate != ORACLE_GATE_NONE && log_alpha == NULL) return -1;
+  if (write != ORACLE_WRITE_ADD && beta == NULL) return -1;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
@@ -102,8 +120,8 @@ int oracle_fwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
       const double *la = NULL;
       if (gate == ORACLE_GATE_HEAD) la = log_alpha + th;
       if (gate == ORACLE_GATE_KEY) la = log_alpha + th * dk;
-      oracle_token(dk, dv, gate, q + th * dk, k + th * dk, v + th * dv, beta[th], la, M, r,
-                   o + th * dv);
+      oracle_token(dk, dv, gate, write, q + th * dk, k + th * dk, v + th * dv, beta ? beta[th] : 0.0,
+                   la, M, r, o + th * dv);
     }
     if (final_state) memcpy(final_state + ((size_t)n * H + h) * dk * dv, M, sizeof(double) * dk * dv);
     free(M);
@@ -114,20 +132,21 @@ int oracle_fwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
 
 /* One token per stream, state updated in place: q,k [N][H][d_k], v,o [N][H][d_v],
  * beta [N][H], log_alpha NULL | [N][H] | [N][H][d_k], state [N][H][d_k][d_v]. */
-int oracle_step(int N, int H, int dk, int dv, int gate, const double *q, const double *k,
+int oracle_step(int N, int H, int dk, int dv, int gate, int write, const double *q, const double *k,
                 const double *v, const double *beta, const double *log_alpha, double *state,
                 double *o) {
   int64_t pair;
   if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   if (gate != ORACLE_GATE_NONE && log_alpha == NULL) return -1;
+  if (write != ORACLE_WRITE_ADD && beta == NULL) return -1;
   for (pair = 0; pair < (int64_t)N * H; ++pair) {
     double *r = (double *)malloc(sizeof(double) * (size_t)dv);
     const double *la = NULL;
     if (!r) return -1;
     if (gate == ORACLE_GATE_HEAD) la = log_alpha + pair;
     if (gate == ORACLE_GATE_KEY) la = log_alpha + pair * dk;
-    oracle_token(dk, dv, gate, q + pair * dk, k + pair * dk, v + pair * dv, beta[pair], la,
-                 state + pair * dk * dv, r, o + pair * dv);
+    oracle_token(dk, dv, gate, write, q + pair * dk, k + pair * dk, v + pair * dv,
+                 beta ? beta[pair] : 0.0, la, state + pair * dk * dv, r, o + pair * dv);
     free(r);
   }
   return 0;
