@@ -22,7 +22,9 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gdn.h")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 0, -1, -2, -3, -4
 GDN_F32, GDN_BF16 = 0, 1
-GDN_GATE_NONE, GDN_GATE_HEAD, GDN_GATE_KEY = 0, 1, 2
+GDN_GATE_NONE, GDN_GATE_HEAD, GDN_GATE_KEY, GDN_GATE_HEAD_CONST = 0, 1, 2, 3
+GDN_WRITE_DELTA, GDN_WRITE_ADD = 0, 1
+WRITES = {"delta": GDN_WRITE_DELTA, "add": GDN_WRITE_ADD}
 CHUNK = 64
 
 
@@ -31,6 +33,7 @@ class FwdArgs(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
                 ("d_k", ctypes.c_int), ("d_v", ctypes.c_int), ("chunk", ctypes.c_int),
                 ("N", ctypes.c_int), ("dtype", ctypes.c_int), ("gate", ctypes.c_int),
+                ("write", ctypes.c_int),
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
                 ("initial_state", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
@@ -42,6 +45,7 @@ class StepArgs(ctypes.Structure):
     """Mirror of ``gdn_step_args``."""
     _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("d_k", ctypes.c_int),
                 ("d_v", ctypes.c_int), ("dtype", ctypes.c_int), ("gate", ctypes.c_int),
+                ("write", ctypes.c_int),
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
                 ("state", ctypes.c_void_p), ("o", ctypes.c_void_p)]
@@ -51,7 +55,7 @@ class DecodeArgs(ctypes.Structure):
     """Mirror of ``gdn_decode_args``."""
     _fields_ = [("N", ctypes.c_int), ("L", ctypes.c_int), ("H", ctypes.c_int),
                 ("d_k", ctypes.c_int), ("d_v", ctypes.c_int), ("dtype", ctypes.c_int),
-                ("gate", ctypes.c_int), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("gate", ctypes.c_int), ("write", ctypes.c_int), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
                 ("state_pool", ctypes.c_void_p), ("pool_size", ctypes.c_int),
                 ("src_slots", ctypes.c_void_p), ("dst_slots", ctypes.c_void_p), ("o", ctypes.c_void_p)]
@@ -125,8 +129,13 @@ def _same_device(tensors, ref):
                       "%s must be on the GPU device of q (%s), got %s" % (name, ref.device, t.device))
 
 
+def _check_write(write):
+    _require(write in WRITES, "write must be 'delta' or 'add'")
+    return WRITES[write]
+
+
 def check_fwd_tensors(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None,
-                      out=None, final_state=None):
+                      out=None, final_state=None, write="delta"):
     """Host-side shape, dtype and layout checks for fwd_chunked.
 
     The C ABI receives bare pointers and sizes, so the shapes it is told must be
@@ -143,12 +152,17 @@ def check_fwd_tensors(q, k, v, beta, log_alpha=None, initial_state=None, cu_seql
     _require(v.dim() == 4 and tuple(v.shape[:3]) == (B, T, H), "v must be [B, T, H, d_v]")
     dv = v.shape[3]
     _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share one dtype")
-    _require(tuple(beta.shape) == (B, T, H) and beta.dtype == torch.float32,
-             "beta must be float32 [B, T, H]")
+    _check_write(write)
+    if write == "add":
+        _require(beta is None, "beta must be None with the additive write")
+    else:
+        _require(beta is not None and tuple(beta.shape) == (B, T, H) and beta.dtype == torch.float32,
+                 "beta must be float32 [B, T, H]")
     if log_alpha is not None:
         _require(log_alpha.dtype == torch.float32, "log_alpha must be float32")
-        _require(tuple(log_alpha.shape) in ((B, T, H), (B, T, H, dk)),
-                 "log_alpha must be [B, T, H] (one decay per head) or [B, T, H, d_k]")
+        _require(tuple(log_alpha.shape) in ((H,), (B, T, H), (B, T, H, dk)),
+                 "log_alpha must be [H] (one constant decay per head), [B, T, H] (one decay per "
+                 "token and head) or [B, T, H, d_k]")
     if cu_seqlens is not None:
         _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2,
                  "cu_seqlens must be int32 [N + 1] with N >= 1")
@@ -168,7 +182,7 @@ def check_fwd_tensors(q, k, v, beta, log_alpha=None, initial_state=None, cu_seql
     return N
 
 
-def check_step_tensors(q, k, v, beta, log_alpha, state, out=None):
+def check_step_tensors(q, k, v, beta, log_alpha, state, out=None, write="delta"):
     """Host-side checks for recurrent_step (see check_fwd_tensors)."""
     import torch
     named = [("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
@@ -180,10 +194,15 @@ def check_step_tensors(q, k, v, beta, log_alpha, state, out=None):
     _require(v.dim() == 3 and tuple(v.shape[:2]) == (N, H), "v must be [N, H, d_v]")
     dv = v.shape[2]
     _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share one dtype")
-    _require(tuple(beta.shape) == (N, H) and beta.dtype == torch.float32, "beta must be float32 [N, H]")
+    _check_write(write)
+    if write == "add":
+        _require(beta is None, "beta must be None with the additive write")
+    else:
+        _require(beta is not None and tuple(beta.shape) == (N, H) and beta.dtype == torch.float32,
+                 "beta must be float32 [N, H]")
     if log_alpha is not None:
-        _require(log_alpha.dtype == torch.float32 and tuple(log_alpha.shape) in ((N, H), (N, H, dk)),
-                 "log_alpha must be float32 [N, H] or [N, H, d_k]")
+        _require(log_alpha.dtype == torch.float32 and tuple(log_alpha.shape) in ((H,), (N, H), (N, H, dk)),
+                 "log_alpha must be float32 [H], [N, H] or [N, H, d_k]")
     _require(tuple(state.shape) == (N, H, dk, dv) and state.dtype == torch.float32,
              "state must be float32 [N, H, d_k, d_v]")
     if out is not None:
@@ -194,7 +213,7 @@ def check_step_tensors(q, k, v, beta, log_alpha, state, out=None):
     _same_device(named, q)
 
 
-def check_decode_tensors(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out=None):
+def check_decode_tensors(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out=None, write="delta"):
     """Host-side checks for decode (see check_fwd_tensors).  Slot values live on the
     device and are not inspected here."""
     import torch
@@ -208,11 +227,15 @@ def check_decode_tensors(q, k, v, beta, log_alpha, state_pool, src_slots, dst_sl
     _require(v.dim() == 4 and tuple(v.shape[:3]) == (N, L, H), "v must be [N, L, H, d_v]")
     dv = v.shape[3]
     _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share one dtype")
-    _require(tuple(beta.shape) == (N, L, H) and beta.dtype == torch.float32,
-             "beta must be float32 [N, L, H]")
+    _check_write(write)
+    if write == "add":
+        _require(beta is None, "beta must be None with the additive write")
+    else:
+        _require(beta is not None and tuple(beta.shape) == (N, L, H) and beta.dtype == torch.float32,
+                 "beta must be float32 [N, L, H]")
     if log_alpha is not None:
-        _require(log_alpha.dtype == torch.float32 and tuple(log_alpha.shape) in ((N, L, H), (N, L, H, dk)),
-                 "log_alpha must be float32 [N, L, H] or [N, L, H, d_k]")
+        _require(log_alpha.dtype == torch.float32 and tuple(log_alpha.shape) in ((H,), (N, L, H), (N, L, H, dk)),
+                 "log_alpha must be float32 [H], [N, L, H] or [N, L, H, d_k]")
     _require(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (H, dk, dv) and
              state_pool.shape[0] >= 1 and state_pool.dtype == torch.float32,
              "state_pool must be float32 [P, H, d_k, d_v] with P >= 1")
@@ -228,18 +251,23 @@ def check_decode_tensors(q, k, v, beta, log_alpha, state_pool, src_slots, dst_sl
 
 
 def gate_code(log_alpha, token_ndim: int) -> int:
+    """Gate of a log_alpha tensor: None, [H] (constant per head), token_ndim dims
+    (one value per token and head) or one more (per key channel)."""
     if log_alpha is None:
         return GDN_GATE_NONE
+    if log_alpha.dim() == 1:
+        return GDN_GATE_HEAD_CONST
     return GDN_GATE_HEAD if log_alpha.dim() == token_ndim else GDN_GATE_KEY
 
 
 def make_fwd_args(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None, o=None,
-                  final_state=None, chunk: int = CHUNK) -> FwdArgs:
+                  final_state=None, chunk: int = CHUNK, write: str = "delta") -> FwdArgs:
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
     return FwdArgs(B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=chunk, N=N, dtype=_dtype_code(q),
-                   gate=gate_code(log_alpha, 3), q=_ptr(q), k=_ptr(k), v=_ptr(v), beta=_ptr(beta),
+                   gate=gate_code(log_alpha, 3), write=WRITES[write], q=_ptr(q), k=_ptr(k), v=_ptr(v),
+                   beta=_ptr(beta),
                    log_alpha=_ptr(log_alpha), initial_state=_ptr(initial_state),
                    cu_seqlens=_ptr(cu_seqlens), o=_ptr(o), final_state=_ptr(final_state),
                    workspace=None, workspace_bytes=0)
@@ -251,18 +279,20 @@ def fwd_workspace_size(args: FwdArgs) -> int:
 
 def fwd_chunked(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None,
                 output_final_state: bool = True, chunk: int = CHUNK, out=None, final_state=None,
-                workspace=None, stream=None):
+                workspace=None, stream=None, write: str = "delta"):
     """Chunked forward (gdn_fwd_chunked).
 
     q, k [B,T,H,d_k] and v [B,T,H,d_v] (bf16 or fp32, CUDA, contiguous); beta [B,T,H]
-    fp32; log_alpha None | [B,T,H] | [B,T,H,d_k] fp32; initial_state None |
-    [N,H,d_k,d_v] fp32 (M = S^T); cu_seqlens None | int32 [N+1] (then B == 1).
+    fp32 (None with write="add"); log_alpha None | [H] (constant per head) | [B,T,H] |
+    [B,T,H,d_k] fp32; initial_state None | [N,H,d_k,d_v] fp32 (M = S^T); cu_seqlens
+    None | int32 [N+1] (then B == 1).  write: "delta" (the delta rule) or "add" (the
+    additive write of gated linear attention / RetNet).
     Returns (o [B,T,H,d_v], final_state [N,H,d_k,d_v] or None).  Asynchronous on the
     current (or given) stream.
     """
     import torch
     N = check_fwd_tensors(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out,
-                          final_state if output_final_state else None)
+                          final_state if output_final_state else None, write)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if out is None:
@@ -270,7 +300,7 @@ def fwd_chunked(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=No
     if output_final_state and final_state is None:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     args = make_fwd_args(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out,
-                         final_state if output_final_state else None, chunk)
+                         final_state if output_final_state else None, chunk, write)
     need = fwd_workspace_size(args)
     if need:
         if workspace is None or workspace.numel() < need:
@@ -290,7 +320,7 @@ class PreparedFwd:
 
     def __init__(self, q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None,
                  out=None, final_state=None, output_final_state: bool = True, workspace=None,
-                 chunk: int = CHUNK):
+                 chunk: int = CHUNK, write: str = "delta"):
         import torch
         if output_final_state and final_state is None:
             B, T, H, dk = q.shape
@@ -299,9 +329,9 @@ class PreparedFwd:
         if out is None:
             out = torch.empty(tuple(v.shape), dtype=q.dtype, device=q.device)
         check_fwd_tensors(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out,
-                          final_state if output_final_state else None)
+                          final_state if output_final_state else None, write)
         self.args = make_fwd_args(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out,
-                                  final_state if output_final_state else None, chunk)
+                                  final_state if output_final_state else None, chunk, write)
         need = fwd_workspace_size(self.args)
         if need and (workspace is None or workspace.numel() < need):
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -317,42 +347,46 @@ class PreparedFwd:
         return self.out, self.final_state
 
 
-def recurrent_step(q, k, v, beta, log_alpha, state, out=None, stream=None):
+def recurrent_step(q, k, v, beta, log_alpha, state, out=None, stream=None, write: str = "delta"):
     """One decode token per stream (gdn_fwd_recurrent_step).
 
-    q, k [N,H,d_k], v [N,H,d_v] (bf16 or fp32); beta [N,H]; log_alpha None | [N,H] |
-    [N,H,d_k]; state [N,H,d_k,d_v] fp32, updated in place.  Returns o [N,H,d_v].
+    q, k [N,H,d_k], v [N,H,d_v] (bf16 or fp32); beta [N,H] (None with write="add");
+    log_alpha None | [H] | [N,H] | [N,H,d_k]; state [N,H,d_k,d_v] fp32, updated in
+    place.  Returns o [N,H,d_v].
     """
     import torch
-    check_step_tensors(q, k, v, beta, log_alpha, state, out)
+    check_step_tensors(q, k, v, beta, log_alpha, state, out, write)
     N, H, dk = q.shape
     dv = v.shape[-1]
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     args = StepArgs(N=N, H=H, d_k=dk, d_v=dv, dtype=_dtype_code(q), gate=gate_code(log_alpha, 2),
-                    q=_ptr(q), k=_ptr(k), v=_ptr(v), beta=_ptr(beta), log_alpha=_ptr(log_alpha),
+                    write=WRITES[write], q=_ptr(q), k=_ptr(k), v=_ptr(v), beta=_ptr(beta), log_alpha=_ptr(log_alpha),
                     state=_ptr(state), o=_ptr(out))
     _check(_lib.gdn_fwd_recurrent_step(ctypes.byref(args), _stream(stream)), "gdn_fwd_recurrent_step")
     return out
 
 
-def decode(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out=None, stream=None):
+def decode(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out=None, stream=None,
+           write: str = "delta"):
     """Serving decode (gdn_fwd_decode): L tokens per stream against a pool of states.
 
-    q, k [N,L,H,d_k], v [N,L,H,d_v] (bf16 or fp32); beta [N,L,H]; log_alpha None |
-    [N,L,H] | [N,L,H,d_k]; state_pool [P,H,d_k,d_v] fp32; src_slots int32 [N] (slot
+    q, k [N,L,H,d_k], v [N,L,H,d_v] (bf16 or fp32); beta [N,L,H] (None with
+    write="add"); log_alpha None | [H] | [N,L,H] | [N,L,H,d_k]; state_pool
+    [P,H,d_k,d_v] fp32; src_slots int32 [N] (slot
     each stream starts from; outside [0, P): padding stream, skipped); dst_slots int32
     [N,L] (slot receiving the state after each token; outside [0, P): not stored).
     Returns o [N,L,H,d_v]; rows of padding streams are left as they were in ``out``
     (uninitialised if ``out`` is None).
     """
     import torch
-    check_decode_tensors(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out)
+    check_decode_tensors(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out, write)
     N, L, H, dk = q.shape
     dv = v.shape[-1]
     if out is None:
         out = torch.empty((N, L, H, dv), dtype=q.dtype, device=q.device)
     args = DecodeArgs(N=N, L=L, H=H, d_k=dk, d_v=dv, dtype=_dtype_code(q), gate=gate_code(log_alpha, 3),
+                      write=WRITES[write],
                       q=_ptr(q), k=_ptr(k), v=_ptr(v), beta=_ptr(beta), log_alpha=_ptr(log_alpha),
                       state_pool=_ptr(state_pool), pool_size=state_pool.shape[0],
                       src_slots=_ptr(src_slots), dst_slots=_ptr(dst_slots), o=_ptr(out))

@@ -13,6 +13,17 @@ namespace {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool gate_ok(int g) {
+  return g == GDN_GATE_NONE || g == GDN_GATE_HEAD || g == GDN_GATE_KEY || g == GDN_GATE_HEAD_CONST;
+}
+bool write_ok(int w) { return w == GDN_WRITE_DELTA || w == GDN_WRITE_ADD; }
+// Kernel gate of an ABI gate: the constant per-head gate is the scalar gate read
+// with a token stride of 0.
+int kernel_gate(int g) { return g == GDN_GATE_HEAD_CONST ? gdn::GATE_HEAD : g; }
+// beta is given exactly for the delta write, log_alpha exactly for a gate.
+bool operands_ok(int gate, int write, const void *beta, const void *log_alpha) {
+  return (beta != nullptr) == (write == GDN_WRITE_DELTA) && (log_alpha != nullptr) == (gate != GDN_GATE_NONE);
+}
 
 // Value columns per workgroup: 64, or 32 when there are too few (sequence, head)
 // streams to give every compute unit a workgroup.
@@ -25,8 +36,7 @@ int check_fwd(const gdn_fwd_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
   if (a->B < 0 || a->T < 0 || a->H <= 0 || a->N < 0) return GDN_ERR_INVALID_ARG;
   if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD && a->gate != GDN_GATE_KEY)
-    return GDN_ERR_INVALID_ARG;
+  if (!gate_ok(a->gate) || !write_ok(a->write)) return GDN_ERR_INVALID_ARG;
   if (a->chunk != 64) return GDN_ERR_UNSUPPORTED;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   if (a->dtype == GDN_F32 && a->d_k != 64) return GDN_ERR_UNSUPPORTED;
@@ -37,9 +47,10 @@ int check_fwd(const gdn_fwd_args *a) {
   }
   if ((long)a->B * a->T > INT32_MAX) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long)a->B * a->T > 0;
-  if (tokens && (!a->q || !a->k || !a->v || !a->beta || !a->o)) return GDN_ERR_INVALID_ARG;
-  if ((a->gate == GDN_GATE_NONE) != (a->log_alpha == nullptr) && tokens) return GDN_ERR_INVALID_ARG;
+  if (tokens && (!a->q || !a->k || !a->v || !a->o)) return GDN_ERR_INVALID_ARG;
+  if (tokens && !operands_ok(a->gate, a->write, a->beta, a->log_alpha)) return GDN_ERR_INVALID_ARG;
   if (a->gate == GDN_GATE_NONE && a->log_alpha) return GDN_ERR_INVALID_ARG;
+  if (a->write == GDN_WRITE_ADD && a->beta) return GDN_ERR_INVALID_ARG;
   const void *p16[] = {a->q, a->k, a->v, a->o, a->initial_state, a->final_state};
   for (const void *p : p16)
     if (p && !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
@@ -57,11 +68,14 @@ size_t order_bytes(const gdn_fwd_args *a) {
   return align256((size_t)a->N * sizeof(int32_t));
 }
 
-// The per-key-channel gate on the pipelined kernel (bf16, d_k = 128): a first pass
-// prepares every chunk's operands in the workspace.
-bool key_pipe(const gdn_fwd_args *a) {
-  return a->gate == GDN_GATE_KEY && a->dtype == GDN_BF16 && a->d_k == 128;
+// The pipelined kernel takes bf16 with d_k = 128, the delta write and per-token (or
+// no) decays; everything else runs on the fused kernel.
+bool use_pipe(const gdn_fwd_args *a) {
+  return a->dtype == GDN_BF16 && a->d_k == 128 && a->write == GDN_WRITE_DELTA && a->gate != GDN_GATE_HEAD_CONST;
 }
+// The per-key-channel gate on the pipelined kernel: a first pass prepares every
+// chunk's operands in the workspace.
+bool key_pipe(const gdn_fwd_args *a) { return a->gate == GDN_GATE_KEY && use_pipe(a); }
 struct KeyLayout {
   long slots;
   size_t kq, tp, eg;  // bytes of one pre-scaled K/Q array, the T/P images, e^{g_C}
@@ -82,12 +96,11 @@ int check_step(const gdn_step_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
   if (a->N < 0 || a->H <= 0) return GDN_ERR_INVALID_ARG;
   if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD && a->gate != GDN_GATE_KEY)
-    return GDN_ERR_INVALID_ARG;
+  if (!gate_ok(a->gate) || !write_ok(a->write)) return GDN_ERR_INVALID_ARG;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   if (a->N == 0) return GDN_OK;
-  if (!a->q || !a->k || !a->v || !a->beta || !a->state || !a->o) return GDN_ERR_INVALID_ARG;
-  if ((a->gate == GDN_GATE_NONE) != (a->log_alpha == nullptr)) return GDN_ERR_INVALID_ARG;
+  if (!a->q || !a->k || !a->v || !a->state || !a->o) return GDN_ERR_INVALID_ARG;
+  if (!operands_ok(a->gate, a->write, a->beta, a->log_alpha)) return GDN_ERR_INVALID_ARG;
   if (!aligned(a->state, 16) || !aligned(a->q, 4) || !aligned(a->k, 4) || !aligned(a->v, 4) ||
       !aligned(a->o, 4) || !aligned(a->beta, 4) || (a->log_alpha && !aligned(a->log_alpha, 4)))
     return GDN_ERR_INVALID_ARG;
@@ -99,13 +112,12 @@ int check_decode(const gdn_decode_args *a) {
   if (a->N < 0 || a->L < 1 || a->H <= 0 || a->pool_size < 1) return GDN_ERR_INVALID_ARG;
   if ((long long)a->N * a->H > INT32_MAX || (long long)a->N * a->L > INT32_MAX) return GDN_ERR_UNSUPPORTED;
   if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD && a->gate != GDN_GATE_KEY)
-    return GDN_ERR_INVALID_ARG;
+  if (!gate_ok(a->gate) || !write_ok(a->write)) return GDN_ERR_INVALID_ARG;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   if (a->N == 0) return GDN_OK;
-  if (!a->q || !a->k || !a->v || !a->beta || !a->state_pool || !a->src_slots || !a->dst_slots || !a->o)
+  if (!a->q || !a->k || !a->v || !a->state_pool || !a->src_slots || !a->dst_slots || !a->o)
     return GDN_ERR_INVALID_ARG;
-  if ((a->gate == GDN_GATE_NONE) != (a->log_alpha == nullptr)) return GDN_ERR_INVALID_ARG;
+  if (!operands_ok(a->gate, a->write, a->beta, a->log_alpha)) return GDN_ERR_INVALID_ARG;
   if (!aligned(a->state_pool, 16) || !aligned(a->q, 4) || !aligned(a->k, 4) || !aligned(a->v, 4) ||
       !aligned(a->o, 4) || !aligned(a->beta, 4) || (a->log_alpha && !aligned(a->log_alpha, 4)) ||
       !aligned(a->src_slots, 4) || !aligned(a->dst_slots, 4))
@@ -150,6 +162,7 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
   p.H = a->H;
   p.T = a->T;
   p.dv = a->d_v;
+  p.la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
   if (obytes) {
     if (gdn::launch_seq_order(a->cu_seqlens, a->N, (int32_t *)a->workspace, stream) != hipSuccess)
       return GDN_ERR_HIP;
@@ -177,15 +190,15 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
     p.tp_img = kp.tp_img;
     p.egc = kp.egc;
   }
-  const bool pipe = a->dtype == GDN_BF16 && a->d_k == 128;
-  if (pipe) {
+  if (use_pipe(a)) {
     p.nb = a->d_v / 64;
     if (gdn::launch_fwd_pipe(p, (int)a->gate, stream) != hipSuccess) return GDN_ERR_HIP;
     return GDN_OK;
   }
   const int dvb = choose_dvb(a->N, a->H, a->d_v);
   p.nb = a->d_v / dvb;
-  if (gdn::launch_fwd_fused(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, (int)a->gate, stream) != hipSuccess)
+  if (gdn::launch_fwd_fused(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, kernel_gate(a->gate),
+                            a->write == GDN_WRITE_ADD, stream) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
 }
@@ -204,8 +217,9 @@ int gdn_fwd_recurrent_step(const gdn_step_args *a, void *hip_stream) {
   p.o = a->o;
   p.N = a->N;
   p.H = a->H;
-  if (gdn::launch_recurrent_step(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->d_v, (int)a->gate,
-                                 (hipStream_t)hip_stream) != hipSuccess)
+  p.la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
+  if (gdn::launch_recurrent_step(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->d_v, kernel_gate(a->gate),
+                                 a->write == GDN_WRITE_ADD, (hipStream_t)hip_stream) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
 }
@@ -228,8 +242,9 @@ int gdn_fwd_decode(const gdn_decode_args *a, void *hip_stream) {
   p.L = a->L;
   p.H = a->H;
   p.P = a->pool_size;
-  if (gdn::launch_decode(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->d_v, (int)a->gate,
-                         (hipStream_t)hip_stream) != hipSuccess)
+  p.la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
+  if (gdn::launch_decode(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->d_v, kernel_gate(a->gate),
+                         a->write == GDN_WRITE_ADD, (hipStream_t)hip_stream) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
 }

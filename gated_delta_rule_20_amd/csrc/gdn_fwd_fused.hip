@@ -12,6 +12,9 @@
 //   M_C   = e^{g_C} M0 + K^T diag(e^{g_C - g}) Delta                         (state)
 // The strict mask makes a token's write blind to itself; the inclusive mask lets
 // the read at t see the write at t.
+// With the additive write (S += v k^T: gated linear attention, RetNet, the plain
+// linear transformer; same sec. 3 item 4) there is no erase and no beta: A and T
+// drop out, Delta = V, and the same O and M_C formulas hold.
 // With one decay per key channel (sec. 3, the per-channel gate of the diagonal
 // family) every exp(g_r - g_i) is per channel and moves inside the contractions:
 // K and Q rows carry e^{g_r}, K^T carries e^{g_C - g_i}, the state rows decay by
@@ -101,7 +104,7 @@ constexpr int GT_A[10] = {0, 3, 3, 1, 1, 3, 2, 2, 2, 3};
 constexpr int GT_B[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 constexpr int GT_W[10] = {0, 0, 0, 1, 1, 1, 2, 2, 3, 3};
 
-template <typename E, int DK, int DVB, int GATE>
+template <typename E, int DK, int DVB, int GATE, bool ADD>
 __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   constexpr bool KG = GATE == GATE_KEY;
   typedef Cfg<E, DK, DVB, KG> CF;
@@ -165,8 +168,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   const E *qb = (const E *)p.q + ((size_t)tok0 * H + h) * DK;
   const E *vb = (const E *)p.v + ((size_t)tok0 * H + h) * dv + col0;
   E *ob = (E *)p.o + ((size_t)tok0 * H + h) * dv + col0;
-  const float *bb = p.beta + (size_t)tok0 * H + h;
-  const float *lab = (GATE == GATE_HEAD) ? p.log_alpha + (size_t)tok0 * H + h : nullptr;
+  const float *bb = ADD ? nullptr : p.beta + (size_t)tok0 * H + h;
+  const int ls = p.la_stride;  // H, or 0 for one constant decay per head
+  const float *lab = (GATE == GATE_HEAD) ? p.log_alpha + (size_t)tok0 * ls + h : nullptr;
   const float *lak = KG ? p.log_alpha + ((size_t)tok0 * H + h) * DK : nullptr;
 
   // ---- state: wave w < NWS owns value columns col0 + 16w .. +15 (C-tile layout)
@@ -209,8 +213,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       const int row = min(rgv * CF::RPTV + u, last);
       rv[u] = *(const u32x4 *)(vb + (size_t)(base + row) * sv + cv * VEC);
     }
-    if (tid < C) rbeta = bb[(size_t)(base + min(tid, last)) * H];
-    if (GATE == GATE_HEAD && tid >= C && tid < 2 * C) rla = lab[(size_t)(base + min(tid - C, last)) * H];
+    if (!ADD && tid < C) rbeta = bb[(size_t)(base + min(tid, last)) * H];
+    if (GATE == GATE_HEAD && tid >= C && tid < 2 * C) rla = lab[(size_t)(base + min(tid - C, last)) * ls];
     if (KG) {
 #pragma unroll
       for (int u = 0; u < CF::RPTG; ++u) {
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
             bk[j] = to_e<E>(to_f(bk[j]) * eb);
           }
         }
-        kk = mma(ak, bk, kk);
+        if (!ADD) kk = mma(ak, bk, kk);
         qk = mma(aq, bk, qk);
       }
       const int i = 16 * b + lm;
@@ -342,12 +346,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
         const int r = 16 * a + 4 * lg + j;
         float gam = (i <= r) ? 1.f : 0.f;
         if (GATE == GATE_HEAD) gam = (i <= r) ? __expf(gs[r] - gs[i]) : 0.f;
-        const float av = (i < r) ? betas[r] * kk[j] * gam : 0.f;
         const float pv = qk[j] * gam;
-        if (a == b)
-          AD[(16 * a + 4 * lg + j) * 16 + lm] = av;
-        else
-          As[r * ST + i] = to_e<E>(av);
+        if (!ADD) {
+          const float av = (i < r) ? betas[r] * kk[j] * gam : 0.f;
+          if (a == b)
+            AD[(16 * a + 4 * lg + j) * 16 + lm] = av;
+          else
+            As[r * ST + i] = to_e<E>(av);
+        }
         Ps[r * ST + i] = to_e<E>(pv);
       }
     }
@@ -356,6 +362,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
     // (3) diagonal 16x16 blocks of T = (I + A)^-1: forward substitution in fp32,
     //     lane (lg, lm) solves column lm of block lg
     if (wave == 0) {
+      if (!ADD) {
       const float *ad = AD + lg * 256;
       float x[16];
 #pragma unroll
@@ -367,6 +374,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) Ts[(16 * lg + r) * ST + 16 * lg + lm] = to_e<E>(x[r]);
+      }
     } else if (KG) {
       // per-channel decay folded into the state-phase operands (waves 1-3, while
       // wave 0 solves): K, Q rows times e^{g_r}; K^T entries times e^{g_C - g_i}
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
 
     // (4) off-diagonal blocks: T[a][b] = -T[a][a] * sum_{k=b}^{a-1} A[a][k] T[k][b];
     //     wave b walks block column b downwards, keeping T[k][b] in C tiles
-    if (wave < 3) {
+    if (!ADD && wave < 3) {
       const int b = wave;
       f32x4 Tc[4];
 #pragma unroll
@@ -442,12 +450,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       for (int s = 0; s < CF::KB; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const E *kr = Ks + (16 * i + lm) * SK + 32 * s + 4 * lg;
-          X[i] = mma(ld4x2(kr, kr + 16), MB[s], X[i]);
+          if (!ADD) {
+            const E *kr = Ks + (16 * i + lm) * SK + 32 * s + 4 * lg;
+            X[i] = mma(ld4x2(kr, kr + 16), MB[s], X[i]);
+          }
           const E *qr = Qs + (16 * i + lm) * SK + 32 * s + 4 * lg;
           O[i] = mma(ld4x2(qr, qr + 16), MB[s], O[i]);
         }
-      // X <- beta * (V - e^g * K M0);  O <- e^g * Q M0
+      // X <- beta * (V - e^g * K M0);  O <- e^g * Q M0  (additive write: X <- V)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4 vv = ld4f(VTs + (n0 + lm) * ST + 16 * i + 4 * lg);
@@ -455,18 +465,24 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
         for (int j = 0; j < 4; ++j) {
           const int r = 16 * i + 4 * lg + j;
           const float e = (GATE == GATE_HEAD) ? egs[r] : 1.f;
-          X[i][j] = betas[r] * (vv[j] - e * X[i][j]);
+          X[i][j] = ADD ? vv[j] : betas[r] * (vv[j] - e * X[i][j]);
           O[i][j] *= e;
         }
       }
-      const F XB0 = frag_from_c<E>(X[0], X[1]), XB1 = frag_from_c<E>(X[2], X[3]);
-      // Delta = T X  (T lower triangular: tiles 0,1 need k-block 0 only)
+      // Delta = T X  (T lower triangular: tiles 0,1 need k-block 0 only); Delta = V
+      // for the additive write
       f32x4 D[4];
+      if (ADD) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const E *tr = Ts + (16 * i + lm) * ST + 4 * lg;
-        D[i] = mma(ld4x2(tr, tr + 16), XB0, zero4());
-        if (i >= 2) D[i] = mma(ld4x2(tr + 32, tr + 48), XB1, D[i]);
+        for (int i = 0; i < 4; ++i) D[i] = X[i];
+      } else {
+        const F XB0 = frag_from_c<E>(X[0], X[1]), XB1 = frag_from_c<E>(X[2], X[3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const E *tr = Ts + (16 * i + lm) * ST + 4 * lg;
+          D[i] = mma(ld4x2(tr, tr + 16), XB0, zero4());
+          if (i >= 2) D[i] = mma(ld4x2(tr + 32, tr + 48), XB1, D[i]);
+        }
       }
       const F DB0 = frag_from_c<E>(D[0], D[1]), DB1 = frag_from_c<E>(D[2], D[3]);
       if (GATE == GATE_HEAD) {
@@ -535,34 +551,38 @@ __global__ void seq_order_kernel(const int32_t *cu, int N, int32_t *order) {
 }
 
 template <typename E, int DK, int DVB, int GATE>
-hipError_t launch_t(const FwdParams &p, hipStream_t stream) {
+hipError_t launch_t(const FwdParams &p, bool add, hipStream_t stream) {
   const int blocks = p.N * p.H * p.nb;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_fused_kernel<E, DK, DVB, GATE>), dim3(blocks), dim3(NT), 0, stream, p);
+  if (add)
+    hipLaunchKernelGGL((fwd_fused_kernel<E, DK, DVB, GATE, true>), dim3(blocks), dim3(NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_fused_kernel<E, DK, DVB, GATE, false>), dim3(blocks), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename E, int DK, int DVB>
-hipError_t launch_g(const FwdParams &p, int gate, hipStream_t stream) {
+hipError_t launch_g(const FwdParams &p, int gate, bool add, hipStream_t stream) {
   switch (gate) {
-    case GATE_NONE: return launch_t<E, DK, DVB, GATE_NONE>(p, stream);
-    case GATE_HEAD: return launch_t<E, DK, DVB, GATE_HEAD>(p, stream);
-    case GATE_KEY: return launch_t<E, DK, DVB, GATE_KEY>(p, stream);
+    case GATE_NONE: return launch_t<E, DK, DVB, GATE_NONE>(p, add, stream);
+    case GATE_HEAD: return launch_t<E, DK, DVB, GATE_HEAD>(p, add, stream);
+    case GATE_KEY: return launch_t<E, DK, DVB, GATE_KEY>(p, add, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_fused(const FwdParams &p, int dtype, int dk, int dvb, int gate, hipStream_t stream) {
+hipError_t launch_fwd_fused(const FwdParams &p, int dtype, int dk, int dvb, int gate, bool add,
+                            hipStream_t stream) {
   if (dtype == 1) {
-    if (dk == 128 && dvb == 64) return launch_g<bf16, 128, 64>(p, gate, stream);
-    if (dk == 128 && dvb == 32) return launch_g<bf16, 128, 32>(p, gate, stream);
-    if (dk == 64 && dvb == 64) return launch_g<bf16, 64, 64>(p, gate, stream);
-    if (dk == 64 && dvb == 32) return launch_g<bf16, 64, 32>(p, gate, stream);
+    if (dk == 128 && dvb == 64) return launch_g<bf16, 128, 64>(p, gate, add, stream);
+    if (dk == 128 && dvb == 32) return launch_g<bf16, 128, 32>(p, gate, add, stream);
+    if (dk == 64 && dvb == 64) return launch_g<bf16, 64, 64>(p, gate, add, stream);
+    if (dk == 64 && dvb == 32) return launch_g<bf16, 64, 32>(p, gate, add, stream);
   } else {
-    if (dk == 64 && dvb == 64) return launch_g<float, 64, 64>(p, gate, stream);
-    if (dk == 64 && dvb == 32) return launch_g<float, 64, 32>(p, gate, stream);
+    if (dk == 64 && dvb == 64) return launch_g<float, 64, 64>(p, gate, add, stream);
+    if (dk == 64 && dvb == 32) return launch_g<float, 64, 32>(p, gate, add, stream);
   }
   return hipErrorInvalidValue;
 }

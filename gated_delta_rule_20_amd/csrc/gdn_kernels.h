@@ -25,6 +25,10 @@ struct FwdParams {
   const void *k_hat;             // [tokens, H, d_k] K e^{g_C - G}
   const void *tp_img;            // [slots, H] 16 KiB LDS images of T diag(beta) and P
   const float *egc;              // [slots, H, d_k] e^{g_C} per key channel
+  // Scalar (per-head) gate: elements between consecutive tokens of log_alpha, H
+  // for one value per (token, head), 0 for one constant value per head.  Read by
+  // the fused kernel only (the pipelined kernel takes per-token values).
+  int la_stride;
 };
 
 // Chunk slots of the per-key-channel preparation: chunk c of sequence n (first token
@@ -37,6 +41,7 @@ struct StepParams {
   float *state;
   void *o;
   int N, H;
+  int la_stride;  // scalar gate: elements of log_alpha between streams (H, or 0: per head)
 };
 
 // L decode tokens per stream against a pool of states: slot src[n] is read, the
@@ -48,11 +53,13 @@ struct DecodeParams {
   const int *src, *dst;
   void *o;
   int N, L, H, P;
+  int la_stride;  // scalar gate: elements of log_alpha between tokens (H, or 0: per head)
 };
 
 // dtype: 0 fp32, 1 bf16.  Each launcher returns hipSuccess or the launch error.
 // dvb: columns of d_v per workgroup (32 or 64).
-hipError_t launch_fwd_fused(const FwdParams &p, int dtype, int dk, int dvb, int gate,
+// add: the additive write (S += v k^T; beta unused) instead of the delta rule.
+hipError_t launch_fwd_fused(const FwdParams &p, int dtype, int dk, int dvb, int gate, bool add,
                             hipStream_t stream);
 // Software-pipelined forward for bf16, d_k = 128, 64-column value blocks (nb = d_v / 64).
 // Gate NONE or HEAD; gate KEY after launch_key_prep, with the k_hat, tp_img, egc fields.
@@ -72,8 +79,9 @@ struct KeyPrepParams {
 };
 hipError_t launch_key_prep(const KeyPrepParams &p, long slots, hipStream_t stream);
 hipError_t launch_seq_order(const int32_t *cu_seqlens, int N, int32_t *order, hipStream_t stream);
-hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate,
+hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate, bool add,
                                  hipStream_t stream);
-hipError_t launch_decode(const DecodeParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams &p, int dtype, int dk, int dv, int gate, bool add,
+                         hipStream_t stream);
 
 }  // namespace gdn

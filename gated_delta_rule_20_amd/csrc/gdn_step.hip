@@ -8,6 +8,8 @@
 //   o = M'^T q = (Diag(a) M)^T q + w (q . k)
 // so one read of M gives both reductions r and (Diag(a) M)^T q, and one write stores
 // M'.  The kernel is bound by HBM traffic (2 * 4 * d_k * d_v bytes per stream).
+// The additive write (sec. 3 item 4: gated linear attention; RetNet; the plain
+// linear transformer) is the same body with w = v (no erase, no beta).
 //
 // One workgroup (256 threads) per (stream, head).  Thread (row group rg, column
 // quad cq) holds d_k / RG rows x 4 columns of M in registers: 16-byte coalesced
@@ -21,7 +23,7 @@ namespace gdn {
 
 namespace {
 
-template <typename E, int DK, int DV, int GATE>
+template <typename E, int DK, int DV, int GATE, bool ADD>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
   constexpr int CQ = DV / 4;    // column quads
   constexpr int RG = 256 / CQ;  // row groups
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
     qs[tid] = to_f(q[tid]);
     ks[tid] = to_f(k[tid]);
     float a = 1.f;
-    if (GATE == GATE_HEAD) a = __expf(p.log_alpha[pair]);
+    if (GATE == GATE_HEAD) a = __expf(p.log_alpha[(size_t)(pair / p.H) * p.la_stride + pair % p.H]);
     if (GATE == GATE_KEY) a = __expf(p.log_alpha[(size_t)pair * DK + tid]);
     as_[tid] = a;
   }
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
   f32x4 vv;
 #pragma unroll
   for (int e = 0; e < 4; ++e) vv[e] = to_f(vp[e]);
-  const float beta = p.beta[pair];
+  const float beta = ADD ? 1.f : p.beta[pair];
   __syncthreads();
 
   f32x4 r = zero4(), s = zero4();
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
   }
   f32x4 w;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = beta * (vv[e] - R[e]);
+  for (int e = 0; e < 4; ++e) w[e] = ADD ? vv[e] : beta * (vv[e] - R[e]);
 #pragma unroll
   for (int u = 0; u < RP; ++u) {
     const int row = rg * RP + u;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
 
 // Serving decode with one token per stream (L = 1): the body of recurrent_step_kernel
 // with the state read from and written to pool slots.
-template <typename E, int DK, int DV, int GATE>
+template <typename E, int DK, int DV, int GATE, bool ADD>
 __global__ __launch_bounds__(256) void decode_one_kernel(DecodeParams p) {
   constexpr int CQ = DV / 4;
   constexpr int RG = 256 / CQ;
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(256) void decode_one_kernel(DecodeParams p) {
     qs[tid] = to_f(((const E *)p.q)[(size_t)pair * DK + tid]);
     ks[tid] = to_f(((const E *)p.k)[(size_t)pair * DK + tid]);
     float a = 1.f;
-    if (GATE == GATE_HEAD) a = __expf(p.log_alpha[pair]);
+    if (GATE == GATE_HEAD) a = __expf(p.log_alpha[(size_t)n * p.la_stride + h]);
     if (GATE == GATE_KEY) a = __expf(p.log_alpha[(size_t)pair * DK + tid]);
     as_[tid] = a;
   }
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void decode_one_kernel(DecodeParams p) {
   f32x4 vv;
 #pragma unroll
   for (int e = 0; e < 4; ++e) vv[e] = to_f(vp[e]);
-  const float beta = p.beta[pair];
+  const float beta = ADD ? 1.f : p.beta[pair];
   __syncthreads();
 
   f32x4 r = zero4(), s = zero4();
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_one_kernel(DecodeParams p) {
   }
   f32x4 w;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = beta * (vv[e] - R[e]);
+  for (int e = 0; e < 4; ++e) w[e] = ADD ? vv[e] : beta * (vv[e] - R[e]);
 #pragma unroll
   for (int u = 0; u < RP; ++u) m[u] += ks[rg * RP + u] * w;
   if (rg == 0) {
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(256) void decode_one_kernel(DecodeParams p) {
 // together, issued with the state load, so one memory latency covers them; q . k of
 // every staged token is formed once per batch, and the partial sums alternate
 // between two LDS buffers, so each token needs a single barrier.
-template <typename E, int DK, int DV, int GATE>
+template <typename E, int DK, int DV, int GATE, bool ADD>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int CQ = DV / 4;
   constexpr int RG = 256 / CQ;
@@ -220,8 +222,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
     if (tid < nt) {
       const size_t i = i0 + (size_t)tid * p.H;
-      bs[tid] = p.beta[i];
-      ah[tid] = GATE == GATE_HEAD ? __expf(p.log_alpha[i]) : 1.f;
+      bs[tid] = ADD ? 1.f : p.beta[i];
+      ah[tid] = GATE == GATE_HEAD ? __expf(p.log_alpha[((size_t)n * p.L + t0 + tid) * p.la_stride + h]) : 1.f;
     }
     __syncthreads();
     // q . k of each staged token: wave w takes tokens w, w + 4
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       const f32x4 vv = *(const f32x4 *)&vs[tt][4 * cq];
       f32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = beta * (vv[e] - R[e]);
+      for (int e = 0; e < 4; ++e) w[e] = ADD ? vv[e] : beta * (vv[e] - R[e]);
 #pragma unroll
       for (int u = 0; u < RP; ++u) m[u] += ks[tt][rg * RP + u] * w;
       if (rg == 0) {
@@ -277,67 +279,70 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
 }
 
+// Instantiate a kernel template K<E, DK, DV, GATE, ADD> for the run-time gate and
+// write rule.
+#define GDN_STEP_LAUNCH(K, P)                                                                          \
+  do {                                                                                                 \
+    switch (gate * 2 + (add ? 1 : 0)) {                                                                \
+      case 0: hipLaunchKernelGGL((K<E, DK, DV, GATE_NONE, false>), dim3(blocks), dim3(256), 0, stream, P); break; \
+      case 1: hipLaunchKernelGGL((K<E, DK, DV, GATE_NONE, true>), dim3(blocks), dim3(256), 0, stream, P); break;  \
+      case 2: hipLaunchKernelGGL((K<E, DK, DV, GATE_HEAD, false>), dim3(blocks), dim3(256), 0, stream, P); break; \
+      case 3: hipLaunchKernelGGL((K<E, DK, DV, GATE_HEAD, true>), dim3(blocks), dim3(256), 0, stream, P); break;  \
+      case 4: hipLaunchKernelGGL((K<E, DK, DV, GATE_KEY, false>), dim3(blocks), dim3(256), 0, stream, P); break;  \
+      case 5: hipLaunchKernelGGL((K<E, DK, DV, GATE_KEY, true>), dim3(blocks), dim3(256), 0, stream, P); break;   \
+      default: return hipErrorInvalidValue;                                                            \
+    }                                                                                                  \
+  } while (0)
+
 template <typename E, int DK, int DV>
-hipError_t launch_g(const StepParams &p, int gate, hipStream_t stream) {
+hipError_t launch_g(const StepParams &p, int gate, bool add, hipStream_t stream) {
   const int blocks = p.N * p.H;
   if (blocks == 0) return hipSuccess;
-  switch (gate) {
-    case GATE_NONE: hipLaunchKernelGGL((recurrent_step_kernel<E, DK, DV, GATE_NONE>), dim3(blocks), dim3(256), 0, stream, p); break;
-    case GATE_HEAD: hipLaunchKernelGGL((recurrent_step_kernel<E, DK, DV, GATE_HEAD>), dim3(blocks), dim3(256), 0, stream, p); break;
-    case GATE_KEY: hipLaunchKernelGGL((recurrent_step_kernel<E, DK, DV, GATE_KEY>), dim3(blocks), dim3(256), 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  GDN_STEP_LAUNCH(recurrent_step_kernel, p);
   return hipGetLastError();
 }
 
 template <typename E>
-hipError_t launch_e(const StepParams &p, int dk, int dv, int gate, hipStream_t stream) {
-  if (dk == 128 && dv == 128) return launch_g<E, 128, 128>(p, gate, stream);
-  if (dk == 128 && dv == 64) return launch_g<E, 128, 64>(p, gate, stream);
-  if (dk == 64 && dv == 128) return launch_g<E, 64, 128>(p, gate, stream);
-  if (dk == 64 && dv == 64) return launch_g<E, 64, 64>(p, gate, stream);
+hipError_t launch_e(const StepParams &p, int dk, int dv, int gate, bool add, hipStream_t stream) {
+  if (dk == 128 && dv == 128) return launch_g<E, 128, 128>(p, gate, add, stream);
+  if (dk == 128 && dv == 64) return launch_g<E, 128, 64>(p, gate, add, stream);
+  if (dk == 64 && dv == 128) return launch_g<E, 64, 128>(p, gate, add, stream);
+  if (dk == 64 && dv == 64) return launch_g<E, 64, 64>(p, gate, add, stream);
   return hipErrorInvalidValue;
 }
 
 template <typename E, int DK, int DV>
-hipError_t launch_dg(const DecodeParams &p, int gate, hipStream_t stream) {
+hipError_t launch_dg(const DecodeParams &p, int gate, bool add, hipStream_t stream) {
   const int blocks = p.N * p.H;
   if (blocks == 0) return hipSuccess;
-  if (p.L == 1) {
-    switch (gate) {
-      case GATE_NONE: hipLaunchKernelGGL((decode_one_kernel<E, DK, DV, GATE_NONE>), dim3(blocks), dim3(256), 0, stream, p); break;
-      case GATE_HEAD: hipLaunchKernelGGL((decode_one_kernel<E, DK, DV, GATE_HEAD>), dim3(blocks), dim3(256), 0, stream, p); break;
-      case GATE_KEY: hipLaunchKernelGGL((decode_one_kernel<E, DK, DV, GATE_KEY>), dim3(blocks), dim3(256), 0, stream, p); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
-  switch (gate) {
-    case GATE_NONE: hipLaunchKernelGGL((decode_kernel<E, DK, DV, GATE_NONE>), dim3(blocks), dim3(256), 0, stream, p); break;
-    case GATE_HEAD: hipLaunchKernelGGL((decode_kernel<E, DK, DV, GATE_HEAD>), dim3(blocks), dim3(256), 0, stream, p); break;
-    case GATE_KEY: hipLaunchKernelGGL((decode_kernel<E, DK, DV, GATE_KEY>), dim3(blocks), dim3(256), 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (p.L == 1)
+    GDN_STEP_LAUNCH(decode_one_kernel, p);
+  else
+    GDN_STEP_LAUNCH(decode_kernel, p);
   return hipGetLastError();
 }
 
+#undef GDN_STEP_LAUNCH
+
 template <typename E>
-hipError_t launch_de(const DecodeParams &p, int dk, int dv, int gate, hipStream_t stream) {
-  if (dk == 128 && dv == 128) return launch_dg<E, 128, 128>(p, gate, stream);
-  if (dk == 128 && dv == 64) return launch_dg<E, 128, 64>(p, gate, stream);
-  if (dk == 64 && dv == 128) return launch_dg<E, 64, 128>(p, gate, stream);
-  if (dk == 64 && dv == 64) return launch_dg<E, 64, 64>(p, gate, stream);
+hipError_t launch_de(const DecodeParams &p, int dk, int dv, int gate, bool add, hipStream_t stream) {
+  if (dk == 128 && dv == 128) return launch_dg<E, 128, 128>(p, gate, add, stream);
+  if (dk == 128 && dv == 64) return launch_dg<E, 128, 64>(p, gate, add, stream);
+  if (dk == 64 && dv == 128) return launch_dg<E, 64, 128>(p, gate, add, stream);
+  if (dk == 64 && dv == 64) return launch_dg<E, 64, 64>(p, gate, add, stream);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream) {
-  return dtype == 1 ? launch_de<bf16>(p, dk, dv, gate, stream) : launch_de<float>(p, dk, dv, gate, stream);
+hipError_t launch_decode(const DecodeParams &p, int dtype, int dk, int dv, int gate, bool add,
+                         hipStream_t stream) {
+  return dtype == 1 ? launch_de<bf16>(p, dk, dv, gate, add, stream) : launch_de<float>(p, dk, dv, gate, add, stream);
 }
 
-hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream) {
-  return dtype == 1 ? launch_e<bf16>(p, dk, dv, gate, stream) : launch_e<float>(p, dk, dv, gate, stream);
+hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate, bool add,
+                                 hipStream_t stream) {
+  return dtype == 1 ? launch_e<bf16>(p, dk, dv, gate, add, stream) : launch_e<float>(p, dk, dv, gate, add, stream);
 }
 
 }  // namespace gdn

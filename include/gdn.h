@@ -63,10 +63,24 @@ typedef enum {
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype; /* dtype of q, k, v, o */
 
 typedef enum {
-  GDN_GATE_NONE = 0, /* alpha = 1 (delta rule); log_alpha must be NULL      */
-  GDN_GATE_HEAD = 1, /* one log_alpha per (token, head) (gated delta rule)  */
-  GDN_GATE_KEY = 2   /* one log_alpha per (token, head, key channel)        */
+  GDN_GATE_NONE = 0,      /* alpha = 1 (delta rule); log_alpha must be NULL         */
+  GDN_GATE_HEAD = 1,      /* one log_alpha per (token, head) (gated delta rule)     */
+  GDN_GATE_KEY = 2,       /* one log_alpha per (token, head, key channel)           */
+  GDN_GATE_HEAD_CONST = 3 /* one log_alpha per head, the same at every token: [H]
+                             (RetNet's fixed per-head decay, "Linear Attention
+                             Variants", RetNet section)                            */
 } gdn_gate;
+
+/* How a token writes the state (S = M^T, k a key, v a value):
+ *   DELTA: erase what k retrieves, then write: S <- S + beta (v - S k) k^T, after the
+ *          decay ("Decoding Hybrid Linear Attention Architectures", sec. 3 items 2,
+ *          3 and 6: the delta rule and its gated forms);
+ *   ADD:   accumulate: S <- S + v k^T after the decay, no erase and no beta (sec. 3
+ *          item 4, gated linear attention; with GDN_GATE_HEAD_CONST RetNet's
+ *          retention; without a gate the plain linear-transformer sum, "Linear
+ *          Attention Variants", "The Shared Machinery").  beta must be NULL.
+ * A zero-initialised argument struct selects DELTA. */
+typedef enum { GDN_WRITE_DELTA = 0, GDN_WRITE_ADD = 1 } gdn_write;
 
 /*
  * Chunked forward over whole sequences ("Decoding Hybrid Linear Attention
@@ -89,11 +103,13 @@ typedef struct {
   int N;              /* number of sequences: B, or len(cu_seqlens) - 1              */
   gdn_dtype dtype;    /* dtype of q, k, v, o                                         */
   gdn_gate gate;      /* gate mode                                                   */
+  gdn_write write;    /* write rule                                                  */
   const void *q;      /* [B, T, H, d_k]                                              */
   const void *k;      /* [B, T, H, d_k]                                              */
   const void *v;      /* [B, T, H, d_v]                                              */
-  const float *beta;  /* [B, T, H] fp32                                              */
-  const float *log_alpha;     /* NONE: NULL; HEAD: [B,T,H]; KEY: [B,T,H,d_k] fp32   */
+  const float *beta;  /* DELTA: [B, T, H] fp32; ADD: NULL                            */
+  const float *log_alpha;     /* NONE: NULL; HEAD: [B,T,H]; KEY: [B,T,H,d_k];
+                                 HEAD_CONST: [H]; fp32                               */
   const float *initial_state; /* NULL (zeros) or [N, H, d_k, d_v] fp32 (M = S^T)     */
   const int32_t *cu_seqlens;  /* NULL or [N + 1] int32 (device)                      */
   void *o;                    /* out: [B, T, H, d_v], dtype                          */
@@ -110,11 +126,12 @@ typedef struct {
   int N, H, d_k, d_v; /* streams, heads, head dims (each 64 or 128)                  */
   gdn_dtype dtype;    /* dtype of q, k, v, o                                         */
   gdn_gate gate;
+  gdn_write write;
   const void *q;          /* [N, H, d_k]                                             */
   const void *k;          /* [N, H, d_k]                                             */
   const void *v;          /* [N, H, d_v]                                             */
-  const float *beta;      /* [N, H]                                                  */
-  const float *log_alpha; /* NONE: NULL; HEAD: [N,H]; KEY: [N,H,d_k]                 */
+  const float *beta;      /* DELTA: [N, H]; ADD: NULL                                */
+  const float *log_alpha; /* NONE: NULL; HEAD: [N,H]; KEY: [N,H,d_k]; HEAD_CONST: [H] */
   float *state;           /* in/out: [N, H, d_k, d_v] fp32, read then overwritten   */
   void *o;                /* out: [N, H, d_v], dtype                                 */
 } gdn_step_args;
@@ -139,11 +156,12 @@ typedef struct {
   int N, L, H, d_k, d_v;  /* streams, tokens per stream (>= 1), heads, head dims (64/128) */
   gdn_dtype dtype;        /* dtype of q, k, v, o                                      */
   gdn_gate gate;
+  gdn_write write;
   const void *q;          /* [N, L, H, d_k]                                           */
   const void *k;          /* [N, L, H, d_k]                                           */
   const void *v;          /* [N, L, H, d_v]                                           */
-  const float *beta;      /* [N, L, H]                                                */
-  const float *log_alpha; /* NONE: NULL; HEAD: [N,L,H]; KEY: [N,L,H,d_k]              */
+  const float *beta;      /* DELTA: [N, L, H]; ADD: NULL                              */
+  const float *log_alpha; /* NONE: NULL; HEAD: [N,L,H]; KEY: [N,L,H,d_k]; HEAD_CONST: [H] */
   float *state_pool;      /* in/out: [pool_size, H, d_k, d_v] fp32 (M = S^T), device  */
   int pool_size;          /* number of slots (>= 1)                                   */
   const int32_t *src_slots; /* [N] device: slot each stream's state is read from     */
@@ -154,7 +172,8 @@ typedef struct {
 /* Bytes of device workspace gdn_fwd_chunked needs for these arguments; 0 means none.
  * Returns 0 for arguments that gdn_fwd_chunked would reject.
  *   - with cu_seqlens (N <= 8192): a processing-order table, 4 N bytes rounded up to 256;
- *   - bf16 with d_k = 128 and the per-key-channel gate: the chunk operands prepared in
+ *   - bf16 with d_k = 128, the per-key-channel gate and the delta write: the chunk
+ *     operands prepared in
  *     a first, fully parallel pass (K e^G, Q e^G and K e^{g_C - G}: 3 x 256 bytes per
  *     token and head; T diag(beta) and P: 16 KiB, e^{g_C}: 512 bytes per chunk slot and
  *     head, with floor(B T / 64) + N slots), each part rounded up to 256 bytes.

@@ -87,6 +87,13 @@ def random_inputs(B, T, H, dk, dv, gate="head", dtype="bf16", seed=0, state_std=
                 gate=gate, dtype=dtype, N=N)
 
 
+def retnet_log_gamma(H: int) -> torch.Tensor:
+    """Fixed per-head log decays log(1 - 2^(-5 - h)), h = 0..H-1: the head-wise decay
+    schedule that the RetNet passage gives as its example (float32 [H])."""
+    h = torch.arange(H, dtype=torch.float64)
+    return torch.log1p(-torch.pow(2.0, -5.0 - h)).to(torch.float32)
+
+
 def varlen_lengths(spec):
     g = torch.Generator().manual_seed(int(spec["seed"]))
     return torch.randint(spec["len_lo"], spec["len_hi"] + 1, (spec["N"],), generator=g).tolist()

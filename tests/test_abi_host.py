@@ -85,7 +85,11 @@ def test_package_has_no_cpu_path():
     (dict(d_v=256), UNSUPPORTED),
     (dict(dtype=0), UNSUPPORTED),          # fp32 I/O needs d_k = 64
     (dict(dtype=7), INVALID),
-    (dict(gate=3), INVALID),
+    (dict(gate=4), INVALID),
+    (dict(write=2), INVALID),
+    (dict(write=1), INVALID),              # the additive write takes no beta
+    (dict(beta=None), INVALID),            # the delta write needs beta
+    (dict(gate=3, log_alpha=None), INVALID),  # constant per-head gate without its decays
     (dict(log_alpha=None), INVALID),       # scalar gate without its decays
     (dict(gate=0), INVALID),               # no gate but decays given
     (dict(q=None), INVALID),
@@ -155,6 +159,10 @@ def step_args(g, **kw):
     (dict(state=fake(5, 4)), INVALID),
     (dict(log_alpha=None), INVALID),
     (dict(gate=0), INVALID),
+    (dict(gate=4), INVALID),
+    (dict(write=1), INVALID),
+    (dict(write=-1), INVALID),
+    (dict(beta=None), INVALID),
     (dict(dtype=5), INVALID),
     (dict(H=0), INVALID),
 ])
@@ -186,7 +194,10 @@ def decode_args(g, **kw):
     (dict(o=None), INVALID),
     (dict(log_alpha=None), INVALID),
     (dict(gate=0), INVALID),
-    (dict(gate=3), INVALID),
+    (dict(gate=4), INVALID),
+    (dict(write=3), INVALID),
+    (dict(write=1), INVALID),
+    (dict(beta=None), INVALID),
     (dict(dtype=2), INVALID),
     (dict(state_pool=fake(5, 8)), INVALID),
     (dict(src_slots=fake(6, 2)), INVALID),
@@ -254,3 +265,21 @@ def test_binding_rejects_bad_decode_tensors(g):
                         (dict(), "GPU device")]:
         with pytest.raises(ValueError, match=msg):
             g.decode(**dict(ok, **change))
+
+
+def test_binding_write_rule_and_constant_gate(g):
+    t = fwd_tensors()
+    with pytest.raises(ValueError, match="write must"):
+        g.fwd_chunked(**t, write="erase")
+    with pytest.raises(ValueError, match="beta must be None"):
+        g.fwd_chunked(**t, write="add")
+    t_add = dict(t, beta=None)
+    with pytest.raises(ValueError, match="beta must be float32"):
+        g.fwd_chunked(**t_add)                       # the delta rule needs beta
+    with pytest.raises(ValueError, match="log_alpha must be"):
+        g.fwd_chunked(**dict(t_add, log_alpha=torch.zeros(4)), write="add")  # H = 3
+    with pytest.raises(ValueError, match="GPU device"):  # well-formed: RetNet decays [H]
+        g.fwd_chunked(**dict(t_add, log_alpha=torch.zeros(3)), write="add")
+    assert g.gate_code(torch.zeros(3), 3) == g.GDN_GATE_HEAD_CONST
+    assert g.gate_code(torch.zeros(2, 5, 3), 3) == g.GDN_GATE_HEAD
+    assert g.gate_code(torch.zeros(2, 5, 3, 64), 3) == g.GDN_GATE_KEY
