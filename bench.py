@@ -44,17 +44,23 @@ CHUNK = 64
 SETTLE_MS = 50.0  # continuous load before timing the workloads other than the headline
 
 
-def alg_counts(tokens, H, dk, dv, nseq, gate, esize, has_init, has_final=True):
+def alg_counts(tokens, H, dk, dv, nseq, gate, esize, has_init, has_final=True, write="delta"):
     """Algorithmic flops and bytes of the chunked method (chunk 64).
 
     flops per token-head: 2C(3 d_k + 2 d_v) + 6 d_k d_v + C^2/3 (Gram tiles, UT inverse,
-    W and U, W M, K^T Delta, Q M, Q K^T, P Delta; multiply-add = 2).
-    bytes: q, k, v read and o written in the I/O dtype, beta and log alpha in fp32,
-    the fp32 initial state read (if given) and final state written.
+    W and U, W M, K^T Delta, Q M, Q K^T, P Delta; multiply-add = 2).  The additive
+    write has no erase: 2C(d_k + d_v) + 4 d_k d_v (Q K^T, P V, Q M, K^T V).
+    bytes: q, k, v read and o written in the I/O dtype, beta (delta write only) and
+    log alpha in fp32 (per token for "head", per channel for "key", one value per
+    head for "const"), the fp32 initial state read (if given) and final state written.
     """
     C = CHUNK
-    f_th = 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv + C * C / 3.0
-    b_th = esize * (2 * dk + 2 * dv) + 4 + (4 if gate == "head" else 4 * dk if gate == "key" else 0)
+    if write == "add":
+        f_th = 2 * C * (dk + dv) + 4 * dk * dv
+    else:
+        f_th = 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv + C * C / 3.0
+    b_th = (esize * (2 * dk + 2 * dv) + (4 if write == "delta" else 0)
+            + (4 if gate == "head" else 4 * dk if gate == "key" else 0))
     state = 4 * dk * dv * nseq * H * ((1 if has_init else 0) + (1 if has_final else 0))
     return f_th * tokens * H, b_th * tokens * H + state
 
@@ -103,7 +109,7 @@ def time_chunked(gdn, sets, steps, warmup):
     # one validated call per input copy: each timed step is a single library call
     stream = torch.cuda.current_stream()
     calls = [gdn.PreparedFwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"],
-                             d["cu_seqlens"]) for d in sets]
+                             d["cu_seqlens"], write=d.get("write", "delta")) for d in sets]
 
     def call(i):
         calls[i % len(calls)].launch(stream)
@@ -229,7 +235,7 @@ def bench_workload(gdn, name, steps, warmup):
     tokens = B * T
     esize = 2 if spec["dtype"] == "bf16" else 4
     flops, nbytes = alg_counts(tokens, H, dk, dv, inp["N"], spec["gate"], esize,
-                               inp["initial_state"] is not None)
+                               inp["initial_state"] is not None, write=spec.get("write", "delta"))
     res = {"workload": name, "ms_per_step": wall / steps * 1e3, "launch_ms": launch_ms,
            "tokens_per_s": tokens / (wall / steps), "alg_flops": flops, "alg_bytes": nbytes,
            "tflops": flops / (launch_ms / 1e3) / 1e12,
@@ -303,7 +309,8 @@ def main():
         del sets
         torch.cuda.empty_cache()
         for name in ["gdn-bf16-B4-T2048-H8-d128", "kda-bf16-B2-T16384-H16-d128",
-                     "gdn-varlen-bf16-N32-H16-d128", "deltanet-fp32-B1-T256-H2-d64"]:
+                     "gdn-varlen-bf16-N32-H16-d128", "deltanet-fp32-B1-T256-H2-d64",
+                     "retnet-bf16-B16-T2048-H8-d128", "gla-bf16-B2-T16384-H16-d128"]:
             try:
                 r, winp, wsets = bench_workload(gdn, name, max(5, args.steps // 5), None)
             except RuntimeError as e:

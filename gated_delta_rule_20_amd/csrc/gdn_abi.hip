@@ -68,10 +68,10 @@ size_t order_bytes(const gdn_fwd_args *a) {
   return align256((size_t)a->N * sizeof(int32_t));
 }
 
-// The pipelined kernel takes bf16 with d_k = 128, the delta write and per-token (or
-// no) decays; everything else runs on the fused kernel.
+// The pipelined kernel takes bf16 with d_k = 128 (the per-key-channel gate with the
+// delta write only); everything else runs on the fused kernel.
 bool use_pipe(const gdn_fwd_args *a) {
-  return a->dtype == GDN_BF16 && a->d_k == 128 && a->write == GDN_WRITE_DELTA && a->gate != GDN_GATE_HEAD_CONST;
+  return a->dtype == GDN_BF16 && a->d_k == 128 && !(a->gate == GDN_GATE_KEY && a->write == GDN_WRITE_ADD);
 }
 // The per-key-channel gate on the pipelined kernel: a first pass prepares every
 // chunk's operands in the workspace.
@@ -192,7 +192,8 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
   }
   if (use_pipe(a)) {
     p.nb = a->d_v / 64;
-    if (gdn::launch_fwd_pipe(p, (int)a->gate, stream) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_fwd_pipe(p, (int)a->gate, a->write == GDN_WRITE_ADD, stream) != hipSuccess)
+      return GDN_ERR_HIP;
     return GDN_OK;
   }
   const int dvb = choose_dvb(a->N, a->H, a->d_v);

@@ -60,6 +60,8 @@ constexpr int C = 64, DK = 128, DVB = 64, NT = 512;
 // next chunk: TA, TB (T) and PA, PB (P), which also load (LKQ: K and V; LBL: Q, beta,
 // log alpha, and the decay vectors)
 constexpr int W_TA = 2, W_TB = 3, W_PA = 6, W_PB = 7;
+// one decay per (token, head), or one constant decay per head
+constexpr bool scalar_gate(int g) { return g == GATE_HEAD || g == GATE_CONST; }
 constexpr int W_LKQ = W_PA, W_LBL = W_PB;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -206,6 +208,8 @@ __device__ __forceinline__ void load_bl(const Res &rs, char *dst, int chunk, int
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.beta, (lds_void_t *)dst, 4, lane * rs.row_s, soff, 0, 0);
   if (GATE == GATE_HEAD)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.la, (lds_void_t *)(dst + 256), 4, lane * rs.row_s, soff, 0, 0);
+  if (GATE == GATE_CONST)  // the head's one value, for every row
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.la, (lds_void_t *)(dst + 256), 4, 0, 0, 0, 0);
 }
 
 // ---- decay prefix and the per-position factors of Gamma (loader wave, two chunks ahead).
@@ -217,9 +221,11 @@ __device__ __forceinline__ void load_bl(const Res &rs, char *dst, int chunk, int
 // state-phase vectors with the state waves' running decay scalar folded in.
 // `gam` is that scalar entering this chunk (uniform); it is advanced to the value
 // entering the next chunk with exactly the state waves' rule, so the chunks must be
-// prepared in order.
+// prepared in order.  `nvalid` is the number of the chunk's rows inside the sequence:
+// with the constant per-head decay the rows past the end take log alpha = 0 (the
+// per-token decays of those rows already read as 0).
 template <int GATE>
-__device__ __forceinline__ void gate_vectors(const char *bl, float *gv, int lane, float &gam) {
+__device__ __forceinline__ void gate_vectors(const char *bl, float *gv, int lane, float &gam, int nvalid) {
   gv[GV_BETA + lane] = ((const float *)bl)[lane];
   if (GATE == GATE_NONE) {
     gv[GV_EH + lane] = 1.f;
@@ -235,6 +241,7 @@ __device__ __forceinline__ void gate_vectors(const char *bl, float *gv, int lane
     return;
   }
   float g = ((const float *)bl)[64 + lane];
+  if (GATE == GATE_CONST && lane >= nvalid) g = 0.f;
   // inclusive prefix sum: within rows of 16 lanes by DPP shifts, then row totals
   g += row_shr<1>(g);
   g += row_shr<2>(g);
@@ -256,7 +263,7 @@ __device__ __forceinline__ void gate_vectors(const char *bl, float *gv, int lane
   gv[GV_ET + lane] = __expf(gend - g);
   // Gn = Gam * e^{g_C}; below 2^-100 the state waves renormalise (eager chunk)
   const float Gn = gam * __expf(gE3);
-  const bool eager = GATE == GATE_HEAD && !(Gn >= 0x1p-100f);
+  const bool eager = scalar_gate(GATE) && !(Gn >= 0x1p-100f);
   const float winv = eager ? 1.f : __builtin_amdgcn_rcpf(Gn);
   gv[GV_EGS + lane] = __expf(g) * gam;
   gv[GV_EGCW + lane] = __expf(gE3 - g) * winv;
@@ -315,7 +322,7 @@ __device__ __forceinline__ f32x4 gamma_tile(const GammaRegs &G, int a, int b, in
   return out;
 }
 
-template <int GATE>
+template <int GATE, bool ADD>
 __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   __shared__ __align__(16) char smem[LDS_TOTAL];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -366,9 +373,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     rs.k = __builtin_amdgcn_make_buffer_rsrc((void *)((const bf16 *)p.k + ((size_t)tok0 * H + h) * DK), 0, nk, 0x00020000);
     rs.q = __builtin_amdgcn_make_buffer_rsrc((void *)((const bf16 *)p.q + ((size_t)tok0 * H + h) * DK), 0, nk, 0x00020000);
     rs.v = __builtin_amdgcn_make_buffer_rsrc((void *)((const bf16 *)p.v + ((size_t)tok0 * H + h) * dv + col0), 0, nvb, 0x00020000);
-    rs.beta = __builtin_amdgcn_make_buffer_rsrc((void *)(p.beta + (size_t)tok0 * H + h), 0, ns, 0x00020000);
-    rs.la = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(GATE == GATE_HEAD ? p.log_alpha + (size_t)tok0 * H + h : p.beta), 0, GATE == GATE_HEAD ? ns : 0, 0x00020000);
+    // (the additive write reads no beta: zero records, so its loads return 0)
+    rs.beta = ADD ? __builtin_amdgcn_make_buffer_rsrc((void *)p.q, 0, 0, 0x00020000)
+                  : __builtin_amdgcn_make_buffer_rsrc((void *)(p.beta + (size_t)tok0 * H + h), 0, ns, 0x00020000);
+    if (GATE == GATE_CONST)
+      rs.la = __builtin_amdgcn_make_buffer_rsrc((void *)(p.log_alpha + h), 0, len > 0 ? 4 : 0, 0x00020000);
+    else
+      rs.la = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(GATE == GATE_HEAD ? p.log_alpha + (size_t)tok0 * H + h : (ADD ? p.q : p.beta)), 0,
+          GATE == GATE_HEAD ? ns : 0, 0x00020000);
     rs.kh = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(GATE == GATE_KEY ? (const bf16 *)p.k_hat + ((size_t)tok0 * H + h) * DK : (const bf16 *)p.k), 0,
         GATE == GATE_KEY ? nk : 0, 0x00020000);
@@ -430,6 +443,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     // phase 1: Gram tiles, diagonal inverses (wave TA), P tiles (waves PA, PB)
     // r3 = chunk % 3 (K/Q, decay vectors), r2 = chunk % 2 (T/P)
     auto phase1 = [&](int r3, int r2) {
+      if (ADD && wave != W_PA && wave != W_PB) return;  // the additive write needs no T
       const char *Ks = KQ(r3), *Qs = KQ(r3) + C * DK * 2;
       char *pre = PRE(r2);
       const float *gv = GV(r3);
@@ -570,7 +584,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     // columns 1 and 2.  T[k][b] stay in registers as C tiles (column-distributed); the
     // transposed product -Y^T T[a][a]^T gives the row-distributed copy for LDS.
     auto phase2 = [&](int r3, int r2) {
-      if (wave != W_TA && wave != W_TB) return;
+      if (ADD || (wave != W_TA && wave != W_TB)) return;
       char *Tm = PRE(r2);
       const float *gv = GV(r3);
       bf16x4 aof[6];
@@ -635,17 +649,17 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
           load_kq(rs, KQ(1), 1, lane, true);  // 16 + 2 + 2 loads
           load_bl<GATE>(rs, BL(1), 1, lane);
           load_bl<GATE>(rs, BL(2), 2, lane);
-          if (GATE == GATE_HEAD) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+          if (scalar_gate(GATE)) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
           else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
         } else if (nchunks > 1) {
           load_kq(rs, KQ(1), 1, lane, true);  // 16 + 2 loads
           load_bl<GATE>(rs, BL(1), 1, lane);
-          if (GATE == GATE_HEAD) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+          if (scalar_gate(GATE)) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
           else asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
         } else {
           wait_vm0();
         }
-        gate_vectors<GATE>(BL(0), GV(0), lane, gam_run);
+        gate_vectors<GATE>(BL(0), GV(0), lane, gam_run, len);
       }
     }
     __syncthreads();
@@ -657,7 +671,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     // wait for every outstanding memory operation of the wave first)
     int *flags = (int *)(smem + OFF_FLAGS);
     auto handoff = [&](int cc) {
-      if (wave != W_TA && wave != W_TB) return;
+      if (ADD || (wave != W_TA && wave != W_TB)) return;
       const int mine = wave == W_TA ? 0 : 1;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own LDS writes done
       if (lane == 0) __hip_atomic_store(flags + mine, cc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -675,7 +689,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       wait_vm0();
     } else if (wave == W_LBL) {
       wait_vm0();
-      if (nchunks > 1) gate_vectors<GATE>(BL(1), GV(1), lane, gam_run);
+      if (nchunks > 1) gate_vectors<GATE>(BL(1), GV(1), lane, gam_run, len - C);
     }
     __syncthreads();
     int n3 = 1, n2 = 1, l3 = 2;  // (c + 1) % 3, (c + 1) % 2, (c + 2) % 3
@@ -688,7 +702,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
         // are computed here, off the path that waits for this chunk's loads
         if (c + 2 < nchunks) load_kq(rs, KQ(l3), c + 2, lane, true);
         if (c + 3 < nchunks) load_bl<GATE>(rs, BL(3 - n3 - l3), c + 3, lane);
-        if (c + 2 < nchunks) gate_vectors<GATE>(BL(l3), GV(l3), lane, gam_run);
+        if (c + 2 < nchunks) gate_vectors<GATE>(BL(l3), GV(l3), lane, gam_run, len - (c + 2) * C);
       }
       if (c + 1 < nchunks) {
         phase1(n3, n2);
@@ -792,6 +806,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     for (int i = 0; i < 4; ++i) X[i] = zero4();
     bf16x8 kf[2][4], qf[2][4];
     bf16x4 vv[4];
+    if constexpr (ADD) {  // no erase: nothing to retrieve
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qf[0][i] = *(const bf16x8 *)(kqb[0] + C * DK * 2 + 4096 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] = tr16(Vs + 2048 * i);
+    } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) kf[0][i] = *(const bf16x8 *)(kqb[0] + 4096 * i);
 #pragma unroll
@@ -810,10 +830,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       for (int i = 0; i < 4; ++i) X[i] = mma(kf[st & 1][i], MB[st], X[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    }
     // ---- O^T = M_hat^T Q^T, with the V / decay scaling of X and its B fragments in
     // the MFMA gaps: X <- V - Gam e^g X (beta is folded into T)
     const float Gn = KP ? 1.f : gv[GV_GN];
-    const bool eager = (GATE == GATE_HEAD) && gv[GV_EAGER] != 0.f;
+    const bool eager = (scalar_gate(GATE)) && gv[GV_EAGER] != 0.f;
     f32x4 OT[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) OT[i] = zero4();
@@ -823,7 +844,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       if (st + 1 < 4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) qf[(st + 1) & 1][i] = *(const bf16x8 *)(kqb[st + 1] + C * DK * 2 + 4096 * i);
-      } else {
+      } else if (!ADD) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -835,7 +856,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
       if (st < 2) {
 #pragma unroll
         for (int i = 2 * st; i < 2 * st + 2; ++i) {
-          if (KP) {  // K e^G already carries the row decay
+          if (ADD) {  // Delta = V
+#pragma unroll
+            for (int j = 0; j < 4; ++j) X[i][j] = (float)vv[i][j];
+          } else if (KP) {  // K e^G already carries the row decay
 #pragma unroll
             for (int j = 0; j < 4; ++j) X[i][j] = (float)vv[i][j] - X[i][j];
           } else {
@@ -844,7 +868,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
             for (int j = 0; j < 4; ++j) X[i][j] = (float)vv[i][j] - eg4[j] * X[i][j];
           }
         }
-      } else if (st == 2) {
+      } else if (st == 2 && !ADD) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) XB[s2] = frag_from_c<bf16>(X[2 * s2], X[2 * s2 + 1]);
       }
@@ -852,12 +876,17 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     }
     // ---- Delta = T X  (T lower triangular: row blocks 0, 1 need the first 32 columns only)
     f32x4 D[4];
+    if constexpr (ADD) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) D[i] = X[i];
+    } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) D[i] = zero4();
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int i = 2 * s2; i < 4; ++i) D[i] = mma(tf[i][s2], XB[s2], D[i]);
+    }
     // P fragments and the first K^T fragments in flight; O^T scaled by Gam e^g meanwhile
     bf16x8 pf[4][2];
 #pragma unroll
@@ -1290,13 +1319,17 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
 
 }  // namespace
 
-hipError_t launch_fwd_pipe(const FwdParams &p, int gate, hipStream_t stream) {
+hipError_t launch_fwd_pipe(const FwdParams &p, int gate, bool add, hipStream_t stream) {
   const int blocks = p.N * p.H * p.nb;
   if (blocks == 0) return hipSuccess;
-  switch (gate) {
-    case GATE_NONE: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_NONE>), dim3(blocks), dim3(NT), 0, stream, p); break;
-    case GATE_HEAD: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_HEAD>), dim3(blocks), dim3(NT), 0, stream, p); break;
-    case GATE_KEY: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_KEY>), dim3(blocks), dim3(NT), 0, stream, p); break;
+  switch (gate * 2 + (add ? 1 : 0)) {
+    case 2 * GATE_NONE: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_NONE, false>), dim3(blocks), dim3(NT), 0, stream, p); break;
+    case 2 * GATE_NONE + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_NONE, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+    case 2 * GATE_HEAD: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_HEAD, false>), dim3(blocks), dim3(NT), 0, stream, p); break;
+    case 2 * GATE_HEAD + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_HEAD, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+    case 2 * GATE_CONST: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_CONST, false>), dim3(blocks), dim3(NT), 0, stream, p); break;
+    case 2 * GATE_CONST + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_CONST, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+    case 2 * GATE_KEY: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_KEY, false>), dim3(blocks), dim3(NT), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -5,7 +5,10 @@
 
 namespace gdn {
 
-enum { GATE_NONE = 0, GATE_HEAD = 1, GATE_KEY = 2 };
+// GATE_CONST: one decay per head, the same at every token (read with a token stride
+// of 0); the pipelined kernel has an instantiation of its own for it, the other
+// kernels run it as GATE_HEAD with la_stride = 0.
+enum { GATE_NONE = 0, GATE_HEAD = 1, GATE_KEY = 2, GATE_CONST = 3 };
 
 struct FwdParams {
   const void *q, *k, *v;         // [tokens, H, d_k] / [tokens, H, d_v]
@@ -61,9 +64,11 @@ struct DecodeParams {
 // add: the additive write (S += v k^T; beta unused) instead of the delta rule.
 hipError_t launch_fwd_fused(const FwdParams &p, int dtype, int dk, int dvb, int gate, bool add,
                             hipStream_t stream);
-// Software-pipelined forward for bf16, d_k = 128, 64-column value blocks (nb = d_v / 64).
+// Software-pipelined forward for bf16, d_k = 128, 64-column value blocks (nb = d_v / 64);
+// gate: GATE_NONE, GATE_HEAD, GATE_CONST or GATE_KEY (the latter with the prepared
+// operands, delta write only); add: the additive write.
 // Gate NONE or HEAD; gate KEY after launch_key_prep, with the k_hat, tp_img, egc fields.
-hipError_t launch_fwd_pipe(const FwdParams &p, int gate, hipStream_t stream);
+hipError_t launch_fwd_pipe(const FwdParams &p, int gate, bool add, hipStream_t stream);
 // Per-key-channel gate, bf16, d_k = 128: for every chunk (all in parallel) the
 // pre-scaled operands K e^G, Q e^G, K e^{g_C - G}, e^{g_C}, and T diag(beta) and P as
 // the LDS images the pipelined kernel loads.

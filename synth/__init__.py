@@ -11,6 +11,8 @@ Distributions (the same for every workload unless stated):
   gate   "head": log alpha = -softplus(N(0,1)) * exp(U(-3,0)), one value per (token, head)
          "key":  log alpha = -softplus(N(0,1)), one value per (token, head, key channel)
          "none": absent
+         "const": one fixed log decay per head, log(1 - 2^(-5-h)) (RetNet's schedule)
+  write  "delta" (default) or "add" (beta absent)
   state  optional initial state ~ N(0, std^2), fp32, layout [N,H,d_k,d_v] (M = S^T)
 Draw order: sequence lengths (varlen), q, k, v, beta logits, gate factors, initial
 state, then decode tokens.
@@ -34,6 +36,14 @@ WORKLOADS = {
     "gdn-varlen-bf16-N32-H16-d128": dict(
         N=32, len_lo=512, len_hi=16384, H=16, dk=128, dv=128, gate="head", dtype="bf16",
         state_std=None, seed=1004, decode_steps=64, decode_batch=256),
+    # the additive write at the same shapes: RetNet (fixed per-head decays, the
+    # pages' schedule 1 - 2^(-5-h)) and gated linear attention (per-key decays)
+    "retnet-bf16-B16-T2048-H8-d128": dict(
+        B=16, T=2048, H=8, dk=128, dv=128, gate="const", write="add", dtype="bf16", state_std=0.02,
+        seed=1005),
+    "gla-bf16-B2-T16384-H16-d128": dict(
+        B=2, T=16384, H=16, dk=128, dv=128, gate="key", write="add", dtype="bf16", state_std=None,
+        seed=1006),
 }
 
 CHUNK = 64
@@ -109,8 +119,16 @@ def workload_inputs(name: str):
                             spec["dtype"], seed=spec["seed"] + 7919, lengths=lengths)
         out["lengths"] = lengths
         return out
-    return random_inputs(spec["B"], spec["T"], spec["H"], spec["dk"], spec["dv"], spec["gate"],
-                         spec["dtype"], seed=spec["seed"], state_std=spec["state_std"])
+    const = spec["gate"] == "const"
+    out = random_inputs(spec["B"], spec["T"], spec["H"], spec["dk"], spec["dv"],
+                        "none" if const else spec["gate"], spec["dtype"], seed=spec["seed"],
+                        state_std=spec["state_std"])
+    if const:
+        out["log_alpha"], out["gate"] = retnet_log_gamma(spec["H"]), "const"
+    out["write"] = spec.get("write", "delta")
+    if out["write"] == "add":
+        out["beta"] = None
+    return out
 
 
 def decode_inputs(N, H, dk, dv, steps, gate="head", dtype="bf16", seed=0):

@@ -75,7 +75,7 @@ def test_additive_varlen(gdn, gate):
 
 @pytest.mark.parametrize("dk", [64, 128])
 def test_constant_decay_delta_rule(gdn, dk):
-    """The delta rule with a fixed per-head decay (routed to the fused kernel)."""
+    """The delta rule with a fixed per-head decay."""
     check(gdn, inputs(2, 190, 3, dk, 128, "const", "bf16", seed=9), write="delta")
 
 
@@ -120,3 +120,10 @@ def test_additive_decode_and_step(gdn, gate, L):
                                  inp["state_pool"][src], write="add")
     assert relerr(o1.cpu(), o1_ref) <= TOL["bf16"]
     assert relerr(st.cpu(), st_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["retnet-bf16-B16-T2048-H8-d128", "gla-bf16-B2-T16384-H16-d128"])
+def test_additive_workloads_full_size(gdn, name):
+    """The benchmark's additive-write workloads, at their full sizes, checked in full."""
+    inp = synth.workload_inputs(name)
+    check(gdn, inp, write=inp["write"])
