@@ -68,11 +68,9 @@ size_t order_bytes(const gdn_fwd_args *a) {
   return align256((size_t)a->N * sizeof(int32_t));
 }
 
-// The pipelined kernel takes bf16 with d_k = 128 (the per-key-channel gate with the
-// delta write only); everything else runs on the fused kernel.
-bool use_pipe(const gdn_fwd_args *a) {
-  return a->dtype == GDN_BF16 && a->d_k == 128 && !(a->gate == GDN_GATE_KEY && a->write == GDN_WRITE_ADD);
-}
+// The pipelined kernel takes bf16 with d_k = 128; everything else runs on the fused
+// kernel.
+bool use_pipe(const gdn_fwd_args *a) { return a->dtype == GDN_BF16 && a->d_k == 128; }
 // The per-key-channel gate on the pipelined kernel: a first pass prepares every
 // chunk's operands in the workspace.
 bool key_pipe(const gdn_fwd_args *a) { return a->gate == GDN_GATE_KEY && use_pipe(a); }
@@ -183,7 +181,7 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
     kp.N = a->N;
     kp.H = a->H;
     kp.T = a->T;
-    if (gdn::launch_key_prep(kp, L.slots, stream) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_key_prep(kp, L.slots, a->write == GDN_WRITE_ADD, stream) != hipSuccess) return GDN_ERR_HIP;
     p.k = kp.k_g;  // the pipelined kernel then reads the pre-scaled operands
     p.q = kp.q_g;
     p.k_hat = kp.k_hat;

@@ -410,7 +410,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     const long slot0 = (tok0 >> 6) + n;  // slot of this sequence's chunk 0
     auto ld_chunk = [&](int cc, int st) {
       if (wave == W_TA) {
-        load_kq(rs, KQ(st), cc, lane, false);  // K e^G
+        if (!ADD) load_kq(rs, KQ(st), cc, lane, false);  // K e^G (the additive write reads none)
       } else if (wave == W_TB) {
         load_kq(rs, KQ(st), cc, lane, true);   // Q e^G
       } else if (wave == W_PA) {
@@ -1017,6 +1017,7 @@ __device__ __forceinline__ void kp_barrier() {  // LDS-only barrier: loads stay 
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+template <bool ADD>
 __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, long items) {
   __shared__ __align__(16) char smem[KP_BYTES];
   float *Gs = (float *)(smem + KP_OFF_G);
@@ -1083,7 +1084,7 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
         q_r[u] = *(const u32x4 *)((const bf16 *)p.q + o);
       }
     }
-    b_r = (it.ok && tid < it.nv) ? p.beta[(size_t)(it.t0 + tid) * H + it.h] : 0.f;
+    b_r = (!ADD && it.ok && tid < it.nv) ? p.beta[(size_t)(it.t0 + tid) * H + it.h] : 0.f;
   };
 
   long w = blockIdx.x;
@@ -1167,7 +1168,7 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
       *(bf16x8 *)(QA + r * KP_SK + 8 * g) = qa;  // each thread rewrites only its own Q entries
       if (r < nv) {
         const size_t o = ((size_t)(t0 + r) * H + h) * DK + 8 * g;
-        *(bf16x8 *)((bf16 *)p.k_g + o) = kg;
+        if (!ADD) *(bf16x8 *)((bf16 *)p.k_g + o) = kg;  // the additive write retrieves nothing
         *(bf16x8 *)((bf16 *)p.q_g + o) = qg;
         *(bf16x8 *)((bf16 *)p.k_hat + o) = kh;
       }
@@ -1197,7 +1198,7 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
         bf16x8 bk;
 #pragma unroll
         for (int j = 0; j < 8; ++j) bk[j] = (bf16)((float)kbv[j] * (f[j] * et[j]));
-        kk = mma(ak, bk, kk);
+        if (!ADD) kk = mma(ak, bk, kk);
         qk = mma(aq, bk, qk);
       }
       // lane: column i = 16b + lm, rows r = 16a + 4lg + j
@@ -1205,9 +1206,11 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * a + 4 * lg + j;
-        const float av = i < r ? bs[r] * kk[j] : 0.f;
-        if (a == b) AD[(16 * a + 4 * lg + j) * AD_STRIDE + lm] = av;
-        else As[r * KP_ST + i] = (bf16)av;
+        if (!ADD) {
+          const float av = i < r ? bs[r] * kk[j] : 0.f;
+          if (a == b) AD[(16 * a + 4 * lg + j) * AD_STRIDE + lm] = av;
+          else As[r * KP_ST + i] = (bf16)av;
+        }
         *(bf16 *)(img + PRE_P + tp_off(r, i)) = (bf16)(i <= r ? qk[j] : 0.f);
       }
     };
@@ -1217,7 +1220,8 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
 
     // ---- diagonal blocks of T in fp32: lane (lg, lm) owns row lm of block lg,
     // t_r = e_r - sum_{i<r} A[r][i] t_i with rows broadcast along the 16-lane DPP row
-    if (wave == 0) {
+    // (the additive write needs no T: its half of the image stays zero)
+    if (!ADD && wave == 0) {
       float nar[16], t[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -1276,7 +1280,7 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
     kp_barrier();
     // ---- off-diagonal blocks: T[a][b] = -T[a][a] sum_{k=b}^{a-1} A[a][k] T[k][b];
     // wave b walks block column b downwards with T[k][b] kept as C tiles
-    if (wave < 3) {
+    if (!ADD && wave < 3) {
       const int b = wave;
       const float bc = bs[16 * b + lm];
       f32x4 Tc[4];
@@ -1330,12 +1334,13 @@ hipError_t launch_fwd_pipe(const FwdParams &p, int gate, bool add, hipStream_t s
     case 2 * GATE_CONST: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_CONST, false>), dim3(blocks), dim3(NT), 0, stream, p); break;
     case 2 * GATE_CONST + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_CONST, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
     case 2 * GATE_KEY: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_KEY, false>), dim3(blocks), dim3(NT), 0, stream, p); break;
+    case 2 * GATE_KEY + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_KEY, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_key_prep(const KeyPrepParams &p, long slots, hipStream_t stream) {
+hipError_t launch_key_prep(const KeyPrepParams &p, long slots, bool add, hipStream_t stream) {
   if (slots <= 0 || p.N <= 0 || p.H <= 0) return hipSuccess;
   const long items = slots * p.H;
   int dev = 0, cus = 256;
@@ -1343,7 +1348,10 @@ hipError_t launch_key_prep(const KeyPrepParams &p, long slots, hipStream_t strea
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
   const long grid = items < cus ? items : cus;  // persistent: one workgroup per CU
-  hipLaunchKernelGGL(key_prep_kernel, dim3((unsigned)grid), dim3(KP_NT), 0, stream, p, items);
+  if (add)
+    hipLaunchKernelGGL(key_prep_kernel<true>, dim3((unsigned)grid), dim3(KP_NT), 0, stream, p, items);
+  else
+    hipLaunchKernelGGL(key_prep_kernel<false>, dim3((unsigned)grid), dim3(KP_NT), 0, stream, p, items);
   return hipGetLastError();
 }
 

@@ -82,7 +82,8 @@ struct KeyPrepParams {
   float *egc;                    // [slots, H, 128]
   int N, H, T;
 };
-hipError_t launch_key_prep(const KeyPrepParams &p, long slots, hipStream_t stream);
+// add: operands for the additive write (no beta, no T, no K e^G).
+hipError_t launch_key_prep(const KeyPrepParams &p, long slots, bool add, hipStream_t stream);
 hipError_t launch_seq_order(const int32_t *cu_seqlens, int N, int32_t *order, hipStream_t stream);
 hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate, bool add,
                                  hipStream_t stream);
