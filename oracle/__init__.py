@@ -11,7 +11,9 @@ Parity status: every function here is pinned.  ``fwd`` and ``step`` by
 ``tests/test_oracle_pins.py`` (closed forms, invariants, an autograd-derived
 gradient step, exact rational fixtures under ``tests/golden/`` and planted-mistake
 checks); ``decode_pool`` by ``tests/test_oracle_decode.py`` (against ``fwd`` over
-the same tokens and over every stored prefix, chained and speculative calls); the
+the same tokens and over every stored prefix, chained and speculative calls); ``bwd``
+by ``tests/test_oracle_bwd.py`` (central finite differences of ``fwd`` and torch
+autograd of the recurrence in fp64); the
 additive write (``write="add"``) and the constant per-head gate by
 ``tests/test_oracle_additive.py`` (RetNet's decay-mask parallel form, the
 gated-linear-attention brute-force sum, the plain linear-transformer sum, agreement
@@ -63,6 +65,9 @@ def _declare(lib):
     lib.oracle_step.restype = ctypes.c_int
     lib.oracle_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp]
+    lib.oracle_bwd.restype = ctypes.c_int
+    lib.oracle_bwd.argtypes = [ctypes.c_int, ip, ip, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -132,6 +137,47 @@ def fwd(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None, gate
     if rc != 0:
         raise RuntimeError("oracle_fwd failed (%d)" % rc)
     return o, fs
+
+
+def bwd(q, k, v, beta, log_alpha, initial_state, dout, dfinal=None, cu_seqlens=None, gate=None,
+        nthreads: int = 0, lib=None):
+    """Gradients of the delta-rule recurrence (no gate, one decay per (token, head), or
+    one constant decay per head [H]) with respect to q, k, v, beta, log_alpha and the
+    initial state, given dout [B,T,H,d_v] (the gradient of o) and dfinal None |
+    [N,H,d_k,d_v] (the gradient of the final state).  Shapes as for ``fwd``.
+    Returns (dq, dk, dv, dbeta, dlog_alpha or None, dinit [N,H,d_k,d_v]) in fp64; for
+    the constant gate dlog_alpha is [H] (the per-token gradients summed)."""
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    log_alpha, initial_state, dout, dfinal = _f64(log_alpha), _f64(initial_state), _f64(dout), _f64(dfinal)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if gate is None:
+        gate = infer_gate(log_alpha, 3)
+    const = gate == "const"
+    if const:
+        log_alpha, gate = _per_token(log_alpha, (B, T)), "head"
+    if cu_seqlens is not None:
+        cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64)
+        start, lens = cu[:-1].copy(), np.diff(cu)
+    else:
+        start = np.arange(B, dtype=np.int64) * T
+        lens = np.full(B, T, dtype=np.int64)
+    N = len(start)
+    dq, dk_ = np.zeros_like(q), np.zeros_like(k)
+    dv_, db = np.zeros_like(v), np.zeros_like(beta)
+    dla = np.zeros((B, T, H)) if gate == "head" else None
+    dinit = np.zeros((N, H, dk, dv))
+    lib = lib or load()
+    rc = lib.oracle_bwd(N, start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                        lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv, GATES[gate],
+                        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(initial_state),
+                        _ptr(dout), _ptr(dfinal), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(db), _ptr(dla),
+                        _ptr(dinit), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_bwd failed (%d)" % rc)
+    if const:
+        dla = dla.sum(axis=(0, 1))
+    return dq, dk_, dv_, db, dla, dinit
 
 
 def step(q, k, v, beta, log_alpha, state, gate=None, lib=None, write: str = "delta"):

@@ -152,6 +152,125 @@ int oracle_step(int N, int H, int dk, int dv, int gate, int write, const double 
   return 0;
 }
 
+/*
+ * Gradients of the token recurrence above (reverse mode, fp64), for the delta write
+ * with no gate or one decay per (token, head).  For one token, with M' = a M_{t-1},
+ * r = M'^T k, e = v - r, M_t = M' + beta k e^T, o = M_t^T q, and the gradient G of
+ * the loss with respect to M_t (everything that later tokens and the final state
+ * pass back) plus do:
+ *   G    += q do^T                    dq = M_t do
+ *   dbeta = k^T G e                   de = beta G^T k
+ *   dk    = beta G e - M' de          (from the write, and from r = M'^T k, dr = -de)
+ *   dv    = de
+ *   G'    = G - k de^T                (gradient with respect to M')
+ *   dlog_alpha = sum(G' .* M')        (M' = a M_{t-1}, d a / d log a = a)
+ *   G_{t-1} = a G'
+ * Each sequence's states M_t are recomputed forward and kept, then swept in reverse.
+ * dfinal (NULL: zeros) is the gradient with respect to the final state; the result
+ * dinit is the gradient with respect to the initial state.  Arrays as for
+ * oracle_fwd; dlog_alpha is [tokens][H] (or NULL without a gate).
+ */
+int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, int dv, int gate,
+               const double *q, const double *k, const double *v, const double *beta,
+               const double *log_alpha, const double *initial_state, const double *dout,
+               const double *dfinal, double *dq, double *dk_out, double *dv_out, double *dbeta,
+               double *dlog_alpha, double *dinit, int nthreads) {
+  int64_t pair;
+  int failed = 0;
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || beta == NULL) return -1;
+  if (gate != ORACLE_GATE_NONE && gate != ORACLE_GATE_HEAD) return -1;
+  if (gate == ORACLE_GATE_HEAD && (log_alpha == NULL || dlog_alpha == NULL)) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#endif
+  for (pair = 0; pair < (int64_t)N * H; ++pair) {
+    int n = (int)(pair / H), h = (int)(pair % H);
+    const int64_t L = len[n], S = (int64_t)dk * dv;
+    double *Ms = (double *)malloc(sizeof(double) * (size_t)S * (size_t)(L + 1)); /* M_0 .. M_L */
+    double *G = (double *)malloc(sizeof(double) * (size_t)S);
+    double *Mp = (double *)malloc(sizeof(double) * (size_t)S);
+    double *r = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *e = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *de = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *otmp = (double *)malloc(sizeof(double) * (size_t)dv);
+    int64_t t;
+    int i, j;
+    if (!Ms || !G || !Mp || !r || !e || !de || !otmp) {
+      free(Ms); free(G); free(Mp); free(r); free(e); free(de); free(otmp);
+      failed = 1;
+      continue;
+    }
+    if (initial_state)
+      memcpy(Ms, initial_state + ((size_t)n * H + h) * S, sizeof(double) * S);
+    else
+      memset(Ms, 0, sizeof(double) * S);
+    /* forward: keep every state */
+    for (t = 0; t < L; ++t) {
+      size_t th = (size_t)(start[n] + t) * H + h;
+      memcpy(Ms + (t + 1) * S, Ms + t * S, sizeof(double) * S);
+      oracle_token(dk, dv, gate, ORACLE_WRITE_DELTA, q + th * dk, k + th * dk, v + th * dv, beta[th],
+                   gate == ORACLE_GATE_HEAD ? log_alpha + th : NULL, Ms + (t + 1) * S, r, otmp);
+    }
+    /* reverse sweep */
+    if (dfinal)
+      memcpy(G, dfinal + ((size_t)n * H + h) * S, sizeof(double) * S);
+    else
+      memset(G, 0, sizeof(double) * S);
+    for (t = L - 1; t >= 0; --t) {
+      size_t th = (size_t)(start[n] + t) * H + h;
+      const double *qt = q + th * dk, *kt = k + th * dk, *vt = v + th * dv, *dot = dout + th * dv;
+      const double *Mt = Ms + (t + 1) * S, *Mprev = Ms + t * S;
+      const double a = gate == ORACLE_GATE_HEAD ? exp(log_alpha[th]) : 1.0;
+      const double bt = beta[th];
+      double db = 0.0, dla = 0.0;
+      for (i = 0; i < S; ++i) Mp[i] = a * Mprev[i];
+      for (j = 0; j < dv; ++j) r[j] = 0.0;
+      for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j) r[j] += Mp[i * dv + j] * kt[i];
+      for (j = 0; j < dv; ++j) e[j] = vt[j] - r[j];
+      /* read */
+      for (i = 0; i < dk; ++i) {
+        double acc = 0.0;
+        for (j = 0; j < dv; ++j) {
+          G[i * dv + j] += qt[i] * dot[j];
+          acc += Mt[i * dv + j] * dot[j];
+        }
+        dq[th * dk + i] = acc;
+      }
+      /* write: de = beta G^T k, dbeta = k^T G e */
+      for (j = 0; j < dv; ++j) de[j] = 0.0;
+      for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j) {
+          de[j] += G[i * dv + j] * kt[i];
+          db += kt[i] * G[i * dv + j] * e[j];
+        }
+      for (j = 0; j < dv; ++j) de[j] *= bt;
+      for (i = 0; i < dk; ++i) {
+        double acc = 0.0, acc2 = 0.0;
+        for (j = 0; j < dv; ++j) {
+          acc += G[i * dv + j] * e[j];
+          acc2 += Mp[i * dv + j] * de[j];
+        }
+        dk_out[th * dk + i] = bt * acc - acc2;
+      }
+      for (j = 0; j < dv; ++j) dv_out[th * dv + j] = de[j];
+      dbeta[th] = db;
+      /* gradient with respect to M', then M_{t-1} */
+      for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j) {
+          G[i * dv + j] -= kt[i] * de[j];
+          dla += G[i * dv + j] * Mp[i * dv + j];
+          G[i * dv + j] *= a;
+        }
+      if (gate == ORACLE_GATE_HEAD) dlog_alpha[th] = dla;
+    }
+    if (dinit) memcpy(dinit + ((size_t)n * H + h) * S, G, sizeof(double) * S);
+    free(Ms); free(G); free(Mp); free(r); free(e); free(de); free(otmp);
+  }
+  return failed ? -1 : 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
