@@ -110,3 +110,98 @@ def fwd(q, k, v, beta, log_alpha=None, initial_state=None, chunk: int = 64):
             o[b, :, h], fs[b, h] = fwd_sequence(q[b, :, h], k[b, :, h], v[b, :, h], beta[b, :, h],
                                                 la, m0, chunk)
     return o, fs
+
+
+def chunk_step_bwd(q, k, v, beta, g, M0, dO, dM):
+    """Gradients of one chunk of the scalar-gated (or ungated: g = 0) delta rule.
+
+    q,k [C,dk], v [C,dv], beta [C], g [C] (log decay per position), M0 [dk,dv] the
+    state entering the chunk, dO [C,dv] the gradient of O and dM [dk,dv] the gradient
+    of M_C.  Returns (dq, dk, dv, dbeta, dg [C], dM0).  Reverse mode through the chunk
+    equations of the module docstring, step by step:
+      dDelta = P^T dO + Khat dM                 (O = Qt M0 + P Delta, M_C = gam M0 + Khat^T Delta)
+      Y      = T^T dDelta,  X = diag(beta)(V - Kt M0),  Delta = T X
+      dM0    = Qt^T dO + gam dM - Kt^T diag(beta) Y
+      dV = diag(beta) Y,  dbeta_r += Y_r . (V - Kt M0)_r,  dKt = -diag(beta) Y M0^T
+      dT = dDelta X^T,  dA = -(T^T dT T^T) on the strictly lower part
+      dP = dO Delta^T on the inclusive lower part,  dQt = dO M0^T,  dKhat = Delta dM^T
+    then A = strict(diag(beta)(K K^T * Gamma)) and P = incl(Q K^T * Gamma) give the K,
+    Q, beta and Gamma terms, Kt = e^G K, Qt = e^G Q and Khat = e^{G_C - G} K the
+    rest, and dlog alpha_t is the sum of dG_r over r >= t plus dG_C."""
+    C = q.shape[0]
+    strict = np.tril(np.ones((C, C), dtype=bool), -1)
+    incl = np.tril(np.ones((C, C), dtype=bool), 0)
+    G = np.cumsum(g)
+    gC = G[-1]
+    Gam = np.where(incl, np.exp(np.where(incl, G[:, None] - G[None, :], 0.0)), 0.0)
+    S, R = k @ k.T, q @ k.T
+    A = np.where(strict, beta[:, None] * S * Gam, 0.0)
+    T = forward_substitution_inverse(A)
+    eG, eT, gam = np.exp(G), np.exp(gC - G), np.exp(gC)
+    Kt, Qt, Kh = eG[:, None] * k, eG[:, None] * q, eT[:, None] * k
+    P = np.where(incl, R * Gam, 0.0)
+    VmK = v - Kt @ M0
+    X = beta[:, None] * VmK
+    Delta = T @ X
+    # backward
+    dDelta = P.T @ dO + Kh @ dM
+    Y = T.T @ dDelta
+    dM0 = Qt.T @ dO + gam * dM - Kt.T @ (beta[:, None] * Y)
+    dv = beta[:, None] * Y
+    dbeta = np.sum(Y * VmK, axis=1)
+    dKt = -(beta[:, None] * Y) @ M0.T
+    dT = dDelta @ X.T
+    dA = np.where(strict, -(T.T @ dT @ T.T), 0.0)
+    dP = np.where(incl, dO @ Delta.T, 0.0)
+    dQt = dO @ M0.T
+    dKh = Delta @ dM.T
+    dgam = np.sum(M0 * dM)
+    # A = strict(diag(beta) (K K^T * Gamma))
+    dbeta = dbeta + np.sum(dA * S * Gam, axis=1)
+    Ea = dA * beta[:, None] * Gam
+    dk = Ea @ k + Ea.T @ k
+    dGam = dA * beta[:, None] * S
+    # P = incl(Q K^T * Gamma)
+    Ep = dP * Gam
+    dq = Ep @ k
+    dk = dk + Ep.T @ q
+    dGam = dGam + dP * R
+    # Gamma[r, i] = exp(G_r - G_i)
+    wG = dGam * Gam
+    dG = wG.sum(axis=1) - wG.sum(axis=0)
+    # Kt, Qt, Khat and gam
+    dk = dk + eG[:, None] * dKt + eT[:, None] * dKh
+    dq = dq + eG[:, None] * dQt
+    dG = dG + np.sum(dKt * Kt, axis=1) + np.sum(dQt * Qt, axis=1) - np.sum(dKh * Kh, axis=1)
+    dgC = np.sum(dKh * Kh) + gam * dgam
+    dG[-1] += dgC
+    dg = np.cumsum(dG[::-1])[::-1]
+    return dq, dk, dv, dbeta, dg, dM0
+
+
+def chunked_bwd(q, k, v, beta, log_alpha, M0, dO, dMT, C=64):
+    """Gradients over one sequence by chunks: q,k [T,dk], v [T,dv], beta [T],
+    log_alpha None | [T], M0 [dk,dv], dO [T,dv], dMT None | [dk,dv].  The chunk
+    states are recomputed forward, then the chunks are walked in reverse.  A partial
+    last chunk is padded with zero rows (beta = 0, log alpha = 0)."""
+    Tn, dk_ = q.shape
+    dv_ = v.shape[1]
+    la = np.zeros(Tn) if log_alpha is None else log_alpha
+    nch = (Tn + C - 1) // C
+    pad = nch * C - Tn
+    padf = lambda x: np.concatenate([x, np.zeros((pad,) + x.shape[1:])]) if pad else x
+    qp, kp, vp, bp, lp, dOp = (padf(x) for x in (q, k, v, beta, la, dO))
+    states = [M0]
+    for c in range(nch):
+        sl = slice(c * C, (c + 1) * C)
+        G = np.cumsum(lp[sl])
+        res = chunk_step(qp[sl], kp[sl], vp[sl], bp[sl], np.repeat(G[:, None], dk_, axis=1), states[-1])
+        states.append(res["M"])
+    dM = np.zeros((dk_, dv_)) if dMT is None else dMT
+    out = [np.zeros_like(x) for x in (qp, kp, vp, bp, lp)]
+    for c in reversed(range(nch)):
+        sl = slice(c * C, (c + 1) * C)
+        dq, dk, dv, db, dg, dM = chunk_step_bwd(qp[sl], kp[sl], vp[sl], bp[sl], lp[sl], states[c], dOp[sl], dM)
+        for o_, x in zip(out, (dq, dk, dv, db, dg)):
+            o_[sl] = x
+    return tuple(x[:Tn] for x in out) + (dM,)
