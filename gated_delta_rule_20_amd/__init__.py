@@ -7,8 +7,8 @@ current stream.  There is no fallback: if the library is missing this module
 raises on import.
 
 The names follow the C ABI: ``fwd_chunked`` wraps ``gdn_fwd_chunked``,
-``recurrent_step`` wraps ``gdn_fwd_recurrent_step`` and ``decode`` wraps
-``gdn_fwd_decode``.
+``recurrent_step`` wraps ``gdn_fwd_recurrent_step``, ``decode`` wraps
+``gdn_fwd_decode`` and ``bwd_chunked`` wraps ``gdn_bwd_chunked``.
 """
 from __future__ import annotations
 
@@ -61,6 +61,22 @@ class DecodeArgs(ctypes.Structure):
                 ("src_slots", ctypes.c_void_p), ("dst_slots", ctypes.c_void_p), ("o", ctypes.c_void_p)]
 
 
+class BwdArgs(ctypes.Structure):
+    """Mirror of ``gdn_bwd_args``."""
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("d_k", ctypes.c_int), ("d_v", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("N", ctypes.c_int), ("dtype", ctypes.c_int), ("gate", ctypes.c_int),
+                ("write", ctypes.c_int),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
+                ("initial_state", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("dout", ctypes.c_void_p), ("dfinal_state", ctypes.c_void_p),
+                ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("dbeta", ctypes.c_void_p), ("dlog_alpha", ctypes.c_void_p),
+                ("dinitial_state", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError("libgdn.so is not built (%s); run `python __graft_entry__.py build` "
@@ -74,6 +90,10 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_fwd_recurrent_step.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_void_p]
     lib.gdn_fwd_decode.restype = ctypes.c_int
     lib.gdn_fwd_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+    lib.gdn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
+    lib.gdn_bwd_chunked.restype = ctypes.c_int
+    lib.gdn_bwd_chunked.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
     lib.gdn_status_str.restype = ctypes.c_char_p
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_version.restype = ctypes.c_int
@@ -392,6 +412,37 @@ def decode(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out=None,
                       src_slots=_ptr(src_slots), dst_slots=_ptr(dst_slots), o=_ptr(out))
     _check(_lib.gdn_fwd_decode(ctypes.byref(args), _stream(stream)), "gdn_fwd_decode")
     return out
+
+
+def bwd_chunked(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state=None, cu_seqlens=None,
+                output_dinitial: bool = True, workspace=None, stream=None):
+    """Gradients of fwd_chunked (gdn_bwd_chunked) for the delta rule with no gate or
+    one decay per (token, head).  Inputs as for fwd_chunked, plus dout [B,T,H,d_v]
+    (dtype of q) and dfinal_state None | [N,H,d_k,d_v] fp32.
+    Returns (dq, dk, dv, dbeta, dlog_alpha or None, dinitial_state or None)."""
+    import torch
+    N = check_fwd_tensors(q, k, v, beta, log_alpha, initial_state, cu_seqlens, dout, dfinal_state)
+    _require(log_alpha is None or log_alpha.dim() == 3,
+             "the backward supports no gate or log_alpha [B, T, H] (one decay per token and head)")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbeta = torch.empty_like(beta)
+    dla = torch.empty_like(log_alpha) if log_alpha is not None else None
+    dinit = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device) if output_dinitial else None
+    args = BwdArgs(B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=CHUNK, N=N, dtype=_dtype_code(q),
+                   gate=gate_code(log_alpha, 3), write=GDN_WRITE_DELTA, q=_ptr(q), k=_ptr(k), v=_ptr(v),
+                   beta=_ptr(beta), log_alpha=_ptr(log_alpha), initial_state=_ptr(initial_state),
+                   cu_seqlens=_ptr(cu_seqlens), dout=_ptr(dout), dfinal_state=_ptr(dfinal_state),
+                   dq=_ptr(dq), dk=_ptr(dk_), dv=_ptr(dv_), dbeta=_ptr(dbeta), dlog_alpha=_ptr(dla),
+                   dinitial_state=_ptr(dinit), workspace=None, workspace_bytes=0)
+    need = int(_lib.gdn_bwd_workspace_size(ctypes.byref(args)))
+    if need:
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        args.workspace, args.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    _check(_lib.gdn_bwd_chunked(ctypes.byref(args), _stream(stream)), "gdn_bwd_chunked")
+    return dq, dk_, dv_, dbeta, dla, dinit
 
 
 def version() -> int:

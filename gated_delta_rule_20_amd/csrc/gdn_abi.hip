@@ -123,9 +123,132 @@ int check_decode(const gdn_decode_args *a) {
   return GDN_OK;
 }
 
+// The forward arguments of a backward call, for the shared checks.
+gdn_fwd_args fwd_of(const gdn_bwd_args *a) {
+  gdn_fwd_args f{};
+  f.B = a->B; f.T = a->T; f.H = a->H; f.d_k = a->d_k; f.d_v = a->d_v; f.chunk = a->chunk; f.N = a->N;
+  f.dtype = a->dtype; f.gate = a->gate; f.write = a->write;
+  f.q = a->q; f.k = a->k; f.v = a->v; f.beta = a->beta; f.log_alpha = a->log_alpha;
+  f.initial_state = a->initial_state; f.cu_seqlens = a->cu_seqlens;
+  f.o = const_cast<void *>(a->dout);  // checked like o (present, aligned); never written
+  f.final_state = nullptr;
+  return f;
+}
+
+int check_bwd(const gdn_bwd_args *a) {
+  if (!a) return GDN_ERR_INVALID_ARG;
+  const gdn_fwd_args f = fwd_of(a);
+  const int st = check_fwd(&f);
+  if (st != GDN_OK) return st;
+  if (a->write != GDN_WRITE_DELTA || (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD))
+    return GDN_ERR_UNSUPPORTED;
+  const bool tokens = (long)a->B * a->T > 0;
+  if (tokens && (!a->dq || !a->dk || !a->dv || !a->dbeta)) return GDN_ERR_INVALID_ARG;
+  if (tokens && ((a->gate == GDN_GATE_HEAD) != (a->dlog_alpha != nullptr))) return GDN_ERR_INVALID_ARG;
+  const void *p16[] = {a->dq, a->dk, a->dv, a->dfinal_state, a->dinitial_state};
+  for (const void *p : p16)
+    if (p && !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+  if ((a->dbeta && !aligned(a->dbeta, 4)) || (a->dlog_alpha && !aligned(a->dlog_alpha, 4)))
+    return GDN_ERR_INVALID_ARG;
+  return GDN_OK;
+}
+
+struct BwdLayout {
+  long slots;
+  size_t states, tmat, part;
+  size_t total() const { return states + tmat + part; }
+};
+BwdLayout bwd_layout(const gdn_bwd_args *a) {
+  BwdLayout L{0, 0, 0, 0};
+  const long tokens = (long)a->B * a->T;
+  L.slots = gdn::key_slots(tokens, a->N);
+  L.states = align256((size_t)L.slots * a->H * a->d_k * a->d_v * 4);
+  L.tmat = align256((size_t)L.slots * a->H * 64 * 64 * 4);
+  L.part = align256((size_t)L.slots * a->H * (a->d_v / 32) * gdn::bwd_part_floats(a->d_k) * 4);
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t gdn_bwd_workspace_size(const gdn_bwd_args *a) {
+  if (check_bwd(a) != GDN_OK) return 0;
+  return bwd_layout(a).total();
+}
+
+int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
+  const int st = check_bwd(a);
+  if (st != GDN_OK) return st;
+  const BwdLayout L = bwd_layout(a);
+  if (!a->workspace || a->workspace_bytes < L.total() || !aligned(a->workspace, 256)) return GDN_ERR_WORKSPACE;
+  if (a->N == 0 || (long)a->B * a->T == 0) {
+    // no tokens: the initial-state gradient is the final-state gradient (or zero)
+    if (a->dinitial_state && a->N > 0) {
+      const size_t bytes = (size_t)a->N * a->H * a->d_k * a->d_v * 4;
+      hipError_t e = a->dfinal_state
+                         ? hipMemcpyAsync(a->dinitial_state, a->dfinal_state, bytes, hipMemcpyDeviceToDevice,
+                                          (hipStream_t)hip_stream)
+                         : hipMemsetAsync(a->dinitial_state, 0, bytes, (hipStream_t)hip_stream);
+      if (e != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+  }
+  hipStream_t stream = (hipStream_t)hip_stream;
+  char *ws = (char *)a->workspace;
+  // 1. forward recomputation: every chunk's entering state
+  gdn::FwdParams fp;
+  fp.q = a->q;
+  fp.k = a->k;
+  fp.v = a->v;
+  fp.beta = a->beta;
+  fp.log_alpha = a->log_alpha;
+  fp.init_state = a->initial_state;
+  fp.final_state = nullptr;
+  fp.o = nullptr;
+  fp.cu_seqlens = a->cu_seqlens;
+  fp.order = nullptr;
+  fp.k_hat = nullptr;
+  fp.tp_img = nullptr;
+  fp.egc = nullptr;
+  fp.N = a->N;
+  fp.H = a->H;
+  fp.T = a->T;
+  fp.dv = a->d_v;
+  fp.la_stride = a->H;
+  fp.chunk_states = (float *)ws;
+  const int dvb = choose_dvb(a->N, a->H, a->d_v);
+  fp.nb = a->d_v / dvb;
+  if (gdn::launch_fwd_fused(fp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, (int)a->gate, false, stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  // 2. reverse state pass and 3. per-chunk gradients
+  gdn::BwdParams bp;
+  bp.q = a->q;
+  bp.k = a->k;
+  bp.v = a->v;
+  bp.dout = a->dout;
+  bp.beta = a->beta;
+  bp.log_alpha = a->log_alpha;
+  bp.dfinal = a->dfinal_state;
+  bp.cu_seqlens = a->cu_seqlens;
+  bp.states = (const float *)ws;
+  bp.tmat = (float *)(ws + L.states);
+  bp.part = (float *)(ws + L.states + L.tmat);
+  bp.dq = a->dq;
+  bp.dk = a->dk;
+  bp.dv_out = a->dv;
+  bp.dbeta = a->dbeta;
+  bp.dlog_alpha = a->dlog_alpha;
+  bp.dinit = a->dinitial_state;
+  bp.N = a->N;
+  bp.H = a->H;
+  bp.T = a->T;
+  bp.dv = a->d_v;
+  bp.slots = L.slots;
+  if (gdn::launch_bwd(bp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, (int)a->gate, stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}
 
 size_t gdn_fwd_workspace_size(const gdn_fwd_args *a) {
   if (check_fwd(a) != GDN_OK) return 0;
@@ -161,6 +284,7 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
   p.T = a->T;
   p.dv = a->d_v;
   p.la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
+  p.chunk_states = nullptr;
   if (obytes) {
     if (gdn::launch_seq_order(a->cu_seqlens, a->N, (int32_t *)a->workspace, stream) != hipSuccess)
       return GDN_ERR_HIP;

@@ -280,9 +280,19 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   }
   __syncthreads();
 
+  // chunk-entering states for the backward pass: chunk c of this sequence is slot
+  // floor(tok0 / 64) + c + n of p.chunk_states ([slots, H, d_k, d_v])
+  float *cst = p.chunk_states ? p.chunk_states + ((size_t)((tok0 >> 6) + n) * H + h) * DK * dv : nullptr;
   for (int c = 0; c < nchunks; ++c) {
     const int nv = min(C, len - c * C);
     if (c + 1 < nchunks) gload(c + 1);  // in flight during this chunk's compute
+    if (cst && sw) {
+      float *dst = cst + (size_t)c * H * DK * dv + (sbase - ((size_t)n * H + h) * DK * dv);
+#pragma unroll
+      for (int t = 0; t < CF::MT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[(size_t)(16 * t + 4 * lg + j) * dv] = M[t][j];
+    }
 
     // (1) gate prefix: g = inclusive cumsum of log alpha over the chunk
     if (GATE == GATE_HEAD && wave == 0) {
@@ -521,7 +531,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
     // (6) O tile -> HBM (coalesced rows), next chunk's tiles -> LDS
     for (int idx = tid; idx < C * CF::CHV; idx += NT) {
       const int row = idx / CF::CHV, cq = idx % CF::CHV;
-      if (row < nv)
+      if (row < nv && p.o)
         *(uint4 *)(ob + (size_t)(c * C + row) * sv + cq * VEC) = *(const uint4 *)(Os + row * SO + cq * VEC);
     }
     if (c + 1 < nchunks) lstore(min(C, len - (c + 1) * C));

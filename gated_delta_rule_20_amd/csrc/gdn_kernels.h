@@ -32,6 +32,10 @@ struct FwdParams {
   // for one value per (token, head), 0 for one constant value per head.  Read by
   // the fused kernel only (the pipelined kernel takes per-token values).
   int la_stride;
+  // Backward pass only (fused kernel): when set, every chunk's entering state is
+  // stored here ([slots, H, d_k, d_v], slot of chunk c as for key_slots) and o may be
+  // NULL (not written).
+  float *chunk_states;
 };
 
 // Chunk slots of the per-key-channel preparation: chunk c of sequence n (first token
@@ -58,6 +62,26 @@ struct DecodeParams {
   int N, L, H, P;
   int la_stride;  // scalar gate: elements of log_alpha between tokens (H, or 0: per head)
 };
+
+// Backward pass of the chunked delta rule (no gate or the scalar gate).  The chunk
+// states come from the fused forward with FwdParams::chunk_states; the slots of the
+// chunks are numbered as for key_slots.
+struct BwdParams {
+  const void *q, *k, *v, *dout;  // [tokens, H, d_k] / [tokens, H, d_v], I/O dtype
+  const float *beta, *log_alpha; // [tokens, H]; log_alpha NULL without a gate
+  const float *dfinal;           // NULL | [N, H, d_k, d_v]
+  const int32_t *cu_seqlens;     // NULL (batch) | [N + 1]
+  const float *states;           // [slots, H, d_k, d_v] chunk-entering states
+  float *tmat;                   // [slots, H, 64, 64] T of every chunk (written, then read)
+  float *part;                   // [slots, H, d_v / 32, bwd_part_floats(d_k)] partial sums
+  void *dq, *dk, *dv_out;        // outputs, I/O dtype
+  float *dbeta, *dlog_alpha;     // [tokens, H]; dlog_alpha NULL without a gate
+  float *dinit;                  // NULL | [N, H, d_k, d_v]
+  int N, H, T, dv;
+  long slots;
+};
+size_t bwd_part_floats(int dk);
+hipError_t launch_bwd(const BwdParams &p, int dtype, int dk, int gate, hipStream_t stream);
 
 // dtype: 0 fp32, 1 bf16.  Each launcher returns hipSuccess or the launch error.
 // dvb: columns of d_v per workgroup (32 or 64).

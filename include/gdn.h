@@ -191,6 +191,49 @@ int gdn_fwd_recurrent_step(const gdn_step_args *args, void *hip_stream);
  * requested pool slots; allocates nothing. */
 int gdn_fwd_decode(const gdn_decode_args *args, void *hip_stream);
 
+/*
+ * Gradients of the chunked forward (training): reverse mode through the chunk
+ * equations of "Decoding Hybrid Linear Attention Architectures", sec. 5, written out
+ * in this library's kernels (the pages give the forward only).  Supported: the delta
+ * write with no gate or one decay per (token, head) (GDN_GATE_NONE, GDN_GATE_HEAD);
+ * other modes return GDN_ERR_UNSUPPORTED.  Inputs as for gdn_fwd_chunked (the same
+ * validation rules, which this call repeats), plus the gradients of its outputs;
+ * the forward is recomputed inside the call (chunk-entering states into the
+ * workspace), so nothing of the forward call needs to be kept.  All arithmetic is
+ * fp32; dq, dk, dv are rounded once to dtype.  Deterministic (no atomics).
+ */
+typedef struct {
+  int B, T, H, d_k, d_v, chunk, N; /* as in gdn_fwd_args                          */
+  gdn_dtype dtype;
+  gdn_gate gate;
+  gdn_write write;
+  const void *q, *k, *v;           /* as in gdn_fwd_args                          */
+  const float *beta;               /* [B, T, H]                                   */
+  const float *log_alpha;          /* NONE: NULL; HEAD: [B, T, H]                 */
+  const float *initial_state;      /* NULL (zeros) or [N, H, d_k, d_v]            */
+  const int32_t *cu_seqlens;       /* NULL or [N + 1] int32 (device)              */
+  const void *dout;                /* [B, T, H, d_v], dtype: gradient of o        */
+  const float *dfinal_state;       /* NULL (zeros) or [N, H, d_k, d_v]: gradient of
+                                      the final state                             */
+  void *dq, *dk, *dv;              /* out: [B, T, H, d_k] / [B, T, H, d_v], dtype */
+  float *dbeta;                    /* out: [B, T, H]                              */
+  float *dlog_alpha;               /* out: HEAD: [B, T, H]; NONE: NULL            */
+  float *dinitial_state;           /* out: NULL or [N, H, d_k, d_v]               */
+  void *workspace;                 /* gdn_bwd_workspace_size() bytes, 256-aligned */
+  size_t workspace_bytes;
+} gdn_bwd_args;
+
+/* Bytes of device workspace gdn_bwd_chunked needs (0 for arguments it would reject):
+ * with S = floor(B T / 64) + N chunk slots, the chunk-entering states (4 d_k d_v
+ * bytes per slot and head), T of every chunk (16 KiB per slot and head) and the
+ * partial sums over value columns (d_v / 32 records of 4 (8192 + 128 d_k + 192) bytes
+ * per slot and head), each rounded up to 256 bytes.  Owned by the caller; no
+ * initialisation needed. */
+size_t gdn_bwd_workspace_size(const gdn_bwd_args *args);
+
+/* Gradients: writes dq, dk, dv, dbeta, dlog_alpha (HEAD) and dinitial_state (if given). */
+int gdn_bwd_chunked(const gdn_bwd_args *args, void *hip_stream);
+
 /* Static description of a status code (never NULL). */
 const char *gdn_status_str(int status);
 

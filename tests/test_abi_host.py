@@ -49,8 +49,9 @@ def fwd(g, a):
 
 
 def test_header_declares_the_boundary(g):
-    assert g.header_functions() == ["gdn_fwd_chunked", "gdn_fwd_decode", "gdn_fwd_recurrent_step",
-                                    "gdn_fwd_workspace_size", "gdn_status_str", "gdn_version"]
+    assert g.header_functions() == ["gdn_bwd_chunked", "gdn_bwd_workspace_size", "gdn_fwd_chunked",
+                                    "gdn_fwd_decode", "gdn_fwd_recurrent_step", "gdn_fwd_workspace_size",
+                                    "gdn_status_str", "gdn_version"]
 
 
 def test_library_exports_every_header_function(g):
@@ -283,3 +284,41 @@ def test_binding_write_rule_and_constant_gate(g):
     assert g.gate_code(torch.zeros(3), 3) == g.GDN_GATE_HEAD_CONST
     assert g.gate_code(torch.zeros(2, 5, 3), 3) == g.GDN_GATE_HEAD
     assert g.gate_code(torch.zeros(2, 5, 3, 64), 3) == g.GDN_GATE_KEY
+
+
+def bwd_args(g, **kw):
+    a = g.BwdArgs(B=2, T=128, H=4, d_k=128, d_v=128, chunk=64, N=2, dtype=g.GDN_BF16, gate=g.GDN_GATE_HEAD)
+    a.q, a.k, a.v, a.beta, a.log_alpha, a.dout = (fake(i) for i in range(6))
+    a.dq, a.dk, a.dv, a.dbeta, a.dlog_alpha = (fake(i) for i in range(6, 11))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(gate=2, log_alpha=fake(4, 0), dlog_alpha=fake(10)), UNSUPPORTED),  # per-key gate
+    (dict(gate=3, dlog_alpha=fake(10)), UNSUPPORTED),                         # constant gate
+    (dict(write=1, beta=None), UNSUPPORTED),                                  # additive write
+    (dict(dout=None), INVALID),
+    (dict(dq=None), INVALID),
+    (dict(dbeta=None), INVALID),
+    (dict(dlog_alpha=None), INVALID),       # the scalar gate needs its gradient buffer
+    (dict(gate=0, log_alpha=None, dlog_alpha=None), WORKSPACE),  # valid, but no workspace given
+    (dict(gate=0, log_alpha=None), INVALID),   # no gate: no log-decay gradient either
+    (dict(dq=fake(6, 2)), INVALID),
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(d_k=96), UNSUPPORTED),
+    (dict(), WORKSPACE),
+])
+def test_bwd_host_validation(g, change, status):
+    assert g._lib.gdn_bwd_chunked(ctypes.byref(bwd_args(g, **change)), None) == status
+
+
+def test_bwd_workspace_size(g):
+    a = bwd_args(g)
+    slots = (2 * 128) // 64 + 2
+    part = 8192 + 128 * 128 + 192
+    expect = sum((x + 255) // 256 * 256 for x in (slots * 4 * 128 * 128 * 4, slots * 4 * 4096 * 4,
+                                                   slots * 4 * 4 * part * 4))
+    assert g._lib.gdn_bwd_workspace_size(ctypes.byref(a)) == expect
+    assert g._lib.gdn_bwd_workspace_size(ctypes.byref(bwd_args(g, dq=None))) == 0
