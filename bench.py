@@ -206,6 +206,53 @@ def time_pool_decode(gdn, N, L, H, dk, dv, store, steps=64):
             "hbm_gbs": nbytes / (ms / 1e3) / 1e9, "hbm_frac": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
 
 
+def time_bwd(gdn, name, steps=20):
+    """gdn_bwd_chunked on a workload: the gradients of o and of the final state are
+    seeded N(0,1) and N(0, 0.1^2).  Algorithmic bytes: q, k, v, dout read and dq, dk,
+    dv written in the I/O dtype, beta and log alpha read and their gradients written
+    in fp32, the initial state and the final-state gradient read and the
+    initial-state gradient written in fp32.  Algorithmic flops: the forward
+    recomputation (as for the forward) plus, per token and head, 14 C d_k + 10 C d_v
+    + 14 d_k d_v + 4 C^2 for the backward products (each counted once)."""
+    import torch
+    import synth
+    spec = synth.WORKLOADS[name]
+    inp = synth.workload_inputs(name)
+    B, T, H, dk = inp["q"].shape
+    dv = inp["v"].shape[-1]
+    g = torch.Generator().manual_seed(spec["seed"] + 77)
+    dout = torch.randn(B, T, H, dv, generator=g).to(inp["q"].dtype).cuda()
+    dfs = (torch.randn(inp["N"], H, dk, dv, generator=g) * 0.1).cuda()
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    call = gdn.PreparedBwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"], dout, dfs,
+                           d["cu_seqlens"])
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    call.launch()
+    torch.cuda.synchronize()
+    warm = max(2, int(SETTLE_MS / 1e3 / (time.perf_counter() - t)) + 1)
+    for _ in range(warm):
+        call.launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call.launch()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tokens = B * T
+    esize = 2 if spec["dtype"] == "bf16" else 4
+    th = tokens * H
+    nbytes = th * (esize * (4 * dk + 3 * dv) + 16) + 3 * 4 * dk * dv * inp["N"] * H
+    fwd_flops, _ = alg_counts(tokens, H, dk, dv, inp["N"], spec["gate"], esize, True)
+    flops = fwd_flops + th * (14 * CHUNK * dk + 10 * CHUNK * dv + 14 * dk * dv + 4 * CHUNK * CHUNK)
+    return {"workload": name + " backward", "ms_per_step": ms, "tokens_per_s": tokens / (ms / 1e3),
+            "alg_bytes": nbytes, "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
+            "hbm_frac": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, "alg_flops": flops,
+            "tflops": flops / (ms / 1e3) / 1e12}
+
+
 def cpu_baseline(inp, H):
     """The fp64 oracle on the host cores, on the whole workload (bounded: a few
     seconds), best of two runs."""
@@ -328,6 +375,8 @@ def main():
             del wsets
             torch.cuda.empty_cache()
             extra.append(r)
+        extra.append(time_bwd(gdn, HEADLINE))
+        torch.cuda.empty_cache()
         for e in extra:
             print(json.dumps(e), file=sys.stderr)
     print(json.dumps(line))

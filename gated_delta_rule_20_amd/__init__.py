@@ -100,6 +100,11 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
+# torch ships its own HIP runtime (soname libamdhip64.so.7).  Loading torch first makes
+# libgdn.so bind to that same runtime; loaded the other way round, the process ends up
+# with two runtimes and the second one finds no device.
+import torch  # noqa: E402,F401
+
 _lib = load_library()
 
 
@@ -414,12 +419,23 @@ def decode(q, k, v, beta, log_alpha, state_pool, src_slots, dst_slots, out=None,
     return out
 
 
-def bwd_chunked(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state=None, cu_seqlens=None,
-                output_dinitial: bool = True, workspace=None, stream=None):
-    """Gradients of fwd_chunked (gdn_bwd_chunked) for the delta rule with no gate or
-    one decay per (token, head).  Inputs as for fwd_chunked, plus dout [B,T,H,d_v]
-    (dtype of q) and dfinal_state None | [N,H,d_k,d_v] fp32.
-    Returns (dq, dk, dv, dbeta, dlog_alpha or None, dinitial_state or None)."""
+class PreparedBwd:
+    """A validated gdn_bwd_chunked call on fixed buffers (see PreparedFwd); the
+    gradients are overwritten by every launch."""
+
+    def __init__(self, q, k, v, beta, log_alpha, initial_state, dout, dfinal_state=None, cu_seqlens=None,
+                 output_dinitial: bool = True):
+        self.args, self.outs, self._keep = _bwd_args(q, k, v, beta, log_alpha, initial_state, dout,
+                                                     dfinal_state, cu_seqlens, output_dinitial, None)
+        self._ref = ctypes.byref(self.args)
+
+    def launch(self, stream=None):
+        _check(_lib.gdn_bwd_chunked(self._ref, _stream(stream)), "gdn_bwd_chunked")
+        return self.outs
+
+
+def _bwd_args(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state, cu_seqlens, output_dinitial,
+              workspace):
     import torch
     N = check_fwd_tensors(q, k, v, beta, log_alpha, initial_state, cu_seqlens, dout, dfinal_state)
     _require(log_alpha is None or log_alpha.dim() == 3,
@@ -441,8 +457,20 @@ def bwd_chunked(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state=None
         if workspace is None or workspace.numel() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         args.workspace, args.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    keep = (q, k, v, beta, log_alpha, initial_state, dout, dfinal_state, cu_seqlens, workspace)
+    return args, (dq, dk_, dv_, dbeta, dla, dinit), keep
+
+
+def bwd_chunked(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state=None, cu_seqlens=None,
+                output_dinitial: bool = True, workspace=None, stream=None):
+    """Gradients of fwd_chunked (gdn_bwd_chunked) for the delta rule with no gate or
+    one decay per (token, head).  Inputs as for fwd_chunked, plus dout [B,T,H,d_v]
+    (dtype of q) and dfinal_state None | [N,H,d_k,d_v] fp32.
+    Returns (dq, dk, dv, dbeta, dlog_alpha or None, dinitial_state or None)."""
+    args, outs, keep = _bwd_args(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state, cu_seqlens,
+                                 output_dinitial, workspace)
     _check(_lib.gdn_bwd_chunked(ctypes.byref(args), _stream(stream)), "gdn_bwd_chunked")
-    return dq, dk_, dv_, dbeta, dla, dinit
+    return outs
 
 
 def version() -> int:
