@@ -24,7 +24,8 @@
 //  3. bwd_chunk_kernel, one workgroup per (chunk, head), fully parallel: it sums the
 //     partials in a fixed order (deterministic), forms dA and the Gram / Gamma terms
 //     and writes dq, dk, dbeta and d log alpha.
-// All arithmetic is fp32 (inputs in bf16 or fp32), on LDS tiles.
+// All arithmetic is fp32 (inputs in bf16 or fp32): the products on the matrix cores
+// (v_mfma_f32_16x16x4f32) with operands gathered from LDS, the rest on the vector units.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -37,32 +38,35 @@ constexpr int BNT = 256;  // threads per workgroup
 constexpr int BVB = 32;   // value columns per workgroup of the reverse-state kernel
 constexpr int SV = BVB + 1, ST = BC + 1;  // fp32 row strides (padded)
 
-// acc[TM][TN] += sum_k a(r, k) b(k, c) over this thread's TM x TN patch of an M x N
-// product computed by NTH threads (thread t: rows (t / (N/TN)) TM.., columns (t % (N/TN)) TN..)
-template <int M, int N, int K, int TM, int TN, int NTH, class FA, class FB>
-__device__ __forceinline__ void mm(float (&acc)[TM][TN], int t, FA a, FB b) {
-  static_assert(M * N == NTH * TM * TN && N % TN == 0 && M % TM == 0, "product tiling");
-  const int r0 = (t / (N / TN)) * TM, c0 = (t % (N / TN)) * TN;
-#pragma unroll 2
-  for (int k = 0; k < K; ++k) {
-    float av[TM], bv[TN];
+// One 16x16 tile of C = A B on the matrix cores in fp32 (v_mfma_f32_16x16x4f32, eight
+// per 32-deep step; K a multiple of 32).  Operands are gathered through a(m, k) and
+// b(k, n); lane (lg, lm) supplies A row m0 + lm and B column n0 + lm at k = k0 + 8 lg
+// + i, and ends with C[m0 + 4 lg + j][n0 + lm], j = 0..3.
+template <int K, class FA, class FB>
+__device__ __forceinline__ f32x4 tile(int m0, int n0, int lg, int lm, FA a, FB b) {
+  f32x4 acc = zero4();
 #pragma unroll
-    for (int i = 0; i < TM; ++i) av[i] = a(r0 + i, k);
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    f32x8 af, bf;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bv[j] = b(k, c0 + j);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] += av[i] * bv[j];
+    for (int i = 0; i < 8; ++i) {
+      af[i] = a(m0 + lm, k0 + 8 * lg + i);
+      bf[i] = b(k0 + 8 * lg + i, n0 + lm);
+    }
+    acc = mma(af, bf, acc);
   }
+  return acc;
 }
-template <int N, int TM, int TN> __device__ __forceinline__ int tile_r0(int t) { return (t / (N / TN)) * TM; }
-template <int N, int TN> __device__ __forceinline__ int tile_c0(int t) { return (t % (N / TN)) * TN; }
-template <int TM, int TN> __device__ __forceinline__ void zero(float (&a)[TM][TN]) {
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) a[i][j] = 0.f;
+// Every 16x16 tile of an M x N product, spread over NW waves (this one is w of them);
+// epi(r, c, v) receives C[r + j][c] = v[j], j = 0..3.
+template <int M, int N, int K, int NW, class FA, class FB, class EPI>
+__device__ __forceinline__ void mfma_mm(int w, int lane, FA a, FB b, EPI epi) {
+  const int lg = lane >> 4, lm = lane & 15;
+  constexpr int TN = N / 16, TILES = (M / 16) * TN;
+  for (int t = w; t < TILES; t += NW) {
+    const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+    epi(m0 + 4 * lg, n0 + lm, tile<K>(m0, n0, lg, lm, a, b));
+  }
 }
 
 // floats of one partial record (per chunk slot, head and value block)
@@ -88,13 +92,21 @@ __device__ __forceinline__ bool seq_extent(const BwdParams &p, int n, long &tok0
 template <typename E, int DK, int GATE>
 __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
   constexpr int SKE = DK + 8;
-  constexpr int TNK = DK / 16;  // 64 x DK products: 16 threads per row group
+  constexpr int VE = 16 / (int)sizeof(E);        // elements per 16-byte piece
+  constexpr int RK = BC * (DK / VE) / BNT;       // K / Q pieces per thread
+  constexpr int RV = BC * (BVB / VE) / BNT;      // V / dO pieces per thread
+  constexpr int RM = DK * (BVB / 4) / BNT;       // entering-state pieces per thread
+  typedef E EV __attribute__((ext_vector_type(VE)));
   typedef Part<DK> PT;
-  __shared__ E Kl[BC * SKE], Ql[BC * SKE];
+  __shared__ __align__(16) E Kl[BC * SKE];
+  __shared__ __align__(16) E Ql[BC * SKE];
   __shared__ float Vb[BC * SV], dOb[BC * SV], M0[DK * SV], dM[DK * SV];
-  __shared__ float Tl[BC * ST], Pl[BC * ST];
-  __shared__ float Xl[BC * SV], Dl[BC * SV], dDl[BC * SV], Yl[BC * SV];
+  __shared__ float Tl[BC * ST], Pl[BC * ST], Tb[BC * ST];
+  __shared__ float Xl[BC * SV], dDl[BC * SV];
   __shared__ float bs[BC], gs[BC], eg[BC], et[BC], red[BC], wsum[4], misc[4];
+  float *const Yl = Vb;   // V is dead once X is formed
+  float *const Dl = Tl;   // A is dead once T is formed
+  float *const Ys = dDl;  // scratch of the block substitution, before dDelta exists
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = p.H, dv = p.dv, nb = dv / BVB;
@@ -106,38 +118,93 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
   const int nchunks = (len + BC - 1) / BC;
   const long slot0 = (tok0 >> 6) + n;
   const size_t sstate = ((size_t)n * H + h) * DK * dv + col0;
+  auto K_ = [&](int r, int d) { return to_f(Kl[r * SKE + d]); };
+  auto Q_ = [&](int r, int d) { return to_f(Ql[r * SKE + d]); };
 
   for (int i = tid; i < DK * BVB; i += BNT) {
     const int d = i / BVB, j = i % BVB;
     dM[d * SV + j] = p.dfinal ? p.dfinal[sstate + (size_t)d * dv + j] : 0.f;
   }
+  for (int i = tid; i < BC * ST; i += BNT) Tb[i] = 0.f;  // T's upper blocks stay zero
+
+  // ---- a chunk's inputs: 16-byte loads into registers one chunk ahead (rows past the
+  // sequence end re-read its last row and are zeroed when staged)
+  u32x4 pk[RK], pq[RK], pv[RV], pd[RV];
+  f32x4 pm[RM];
+  float pb = 0.f, pl = 0.f;
+  auto fetch = [&](int cc) {
+    const int last = min(BC, len - cc * BC) - 1;
+    const size_t tbc = (size_t)tok0 + (size_t)cc * BC;
+#pragma unroll
+    for (int u = 0; u < RK; ++u) {
+      const int pc = tid + BNT * u, r = min(pc / (DK / VE), last), g = pc % (DK / VE);
+      const size_t o = ((tbc + r) * H + h) * DK + g * VE;
+      pk[u] = *(const u32x4 *)((const E *)p.k + o);
+      pq[u] = *(const u32x4 *)((const E *)p.q + o);
+    }
+#pragma unroll
+    for (int u = 0; u < RV; ++u) {
+      const int pc = tid + BNT * u, r = min(pc / (BVB / VE), last), g = pc % (BVB / VE);
+      const size_t o = ((tbc + r) * H + h) * dv + col0 + g * VE;
+      pv[u] = *(const u32x4 *)((const E *)p.v + o);
+      pd[u] = *(const u32x4 *)((const E *)p.dout + o);
+    }
+#pragma unroll
+    for (int u = 0; u < RM; ++u) {
+      const int pc = tid + BNT * u, d = pc / (BVB / 4), g = pc % (BVB / 4);
+      pm[u] = *(const f32x4 *)(p.states + ((((size_t)slot0 + cc) * H + h) * DK + d) * dv + col0 + 4 * g);
+    }
+    if (tid < BC) {
+      const size_t t = tbc + min(tid, last);
+      pb = p.beta[t * H + h];
+      pl = GATE == GATE_HEAD ? p.log_alpha[t * H + h] : 0.f;
+    }
+  };
+  auto stage = [&](int nvc) {
+#pragma unroll
+    for (int u = 0; u < RK; ++u) {
+      opaque(pk[u]);
+      opaque(pq[u]);
+      const int pc = tid + BNT * u, r = pc / (DK / VE), g = pc % (DK / VE);
+      if (r >= nvc) pk[u] = pq[u] = (u32x4){0u, 0u, 0u, 0u};
+      *(u32x4 *)(Kl + r * SKE + g * VE) = pk[u];
+      *(u32x4 *)(Ql + r * SKE + g * VE) = pq[u];
+    }
+#pragma unroll
+    for (int u = 0; u < RV; ++u) {
+      opaque(pv[u]);
+      opaque(pd[u]);
+      const int pc = tid + BNT * u, r = pc / (BVB / VE), g = pc % (BVB / VE);
+      const EV ev = __builtin_bit_cast(EV, pv[u]), ed = __builtin_bit_cast(EV, pd[u]);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        Vb[r * SV + g * VE + e] = r < nvc ? to_f(ev[e]) : 0.f;
+        dOb[r * SV + g * VE + e] = r < nvc ? to_f(ed[e]) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RM; ++u) {
+      opaque(pm[u]);
+      const int pc = tid + BNT * u, d = pc / (BVB / 4), g = pc % (BVB / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) M0[d * SV + 4 * g + e] = pm[u][e];
+    }
+    if (tid < BC) {
+      opaque(pb);
+      opaque(pl);
+      bs[tid] = tid < nvc ? pb : 0.f;
+      gs[tid] = tid < nvc ? pl : 0.f;
+    }
+  };
+  if (nchunks > 0) fetch(nchunks - 1);
+
   for (int c = nchunks - 1; c >= 0; --c) {
     const int nv = min(BC, len - c * BC);
     const size_t tb = (size_t)tok0 + (size_t)c * BC;  // token of row 0
     const size_t slot = (size_t)(slot0 + c);
     __syncthreads();  // the previous chunk is done with every buffer
-    // ---- inputs of the chunk (rows past the sequence end are zero)
-    for (int i = tid; i < BC * DK; i += BNT) {
-      const int r = i / DK, d = i % DK;
-      const size_t o = ((tb + r) * H + h) * DK + d;
-      Kl[r * SKE + d] = r < nv ? ((const E *)p.k)[o] : to_e<E>(0.f);
-      Ql[r * SKE + d] = r < nv ? ((const E *)p.q)[o] : to_e<E>(0.f);
-    }
-    for (int i = tid; i < BC * BVB; i += BNT) {
-      const int r = i / BVB, j = i % BVB;
-      const size_t o = ((tb + r) * H + h) * dv + col0 + j;
-      Vb[r * SV + j] = r < nv ? to_f(((const E *)p.v)[o]) : 0.f;
-      dOb[r * SV + j] = r < nv ? to_f(((const E *)p.dout)[o]) : 0.f;
-    }
-    for (int i = tid; i < DK * BVB; i += BNT) {
-      const int d = i / BVB, j = i % BVB;
-      M0[d * SV + j] = p.states[((slot * H + h) * DK + d) * dv + col0 + j];
-    }
-    if (tid < BC) {
-      const bool ok = tid < nv;
-      bs[tid] = ok ? p.beta[(tb + tid) * H + h] : 0.f;
-      gs[tid] = (GATE == GATE_HEAD && ok) ? p.log_alpha[(tb + tid) * H + h] : 0.f;
-    }
+    stage(nv);
+    if (c > 0) fetch(c - 1);  // in flight during this chunk's compute
     __syncthreads();
     if (wave == 0) {  // decay prefix
       float g = gs[lane];
@@ -153,94 +220,97 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       if (lane == 0) misc[0] = __expf(gC);
     }
     __syncthreads();
-    // ---- A (strictly lower) into Tl and P (lower inclusive) into Pl
+    // ---- A (strictly lower) into Tl and P (lower inclusive) into Pl; tiles above the
+    // diagonal are zero
+    auto gam_at = [&](int r, int i) {
+      return i <= r ? (GATE == GATE_HEAD ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
+    };
     {
-      float aa[4][4], pp[4][4];
-      zero(aa);
-      zero(pp);
-      mm<BC, BC, DK, 4, 4, BNT>(aa, tid, [&](int r, int d) { return to_f(Kl[r * SKE + d]); },
-                                [&](int d, int i) { return to_f(Kl[i * SKE + d]); });
-      mm<BC, BC, DK, 4, 4, BNT>(pp, tid, [&](int r, int d) { return to_f(Ql[r * SKE + d]); },
-                                [&](int d, int i) { return to_f(Kl[i * SKE + d]); });
-      const int r0 = tile_r0<BC, 4, 4>(tid), c0 = tile_c0<BC, 4>(tid);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = r0 + u, i = c0 + v;
-          const float gam = i <= r ? (GATE == GATE_HEAD ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
-          Tl[r * ST + i] = i < r ? bs[r] * aa[u][v] * gam : 0.f;
-          Pl[r * ST + i] = pp[u][v] * gam;
+      const int lg = lane >> 4, lm = lane & 15;
+      for (int t = wave; t < 16; t += 4) {
+        const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
+        f32x4 av = zero4(), pv4 = zero4();
+        if (n0 <= m0) {
+          av = tile<DK>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
+          pv4 = tile<DK>(m0, n0, lg, lm, Q_, [&](int d, int i) { return K_(i, d); });
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = m0 + 4 * lg + u, i = n0 + lm;
+          Tl[r * ST + i] = i < r ? bs[r] * av[u] * gam_at(r, i) : 0.f;
+          Pl[r * ST + i] = pv4[u] * gam_at(r, i);
+        }
+      }
     }
     __syncthreads();
     if (wave == 0) {
-      // T = (I + A)^-1 in place: lane owns column `lane`; row r of T needs A[r][i < r]
-      // (read by every lane in the same step) and the column's earlier entries
-      float x[BC];
+      // diagonal 16x16 blocks of T = (I + A)^-1: lane (lg, lm) solves column lm of block lg
+      const int lg = lane >> 4, lm = lane & 15, o = 16 * lg;
+      float x[16];
 #pragma unroll
-      for (int r = 0; r < BC; ++r) {
-        float acc = r == lane ? 1.f : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        float acc = r == lm ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) acc -= Tl[r * ST + i] * x[i];
+        for (int i = 0; i < r; ++i) acc -= Tl[(o + r) * ST + o + i] * x[i];
         x[r] = acc;
       }
 #pragma unroll
-      for (int r = 0; r < BC; ++r) Tl[r * ST + lane] = x[r];
-    } else if (wave < 3) {
-      // V - Kt M0 into Xl (64 x 32, two waves)
-      float xx[4][4];
-      zero(xx);
-      const int t = tid - 64;
-      mm<BC, BVB, DK, 4, 4, 128>(xx, t, [&](int r, int d) { return to_f(Kl[r * SKE + d]); },
-                                 [&](int d, int j) { return M0[d * SV + j]; });
-      const int r0 = tile_r0<BVB, 4, 4>(t), c0 = tile_c0<BVB, 4>(t);
+      for (int r = 0; r < 16; ++r) Tb[(o + r) * ST + o + lm] = x[r];
+    } else {
+      // V - Kt M0 into Xl (64 x 32, three waves)
+      mfma_mm<BC, BVB, DK, 3>(wave - 1, lane, K_, [&](int d, int j) { return M0[d * SV + j]; },
+                              [&](int r, int j, f32x4 v) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+                                for (int u = 0; u < 4; ++u) Xl[(r + u) * SV + j] = Vb[(r + u) * SV + j] - eg[r + u] * v[u];
+                              });
+    }
+    __syncthreads();
+    if (wave < 3) {
+      // off-diagonal blocks, block column b = wave, downwards:
+      // T[a][b] = -T[a][a] sum_{k=b}^{a-1} A[a][k] T[k][b]
+      const int lg = lane >> 4, lm = lane & 15, b = wave;
+      float *ys = Ys + wave * (16 * 17);
+      for (int a = b + 1; a < 4; ++a) {
+        const f32x4 y = tile<BC>(16 * a, 16 * b, lg, lm,
+                                 [&](int r, int k) { return (k >= 16 * b && k < 16 * a) ? Tl[r * ST + k] : 0.f; },
+                                 [&](int k, int col) { return Tb[k * ST + col]; });
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = r0 + u, j = c0 + v;
-          Xl[r * SV + j] = Vb[r * SV + j] - eg[r] * xx[u][v];
-        }
+        for (int u = 0; u < 4; ++u) ys[(4 * lg + u) * 17 + lm] = y[u];
+        const f32x4 z = tile<32>(16 * a, 16 * b, lg, lm,
+                                 [&](int r, int k) { return k < 16 ? Tb[r * ST + 16 * a + k] : 0.f; },
+                                 [&](int k, int col) { return k < 16 ? ys[k * 17 + col - 16 * b] : 0.f; });
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Tb[(16 * a + 4 * lg + u) * ST + 16 * b + lm] = -z[u];
+      }
     }
     __syncthreads();
     if (jb == 0)  // T for the per-chunk kernel
-      for (int i = tid; i < BC * BC; i += BNT) p.tmat[(slot * H + h) * BC * BC + i] = Tl[(i / BC) * ST + i % BC];
-    // ---- Delta = T diag(beta) (V - Kt M0);  dDelta = P^T dO + diag(e^{G_C - G}) K dM
+      for (int i = tid; i < BC * BC; i += BNT) p.tmat[(slot * H + h) * BC * BC + i] = Tb[(i / BC) * ST + i % BC];
+    // ---- Delta = T diag(beta) (V - Kt M0);  dDelta = P^T dO + diag(e^{G_C - G}) K dM  (8 tiles each)
     {
-      float dd[2][4], d1[2][4], d2[2][4];
-      zero(dd);
-      zero(d1);
-      zero(d2);
-      mm<BC, BVB, BC, 2, 4, BNT>(dd, tid, [&](int r, int i) { return Tl[r * ST + i]; },
-                                 [&](int i, int j) { return bs[i] * Xl[i * SV + j]; });
-      mm<BC, BVB, BC, 2, 4, BNT>(d1, tid, [&](int r, int i) { return Pl[i * ST + r]; },
-                                 [&](int i, int j) { return dOb[i * SV + j]; });
-      mm<BC, BVB, DK, 2, 4, BNT>(d2, tid, [&](int r, int d) { return to_f(Kl[r * SKE + d]); },
-                                 [&](int d, int j) { return dM[d * SV + j]; });
-      const int r0 = tile_r0<BVB, 2, 4>(tid), c0 = tile_c0<BVB, 4>(tid);
+      const int lg = lane >> 4, lm = lane & 15;
+      for (int t = wave; t < 8; t += 4) {
+        const int m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+        const f32x4 dd = tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Tb[r * ST + i]; },
+                                  [&](int i, int j) { return bs[i] * Xl[i * SV + j]; });
+        const f32x4 d1 = tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Pl[i * ST + r]; },
+                                  [&](int i, int j) { return dOb[i * SV + j]; });
+        const f32x4 d2 = tile<DK>(m0, n0, lg, lm, K_, [&](int d, int j) { return dM[d * SV + j]; });
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = r0 + u, j = c0 + v;
-          Dl[r * SV + j] = dd[u][v];
-          dDl[r * SV + j] = d1[u][v] + et[r] * d2[u][v];
+        for (int u = 0; u < 4; ++u) {
+          const int r = m0 + 4 * lg + u, j = n0 + lm;
+          Dl[r * SV + j] = dd[u];
+          dDl[r * SV + j] = d1[u] + et[r] * d2[u];
         }
+      }
     }
     __syncthreads();
     // ---- Y = T^T dDelta
-    {
-      float yy[2][4];
-      zero(yy);
-      mm<BC, BVB, BC, 2, 4, BNT>(yy, tid, [&](int r, int i) { return Tl[i * ST + r]; },
-                                 [&](int i, int j) { return dDl[i * SV + j]; });
-      const int r0 = tile_r0<BVB, 2, 4>(tid), c0 = tile_c0<BVB, 4>(tid);
+    mfma_mm<BC, BVB, BC, 4>(wave, lane, [&](int r, int i) { return Tb[i * ST + r]; },
+                            [&](int i, int j) { return dDl[i * SV + j]; }, [&](int r, int j, f32x4 v) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Yl[(r0 + u) * SV + c0 + v] = yy[u][v];
-    }
+                              for (int u = 0; u < 4; ++u) Yl[(r + u) * SV + j] = v[u];
+                            });
     __syncthreads();
     // ---- dV (complete for this value block)
     for (int i = tid; i < BC * BVB; i += BNT) {
@@ -249,55 +319,43 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     }
     float *pr = p.part + ((slot * H + h) * nb + jb) * (size_t)PT::SIZE;
     // ---- dP = incl(dO Delta^T), dT = dDelta (diag(beta) X)^T  (partial over value columns)
+    mfma_mm<BC, BC, BVB, 4>(wave, lane, [&](int r, int j) { return dOb[r * SV + j]; },
+                            [&](int j, int i) { return Dl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
+#pragma unroll
+                              for (int u = 0; u < 4; ++u) pr[PT::DP + (r + u) * BC + i] = i <= r + u ? v[u] : 0.f;
+                            });
+    mfma_mm<BC, BC, BVB, 4>(wave, lane, [&](int r, int j) { return dDl[r * SV + j]; },
+                            [&](int j, int i) { return bs[i] * Xl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
+#pragma unroll
+                              for (int u = 0; u < 4; ++u) pr[PT::DT + (r + u) * BC + i] = v[u];
+                            });
+    // ---- dQ = e^G dO M0^T, dK = -e^G beta Y M0^T + e^{G_C - G} Delta dM^T, and the rows of
+    // dG: e^G (dO M0^T).Q - e^G beta (Y M0^T).K - e^{G_C - G} (Delta dM^T).K.  A wave takes
+    // whole 16-row blocks (all DK columns), so its row sums stay in the wave.
     {
-      float ap[4][4], at[4][4];
-      zero(ap);
-      zero(at);
-      mm<BC, BC, BVB, 4, 4, BNT>(ap, tid, [&](int r, int j) { return dOb[r * SV + j]; },
-                                 [&](int j, int i) { return Dl[i * SV + j]; });
-      mm<BC, BC, BVB, 4, 4, BNT>(at, tid, [&](int r, int j) { return dDl[r * SV + j]; },
-                                 [&](int j, int i) { return bs[i] * Xl[i * SV + j]; });
-      const int r0 = tile_r0<BC, 4, 4>(tid), c0 = tile_c0<BC, 4>(tid);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = r0 + u, i = c0 + v;
-          pr[PT::DP + r * BC + i] = i <= r ? ap[u][v] : 0.f;
-          pr[PT::DT + r * BC + i] = at[u][v];
-        }
-    }
-    // ---- dQ = e^G dO M0^T, dK = -e^G beta Y M0^T + e^{G_C - G} Delta dM^T, and the row
-    // sums of dG: e^G (dO M0^T).Q - e^G beta (Y M0^T).K - e^{G_C - G} (Delta dM^T).K
-    {
-      float w[4][TNK], uu[4][TNK], z[4][TNK];
-      zero(w);
-      zero(uu);
-      zero(z);
-      mm<BC, DK, BVB, 4, TNK, BNT>(w, tid, [&](int r, int j) { return dOb[r * SV + j]; },
+      const int lg = lane >> 4, lm = lane & 15;
+      const int m0 = 16 * wave;
+      float gq[4] = {0.f, 0.f, 0.f, 0.f}, gk[4] = {0.f, 0.f, 0.f, 0.f}, gz[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int n0 = 0; n0 < DK; n0 += 16) {
+        const f32x4 w = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return dOb[r * SV + j]; },
+                                  [&](int j, int d) { return M0[d * SV + j]; });
+        const f32x4 uu = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Yl[r * SV + j]; },
                                    [&](int j, int d) { return M0[d * SV + j]; });
-      mm<BC, DK, BVB, 4, TNK, BNT>(uu, tid, [&](int r, int j) { return Yl[r * SV + j]; },
-                                   [&](int j, int d) { return M0[d * SV + j]; });
-      mm<BC, DK, BVB, 4, TNK, BNT>(z, tid, [&](int r, int j) { return Dl[r * SV + j]; },
-                                   [&](int j, int d) { return dM[d * SV + j]; });
-      const int r0 = tile_r0<DK, 4, TNK>(tid), c0 = tile_c0<DK, TNK>(tid);
-      float gq[4], gk[4], gz[4];
+        const f32x4 z = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Dl[r * SV + j]; },
+                                  [&](int j, int d) { return dM[d * SV + j]; });
+        const int d = n0 + lm;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = r0 + u;
-        gq[u] = gk[u] = gz[u] = 0.f;
-#pragma unroll
-        for (int v = 0; v < TNK; ++v) {
-          const int d = c0 + v;
-          const float qv = to_f(Ql[r * SKE + d]), kv = to_f(Kl[r * SKE + d]);
-          pr[PT::DQ + r * DK + d] = eg[r] * w[u][v];
-          pr[PT::DKO + r * DK + d] = -eg[r] * bs[r] * uu[u][v] + et[r] * z[u][v];
-          gq[u] += w[u][v] * qv;
-          gk[u] += uu[u][v] * kv;
-          gz[u] += z[u][v] * kv;
+        for (int u = 0; u < 4; ++u) {
+          const int r = m0 + 4 * lg + u;
+          const float qv = Q_(r, d), kv = K_(r, d);
+          pr[PT::DQ + r * DK + d] = eg[r] * w[u];
+          pr[PT::DKO + r * DK + d] = -eg[r] * bs[r] * uu[u] + et[r] * z[u];
+          gq[u] += w[u] * qv;
+          gk[u] += uu[u] * kv;
+          gz[u] += z[u] * kv;
         }
       }
-      // a row group's 16 threads are 16 consecutive lanes
+      // a row's columns are spread over the 16 lanes lm of its lane group
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1)
 #pragma unroll
@@ -306,10 +364,10 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
           gk[u] += __shfl_xor(gk[u], off);
           gz[u] += __shfl_xor(gz[u], off);
         }
-      if ((lane & 15) == 0)
+      if (lm == 0)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int r = r0 + u;
+          const int r = m0 + 4 * lg + u;
           pr[PT::DG + r] = eg[r] * gq[u] - eg[r] * bs[r] * gk[u] - et[r] * gz[u];
           red[r] = et[r] * gz[u];  // this row's term of dG_C
         }
@@ -321,39 +379,40 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     for (int off = 32; off >= 1; off >>= 1) part_m += __shfl_xor(part_m, off);
     if (lane == 0) wsum[wave] = part_m;
     if (tid < BC) {
-      float s = 0.f;
-      for (int j = 0; j < BVB; ++j) s += Yl[tid * SV + j] * Xl[tid * SV + j];
-      pr[PT::DB + tid] = s;
+      float sb = 0.f;
+      for (int j = 0; j < BVB; ++j) sb += Yl[tid * SV + j] * Xl[tid * SV + j];
+      pr[PT::DB + tid] = sb;
     }
     __syncthreads();
     if (wave == 0) {
-      float s = red[lane];
+      float sg = red[lane];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-      if (lane == 0) pr[PT::GC] = s + misc[0] * (wsum[0] + wsum[1] + wsum[2] + wsum[3]);
+      for (int off = 32; off >= 1; off >>= 1) sg += __shfl_xor(sg, off);
+      if (lane == 0) pr[PT::GC] = sg + misc[0] * (wsum[0] + wsum[1] + wsum[2] + wsum[3]);
     }
-    // ---- dM <- gam dM + Qt^T dO - Kt^T diag(beta) Y   (DK x 32)
+    // ---- dM <- gam dM + Qt^T dO - Kt^T diag(beta) Y   (DK x 32: DK / 8 tiles)
     {
-      constexpr int TMD = DK / 32;
-      float n1[TMD][4], n2[TMD][4];
-      zero(n1);
-      zero(n2);
-      mm<DK, BVB, BC, TMD, 4, BNT>(n1, tid, [&](int d, int r) { return eg[r] * to_f(Ql[r * SKE + d]); },
-                                   [&](int r, int j) { return dOb[r * SV + j]; });
-      mm<DK, BVB, BC, TMD, 4, BNT>(n2, tid, [&](int d, int r) { return eg[r] * bs[r] * to_f(Kl[r * SKE + d]); },
-                                   [&](int r, int j) { return Yl[r * SV + j]; });
-      const int r0 = tile_r0<BVB, TMD, 4>(tid), c0 = tile_c0<BVB, 4>(tid);
+      const int lg = lane >> 4, lm = lane & 15;
+      constexpr int TILES = (DK / 16) * 2;
+      f32x4 nm[TILES / 4];
       const float gam = misc[0];
-      float nm[TMD][4];
 #pragma unroll
-      for (int u = 0; u < TMD; ++u)
+      for (int q = 0; q < TILES / 4; ++q) {
+        const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+        const f32x4 n1 = tile<BC>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * Q_(r, d); },
+                                  [&](int r, int j) { return dOb[r * SV + j]; });
+        const f32x4 n2 = tile<BC>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * bs[r] * K_(r, d); },
+                                  [&](int r, int j) { return Yl[r * SV + j]; });
 #pragma unroll
-        for (int v = 0; v < 4; ++v) nm[u][v] = gam * dM[(r0 + u) * SV + c0 + v] + n1[u][v] - n2[u][v];
+        for (int u = 0; u < 4; ++u) nm[q][u] = gam * dM[(m0 + 4 * lg + u) * SV + n0 + lm] + n1[u] - n2[u];
+      }
       __syncthreads();  // every read of the old dM is done
 #pragma unroll
-      for (int u = 0; u < TMD; ++u)
+      for (int q = 0; q < TILES / 4; ++q) {
+        const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) dM[(r0 + u) * SV + c0 + v] = nm[u][v];
+        for (int u = 0; u < 4; ++u) dM[(m0 + 4 * lg + u) * SV + n0 + lm] = nm[q][u];
+      }
     }
   }
   __syncthreads();
@@ -367,12 +426,12 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
 template <typename E, int DK, int GATE>
 __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   constexpr int SKE = DK + 8;
-  constexpr int TNK = DK / 16;
   typedef Part<DK> PT;
   __shared__ E Kl[BC * SKE], Ql[BC * SKE];
   __shared__ float Tl[BC * ST], Pl[BC * ST], Dt[BC * ST], Zl[BC * ST], Sl[BC * ST], Rl[BC * ST];
   __shared__ float bs[BC], gs[BC], dGs[BC], dBs[BC], misc[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H, nb = p.dv / BVB;
   const long slot = blockIdx.x / H;
   const int h = blockIdx.x % H;
@@ -391,6 +450,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   if (c < 0 || 64 * c >= len) return;  // no chunk owns this slot
   const int nv = (int)min(64L, (long)len - 64 * c);
   const size_t tb = (size_t)tok0 + (size_t)c * BC;
+  auto K_ = [&](int r, int d) { return to_f(Kl[r * SKE + d]); };
+  auto Q_ = [&](int r, int d) { return to_f(Ql[r * SKE + d]); };
 
   for (int i = tid; i < BC * DK; i += BNT) {
     const int r = i / DK, d = i % DK;
@@ -423,9 +484,9 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     dBs[tid] = sb;
   }
   if (tid == 0) {
-    float s = 0.f;
-    for (int b = 0; b < nb; ++b) s += pr0[(size_t)b * PT::SIZE + PT::GC];
-    misc[0] = s;
+    float sc = 0.f;
+    for (int b = 0; b < nb; ++b) sc += pr0[(size_t)b * PT::SIZE + PT::GC];
+    misc[0] = sc;
   }
   __syncthreads();
   if (wave == 0) {
@@ -439,52 +500,48 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   }
   __syncthreads();
   // S = K K^T, R = Q K^T;  Z = dT T^T
-  {
-    float s_[4][4], r_[4][4], z_[4][4];
-    zero(s_);
-    zero(r_);
-    zero(z_);
-    mm<BC, BC, DK, 4, 4, BNT>(s_, tid, [&](int r, int d) { return to_f(Kl[r * SKE + d]); },
-                              [&](int d, int i) { return to_f(Kl[i * SKE + d]); });
-    mm<BC, BC, DK, 4, 4, BNT>(r_, tid, [&](int r, int d) { return to_f(Ql[r * SKE + d]); },
-                              [&](int d, int i) { return to_f(Kl[i * SKE + d]); });
-    mm<BC, BC, BC, 4, 4, BNT>(z_, tid, [&](int r, int k) { return Dt[r * ST + k]; },
-                              [&](int k, int i) { return Tl[i * ST + k]; });
-    const int r0 = tile_r0<BC, 4, 4>(tid), c0 = tile_c0<BC, 4>(tid);
+  mfma_mm<BC, BC, DK, 4>(wave, lane, K_, [&](int d, int i) { return K_(i, d); }, [&](int r, int i, f32x4 v) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u) Sl[(r + u) * ST + i] = v[u];
+  });
+  mfma_mm<BC, BC, DK, 4>(wave, lane, Q_, [&](int d, int i) { return K_(i, d); }, [&](int r, int i, f32x4 v) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = r0 + u, i = c0 + v;
-        Sl[r * ST + i] = s_[u][v];
-        Rl[r * ST + i] = r_[u][v];
-        Zl[r * ST + i] = z_[u][v];
-      }
-  }
+    for (int u = 0; u < 4; ++u) Rl[(r + u) * ST + i] = v[u];
+  });
+  mfma_mm<BC, BC, BC, 4>(wave, lane, [&](int r, int k) { return Dt[r * ST + k]; },
+                         [&](int k, int i) { return Tl[i * ST + k]; }, [&](int r, int i, f32x4 v) {
+#pragma unroll
+                           for (int u = 0; u < 4; ++u) Zl[(r + u) * ST + i] = v[u];
+                         });
   __syncthreads();
   // dA = -strict(T^T Z), then per entry: Gamma, Ea = dA beta_r Gamma, Ep = dP Gamma,
-  // wG = (dA beta_r S + dP R) Gamma, and dA S Gamma (for dbeta)
+  // wG = (dA beta_r S + dP R) Gamma, and dA S Gamma (for dbeta).  Each wave's 4 tiles
+  // are computed first (Zl is read), then written after a barrier.
   {
-    float a_[4][4];
-    zero(a_);
-    mm<BC, BC, BC, 4, 4, BNT>(a_, tid, [&](int r, int k) { return Tl[k * ST + r]; },
-                              [&](int k, int i) { return Zl[k * ST + i]; });
-    const int r0 = tile_r0<BC, 4, 4>(tid), c0 = tile_c0<BC, 4>(tid);
-    __syncthreads();  // Zl is rewritten below
+    f32x4 da[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int q = 0; q < 4; ++q) {
+      const int t = wave + 4 * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
+      da[q] = tile<BC>(m0, n0, lg, lm, [&](int r, int k) { return Tl[k * ST + r]; },
+                       [&](int k, int i) { return Zl[k * ST + i]; });
+    }
+    __syncthreads();
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = r0 + u, i = c0 + v;
+    for (int q = 0; q < 4; ++q) {
+      const int t = wave + 4 * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = m0 + 4 * lg + u, i = n0 + lm;
         const float gam = i <= r ? (GATE == GATE_HEAD ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
-        const float dA = i < r ? -a_[u][v] : 0.f;
+        const float dA = i < r ? -da[q][u] : 0.f;
         const float dP = Pl[r * ST + i];
         const float S = Sl[r * ST + i], R = Rl[r * ST + i];
-        Zl[r * ST + i] = dA * bs[r] * gam;            // Ea
-        Pl[r * ST + i] = dP * gam;                    // Ep
+        Zl[r * ST + i] = dA * bs[r] * gam;                 // Ea
+        Pl[r * ST + i] = dP * gam;                         // Ep
         Sl[r * ST + i] = (dA * bs[r] * S + dP * R) * gam;  // wG
-        Rl[r * ST + i] = dA * S * gam;                // dbeta terms
+        Rl[r * ST + i] = dA * S * gam;                     // dbeta terms
       }
+    }
   }
   __syncthreads();
   // row / column sums: dG and dbeta; then d log alpha = reverse prefix of dG (+ dG_C)
@@ -513,32 +570,25 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     }
   }
   // dq = Ep K + (partials), dk = (Ea + Ea^T) K + Ep^T Q + (partials)
-  {
-    float q_[4][TNK], k_[4][TNK];
-    zero(q_);
-    zero(k_);
-    mm<BC, DK, BC, 4, TNK, BNT>(q_, tid, [&](int r, int i) { return Pl[r * ST + i]; },
-                                [&](int i, int d) { return to_f(Kl[i * SKE + d]); });
-    mm<BC, DK, BC, 4, TNK, BNT>(k_, tid, [&](int r, int i) { return Zl[r * ST + i] + Zl[i * ST + r]; },
-                                [&](int i, int d) { return to_f(Kl[i * SKE + d]); });
-    mm<BC, DK, BC, 4, TNK, BNT>(k_, tid, [&](int r, int i) { return Pl[i * ST + r]; },
-                                [&](int i, int d) { return to_f(Ql[i * SKE + d]); });
-    const int r0 = tile_r0<DK, 4, TNK>(tid), c0 = tile_c0<DK, TNK>(tid);
+  for (int t = wave; t < (DK / 16) * 4; t += 4) {
+    const int m0 = (t / (DK / 16)) * 16, n0 = (t % (DK / 16)) * 16;
+    const f32x4 q_ = tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Pl[r * ST + i]; },
+                              [&](int i, int d) { return K_(i, d); });
+    f32x4 k_ = tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Zl[r * ST + i] + Zl[i * ST + r]; },
+                        [&](int i, int d) { return K_(i, d); });
+    k_ += tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Pl[i * ST + r]; }, [&](int i, int d) { return Q_(i, d); });
+    const int d = n0 + lm;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int r = r0 + u;
+      const int r = m0 + 4 * lg + u;
       if (r >= nv) continue;
-#pragma unroll
-      for (int v = 0; v < TNK; ++v) {
-        const int d = c0 + v;
-        float sq = q_[u][v], sk = k_[u][v];
-        for (int b = 0; b < nb; ++b) {
-          sq += pr0[(size_t)b * PT::SIZE + PT::DQ + r * DK + d];
-          sk += pr0[(size_t)b * PT::SIZE + PT::DKO + r * DK + d];
-        }
-        ((E *)p.dq)[((tb + r) * H + h) * DK + d] = to_e<E>(sq);
-        ((E *)p.dk)[((tb + r) * H + h) * DK + d] = to_e<E>(sk);
+      float sq = q_[u], sk = k_[u];
+      for (int b = 0; b < nb; ++b) {
+        sq += pr0[(size_t)b * PT::SIZE + PT::DQ + r * DK + d];
+        sk += pr0[(size_t)b * PT::SIZE + PT::DKO + r * DK + d];
       }
+      ((E *)p.dq)[((tb + r) * H + h) * DK + d] = to_e<E>(sq);
+      ((E *)p.dk)[((tb + r) * H + h) * DK + d] = to_e<E>(sk);
     }
   }
 }
