@@ -427,7 +427,8 @@ template <typename E, int DK, int GATE>
 __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   constexpr int SKE = DK + 8;
   typedef Part<DK> PT;
-  __shared__ E Kl[BC * SKE], Ql[BC * SKE];
+  __shared__ __align__(16) E Kl[BC * SKE];
+  __shared__ __align__(16) E Ql[BC * SKE];
   __shared__ float Tl[BC * ST], Pl[BC * ST], Dt[BC * ST], Zl[BC * ST], Sl[BC * ST], Rl[BC * ST];
   __shared__ float bs[BC], gs[BC], dGs[BC], dBs[BC], misc[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -453,23 +454,38 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   auto K_ = [&](int r, int d) { return to_f(Kl[r * SKE + d]); };
   auto Q_ = [&](int r, int d) { return to_f(Ql[r * SKE + d]); };
 
-  for (int i = tid; i < BC * DK; i += BNT) {
-    const int r = i / DK, d = i % DK;
-    const size_t o = ((tb + r) * H + h) * DK + d;
-    Kl[r * SKE + d] = r < nv ? ((const E *)p.k)[o] : to_e<E>(0.f);
-    Ql[r * SKE + d] = r < nv ? ((const E *)p.q)[o] : to_e<E>(0.f);
-  }
-  const float *pr0 = p.part + ((size_t)slot * H + h) * nb * (size_t)PT::SIZE;
-  for (int i = tid; i < BC * BC; i += BNT) {
-    const int r = i / BC, col = i % BC;
-    float sp = 0.f, st = 0.f;
-    for (int b = 0; b < nb; ++b) {
-      sp += pr0[(size_t)b * PT::SIZE + PT::DP + i];
-      st += pr0[(size_t)b * PT::SIZE + PT::DT + i];
+  // K, Q: 16-byte loads (rows past the sequence end are zero)
+  constexpr int VE = 16 / (int)sizeof(E), RK = BC * (DK / VE) / BNT;
+#pragma unroll
+  for (int u = 0; u < RK; ++u) {
+    const int pc = tid + BNT * u, r = pc / (DK / VE), g = pc % (DK / VE);
+    u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+    if (r < nv) {
+      const size_t o = ((tb + r) * H + h) * DK + g * VE;
+      kv = *(const u32x4 *)((const E *)p.k + o);
+      qv = *(const u32x4 *)((const E *)p.q + o);
     }
-    Pl[r * ST + col] = sp;
-    Dt[r * ST + col] = st;
-    Tl[r * ST + col] = p.tmat[((size_t)slot * H + h) * BC * BC + i];
+    *(u32x4 *)(Kl + r * SKE + g * VE) = kv;
+    *(u32x4 *)(Ql + r * SKE + g * VE) = qv;
+  }
+  // dP and dT summed over the value blocks in a fixed order, and T: 16-byte loads
+  const float *pr0 = p.part + ((size_t)slot * H + h) * nb * (size_t)PT::SIZE;
+  const float *tm = p.tmat + ((size_t)slot * H + h) * BC * BC;
+#pragma unroll
+  for (int u = 0; u < BC * BC / 4 / BNT; ++u) {
+    const int i4 = 4 * (tid + BNT * u), r = i4 / BC, col = i4 % BC;
+    f32x4 sp = zero4(), st = zero4();
+    for (int b = 0; b < nb; ++b) {
+      sp += *(const f32x4 *)(pr0 + (size_t)b * PT::SIZE + PT::DP + i4);
+      st += *(const f32x4 *)(pr0 + (size_t)b * PT::SIZE + PT::DT + i4);
+    }
+    const f32x4 tv = *(const f32x4 *)(tm + i4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Pl[r * ST + col + e] = sp[e];
+      Dt[r * ST + col + e] = st[e];
+      Tl[r * ST + col + e] = tv[e];
+    }
   }
   if (tid < BC) {
     const bool ok = tid < nv;
@@ -569,9 +585,18 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
       if (GATE == GATE_HEAD) p.dlog_alpha[(tb + t) * H + h] = g;
     }
   }
-  // dq = Ep K + (partials), dk = (Ea + Ea^T) K + Ep^T Q + (partials)
+  // dq = Ep K + (partials), dk = (Ea + Ea^T) K + Ep^T Q + (partials); the partials of a
+  // tile are loaded before its products, so the loads overlap them
   for (int t = wave; t < (DK / 16) * 4; t += 4) {
     const int m0 = (t / (DK / 16)) * 16, n0 = (t % (DK / 16)) * 16;
+    float pq_[4] = {0.f, 0.f, 0.f, 0.f}, pk_[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < nb; ++b)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = m0 + 4 * lg + u, d = n0 + lm;
+        pq_[u] += pr0[(size_t)b * PT::SIZE + PT::DQ + r * DK + d];
+        pk_[u] += pr0[(size_t)b * PT::SIZE + PT::DKO + r * DK + d];
+      }
     const f32x4 q_ = tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Pl[r * ST + i]; },
                               [&](int i, int d) { return K_(i, d); });
     f32x4 k_ = tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Zl[r * ST + i] + Zl[i * ST + r]; },
@@ -582,13 +607,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     for (int u = 0; u < 4; ++u) {
       const int r = m0 + 4 * lg + u;
       if (r >= nv) continue;
-      float sq = q_[u], sk = k_[u];
-      for (int b = 0; b < nb; ++b) {
-        sq += pr0[(size_t)b * PT::SIZE + PT::DQ + r * DK + d];
-        sk += pr0[(size_t)b * PT::SIZE + PT::DKO + r * DK + d];
-      }
-      ((E *)p.dq)[((tb + r) * H + h) * DK + d] = to_e<E>(sq);
-      ((E *)p.dk)[((tb + r) * H + h) * DK + d] = to_e<E>(sk);
+      ((E *)p.dq)[((tb + r) * H + h) * DK + d] = to_e<E>(q_[u] + pq_[u]);
+      ((E *)p.dk)[((tb + r) * H + h) * DK + d] = to_e<E>(k_[u] + pk_[u]);
     }
   }
 }
