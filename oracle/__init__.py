@@ -13,7 +13,9 @@ gradient step, exact rational fixtures under ``tests/golden/`` and planted-mista
 checks); ``decode_pool`` by ``tests/test_oracle_decode.py`` (against ``fwd`` over
 the same tokens and over every stored prefix, chained and speculative calls); ``bwd``
 by ``tests/test_oracle_bwd.py`` (central finite differences of ``fwd`` and torch
-autograd of the recurrence in fp64); the
+autograd of the recurrence in fp64); ``fwd_dplr`` by ``tests/test_oracle_dplr.py``
+(reduces exactly to the delta rule and to the additive write, and equals the
+product of the dense transition matrices); the
 additive write (``write="add"``) and the constant per-head gate by
 ``tests/test_oracle_additive.py`` (RetNet's decay-mask parallel form, the
 gated-linear-attention brute-force sum, the plain linear-transformer sum, agreement
@@ -68,6 +70,9 @@ def _declare(lib):
     lib.oracle_bwd.restype = ctypes.c_int
     lib.oracle_bwd.argtypes = [ctypes.c_int, ip, ip, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_fwd_dplr.restype = ctypes.c_int
+    lib.oracle_fwd_dplr.argtypes = [ctypes.c_int, ip, ip, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -178,6 +183,37 @@ def bwd(q, k, v, beta, log_alpha, initial_state, dout, dfinal=None, cu_seqlens=N
     if const:
         dla = dla.sum(axis=(0, 1))
     return dq, dk_, dv_, db, dla, dinit
+
+
+def fwd_dplr(q, k, v, a, b, log_alpha=None, initial_state=None, cu_seqlens=None, gate=None,
+             nthreads: int = 0, lib=None):
+    """The diagonal-plus-low-rank transition M_t = Diag(alpha_t) M_{t-1} + b_t (a_t^T
+    M_{t-1}) + k_t v_t^T, o_t = M_t^T q_t, over whole sequences.  q, k, a, b
+    [B,T,H,d_k], v [B,T,H,d_v], log_alpha None | [B,T,H] | [B,T,H,d_k]; other
+    arguments as for ``fwd``.  Returns (o, final_state) in fp64."""
+    q, k, v, a, b = _f64(q), _f64(k), _f64(v), _f64(a), _f64(b)
+    log_alpha, initial_state = _f64(log_alpha), _f64(initial_state)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if gate is None:
+        gate = infer_gate(log_alpha, 3)
+    if cu_seqlens is not None:
+        cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64)
+        start, lens = cu[:-1].copy(), np.diff(cu)
+    else:
+        start = np.arange(B, dtype=np.int64) * T
+        lens = np.full(B, T, dtype=np.int64)
+    N = len(start)
+    o = np.zeros((B, T, H, dv))
+    fs = np.zeros((N, H, dk, dv))
+    lib = lib or load()
+    rc = lib.oracle_fwd_dplr(N, start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                             lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv, GATES[gate],
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(log_alpha), _ptr(initial_state),
+                             _ptr(o), _ptr(fs), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_fwd_dplr failed (%d)" % rc)
+    return o, fs
 
 
 def step(q, k, v, beta, log_alpha, state, gate=None, lib=None, write: str = "delta"):

@@ -205,3 +205,42 @@ def chunked_bwd(q, k, v, beta, log_alpha, M0, dO, dMT, C=64):
         for o_, x in zip(out, (dq, dk, dv, db, dg)):
             o_[sl] = x
     return tuple(x[:Tn] for x in out) + (dM,)
+
+
+def chunk_step_dplr(q, k, v, a, b, g, M0):
+    """One chunk of the diagonal-plus-low-rank transition with one decay per position
+    (g [C] log decays; zeros without a gate).  With u_j = a_j^T M_{j-1} (the rows U),
+    G the inclusive prefix of g and G_{-1} = 0:
+      (I - A_ab) U = diag(e^{G_{j-1}}) A M0 + A_ak V,
+      A_ab[j,i] = (a_j . b_i) e^{G_{j-1} - G_i},  A_ak[j,i] = (a_j . k_i) e^{G_{j-1} - G_i}  (i < j)
+      O   = diag(e^G) Q M0 + P_qb U + P_qk V,
+      P_qb[r,j] = (q_r . b_j) e^{G_r - G_j},  P_qk[r,j] = (q_r . k_j) e^{G_r - G_j}  (j <= r)
+      M_C = e^{G_C} M0 + (diag(e^{G_C - G}) B)^T U + (diag(e^{G_C - G}) K)^T V.
+    Returns (O, M_C)."""
+    C = q.shape[0]
+    strict = np.tril(np.ones((C, C), dtype=bool), -1)
+    incl = np.tril(np.ones((C, C), dtype=bool), 0)
+    G = np.cumsum(g)
+    Gp = np.concatenate([[0.0], G[:-1]])  # G_{j-1}
+    E1 = np.where(strict, np.exp(np.where(strict, Gp[:, None] - G[None, :], 0.0)), 0.0)
+    E2 = np.where(incl, np.exp(np.where(incl, G[:, None] - G[None, :], 0.0)), 0.0)
+    Aab, Aak = (a @ b.T) * E1, (a @ k.T) * E1
+    U = np.linalg.solve(np.eye(C) - Aab, np.exp(Gp)[:, None] * (a @ M0) + Aak @ v)
+    O = np.exp(G)[:, None] * (q @ M0) + ((q @ b.T) * E2) @ U + ((q @ k.T) * E2) @ v
+    w = np.exp(G[-1] - G)[:, None]
+    MC = np.exp(G[-1]) * M0 + (w * b).T @ U + (w * k).T @ v
+    return O, MC
+
+
+def chunked_dplr(q, k, v, a, b, log_alpha, M0, C=64):
+    """The chunked form over one sequence (q, k, a, b [T,dk], v [T,dv], log_alpha None
+    | [T]); a partial last chunk is padded with zero rows and log alpha = 0."""
+    Tn, dk_ = q.shape
+    la = np.zeros(Tn) if log_alpha is None else log_alpha
+    O = np.zeros((Tn, v.shape[1]))
+    M = M0
+    for c0 in range(0, Tn, C):
+        sl = slice(c0, min(c0 + C, Tn))
+        Oc, M = chunk_step_dplr(q[sl], k[sl], v[sl], a[sl], b[sl], la[sl], M)
+        O[sl] = Oc
+    return O, M

@@ -271,6 +271,66 @@ int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
   return failed ? -1 : 0;
 }
 
+/*
+ * The diagonal-plus-low-rank transition ("Decoding Hybrid Linear Attention
+ * Architectures", sec. 3 item 5): S_t = S_{t-1} (Diag(alpha_t) + a_t b_t^T) + v_t k_t^T,
+ * so in storage orientation (M = S^T) one token is
+ *   u = a^T M_{t-1}                 (a row of d_v values, read before anything changes)
+ *   M_t = Diag(alpha) M_{t-1} + b u + k v^T
+ *   o = M_t^T q                     (the read follows the write)
+ * alpha = exp(log_alpha): none (1), one per (token, head), or one per key channel.
+ * Arrays as for oracle_fwd, with a, b: [tokens][H][d_k].
+ */
+int oracle_fwd_dplr(int N, const int64_t *start, const int64_t *len, int H, int dk, int dv, int gate,
+                    const double *q, const double *k, const double *v, const double *a, const double *b,
+                    const double *log_alpha, const double *initial_state, double *o, double *final_state,
+                    int nthreads) {
+  int64_t pair;
+  int failed = 0;
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  if (gate != ORACLE_GATE_NONE && log_alpha == NULL) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+#endif
+  for (pair = 0; pair < (int64_t)N * H; ++pair) {
+    int n = (int)(pair / H), h = (int)(pair % H), i, j;
+    double *M = (double *)malloc(sizeof(double) * (size_t)dk * dv);
+    double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+    int64_t t;
+    if (!M || !u) { free(M); free(u); failed = 1; continue; }
+    if (initial_state)
+      memcpy(M, initial_state + ((size_t)n * H + h) * dk * dv, sizeof(double) * dk * dv);
+    else
+      memset(M, 0, sizeof(double) * dk * dv);
+    for (t = start[n]; t < start[n] + len[n]; ++t) {
+      const size_t th = (size_t)t * H + h;
+      const double *qt = q + th * dk, *kt = k + th * dk, *at = a + th * dk, *bt = b + th * dk, *vt = v + th * dv;
+      /* u = a^T M_{t-1} */
+      for (j = 0; j < dv; ++j) u[j] = 0.0;
+      for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j) u[j] += at[i] * M[i * dv + j];
+      /* M = Diag(alpha) M + b u + k v^T */
+      for (i = 0; i < dk; ++i) {
+        double al = 1.0;
+        if (gate == ORACLE_GATE_HEAD) al = exp(log_alpha[th]);
+        if (gate == ORACLE_GATE_KEY) al = exp(log_alpha[th * dk + i]);
+        for (j = 0; j < dv; ++j) M[i * dv + j] = al * M[i * dv + j] + bt[i] * u[j] + kt[i] * vt[j];
+      }
+      /* o = M^T q */
+      for (j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (i = 0; i < dk; ++i) acc += M[i * dv + j] * qt[i];
+        o[th * dv + j] = acc;
+      }
+    }
+    if (final_state) memcpy(final_state + ((size_t)n * H + h) * dk * dv, M, sizeof(double) * dk * dv);
+    free(M);
+    free(u);
+  }
+  return failed ? -1 : 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
