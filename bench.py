@@ -49,17 +49,23 @@ def alg_counts(tokens, H, dk, dv, nseq, gate, esize, has_init, has_final=True, w
 
     flops per token-head: 2C(3 d_k + 2 d_v) + 6 d_k d_v + C^2/3 (Gram tiles, UT inverse,
     W and U, W M, K^T Delta, Q M, Q K^T, P Delta; multiply-add = 2).  The additive
-    write has no erase: 2C(d_k + d_v) + 4 d_k d_v (Q K^T, P V, Q M, K^T V).
-    bytes: q, k, v read and o written in the I/O dtype, beta (delta write only) and
+    write has no erase: 2C(d_k + d_v) + 4 d_k d_v (Q K^T, P V, Q M, K^T V).  The
+    diagonal-plus-low-rank transition ("dplr"): 4C(d_k + d_v) + 8 d_k d_v + C^2/3 (four
+    lower-triangular Gram products, P_qk V, A_ak V, T R, P_qb U, Q M, A M and the two
+    state products; T's inverse).
+    bytes: q, k, v (and a, b for "dplr") read and o written in the I/O dtype, beta
+    (delta write only) and
     log alpha in fp32 (per token for "head", per channel for "key", one value per
     head for "const"), the fp32 initial state read (if given) and final state written.
     """
     C = CHUNK
     if write == "add":
         f_th = 2 * C * (dk + dv) + 4 * dk * dv
+    elif write == "dplr":
+        f_th = 4 * C * (dk + dv) + 8 * dk * dv + C * C / 3.0
     else:
         f_th = 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv + C * C / 3.0
-    b_th = (esize * (2 * dk + 2 * dv) + (4 if write == "delta" else 0)
+    b_th = (esize * ((4 if write == "dplr" else 2) * dk + 2 * dv) + (4 if write == "delta" else 0)
             + (4 if gate == "head" else 4 * dk if gate == "key" else 0))
     state = 4 * dk * dv * nseq * H * ((1 if has_init else 0) + (1 if has_final else 0))
     return f_th * tokens * H, b_th * tokens * H + state
@@ -108,7 +114,9 @@ def time_chunked(gdn, sets, steps, warmup):
     import torch
     # one validated call per input copy: each timed step is a single library call
     stream = torch.cuda.current_stream()
-    calls = [gdn.PreparedFwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"],
+    calls = [gdn.PreparedDplr(d["q"], d["k"], d["v"], d["a"], d["b"], d["log_alpha"], d["initial_state"],
+                              d["cu_seqlens"]) if d.get("write") == "dplr" else
+             gdn.PreparedFwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"],
                              d["cu_seqlens"], write=d.get("write", "delta")) for d in sets]
 
     def call(i):
@@ -286,7 +294,8 @@ def bench_workload(gdn, name, steps, warmup):
     res = {"workload": name, "ms_per_step": wall / steps * 1e3, "launch_ms": launch_ms,
            "tokens_per_s": tokens / (wall / steps), "alg_flops": flops, "alg_bytes": nbytes,
            "tflops": flops / (launch_ms / 1e3) / 1e12,
-           "mfma_frac": flops / (launch_ms / 1e3) / 1e12 / PEAK_MFMA[spec["dtype"]],
+           "mfma_frac": flops / (launch_ms / 1e3) / 1e12 / PEAK_MFMA["f32" if spec.get("write") == "dplr"
+                                                                     else spec["dtype"]],
            "hbm_gbs": nbytes / (launch_ms / 1e3) / 1e9,
            "hbm_frac": nbytes / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBS}
     return res, inp, sets
@@ -357,7 +366,8 @@ def main():
         torch.cuda.empty_cache()
         for name in ["gdn-bf16-B4-T2048-H8-d128", "kda-bf16-B2-T16384-H16-d128",
                      "gdn-varlen-bf16-N32-H16-d128", "deltanet-fp32-B1-T256-H2-d64",
-                     "retnet-bf16-B16-T2048-H8-d128", "gla-bf16-B2-T16384-H16-d128"]:
+                     "retnet-bf16-B16-T2048-H8-d128", "gla-bf16-B2-T16384-H16-d128",
+                     "dplr-bf16-B16-T2048-H8-d128"]:
             try:
                 r, winp, wsets = bench_workload(gdn, name, max(5, args.steps // 5), None)
             except RuntimeError as e:

@@ -8,7 +8,8 @@ raises on import.
 
 The names follow the C ABI: ``fwd_chunked`` wraps ``gdn_fwd_chunked``,
 ``recurrent_step`` wraps ``gdn_fwd_recurrent_step``, ``decode`` wraps
-``gdn_fwd_decode`` and ``bwd_chunked`` wraps ``gdn_bwd_chunked``.
+``gdn_fwd_decode``, ``bwd_chunked`` wraps ``gdn_bwd_chunked`` and ``fwd_dplr``
+wraps ``gdn_fwd_dplr``.
 """
 from __future__ import annotations
 
@@ -77,6 +78,17 @@ class BwdArgs(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class DplrArgs(ctypes.Structure):
+    """Mirror of ``gdn_dplr_args``."""
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("d_k", ctypes.c_int), ("d_v", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("N", ctypes.c_int), ("dtype", ctypes.c_int), ("gate", ctypes.c_int),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("a", ctypes.c_void_p),
+                ("b", ctypes.c_void_p), ("v", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
+                ("initial_state", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("final_state", ctypes.c_void_p)]
+
+
 def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError("libgdn.so is not built (%s); run `python __graft_entry__.py build` "
@@ -94,6 +106,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
     lib.gdn_bwd_chunked.restype = ctypes.c_int
     lib.gdn_bwd_chunked.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
+    lib.gdn_fwd_dplr.restype = ctypes.c_int
+    lib.gdn_fwd_dplr.argtypes = [ctypes.POINTER(DplrArgs), ctypes.c_void_p]
     lib.gdn_status_str.restype = ctypes.c_char_p
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_version.restype = ctypes.c_int
@@ -370,6 +384,66 @@ class PreparedFwd:
         """Enqueue the forward on `stream` (default: torch's current stream)."""
         _check(_lib.gdn_fwd_chunked(self._ref, _stream(stream)), "gdn_fwd_chunked")
         return self.out, self.final_state
+
+
+def check_dplr_tensors(q, k, v, a, b, log_alpha=None, initial_state=None, cu_seqlens=None, out=None,
+                       final_state=None):
+    """Host-side checks for fwd_dplr: those of fwd_chunked with the additive write,
+    plus a and b shaped and typed like q.  Returns N."""
+    for name, t in (("a", a), ("b", b)):
+        _require(t is not None and tuple(t.shape) == tuple(q.shape) and t.dtype == q.dtype,
+                 "%s must have the shape and dtype of q" % name)
+        _require(t.is_contiguous(), "%s must be contiguous" % name)
+    N = check_fwd_tensors(q, k, v, None, log_alpha, initial_state, cu_seqlens, out, final_state, "add")
+    _same_device([("a", a), ("b", b)], q)
+    return N
+
+
+def make_dplr_args(q, k, v, a, b, log_alpha, initial_state, cu_seqlens, o, final_state,
+                   chunk: int = CHUNK) -> DplrArgs:
+    B, T, H, dk = q.shape
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    return DplrArgs(B=B, T=T, H=H, d_k=dk, d_v=v.shape[-1], chunk=chunk, N=N, dtype=_dtype_code(q),
+                    gate=gate_code(log_alpha, 3), q=_ptr(q), k=_ptr(k), a=_ptr(a), b=_ptr(b), v=_ptr(v),
+                    log_alpha=_ptr(log_alpha), initial_state=_ptr(initial_state),
+                    cu_seqlens=_ptr(cu_seqlens), o=_ptr(o), final_state=_ptr(final_state))
+
+
+class PreparedDplr:
+    """A validated gdn_fwd_dplr call on fixed buffers (see PreparedFwd)."""
+
+    def __init__(self, q, k, v, a, b, log_alpha=None, initial_state=None, cu_seqlens=None, out=None,
+                 final_state=None, output_final_state: bool = True, chunk: int = CHUNK):
+        import torch
+        B, T, H, dk = q.shape
+        N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+        if output_final_state and final_state is None:
+            final_state = torch.empty((N, H, dk, v.shape[-1]), dtype=torch.float32, device=q.device)
+        if out is None:
+            out = torch.empty(tuple(v.shape), dtype=q.dtype, device=q.device)
+        fs = final_state if output_final_state else None
+        check_dplr_tensors(q, k, v, a, b, log_alpha, initial_state, cu_seqlens, out, fs)
+        self.args = make_dplr_args(q, k, v, a, b, log_alpha, initial_state, cu_seqlens, out, fs, chunk)
+        self._keep = (q, k, v, a, b, log_alpha, initial_state, cu_seqlens)
+        self.out, self.final_state = out, fs
+        self._ref = ctypes.byref(self.args)
+
+    def launch(self, stream=None):
+        _check(_lib.gdn_fwd_dplr(self._ref, _stream(stream)), "gdn_fwd_dplr")
+        return self.out, self.final_state
+
+
+def fwd_dplr(q, k, v, a, b, log_alpha=None, initial_state=None, cu_seqlens=None,
+             output_final_state: bool = True, chunk: int = CHUNK, out=None, final_state=None, stream=None):
+    """Chunked forward of the diagonal-plus-low-rank transition (gdn_fwd_dplr):
+    M_t = Diag(alpha_t) M_{t-1} + b_t (a_t^T M_{t-1}) + k_t v_t^T, o_t = M_t^T q_t.
+
+    q, k, a, b [B,T,H,d_k] and v [B,T,H,d_v] (one dtype, bf16 or fp32); log_alpha None
+    | [B,T,H] fp32; initial_state, cu_seqlens as for fwd_chunked.  Returns (o,
+    final_state or None), asynchronous on the current (or given) stream."""
+    p = PreparedDplr(q, k, v, a, b, log_alpha, initial_state, cu_seqlens, out, final_state,
+                     output_final_state, chunk)
+    return p.launch(stream)
 
 
 def recurrent_step(q, k, v, beta, log_alpha, state, out=None, stream=None, write: str = "delta"):

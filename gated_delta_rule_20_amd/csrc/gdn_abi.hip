@@ -153,6 +153,21 @@ int check_bwd(const gdn_bwd_args *a) {
   return GDN_OK;
 }
 
+int check_dplr(const gdn_dplr_args *a) {
+  if (!a) return GDN_ERR_INVALID_ARG;
+  gdn_fwd_args f{};
+  f.B = a->B; f.T = a->T; f.H = a->H; f.d_k = a->d_k; f.d_v = a->d_v; f.chunk = a->chunk; f.N = a->N;
+  f.dtype = a->dtype; f.gate = a->gate; f.write = GDN_WRITE_ADD;
+  f.q = a->q; f.k = a->k; f.v = a->v; f.beta = nullptr; f.log_alpha = a->log_alpha;
+  f.initial_state = a->initial_state; f.cu_seqlens = a->cu_seqlens; f.o = a->o; f.final_state = a->final_state;
+  const int st = check_fwd(&f);
+  if (st != GDN_OK) return st;
+  if (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD) return GDN_ERR_UNSUPPORTED;
+  if ((long)a->B * a->T > 0 && (!a->a || !a->b)) return GDN_ERR_INVALID_ARG;
+  if ((a->a && !aligned(a->a, 16)) || (a->b && !aligned(a->b, 16))) return GDN_ERR_INVALID_ARG;
+  return GDN_OK;
+}
+
 struct BwdLayout {
   long slots;
   size_t states, tmat, part;
@@ -368,6 +383,31 @@ int gdn_fwd_decode(const gdn_decode_args *a, void *hip_stream) {
   p.la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
   if (gdn::launch_decode(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->d_v, kernel_gate(a->gate),
                          a->write == GDN_WRITE_ADD, (hipStream_t)hip_stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+int gdn_fwd_dplr(const gdn_dplr_args *a, void *hip_stream) {
+  const int st = check_dplr(a);
+  if (st != GDN_OK) return st;
+  if (a->N == 0) return GDN_OK;
+  gdn::DplrParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.a = a->a;
+  p.b = a->b;
+  p.log_alpha = a->log_alpha;
+  p.init_state = a->initial_state;
+  p.final_state = a->final_state;
+  p.o = a->o;
+  p.cu_seqlens = a->cu_seqlens;
+  p.N = a->N;
+  p.H = a->H;
+  p.T = a->T;
+  p.dv = a->d_v;
+  if (gdn::launch_dplr(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, (int)a->gate, (hipStream_t)hip_stream) !=
+      hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
 }

@@ -1,0 +1,277 @@
+// gdn_dplr.hip -- chunked forward of the diagonal-plus-low-rank transition.
+//
+// "Decoding Hybrid Linear Attention Architectures", sec. 3 item 5: the state transition
+// Diag(alpha_t) + a_t b_t^T with an additive write, S_t = S_{t-1}(Diag(alpha_t) + a_t b_t^T)
+// + v_t k_t^T, here with one decay per (token, head) or none.  In storage orientation
+// (M = S^T) one token is u = a^T M_{t-1}, M_t = alpha M_{t-1} + b u + k v^T, o = M_t^T q.
+// Within a chunk entering with M0 (G the inclusive prefix of log alpha, G_{-1} = 0) the
+// rows u_j solve a unit lower-triangular system, the UT form of the delta rule:
+//   (I - A_ab) U = diag(e^{G_{j-1}}) A M0 + A_ak V,
+//   A_ab[j,i] = (a_j . b_i) e^{G_{j-1} - G_i},  A_ak[j,i] = (a_j . k_i) e^{G_{j-1} - G_i}  (i < j)
+//   O   = diag(e^G) Q M0 + P_qb U + P_qk V,
+//   P_qb[r,j] = (q_r . b_j) e^{G_r - G_j},  P_qk[r,j] = (q_r . k_j) e^{G_r - G_j}  (j <= r)
+//   M_C = e^{G_C} M0 + (diag(e^{G_C - G}) B)^T U + (diag(e^{G_C - G}) K)^T V.
+//
+// One workgroup (4 waves) per (sequence, head, 32 value columns) walks its sequence;
+// the state block (d_k x 32, fp32) stays in LDS.  Products on the fp32 matrix cores
+// (16x16 tiles, operands gathered from LDS); T = (I - A_ab)^-1 by forward substitution
+// of the 16x16 diagonal blocks and block substitution of the rest.
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+#include "gdn_tile.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int DC = 64;    // chunk length
+constexpr int DNT = 256;  // threads per workgroup
+constexpr int DVB = 32;   // value columns per workgroup
+constexpr int DSV = DVB + 1, DST = DC + 1;
+
+template <typename E, int DK, int GATE>
+__global__ __launch_bounds__(DNT, 1) void dplr_fwd_kernel(DplrParams p) {
+  constexpr int SKE = DK + 8;
+  constexpr int VE = 16 / (int)sizeof(E);
+  constexpr int RK = DC * (DK / VE) / DNT;  // 16-byte pieces of a [64][DK] operand per thread
+  __shared__ __align__(16) E Ql[DC * SKE];
+  __shared__ __align__(16) E Kl[DC * SKE];
+  __shared__ __align__(16) E Al[DC * SKE];
+  __shared__ __align__(16) E Bl[DC * SKE];
+  __shared__ float X1[DC * DST], Tb[DC * DST];
+  __shared__ float Ml[DK * DSV], Vb[DC * DSV], Rb[DC * DSV], Ub[DC * DSV];
+  __shared__ float gs[DC], eg[DC], egp[DC], et[DC], misc[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lm = lane & 15;
+  const int H = p.H, dv = p.dv, nb = dv / DVB;
+  const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
+  const int n = pair / H, h = pair % H, col0 = jb * DVB;
+  long tok0;
+  int len;
+  if (p.cu_seqlens) {
+    const int s0 = p.cu_seqlens[n], s1 = p.cu_seqlens[n + 1];
+    if (s0 < 0 || s1 < s0 || s1 > p.T) return;  // malformed offsets: leave untouched
+    tok0 = s0;
+    len = s1 - s0;
+  } else {
+    tok0 = (long)n * p.T;
+    len = p.T;
+  }
+  const int nchunks = (len + DC - 1) / DC;
+  const size_t sstate = ((size_t)n * H + h) * DK * dv + col0;
+  auto Q_ = [&](int r, int d) { return to_f(Ql[r * SKE + d]); };
+  auto K_ = [&](int r, int d) { return to_f(Kl[r * SKE + d]); };
+  auto A_ = [&](int r, int d) { return to_f(Al[r * SKE + d]); };
+  auto B_ = [&](int r, int d) { return to_f(Bl[r * SKE + d]); };
+
+  for (int i = tid; i < DK * DVB; i += DNT) {
+    const int d = i / DVB, j = i % DVB;
+    Ml[d * DSV + j] = p.init_state ? p.init_state[sstate + (size_t)d * dv + j] : 0.f;
+  }
+  for (int i = tid; i < DC * DST; i += DNT) Tb[i] = X1[i] = 0.f;  // upper blocks stay zero
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int nv = min(DC, len - c * DC);
+    const size_t tb = (size_t)tok0 + (size_t)c * DC;
+    __syncthreads();  // the previous chunk is done with every buffer
+    // ---- inputs (rows past the sequence end are zero): 16-byte loads
+#pragma unroll
+    for (int u = 0; u < RK; ++u) {
+      const int pc = tid + DNT * u, r = pc / (DK / VE), g = pc % (DK / VE);
+      u32x4 qv = {0u, 0u, 0u, 0u}, kv = qv, av = qv, bv = qv;
+      if (r < nv) {
+        const size_t o = ((tb + r) * H + h) * DK + g * VE;
+        qv = *(const u32x4 *)((const E *)p.q + o);
+        kv = *(const u32x4 *)((const E *)p.k + o);
+        av = *(const u32x4 *)((const E *)p.a + o);
+        bv = *(const u32x4 *)((const E *)p.b + o);
+      }
+      *(u32x4 *)(Ql + r * SKE + g * VE) = qv;
+      *(u32x4 *)(Kl + r * SKE + g * VE) = kv;
+      *(u32x4 *)(Al + r * SKE + g * VE) = av;
+      *(u32x4 *)(Bl + r * SKE + g * VE) = bv;
+    }
+    for (int i = tid; i < DC * DVB; i += DNT) {
+      const int r = i / DVB, j = i % DVB;
+      Vb[r * DSV + j] = r < nv ? to_f(((const E *)p.v)[((tb + r) * H + h) * dv + col0 + j]) : 0.f;
+    }
+    if (tid < DC) gs[tid] = (GATE == GATE_HEAD && tid < nv) ? p.log_alpha[(tb + tid) * H + h] : 0.f;
+    __syncthreads();
+    if (wave == 0) {  // decay prefix: e^G, e^{G_{j-1}}, e^{G_C - G}, e^{G_C}
+      float g = gs[lane];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(g, off);
+        if (lane >= off) g += y;
+      }
+      const float gC = __shfl(g, 63), gp = __shfl_up(g, 1);
+      gs[lane] = g;
+      eg[lane] = __expf(g);
+      egp[lane] = lane == 0 ? 1.f : __expf(gp);
+      et[lane] = __expf(gC - g);
+      if (lane == 0) misc[0] = __expf(gC);
+    }
+    __syncthreads();
+    auto e_out = [&](int r, int j) {  // e^{G_r - G_j}, j <= r
+      return j <= r ? (GATE == GATE_HEAD ? __expf(gs[r] - gs[j]) : 1.f) : 0.f;
+    };
+    auto e_in = [&](int j, int i) {  // e^{G_{j-1} - G_i}, i < j
+      return i < j ? (GATE == GATE_HEAD ? __expf((j > 0 ? gs[j - 1] : 0.f) - gs[i]) : 1.f) : 0.f;
+    };
+    // ---- P_qk into X1; O = e^G Q M0 (two tiles of the 64 x 32 output per wave, kept in registers)
+    f32x4 Oacc[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+      const f32x4 v = tile<DK>(m0, n0, lg, lm, Q_, [&](int d, int j) { return Ml[d * DSV + j]; });
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Oacc[q][u] = eg[m0 + 4 * lg + u] * v[u];
+    }
+    // X1 = lower(rowf colf^T * fac): the 10 lower 16x16 tiles, 3/3/2/2 per wave (the
+    // upper ones were zeroed once and are never written)
+    auto gram = [&](auto rowf, auto colf, auto fac) {
+      for (int t = wave; t < 10; t += 4) {
+        const int mb = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int m0 = 16 * mb, n0 = 16 * (t - mb * (mb + 1) / 2);
+        const f32x4 v = tile<DK>(m0, n0, lg, lm, rowf, [&](int d, int i) { return colf(i, d); });
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = m0 + 4 * lg + u, i = n0 + lm;
+          X1[r * DST + i] = v[u] * fac(r, i);
+        }
+      }
+    };
+    gram(Q_, K_, e_out);
+    __syncthreads();
+    // ---- O += P_qk V
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+      Oacc[q] += tile<DC>(m0, n0, lg, lm, [&](int r, int i) { return X1[r * DST + i]; },
+                          [&](int i, int j) { return Vb[i * DSV + j]; });
+    }
+    __syncthreads();
+    // ---- A_ab into X1, then T = (I - A_ab)^-1 into Tb
+    gram(A_, B_, e_in);
+    __syncthreads();
+    if (wave == 0) {  // diagonal blocks: lane (lg, lm) solves column lm of block lg
+      const int o = 16 * lg;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = r == lm ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) acc += X1[(o + r) * DST + o + i] * x[i];
+        x[r] = acc;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tb[(o + r) * DST + o + lm] = x[r];
+    }
+    __syncthreads();
+    if (wave < 3) {  // off-diagonal blocks, block column b = wave: T[a][b] = T[a][a] sum_k A[a][k] T[k][b]
+      const int b = wave;
+      float *ys = Rb + wave * (16 * 17);  // scratch (R is formed afterwards)
+      for (int a = b + 1; a < 4; ++a) {
+        const f32x4 y = tile<DC>(16 * a, 16 * b, lg, lm,
+                                 [&](int r, int k) { return (k >= 16 * b && k < 16 * a) ? X1[r * DST + k] : 0.f; },
+                                 [&](int k, int col) { return Tb[k * DST + col]; });
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ys[(4 * lg + u) * 17 + lm] = y[u];
+        const f32x4 z = tile<32>(16 * a, 16 * b, lg, lm,
+                                 [&](int r, int k) { return k < 16 ? Tb[r * DST + 16 * a + k] : 0.f; },
+                                 [&](int k, int col) { return k < 16 ? ys[k * 17 + col - 16 * b] : 0.f; });
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Tb[(16 * a + 4 * lg + u) * DST + 16 * b + lm] = z[u];
+      }
+    }
+    __syncthreads();
+    // ---- A_ak into X1; R = diag(e^{G_{j-1}}) A M0 + A_ak V into Rb
+    gram(A_, K_, e_in);
+    __syncthreads();
+    mfma_mm<DC, DVB, DK, 4>(wave, lane, A_, [&](int d, int j) { return Ml[d * DSV + j]; }, [&](int r, int j, f32x4 v) {
+      const f32x4 w = tile<DC>(r - 4 * lg, j - lm, lg, lm, [&](int rr, int i) { return X1[rr * DST + i]; },
+                               [&](int i, int jj) { return Vb[i * DSV + jj]; });
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Rb[(r + u) * DSV + j] = egp[r + u] * v[u] + w[u];
+    });
+    __syncthreads();
+    // ---- U = T R
+    mfma_mm<DC, DVB, DC, 4>(wave, lane, [&](int r, int i) { return Tb[r * DST + i]; },
+                            [&](int i, int j) { return Rb[i * DSV + j]; }, [&](int r, int j, f32x4 v) {
+#pragma unroll
+                              for (int u = 0; u < 4; ++u) Ub[(r + u) * DSV + j] = v[u];
+                            });
+    __syncthreads();
+    // ---- P_qb into X1; O += P_qb U
+    gram(Q_, B_, e_out);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+      Oacc[q] += tile<DC>(m0, n0, lg, lm, [&](int r, int i) { return X1[r * DST + i]; },
+                          [&](int i, int j) { return Ub[i * DSV + j]; });
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = m0 + 4 * lg + u;
+        if (r < nv) ((E *)p.o)[((tb + r) * H + h) * dv + col0 + n0 + lm] = to_e<E>(Oacc[q][u]);
+      }
+    }
+    // ---- M <- e^{G_C} M + (e^{G_C - G} B)^T U + (e^{G_C - G} K)^T V   (DK x 32)
+    {
+      constexpr int TPW = (DK / 16) * 2 / 4;  // tiles per wave
+      f32x4 nm[TPW];
+      const float gam = misc[0];
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+        const f32x4 t1 = tile<DC>(m0, n0, lg, lm, [&](int d, int r) { return et[r] * B_(r, d); },
+                                  [&](int r, int j) { return Ub[r * DSV + j]; });
+        const f32x4 t2 = tile<DC>(m0, n0, lg, lm, [&](int d, int r) { return et[r] * K_(r, d); },
+                                  [&](int r, int j) { return Vb[r * DSV + j]; });
+#pragma unroll
+        for (int u = 0; u < 4; ++u) nm[q][u] = gam * Ml[(m0 + 4 * lg + u) * DSV + n0 + lm] + t1[u] + t2[u];
+      }
+      __syncthreads();  // every read of the old state is done
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Ml[(m0 + 4 * lg + u) * DSV + n0 + lm] = nm[q][u];
+      }
+    }
+  }
+  __syncthreads();
+  if (p.final_state)
+    for (int i = tid; i < DK * DVB; i += DNT) {
+      const int d = i / DVB, j = i % DVB;
+      p.final_state[sstate + (size_t)d * dv + j] = Ml[d * DSV + j];
+    }
+}
+
+template <typename E, int DK>
+hipError_t launch_dp(const DplrParams &p, int gate, hipStream_t stream) {
+  const int blocks = p.N * p.H * (p.dv / DVB);
+  if (blocks == 0) return hipSuccess;
+  if (gate == GATE_HEAD)
+    hipLaunchKernelGGL((dplr_fwd_kernel<E, DK, GATE_HEAD>), dim3(blocks), dim3(DNT), 0, stream, p);
+  else if (gate == GATE_NONE)
+    hipLaunchKernelGGL((dplr_fwd_kernel<E, DK, GATE_NONE>), dim3(blocks), dim3(DNT), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dplr(const DplrParams &p, int dtype, int dk, int gate, hipStream_t stream) {
+  if (dtype == 1) {
+    if (dk == 128) return launch_dp<bf16, 128>(p, gate, stream);
+    if (dk == 64) return launch_dp<bf16, 64>(p, gate, stream);
+  } else {
+    if (dk == 64) return launch_dp<float, 64>(p, gate, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -83,6 +83,18 @@ struct BwdParams {
 size_t bwd_part_floats(int dk);
 hipError_t launch_bwd(const BwdParams &p, int dtype, int dk, int gate, hipStream_t stream);
 
+// Forward of the diagonal-plus-low-rank transition (no gate or the scalar gate).
+struct DplrParams {
+  const void *q, *k, *v, *a, *b;  // [tokens, H, d_k] (v: d_v), I/O dtype
+  const float *log_alpha;         // NULL | [tokens, H]
+  const float *init_state;        // NULL | [N, H, d_k, d_v]
+  float *final_state;             // NULL | [N, H, d_k, d_v]
+  void *o;                        // [tokens, H, d_v]
+  const int32_t *cu_seqlens;      // NULL (batch) | [N + 1]
+  int N, H, T, dv;
+};
+hipError_t launch_dplr(const DplrParams &p, int dtype, int dk, int gate, hipStream_t stream);
+
 // dtype: 0 fp32, 1 bf16.  Each launcher returns hipSuccess or the launch error.
 // dvb: columns of d_v per workgroup (32 or 64).
 // add: the additive write (S += v k^T; beta unused) instead of the delta rule.

@@ -234,6 +234,41 @@ size_t gdn_bwd_workspace_size(const gdn_bwd_args *args);
 /* Gradients: writes dq, dk, dv, dbeta, dlog_alpha (HEAD) and dinitial_state (if given). */
 int gdn_bwd_chunked(const gdn_bwd_args *args, void *hip_stream);
 
+/*
+ * Chunked forward of the diagonal-plus-low-rank transition ("Decoding Hybrid Linear
+ * Attention Architectures", sec. 3 item 5: a transition Diag(alpha_t) + a_t b_t^T
+ * with an additive write).  Per token, in the state orientation M = S^T used here:
+ *
+ *   M_t = Diag(alpha_t) M_{t-1} + b_t (a_t^T M_{t-1}) + k_t v_t^T,   o_t = M_t^T q_t
+ *
+ * i.e. S_t = S_{t-1} (Diag(alpha_t) + a_t b_t^T) + v_t k_t^T.  With b_t = k_t,
+ * a_t = -alpha_t beta_t k_t and v scaled by beta_t it is the (gated) delta rule of
+ * gdn_fwd_chunked; with a_t = 0 it is its additive write.  Computed chunk by chunk
+ * (C = 64; the pages' chunkwise algorithm of sec. 5, with the within-chunk low-rank
+ * products solved in UT form as for the delta rule).  Supported: GDN_GATE_NONE and
+ * GDN_GATE_HEAD (other gates return GDN_ERR_UNSUPPORTED); bf16 with d_k 64 or 128,
+ * fp32 with d_k 64; d_v 64 or 128.  Batch and varlen modes, partial chunks, empty
+ * sequences, alignment and validation as for gdn_fwd_chunked.  No workspace.
+ * The recurrence is stable only when the transitions are (e.g. a = -kappa,
+ * b = kappa * w with |kappa| = 1 and 0 <= w <= 1); the library does not check this.
+ */
+typedef struct {
+  int B, T, H, d_k, d_v, chunk, N; /* as in gdn_fwd_args                          */
+  gdn_dtype dtype;                 /* dtype of q, k, v, a, b, o                   */
+  gdn_gate gate;                   /* GDN_GATE_NONE or GDN_GATE_HEAD              */
+  const void *q, *k, *a, *b;       /* [B, T, H, d_k], dtype                       */
+  const void *v;                   /* [B, T, H, d_v], dtype                       */
+  const float *log_alpha;          /* NONE: NULL; HEAD: [B, T, H] fp32            */
+  const float *initial_state;      /* NULL (zeros) or [N, H, d_k, d_v] fp32       */
+  const int32_t *cu_seqlens;       /* NULL or [N + 1] int32 (device)              */
+  void *o;                         /* out: [B, T, H, d_v], dtype                  */
+  float *final_state;              /* out: NULL or [N, H, d_k, d_v]; may alias
+                                      initial_state                               */
+} gdn_dplr_args;
+
+/* Diagonal-plus-low-rank forward: writes o (and final_state when non-NULL). */
+int gdn_fwd_dplr(const gdn_dplr_args *args, void *hip_stream);
+
 /* Static description of a status code (never NULL). */
 const char *gdn_status_str(int status);
 

@@ -14,6 +14,10 @@ Distributions (the same for every workload unless stated):
          "const": one fixed log decay per head, log(1 - 2^(-5-h)) (RetNet's schedule)
   write  "delta" (default) or "add" (beta absent)
   state  optional initial state ~ N(0, std^2), fp32, layout [N,H,d_k,d_v] (M = S^T)
+  dplr   the diagonal-plus-low-rank transition's a = -kappa, b = kappa * w, with kappa
+         ~ N(0,1) L2-normalised and w = sigmoid(N(0,1)) per key channel (so the
+         low-rank correction shrinks the state along kappa by a factor in (0, 1)),
+         drawn from a second generator seeded seed + 7919; beta is dropped
 Draw order: sequence lengths (varlen), q, k, v, beta logits, gate factors, initial
 state, then decode tokens.
 """
@@ -44,6 +48,10 @@ WORKLOADS = {
     "gla-bf16-B2-T16384-H16-d128": dict(
         B=2, T=16384, H=16, dk=128, dv=128, gate="key", write="add", dtype="bf16", state_std=None,
         seed=1006),
+    # the diagonal-plus-low-rank transition with the scalar gate, at the 350M-class shape
+    "dplr-bf16-B16-T2048-H8-d128": dict(
+        B=16, T=2048, H=8, dk=128, dv=128, gate="head", write="dplr", dtype="bf16", state_std=0.02,
+        seed=1007),
 }
 
 CHUNK = 64
@@ -97,6 +105,21 @@ def random_inputs(B, T, H, dk, dv, gate="head", dtype="bf16", seed=0, state_std=
                 gate=gate, dtype=dtype, N=N)
 
 
+def dplr_inputs(B, T, H, dk, dv, gate="head", dtype="bf16", seed=0, state_std=None, lengths=None):
+    """Inputs of the diagonal-plus-low-rank transition: those of ``random_inputs``
+    without beta, plus a = -kappa and b = kappa * w (kappa a unit vector, w in (0, 1)
+    per key channel) in the I/O dtype."""
+    out = random_inputs(B, T, H, dk, dv, gate, dtype, seed=seed, state_std=state_std, lengths=lengths)
+    g = torch.Generator().manual_seed(int(seed) + 7919)
+    lead = tuple(out["q"].shape[:2])
+    kappa = _unit(torch.randn(*lead, H, dk, generator=g))
+    w = torch.sigmoid(torch.randn(*lead, H, dk, generator=g))
+    dt = _DTYPES[dtype]
+    out["a"], out["b"] = (-kappa).to(dt), (kappa * w).to(dt)
+    out["beta"], out["write"] = None, "dplr"
+    return out
+
+
 def retnet_log_gamma(H: int) -> torch.Tensor:
     """Fixed per-head log decays log(1 - 2^(-5 - h)), h = 0..H-1: the head-wise decay
     schedule that the RetNet passage gives as its example (float32 [H])."""
@@ -119,6 +142,9 @@ def workload_inputs(name: str):
                             spec["dtype"], seed=spec["seed"] + 7919, lengths=lengths)
         out["lengths"] = lengths
         return out
+    if spec.get("write") == "dplr":
+        return dplr_inputs(spec["B"], spec["T"], spec["H"], spec["dk"], spec["dv"], spec["gate"],
+                           spec["dtype"], seed=spec["seed"], state_std=spec["state_std"])
     const = spec["gate"] == "const"
     out = random_inputs(spec["B"], spec["T"], spec["H"], spec["dk"], spec["dv"],
                         "none" if const else spec["gate"], spec["dtype"], seed=spec["seed"],

@@ -50,8 +50,8 @@ def fwd(g, a):
 
 def test_header_declares_the_boundary(g):
     assert g.header_functions() == ["gdn_bwd_chunked", "gdn_bwd_workspace_size", "gdn_fwd_chunked",
-                                    "gdn_fwd_decode", "gdn_fwd_recurrent_step", "gdn_fwd_workspace_size",
-                                    "gdn_status_str", "gdn_version"]
+                                    "gdn_fwd_decode", "gdn_fwd_dplr", "gdn_fwd_recurrent_step",
+                                    "gdn_fwd_workspace_size", "gdn_status_str", "gdn_version"]
 
 
 def test_library_exports_every_header_function(g):
@@ -322,3 +322,42 @@ def test_bwd_workspace_size(g):
                                                    slots * 4 * 4 * part * 4))
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(a)) == expect
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(bwd_args(g, dq=None))) == 0
+
+
+def dplr_args(g, **kw):
+    a = g.DplrArgs(B=2, T=128, H=4, d_k=128, d_v=128, chunk=64, N=2, dtype=g.GDN_BF16, gate=g.GDN_GATE_HEAD)
+    a.q, a.k, a.a, a.b, a.v, a.log_alpha, a.o = (fake(i) for i in range(7))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(gate=2), UNSUPPORTED),                  # per-key-channel gate
+    (dict(gate=3), UNSUPPORTED),                  # constant per-head gate
+    (dict(gate=7), INVALID),
+    (dict(a=None), INVALID),
+    (dict(b=None), INVALID),
+    (dict(b=fake(3, 8)), INVALID),                # 16-byte alignment
+    (dict(log_alpha=None), INVALID),              # the scalar gate needs its decays
+    (dict(gate=0), INVALID),                      # no gate: no decays either
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(d_k=96), UNSUPPORTED),
+    (dict(dtype=0, d_k=128), UNSUPPORTED)    ,  # fp32 takes d_k = 64 only
+    (dict(N=3), INVALID),                         # batch mode: N == B
+    (dict(B=0, N=0), OK),                         # nothing to do, nothing launched
+])
+def test_dplr_host_validation(g, change, status):
+    assert g._lib.gdn_fwd_dplr(ctypes.byref(dplr_args(g, **change)), None) == status
+    assert g._lib.gdn_fwd_dplr(None, None) == INVALID
+
+
+def test_binding_rejects_bad_dplr_tensors(g):
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    v = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="a must have the shape"):
+        g.fwd_dplr(q, q, v, q[:, :4], q)
+    with pytest.raises(ValueError, match="b must have the shape"):
+        g.fwd_dplr(q, q, v, q, q.float())
+    with pytest.raises(ValueError, match="GPU device"):
+        g.fwd_dplr(q, q, v, q, q)
