@@ -13,9 +13,12 @@
 //   M_C = e^{G_C} M0 + (diag(e^{G_C - G}) B)^T U + (diag(e^{G_C - G}) K)^T V.
 //
 // One workgroup (4 waves) per (sequence, head, 32 value columns) walks its sequence;
-// the state block (d_k x 32, fp32) stays in LDS.  Products on the fp32 matrix cores
-// (16x16 tiles, operands gathered from LDS); T = (I - A_ab)^-1 by forward substitution
-// of the 16x16 diagonal blocks and block substitution of the rest.
+// the state block (d_k x 32, fp32) stays in LDS.  T = (I - A_ab)^-1 by forward
+// substitution of the 16x16 diagonal blocks and block substitution of the rest.  Two
+// kernels: fp32 I/O (d_k = 64) on the fp32 matrix cores with operands gathered from
+// LDS (dplr_fwd_kernel), and bf16 I/O on the bf16 matrix cores (dplr_bf16_kernel).
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 #include "gdn_tile.h"
@@ -249,16 +252,329 @@ __global__ __launch_bounds__(DNT, 1) void dplr_fwd_kernel(DplrParams p) {
     }
 }
 
+// bf16 I/O: every product on the bf16 matrix cores (16x16x32).  The inputs q, k, a, b,
+// v are bf16 already, so the four Gram products Q K^T, A B^T, A K^T, Q B^T are exact
+// bf16 MFMAs; a product with an fp32 operand (the state, T, R, U, the decayed Gram
+// tiles) takes that operand as a hi + lo pair of bf16 terms (Split), which keeps it to
+// about 2^-17 relative.  M, R, U and V are kept transposed ([value column][k]) so that
+// every fragment is one or two 16-byte LDS reads; K^T and B^T fragments of the state
+// update come from the transposing LDS read.  The next chunk's inputs are loaded into
+// registers while the current one computes.
+template <int DK, int GATE>
+__global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
+  constexpr int SKE = DK + 8;  // bf16 row pitch of Q, K, A, B
+  constexpr int SX = DC + 4;   // fp32 row pitch of the 64 x 64 tiles
+  constexpr int SM = DK + 4;   // fp32 row pitch of M^T
+  constexpr int SVT = DC + 8;  // bf16 row pitch of V^T
+  constexpr int SR = DC + 4;   // fp32 row pitch of R^T and U^T
+  constexpr int RK = DC * DK / 8 / DNT;  // 16-byte pieces of a [64][DK] operand per thread
+  __shared__ __align__(16) bf16 Ql[DC * SKE];
+  __shared__ __align__(16) bf16 Kl[DC * SKE];
+  __shared__ __align__(16) bf16 Al[DC * SKE];
+  __shared__ __align__(16) bf16 Bl[DC * SKE];
+  __shared__ __align__(16) bf16 Vt[DVB * SVT];
+  __shared__ __align__(16) float X1[DC * SX];
+  __shared__ __align__(16) float Tb[DC * SX];
+  __shared__ __align__(16) float Mt[DVB * SM];
+  __shared__ __align__(16) float Rt[DVB * SR];
+  __shared__ __align__(16) float Ut[DVB * SR];
+  __shared__ __align__(16) float gs[DC], eg[DC], egp[DC], et[DC];
+  __shared__ float misc[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lm = lane & 15;
+  const int H = p.H, dv = p.dv, nb = dv / DVB;
+  const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
+  const int n = pair / H, h = pair % H, col0 = jb * DVB;
+  long tok0;
+  int len;
+  if (p.cu_seqlens) {
+    const int s0 = p.cu_seqlens[n], s1 = p.cu_seqlens[n + 1];
+    if (s0 < 0 || s1 < s0 || s1 > p.T) return;  // malformed offsets: leave untouched
+    tok0 = s0;
+    len = s1 - s0;
+  } else {
+    tok0 = (long)n * p.T;
+    len = p.T;
+  }
+  const int nchunks = (len + DC - 1) / DC;
+  const size_t sstate = ((size_t)n * H + h) * DK * dv + col0;
+
+  // fragment loaders: rows of a bf16 operand (exact), rows of an fp32 one (split)
+  auto rowb = [&](const bf16 *X, int pitch, int row) {
+    const bf16 *base = X + row * pitch + 8 * lg;
+    return [=](int k0) { return ld8(base + k0); };
+  };
+  auto rowf = [&](const float *X, int pitch, int row) {
+    const float *base = X + row * pitch + 8 * lg;
+    return [=](int k0) { return split8(ld8(base + k0)); };
+  };
+
+  for (int i = tid; i < DK * DVB; i += DNT) {
+    const int d = i / DVB, j = i % DVB;
+    Mt[j * SM + d] = p.init_state ? p.init_state[sstate + (size_t)d * dv + j] : 0.f;
+  }
+  for (int i = tid; i < DC * SX; i += DNT) Tb[i] = X1[i] = 0.f;  // upper blocks stay zero
+
+  // ---- a chunk's inputs: 16-byte loads into registers one chunk ahead (rows past the
+  // sequence end re-read its last row and are zeroed when staged)
+  u32x4 pq[RK], pk[RK], pa[RK], pb[RK], pv;
+  float pl = 0.f;
+  auto fetch = [&](int cc) {
+    const int last = min(DC, len - cc * DC) - 1;
+    const size_t tbc = (size_t)tok0 + (size_t)cc * DC;
+#pragma unroll
+    for (int u = 0; u < RK; ++u) {
+      const int pc = tid + DNT * u, r = min(pc / (DK / 8), last), g = pc % (DK / 8);
+      const size_t o = ((tbc + r) * H + h) * DK + g * 8;
+      pq[u] = *(const u32x4 *)((const bf16 *)p.q + o);
+      pk[u] = *(const u32x4 *)((const bf16 *)p.k + o);
+      pa[u] = *(const u32x4 *)((const bf16 *)p.a + o);
+      pb[u] = *(const u32x4 *)((const bf16 *)p.b + o);
+    }
+    {
+      const int r = min(tid / 4, last), g = tid % 4;
+      pv = *(const u32x4 *)((const bf16 *)p.v + ((tbc + r) * H + h) * dv + col0 + 8 * g);
+    }
+    if (GATE == GATE_HEAD && tid < DC) pl = p.log_alpha[(tbc + min(tid, last)) * H + h];
+  };
+  if (nchunks > 0) fetch(0);
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int nv = min(DC, len - c * DC);
+    const size_t tb = (size_t)tok0 + (size_t)c * DC;
+    __syncthreads();  // the previous chunk is done with every buffer
+    // ---- stage the inputs; wave 0 forms the decay prefix from its registers
+#pragma unroll
+    for (int u = 0; u < RK; ++u) {
+      opaque(pq[u]);
+      opaque(pk[u]);
+      opaque(pa[u]);
+      opaque(pb[u]);
+      const int pc = tid + DNT * u, r = pc / (DK / 8), g = pc % (DK / 8);
+      if (r >= nv) pq[u] = pk[u] = pa[u] = pb[u] = (u32x4){0u, 0u, 0u, 0u};
+      *(u32x4 *)(Ql + r * SKE + g * 8) = pq[u];
+      *(u32x4 *)(Kl + r * SKE + g * 8) = pk[u];
+      *(u32x4 *)(Al + r * SKE + g * 8) = pa[u];
+      *(u32x4 *)(Bl + r * SKE + g * 8) = pb[u];
+    }
+    {
+      opaque(pv);
+      const int r = tid / 4, g = tid % 4;
+      const bf16x8 v8 = __builtin_bit_cast(bf16x8, pv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(8 * g + e) * SVT + r] = r < nv ? v8[e] : (bf16)0.f;
+    }
+    if (wave == 0) {  // e^G, e^{G_{j-1}}, e^{G_C - G}, e^{G_C}
+      opaque(pl);
+      float g = lane < nv ? pl : 0.f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(g, off);
+        if (lane >= off) g += y;
+      }
+      const float gC = __shfl(g, 63), gp = __shfl_up(g, 1);
+      gs[lane] = g;
+      eg[lane] = __expf(g);
+      egp[lane] = lane == 0 ? 1.f : __expf(gp);
+      et[lane] = __expf(gC - g);
+      if (lane == 0) misc[0] = __expf(gC);
+    }
+    if (c + 1 < nchunks) fetch(c + 1);  // in flight during this chunk's compute
+    __syncthreads();
+    auto e_out = [&](int r, int j) {  // e^{G_r - G_j}, j <= r
+      return j <= r ? (GATE == GATE_HEAD ? __expf(gs[r] - gs[j]) : 1.f) : 0.f;
+    };
+    auto e_in = [&](int j, int i) {  // e^{G_{j-1} - G_i}, i < j
+      return i < j ? (GATE == GATE_HEAD ? __expf((j > 0 ? gs[j - 1] : 0.f) - gs[i]) : 1.f) : 0.f;
+    };
+    // X1 = lower(R C^T * fac): the 10 lower 16x16 tiles, 3/3/2/2 per wave (the upper
+    // ones were zeroed once and are never written)
+    auto gram = [&](const bf16 *R, const bf16 *Cm, auto fac) {
+      for (int t = wave; t < 10; t += 4) {
+        const int mb = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int m0 = 16 * mb, n0 = 16 * (t - mb * (mb + 1) / 2);
+        const f32x4 v = tile_frag<DK>(rowb(R, SKE, m0 + lm), rowb(Cm, SKE, n0 + lm));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = m0 + 4 * lg + u, i = n0 + lm;
+          X1[r * SX + i] = v[u] * fac(r, i);
+        }
+      }
+    };
+    // output tiles of a 64 x 32 product: two per wave
+    auto otile = [&](int q, int &m0, int &n0) {
+      const int t = wave + 4 * q;
+      m0 = (t >> 1) * 16;
+      n0 = (t & 1) * 16;
+    };
+    auto kend = [](int m0) { return m0 < 32 ? 32 : 64; };  // last nonzero column of a lower row block
+    // ---- O = diag(e^G) Q M0 in registers; P_qk into X1
+    f32x4 Oacc[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int m0, n0;
+      otile(q, m0, n0);
+      const f32x4 v = tile_frag<DK>(rowb(Ql, SKE, m0 + lm), rowf(Mt, SM, n0 + lm));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Oacc[q][u] = eg[m0 + 4 * lg + u] * v[u];
+    }
+    gram(Ql, Kl, e_out);
+    __syncthreads();
+    // ---- O += P_qk V
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int m0, n0;
+      otile(q, m0, n0);
+      Oacc[q] += tile_frag<DC>(rowf(X1, SX, m0 + lm), rowb(Vt, SVT, n0 + lm), kend(m0));
+    }
+    __syncthreads();
+    // ---- A_ab into X1, then T = (I - A_ab)^-1 into Tb
+    gram(Al, Bl, e_in);
+    __syncthreads();
+    if (wave == 0) {  // diagonal blocks: lane (lg, lm) solves column lm of block lg
+      const int o = 16 * lg;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float *arow = X1 + (o + r) * SX + o;
+        float acc = r == lm ? 1.f : 0.f;
+#pragma unroll
+        for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
+          const f32x4 a4 = *(const f32x4 *)(arow + 4 * i4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * i4 + e < r) acc += a4[e] * x[4 * i4 + e];
+        }
+        x[r] = acc;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tb[(o + r) * SX + o + lm] = x[r];
+    }
+    __syncthreads();
+    if (wave < 3) {  // off-diagonal blocks, block column b = wave: T[a][b] = T[a][a] sum_k A[a][k] T[k][b]
+      const int b = wave;
+      float *ys = Rt + wave * (16 * 20);  // scratch (R is formed afterwards): y^T, row pitch 20
+      for (int a = b + 1; a < 4; ++a) {
+        f32x4 y = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < DC; k0 += 32) {
+          if (k0 + 32 <= 16 * b || k0 >= 16 * a) continue;  // wave-uniform
+          const int kk = k0 + 8 * lg;                        // this lane's 8 k-slots
+          const bool in = kk >= 16 * b && kk < 16 * a;
+          f32x8 af = ld8(X1 + (16 * a + lm) * SX + kk), bfv;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (!in) af[i] = 0.f;
+            bfv[i] = Tb[(kk + i) * SX + 16 * b + lm];
+          }
+          y = mm(split8(af), split8(bfv), y);
+        }
+        *(f32x4 *)(ys + lm * 20 + 4 * lg) = y;
+        __builtin_amdgcn_wave_barrier();
+        f32x8 tf = ld8(Tb + (16 * a + lm) * SX + 16 * a + 8 * (lg & 1));
+        f32x8 yf = ld8(ys + lm * 20 + 8 * (lg & 1));
+        if (lg >= 2) tf = yf = (f32x8){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const f32x4 z = mm(split8(tf), split8(yf), zero4());
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Tb[(16 * a + 4 * lg + u) * SX + 16 * b + lm] = z[u];
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    __syncthreads();
+    // ---- A_ak into X1; R = diag(e^{G_{j-1}}) A M0 + A_ak V into R^T
+    gram(Al, Kl, e_in);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int m0, n0;
+      otile(q, m0, n0);
+      const f32x4 v = tile_frag<DK>(rowb(Al, SKE, m0 + lm), rowf(Mt, SM, n0 + lm));
+      const f32x4 w = tile_frag<DC>(rowf(X1, SX, m0 + lm), rowb(Vt, SVT, n0 + lm), kend(m0));
+      f32x4 res;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) res[u] = egp[m0 + 4 * lg + u] * v[u] + w[u];
+      *(f32x4 *)(Rt + (n0 + lm) * SR + m0 + 4 * lg) = res;
+    }
+    __syncthreads();
+    // ---- U = T R into U^T
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int m0, n0;
+      otile(q, m0, n0);
+      const f32x4 v = tile_frag<DC>(rowf(Tb, SX, m0 + lm), rowf(Rt, SR, n0 + lm), kend(m0));
+      *(f32x4 *)(Ut + (n0 + lm) * SR + m0 + 4 * lg) = v;
+    }
+    __syncthreads();
+    // ---- P_qb into X1; O += P_qb U; store O
+    gram(Ql, Bl, e_out);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int m0, n0;
+      otile(q, m0, n0);
+      Oacc[q] += tile_frag<DC>(rowf(X1, SX, m0 + lm), rowf(Ut, SR, n0 + lm), kend(m0));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = m0 + 4 * lg + u;
+        if (r < nv) ((bf16 *)p.o)[((tb + r) * H + h) * dv + col0 + n0 + lm] = (bf16)Oacc[q][u];
+      }
+    }
+    // ---- M <- e^{G_C} M + B^T diag(e^{G_C - G}) U + K^T diag(e^{G_C - G}) V   (DK x 32)
+    {
+      constexpr int TPW = (DK / 16) * 2 / 4;  // tiles per wave
+      f32x4 nm[TPW];
+      const float gam = misc[0];
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+        const float *urow = Ut + (n0 + lm) * SR + 8 * lg;
+        const bf16 *vrow = Vt + (n0 + lm) * SVT + 8 * lg;
+        const f32x4 t1 = tile_frag<DC>([&](int k0) { return col_frag(Bl, SKE, k0, m0, lg, lm); },
+                                       [&](int k0) {
+                                         const f32x8 e8 = ld8(et + k0 + 8 * lg);
+                                         return split8(ld8(urow + k0) * e8);
+                                       });
+        const f32x4 t2 = tile_frag<DC>([&](int k0) { return col_frag(Kl, SKE, k0, m0, lg, lm); },
+                                       [&](int k0) {
+                                         const f32x8 e8 = ld8(et + k0 + 8 * lg);
+                                         return split8(widen8(ld8(vrow + k0)) * e8);
+                                       });
+        const f32x4 mo = *(const f32x4 *)(Mt + (n0 + lm) * SM + m0 + 4 * lg);
+        nm[q] = gam * mo + t1 + t2;
+      }
+      __syncthreads();  // every read of the old state is done
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+        *(f32x4 *)(Mt + (n0 + lm) * SM + m0 + 4 * lg) = nm[q];
+      }
+    }
+  }
+  __syncthreads();
+  if (p.final_state)
+    for (int i = tid; i < DK * DVB; i += DNT) {
+      const int d = i / DVB, j = i % DVB;
+      p.final_state[sstate + (size_t)d * dv + j] = Mt[j * SM + d];
+    }
+}
+
 template <typename E, int DK>
 hipError_t launch_dp(const DplrParams &p, int gate, hipStream_t stream) {
   const int blocks = p.N * p.H * (p.dv / DVB);
   if (blocks == 0) return hipSuccess;
-  if (gate == GATE_HEAD)
-    hipLaunchKernelGGL((dplr_fwd_kernel<E, DK, GATE_HEAD>), dim3(blocks), dim3(DNT), 0, stream, p);
-  else if (gate == GATE_NONE)
-    hipLaunchKernelGGL((dplr_fwd_kernel<E, DK, GATE_NONE>), dim3(blocks), dim3(DNT), 0, stream, p);
-  else
-    return hipErrorInvalidValue;
+  if (gate != GATE_HEAD && gate != GATE_NONE) return hipErrorInvalidValue;
+  if constexpr (std::is_same<E, bf16>::value) {
+    if (gate == GATE_HEAD)
+      hipLaunchKernelGGL((dplr_bf16_kernel<DK, GATE_HEAD>), dim3(blocks), dim3(DNT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((dplr_bf16_kernel<DK, GATE_NONE>), dim3(blocks), dim3(DNT), 0, stream, p);
+  } else {
+    if (gate == GATE_HEAD)
+      hipLaunchKernelGGL((dplr_fwd_kernel<E, DK, GATE_HEAD>), dim3(blocks), dim3(DNT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((dplr_fwd_kernel<E, DK, GATE_NONE>), dim3(blocks), dim3(DNT), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

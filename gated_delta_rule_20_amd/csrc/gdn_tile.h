@@ -36,4 +36,62 @@ __device__ __forceinline__ void mfma_mm(int w, int lane, FA a, FB b, EPI epi) {
   }
 }
 
+// ---- bf16 matrix cores on fp32 data: a split into two bf16 terms.
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (both round to nearest even):
+// |x - hi| <= 2^-9 |x| and |x - hi - lo| <= 2^-18 |x|.  A product then takes three bf16
+// MFMAs (lo*hi', hi*lo', hi*hi'; the dropped lo*lo' is below 2^-18 of it), or two when
+// one operand is exactly bf16 already (an input), for a relative error near 2^-17
+// where one bf16 rounding would give 2^-9.  Accumulation is fp32.
+struct Split {
+  bf16x8 hi, lo;
+};
+__device__ __forceinline__ Split split8(const f32x8 &x) {
+  Split s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s.hi[i] = (bf16)x[i];
+    s.lo[i] = (bf16)(x[i] - (float)s.hi[i]);
+  }
+  return s;
+}
+__device__ __forceinline__ f32x8 widen8(const bf16x8 &x) {
+  f32x8 y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = (float)x[i];
+  return y;
+}
+__device__ __forceinline__ f32x4 mm(const bf16x8 &a, const bf16x8 &b, f32x4 c) { return mma(a, b, c); }
+__device__ __forceinline__ f32x4 mm(const bf16x8 &a, const Split &b, f32x4 c) { return mma(a, b.hi, mma(a, b.lo, c)); }
+__device__ __forceinline__ f32x4 mm(const Split &a, const bf16x8 &b, f32x4 c) { return mma(a.hi, b, mma(a.lo, b, c)); }
+__device__ __forceinline__ f32x4 mm(const Split &a, const Split &b, f32x4 c) {
+  return mma(a.hi, b.hi, mma(a.hi, b.lo, mma(a.lo, b.hi, c)));
+}
+// One 16x16 tile of C = A B from fragment loaders: fa(k0) gives this lane's A
+// fragment (its row, k = k0 + 8 lg .. + 7), fb(k0) its B fragment (its column, the
+// same k), each a bf16x8 (exact) or a Split.  32-deep steps from k0 = kend on are
+// skipped (known zeros of a triangular operand); kend must be wave-uniform.
+template <int K, class FA, class FB>
+__device__ __forceinline__ f32x4 tile_frag(FA fa, FB fb, int kend = K) {
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32)
+    if (k0 < kend) acc = mm(fa(k0), fb(k0), acc);
+  return acc;
+}
+// Four bf16 of one column of a row-major bf16 matrix per lane, through the gfx950
+// transposing LDS read: within each 16-lane group, lane L receives element j
+// (j = 0..3) from the 8 bytes that lane 4j + L/4 addressed, at position L % 4.
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16 *p) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)p);
+  return __builtin_bit_cast(bf16x4, v);
+}
+// The 8-deep column fragment X[k0 + 8 lg + j][c0 + lm], j = 0..7, of a row-major bf16
+// matrix X in LDS with row pitch `pitch` (elements; rows 8-byte aligned).
+__device__ __forceinline__ bf16x8 col_frag(const bf16 *X, int pitch, int k0, int c0, int lg, int lm) {
+  const bf16 *p0 = X + (k0 + 8 * lg + (lm >> 2)) * pitch + c0 + 4 * (lm & 3);
+  const bf16x4 a = lds_tr4(p0), b = lds_tr4(p0 + 4 * pitch);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 }  // namespace gdn
