@@ -95,7 +95,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     const int d = i / BVB, j = i % BVB;
     dM[d * SV + j] = p.dfinal ? p.dfinal[sstate + (size_t)d * dv + j] : 0.f;
   }
-  for (int i = tid; i < BC * ST; i += BNT) Tb[i] = 0.f;  // T's upper blocks stay zero
+  for (int i = tid; i < BC * ST; i += BNT) Tb[i] = Pl[i] = 0.f;  // upper blocks stay zero
 
   // ---- a chunk's inputs: 16-byte loads into registers one chunk ahead (rows past the
   // sequence end re-read its last row and are zeroed when staged)
@@ -196,11 +196,18 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       return i <= r ? (GATE == GATE_HEAD ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
     };
     {
+      // the ten lower tiles, 3/3/2/2 per wave (the upper ones were zeroed once)
       const int lg = lane >> 4, lm = lane & 15;
-      for (int t = wave; t < 16; t += 4) {
-        const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
-        f32x4 av = zero4(), pv4 = zero4();
-        if (n0 <= m0) {
+      for (int t = wave; t < 10; t += 4) {
+        const int mb = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int m0 = 16 * mb, n0 = 16 * (t - mb * (mb + 1) / 2);
+        f32x4 av, pv4;
+        if constexpr (std::is_same<E, bf16>::value) {
+          const E *kr = Kl + (m0 + lm) * SKE + 8 * lg, *qr = Ql + (m0 + lm) * SKE + 8 * lg;
+          const E *kc = Kl + (n0 + lm) * SKE + 8 * lg;
+          av = tile_frag<DK>([&](int k0) { return ld8(kr + k0); }, [&](int k0) { return ld8(kc + k0); });
+          pv4 = tile_frag<DK>([&](int k0) { return ld8(qr + k0); }, [&](int k0) { return ld8(kc + k0); });
+        } else {
           av = tile<DK>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
           pv4 = tile<DK>(m0, n0, lg, lm, Q_, [&](int d, int i) { return K_(i, d); });
         }
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       for (int r = 0; r < 16; ++r) Tb[(o + r) * ST + o + lm] = x[r];
     } else {
       // V - Kt M0 into Xl (64 x 32, three waves)
-      mfma_mm<BC, BVB, DK, 3>(wave - 1, lane, K_, [&](int d, int j) { return M0[d * SV + j]; },
+      mm_g<E, BC, BVB, DK, 3, true, false>(wave - 1, lane, K_, [&](int d, int j) { return M0[d * SV + j]; },
                               [&](int r, int j, f32x4 v) {
 #pragma unroll
                                 for (int u = 0; u < 4; ++u) Xl[(r + u) * SV + j] = Vb[(r + u) * SV + j] - eg[r + u] * v[u];
@@ -241,12 +248,12 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       const int lg = lane >> 4, lm = lane & 15, b = wave;
       float *ys = Ys + wave * (16 * 17);
       for (int a = b + 1; a < 4; ++a) {
-        const f32x4 y = tile<BC>(16 * a, 16 * b, lg, lm,
+        const f32x4 y = tile_g<E, BC, false, false>(16 * a, 16 * b, lg, lm,
                                  [&](int r, int k) { return (k >= 16 * b && k < 16 * a) ? Tl[r * ST + k] : 0.f; },
-                                 [&](int k, int col) { return Tb[k * ST + col]; });
+                                 [&](int k, int col) { return Tb[k * ST + col]; }, 16 * b, 16 * a);
 #pragma unroll
         for (int u = 0; u < 4; ++u) ys[(4 * lg + u) * 17 + lm] = y[u];
-        const f32x4 z = tile<32>(16 * a, 16 * b, lg, lm,
+        const f32x4 z = tile_g<E, 32, false, false>(16 * a, 16 * b, lg, lm,
                                  [&](int r, int k) { return k < 16 ? Tb[r * ST + 16 * a + k] : 0.f; },
                                  [&](int k, int col) { return k < 16 ? ys[k * 17 + col - 16 * b] : 0.f; });
 #pragma unroll
@@ -261,11 +268,12 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       const int lg = lane >> 4, lm = lane & 15;
       for (int t = wave; t < 8; t += 4) {
         const int m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
-        const f32x4 dd = tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Tb[r * ST + i]; },
-                                  [&](int i, int j) { return bs[i] * Xl[i * SV + j]; });
-        const f32x4 d1 = tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Pl[i * ST + r]; },
-                                  [&](int i, int j) { return dOb[i * SV + j]; });
-        const f32x4 d2 = tile<DK>(m0, n0, lg, lm, K_, [&](int d, int j) { return dM[d * SV + j]; });
+        const f32x4 dd = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int i) { return Tb[r * ST + i]; },
+                                                     [&](int i, int j) { return bs[i] * Xl[i * SV + j]; }, 0, m0 + 16);
+        const f32x4 d1 = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int r, int i) { return Pl[i * ST + r]; },
+                                                    [&](int i, int j) { return dOb[i * SV + j]; }, m0);
+        const f32x4 d2 =
+            tile_g<E, DK, true, false>(m0, n0, lg, lm, K_, [&](int d, int j) { return dM[d * SV + j]; });
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = m0 + 4 * lg + u, j = n0 + lm;
@@ -276,7 +284,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     }
     __syncthreads();
     // ---- Y = T^T dDelta
-    mfma_mm<BC, BVB, BC, 4>(wave, lane, [&](int r, int i) { return Tb[i * ST + r]; },
+    mm_g<E, BC, BVB, BC, 4, false, false>(wave, lane, [&](int r, int i) { return Tb[i * ST + r]; },
                             [&](int i, int j) { return dDl[i * SV + j]; }, [&](int r, int j, f32x4 v) {
 #pragma unroll
                               for (int u = 0; u < 4; ++u) Yl[(r + u) * SV + j] = v[u];
@@ -289,12 +297,12 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     }
     float *pr = p.part + ((slot * H + h) * nb + jb) * (size_t)PT::SIZE;
     // ---- dP = incl(dO Delta^T), dT = dDelta (diag(beta) X)^T  (partial over value columns)
-    mfma_mm<BC, BC, BVB, 4>(wave, lane, [&](int r, int j) { return dOb[r * SV + j]; },
+    mm_g<E, BC, BC, BVB, 4, true, false>(wave, lane, [&](int r, int j) { return dOb[r * SV + j]; },
                             [&](int j, int i) { return Dl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
 #pragma unroll
                               for (int u = 0; u < 4; ++u) pr[PT::DP + (r + u) * BC + i] = i <= r + u ? v[u] : 0.f;
                             });
-    mfma_mm<BC, BC, BVB, 4>(wave, lane, [&](int r, int j) { return dDl[r * SV + j]; },
+    mm_g<E, BC, BC, BVB, 4, false, false>(wave, lane, [&](int r, int j) { return dDl[r * SV + j]; },
                             [&](int j, int i) { return bs[i] * Xl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
 #pragma unroll
                               for (int u = 0; u < 4; ++u) pr[PT::DT + (r + u) * BC + i] = v[u];
@@ -307,11 +315,11 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       const int m0 = 16 * wave;
       float gq[4] = {0.f, 0.f, 0.f, 0.f}, gk[4] = {0.f, 0.f, 0.f, 0.f}, gz[4] = {0.f, 0.f, 0.f, 0.f};
       for (int n0 = 0; n0 < DK; n0 += 16) {
-        const f32x4 w = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return dOb[r * SV + j]; },
+        const f32x4 w = tile_g<E, BVB, true, false>(m0, n0, lg, lm, [&](int r, int j) { return dOb[r * SV + j]; },
                                   [&](int j, int d) { return M0[d * SV + j]; });
-        const f32x4 uu = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Yl[r * SV + j]; },
+        const f32x4 uu = tile_g<E, BVB, false, false>(m0, n0, lg, lm, [&](int r, int j) { return Yl[r * SV + j]; },
                                    [&](int j, int d) { return M0[d * SV + j]; });
-        const f32x4 z = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Dl[r * SV + j]; },
+        const f32x4 z = tile_g<E, BVB, false, false>(m0, n0, lg, lm, [&](int r, int j) { return Dl[r * SV + j]; },
                                   [&](int j, int d) { return dM[d * SV + j]; });
         const int d = n0 + lm;
 #pragma unroll
@@ -369,9 +377,9 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
       for (int q = 0; q < TILES / 4; ++q) {
         const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
-        const f32x4 n1 = tile<BC>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * Q_(r, d); },
+        const f32x4 n1 = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * Q_(r, d); },
                                   [&](int r, int j) { return dOb[r * SV + j]; });
-        const f32x4 n2 = tile<BC>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * bs[r] * K_(r, d); },
+        const f32x4 n2 = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * bs[r] * K_(r, d); },
                                   [&](int r, int j) { return Yl[r * SV + j]; });
 #pragma unroll
         for (int u = 0; u < 4; ++u) nm[q][u] = gam * dM[(m0 + 4 * lg + u) * SV + n0 + lm] + n1[u] - n2[u];
@@ -485,20 +493,26 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     gs[lane] = g;
   }
   __syncthreads();
-  // S = K K^T, R = Q K^T;  Z = dT T^T
-  mfma_mm<BC, BC, DK, 4>(wave, lane, K_, [&](int d, int i) { return K_(i, d); }, [&](int r, int i, f32x4 v) {
+  // S = K K^T, R = Q K^T (only their lower tiles are used: the upper ones are set to
+  // zero);  Z = dT T^T
+  for (int t = wave; t < 16; t += 4) {
+    const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
+    f32x4 sv = zero4(), rv = zero4();
+    if (n0 <= m0) {
+      sv = tile_g<E, DK, true, true>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
+      rv = tile_g<E, DK, true, true>(m0, n0, lg, lm, Q_, [&](int d, int i) { return K_(i, d); });
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) Sl[(r + u) * ST + i] = v[u];
-  });
-  mfma_mm<BC, BC, DK, 4>(wave, lane, Q_, [&](int d, int i) { return K_(i, d); }, [&](int r, int i, f32x4 v) {
+    for (int u = 0; u < 4; ++u) {
+      Sl[(m0 + 4 * lg + u) * ST + n0 + lm] = sv[u];
+      Rl[(m0 + 4 * lg + u) * ST + n0 + lm] = rv[u];
+    }
+    // T^T is upper triangular: T[i][k] = 0 for k > i
+    const f32x4 zv = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int k) { return Dt[r * ST + k]; },
+                                                 [&](int k, int i) { return Tl[i * ST + k]; }, 0, n0 + 16);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) Rl[(r + u) * ST + i] = v[u];
-  });
-  mfma_mm<BC, BC, BC, 4>(wave, lane, [&](int r, int k) { return Dt[r * ST + k]; },
-                         [&](int k, int i) { return Tl[i * ST + k]; }, [&](int r, int i, f32x4 v) {
-#pragma unroll
-                           for (int u = 0; u < 4; ++u) Zl[(r + u) * ST + i] = v[u];
-                         });
+    for (int u = 0; u < 4; ++u) Zl[(m0 + 4 * lg + u) * ST + n0 + lm] = zv[u];
+  }
   __syncthreads();
   // dA = -strict(T^T Z), then per entry: Gamma, Ea = dA beta_r Gamma, Ep = dP Gamma,
   // wG = (dA beta_r S + dP R) Gamma, and dA S Gamma (for dbeta).  Each wave's 4 tiles
@@ -508,8 +522,10 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int t = wave + 4 * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
-      da[q] = tile<BC>(m0, n0, lg, lm, [&](int r, int k) { return Tl[k * ST + r]; },
-                       [&](int k, int i) { return Zl[k * ST + i]; });
+      da[q] = zero4();  // only the strictly lower part is kept
+      if (n0 <= m0)
+        da[q] = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int k) { return Tl[k * ST + r]; },
+                                            [&](int k, int i) { return Zl[k * ST + i]; }, m0);
     }
     __syncthreads();
 #pragma unroll
@@ -567,11 +583,13 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
         pq_[u] += pr0[(size_t)b * PT::SIZE + PT::DQ + r * DK + d];
         pk_[u] += pr0[(size_t)b * PT::SIZE + PT::DKO + r * DK + d];
       }
-    const f32x4 q_ = tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Pl[r * ST + i]; },
-                              [&](int i, int d) { return K_(i, d); });
-    f32x4 k_ = tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Zl[r * ST + i] + Zl[i * ST + r]; },
-                        [&](int i, int d) { return K_(i, d); });
-    k_ += tile<BC>(m0, n0, lg, lm, [&](int r, int i) { return Pl[i * ST + r]; }, [&](int i, int d) { return Q_(i, d); });
+    const f32x4 q_ = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int r, int i) { return Pl[r * ST + i]; },
+                                                [&](int i, int d) { return K_(i, d); }, 0, m0 + 16);
+    f32x4 k_ = tile_g<E, BC, false, true>(m0, n0, lg, lm,
+                                          [&](int r, int i) { return Zl[r * ST + i] + Zl[i * ST + r]; },
+                                          [&](int i, int d) { return K_(i, d); });
+    k_ += tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int r, int i) { return Pl[i * ST + r]; },
+                                     [&](int i, int d) { return Q_(i, d); }, m0);
     const int d = n0 + lm;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {

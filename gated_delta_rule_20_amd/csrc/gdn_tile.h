@@ -1,6 +1,8 @@
 // gdn_tile.h -- 16x16 fp32 matrix-core tiles with gathered operands (backward and the
 // diagonal-plus-low-rank forward).
 #pragma once
+#include <type_traits>
+
 #include "gdn_common.h"
 
 namespace gdn {
@@ -77,6 +79,54 @@ __device__ __forceinline__ f32x4 tile_frag(FA fa, FB fb, int kend = K) {
   for (int k0 = 0; k0 < K; k0 += 32)
     if (k0 < kend) acc = mm(fa(k0), fb(k0), acc);
   return acc;
+}
+__device__ __forceinline__ bf16x8 to_bf8(const f32x8 &x) {
+  bf16x8 y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = (bf16)x[i];
+  return y;
+}
+// One 16x16 tile of C = A B with operands gathered through a(m, k) and b(k, n), as
+// `tile`: on the fp32 matrix cores when E is float; when E is bf16, on the bf16 matrix
+// cores, an operand whose values are bf16 inputs (XA, XB) taken exactly and any other
+// as a Split pair.  On the bf16 path 32-deep steps outside [kbeg, kend) (known zeros of
+// a triangular operand; wave-uniform bounds) are skipped.
+template <typename E, int K, bool XA, bool XB, class FA, class FB>
+__device__ __forceinline__ f32x4 tile_g(int m0, int n0, int lg, int lm, FA a, FB b, int kbeg = 0, int kend = K) {
+  if constexpr (!std::is_same<E, bf16>::value) {
+    return tile<K>(m0, n0, lg, lm, a, b);
+  } else {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      if (k0 + 32 <= kbeg || k0 >= kend) continue;
+      f32x8 af, bv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        af[i] = a(m0 + lm, k0 + 8 * lg + i);
+        bv[i] = b(k0 + 8 * lg + i, n0 + lm);
+      }
+      if constexpr (XA && XB)
+        acc = mm(to_bf8(af), to_bf8(bv), acc);
+      else if constexpr (XA)
+        acc = mm(to_bf8(af), split8(bv), acc);
+      else if constexpr (XB)
+        acc = mm(split8(af), to_bf8(bv), acc);
+      else
+        acc = mm(split8(af), split8(bv), acc);
+    }
+    return acc;
+  }
+}
+// Every 16x16 tile of an M x N product through tile_g, spread over NW waves (as mfma_mm).
+template <typename E, int M, int N, int K, int NW, bool XA, bool XB, class FA, class FB, class EPI>
+__device__ __forceinline__ void mm_g(int w, int lane, FA a, FB b, EPI epi) {
+  const int lg = lane >> 4, lm = lane & 15;
+  constexpr int TN = N / 16, TILES = (M / 16) * TN;
+  for (int t = w; t < TILES; t += NW) {
+    const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+    epi(m0 + 4 * lg, n0 + lm, tile_g<E, K, XA, XB>(m0, n0, lg, lm, a, b));
+  }
 }
 // Four bf16 of one column of a row-major bf16 matrix per lane, through the gfx950
 // transposing LDS read: within each 16-lane group, lane L receives element j
