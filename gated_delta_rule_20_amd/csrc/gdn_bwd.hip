@@ -37,9 +37,11 @@ namespace {
 constexpr int BC = 64;    // chunk length
 constexpr int BNT = 256;  // threads per workgroup
 constexpr int BVB = 32;   // value columns per workgroup of the reverse-state kernel
-constexpr int SV = BVB + 1, ST = BC + 1;  // fp32 row strides (padded)
+constexpr int SV = BVB + 4, ST = BC + 1;  // fp32 row strides (padded; SV rows 16-byte aligned)
 
-// floats of one partial record (per chunk slot, head and value block)
+// floats of one partial record (per chunk slot, head and value block); dP, dT (64 x 64)
+// and dQ, dK (64 x d_k) are stored transposed, [column][row], so that a lane's four
+// rows of a matrix-core tile are one 16-byte store and one 16-byte load
 template <int DK> struct Part {
   static constexpr int DP = 0, DT = BC * BC, DQ = 2 * BC * BC, DKO = DQ + BC * DK, DG = DKO + BC * DK,
                        DB = DG + BC, GC = DB + BC, SIZE = GC + BC;
@@ -70,9 +72,15 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
   typedef Part<DK> PT;
   __shared__ __align__(16) E Kl[BC * SKE];
   __shared__ __align__(16) E Ql[BC * SKE];
-  __shared__ float Vb[BC * SV], dOb[BC * SV], M0[DK * SV], dM[DK * SV];
-  __shared__ float Tl[BC * ST], Pl[BC * ST], Tb[BC * ST];
-  __shared__ float Xl[BC * SV], dDl[BC * SV];
+  __shared__ __align__(16) float Vb[BC * SV];
+  __shared__ __align__(16) float dOb[BC * SV];
+  __shared__ __align__(16) float M0[DK * SV];
+  __shared__ __align__(16) float dM[DK * SV];
+  __shared__ __align__(16) float Tl[BC * ST];
+  __shared__ __align__(16) float Pl[BC * ST];
+  __shared__ __align__(16) float Tb[BC * ST];
+  __shared__ __align__(16) float Xl[BC * SV];
+  __shared__ __align__(16) float dDl[BC * SV];
   __shared__ float bs[BC], gs[BC], eg[BC], et[BC], red[BC], wsum[4], misc[4];
   float *const Yl = Vb;   // V is dead once X is formed
   float *const Dl = Tl;   // A is dead once T is formed
@@ -297,16 +305,36 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     }
     float *pr = p.part + ((slot * H + h) * nb + jb) * (size_t)PT::SIZE;
     // ---- dP = incl(dO Delta^T), dT = dDelta (diag(beta) X)^T  (partial over value columns)
-    mm_g<E, BC, BC, BVB, 4, true, false>(wave, lane, [&](int r, int j) { return dOb[r * SV + j]; },
-                            [&](int j, int i) { return Dl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
+    if constexpr (std::is_same<E, bf16>::value) {
+      // these contract over the 32 value columns: every fragment is a row piece
+      const int lg = lane >> 4, lm = lane & 15;
+      for (int t = wave; t < 16; t += 4) {
+        const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16, i = n0 + lm;
+        f32x4 vp = zero4();
+        if (n0 <= m0)
+          vp = tile_frag<BVB>([&](int k0) { return to_bf8(ld8(dOb + (m0 + lm) * SV + 8 * lg + k0)); },
+                              [&](int k0) { return split8(ld8(Dl + i * SV + 8 * lg + k0)); });
+        const float bi = bs[i];
+        const f32x4 vt = tile_frag<BVB>([&](int k0) { return split8(ld8(dDl + (m0 + lm) * SV + 8 * lg + k0)); },
+                                        [&](int k0) { return split8(ld8(Xl + i * SV + 8 * lg + k0) * bi); });
 #pragma unroll
-                              for (int u = 0; u < 4; ++u) pr[PT::DP + (r + u) * BC + i] = i <= r + u ? v[u] : 0.f;
-                            });
-    mm_g<E, BC, BC, BVB, 4, false, false>(wave, lane, [&](int r, int j) { return dDl[r * SV + j]; },
-                            [&](int j, int i) { return bs[i] * Xl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
+        for (int u = 0; u < 4; ++u)
+          if (i > m0 + 4 * lg + u) vp[u] = 0.f;
+        *(f32x4 *)(pr + PT::DP + i * BC + m0 + 4 * lg) = vp;
+        *(f32x4 *)(pr + PT::DT + i * BC + m0 + 4 * lg) = vt;
+      }
+    } else {
+      mm_g<E, BC, BC, BVB, 4, true, false>(wave, lane, [&](int r, int j) { return dOb[r * SV + j]; },
+                              [&](int j, int i) { return Dl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
 #pragma unroll
-                              for (int u = 0; u < 4; ++u) pr[PT::DT + (r + u) * BC + i] = v[u];
-                            });
+                                for (int u = 0; u < 4; ++u) pr[PT::DP + i * BC + r + u] = i <= r + u ? v[u] : 0.f;
+                              });
+      mm_g<E, BC, BC, BVB, 4, false, false>(wave, lane, [&](int r, int j) { return dDl[r * SV + j]; },
+                              [&](int j, int i) { return bs[i] * Xl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) pr[PT::DT + i * BC + r + u] = v[u];
+                              });
+    }
     // ---- dQ = e^G dO M0^T, dK = -e^G beta Y M0^T + e^{G_C - G} Delta dM^T, and the rows of
     // dG: e^G (dO M0^T).Q - e^G beta (Y M0^T).K - e^{G_C - G} (Delta dM^T).K.  A wave takes
     // whole 16-row blocks (all DK columns), so its row sums stay in the wave.
@@ -314,24 +342,45 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       const int lg = lane >> 4, lm = lane & 15;
       const int m0 = 16 * wave;
       float gq[4] = {0.f, 0.f, 0.f, 0.f}, gk[4] = {0.f, 0.f, 0.f, 0.f}, gz[4] = {0.f, 0.f, 0.f, 0.f};
+      // this wave's rows of dO, Y and Delta as A fragments (the contraction is over the
+      // 32 value columns: one 32-deep step)
+      [[maybe_unused]] bf16x8 fdo;
+      [[maybe_unused]] Split fy, fd;
+      if constexpr (std::is_same<E, bf16>::value) {
+        fdo = to_bf8(ld8(dOb + (m0 + lm) * SV + 8 * lg));
+        fy = split8(ld8(Yl + (m0 + lm) * SV + 8 * lg));
+        fd = split8(ld8(Dl + (m0 + lm) * SV + 8 * lg));
+      }
       for (int n0 = 0; n0 < DK; n0 += 16) {
-        const f32x4 w = tile_g<E, BVB, true, false>(m0, n0, lg, lm, [&](int r, int j) { return dOb[r * SV + j]; },
-                                  [&](int j, int d) { return M0[d * SV + j]; });
-        const f32x4 uu = tile_g<E, BVB, false, false>(m0, n0, lg, lm, [&](int r, int j) { return Yl[r * SV + j]; },
-                                   [&](int j, int d) { return M0[d * SV + j]; });
-        const f32x4 z = tile_g<E, BVB, false, false>(m0, n0, lg, lm, [&](int r, int j) { return Dl[r * SV + j]; },
-                                  [&](int j, int d) { return dM[d * SV + j]; });
+        f32x4 w, uu, z;
+        if constexpr (std::is_same<E, bf16>::value) {
+          const Split fm = split8(ld8(M0 + (n0 + lm) * SV + 8 * lg));
+          const Split fdm = split8(ld8(dM + (n0 + lm) * SV + 8 * lg));
+          w = mm(fdo, fm, zero4());
+          uu = mm(fy, fm, zero4());
+          z = mm(fd, fdm, zero4());
+        } else {
+          w = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return dOb[r * SV + j]; },
+                        [&](int j, int d) { return M0[d * SV + j]; });
+          uu = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Yl[r * SV + j]; },
+                         [&](int j, int d) { return M0[d * SV + j]; });
+          z = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Dl[r * SV + j]; },
+                        [&](int j, int d) { return dM[d * SV + j]; });
+        }
         const int d = n0 + lm;
+        f32x4 sq, sk;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = m0 + 4 * lg + u;
           const float qv = Q_(r, d), kv = K_(r, d);
-          pr[PT::DQ + r * DK + d] = eg[r] * w[u];
-          pr[PT::DKO + r * DK + d] = -eg[r] * bs[r] * uu[u] + et[r] * z[u];
+          sq[u] = eg[r] * w[u];
+          sk[u] = -eg[r] * bs[r] * uu[u] + et[r] * z[u];
           gq[u] += w[u] * qv;
           gk[u] += uu[u] * kv;
           gz[u] += z[u] * kv;
         }
+        *(f32x4 *)(pr + PT::DQ + d * BC + m0 + 4 * lg) = sq;
+        *(f32x4 *)(pr + PT::DKO + d * BC + m0 + 4 * lg) = sk;
       }
       // a row's columns are spread over the 16 lanes lm of its lane group
 #pragma unroll
@@ -451,6 +500,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   const float *tm = p.tmat + ((size_t)slot * H + h) * BC * BC;
 #pragma unroll
   for (int u = 0; u < BC * BC / 4 / BNT; ++u) {
+    // T is row-major; the partials are stored transposed (column i, rows r0 .. r0+3)
     const int i4 = 4 * (tid + BNT * u), r = i4 / BC, col = i4 % BC;
     f32x4 sp = zero4(), st = zero4();
     for (int b = 0; b < nb; ++b) {
@@ -460,8 +510,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     const f32x4 tv = *(const f32x4 *)(tm + i4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      Pl[r * ST + col + e] = sp[e];
-      Dt[r * ST + col + e] = st[e];
+      Pl[(col + e) * ST + r] = sp[e];
+      Dt[(col + e) * ST + r] = st[e];
       Tl[r * ST + col + e] = tv[e];
     }
   }
@@ -575,14 +625,12 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   // tile are loaded before its products, so the loads overlap them
   for (int t = wave; t < (DK / 16) * 4; t += 4) {
     const int m0 = (t / (DK / 16)) * 16, n0 = (t % (DK / 16)) * 16;
-    float pq_[4] = {0.f, 0.f, 0.f, 0.f}, pk_[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int b = 0; b < nb; ++b)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = m0 + 4 * lg + u, d = n0 + lm;
-        pq_[u] += pr0[(size_t)b * PT::SIZE + PT::DQ + r * DK + d];
-        pk_[u] += pr0[(size_t)b * PT::SIZE + PT::DKO + r * DK + d];
-      }
+    f32x4 pq_ = zero4(), pk_ = zero4();  // partials stored [d][r]: this lane's 4 rows are contiguous
+    for (int b = 0; b < nb; ++b) {
+      const size_t o = (size_t)b * PT::SIZE + (size_t)(n0 + lm) * BC + m0 + 4 * lg;
+      pq_ += *(const f32x4 *)(pr0 + PT::DQ + o);
+      pk_ += *(const f32x4 *)(pr0 + PT::DKO + o);
+    }
     const f32x4 q_ = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int r, int i) { return Pl[r * ST + i]; },
                                                 [&](int i, int d) { return K_(i, d); }, 0, m0 + 16);
     f32x4 k_ = tile_g<E, BC, false, true>(m0, n0, lg, lm,
