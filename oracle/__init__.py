@@ -12,8 +12,9 @@ Parity status: every function here is pinned.  ``fwd`` and ``step`` by
 gradient step, exact rational fixtures under ``tests/golden/`` and planted-mistake
 checks); ``decode_pool`` by ``tests/test_oracle_decode.py`` (against ``fwd`` over
 the same tokens and over every stored prefix, chained and speculative calls); ``bwd``
-by ``tests/test_oracle_bwd.py`` (central finite differences of ``fwd`` and torch
-autograd of the recurrence in fp64); ``fwd_dplr`` by ``tests/test_oracle_dplr.py``
+by ``tests/test_oracle_bwd.py`` and, for the additive write,
+``tests/test_oracle_bwd_additive.py`` (central finite differences of ``fwd`` and torch
+autograd of the recurrence in fp64, planted mutants); ``fwd_dplr`` by ``tests/test_oracle_dplr.py``
 (reduces exactly to the delta rule and to the additive write, and equals the
 product of the dense transition matrices); the
 additive write (``write="add"``) and the constant per-head gate by
@@ -69,7 +70,7 @@ def _declare(lib):
                                 ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp]
     lib.oracle_bwd.restype = ctypes.c_int
     lib.oracle_bwd.argtypes = [ctypes.c_int, ip, ip, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                               dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+                               ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
     lib.oracle_fwd_dplr.restype = ctypes.c_int
     lib.oracle_fwd_dplr.argtypes = [ctypes.c_int, ip, ip, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
@@ -145,13 +146,14 @@ def fwd(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None, gate
 
 
 def bwd(q, k, v, beta, log_alpha, initial_state, dout, dfinal=None, cu_seqlens=None, gate=None,
-        nthreads: int = 0, lib=None):
-    """Gradients of the delta-rule recurrence (no gate, one decay per (token, head), or
-    one constant decay per head [H]) with respect to q, k, v, beta, log_alpha and the
-    initial state, given dout [B,T,H,d_v] (the gradient of o) and dfinal None |
-    [N,H,d_k,d_v] (the gradient of the final state).  Shapes as for ``fwd``.
-    Returns (dq, dk, dv, dbeta, dlog_alpha or None, dinit [N,H,d_k,d_v]) in fp64; for
-    the constant gate dlog_alpha is [H] (the per-token gradients summed)."""
+        nthreads: int = 0, lib=None, write: str = "delta"):
+    """Gradients of the recurrence (the delta write, or the additive write with beta
+    None; no gate, one decay per (token, head), or one constant decay per head [H]) with
+    respect to q, k, v, beta, log_alpha and the initial state, given dout [B,T,H,d_v]
+    (the gradient of o) and dfinal None | [N,H,d_k,d_v] (the gradient of the final
+    state).  Shapes as for ``fwd``.  Returns (dq, dk, dv, dbeta or None, dlog_alpha or
+    None, dinit [N,H,d_k,d_v]) in fp64; for the constant gate dlog_alpha is [H] (the
+    per-token gradients summed)."""
     q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
     log_alpha, initial_state, dout, dfinal = _f64(log_alpha), _f64(initial_state), _f64(dout), _f64(dfinal)
     B, T, H, dk = q.shape
@@ -169,13 +171,14 @@ def bwd(q, k, v, beta, log_alpha, initial_state, dout, dfinal=None, cu_seqlens=N
         lens = np.full(B, T, dtype=np.int64)
     N = len(start)
     dq, dk_ = np.zeros_like(q), np.zeros_like(k)
-    dv_, db = np.zeros_like(v), np.zeros_like(beta)
+    dv_ = np.zeros_like(v)
+    db = None if write == "add" else np.zeros_like(beta)
     dla = np.zeros((B, T, H)) if gate == "head" else None
     dinit = np.zeros((N, H, dk, dv))
     lib = lib or load()
     rc = lib.oracle_bwd(N, start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                         lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv, GATES[gate],
-                        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(initial_state),
+                        WRITES[write], _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(initial_state),
                         _ptr(dout), _ptr(dfinal), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(db), _ptr(dla),
                         _ptr(dinit), int(nthreads))
     if rc != 0:

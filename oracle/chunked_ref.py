@@ -112,8 +112,9 @@ def fwd(q, k, v, beta, log_alpha=None, initial_state=None, chunk: int = 64):
     return o, fs
 
 
-def chunk_step_bwd(q, k, v, beta, g, M0, dO, dM):
-    """Gradients of one chunk of the scalar-gated (or ungated: g = 0) delta rule.
+def chunk_step_bwd(q, k, v, beta, g, M0, dO, dM, write="delta"):
+    """Gradients of one chunk of the scalar-gated (or ungated: g = 0) delta rule, or of
+    the additive write (write="add", beta None: Delta = V, no A or T, dbeta None).
 
     q,k [C,dk], v [C,dv], beta [C], g [C] (log decay per position), M0 [dk,dv] the
     state entering the chunk, dO [C,dv] the gradient of O and dM [dk,dv] the gradient
@@ -135,6 +136,8 @@ def chunk_step_bwd(q, k, v, beta, g, M0, dO, dM):
     gC = G[-1]
     Gam = np.where(incl, np.exp(np.where(incl, G[:, None] - G[None, :], 0.0)), 0.0)
     S, R = k @ k.T, q @ k.T
+    if write == "add":
+        return _chunk_step_bwd_add(q, k, v, G, Gam, R, M0, dO, dM)
     A = np.where(strict, beta[:, None] * S * Gam, 0.0)
     T = forward_substitution_inverse(A)
     eG, eT, gam = np.exp(G), np.exp(gC - G), np.exp(gC)
@@ -179,14 +182,45 @@ def chunk_step_bwd(q, k, v, beta, g, M0, dO, dM):
     return dq, dk, dv, dbeta, dg, dM0
 
 
-def chunked_bwd(q, k, v, beta, log_alpha, M0, dO, dMT, C=64):
-    """Gradients over one sequence by chunks: q,k [T,dk], v [T,dv], beta [T],
-    log_alpha None | [T], M0 [dk,dv], dO [T,dv], dMT None | [dk,dv].  The chunk
-    states are recomputed forward, then the chunks are walked in reverse.  A partial
-    last chunk is padded with zero rows (beta = 0, log alpha = 0)."""
+def _chunk_step_bwd_add(q, k, v, G, Gam, R, M0, dO, dM):
+    """The additive write's chunk: O = Qt M0 + P V, M_C = gam M0 + Khat^T V (Delta = V).
+    Reverse mode:
+      dV = P^T dO + Khat dM,  dM0 = Qt^T dO + gam dM,
+      dP = dO V^T on the inclusive lower part,  dQt = dO M0^T,  dKhat = V dM^T,
+    then P = incl(Q K^T * Gamma), Qt, Khat and gam as for the delta rule."""
+    C = q.shape[0]
+    incl = np.tril(np.ones((C, C), dtype=bool), 0)
+    gC = G[-1]
+    eG, eT, gam = np.exp(G), np.exp(gC - G), np.exp(gC)
+    Qt, Kh = eG[:, None] * q, eT[:, None] * k
+    P = np.where(incl, R * Gam, 0.0)
+    dv = P.T @ dO + Kh @ dM
+    dM0 = Qt.T @ dO + gam * dM
+    dP = np.where(incl, dO @ v.T, 0.0)
+    dQt = dO @ M0.T
+    dKh = v @ dM.T
+    dgam = np.sum(M0 * dM)
+    Ep = dP * Gam
+    dq = Ep @ k + eG[:, None] * dQt
+    dk = Ep.T @ q + eT[:, None] * dKh
+    wG = dP * R * Gam
+    dG = wG.sum(axis=1) - wG.sum(axis=0)
+    dG = dG + np.sum(dQt * Qt, axis=1) - np.sum(dKh * Kh, axis=1)
+    dG[-1] += np.sum(dKh * Kh) + gam * dgam
+    dg = np.cumsum(dG[::-1])[::-1]
+    return dq, dk, dv, None, dg, dM0
+
+
+def chunked_bwd(q, k, v, beta, log_alpha, M0, dO, dMT, C=64, write="delta"):
+    """Gradients over one sequence by chunks: q,k [T,dk], v [T,dv], beta [T] (None with
+    write="add"), log_alpha None | [T], M0 [dk,dv], dO [T,dv], dMT None | [dk,dv].  The
+    chunk states are recomputed forward, then the chunks are walked in reverse.  A
+    partial last chunk is padded with zero rows (beta = 0, log alpha = 0)."""
     Tn, dk_ = q.shape
     dv_ = v.shape[1]
     la = np.zeros(Tn) if log_alpha is None else log_alpha
+    if beta is None:
+        beta = np.zeros(Tn)
     nch = (Tn + C - 1) // C
     pad = nch * C - Tn
     padf = lambda x: np.concatenate([x, np.zeros((pad,) + x.shape[1:])]) if pad else x
@@ -195,15 +229,20 @@ def chunked_bwd(q, k, v, beta, log_alpha, M0, dO, dMT, C=64):
     for c in range(nch):
         sl = slice(c * C, (c + 1) * C)
         G = np.cumsum(lp[sl])
-        res = chunk_step(qp[sl], kp[sl], vp[sl], bp[sl], np.repeat(G[:, None], dk_, axis=1), states[-1])
-        states.append(res["M"])
+        if write == "add":  # M_C = e^{G_C} M0 + (e^{G_C - G} K)^T V
+            states.append(np.exp(G[-1]) * states[-1] + (np.exp(G[-1] - G)[:, None] * kp[sl]).T @ vp[sl])
+        else:
+            res = chunk_step(qp[sl], kp[sl], vp[sl], bp[sl], np.repeat(G[:, None], dk_, axis=1), states[-1])
+            states.append(res["M"])
     dM = np.zeros((dk_, dv_)) if dMT is None else dMT
     out = [np.zeros_like(x) for x in (qp, kp, vp, bp, lp)]
     for c in reversed(range(nch)):
         sl = slice(c * C, (c + 1) * C)
-        dq, dk, dv, db, dg, dM = chunk_step_bwd(qp[sl], kp[sl], vp[sl], bp[sl], lp[sl], states[c], dOp[sl], dM)
+        dq, dk, dv, db, dg, dM = chunk_step_bwd(qp[sl], kp[sl], vp[sl], bp[sl], lp[sl], states[c], dOp[sl], dM,
+                                                write=write)
         for o_, x in zip(out, (dq, dk, dv, db, dg)):
-            o_[sl] = x
+            if x is not None:
+                o_[sl] = x
     return tuple(x[:Tn] for x in out) + (dM,)
 
 

@@ -153,8 +153,9 @@ int oracle_step(int N, int H, int dk, int dv, int gate, int write, const double 
 }
 
 /*
- * Gradients of the token recurrence above (reverse mode, fp64), for the delta write
- * with no gate or one decay per (token, head).  For one token, with M' = a M_{t-1},
+ * Gradients of the token recurrence above (reverse mode, fp64), for the delta write and
+ * the additive write with no gate or one decay per (token, head).  For one token of the
+ * delta write, with M' = a M_{t-1},
  * r = M'^T k, e = v - r, M_t = M' + beta k e^T, o = M_t^T q, and the gradient G of
  * the loss with respect to M_t (everything that later tokens and the final state
  * pass back) plus do:
@@ -165,19 +166,23 @@ int oracle_step(int N, int H, int dk, int dv, int gate, int write, const double 
  *   G'    = G - k de^T                (gradient with respect to M')
  *   dlog_alpha = sum(G' .* M')        (M' = a M_{t-1}, d a / d log a = a)
  *   G_{t-1} = a G'
+ * The additive write M_t = M' + k v^T passes G to M' unchanged, with dk = G v and
+ * dv = G^T k (no beta: dbeta may be NULL).
  * Each sequence's states M_t are recomputed forward and kept, then swept in reverse.
  * dfinal (NULL: zeros) is the gradient with respect to the final state; the result
  * dinit is the gradient with respect to the initial state.  Arrays as for
  * oracle_fwd; dlog_alpha is [tokens][H] (or NULL without a gate).
  */
 int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, int dv, int gate,
-               const double *q, const double *k, const double *v, const double *beta,
+               int write, const double *q, const double *k, const double *v, const double *beta,
                const double *log_alpha, const double *initial_state, const double *dout,
                const double *dfinal, double *dq, double *dk_out, double *dv_out, double *dbeta,
                double *dlog_alpha, double *dinit, int nthreads) {
   int64_t pair;
   int failed = 0;
-  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || beta == NULL) return -1;
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+  if (write != ORACLE_WRITE_DELTA && write != ORACLE_WRITE_ADD) return -1;
+  if (write == ORACLE_WRITE_DELTA && (beta == NULL || dbeta == NULL)) return -1;
   if (gate != ORACLE_GATE_NONE && gate != ORACLE_GATE_HEAD) return -1;
   if (gate == ORACLE_GATE_HEAD && (log_alpha == NULL || dlog_alpha == NULL)) return -1;
 #ifdef _OPENMP
@@ -209,7 +214,7 @@ int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
     for (t = 0; t < L; ++t) {
       size_t th = (size_t)(start[n] + t) * H + h;
       memcpy(Ms + (t + 1) * S, Ms + t * S, sizeof(double) * S);
-      oracle_token(dk, dv, gate, ORACLE_WRITE_DELTA, q + th * dk, k + th * dk, v + th * dv, beta[th],
+      oracle_token(dk, dv, gate, write, q + th * dk, k + th * dk, v + th * dv, beta ? beta[th] : 0.0,
                    gate == ORACLE_GATE_HEAD ? log_alpha + th : NULL, Ms + (t + 1) * S, r, otmp);
     }
     /* reverse sweep */
@@ -222,7 +227,7 @@ int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
       const double *qt = q + th * dk, *kt = k + th * dk, *vt = v + th * dv, *dot = dout + th * dv;
       const double *Mt = Ms + (t + 1) * S, *Mprev = Ms + t * S;
       const double a = gate == ORACLE_GATE_HEAD ? exp(log_alpha[th]) : 1.0;
-      const double bt = beta[th];
+      const double bt = beta ? beta[th] : 0.0;
       double db = 0.0, dla = 0.0;
       for (i = 0; i < S; ++i) Mp[i] = a * Mprev[i];
       for (j = 0; j < dv; ++j) r[j] = 0.0;
@@ -237,6 +242,25 @@ int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
           acc += Mt[i * dv + j] * dot[j];
         }
         dq[th * dk + i] = acc;
+      }
+      if (write == ORACLE_WRITE_ADD) {
+        /* additive write: dk = G v, dv = G^T k; G passes to M' unchanged */
+        for (i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (j = 0; j < dv; ++j) acc += G[i * dv + j] * vt[j];
+          dk_out[th * dk + i] = acc;
+        }
+        for (j = 0; j < dv; ++j) {
+          double acc = 0.0;
+          for (i = 0; i < dk; ++i) acc += G[i * dv + j] * kt[i];
+          dv_out[th * dv + j] = acc;
+        }
+        for (i = 0; i < S; ++i) {
+          dla += G[i] * Mp[i];
+          G[i] *= a;
+        }
+        if (gate == ORACLE_GATE_HEAD) dlog_alpha[th] = dla;
+        continue;
       }
       /* write: de = beta G^T k, dbeta = k^T G e */
       for (j = 0; j < dv; ++j) de[j] = 0.0;

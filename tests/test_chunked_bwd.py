@@ -35,3 +35,28 @@ def test_chunked_gradients_equal_token_gradients(C, gate, T):
         if rr is None:
             continue
         np.testing.assert_allclose(g, rr, atol=1e-10, rtol=1e-10, err_msg=name)
+
+
+@pytest.mark.parametrize("C", [1, 3, 16, 64])
+@pytest.mark.parametrize("gate", ["none", "head"])
+@pytest.mark.parametrize("T", [1, 40, 130])
+def test_chunked_additive_gradients_equal_token_gradients(C, gate, T):
+    """The additive write's chunk adjoint (Delta = V, no A or T) against oracle.bwd."""
+    r = np.random.default_rng(T * 11 + C)
+    dk, dv = 7, 5
+    q, k = unit(r.standard_normal((T, dk))), unit(r.standard_normal((T, dk)))
+    v = r.standard_normal((T, dv))
+    la = None if gate == "none" else -np.log1p(np.exp(r.standard_normal(T))) * 2.0
+    M0 = r.standard_normal((dk, dv)) * 0.5
+    dO, dMT = r.standard_normal((T, dv)), r.standard_normal((dk, dv))
+    got = chunked_ref.chunked_bwd(q, k, v, None, la, M0, dO, dMT, C=C, write="add")
+    ref = oracle.bwd(q[None, :, None], k[None, :, None], v[None, :, None], None,
+                     None if la is None else la[None, :, None], M0[None, None], dO[None, :, None], dMT[None, None],
+                     write="add")
+    names = ["dq", "dk", "dv", "dlog_alpha", "dM0"]
+    refs = [ref[0][0, :, 0], ref[1][0, :, 0], ref[2][0, :, 0], None if la is None else ref[4][0, :, 0], ref[5][0, 0]]
+    gots = [got[0], got[1], got[2], got[4], got[5]]
+    for name, g, rr in zip(names, gots, refs):
+        if rr is None:
+            continue
+        np.testing.assert_allclose(g, rr, atol=1e-10, rtol=1e-10, err_msg=name)
