@@ -217,11 +217,12 @@ def time_pool_decode(gdn, N, L, H, dk, dv, store, steps=64):
 def time_bwd(gdn, name, steps=20):
     """gdn_bwd_chunked on a workload: the gradients of o and of the final state are
     seeded N(0,1) and N(0, 0.1^2).  Algorithmic bytes: q, k, v, dout read and dq, dk,
-    dv written in the I/O dtype, beta and log alpha read and their gradients written
-    in fp32, the initial state and the final-state gradient read and the
-    initial-state gradient written in fp32.  Algorithmic flops: the forward
-    recomputation (as for the forward) plus, per token and head, 14 C d_k + 10 C d_v
-    + 14 d_k d_v + 4 C^2 for the backward products (each counted once)."""
+    dv written in the I/O dtype, beta (delta write) and a per-token log alpha read and
+    their gradients written in fp32, the initial state and the final-state gradient
+    read and the initial-state gradient written in fp32.  Algorithmic flops: the
+    forward recomputation (as for the forward) plus, per token and head, 14 C d_k +
+    10 C d_v + 14 d_k d_v + 4 C^2 for the delta write's backward products, or 6 C d_k
+    + 4 C d_v + 8 d_k d_v for the additive write's (each product counted once)."""
     import torch
     import synth
     spec = synth.WORKLOADS[name]
@@ -232,8 +233,9 @@ def time_bwd(gdn, name, steps=20):
     dout = torch.randn(B, T, H, dv, generator=g).to(inp["q"].dtype).cuda()
     dfs = (torch.randn(inp["N"], H, dk, dv, generator=g) * 0.1).cuda()
     d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    write = inp.get("write", "delta")
     call = gdn.PreparedBwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"], dout, dfs,
-                           d["cu_seqlens"])
+                           d["cu_seqlens"], write=write)
     torch.cuda.synchronize()
     t = time.perf_counter()
     call.launch()
@@ -252,9 +254,13 @@ def time_bwd(gdn, name, steps=20):
     tokens = B * T
     esize = 2 if spec["dtype"] == "bf16" else 4
     th = tokens * H
-    nbytes = th * (esize * (4 * dk + 3 * dv) + 16) + 3 * 4 * dk * dv * inp["N"] * H
-    fwd_flops, _ = alg_counts(tokens, H, dk, dv, inp["N"], spec["gate"], esize, True)
-    flops = fwd_flops + th * (14 * CHUNK * dk + 10 * CHUNK * dv + 14 * dk * dv + 4 * CHUNK * CHUNK)
+    per_tok = (8 if write == "delta" else 0) + (8 if spec["gate"] == "head" else 0)
+    nbytes = th * (esize * (4 * dk + 3 * dv) + per_tok) + 3 * 4 * dk * dv * inp["N"] * H
+    fwd_flops, _ = alg_counts(tokens, H, dk, dv, inp["N"], spec["gate"], esize, True, write=write)
+    if write == "add":
+        flops = fwd_flops + th * (6 * CHUNK * dk + 4 * CHUNK * dv + 8 * dk * dv)
+    else:
+        flops = fwd_flops + th * (14 * CHUNK * dk + 10 * CHUNK * dv + 14 * dk * dv + 4 * CHUNK * CHUNK)
     return {"workload": name + " backward", "ms_per_step": ms, "tokens_per_s": tokens / (ms / 1e3),
             "alg_bytes": nbytes, "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
             "hbm_frac": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, "alg_flops": flops,
@@ -386,6 +392,8 @@ def main():
             torch.cuda.empty_cache()
             extra.append(r)
         extra.append(time_bwd(gdn, HEADLINE))
+        torch.cuda.empty_cache()
+        extra.append(time_bwd(gdn, "retnet-bf16-B16-T2048-H8-d128"))
         torch.cuda.empty_cache()
         for e in extra:
             print(json.dumps(e), file=sys.stderr)

@@ -498,9 +498,9 @@ class PreparedBwd:
     gradients are overwritten by every launch."""
 
     def __init__(self, q, k, v, beta, log_alpha, initial_state, dout, dfinal_state=None, cu_seqlens=None,
-                 output_dinitial: bool = True):
+                 output_dinitial: bool = True, write: str = "delta"):
         self.args, self.outs, self._keep = _bwd_args(q, k, v, beta, log_alpha, initial_state, dout,
-                                                     dfinal_state, cu_seqlens, output_dinitial, None)
+                                                     dfinal_state, cu_seqlens, output_dinitial, None, write)
         self._ref = ctypes.byref(self.args)
 
     def launch(self, stream=None):
@@ -509,19 +509,20 @@ class PreparedBwd:
 
 
 def _bwd_args(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state, cu_seqlens, output_dinitial,
-              workspace):
+              workspace, write="delta"):
     import torch
-    N = check_fwd_tensors(q, k, v, beta, log_alpha, initial_state, cu_seqlens, dout, dfinal_state)
-    _require(log_alpha is None or log_alpha.dim() == 3,
-             "the backward supports no gate or log_alpha [B, T, H] (one decay per token and head)")
+    N = check_fwd_tensors(q, k, v, beta, log_alpha, initial_state, cu_seqlens, dout, dfinal_state, write)
+    _require(log_alpha is None or log_alpha.dim() in (1, 3),
+             "the backward supports no gate, log_alpha [B, T, H] (one decay per token and head) or [H] "
+             "(one constant decay per head)")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dbeta = torch.empty_like(beta)
+    dbeta = torch.empty_like(beta) if write == "delta" else None
     dla = torch.empty_like(log_alpha) if log_alpha is not None else None
     dinit = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device) if output_dinitial else None
     args = BwdArgs(B=B, T=T, H=H, d_k=dk, d_v=dv, chunk=CHUNK, N=N, dtype=_dtype_code(q),
-                   gate=gate_code(log_alpha, 3), write=GDN_WRITE_DELTA, q=_ptr(q), k=_ptr(k), v=_ptr(v),
+                   gate=gate_code(log_alpha, 3), write=WRITES[write], q=_ptr(q), k=_ptr(k), v=_ptr(v),
                    beta=_ptr(beta), log_alpha=_ptr(log_alpha), initial_state=_ptr(initial_state),
                    cu_seqlens=_ptr(cu_seqlens), dout=_ptr(dout), dfinal_state=_ptr(dfinal_state),
                    dq=_ptr(dq), dk=_ptr(dk_), dv=_ptr(dv_), dbeta=_ptr(dbeta), dlog_alpha=_ptr(dla),
@@ -536,13 +537,15 @@ def _bwd_args(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state, cu_se
 
 
 def bwd_chunked(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state=None, cu_seqlens=None,
-                output_dinitial: bool = True, workspace=None, stream=None):
-    """Gradients of fwd_chunked (gdn_bwd_chunked) for the delta rule with no gate or
-    one decay per (token, head).  Inputs as for fwd_chunked, plus dout [B,T,H,d_v]
-    (dtype of q) and dfinal_state None | [N,H,d_k,d_v] fp32.
-    Returns (dq, dk, dv, dbeta, dlog_alpha or None, dinitial_state or None)."""
+                output_dinitial: bool = True, workspace=None, stream=None, write: str = "delta"):
+    """Gradients of fwd_chunked (gdn_bwd_chunked) for the delta write (beta [B,T,H]) or
+    the additive write (write="add", beta None), with no gate, one decay per (token,
+    head) ([B,T,H]) or one constant decay per head ([H]).  Inputs as for fwd_chunked,
+    plus dout [B,T,H,d_v] (dtype of q) and dfinal_state None | [N,H,d_k,d_v] fp32.
+    Returns (dq, dk, dv, dbeta or None, dlog_alpha or None (shaped like log_alpha),
+    dinitial_state or None)."""
     args, outs, keep = _bwd_args(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state, cu_seqlens,
-                                 output_dinitial, workspace)
+                                 output_dinitial, workspace, write)
     _check(_lib.gdn_bwd_chunked(ctypes.byref(args), _stream(stream)), "gdn_bwd_chunked")
     return outs
 

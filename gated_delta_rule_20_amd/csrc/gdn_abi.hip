@@ -140,11 +140,15 @@ int check_bwd(const gdn_bwd_args *a) {
   const gdn_fwd_args f = fwd_of(a);
   const int st = check_fwd(&f);
   if (st != GDN_OK) return st;
-  if (a->write != GDN_WRITE_DELTA || (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD))
-    return GDN_ERR_UNSUPPORTED;
+  if (a->gate == GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long)a->B * a->T > 0;
-  if (tokens && (!a->dq || !a->dk || !a->dv || !a->dbeta)) return GDN_ERR_INVALID_ARG;
-  if (tokens && ((a->gate == GDN_GATE_HEAD) != (a->dlog_alpha != nullptr))) return GDN_ERR_INVALID_ARG;
+  if (tokens && (!a->dq || !a->dk || !a->dv)) return GDN_ERR_INVALID_ARG;
+  // dbeta exactly for the delta write; dlog_alpha exactly for a gate (the constant
+  // per-head decay's gradient is [H], written even without tokens)
+  if ((tokens || a->dbeta) && ((a->write == GDN_WRITE_DELTA) != (a->dbeta != nullptr))) return GDN_ERR_INVALID_ARG;
+  if ((tokens || a->gate == GDN_GATE_HEAD_CONST || a->dlog_alpha) &&
+      ((a->gate != GDN_GATE_NONE) != (a->dlog_alpha != nullptr)))
+    return GDN_ERR_INVALID_ARG;
   const void *p16[] = {a->dq, a->dk, a->dv, a->dfinal_state, a->dinitial_state};
   for (const void *p : p16)
     if (p && !aligned(p, 16)) return GDN_ERR_INVALID_ARG;
@@ -170,16 +174,18 @@ int check_dplr(const gdn_dplr_args *a) {
 
 struct BwdLayout {
   long slots;
-  size_t states, tmat, part;
-  size_t total() const { return states + tmat + part; }
+  size_t states, tmat, part, dla;
+  size_t total() const { return states + tmat + part + dla; }
 };
 BwdLayout bwd_layout(const gdn_bwd_args *a) {
-  BwdLayout L{0, 0, 0, 0};
+  BwdLayout L{0, 0, 0, 0, 0};
   const long tokens = (long)a->B * a->T;
   L.slots = gdn::key_slots(tokens, a->N);
   L.states = align256((size_t)L.slots * a->H * a->d_k * a->d_v * 4);
-  L.tmat = align256((size_t)L.slots * a->H * 64 * 64 * 4);
+  if (a->write == GDN_WRITE_DELTA) L.tmat = align256((size_t)L.slots * a->H * 64 * 64 * 4);  // T per chunk
   L.part = align256((size_t)L.slots * a->H * (a->d_v / 32) * gdn::bwd_part_floats(a->d_k) * 4);
+  // the constant per-head decay: per-token gradients, summed per head afterwards
+  if (a->gate == GDN_GATE_HEAD_CONST) L.dla = align256((size_t)tokens * a->H * 4);
   return L;
 }
 
@@ -197,8 +203,13 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   if (st != GDN_OK) return st;
   const BwdLayout L = bwd_layout(a);
   if (!a->workspace || a->workspace_bytes < L.total() || !aligned(a->workspace, 256)) return GDN_ERR_WORKSPACE;
-  if (a->N == 0 || (long)a->B * a->T == 0) {
-    // no tokens: the initial-state gradient is the final-state gradient (or zero)
+  const long tokens = (long)a->B * a->T;
+  if (a->N == 0 || tokens == 0) {
+    // no tokens: the initial-state gradient is the final-state gradient (or zero), and a
+    // constant decay's gradient is zero
+    if (a->gate == GDN_GATE_HEAD_CONST &&
+        gdn::launch_sum_tokens(nullptr, 0, a->H, a->dlog_alpha, (hipStream_t)hip_stream) != hipSuccess)
+      return GDN_ERR_HIP;
     if (a->dinitial_state && a->N > 0) {
       const size_t bytes = (size_t)a->N * a->H * a->d_k * a->d_v * 4;
       hipError_t e = a->dfinal_state
@@ -230,11 +241,14 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   fp.H = a->H;
   fp.T = a->T;
   fp.dv = a->d_v;
-  fp.la_stride = a->H;
+  const bool add = a->write == GDN_WRITE_ADD;
+  const int la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
+  fp.la_stride = la_stride;
   fp.chunk_states = (float *)ws;
   const int dvb = choose_dvb(a->N, a->H, a->d_v);
   fp.nb = a->d_v / dvb;
-  if (gdn::launch_fwd_fused(fp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, (int)a->gate, false, stream) != hipSuccess)
+  if (gdn::launch_fwd_fused(fp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, kernel_gate(a->gate), add, stream) !=
+      hipSuccess)
     return GDN_ERR_HIP;
   // 2. reverse state pass and 3. per-chunk gradients
   gdn::BwdParams bp;
@@ -253,14 +267,19 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   bp.dk = a->dk;
   bp.dv_out = a->dv;
   bp.dbeta = a->dbeta;
-  bp.dlog_alpha = a->dlog_alpha;
+  float *const dla_tok = (float *)(ws + L.states + L.tmat + L.part);
+  bp.dlog_alpha = a->gate == GDN_GATE_HEAD_CONST ? dla_tok : a->dlog_alpha;
+  bp.la_stride = la_stride;
   bp.dinit = a->dinitial_state;
   bp.N = a->N;
   bp.H = a->H;
   bp.T = a->T;
   bp.dv = a->d_v;
   bp.slots = L.slots;
-  if (gdn::launch_bwd(bp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, (int)a->gate, stream) != hipSuccess)
+  if (gdn::launch_bwd(bp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, kernel_gate(a->gate), add, stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (a->gate == GDN_GATE_HEAD_CONST &&
+      gdn::launch_sum_tokens(dla_tok, tokens, a->H, a->dlog_alpha, stream) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
 }

@@ -61,7 +61,7 @@ __device__ __forceinline__ bool seq_extent(const BwdParams &p, int n, long &tok0
   return true;
 }
 
-template <typename E, int DK, int GATE>
+template <typename E, int DK, int GATE, bool ADD>
 __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
   constexpr int SKE = DK + 8;
   constexpr int VE = 16 / (int)sizeof(E);        // elements per 16-byte piece
@@ -82,8 +82,10 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
   __shared__ __align__(16) float Xl[BC * SV];
   __shared__ __align__(16) float dDl[BC * SV];
   __shared__ float bs[BC], gs[BC], eg[BC], et[BC], red[BC], wsum[4], misc[4];
-  float *const Yl = Vb;   // V is dead once X is formed
-  float *const Dl = Tl;   // A is dead once T is formed
+  // delta write: V is dead once X is formed and A once T is; additive write: Delta = V
+  // and Y = dDelta
+  float *const Yl = ADD ? dDl : Vb;
+  float *const Dl = ADD ? Vb : Tl;
   float *const Ys = dDl;  // scratch of the block substitution, before dDelta exists
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -134,8 +136,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     }
     if (tid < BC) {
       const size_t t = tbc + min(tid, last);
-      pb = p.beta[t * H + h];
-      pl = GATE == GATE_HEAD ? p.log_alpha[t * H + h] : 0.f;
+      pb = ADD ? 0.f : p.beta[t * H + h];
+      pl = GATE == GATE_HEAD ? p.log_alpha[t * p.la_stride + h] : 0.f;
     }
   };
   auto stage = [&](int nvc) {
@@ -209,26 +211,28 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       for (int t = wave; t < 10; t += 4) {
         const int mb = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
         const int m0 = 16 * mb, n0 = 16 * (t - mb * (mb + 1) / 2);
-        f32x4 av, pv4;
+        f32x4 av = zero4(), pv4;
         if constexpr (std::is_same<E, bf16>::value) {
           const E *kr = Kl + (m0 + lm) * SKE + 8 * lg, *qr = Ql + (m0 + lm) * SKE + 8 * lg;
           const E *kc = Kl + (n0 + lm) * SKE + 8 * lg;
-          av = tile_frag<DK>([&](int k0) { return ld8(kr + k0); }, [&](int k0) { return ld8(kc + k0); });
+          if (!ADD) av = tile_frag<DK>([&](int k0) { return ld8(kr + k0); }, [&](int k0) { return ld8(kc + k0); });
           pv4 = tile_frag<DK>([&](int k0) { return ld8(qr + k0); }, [&](int k0) { return ld8(kc + k0); });
         } else {
-          av = tile<DK>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
+          if (!ADD) av = tile<DK>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
           pv4 = tile<DK>(m0, n0, lg, lm, Q_, [&](int d, int i) { return K_(i, d); });
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = m0 + 4 * lg + u, i = n0 + lm;
-          Tl[r * ST + i] = i < r ? bs[r] * av[u] * gam_at(r, i) : 0.f;
+          if (!ADD) Tl[r * ST + i] = i < r ? bs[r] * av[u] * gam_at(r, i) : 0.f;
           Pl[r * ST + i] = pv4[u] * gam_at(r, i);
         }
       }
     }
     __syncthreads();
-    if (wave == 0) {
+    if (ADD) {
+      // the additive write has no A, T or X
+    } else if (wave == 0) {
       // diagonal 16x16 blocks of T = (I + A)^-1: lane (lg, lm) solves column lm of block lg
       const int lg = lane >> 4, lm = lane & 15, o = 16 * lg;
       float x[16];
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
                               });
     }
     __syncthreads();
-    if (wave < 3) {
+    if (!ADD && wave < 3) {
       // off-diagonal blocks, block column b = wave, downwards:
       // T[a][b] = -T[a][a] sum_{k=b}^{a-1} A[a][k] T[k][b]
       const int lg = lane >> 4, lm = lane & 15, b = wave;
@@ -269,15 +273,18 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       }
     }
     __syncthreads();
-    if (jb == 0)  // T for the per-chunk kernel
+    if (!ADD && jb == 0)  // T for the per-chunk kernel
       for (int i = tid; i < BC * BC; i += BNT) p.tmat[(slot * H + h) * BC * BC + i] = Tb[(i / BC) * ST + i % BC];
-    // ---- Delta = T diag(beta) (V - Kt M0);  dDelta = P^T dO + diag(e^{G_C - G}) K dM  (8 tiles each)
+    // ---- Delta = T diag(beta) (V - Kt M0) (the additive write: Delta = V, already in Vb);
+    // dDelta = P^T dO + diag(e^{G_C - G}) K dM  (8 tiles each)
     {
       const int lg = lane >> 4, lm = lane & 15;
       for (int t = wave; t < 8; t += 4) {
         const int m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
-        const f32x4 dd = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int i) { return Tb[r * ST + i]; },
-                                                     [&](int i, int j) { return bs[i] * Xl[i * SV + j]; }, 0, m0 + 16);
+        f32x4 dd = zero4();
+        if (!ADD)
+          dd = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int i) { return Tb[r * ST + i]; },
+                                           [&](int i, int j) { return bs[i] * Xl[i * SV + j]; }, 0, m0 + 16);
         const f32x4 d1 = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int r, int i) { return Pl[i * ST + r]; },
                                                     [&](int i, int j) { return dOb[i * SV + j]; }, m0);
         const f32x4 d2 =
@@ -285,26 +292,28 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = m0 + 4 * lg + u, j = n0 + lm;
-          Dl[r * SV + j] = dd[u];
+          if (!ADD) Dl[r * SV + j] = dd[u];
           dDl[r * SV + j] = d1[u] + et[r] * d2[u];
         }
       }
     }
     __syncthreads();
-    // ---- Y = T^T dDelta
-    mm_g<E, BC, BVB, BC, 4, false, false>(wave, lane, [&](int r, int i) { return Tb[i * ST + r]; },
-                            [&](int i, int j) { return dDl[i * SV + j]; }, [&](int r, int j, f32x4 v) {
+    // ---- Y = T^T dDelta (the additive write: Y = dDelta, already in dDl)
+    if constexpr (!ADD)
+      mm_g<E, BC, BVB, BC, 4, false, false>(wave, lane, [&](int r, int i) { return Tb[i * ST + r]; },
+                              [&](int i, int j) { return dDl[i * SV + j]; }, [&](int r, int j, f32x4 v) {
 #pragma unroll
-                              for (int u = 0; u < 4; ++u) Yl[(r + u) * SV + j] = v[u];
-                            });
+                                for (int u = 0; u < 4; ++u) Yl[(r + u) * SV + j] = v[u];
+                              });
     __syncthreads();
     // ---- dV (complete for this value block)
     for (int i = tid; i < BC * BVB; i += BNT) {
       const int r = i / BVB, j = i % BVB;
-      if (r < nv) ((E *)p.dv_out)[((tb + r) * H + h) * dv + col0 + j] = to_e<E>(bs[r] * Yl[r * SV + j]);
+      if (r < nv) ((E *)p.dv_out)[((tb + r) * H + h) * dv + col0 + j] = to_e<E>(ADD ? Yl[r * SV + j] : bs[r] * Yl[r * SV + j]);
     }
     float *pr = p.part + ((slot * H + h) * nb + jb) * (size_t)PT::SIZE;
-    // ---- dP = incl(dO Delta^T), dT = dDelta (diag(beta) X)^T  (partial over value columns)
+    // ---- dP = incl(dO Delta^T), dT = dDelta (diag(beta) X)^T  (partial over value columns;
+    // no dT for the additive write)
     if constexpr (std::is_same<E, bf16>::value) {
       // these contract over the 32 value columns: every fragment is a row piece
       const int lg = lane >> 4, lm = lane & 15;
@@ -314,14 +323,16 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
         if (n0 <= m0)
           vp = tile_frag<BVB>([&](int k0) { return to_bf8(ld8(dOb + (m0 + lm) * SV + 8 * lg + k0)); },
                               [&](int k0) { return split8(ld8(Dl + i * SV + 8 * lg + k0)); });
-        const float bi = bs[i];
-        const f32x4 vt = tile_frag<BVB>([&](int k0) { return split8(ld8(dDl + (m0 + lm) * SV + 8 * lg + k0)); },
-                                        [&](int k0) { return split8(ld8(Xl + i * SV + 8 * lg + k0) * bi); });
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           if (i > m0 + 4 * lg + u) vp[u] = 0.f;
         *(f32x4 *)(pr + PT::DP + i * BC + m0 + 4 * lg) = vp;
-        *(f32x4 *)(pr + PT::DT + i * BC + m0 + 4 * lg) = vt;
+        if (!ADD) {
+          const float bi = bs[i];
+          const f32x4 vt = tile_frag<BVB>([&](int k0) { return split8(ld8(dDl + (m0 + lm) * SV + 8 * lg + k0)); },
+                                          [&](int k0) { return split8(ld8(Xl + i * SV + 8 * lg + k0) * bi); });
+          *(f32x4 *)(pr + PT::DT + i * BC + m0 + 4 * lg) = vt;
+        }
       }
     } else {
       mm_g<E, BC, BC, BVB, 4, true, false>(wave, lane, [&](int r, int j) { return dOb[r * SV + j]; },
@@ -329,11 +340,12 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
                                 for (int u = 0; u < 4; ++u) pr[PT::DP + i * BC + r + u] = i <= r + u ? v[u] : 0.f;
                               });
-      mm_g<E, BC, BC, BVB, 4, false, false>(wave, lane, [&](int r, int j) { return dDl[r * SV + j]; },
-                              [&](int j, int i) { return bs[i] * Xl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
+      if constexpr (!ADD)
+        mm_g<E, BC, BC, BVB, 4, false, false>(wave, lane, [&](int r, int j) { return dDl[r * SV + j]; },
+                                [&](int j, int i) { return bs[i] * Xl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
 #pragma unroll
-                                for (int u = 0; u < 4; ++u) pr[PT::DT + i * BC + r + u] = v[u];
-                              });
+                                  for (int u = 0; u < 4; ++u) pr[PT::DT + i * BC + r + u] = v[u];
+                                });
     }
     // ---- dQ = e^G dO M0^T, dK = -e^G beta Y M0^T + e^{G_C - G} Delta dM^T, and the rows of
     // dG: e^G (dO M0^T).Q - e^G beta (Y M0^T).K - e^{G_C - G} (Delta dM^T).K.  A wave takes
@@ -357,13 +369,15 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
           const Split fm = split8(ld8(M0 + (n0 + lm) * SV + 8 * lg));
           const Split fdm = split8(ld8(dM + (n0 + lm) * SV + 8 * lg));
           w = mm(fdo, fm, zero4());
-          uu = mm(fy, fm, zero4());
+          uu = ADD ? zero4() : mm(fy, fm, zero4());
           z = mm(fd, fdm, zero4());
         } else {
           w = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return dOb[r * SV + j]; },
                         [&](int j, int d) { return M0[d * SV + j]; });
-          uu = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Yl[r * SV + j]; },
-                         [&](int j, int d) { return M0[d * SV + j]; });
+          uu = zero4();
+          if (!ADD)
+            uu = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Yl[r * SV + j]; },
+                           [&](int j, int d) { return M0[d * SV + j]; });
           z = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Dl[r * SV + j]; },
                         [&](int j, int d) { return dM[d * SV + j]; });
         }
@@ -405,7 +419,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) part_m += __shfl_xor(part_m, off);
     if (lane == 0) wsum[wave] = part_m;
-    if (tid < BC) {
+    if (!ADD && tid < BC) {
       float sb = 0.f;
       for (int j = 0; j < BVB; ++j) sb += Yl[tid * SV + j] * Xl[tid * SV + j];
       pr[PT::DB + tid] = sb;
@@ -417,7 +431,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       for (int off = 32; off >= 1; off >>= 1) sg += __shfl_xor(sg, off);
       if (lane == 0) pr[PT::GC] = sg + misc[0] * (wsum[0] + wsum[1] + wsum[2] + wsum[3]);
     }
-    // ---- dM <- gam dM + Qt^T dO - Kt^T diag(beta) Y   (DK x 32: DK / 8 tiles)
+    // ---- dM <- gam dM + Qt^T dO - Kt^T diag(beta) Y (no last term for the additive write)
+    // (DK x 32: DK / 8 tiles)
     {
       const int lg = lane >> 4, lm = lane & 15;
       constexpr int TILES = (DK / 16) * 2;
@@ -428,8 +443,10 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
         const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
         const f32x4 n1 = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * Q_(r, d); },
                                   [&](int r, int j) { return dOb[r * SV + j]; });
-        const f32x4 n2 = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * bs[r] * K_(r, d); },
-                                  [&](int r, int j) { return Yl[r * SV + j]; });
+        f32x4 n2 = zero4();
+        if (!ADD)
+          n2 = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * bs[r] * K_(r, d); },
+                                           [&](int r, int j) { return Yl[r * SV + j]; });
 #pragma unroll
         for (int u = 0; u < 4; ++u) nm[q][u] = gam * dM[(m0 + 4 * lg + u) * SV + n0 + lm] + n1[u] - n2[u];
       }
@@ -450,7 +467,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     }
 }
 
-template <typename E, int DK, int GATE>
+template <typename E, int DK, int GATE, bool ADD>
 __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   constexpr int SKE = DK + 8;
   typedef Part<DK> PT;
@@ -502,12 +519,12 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   for (int u = 0; u < BC * BC / 4 / BNT; ++u) {
     // T is row-major; the partials are stored transposed (column i, rows r0 .. r0+3)
     const int i4 = 4 * (tid + BNT * u), r = i4 / BC, col = i4 % BC;
-    f32x4 sp = zero4(), st = zero4();
+    f32x4 sp = zero4(), st = zero4(), tv = zero4();
     for (int b = 0; b < nb; ++b) {
       sp += *(const f32x4 *)(pr0 + (size_t)b * PT::SIZE + PT::DP + i4);
-      st += *(const f32x4 *)(pr0 + (size_t)b * PT::SIZE + PT::DT + i4);
+      if (!ADD) st += *(const f32x4 *)(pr0 + (size_t)b * PT::SIZE + PT::DT + i4);
     }
-    const f32x4 tv = *(const f32x4 *)(tm + i4);
+    if (!ADD) tv = *(const f32x4 *)(tm + i4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       Pl[(col + e) * ST + r] = sp[e];
@@ -517,12 +534,12 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   }
   if (tid < BC) {
     const bool ok = tid < nv;
-    bs[tid] = ok ? p.beta[(tb + tid) * H + h] : 0.f;
-    gs[tid] = (GATE == GATE_HEAD && ok) ? p.log_alpha[(tb + tid) * H + h] : 0.f;
+    bs[tid] = (!ADD && ok) ? p.beta[(tb + tid) * H + h] : 0.f;
+    gs[tid] = (GATE == GATE_HEAD && ok) ? p.log_alpha[(tb + tid) * p.la_stride + h] : 0.f;
     float sg = 0.f, sb = 0.f;
     for (int b = 0; b < nb; ++b) {
       sg += pr0[(size_t)b * PT::SIZE + PT::DG + tid];
-      sb += pr0[(size_t)b * PT::SIZE + PT::DB + tid];
+      if (!ADD) sb += pr0[(size_t)b * PT::SIZE + PT::DB + tid];
     }
     dGs[tid] = sg;
     dBs[tid] = sb;
@@ -549,7 +566,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
     f32x4 sv = zero4(), rv = zero4();
     if (n0 <= m0) {
-      sv = tile_g<E, DK, true, true>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
+      if (!ADD) sv = tile_g<E, DK, true, true>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
       rv = tile_g<E, DK, true, true>(m0, n0, lg, lm, Q_, [&](int d, int i) { return K_(i, d); });
     }
 #pragma unroll
@@ -557,9 +574,11 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
       Sl[(m0 + 4 * lg + u) * ST + n0 + lm] = sv[u];
       Rl[(m0 + 4 * lg + u) * ST + n0 + lm] = rv[u];
     }
-    // T^T is upper triangular: T[i][k] = 0 for k > i
-    const f32x4 zv = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int k) { return Dt[r * ST + k]; },
-                                                 [&](int k, int i) { return Tl[i * ST + k]; }, 0, n0 + 16);
+    // T^T is upper triangular: T[i][k] = 0 for k > i (no T for the additive write)
+    f32x4 zv = zero4();
+    if (!ADD)
+      zv = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int k) { return Dt[r * ST + k]; },
+                                       [&](int k, int i) { return Tl[i * ST + k]; }, 0, n0 + 16);
 #pragma unroll
     for (int u = 0; u < 4; ++u) Zl[(m0 + 4 * lg + u) * ST + n0 + lm] = zv[u];
   }
@@ -572,8 +591,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int t = wave + 4 * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
-      da[q] = zero4();  // only the strictly lower part is kept
-      if (n0 <= m0)
+      da[q] = zero4();  // only the strictly lower part is kept (none for the additive write)
+      if (!ADD && n0 <= m0)
         da[q] = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int k) { return Tl[k * ST + r]; },
                                             [&](int k, int i) { return Zl[k * ST + i]; }, m0);
     }
@@ -617,7 +636,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     }
     const int t = BC - 1 - lane;
     if (t < nv) {
-      p.dbeta[(tb + t) * H + h] = dBs[t];
+      if (!ADD) p.dbeta[(tb + t) * H + h] = dBs[t];
       if (GATE == GATE_HEAD) p.dlog_alpha[(tb + t) * H + h] = g;
     }
   }
@@ -633,9 +652,10 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     }
     const f32x4 q_ = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int r, int i) { return Pl[r * ST + i]; },
                                                 [&](int i, int d) { return K_(i, d); }, 0, m0 + 16);
-    f32x4 k_ = tile_g<E, BC, false, true>(m0, n0, lg, lm,
-                                          [&](int r, int i) { return Zl[r * ST + i] + Zl[i * ST + r]; },
-                                          [&](int i, int d) { return K_(i, d); });
+    f32x4 k_ = zero4();
+    if (!ADD)
+      k_ = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int r, int i) { return Zl[r * ST + i] + Zl[i * ST + r]; },
+                                      [&](int i, int d) { return K_(i, d); });
     k_ += tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int r, int i) { return Pl[i * ST + r]; },
                                      [&](int i, int d) { return Q_(i, d); }, m0);
     const int d = n0 + lm;
@@ -649,33 +669,57 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   }
 }
 
-template <typename E, int DK>
-hipError_t launch_b(const BwdParams &p, int gate, hipStream_t stream) {
+template <typename E, int DK, int GATE, bool ADD>
+void launch_bg(const BwdParams &p, hipStream_t stream) {
   const int nb = p.dv / BVB;
-  const long items = p.slots * p.H;
-  if (p.N == 0 || items == 0) return hipSuccess;
-  if (gate == GATE_HEAD) {
-    hipLaunchKernelGGL((bwd_state_kernel<E, DK, GATE_HEAD>), dim3(p.N * p.H * nb), dim3(BNT), 0, stream, p);
-    hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, GATE_HEAD>), dim3((unsigned)items), dim3(BNT), 0, stream, p);
-  } else if (gate == GATE_NONE) {
-    hipLaunchKernelGGL((bwd_state_kernel<E, DK, GATE_NONE>), dim3(p.N * p.H * nb), dim3(BNT), 0, stream, p);
-    hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, GATE_NONE>), dim3((unsigned)items), dim3(BNT), 0, stream, p);
-  } else {
+  hipLaunchKernelGGL((bwd_state_kernel<E, DK, GATE, ADD>), dim3(p.N * p.H * nb), dim3(BNT), 0, stream, p);
+  hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, GATE, ADD>), dim3((unsigned)(p.slots * p.H)), dim3(BNT), 0, stream, p);
+}
+
+template <typename E, int DK>
+hipError_t launch_b(const BwdParams &p, int gate, bool add, hipStream_t stream) {
+  if (p.N == 0 || p.slots * p.H == 0) return hipSuccess;
+  if (gate == GATE_HEAD)
+    add ? launch_bg<E, DK, GATE_HEAD, true>(p, stream) : launch_bg<E, DK, GATE_HEAD, false>(p, stream);
+  else if (gate == GATE_NONE)
+    add ? launch_bg<E, DK, GATE_NONE, true>(p, stream) : launch_bg<E, DK, GATE_NONE, false>(p, stream);
+  else
     return hipErrorInvalidValue;
-  }
   return hipGetLastError();
+}
+
+// out[h] = sum over t of x[t * H + h], in a fixed order (deterministic): one workgroup
+// per head, a strided partial sum per thread, then a tree in LDS.
+__global__ __launch_bounds__(256) void sum_tokens_kernel(const float *x, long tokens, int H, float *out) {
+  __shared__ float part[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  float acc = 0.f;
+  for (long t = tid; t < tokens; t += 256) acc += x[t * H + h];
+  part[tid] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) part[tid] += part[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) out[h] = part[0];
 }
 
 }  // namespace
 
 size_t bwd_part_floats(int dk) { return dk == 128 ? Part<128>::SIZE : Part<64>::SIZE; }
 
-hipError_t launch_bwd(const BwdParams &p, int dtype, int dk, int gate, hipStream_t stream) {
+hipError_t launch_sum_tokens(const float *x, long tokens, int H, float *out, hipStream_t stream) {
+  if (H <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_tokens_kernel, dim3(H), dim3(256), 0, stream, x, tokens, H, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams &p, int dtype, int dk, int gate, bool add, hipStream_t stream) {
   if (dtype == 1) {
-    if (dk == 128) return launch_b<bf16, 128>(p, gate, stream);
-    if (dk == 64) return launch_b<bf16, 64>(p, gate, stream);
+    if (dk == 128) return launch_b<bf16, 128>(p, gate, add, stream);
+    if (dk == 64) return launch_b<bf16, 64>(p, gate, add, stream);
   } else {
-    if (dk == 64) return launch_b<float, 64>(p, gate, stream);
+    if (dk == 64) return launch_b<float, 64>(p, gate, add, stream);
   }
   return hipErrorInvalidValue;
 }

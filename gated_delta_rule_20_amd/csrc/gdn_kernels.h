@@ -68,20 +68,25 @@ struct DecodeParams {
 // chunks are numbered as for key_slots.
 struct BwdParams {
   const void *q, *k, *v, *dout;  // [tokens, H, d_k] / [tokens, H, d_v], I/O dtype
-  const float *beta, *log_alpha; // [tokens, H]; log_alpha NULL without a gate
+  const float *beta, *log_alpha; // [tokens, H] (beta NULL for the additive write; log_alpha
+                                 // NULL without a gate, read at t * la_stride + h)
   const float *dfinal;           // NULL | [N, H, d_k, d_v]
   const int32_t *cu_seqlens;     // NULL (batch) | [N + 1]
   const float *states;           // [slots, H, d_k, d_v] chunk-entering states
   float *tmat;                   // [slots, H, 64, 64] T of every chunk (written, then read)
   float *part;                   // [slots, H, d_v / 32, bwd_part_floats(d_k)] partial sums
   void *dq, *dk, *dv_out;        // outputs, I/O dtype
-  float *dbeta, *dlog_alpha;     // [tokens, H]; dlog_alpha NULL without a gate
+  float *dbeta, *dlog_alpha;     // [tokens, H]; dbeta NULL for the additive write, dlog_alpha
+                                 // NULL without a gate (per token also for a constant decay)
   float *dinit;                  // NULL | [N, H, d_k, d_v]
   int N, H, T, dv;
+  int la_stride;                 // H, or 0 for one constant decay per head
   long slots;
 };
 size_t bwd_part_floats(int dk);
-hipError_t launch_bwd(const BwdParams &p, int dtype, int dk, int gate, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams &p, int dtype, int dk, int gate, bool add, hipStream_t stream);
+// out[h] = sum over tokens of x[t, h] (deterministic order)
+hipError_t launch_sum_tokens(const float *x, long tokens, int H, float *out, hipStream_t stream);
 
 // Forward of the diagonal-plus-low-rank transition (no gate or the scalar gate).
 struct DplrParams {

@@ -195,9 +195,11 @@ int gdn_fwd_decode(const gdn_decode_args *args, void *hip_stream);
  * Gradients of the chunked forward (training): reverse mode through the chunk
  * equations of "Decoding Hybrid Linear Attention Architectures", sec. 5, written out
  * in this library's kernels (the pages give the forward only).  Supported: the delta
- * write with no gate or one decay per (token, head) (GDN_GATE_NONE, GDN_GATE_HEAD);
- * other modes return GDN_ERR_UNSUPPORTED.  Inputs as for gdn_fwd_chunked (the same
- * validation rules, which this call repeats), plus the gradients of its outputs;
+ * write and the additive write (GDN_WRITE_ADD: gated linear attention / RetNet), each
+ * with no gate, one decay per (token, head) or one constant decay per head
+ * (GDN_GATE_NONE, GDN_GATE_HEAD, GDN_GATE_HEAD_CONST); the per-key-channel gate returns
+ * GDN_ERR_UNSUPPORTED.  Inputs as for gdn_fwd_chunked (the same validation rules, which
+ * this call repeats), plus the gradients of its outputs;
  * the forward is recomputed inside the call (chunk-entering states into the
  * workspace), so nothing of the forward call needs to be kept.  All arithmetic is
  * fp32; dq, dk, dv are rounded once to dtype.  Deterministic (no atomics).
@@ -208,16 +210,18 @@ typedef struct {
   gdn_gate gate;
   gdn_write write;
   const void *q, *k, *v;           /* as in gdn_fwd_args                          */
-  const float *beta;               /* [B, T, H]                                   */
-  const float *log_alpha;          /* NONE: NULL; HEAD: [B, T, H]                 */
+  const float *beta;               /* DELTA: [B, T, H]; ADD: NULL                 */
+  const float *log_alpha;          /* NONE: NULL; HEAD: [B, T, H]; HEAD_CONST: [H] */
   const float *initial_state;      /* NULL (zeros) or [N, H, d_k, d_v]            */
   const int32_t *cu_seqlens;       /* NULL or [N + 1] int32 (device)              */
   const void *dout;                /* [B, T, H, d_v], dtype: gradient of o        */
   const float *dfinal_state;       /* NULL (zeros) or [N, H, d_k, d_v]: gradient of
                                       the final state                             */
   void *dq, *dk, *dv;              /* out: [B, T, H, d_k] / [B, T, H, d_v], dtype */
-  float *dbeta;                    /* out: [B, T, H]                              */
-  float *dlog_alpha;               /* out: HEAD: [B, T, H]; NONE: NULL            */
+  float *dbeta;                    /* out: DELTA: [B, T, H]; ADD: NULL            */
+  float *dlog_alpha;               /* out: HEAD: [B, T, H]; HEAD_CONST: [H] (the
+                                      sum over all tokens, written also when there
+                                      are none); NONE: NULL                       */
   float *dinitial_state;           /* out: NULL or [N, H, d_k, d_v]               */
   void *workspace;                 /* gdn_bwd_workspace_size() bytes, 256-aligned */
   size_t workspace_bytes;
@@ -225,13 +229,15 @@ typedef struct {
 
 /* Bytes of device workspace gdn_bwd_chunked needs (0 for arguments it would reject):
  * with S = floor(B T / 64) + N chunk slots, the chunk-entering states (4 d_k d_v
- * bytes per slot and head), T of every chunk (16 KiB per slot and head) and the
- * partial sums over value columns (d_v / 32 records of 4 (8192 + 128 d_k + 192) bytes
- * per slot and head), each rounded up to 256 bytes.  Owned by the caller; no
- * initialisation needed. */
+ * bytes per slot and head), T of every chunk (delta write only: 16 KiB per slot and
+ * head), the partial sums over value columns (d_v / 32 records of 4 (8192 + 128 d_k +
+ * 192) bytes per slot and head) and, for the constant per-head decay, the per-token
+ * decay gradients (4 bytes per token and head), each rounded up to 256 bytes.  Owned
+ * by the caller; no initialisation needed. */
 size_t gdn_bwd_workspace_size(const gdn_bwd_args *args);
 
-/* Gradients: writes dq, dk, dv, dbeta, dlog_alpha (HEAD) and dinitial_state (if given). */
+/* Gradients: writes dq, dk, dv, dbeta (DELTA), dlog_alpha (a gate) and dinitial_state
+ * (if given). */
 int gdn_bwd_chunked(const gdn_bwd_args *args, void *hip_stream);
 
 /*

@@ -297,8 +297,11 @@ def bwd_args(g, **kw):
 
 @pytest.mark.parametrize("change,status", [
     (dict(gate=2, log_alpha=fake(4, 0), dlog_alpha=fake(10)), UNSUPPORTED),  # per-key gate
-    (dict(gate=3, dlog_alpha=fake(10)), UNSUPPORTED),                         # constant gate
-    (dict(write=1, beta=None), UNSUPPORTED),                                  # additive write
+    (dict(gate=3, dlog_alpha=fake(10)), WORKSPACE),                           # constant gate: valid
+    (dict(gate=3, dlog_alpha=None), INVALID),                                 # ... needs its [H] gradient
+    (dict(write=1, beta=None, dbeta=None), WORKSPACE),                        # additive write: valid
+    (dict(write=1, beta=None), INVALID),                                      # ... and has no dbeta
+    (dict(write=1, dbeta=None), INVALID),                                     # ... nor beta
     (dict(dout=None), INVALID),
     (dict(dq=None), INVALID),
     (dict(dbeta=None), INVALID),
@@ -322,6 +325,11 @@ def test_bwd_workspace_size(g):
                                                    slots * 4 * 4 * part * 4))
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(a)) == expect
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(bwd_args(g, dq=None))) == 0
+    # the additive write keeps no T; the constant gate adds the per-token decay gradients
+    add = bwd_args(g, write=1, beta=None, dbeta=None)
+    assert g._lib.gdn_bwd_workspace_size(ctypes.byref(add)) == expect - slots * 4 * 4096 * 4
+    const = bwd_args(g, gate=3)
+    assert g._lib.gdn_bwd_workspace_size(ctypes.byref(const)) == expect + 2 * 128 * 4 * 4
 
 
 def dplr_args(g, **kw):
