@@ -179,6 +179,41 @@ def time_decode(gdn, spec, final_states, steps=64):
             "hbm_gbs": bytes_step / (ms / 1e3) / 1e9, "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
 
 
+def time_dplr_step(gdn, N=256, H=16, dk=128, dv=128, steps=64):
+    """gdn_fwd_dplr_step, one token per stream, scalar gate, state in place (N x H states
+    of d_k x d_v fp32, 268 MB at the default shape).  Algorithmic bytes per stream and
+    head: the state read and written in fp32, q, k, a, b, v read and o written in bf16,
+    log alpha read."""
+    import torch
+    import synth
+    inp = synth.dplr_inputs(N, steps, H, dk, dv, "head", "bf16", seed=1107, state_std=0.02)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    tok = {k: [d[k][:, s].contiguous() for s in range(steps)] for k in ("q", "k", "v", "a", "b", "log_alpha")}
+    st = d["initial_state"].clone()
+    out = torch.empty((N, H, dv), dtype=torch.bfloat16, device="cuda")
+    call = lambda s: gdn.dplr_step(tok["q"][s], tok["k"][s], tok["v"][s], tok["a"][s], tok["b"][s],
+                                   tok["log_alpha"][s], st, out=out)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    call(0)
+    torch.cuda.synchronize()
+    warm = max(4, int(SETTLE_MS / 1e3 / (time.perf_counter() - t)) + 1)
+    for i in range(warm):
+        call(i % steps)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        call(s)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    bytes_step = N * H * (2 * 4 * dk * dv + 2 * (4 * dk + 2 * dv) + 4)
+    return {"workload": "dplr-decode-bf16-N%d-H%d-d%d" % (N, H, dk), "ms_per_step": ms,
+            "tokens_per_s": N / (ms / 1e3), "hbm_gbs": bytes_step / (ms / 1e3) / 1e9,
+            "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+
+
 def time_pool_decode(gdn, N, L, H, dk, dv, store, steps=64):
     """gdn_fwd_decode: L tokens for each of N streams per call, states in a pool.
     ``store="last"`` writes each stream's state back in place; ``"all"`` stores the
@@ -391,6 +426,8 @@ def main():
             del wsets
             torch.cuda.empty_cache()
             extra.append(r)
+        extra.append(time_dplr_step(gdn))
+        torch.cuda.empty_cache()
         extra.append(time_bwd(gdn, HEADLINE))
         torch.cuda.empty_cache()
         extra.append(time_bwd(gdn, "retnet-bf16-B16-T2048-H8-d128"))

@@ -8,8 +8,8 @@ raises on import.
 
 The names follow the C ABI: ``fwd_chunked`` wraps ``gdn_fwd_chunked``,
 ``recurrent_step`` wraps ``gdn_fwd_recurrent_step``, ``decode`` wraps
-``gdn_fwd_decode``, ``bwd_chunked`` wraps ``gdn_bwd_chunked`` and ``fwd_dplr``
-wraps ``gdn_fwd_dplr``.
+``gdn_fwd_decode``, ``bwd_chunked`` wraps ``gdn_bwd_chunked``, ``fwd_dplr`` wraps
+``gdn_fwd_dplr`` and ``dplr_step`` wraps ``gdn_fwd_dplr_step``.
 """
 from __future__ import annotations
 
@@ -89,6 +89,15 @@ class DplrArgs(ctypes.Structure):
                 ("o", ctypes.c_void_p), ("final_state", ctypes.c_void_p)]
 
 
+class DplrStepArgs(ctypes.Structure):
+    """Mirror of ``gdn_dplr_step_args``."""
+    _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("d_k", ctypes.c_int), ("d_v", ctypes.c_int),
+                ("dtype", ctypes.c_int), ("gate", ctypes.c_int),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p), ("state", ctypes.c_void_p),
+                ("o", ctypes.c_void_p)]
+
+
 def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError("libgdn.so is not built (%s); run `python __graft_entry__.py build` "
@@ -106,6 +115,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
     lib.gdn_bwd_chunked.restype = ctypes.c_int
     lib.gdn_bwd_chunked.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
+    lib.gdn_fwd_dplr_step.restype = ctypes.c_int
+    lib.gdn_fwd_dplr_step.argtypes = [ctypes.POINTER(DplrStepArgs), ctypes.c_void_p]
     lib.gdn_fwd_dplr.restype = ctypes.c_int
     lib.gdn_fwd_dplr.argtypes = [ctypes.POINTER(DplrArgs), ctypes.c_void_p]
     lib.gdn_status_str.restype = ctypes.c_char_p
@@ -444,6 +455,29 @@ def fwd_dplr(q, k, v, a, b, log_alpha=None, initial_state=None, cu_seqlens=None,
     p = PreparedDplr(q, k, v, a, b, log_alpha, initial_state, cu_seqlens, out, final_state,
                      output_final_state, chunk)
     return p.launch(stream)
+
+
+def dplr_step(q, k, v, a, b, log_alpha, state, out=None, stream=None):
+    """One decode token per stream of the diagonal-plus-low-rank transition
+    (gdn_fwd_dplr_step): q, k, a, b [N,H,d_k], v [N,H,d_v] (one dtype), log_alpha None |
+    [H] | [N,H] | [N,H,d_k] fp32, state [N,H,d_k,d_v] fp32 updated in place.  Returns o
+    [N,H,d_v]."""
+    import torch
+    for name, t in (("a", a), ("b", b)):
+        _require(t is not None and tuple(t.shape) == tuple(q.shape) and t.dtype == q.dtype,
+                 "%s must have the shape and dtype of q" % name)
+        _require(t.is_contiguous(), "%s must be contiguous" % name)
+    check_step_tensors(q, k, v, None, log_alpha, state, out, write="add")
+    _same_device([("a", a), ("b", b)], q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    args = DplrStepArgs(N=N, H=H, d_k=dk, d_v=dv, dtype=_dtype_code(q), gate=gate_code(log_alpha, 2),
+                        q=_ptr(q), k=_ptr(k), a=_ptr(a), b=_ptr(b), v=_ptr(v), log_alpha=_ptr(log_alpha),
+                        state=_ptr(state), o=_ptr(out))
+    _check(_lib.gdn_fwd_dplr_step(ctypes.byref(args), _stream(stream)), "gdn_fwd_dplr_step")
+    return out
 
 
 def recurrent_step(q, k, v, beta, log_alpha, state, out=None, stream=None, write: str = "delta"):

@@ -559,6 +559,114 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
     }
 }
 
+// One token per stream, the state updated in place (the constant-cost decode step of
+// "Decoding Hybrid Linear Attention Architectures", sec. 6, for this transition).  With
+// the state M (rows d, columns j) read once:
+//   u_j = sum_d a_d M[d][j],  s_j = sum_d q_d alpha_d M[d][j]
+//   M'  = Diag(alpha) M + b u^T + k v^T,   o_j = s_j + (q . b) u_j + (q . k) v_j
+// One workgroup per (stream, head); each thread keeps RP rows x 4 columns of M in
+// registers, the two column reductions go through LDS.
+template <typename E, int DK, int DV, int GATE>
+__global__ __launch_bounds__(256) void dplr_step_kernel(DplrStepParams p) {
+  constexpr int CQ = DV / 4;    // column quads
+  constexpr int RG = 256 / CQ;  // row groups
+  constexpr int RP = DK / RG;   // rows per thread
+  static_assert(RP >= 1 && RG * RP == DK, "step geometry");
+  __shared__ float qs[DK], as_[DK], bs_[DK], ks[DK], al[DK];
+  __shared__ f32x4 red_u[RG][CQ], red_s[RG][CQ];
+  __shared__ float dots[2];
+
+  const int pair = blockIdx.x;  // stream * H + head
+  const int tid = threadIdx.x, cq = tid % CQ, rg = tid / CQ;
+  const size_t rowk = (size_t)pair * DK;
+  if (tid < DK) {
+    qs[tid] = to_f(((const E *)p.q)[rowk + tid]);
+    as_[tid] = to_f(((const E *)p.a)[rowk + tid]);
+    bs_[tid] = to_f(((const E *)p.b)[rowk + tid]);
+    ks[tid] = to_f(((const E *)p.k)[rowk + tid]);
+    float a = 1.f;
+    if (GATE == GATE_HEAD) a = __expf(p.log_alpha[(size_t)(pair / p.H) * p.la_stride + pair % p.H]);
+    if (GATE == GATE_KEY) a = __expf(p.log_alpha[rowk + tid]);
+    al[tid] = a;
+  }
+  float *st = p.state + (size_t)pair * DK * DV;
+  f32x4 m[RP];
+#pragma unroll
+  for (int u = 0; u < RP; ++u) m[u] = *(const f32x4 *)(st + (size_t)(rg * RP + u) * DV + 4 * cq);
+  const E *vp = (const E *)p.v + (size_t)pair * DV + 4 * cq;  // needed only after the reductions
+  f32x4 vv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vv[e] = to_f(vp[e]);
+  __syncthreads();
+
+  f32x4 uu = zero4(), ss = zero4();
+#pragma unroll
+  for (int u = 0; u < RP; ++u) {
+    const int row = rg * RP + u;
+    uu += m[u] * as_[row];
+    ss += m[u] * (qs[row] * al[row]);
+  }
+  red_u[rg][cq] = uu;
+  red_s[rg][cq] = ss;
+  if (tid < 64) {  // q . b and q . k
+    float db = 0.f, dk = 0.f;
+    for (int i = tid; i < DK; i += 64) {
+      db += qs[i] * bs_[i];
+      dk += qs[i] * ks[i];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      db += __shfl_xor(db, off);
+      dk += __shfl_xor(dk, off);
+    }
+    if (tid == 0) {
+      dots[0] = db;
+      dots[1] = dk;
+    }
+  }
+  __syncthreads();
+
+  f32x4 U = zero4(), S = zero4();
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    U += red_u[g][cq];
+    S += red_s[g][cq];
+  }
+#pragma unroll
+  for (int u = 0; u < RP; ++u) {
+    const int row = rg * RP + u;
+    *(f32x4 *)(st + (size_t)row * DV + 4 * cq) = m[u] * al[row] + U * bs_[row] + vv * ks[row];
+  }
+  if (rg == 0) {
+    E *o = (E *)p.o + (size_t)pair * DV + 4 * cq;
+    const float qb = dots[0], qk = dots[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = to_e<E>(S[e] + qb * U[e] + qk * vv[e]);
+  }
+}
+
+template <typename E, int DK, int DV>
+hipError_t launch_ds(const DplrStepParams &p, int gate, hipStream_t stream) {
+  const dim3 grid(p.N * p.H), block(256);
+  if (gate == GATE_NONE)
+    hipLaunchKernelGGL((dplr_step_kernel<E, DK, DV, GATE_NONE>), grid, block, 0, stream, p);
+  else if (gate == GATE_HEAD)
+    hipLaunchKernelGGL((dplr_step_kernel<E, DK, DV, GATE_HEAD>), grid, block, 0, stream, p);
+  else if (gate == GATE_KEY)
+    hipLaunchKernelGGL((dplr_step_kernel<E, DK, DV, GATE_KEY>), grid, block, 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+template <typename E>
+hipError_t launch_ds_e(const DplrStepParams &p, int dk, int dv, int gate, hipStream_t stream) {
+  if (dk == 64 && dv == 64) return launch_ds<E, 64, 64>(p, gate, stream);
+  if (dk == 64 && dv == 128) return launch_ds<E, 64, 128>(p, gate, stream);
+  if (dk == 128 && dv == 64) return launch_ds<E, 128, 64>(p, gate, stream);
+  if (dk == 128 && dv == 128) return launch_ds<E, 128, 128>(p, gate, stream);
+  return hipErrorInvalidValue;
+}
+
 template <typename E, int DK>
 hipError_t launch_dp(const DplrParams &p, int gate, hipStream_t stream) {
   const int blocks = p.N * p.H * (p.dv / DVB);
@@ -579,6 +687,11 @@ hipError_t launch_dp(const DplrParams &p, int gate, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_dplr_step(const DplrStepParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream) {
+  if (p.N == 0) return hipSuccess;
+  return dtype == 1 ? launch_ds_e<bf16>(p, dk, dv, gate, stream) : launch_ds_e<float>(p, dk, dv, gate, stream);
+}
 
 hipError_t launch_dplr(const DplrParams &p, int dtype, int dk, int gate, hipStream_t stream) {
   if (dtype == 1) {

@@ -99,6 +99,15 @@ struct DplrParams {
   int N, H, T, dv;
 };
 hipError_t launch_dplr(const DplrParams &p, int dtype, int dk, int gate, hipStream_t stream);
+// One decode token per stream of the diagonal-plus-low-rank transition, state in place.
+struct DplrStepParams {
+  const void *q, *k, *v, *a, *b;  // [N, H, d_k] (v: d_v), I/O dtype
+  const float *log_alpha;         // NULL | [N, H] (read at n * la_stride + h) | [N, H, d_k]
+  float *state;                   // [N, H, d_k, d_v], read then overwritten
+  void *o;                        // [N, H, d_v]
+  int N, H, la_stride;
+};
+hipError_t launch_dplr_step(const DplrStepParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream);
 
 // dtype: 0 fp32, 1 bf16.  Each launcher returns hipSuccess or the launch error.
 // dvb: columns of d_v per workgroup (32 or 64).

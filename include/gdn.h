@@ -275,6 +275,26 @@ typedef struct {
 /* Diagonal-plus-low-rank forward: writes o (and final_state when non-NULL). */
 int gdn_fwd_dplr(const gdn_dplr_args *args, void *hip_stream);
 
+/* One decode token per stream of the diagonal-plus-low-rank transition, the state
+ * updated in place (the constant-cost decode update of "Decoding Hybrid Linear
+ * Attention Architectures", sec. 6, with the transition of sec. 3 item 5):
+ *   M' = Diag(alpha) M + b (a^T M) + k v^T,   o = M'^T q.
+ * All gates (none, one decay per (stream, head), one constant decay per head [H], one
+ * per key channel); any dtype; d_k, d_v in {64, 128}.  Validation as for
+ * gdn_fwd_recurrent_step. */
+typedef struct {
+  int N, H, d_k, d_v;     /* streams, heads, head dims (each 64 or 128)                */
+  gdn_dtype dtype;        /* dtype of q, k, a, b, v, o                                 */
+  gdn_gate gate;
+  const void *q, *k, *a, *b; /* [N, H, d_k]                                            */
+  const void *v;          /* [N, H, d_v]                                               */
+  const float *log_alpha; /* NONE: NULL; HEAD: [N,H]; KEY: [N,H,d_k]; HEAD_CONST: [H]   */
+  float *state;           /* in/out: [N, H, d_k, d_v] fp32 (M = S^T), 16-byte aligned  */
+  void *o;                /* out: [N, H, d_v], dtype                                   */
+} gdn_dplr_step_args;
+
+int gdn_fwd_dplr_step(const gdn_dplr_step_args *args, void *hip_stream);
+
 /* Static description of a status code (never NULL). */
 const char *gdn_status_str(int status);
 

@@ -50,7 +50,7 @@ def fwd(g, a):
 
 def test_header_declares_the_boundary(g):
     assert g.header_functions() == ["gdn_bwd_chunked", "gdn_bwd_workspace_size", "gdn_fwd_chunked",
-                                    "gdn_fwd_decode", "gdn_fwd_dplr", "gdn_fwd_recurrent_step",
+                                    "gdn_fwd_decode", "gdn_fwd_dplr", "gdn_fwd_dplr_step", "gdn_fwd_recurrent_step",
                                     "gdn_fwd_workspace_size", "gdn_status_str", "gdn_version"]
 
 
@@ -369,3 +369,36 @@ def test_binding_rejects_bad_dplr_tensors(g):
         g.fwd_dplr(q, q, v, q, q.float())
     with pytest.raises(ValueError, match="GPU device"):
         g.fwd_dplr(q, q, v, q, q)
+
+
+def dplr_step_args(g, **kw):
+    a = g.DplrStepArgs(N=3, H=2, d_k=128, d_v=64, dtype=g.GDN_BF16, gate=g.GDN_GATE_HEAD)
+    a.q, a.k, a.a, a.b, a.v, a.log_alpha, a.state, a.o = (fake(i) for i in range(8))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(gate=9), INVALID),
+    (dict(a=None), INVALID),
+    (dict(b=None), INVALID),
+    (dict(log_alpha=None), INVALID),
+    (dict(gate=0), INVALID),                 # no gate: no decays either
+    (dict(state=fake(6, 8)), INVALID),       # the state needs 16-byte alignment
+    (dict(d_v=96), UNSUPPORTED),
+    (dict(N=0), OK),                         # nothing to do, nothing launched
+])
+def test_dplr_step_host_validation(g, change, status):
+    assert g._lib.gdn_fwd_dplr_step(ctypes.byref(dplr_step_args(g, **change)), None) == status
+    assert g._lib.gdn_fwd_dplr_step(None, None) == INVALID
+
+
+def test_binding_rejects_bad_dplr_step_tensors(g):
+    q = torch.zeros(2, 3, 64, dtype=torch.bfloat16)
+    v = torch.zeros(2, 3, 64, dtype=torch.bfloat16)
+    st = torch.zeros(2, 3, 64, 64)
+    with pytest.raises(ValueError, match="b must have the shape"):
+        g.dplr_step(q, q, v, q, q[:1], None, st)
+    with pytest.raises(ValueError, match="GPU device"):
+        g.dplr_step(q, q, v, q, q, None, st)

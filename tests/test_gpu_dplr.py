@@ -1,5 +1,6 @@
-"""GPU parity of the diagonal-plus-low-rank transition forward (gdn_fwd_dplr), through
-the C ABI, against the fp64 oracle (oracle.fwd_dplr, the token recurrence).
+"""GPU parity of the diagonal-plus-low-rank transition, the chunked forward
+(gdn_fwd_dplr) and the decode step (gdn_fwd_dplr_step), through the C ABI, against the
+fp64 oracle (oracle.fwd_dplr, the token recurrence).
 
 Metric: max |x - x_ref| / max |x_ref| per output tensor; 2e-2 for bf16 inputs, 1e-4
 for the fp32 mode.  The oracle sees the same (rounded) inputs.  Inputs: synth's
@@ -96,3 +97,53 @@ def test_dplr_empty_and_aliased_state(gdn):
 def test_dplr_workload_full_size(gdn):
     """The 350M-class shape (B16, T2048, H8, d128), every output against the oracle."""
     run(gdn, synth.workload_inputs("dplr-bf16-B16-T2048-H8-d128"))
+
+
+def step_case(N, H, dk, dv, gate, dtype, seed, T=1):
+    """T tokens for N streams (gate: none | head | key | const) and a random state."""
+    inp = synth.dplr_inputs(N, T, H, dk, dv, "head" if gate == "const" else gate, dtype, seed=seed, state_std=0.3)
+    if gate == "const":
+        inp["log_alpha"] = synth.retnet_log_gamma(H)
+    return inp
+
+
+def oracle_la(inp, gate, N, T):
+    la = inp["log_alpha"]
+    if gate == "const":  # the oracle takes the constant decay broadcast to every token
+        la = la[None, None, :].expand(N, T, la.shape[0]).contiguous()
+    return la
+
+
+@pytest.mark.parametrize("gate", ["none", "head", "key", "const"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dplr_step(gdn, gate, dk, dv, dtype):
+    N, H = 5, 3
+    inp = step_case(N, H, dk, dv, gate, dtype, seed=dk + 2 * dv + len(gate))
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    sq = lambda t: None if t is None else (t if t.dim() == 1 else t[:, 0].contiguous())
+    state = d["initial_state"].clone()
+    o = gdn.dplr_step(sq(d["q"]), sq(d["k"]), sq(d["v"]), sq(d["a"]), sq(d["b"]), sq(d["log_alpha"]), state)
+    torch.cuda.synchronize()
+    o_ref, fs_ref = oracle.fwd_dplr(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], oracle_la(inp, gate, N, 1),
+                                    inp["initial_state"])
+    tol = TOL[dtype]
+    assert relerr(o, o_ref[:, 0]) <= tol and relerr(state, fs_ref) <= max(tol, 1e-5)
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_dplr_steps_equal_forward(gdn, gate):
+    """Seven chained steps equal the oracle's recurrence over the same seven tokens."""
+    N, H, T = 4, 2, 7
+    inp = step_case(N, H, 128, 128, gate, "bf16", seed=21, T=T)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    state = d["initial_state"].clone()
+    outs = []
+    for t in range(T):
+        pick = lambda x: x[:, t].contiguous()
+        outs.append(gdn.dplr_step(pick(d["q"]), pick(d["k"]), pick(d["v"]), pick(d["a"]), pick(d["b"]),
+                                  pick(d["log_alpha"]), state))
+    torch.cuda.synchronize()
+    o_ref, fs_ref = oracle.fwd_dplr(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["log_alpha"],
+                                    inp["initial_state"])
+    assert relerr(torch.stack(outs, 1), o_ref) <= TOL["bf16"] and relerr(state, fs_ref) <= 1e-5
