@@ -12,7 +12,7 @@
 //   P_qb[r,j] = (q_r . b_j) e^{G_r - G_j},  P_qk[r,j] = (q_r . k_j) e^{G_r - G_j}  (j <= r)
 //   M_C = e^{G_C} M0 + (diag(e^{G_C - G}) B)^T U + (diag(e^{G_C - G}) K)^T V.
 //
-// One workgroup (4 waves) per (sequence, head, 32 value columns) walks its sequence;
+// One workgroup (4 waves; 8 for bf16) per (sequence, head, 32 value columns) walks its sequence;
 // the state block (d_k x 32, fp32) stays in LDS.  T = (I - A_ab)^-1 by forward
 // substitution of the 16x16 diagonal blocks and block substitution of the rest.  Two
 // kernels: fp32 I/O (d_k = 64) on the fp32 matrix cores with operands gathered from
@@ -28,7 +28,9 @@ namespace gdn {
 namespace {
 
 constexpr int DC = 64;    // chunk length
-constexpr int DNT = 256;  // threads per workgroup
+constexpr int DNT = 256;  // threads per workgroup (fp32 kernel)
+constexpr int DNB = 512;  // threads per workgroup (bf16 kernel): two waves per SIMD
+constexpr int NWB = DNB / 64;
 constexpr int DVB = 32;   // value columns per workgroup
 constexpr int DSV = DVB + 1, DST = DC + 1;
 
@@ -261,13 +263,14 @@ __global__ __launch_bounds__(DNT, 1) void dplr_fwd_kernel(DplrParams p) {
 // update come from the transposing LDS read.  The next chunk's inputs are loaded into
 // registers while the current one computes.
 template <int DK, int GATE>
-__global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
+__global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
   constexpr int SKE = DK + 8;  // bf16 row pitch of Q, K, A, B
   constexpr int SX = DC + 4;   // fp32 row pitch of the 64 x 64 tiles
   constexpr int SM = DK + 4;   // fp32 row pitch of M^T
   constexpr int SVT = DC + 8;  // bf16 row pitch of V^T
   constexpr int SR = DC + 4;   // fp32 row pitch of R^T and U^T
-  constexpr int RK = DC * DK / 8 / DNT;  // 16-byte pieces of a [64][DK] operand per thread
+  constexpr int RK = DC * DK / 8 / DNB;  // 16-byte pieces of a [64][DK] operand per thread
+  constexpr int OQ = 8 / NWB;             // 64 x 32 output tiles per wave
   __shared__ __align__(16) bf16 Ql[DC * SKE];
   __shared__ __align__(16) bf16 Kl[DC * SKE];
   __shared__ __align__(16) bf16 Al[DC * SKE];
@@ -310,11 +313,11 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
     return [=](int k0) { return split8(ld8(base + k0)); };
   };
 
-  for (int i = tid; i < DK * DVB; i += DNT) {
+  for (int i = tid; i < DK * DVB; i += DNB) {
     const int d = i / DVB, j = i % DVB;
     Mt[j * SM + d] = p.init_state ? p.init_state[sstate + (size_t)d * dv + j] : 0.f;
   }
-  for (int i = tid; i < DC * SX; i += DNT) Tb[i] = X1[i] = 0.f;  // upper blocks stay zero
+  for (int i = tid; i < DC * SX; i += DNB) Tb[i] = X1[i] = 0.f;  // upper blocks stay zero
 
   // ---- a chunk's inputs: 16-byte loads into registers one chunk ahead (rows past the
   // sequence end re-read its last row and are zeroed when staged)
@@ -325,14 +328,14 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
     const size_t tbc = (size_t)tok0 + (size_t)cc * DC;
 #pragma unroll
     for (int u = 0; u < RK; ++u) {
-      const int pc = tid + DNT * u, r = min(pc / (DK / 8), last), g = pc % (DK / 8);
+      const int pc = tid + DNB * u, r = min(pc / (DK / 8), last), g = pc % (DK / 8);
       const size_t o = ((tbc + r) * H + h) * DK + g * 8;
       pq[u] = *(const u32x4 *)((const bf16 *)p.q + o);
       pk[u] = *(const u32x4 *)((const bf16 *)p.k + o);
       pa[u] = *(const u32x4 *)((const bf16 *)p.a + o);
       pb[u] = *(const u32x4 *)((const bf16 *)p.b + o);
     }
-    {
+    if (tid < DC * DVB / 8) {  // V: one 16-byte piece per thread of the first 256
       const int r = min(tid / 4, last), g = tid % 4;
       pv = *(const u32x4 *)((const bf16 *)p.v + ((tbc + r) * H + h) * dv + col0 + 8 * g);
     }
@@ -351,14 +354,14 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
       opaque(pk[u]);
       opaque(pa[u]);
       opaque(pb[u]);
-      const int pc = tid + DNT * u, r = pc / (DK / 8), g = pc % (DK / 8);
+      const int pc = tid + DNB * u, r = pc / (DK / 8), g = pc % (DK / 8);
       if (r >= nv) pq[u] = pk[u] = pa[u] = pb[u] = (u32x4){0u, 0u, 0u, 0u};
       *(u32x4 *)(Ql + r * SKE + g * 8) = pq[u];
       *(u32x4 *)(Kl + r * SKE + g * 8) = pk[u];
       *(u32x4 *)(Al + r * SKE + g * 8) = pa[u];
       *(u32x4 *)(Bl + r * SKE + g * 8) = pb[u];
     }
-    {
+    if (tid < DC * DVB / 8) {
       opaque(pv);
       const int r = tid / 4, g = tid % 4;
       const bf16x8 v8 = __builtin_bit_cast(bf16x8, pv);
@@ -388,10 +391,10 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
     auto e_in = [&](int j, int i) {  // e^{G_{j-1} - G_i}, i < j
       return i < j ? (GATE == GATE_HEAD ? __expf((j > 0 ? gs[j - 1] : 0.f) - gs[i]) : 1.f) : 0.f;
     };
-    // X1 = lower(R C^T * fac): the 10 lower 16x16 tiles, 3/3/2/2 per wave (the upper
+    // X1 = lower(R C^T * fac): the 10 lower 16x16 tiles over the waves (the upper
     // ones were zeroed once and are never written)
     auto gram = [&](const bf16 *R, const bf16 *Cm, auto fac) {
-      for (int t = wave; t < 10; t += 4) {
+      for (int t = wave; t < 10; t += NWB) {
         const int mb = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
         const int m0 = 16 * mb, n0 = 16 * (t - mb * (mb + 1) / 2);
         const f32x4 v = tile_frag<DK>(rowb(R, SKE, m0 + lm), rowb(Cm, SKE, n0 + lm));
@@ -404,15 +407,15 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
     };
     // output tiles of a 64 x 32 product: two per wave
     auto otile = [&](int q, int &m0, int &n0) {
-      const int t = wave + 4 * q;
+      const int t = wave + NWB * q;
       m0 = (t >> 1) * 16;
       n0 = (t & 1) * 16;
     };
     auto kend = [](int m0) { return m0 < 32 ? 32 : 64; };  // last nonzero column of a lower row block
     // ---- O = diag(e^G) Q M0 in registers; P_qk into X1
-    f32x4 Oacc[2];
+    f32x4 Oacc[OQ];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < OQ; ++q) {
       int m0, n0;
       otile(q, m0, n0);
       const f32x4 v = tile_frag<DK>(rowb(Ql, SKE, m0 + lm), rowf(Mt, SM, n0 + lm));
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
     __syncthreads();
     // ---- O += P_qk V
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < OQ; ++q) {
       int m0, n0;
       otile(q, m0, n0);
       Oacc[q] += tile_frag<DC>(rowf(X1, SX, m0 + lm), rowb(Vt, SVT, n0 + lm), kend(m0));
@@ -486,7 +489,7 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
     gram(Al, Kl, e_in);
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < OQ; ++q) {
       int m0, n0;
       otile(q, m0, n0);
       const f32x4 v = tile_frag<DK>(rowb(Al, SKE, m0 + lm), rowf(Mt, SM, n0 + lm));
@@ -499,7 +502,7 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
     __syncthreads();
     // ---- U = T R into U^T
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < OQ; ++q) {
       int m0, n0;
       otile(q, m0, n0);
       const f32x4 v = tile_frag<DC>(rowf(Tb, SX, m0 + lm), rowf(Rt, SR, n0 + lm), kend(m0));
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
     gram(Ql, Bl, e_out);
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < OQ; ++q) {
       int m0, n0;
       otile(q, m0, n0);
       Oacc[q] += tile_frag<DC>(rowf(X1, SX, m0 + lm), rowf(Ut, SR, n0 + lm), kend(m0));
@@ -522,12 +525,12 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
     }
     // ---- M <- e^{G_C} M + B^T diag(e^{G_C - G}) U + K^T diag(e^{G_C - G}) V   (DK x 32)
     {
-      constexpr int TPW = (DK / 16) * 2 / 4;  // tiles per wave
+      constexpr int TPW = (DK / 16) * 2 / NWB;  // tiles per wave
       f32x4 nm[TPW];
       const float gam = misc[0];
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
-        const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+        const int t = wave + NWB * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
         const float *urow = Ut + (n0 + lm) * SR + 8 * lg;
         const bf16 *vrow = Vt + (n0 + lm) * SVT + 8 * lg;
         const f32x4 t1 = tile_frag<DC>([&](int k0) { return col_frag(Bl, SKE, k0, m0, lg, lm); },
@@ -546,14 +549,14 @@ __global__ __launch_bounds__(DNT, 1) void dplr_bf16_kernel(DplrParams p) {
       __syncthreads();  // every read of the old state is done
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
-        const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+        const int t = wave + NWB * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
         *(f32x4 *)(Mt + (n0 + lm) * SM + m0 + 4 * lg) = nm[q];
       }
     }
   }
   __syncthreads();
   if (p.final_state)
-    for (int i = tid; i < DK * DVB; i += DNT) {
+    for (int i = tid; i < DK * DVB; i += DNB) {
       const int d = i / DVB, j = i % DVB;
       p.final_state[sstate + (size_t)d * dv + j] = Mt[j * SM + d];
     }
@@ -674,9 +677,9 @@ hipError_t launch_dp(const DplrParams &p, int gate, hipStream_t stream) {
   if (gate != GATE_HEAD && gate != GATE_NONE) return hipErrorInvalidValue;
   if constexpr (std::is_same<E, bf16>::value) {
     if (gate == GATE_HEAD)
-      hipLaunchKernelGGL((dplr_bf16_kernel<DK, GATE_HEAD>), dim3(blocks), dim3(DNT), 0, stream, p);
+      hipLaunchKernelGGL((dplr_bf16_kernel<DK, GATE_HEAD>), dim3(blocks), dim3(DNB), 0, stream, p);
     else
-      hipLaunchKernelGGL((dplr_bf16_kernel<DK, GATE_NONE>), dim3(blocks), dim3(DNT), 0, stream, p);
+      hipLaunchKernelGGL((dplr_bf16_kernel<DK, GATE_NONE>), dim3(blocks), dim3(DNB), 0, stream, p);
   } else {
     if (gate == GATE_HEAD)
       hipLaunchKernelGGL((dplr_fwd_kernel<E, DK, GATE_HEAD>), dim3(blocks), dim3(DNT), 0, stream, p);
