@@ -277,6 +277,7 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
   __shared__ __align__(16) bf16 Bl[DC * SKE];
   __shared__ __align__(16) bf16 Vt[DVB * SVT];
   __shared__ __align__(16) float X1[DC * SX];
+  __shared__ __align__(16) float X2[DC * SX];
   __shared__ __align__(16) float Tb[DC * SX];
   __shared__ __align__(16) float Mt[DVB * SM];
   __shared__ __align__(16) float Rt[DVB * SR];
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
     const int d = i / DVB, j = i % DVB;
     Mt[j * SM + d] = p.init_state ? p.init_state[sstate + (size_t)d * dv + j] : 0.f;
   }
-  for (int i = tid; i < DC * SX; i += DNB) Tb[i] = X1[i] = 0.f;  // upper blocks stay zero
+  for (int i = tid; i < DC * SX; i += DNB) Tb[i] = X1[i] = X2[i] = 0.f;  // upper blocks stay zero
 
   // ---- a chunk's inputs: 16-byte loads into registers one chunk ahead (rows past the
   // sequence end re-read its last row and are zeroed when staged)
@@ -391,17 +392,17 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
     auto e_in = [&](int j, int i) {  // e^{G_{j-1} - G_i}, i < j
       return i < j ? (GATE == GATE_HEAD ? __expf((j > 0 ? gs[j - 1] : 0.f) - gs[i]) : 1.f) : 0.f;
     };
-    // X1 = lower(R C^T * fac): the 10 lower 16x16 tiles over the waves (the upper
-    // ones were zeroed once and are never written)
-    auto gram = [&](const bf16 *R, const bf16 *Cm, auto fac) {
-      for (int t = wave; t < 10; t += NWB) {
+    // X = lower(R C^T * fac): the 10 lower 16x16 tiles over waves w0 .. w0 + nw - 1 (the
+    // upper ones were zeroed once and are never written)
+    auto gram = [&](const bf16 *R, const bf16 *Cm, auto fac, float *X, int w0, int nw) {
+      for (int t = wave - w0; t < 10; t += nw) {
         const int mb = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
         const int m0 = 16 * mb, n0 = 16 * (t - mb * (mb + 1) / 2);
         const f32x4 v = tile_frag<DK>(rowb(R, SKE, m0 + lm), rowb(Cm, SKE, n0 + lm));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = m0 + 4 * lg + u, i = n0 + lm;
-          X1[r * SX + i] = v[u] * fac(r, i);
+          X[r * SX + i] = v[u] * fac(r, i);
         }
       }
     };
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) Oacc[q][u] = eg[m0 + 4 * lg + u] * v[u];
     }
-    gram(Ql, Kl, e_out);
+    gram(Ql, Kl, e_out, X1, 0, NWB);
     __syncthreads();
     // ---- O += P_qk V
 #pragma unroll
@@ -432,9 +433,11 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
       Oacc[q] += tile_frag<DC>(rowf(X1, SX, m0 + lm), rowb(Vt, SVT, n0 + lm), kend(m0));
     }
     __syncthreads();
-    // ---- A_ab into X1, then T = (I - A_ab)^-1 into Tb
-    gram(Al, Bl, e_in);
+    // ---- A_ab into X1
+    gram(Al, Bl, e_in, X1, 0, NWB);
     __syncthreads();
+    // ---- T = (I - A_ab)^-1 into Tb (waves 0-2) while the other waves form A_ak (into X2)
+    // and then R = diag(e^{G_{j-1}}) A M0 + A_ak V (into R^T)
     if (wave == 0) {  // diagonal blocks: lane (lg, lm) solves column lm of block lg
       const int o = 16 * lg;
       float x[16];
@@ -453,11 +456,13 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) Tb[(o + r) * SX + o + lm] = x[r];
+    } else {
+      gram(Al, Kl, e_in, X2, 1, NWB - 1);
     }
     __syncthreads();
     if (wave < 3) {  // off-diagonal blocks, block column b = wave: T[a][b] = T[a][a] sum_k A[a][k] T[k][b]
       const int b = wave;
-      float *ys = Rt + wave * (16 * 20);  // scratch (R is formed afterwards): y^T, row pitch 20
+      float *ys = Ut + wave * (16 * 20);  // scratch (U is formed afterwards): y^T, row pitch 20
       for (int a = b + 1; a < 4; ++a) {
         f32x4 y = zero4();
 #pragma unroll
@@ -483,24 +488,19 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
         for (int u = 0; u < 4; ++u) Tb[(16 * a + 4 * lg + u) * SX + 16 * b + lm] = z[u];
         __builtin_amdgcn_wave_barrier();
       }
+    } else {
+      for (int t = wave - 3; t < 8; t += NWB - 3) {  // the 8 tiles of R over waves 3 ..
+        const int m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+        const f32x4 v = tile_frag<DK>(rowb(Al, SKE, m0 + lm), rowf(Mt, SM, n0 + lm));
+        const f32x4 w = tile_frag<DC>(rowf(X2, SX, m0 + lm), rowb(Vt, SVT, n0 + lm), kend(m0));
+        f32x4 res;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) res[u] = egp[m0 + 4 * lg + u] * v[u] + w[u];
+        *(f32x4 *)(Rt + (n0 + lm) * SR + m0 + 4 * lg) = res;
+      }
     }
     __syncthreads();
-    // ---- A_ak into X1; R = diag(e^{G_{j-1}}) A M0 + A_ak V into R^T
-    gram(Al, Kl, e_in);
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < OQ; ++q) {
-      int m0, n0;
-      otile(q, m0, n0);
-      const f32x4 v = tile_frag<DK>(rowb(Al, SKE, m0 + lm), rowf(Mt, SM, n0 + lm));
-      const f32x4 w = tile_frag<DC>(rowf(X1, SX, m0 + lm), rowb(Vt, SVT, n0 + lm), kend(m0));
-      f32x4 res;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) res[u] = egp[m0 + 4 * lg + u] * v[u] + w[u];
-      *(f32x4 *)(Rt + (n0 + lm) * SR + m0 + 4 * lg) = res;
-    }
-    __syncthreads();
-    // ---- U = T R into U^T
+    // ---- U = T R into U^T; P_qb into X1
 #pragma unroll
     for (int q = 0; q < OQ; ++q) {
       int m0, n0;
@@ -508,10 +508,9 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
       const f32x4 v = tile_frag<DC>(rowf(Tb, SX, m0 + lm), rowf(Rt, SR, n0 + lm), kend(m0));
       *(f32x4 *)(Ut + (n0 + lm) * SR + m0 + 4 * lg) = v;
     }
+    gram(Ql, Bl, e_out, X1, 0, NWB);
     __syncthreads();
-    // ---- P_qb into X1; O += P_qb U; store O
-    gram(Ql, Bl, e_out);
-    __syncthreads();
+    // ---- O += P_qb U; store O
 #pragma unroll
     for (int q = 0; q < OQ; ++q) {
       int m0, n0;
