@@ -35,7 +35,11 @@ namespace gdn {
 namespace {
 
 constexpr int BC = 64;    // chunk length
-constexpr int BNT = 256;  // threads per workgroup
+constexpr int BNT = 256;  // threads per workgroup of the per-chunk kernel
+// threads per workgroup of the reverse-state kernel: the additive write's variant runs
+// two waves per SIMD; the delta write's needs more registers than that leaves (256 per
+// wave) and runs one
+template <bool ADD> constexpr int state_threads() { return ADD ? 512 : 256; }
 constexpr int BVB = 32;   // value columns per workgroup of the reverse-state kernel
 constexpr int SV = BVB + 4, ST = BC + 1;  // fp32 row strides (padded; SV rows 16-byte aligned)
 
@@ -62,12 +66,15 @@ __device__ __forceinline__ bool seq_extent(const BwdParams &p, int n, long &tok0
 }
 
 template <typename E, int DK, int GATE, bool ADD>
-__global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
+__global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdParams p) {
+  constexpr int SNT = state_threads<ADD>(), NWS = SNT / 64;
+  constexpr int NH = NWS / 4;  // column parts of the dQ / dK phase
   constexpr int SKE = DK + 8;
   constexpr int VE = 16 / (int)sizeof(E);        // elements per 16-byte piece
-  constexpr int RK = BC * (DK / VE) / BNT;       // K / Q pieces per thread
-  constexpr int RV = BC * (BVB / VE) / BNT;      // V / dO pieces per thread
-  constexpr int RM = DK * (BVB / 4) / BNT;       // entering-state pieces per thread
+  constexpr int RK = BC * (DK / VE) / SNT;       // K / Q pieces per thread
+  constexpr int NPV = BC * (BVB / VE);           // V / dO pieces
+  constexpr int RV = (NPV + SNT - 1) / SNT;      // ... per thread (the first NPV threads)
+  constexpr int RM = DK * (BVB / 4) / SNT;       // entering-state pieces per thread
   typedef E EV __attribute__((ext_vector_type(VE)));
   typedef Part<DK> PT;
   __shared__ __align__(16) E Kl[BC * SKE];
@@ -81,7 +88,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
   __shared__ __align__(16) float Tb[BC * ST];
   __shared__ __align__(16) float Xl[BC * SV];
   __shared__ __align__(16) float dDl[BC * SV];
-  __shared__ float bs[BC], gs[BC], eg[BC], et[BC], red[BC], wsum[4], misc[4];
+  __shared__ float bs[BC], gs[BC], eg[BC], et[BC], wsum[NWS], misc[4];
+  __shared__ float rsum[NH][3][BC];  // row sums of the dQ / dK products, per column part
   // delta write: V is dead once X is formed and A once T is; additive write: Delta = V
   // and Y = dDelta
   float *const Yl = ADD ? dDl : Vb;
@@ -101,11 +109,11 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
   auto K_ = [&](int r, int d) { return to_f(Kl[r * SKE + d]); };
   auto Q_ = [&](int r, int d) { return to_f(Ql[r * SKE + d]); };
 
-  for (int i = tid; i < DK * BVB; i += BNT) {
+  for (int i = tid; i < DK * BVB; i += SNT) {
     const int d = i / BVB, j = i % BVB;
     dM[d * SV + j] = p.dfinal ? p.dfinal[sstate + (size_t)d * dv + j] : 0.f;
   }
-  for (int i = tid; i < BC * ST; i += BNT) Tb[i] = Pl[i] = 0.f;  // upper blocks stay zero
+  for (int i = tid; i < BC * ST; i += SNT) Tb[i] = Pl[i] = 0.f;  // upper blocks stay zero
 
   // ---- a chunk's inputs: 16-byte loads into registers one chunk ahead (rows past the
   // sequence end re-read its last row and are zeroed when staged)
@@ -117,21 +125,22 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     const size_t tbc = (size_t)tok0 + (size_t)cc * BC;
 #pragma unroll
     for (int u = 0; u < RK; ++u) {
-      const int pc = tid + BNT * u, r = min(pc / (DK / VE), last), g = pc % (DK / VE);
+      const int pc = tid + SNT * u, r = min(pc / (DK / VE), last), g = pc % (DK / VE);
       const size_t o = ((tbc + r) * H + h) * DK + g * VE;
       pk[u] = *(const u32x4 *)((const E *)p.k + o);
       pq[u] = *(const u32x4 *)((const E *)p.q + o);
     }
 #pragma unroll
     for (int u = 0; u < RV; ++u) {
-      const int pc = tid + BNT * u, r = min(pc / (BVB / VE), last), g = pc % (BVB / VE);
+      const int pc = tid + SNT * u, r = min(pc / (BVB / VE), last), g = pc % (BVB / VE);
+      if (pc >= NPV) break;
       const size_t o = ((tbc + r) * H + h) * dv + col0 + g * VE;
       pv[u] = *(const u32x4 *)((const E *)p.v + o);
       pd[u] = *(const u32x4 *)((const E *)p.dout + o);
     }
 #pragma unroll
     for (int u = 0; u < RM; ++u) {
-      const int pc = tid + BNT * u, d = pc / (BVB / 4), g = pc % (BVB / 4);
+      const int pc = tid + SNT * u, d = pc / (BVB / 4), g = pc % (BVB / 4);
       pm[u] = *(const f32x4 *)(p.states + ((((size_t)slot0 + cc) * H + h) * DK + d) * dv + col0 + 4 * g);
     }
     if (tid < BC) {
@@ -145,16 +154,17 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     for (int u = 0; u < RK; ++u) {
       opaque(pk[u]);
       opaque(pq[u]);
-      const int pc = tid + BNT * u, r = pc / (DK / VE), g = pc % (DK / VE);
+      const int pc = tid + SNT * u, r = pc / (DK / VE), g = pc % (DK / VE);
       if (r >= nvc) pk[u] = pq[u] = (u32x4){0u, 0u, 0u, 0u};
       *(u32x4 *)(Kl + r * SKE + g * VE) = pk[u];
       *(u32x4 *)(Ql + r * SKE + g * VE) = pq[u];
     }
 #pragma unroll
     for (int u = 0; u < RV; ++u) {
+      const int pc = tid + SNT * u, r = pc / (BVB / VE), g = pc % (BVB / VE);
+      if (pc >= NPV) break;
       opaque(pv[u]);
       opaque(pd[u]);
-      const int pc = tid + BNT * u, r = pc / (BVB / VE), g = pc % (BVB / VE);
       const EV ev = __builtin_bit_cast(EV, pv[u]), ed = __builtin_bit_cast(EV, pd[u]);
 #pragma unroll
       for (int e = 0; e < VE; ++e) {
@@ -165,7 +175,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < RM; ++u) {
       opaque(pm[u]);
-      const int pc = tid + BNT * u, d = pc / (BVB / 4), g = pc % (BVB / 4);
+      const int pc = tid + SNT * u, d = pc / (BVB / 4), g = pc % (BVB / 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) M0[d * SV + 4 * g + e] = pm[u][e];
     }
@@ -208,7 +218,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     {
       // the ten lower tiles, 3/3/2/2 per wave (the upper ones were zeroed once)
       const int lg = lane >> 4, lm = lane & 15;
-      for (int t = wave; t < 10; t += 4) {
+      for (int t = wave; t < 10; t += NWS) {
         const int mb = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
         const int m0 = 16 * mb, n0 = 16 * (t - mb * (mb + 1) / 2);
         f32x4 av = zero4(), pv4;
@@ -246,8 +256,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) Tb[(o + r) * ST + o + lm] = x[r];
     } else {
-      // V - Kt M0 into Xl (64 x 32, three waves)
-      mm_g<E, BC, BVB, DK, 3, true, false>(wave - 1, lane, K_, [&](int d, int j) { return M0[d * SV + j]; },
+      // V - Kt M0 into Xl (64 x 32, the other waves)
+      mm_g<E, BC, BVB, DK, NWS - 1, true, false>(wave - 1, lane, K_, [&](int d, int j) { return M0[d * SV + j]; },
                               [&](int r, int j, f32x4 v) {
 #pragma unroll
                                 for (int u = 0; u < 4; ++u) Xl[(r + u) * SV + j] = Vb[(r + u) * SV + j] - eg[r + u] * v[u];
@@ -274,12 +284,12 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     }
     __syncthreads();
     if (!ADD && jb == 0)  // T for the per-chunk kernel
-      for (int i = tid; i < BC * BC; i += BNT) p.tmat[(slot * H + h) * BC * BC + i] = Tb[(i / BC) * ST + i % BC];
+      for (int i = tid; i < BC * BC; i += SNT) p.tmat[(slot * H + h) * BC * BC + i] = Tb[(i / BC) * ST + i % BC];
     // ---- Delta = T diag(beta) (V - Kt M0) (the additive write: Delta = V, already in Vb);
     // dDelta = P^T dO + diag(e^{G_C - G}) K dM  (8 tiles each)
     {
       const int lg = lane >> 4, lm = lane & 15;
-      for (int t = wave; t < 8; t += 4) {
+      for (int t = wave; t < 8; t += NWS) {
         const int m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
         f32x4 dd = zero4();
         if (!ADD)
@@ -300,14 +310,14 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     __syncthreads();
     // ---- Y = T^T dDelta (the additive write: Y = dDelta, already in dDl)
     if constexpr (!ADD)
-      mm_g<E, BC, BVB, BC, 4, false, false>(wave, lane, [&](int r, int i) { return Tb[i * ST + r]; },
+      mm_g<E, BC, BVB, BC, NWS, false, false>(wave, lane, [&](int r, int i) { return Tb[i * ST + r]; },
                               [&](int i, int j) { return dDl[i * SV + j]; }, [&](int r, int j, f32x4 v) {
 #pragma unroll
                                 for (int u = 0; u < 4; ++u) Yl[(r + u) * SV + j] = v[u];
                               });
     __syncthreads();
     // ---- dV (complete for this value block)
-    for (int i = tid; i < BC * BVB; i += BNT) {
+    for (int i = tid; i < BC * BVB; i += SNT) {
       const int r = i / BVB, j = i % BVB;
       if (r < nv) ((E *)p.dv_out)[((tb + r) * H + h) * dv + col0 + j] = to_e<E>(ADD ? Yl[r * SV + j] : bs[r] * Yl[r * SV + j]);
     }
@@ -317,7 +327,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     if constexpr (std::is_same<E, bf16>::value) {
       // these contract over the 32 value columns: every fragment is a row piece
       const int lg = lane >> 4, lm = lane & 15;
-      for (int t = wave; t < 16; t += 4) {
+      for (int t = wave; t < 16; t += NWS) {
         const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16, i = n0 + lm;
         f32x4 vp = zero4();
         if (n0 <= m0)
@@ -335,13 +345,13 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
         }
       }
     } else {
-      mm_g<E, BC, BC, BVB, 4, true, false>(wave, lane, [&](int r, int j) { return dOb[r * SV + j]; },
+      mm_g<E, BC, BC, BVB, NWS, true, false>(wave, lane, [&](int r, int j) { return dOb[r * SV + j]; },
                               [&](int j, int i) { return Dl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
 #pragma unroll
                                 for (int u = 0; u < 4; ++u) pr[PT::DP + i * BC + r + u] = i <= r + u ? v[u] : 0.f;
                               });
       if constexpr (!ADD)
-        mm_g<E, BC, BC, BVB, 4, false, false>(wave, lane, [&](int r, int j) { return dDl[r * SV + j]; },
+        mm_g<E, BC, BC, BVB, NWS, false, false>(wave, lane, [&](int r, int j) { return dDl[r * SV + j]; },
                                 [&](int j, int i) { return bs[i] * Xl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
 #pragma unroll
                                   for (int u = 0; u < 4; ++u) pr[PT::DT + i * BC + r + u] = v[u];
@@ -349,10 +359,11 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
     }
     // ---- dQ = e^G dO M0^T, dK = -e^G beta Y M0^T + e^{G_C - G} Delta dM^T, and the rows of
     // dG: e^G (dO M0^T).Q - e^G beta (Y M0^T).K - e^{G_C - G} (Delta dM^T).K.  A wave takes
-    // whole 16-row blocks (all DK columns), so its row sums stay in the wave.
+    // one 16-row block and one of NH parts of the DK columns; the row sums of the parts
+    // meet in LDS.
     {
       const int lg = lane >> 4, lm = lane & 15;
-      const int m0 = 16 * wave;
+      const int m0 = 16 * (wave & 3), half = wave >> 2;
       float gq[4] = {0.f, 0.f, 0.f, 0.f}, gk[4] = {0.f, 0.f, 0.f, 0.f}, gz[4] = {0.f, 0.f, 0.f, 0.f};
       // this wave's rows of dO, Y and Delta as A fragments (the contraction is over the
       // 32 value columns: one 32-deep step)
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
         fy = split8(ld8(Yl + (m0 + lm) * SV + 8 * lg));
         fd = split8(ld8(Dl + (m0 + lm) * SV + 8 * lg));
       }
-      for (int n0 = 0; n0 < DK; n0 += 16) {
+      for (int n0 = half * (DK / NH); n0 < (half + 1) * (DK / NH); n0 += 16) {
         f32x4 w, uu, z;
         if constexpr (std::is_same<E, bf16>::value) {
           const Split fm = split8(ld8(M0 + (n0 + lm) * SV + 8 * lg));
@@ -409,13 +420,14 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = m0 + 4 * lg + u;
-          pr[PT::DG + r] = eg[r] * gq[u] - eg[r] * bs[r] * gk[u] - et[r] * gz[u];
-          red[r] = et[r] * gz[u];  // this row's term of dG_C
+          rsum[half][0][r] = gq[u];
+          rsum[half][1][r] = gk[u];
+          rsum[half][2][r] = gz[u];
         }
     }
     // ---- dbeta rows: Y . (V - Kt M0);  dG_C: the e^{G_C - G} terms plus gam <M0, dM>
     float part_m = 0.f;
-    for (int i = tid; i < DK * BVB; i += BNT) part_m += M0[(i / BVB) * SV + i % BVB] * dM[(i / BVB) * SV + i % BVB];
+    for (int i = tid; i < DK * BVB; i += SNT) part_m += M0[(i / BVB) * SV + i % BVB] * dM[(i / BVB) * SV + i % BVB];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) part_m += __shfl_xor(part_m, off);
     if (lane == 0) wsum[wave] = part_m;
@@ -425,22 +437,34 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       pr[PT::DB + tid] = sb;
     }
     __syncthreads();
-    if (wave == 0) {
-      float sg = red[lane];
+    if (wave == 0) {  // lane = row: the dG rows, and dG_C (their e^{G_C - G} terms plus gam <M0, dM>)
+      const int r = lane;
+      float gq = 0.f, gk = 0.f, gz = 0.f;
+#pragma unroll
+      for (int c = 0; c < NH; ++c) {
+        gq += rsum[c][0][r];
+        gk += rsum[c][1][r];
+        gz += rsum[c][2][r];
+      }
+      pr[PT::DG + r] = eg[r] * gq - eg[r] * bs[r] * gk - et[r] * gz;
+      float sg = et[r] * gz;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) sg += __shfl_xor(sg, off);
-      if (lane == 0) pr[PT::GC] = sg + misc[0] * (wsum[0] + wsum[1] + wsum[2] + wsum[3]);
+      float wm = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWS; ++w) wm += wsum[w];
+      if (lane == 0) pr[PT::GC] = sg + misc[0] * wm;
     }
     // ---- dM <- gam dM + Qt^T dO - Kt^T diag(beta) Y (no last term for the additive write)
     // (DK x 32: DK / 8 tiles)
     {
       const int lg = lane >> 4, lm = lane & 15;
       constexpr int TILES = (DK / 16) * 2;
-      f32x4 nm[TILES / 4];
+      f32x4 nm[TILES / NWS];
       const float gam = misc[0];
 #pragma unroll
-      for (int q = 0; q < TILES / 4; ++q) {
-        const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+      for (int q = 0; q < TILES / NWS; ++q) {
+        const int t = wave + NWS * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
         const f32x4 n1 = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * Q_(r, d); },
                                   [&](int r, int j) { return dOb[r * SV + j]; });
         f32x4 n2 = zero4();
@@ -452,8 +476,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
       }
       __syncthreads();  // every read of the old dM is done
 #pragma unroll
-      for (int q = 0; q < TILES / 4; ++q) {
-        const int t = wave + 4 * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+      for (int q = 0; q < TILES / NWS; ++q) {
+        const int t = wave + NWS * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
 #pragma unroll
         for (int u = 0; u < 4; ++u) dM[(m0 + 4 * lg + u) * SV + n0 + lm] = nm[q][u];
       }
@@ -461,7 +485,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_state_kernel(BwdParams p) {
   }
   __syncthreads();
   if (p.dinit)
-    for (int i = tid; i < DK * BVB; i += BNT) {
+    for (int i = tid; i < DK * BVB; i += SNT) {
       const int d = i / BVB, j = i % BVB;
       p.dinit[sstate + (size_t)d * dv + j] = dM[d * SV + j];
     }
@@ -672,7 +696,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
 template <typename E, int DK, int GATE, bool ADD>
 void launch_bg(const BwdParams &p, hipStream_t stream) {
   const int nb = p.dv / BVB;
-  hipLaunchKernelGGL((bwd_state_kernel<E, DK, GATE, ADD>), dim3(p.N * p.H * nb), dim3(BNT), 0, stream, p);
+  hipLaunchKernelGGL((bwd_state_kernel<E, DK, GATE, ADD>), dim3(p.N * p.H * nb), dim3(state_threads<ADD>()), 0,
+                     stream, p);
   hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, GATE, ADD>), dim3((unsigned)(p.slots * p.H)), dim3(BNT), 0, stream, p);
 }
 
