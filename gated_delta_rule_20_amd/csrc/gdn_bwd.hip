@@ -552,8 +552,10 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       Pl[(col + e) * ST + r] = sp[e];
-      Dt[(col + e) * ST + r] = st[e];
-      Tl[r * ST + col + e] = tv[e];
+      if (!ADD) {  // no T for the additive write (its LDS then goes unused)
+        Dt[(col + e) * ST + r] = st[e];
+        Tl[r * ST + col + e] = tv[e];
+      }
     }
   }
   if (tid < BC) {
@@ -595,7 +597,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      Sl[(m0 + 4 * lg + u) * ST + n0 + lm] = sv[u];
+      if (!ADD) Sl[(m0 + 4 * lg + u) * ST + n0 + lm] = sv[u];
       Rl[(m0 + 4 * lg + u) * ST + n0 + lm] = rv[u];
     }
     // T^T is upper triangular: T[i][k] = 0 for k > i (no T for the additive write)
@@ -604,7 +606,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
       zv = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int k) { return Dt[r * ST + k]; },
                                        [&](int k, int i) { return Tl[i * ST + k]; }, 0, n0 + 16);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) Zl[(m0 + 4 * lg + u) * ST + n0 + lm] = zv[u];
+    for (int u = 0; u < 4; ++u)
+      if (!ADD) Zl[(m0 + 4 * lg + u) * ST + n0 + lm] = zv[u];
   }
   __syncthreads();
   // dA = -strict(T^T Z), then per entry: Gamma, Ea = dA beta_r Gamma, Ep = dP Gamma,
@@ -630,11 +633,15 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
         const float gam = i <= r ? (GATE == GATE_HEAD ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
         const float dA = i < r ? -da[q][u] : 0.f;
         const float dP = Pl[r * ST + i];
-        const float S = Sl[r * ST + i], R = Rl[r * ST + i];
-        Zl[r * ST + i] = dA * bs[r] * gam;                 // Ea
-        Pl[r * ST + i] = dP * gam;                         // Ep
-        Sl[r * ST + i] = (dA * bs[r] * S + dP * R) * gam;  // wG
-        Rl[r * ST + i] = dA * S * gam;                     // dbeta terms
+        const float S = ADD ? 0.f : Sl[r * ST + i], R = Rl[r * ST + i];
+        Pl[r * ST + i] = dP * gam;  // Ep
+        if (ADD) {
+          Rl[r * ST + i] = dP * R * gam;  // wG, in place of R (the additive write needs no more)
+        } else {
+          Zl[r * ST + i] = dA * bs[r] * gam;                 // Ea
+          Sl[r * ST + i] = (dA * bs[r] * S + dP * R) * gam;  // wG
+          Rl[r * ST + i] = dA * S * gam;                     // dbeta terms
+        }
       }
     }
   }
@@ -643,9 +650,10 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   if (tid < BC) {
     float rs = 0.f, cs = 0.f, bsum = 0.f;
     for (int i = 0; i < BC; ++i) {
-      rs += Sl[tid * ST + i];
-      cs += Sl[i * ST + tid];
-      bsum += Rl[tid * ST + i];
+      const float *Wl = ADD ? Rl : Sl;  // wG
+      rs += Wl[tid * ST + i];
+      cs += Wl[i * ST + tid];
+      if (!ADD) bsum += Rl[tid * ST + i];
     }
     dGs[tid] += rs - cs + (tid == BC - 1 ? misc[0] : 0.f);
     dBs[tid] += bsum;
@@ -714,15 +722,22 @@ hipError_t launch_b(const BwdParams &p, int gate, bool add, hipStream_t stream) 
 }
 
 // out[h] = sum over t of x[t * H + h], in a fixed order (deterministic): one workgroup
-// per head, a strided partial sum per thread, then a tree in LDS.
-__global__ __launch_bounds__(256) void sum_tokens_kernel(const float *x, long tokens, int H, float *out) {
-  __shared__ float part[256];
+// of 1024 threads per head, eight independent partial sums per thread (loads in
+// flight together), then a tree in LDS.
+__global__ __launch_bounds__(1024) void sum_tokens_kernel(const float *x, long tokens, int H, float *out) {
+  __shared__ float part[1024];
   const int h = blockIdx.x, tid = threadIdx.x;
-  float acc = 0.f;
-  for (long t = tid; t < tokens; t += 256) acc += x[t * H + h];
-  part[tid] = acc;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (long t0 = tid; t0 < tokens; t0 += 8 * 1024) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const long t = t0 + (long)u * 1024;
+      if (t < tokens) acc[u] += x[t * H + h];
+    }
+  }
+  part[tid] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = 512; w > 0; w >>= 1) {
     if (tid < w) part[tid] += part[tid + w];
     __syncthreads();
   }
@@ -735,7 +750,7 @@ size_t bwd_part_floats(int dk) { return dk == 128 ? Part<128>::SIZE : Part<64>::
 
 hipError_t launch_sum_tokens(const float *x, long tokens, int H, float *out, hipStream_t stream) {
   if (H <= 0) return hipSuccess;
-  hipLaunchKernelGGL(sum_tokens_kernel, dim3(H), dim3(256), 0, stream, x, tokens, H, out);
+  hipLaunchKernelGGL(sum_tokens_kernel, dim3(H), dim3(1024), 0, stream, x, tokens, H, out);
   return hipGetLastError();
 }
 
