@@ -147,7 +147,7 @@ def time_chunked(gdn, sets, steps, warmup):
     return wall, e0.elapsed_time(e1) / steps
 
 
-def time_decode(gdn, spec, final_states, steps=64):
+def time_decode(gdn, spec, final_states, steps=64, cpu=False):
     import torch
     import synth
     batch = spec["decode_batch"]
@@ -174,12 +174,21 @@ def time_decode(gdn, spec, final_states, steps=64):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     bytes_step = batch * spec["H"] * (2 * 4 * spec["dk"] * spec["dv"] + 2 * (2 * spec["dk"] + 2 * spec["dv"]) + 8)
-    return {"workload": "gdn-decode-bf16-N%d-H%d-d%d" % (batch, spec["H"], spec["dk"]),
-            "ms_per_step": ms, "tokens_per_s": batch / (ms / 1e3),
-            "hbm_gbs": bytes_step / (ms / 1e3) / 1e9, "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+    res = {"workload": "gdn-decode-bf16-N%d-H%d-d%d" % (batch, spec["H"], spec["dk"]),
+           "ms_per_step": ms, "tokens_per_s": batch / (ms / 1e3),
+           "hbm_gbs": bytes_step / (ms / 1e3) / 1e9, "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+    if cpu:
+        import oracle
+        st_h = synth.decode_initial_states(final_states.cpu(), batch)
+        t0 = time.perf_counter()
+        oracle.step(dec["q"][0], dec["k"][0], dec["v"][0], dec["beta"][0], dec["log_alpha"][0], st_h)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": batch / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": "one decode step of all %d streams x %d heads (%.2f s)" % (batch, spec["H"], dt)}
+    return res
 
 
-def time_dplr_step(gdn, N=256, H=16, dk=128, dv=128, steps=64):
+def time_dplr_step(gdn, N=256, H=16, dk=128, dv=128, steps=64, cpu=False):
     """gdn_fwd_dplr_step, one token per stream, scalar gate, state in place (N x H states
     of d_k x d_v fp32, 268 MB at the default shape).  Algorithmic bytes per stream and
     head: the state read and written in fp32, q, k, a, b, v read and o written in bf16,
@@ -209,9 +218,20 @@ def time_dplr_step(gdn, N=256, H=16, dk=128, dv=128, steps=64):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     bytes_step = N * H * (2 * 4 * dk * dv + 2 * (4 * dk + 2 * dv) + 4)
-    return {"workload": "dplr-decode-bf16-N%d-H%d-d%d" % (N, H, dk), "ms_per_step": ms,
+    res = {"workload": "dplr-decode-bf16-N%d-H%d-d%d" % (N, H, dk), "ms_per_step": ms,
             "tokens_per_s": N / (ms / 1e3), "hbm_gbs": bytes_step / (ms / 1e3) / 1e9,
             "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+    if cpu:
+        import oracle
+        one = {k: (v[:, :1] if isinstance(v, torch.Tensor) and v.dim() > 1 and k != "initial_state" else v)
+               for k, v in inp.items()}
+        t0 = time.perf_counter()
+        oracle.fwd_dplr(one["q"], one["k"], one["v"], one["a"], one["b"], one["log_alpha"], one["initial_state"],
+                        nthreads=oracle.max_threads())
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": N / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": "one decode step of all %d streams x %d heads (%.2f s)" % (N, H, dt)}
+    return res
 
 
 def time_pool_decode(gdn, N, L, H, dk, dv, store, steps=64):
@@ -249,7 +269,7 @@ def time_pool_decode(gdn, N, L, H, dk, dv, store, steps=64):
             "hbm_gbs": nbytes / (ms / 1e3) / 1e9, "hbm_frac": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
 
 
-def time_bwd(gdn, name, steps=20):
+def time_bwd(gdn, name, steps=20, cpu=False):
     """gdn_bwd_chunked on a workload: the gradients of o and of the final state are
     seeded N(0,1) and N(0, 0.1^2).  Algorithmic bytes: q, k, v, dout read and dq, dk,
     dv written in the I/O dtype, beta (delta write) and a per-token log alpha read and
@@ -265,8 +285,9 @@ def time_bwd(gdn, name, steps=20):
     B, T, H, dk = inp["q"].shape
     dv = inp["v"].shape[-1]
     g = torch.Generator().manual_seed(spec["seed"] + 77)
-    dout = torch.randn(B, T, H, dv, generator=g).to(inp["q"].dtype).cuda()
-    dfs = (torch.randn(inp["N"], H, dk, dv, generator=g) * 0.1).cuda()
+    dout_h = torch.randn(B, T, H, dv, generator=g).to(inp["q"].dtype)
+    dfs_h = torch.randn(inp["N"], H, dk, dv, generator=g) * 0.1
+    dout, dfs = dout_h.cuda(), dfs_h.cuda()
     d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     write = inp.get("write", "delta")
     call = gdn.PreparedBwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"], dout, dfs,
@@ -296,10 +317,13 @@ def time_bwd(gdn, name, steps=20):
         flops = fwd_flops + th * (6 * CHUNK * dk + 4 * CHUNK * dv + 8 * dk * dv)
     else:
         flops = fwd_flops + th * (14 * CHUNK * dk + 10 * CHUNK * dv + 14 * dk * dv + 4 * CHUNK * CHUNK)
-    return {"workload": name + " backward", "ms_per_step": ms, "tokens_per_s": tokens / (ms / 1e3),
+    res = {"workload": name + " backward", "ms_per_step": ms, "tokens_per_s": tokens / (ms / 1e3),
             "alg_bytes": nbytes, "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
             "hbm_frac": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, "alg_flops": flops,
             "tflops": flops / (ms / 1e3) / 1e12}
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline_sample(dict(inp, dout=dout_h, dfinal=dfs_h), "bwd", max_tokens=8192)
+    return res
 
 
 def cpu_baseline(inp, H):
@@ -318,6 +342,59 @@ def cpu_baseline(inp, H):
     return {"value": tokens / best, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "whole workload (%d tokens x %d heads), fp64 token-by-token recurrence, "
                       "OpenMP over (sequence, head), best of 2 runs (%.2f s)" % (tokens, H, best)}
+
+
+def _leading(inp, max_tokens):
+    """The leading batch rows (or packed sequences) of a workload, up to max_tokens
+    tokens (at least one row or sequence), all heads: (sliced inputs, tokens, text)."""
+    import torch
+    out = dict(inp)
+    s0 = inp.get("initial_state")
+    if inp.get("cu_seqlens") is None:
+        B, T = inp["q"].shape[:2]
+        nb = max(1, min(B, max_tokens // max(T, 1)))
+        for k in ("q", "k", "v", "a", "b", "beta", "log_alpha", "dout"):
+            if out.get(k) is not None and out[k].dim() > 1:
+                out[k] = out[k][:nb]
+        out["initial_state"] = None if s0 is None else s0[:nb]
+        return out, nb * T, "the first %d of %d batch rows" % (nb, B)
+    cu = [int(x) for x in inp["cu_seqlens"]]
+    n = 1
+    while n < len(cu) - 1 and cu[n + 1] <= max_tokens:
+        n += 1
+    for k in ("q", "k", "v", "a", "b", "beta", "log_alpha", "dout"):
+        if out.get(k) is not None and out[k].dim() > 1:
+            out[k] = out[k][:, :cu[n]]
+    out["cu_seqlens"] = torch.tensor(cu[:n + 1], dtype=torch.int32)
+    out["initial_state"] = None if s0 is None else s0[:n]
+    return out, cu[n], "the first %d of %d packed sequences" % (n, len(cu) - 1)
+
+
+def cpu_baseline_sample(inp, kind="fwd", max_tokens=32768):
+    """The fp64 oracle timed beside a GPU line, on a bounded sample of the same workload
+    (leading rows or sequences, all heads; one run of a few seconds on the host cores):
+    kind "fwd" (oracle.fwd, either write rule), "dplr" (oracle.fwd_dplr) or "bwd"
+    (oracle.bwd, with inp["dout"] and inp["dfinal"])."""
+    import oracle
+    threads = oracle.max_threads()
+    smp, tokens, text = _leading(inp, max_tokens)
+    H = inp["q"].shape[2]
+    t0 = time.perf_counter()
+    if kind == "dplr":
+        oracle.fwd_dplr(smp["q"], smp["k"], smp["v"], smp["a"], smp["b"], smp["log_alpha"], smp["initial_state"],
+                        smp["cu_seqlens"], nthreads=threads)
+    elif kind == "bwd":
+        dfinal = smp.get("dfinal")
+        if dfinal is not None and smp["initial_state"] is not None:
+            dfinal = dfinal[:smp["initial_state"].shape[0]]
+        oracle.bwd(smp["q"], smp["k"], smp["v"], smp["beta"], smp["log_alpha"], smp["initial_state"], smp["dout"],
+                   dfinal, cu_seqlens=smp["cu_seqlens"], nthreads=threads, write=smp.get("write", "delta"))
+    else:
+        oracle.fwd(smp["q"], smp["k"], smp["v"], smp["beta"], smp["log_alpha"], smp["initial_state"],
+                   smp["cu_seqlens"], nthreads=threads, write=smp.get("write", "delta"))
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%s (%d tokens x %d heads), one run (%.2f s)" % (text, tokens, H, dt)}
 
 
 def bench_workload(gdn, name, steps, warmup):
@@ -411,6 +488,8 @@ def main():
                      "dplr-bf16-B16-T2048-H8-d128"]:
             try:
                 r, winp, wsets = bench_workload(gdn, name, max(5, args.steps // 5), None)
+                if not args.no_cpu:
+                    r["cpu_baseline"] = cpu_baseline_sample(winp, "dplr" if winp.get("write") == "dplr" else "fwd")
             except RuntimeError as e:
                 extra.append({"workload": name, "error": str(e)})
                 continue
@@ -419,18 +498,18 @@ def main():
                 _, fs = gdn.fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], None,
                                         d["cu_seqlens"])
                 torch.cuda.synchronize()
-                extra.append(time_decode(gdn, synth.WORKLOADS[name], fs))
+                extra.append(time_decode(gdn, synth.WORKLOADS[name], fs, cpu=not args.no_cpu))
                 del fs
                 for store in ("last", "all"):
                     extra.append(time_pool_decode(gdn, 256, 4, 16, 128, 128, store))
             del wsets
             torch.cuda.empty_cache()
             extra.append(r)
-        extra.append(time_dplr_step(gdn))
+        extra.append(time_dplr_step(gdn, cpu=not args.no_cpu))
         torch.cuda.empty_cache()
-        extra.append(time_bwd(gdn, HEADLINE))
+        extra.append(time_bwd(gdn, HEADLINE, cpu=not args.no_cpu))
         torch.cuda.empty_cache()
-        extra.append(time_bwd(gdn, "retnet-bf16-B16-T2048-H8-d128"))
+        extra.append(time_bwd(gdn, "retnet-bf16-B16-T2048-H8-d128", cpu=not args.no_cpu))
         torch.cuda.empty_cache()
         for e in extra:
             print(json.dumps(e), file=sys.stderr)
