@@ -261,11 +261,17 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   const int la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
   fp.la_stride = la_stride;
   fp.chunk_states = (float *)ws;
-  const int dvb = choose_dvb(a->N, a->H, a->d_v);
-  fp.nb = a->d_v / dvb;
-  if (gdn::launch_fwd_fused(fp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, kernel_gate(a->gate), add, stream) !=
-      hipSuccess)
-    return GDN_ERR_HIP;
+  const gdn_fwd_args f = fwd_of(a);
+  if (use_pipe(&f)) {  // bf16, d_k = 128: the pipelined kernel, chunk states instead of o
+    fp.nb = a->d_v / 64;
+    if (gdn::launch_fwd_pipe(fp, (int)a->gate, add, stream) != hipSuccess) return GDN_ERR_HIP;
+  } else {
+    const int dvb = choose_dvb(a->N, a->H, a->d_v);
+    fp.nb = a->d_v / dvb;
+    if (gdn::launch_fwd_fused(fp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, kernel_gate(a->gate), add, stream) !=
+        hipSuccess)
+      return GDN_ERR_HIP;
+  }
   // 2. reverse state pass and 3. per-chunk gradients
   gdn::BwdParams bp;
   bp.q = a->q;

@@ -322,7 +322,9 @@ __device__ __forceinline__ f32x4 gamma_tile(const GammaRegs &G, int a, int b, in
   return out;
 }
 
-template <int GATE, bool ADD>
+// STATES: instead of o, store every chunk's entering state into p.chunk_states
+// ([slot, H, d_k, d_v], slot floor(tok0 / 64) + n + c), for the gradient pass.
+template <int GATE, bool ADD, bool STATES = false>
 __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   __shared__ __align__(16) char smem[LDS_TOTAL];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -779,6 +781,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   // T/P: 2), so every LDS address is a lane base plus a uniform offset plus a constant
   int ring3 = 0, ring2 = 0;
   for (int c = 0; c < nchunks; ++c) {
+    if constexpr (STATES) {  // the state entering chunk c: M = M_hat Gam
+      float *cs = p.chunk_states + (((size_t)((tok0 >> 6) + n + c) * H + h) * DK) * dv + col0 + n0 + lm;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cs[(size_t)(32 * (t >> 1) + 8 * lg + 4 * (t & 1) + j) * dv] = M[t][j] * Gam;
+    }
     // (per-key-channel gate: two stages of everything; K holds K e^G, Q holds Q e^G
     // and the update reads K e^{g_C - G}; gv holds e^{g_C} per key channel)
     constexpr bool KP = GATE == GATE_KEY;
@@ -949,9 +958,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     }
     // O rows -> HBM: lane holds O[16i+lm][n0 + 4lg .. 4lg+3] (one 8-byte store)
     const int nv = min(C, len - c * C);
+    if constexpr (!STATES) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (nv == C || 16 * i + lm < nv) *(bf16x4 *)(olane + (size_t)(c * C + 16 * i) * orow) = to_bf4(OT[i]);
+      for (int i = 0; i < 4; ++i)
+        if (nv == C || 16 * i + lm < nv) *(bf16x4 *)(olane + (size_t)(c * C + 16 * i) * orow) = to_bf4(OT[i]);
+    }
     __syncthreads();
   }
 
@@ -1326,6 +1337,18 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
 hipError_t launch_fwd_pipe(const FwdParams &p, int gate, bool add, hipStream_t stream) {
   const int blocks = p.N * p.H * p.nb;
   if (blocks == 0) return hipSuccess;
+  if (p.chunk_states) {  // the gradient pass's recomputation: chunk states, no o
+    switch (gate * 2 + (add ? 1 : 0)) {
+      case 2 * GATE_NONE: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_NONE, false, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+      case 2 * GATE_NONE + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_NONE, true, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+      case 2 * GATE_HEAD: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_HEAD, false, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+      case 2 * GATE_HEAD + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_HEAD, true, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+      case 2 * GATE_CONST: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_CONST, false, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+      case 2 * GATE_CONST + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_CONST, true, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (gate * 2 + (add ? 1 : 0)) {
     case 2 * GATE_NONE: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_NONE, false>), dim3(blocks), dim3(NT), 0, stream, p); break;
     case 2 * GATE_NONE + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_NONE, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
