@@ -425,6 +425,26 @@ __global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdP
           rsum[half][2][r] = gz[u];
         }
     }
+    // ---- dM <- gam dM + Qt^T dO - Kt^T diag(beta) Y (no last term for the additive write)
+    // (DK x 32: DK / 8 tiles), into registers: written after the next barrier
+    const int lgm = lane >> 4, lmm = lane & 15;
+    constexpr int TILES = (DK / 16) * 2;
+    f32x4 nm[TILES / NWS];
+    {
+      const float gam = misc[0];
+#pragma unroll
+      for (int q = 0; q < TILES / NWS; ++q) {
+        const int t = wave + NWS * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
+        const f32x4 n1 = tile_g<E, BC, false, true>(m0, n0, lgm, lmm, [&](int d, int r) { return eg[r] * Q_(r, d); },
+                                  [&](int r, int j) { return dOb[r * SV + j]; });
+        f32x4 n2 = zero4();
+        if (!ADD)
+          n2 = tile_g<E, BC, false, false>(m0, n0, lgm, lmm, [&](int d, int r) { return eg[r] * bs[r] * K_(r, d); },
+                                           [&](int r, int j) { return Yl[r * SV + j]; });
+#pragma unroll
+        for (int u = 0; u < 4; ++u) nm[q][u] = gam * dM[(m0 + 4 * lgm + u) * SV + n0 + lmm] + n1[u] - n2[u];
+      }
+    }
     // ---- dbeta rows: Y . (V - Kt M0);  dG_C: the e^{G_C - G} terms plus gam <M0, dM>
     float part_m = 0.f;
     for (int i = tid; i < DK * BVB; i += SNT) part_m += M0[(i / BVB) * SV + i % BVB] * dM[(i / BVB) * SV + i % BVB];
@@ -436,7 +456,7 @@ __global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdP
       for (int j = 0; j < BVB; ++j) sb += Yl[tid * SV + j] * Xl[tid * SV + j];
       pr[PT::DB + tid] = sb;
     }
-    __syncthreads();
+    __syncthreads();  // every read of the old dM is done; the row sums are in LDS
     if (wave == 0) {  // lane = row: the dG rows, and dG_C (their e^{G_C - G} terms plus gam <M0, dM>)
       const int r = lane;
       float gq = 0.f, gk = 0.f, gz = 0.f;
@@ -455,32 +475,11 @@ __global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdP
       for (int w = 0; w < NWS; ++w) wm += wsum[w];
       if (lane == 0) pr[PT::GC] = sg + misc[0] * wm;
     }
-    // ---- dM <- gam dM + Qt^T dO - Kt^T diag(beta) Y (no last term for the additive write)
-    // (DK x 32: DK / 8 tiles)
-    {
-      const int lg = lane >> 4, lm = lane & 15;
-      constexpr int TILES = (DK / 16) * 2;
-      f32x4 nm[TILES / NWS];
-      const float gam = misc[0];
 #pragma unroll
-      for (int q = 0; q < TILES / NWS; ++q) {
-        const int t = wave + NWS * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
-        const f32x4 n1 = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * Q_(r, d); },
-                                  [&](int r, int j) { return dOb[r * SV + j]; });
-        f32x4 n2 = zero4();
-        if (!ADD)
-          n2 = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int d, int r) { return eg[r] * bs[r] * K_(r, d); },
-                                           [&](int r, int j) { return Yl[r * SV + j]; });
+    for (int q = 0; q < TILES / NWS; ++q) {
+      const int t = wave + NWS * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) nm[q][u] = gam * dM[(m0 + 4 * lg + u) * SV + n0 + lm] + n1[u] - n2[u];
-      }
-      __syncthreads();  // every read of the old dM is done
-#pragma unroll
-      for (int q = 0; q < TILES / NWS; ++q) {
-        const int t = wave + NWS * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) dM[(m0 + 4 * lg + u) * SV + n0 + lm] = nm[q][u];
-      }
+      for (int u = 0; u < 4; ++u) dM[(m0 + 4 * lgm + u) * SV + n0 + lmm] = nm[q][u];
     }
   }
   __syncthreads();
