@@ -9,7 +9,8 @@ raises on import.
 The names follow the C ABI: ``fwd_chunked`` wraps ``gdn_fwd_chunked``,
 ``recurrent_step`` wraps ``gdn_fwd_recurrent_step``, ``decode`` wraps
 ``gdn_fwd_decode``, ``bwd_chunked`` wraps ``gdn_bwd_chunked``, ``fwd_dplr`` wraps
-``gdn_fwd_dplr`` and ``dplr_step`` wraps ``gdn_fwd_dplr_step``.
+``gdn_fwd_dplr``, ``dplr_step`` wraps ``gdn_fwd_dplr_step`` and ``dplr_decode`` wraps
+``gdn_fwd_dplr_decode``.
 """
 from __future__ import annotations
 
@@ -98,6 +99,16 @@ class DplrStepArgs(ctypes.Structure):
                 ("o", ctypes.c_void_p)]
 
 
+class DplrDecodeArgs(ctypes.Structure):
+    """Mirror of ``gdn_dplr_decode_args``."""
+    _fields_ = [("N", ctypes.c_int), ("L", ctypes.c_int), ("H", ctypes.c_int), ("d_k", ctypes.c_int),
+                ("d_v", ctypes.c_int), ("dtype", ctypes.c_int), ("gate", ctypes.c_int),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p), ("state_pool", ctypes.c_void_p),
+                ("pool_size", ctypes.c_int), ("src_slots", ctypes.c_void_p), ("dst_slots", ctypes.c_void_p),
+                ("o", ctypes.c_void_p)]
+
+
 def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError("libgdn.so is not built (%s); run `python __graft_entry__.py build` "
@@ -115,6 +126,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs)]
     lib.gdn_bwd_chunked.restype = ctypes.c_int
     lib.gdn_bwd_chunked.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
+    lib.gdn_fwd_dplr_decode.restype = ctypes.c_int
+    lib.gdn_fwd_dplr_decode.argtypes = [ctypes.POINTER(DplrDecodeArgs), ctypes.c_void_p]
     lib.gdn_fwd_dplr_step.restype = ctypes.c_int
     lib.gdn_fwd_dplr_step.argtypes = [ctypes.POINTER(DplrStepArgs), ctypes.c_void_p]
     lib.gdn_fwd_dplr.restype = ctypes.c_int
@@ -477,6 +490,30 @@ def dplr_step(q, k, v, a, b, log_alpha, state, out=None, stream=None):
                         q=_ptr(q), k=_ptr(k), a=_ptr(a), b=_ptr(b), v=_ptr(v), log_alpha=_ptr(log_alpha),
                         state=_ptr(state), o=_ptr(out))
     _check(_lib.gdn_fwd_dplr_step(ctypes.byref(args), _stream(stream)), "gdn_fwd_dplr_step")
+    return out
+
+
+def dplr_decode(q, k, v, a, b, log_alpha, state_pool, src_slots, dst_slots, out=None, stream=None):
+    """Serving decode of the diagonal-plus-low-rank transition (gdn_fwd_dplr_decode): q, k,
+    a, b [N,L,H,d_k], v [N,L,H,d_v] (one dtype), log_alpha None | [H] | [N,L,H] |
+    [N,L,H,d_k] fp32, state_pool [P,H,d_k,d_v] fp32, src_slots int32 [N], dst_slots int32
+    [N,L] (see gdn_fwd_decode for the slot convention).  Returns o [N,L,H,d_v]."""
+    import torch
+    for name, t in (("a", a), ("b", b)):
+        _require(t is not None and tuple(t.shape) == tuple(q.shape) and t.dtype == q.dtype,
+                 "%s must have the shape and dtype of q" % name)
+        _require(t.is_contiguous(), "%s must be contiguous" % name)
+    check_decode_tensors(q, k, v, None, log_alpha, state_pool, src_slots, dst_slots, out, write="add")
+    _same_device([("a", a), ("b", b)], q)
+    N, L, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((N, L, H, dv), dtype=q.dtype, device=q.device)
+    args = DplrDecodeArgs(N=N, L=L, H=H, d_k=dk, d_v=dv, dtype=_dtype_code(q), gate=gate_code(log_alpha, 3),
+                          q=_ptr(q), k=_ptr(k), a=_ptr(a), b=_ptr(b), v=_ptr(v), log_alpha=_ptr(log_alpha),
+                          state_pool=_ptr(state_pool), pool_size=state_pool.shape[0], src_slots=_ptr(src_slots),
+                          dst_slots=_ptr(dst_slots), o=_ptr(out))
+    _check(_lib.gdn_fwd_dplr_decode(ctypes.byref(args), _stream(stream)), "gdn_fwd_dplr_decode")
     return out
 
 

@@ -188,6 +188,24 @@ int check_dplr_step(const gdn_dplr_step_args *a) {
   return GDN_OK;
 }
 
+int check_dplr_decode(const gdn_dplr_decode_args *a) {
+  if (!a) return GDN_ERR_INVALID_ARG;
+  if (a->N < 0 || a->L < 1 || a->H <= 0 || a->pool_size < 1) return GDN_ERR_INVALID_ARG;
+  if ((long long)a->N * a->H > INT32_MAX || (long long)a->N * a->L > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+  if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (!gate_ok(a->gate)) return GDN_ERR_INVALID_ARG;
+  if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
+  if (a->N == 0) return GDN_OK;
+  if (!a->q || !a->k || !a->a || !a->b || !a->v || !a->state_pool || !a->src_slots || !a->dst_slots || !a->o)
+    return GDN_ERR_INVALID_ARG;
+  if ((a->log_alpha != nullptr) != (a->gate != GDN_GATE_NONE)) return GDN_ERR_INVALID_ARG;
+  const void *p4[] = {a->q, a->k, a->a, a->b, a->v, a->o, a->log_alpha, a->src_slots, a->dst_slots};
+  for (const void *p : p4)
+    if (p && !aligned(p, 4)) return GDN_ERR_INVALID_ARG;
+  if (!aligned(a->state_pool, 16)) return GDN_ERR_INVALID_ARG;
+  return GDN_OK;
+}
+
 struct BwdLayout {
   long slots;
   size_t states, tmat, part, dla;
@@ -471,6 +489,32 @@ int gdn_fwd_dplr_step(const gdn_dplr_step_args *a, void *hip_stream) {
   p.la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
   if (gdn::launch_dplr_step(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->d_v, kernel_gate(a->gate),
                             (hipStream_t)hip_stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+int gdn_fwd_dplr_decode(const gdn_dplr_decode_args *a, void *hip_stream) {
+  const int st = check_dplr_decode(a);
+  if (st != GDN_OK) return st;
+  if (a->N == 0) return GDN_OK;
+  gdn::DplrDecodeParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.a = a->a;
+  p.b = a->b;
+  p.log_alpha = a->log_alpha;
+  p.pool = a->state_pool;
+  p.src = a->src_slots;
+  p.dst = a->dst_slots;
+  p.o = a->o;
+  p.N = a->N;
+  p.L = a->L;
+  p.H = a->H;
+  p.P = a->pool_size;
+  p.la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
+  if (gdn::launch_dplr_decode(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->d_v, kernel_gate(a->gate),
+                              (hipStream_t)hip_stream) != hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;
 }

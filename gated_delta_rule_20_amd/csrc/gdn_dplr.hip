@@ -647,6 +647,126 @@ __global__ __launch_bounds__(256) void dplr_step_kernel(DplrStepParams p) {
   }
 }
 
+// Serving decode of this transition: L tokens per stream against a pool of states.  The
+// stream's state is read once from slot src[n], carried through its L tokens in
+// registers (the step above, token by token), and stored after token t into slot
+// dst[n, t] when that slot is in [0, P).  A stream whose src slot is outside [0, P) is
+// padding: nothing is read or written for it.
+template <typename E, int DK, int DV, int GATE>
+__global__ __launch_bounds__(256) void dplr_decode_kernel(DplrDecodeParams p) {
+  constexpr int CQ = DV / 4;
+  constexpr int RG = 256 / CQ;
+  constexpr int RP = DK / RG;
+  static_assert(RP >= 1 && RG * RP == DK, "decode geometry");
+  __shared__ float qs[2][DK], as_[2][DK], bs_[2][DK], ks[2][DK], al[2][DK];
+  __shared__ f32x4 red_u[RG][CQ], red_s[RG][CQ];
+  __shared__ float dots[2][2];
+
+  const int pair = blockIdx.x, n = pair / p.H, h = pair % p.H;
+  const int src = p.src[n];
+  if (src < 0 || src >= p.P) return;  // padding stream
+  const int tid = threadIdx.x, cq = tid % CQ, rg = tid / CQ;
+  const size_t slot = (size_t)p.H * DK * DV, head = (size_t)h * DK * DV;
+  f32x4 m[RP];
+  {
+    const float *st = p.pool + (size_t)src * slot + head;
+#pragma unroll
+    for (int u = 0; u < RP; ++u) m[u] = *(const f32x4 *)(st + (size_t)(rg * RP + u) * DV + 4 * cq);
+  }
+  for (int t = 0; t < p.L; ++t) {
+    const int b = t & 1;  // the token vectors alternate between two buffers
+    const size_t tok = (size_t)n * p.L + t, rowk = (tok * p.H + h) * DK;
+    if (tid < DK) {
+      qs[b][tid] = to_f(((const E *)p.q)[rowk + tid]);
+      as_[b][tid] = to_f(((const E *)p.a)[rowk + tid]);
+      bs_[b][tid] = to_f(((const E *)p.b)[rowk + tid]);
+      ks[b][tid] = to_f(((const E *)p.k)[rowk + tid]);
+      float a = 1.f;
+      if (GATE == GATE_HEAD) a = __expf(p.log_alpha[tok * p.la_stride + h]);
+      if (GATE == GATE_KEY) a = __expf(p.log_alpha[rowk + tid]);
+      al[b][tid] = a;
+    }
+    const E *vp = (const E *)p.v + (tok * p.H + h) * DV + 4 * cq;
+    f32x4 vv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = to_f(vp[e]);
+    __syncthreads();
+    f32x4 uu = zero4(), ss = zero4();
+#pragma unroll
+    for (int u = 0; u < RP; ++u) {
+      const int row = rg * RP + u;
+      uu += m[u] * as_[b][row];
+      ss += m[u] * (qs[b][row] * al[b][row]);
+    }
+    red_u[rg][cq] = uu;
+    red_s[rg][cq] = ss;
+    if (tid < 64) {
+      float db = 0.f, dk = 0.f;
+      for (int i = tid; i < DK; i += 64) {
+        db += qs[b][i] * bs_[b][i];
+        dk += qs[b][i] * ks[b][i];
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        db += __shfl_xor(db, off);
+        dk += __shfl_xor(dk, off);
+      }
+      if (tid == 0) {
+        dots[b][0] = db;
+        dots[b][1] = dk;
+      }
+    }
+    __syncthreads();
+    f32x4 U = zero4(), S = zero4();
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      U += red_u[g][cq];
+      S += red_s[g][cq];
+    }
+#pragma unroll
+    for (int u = 0; u < RP; ++u) {
+      const int row = rg * RP + u;
+      m[u] = m[u] * al[b][row] + U * bs_[b][row] + vv * ks[b][row];
+    }
+    if (rg == 0) {
+      E *o = (E *)p.o + (tok * p.H + h) * DV + 4 * cq;
+      const float qb = dots[b][0], qk = dots[b][1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = to_e<E>(S[e] + qb * U[e] + qk * vv[e]);
+    }
+    const int dst = p.dst[tok];
+    if (dst >= 0 && dst < p.P) {
+      float *sd = p.pool + (size_t)dst * slot + head;
+#pragma unroll
+      for (int u = 0; u < RP; ++u) *(f32x4 *)(sd + (size_t)(rg * RP + u) * DV + 4 * cq) = m[u];
+    }
+    // red_u / red_s are rewritten by the next token only after its first barrier, which
+    // every thread reaches after reading them here
+  }
+}
+
+template <typename E, int DK, int DV>
+hipError_t launch_dd(const DplrDecodeParams &p, int gate, hipStream_t stream) {
+  const dim3 grid(p.N * p.H), block(256);
+  if (gate == GATE_NONE)
+    hipLaunchKernelGGL((dplr_decode_kernel<E, DK, DV, GATE_NONE>), grid, block, 0, stream, p);
+  else if (gate == GATE_HEAD)
+    hipLaunchKernelGGL((dplr_decode_kernel<E, DK, DV, GATE_HEAD>), grid, block, 0, stream, p);
+  else if (gate == GATE_KEY)
+    hipLaunchKernelGGL((dplr_decode_kernel<E, DK, DV, GATE_KEY>), grid, block, 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+template <typename E>
+hipError_t launch_dd_e(const DplrDecodeParams &p, int dk, int dv, int gate, hipStream_t stream) {
+  if (dk == 64 && dv == 64) return launch_dd<E, 64, 64>(p, gate, stream);
+  if (dk == 64 && dv == 128) return launch_dd<E, 64, 128>(p, gate, stream);
+  if (dk == 128 && dv == 64) return launch_dd<E, 128, 64>(p, gate, stream);
+  if (dk == 128 && dv == 128) return launch_dd<E, 128, 128>(p, gate, stream);
+  return hipErrorInvalidValue;
+}
+
 template <typename E, int DK, int DV>
 hipError_t launch_ds(const DplrStepParams &p, int gate, hipStream_t stream) {
   const dim3 grid(p.N * p.H), block(256);
@@ -689,6 +809,11 @@ hipError_t launch_dp(const DplrParams &p, int gate, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_dplr_decode(const DplrDecodeParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream) {
+  if (p.N == 0) return hipSuccess;
+  return dtype == 1 ? launch_dd_e<bf16>(p, dk, dv, gate, stream) : launch_dd_e<float>(p, dk, dv, gate, stream);
+}
 
 hipError_t launch_dplr_step(const DplrStepParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream) {
   if (p.N == 0) return hipSuccess;

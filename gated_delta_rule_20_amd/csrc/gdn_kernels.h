@@ -108,6 +108,16 @@ struct DplrStepParams {
   int N, H, la_stride;
 };
 hipError_t launch_dplr_step(const DplrStepParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream);
+// L decode tokens per stream of the same transition against a pool of states.
+struct DplrDecodeParams {
+  const void *q, *k, *v, *a, *b;  // [N, L, H, d_k] (v: d_v), I/O dtype
+  const float *log_alpha;         // NULL | [N, L, H] (read at token * la_stride + h) | [N, L, H, d_k]
+  float *pool;                    // [P, H, d_k, d_v]
+  const int32_t *src, *dst;       // [N], [N, L]
+  void *o;                        // [N, L, H, d_v]
+  int N, L, H, P, la_stride;
+};
+hipError_t launch_dplr_decode(const DplrDecodeParams &p, int dtype, int dk, int dv, int gate, hipStream_t stream);
 
 // dtype: 0 fp32, 1 bf16.  Each launcher returns hipSuccess or the launch error.
 // dvb: columns of d_v per workgroup (32 or 64).

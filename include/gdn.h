@@ -295,6 +295,28 @@ typedef struct {
 
 int gdn_fwd_dplr_step(const gdn_dplr_step_args *args, void *hip_stream);
 
+/* Serving decode of the diagonal-plus-low-rank transition: L tokens per stream against
+ * a pool of states, with the per-token update of gdn_fwd_dplr_step and the pool and
+ * slot convention of gdn_fwd_decode (src_slots[n] read once, the state after token t
+ * stored into dst_slots[n, t] when in [0, pool_size), a stream with src outside
+ * [0, pool_size) is padding; the dst slots of one call must differ from each other and
+ * from the other streams' src slots).  Every gate; any dtype; d_k, d_v in {64, 128}. */
+typedef struct {
+  int N, L, H, d_k, d_v;     /* streams, tokens per stream (>= 1), heads, head dims     */
+  gdn_dtype dtype;           /* dtype of q, k, a, b, v, o                               */
+  gdn_gate gate;
+  const void *q, *k, *a, *b; /* [N, L, H, d_k]                                          */
+  const void *v;             /* [N, L, H, d_v]                                          */
+  const float *log_alpha;    /* NONE: NULL; HEAD: [N,L,H]; KEY: [N,L,H,d_k]; HEAD_CONST: [H] */
+  float *state_pool;         /* in/out: [pool_size, H, d_k, d_v] fp32 (M = S^T)        */
+  int pool_size;             /* number of slots (>= 1)                                  */
+  const int32_t *src_slots;  /* [N] device                                              */
+  const int32_t *dst_slots;  /* [N, L] device                                           */
+  void *o;                   /* out: [N, L, H, d_v], dtype                              */
+} gdn_dplr_decode_args;
+
+int gdn_fwd_dplr_decode(const gdn_dplr_decode_args *args, void *hip_stream);
+
 /* Static description of a status code (never NULL). */
 const char *gdn_status_str(int status);
 

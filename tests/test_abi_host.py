@@ -50,7 +50,8 @@ def fwd(g, a):
 
 def test_header_declares_the_boundary(g):
     assert g.header_functions() == ["gdn_bwd_chunked", "gdn_bwd_workspace_size", "gdn_fwd_chunked",
-                                    "gdn_fwd_decode", "gdn_fwd_dplr", "gdn_fwd_dplr_step", "gdn_fwd_recurrent_step",
+                                    "gdn_fwd_decode", "gdn_fwd_dplr", "gdn_fwd_dplr_decode", "gdn_fwd_dplr_step",
+                                    "gdn_fwd_recurrent_step",
                                     "gdn_fwd_workspace_size", "gdn_status_str", "gdn_version"]
 
 
@@ -402,3 +403,26 @@ def test_binding_rejects_bad_dplr_step_tensors(g):
         g.dplr_step(q, q, v, q, q[:1], None, st)
     with pytest.raises(ValueError, match="GPU device"):
         g.dplr_step(q, q, v, q, q, None, st)
+
+
+def dplr_decode_args(g, **kw):
+    a = g.DplrDecodeArgs(N=3, L=2, H=2, d_k=128, d_v=64, dtype=g.GDN_BF16, gate=g.GDN_GATE_HEAD, pool_size=4)
+    (a.q, a.k, a.a, a.b, a.v, a.log_alpha, a.state_pool, a.src_slots, a.dst_slots, a.o) = (fake(i) for i in range(10))
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(L=0), INVALID),
+    (dict(pool_size=0), INVALID),
+    (dict(a=None), INVALID),
+    (dict(dst_slots=None), INVALID),
+    (dict(log_alpha=None), INVALID),
+    (dict(state_pool=fake(6, 4)), INVALID),  # the pool needs 16-byte alignment
+    (dict(d_k=32), UNSUPPORTED),
+    (dict(N=0), OK),
+])
+def test_dplr_decode_host_validation(g, change, status):
+    assert g._lib.gdn_fwd_dplr_decode(ctypes.byref(dplr_decode_args(g, **change)), None) == status
+    assert g._lib.gdn_fwd_dplr_decode(None, None) == INVALID

@@ -1,5 +1,6 @@
 """GPU parity of the diagonal-plus-low-rank transition, the chunked forward
-(gdn_fwd_dplr) and the decode step (gdn_fwd_dplr_step), through the C ABI, against the
+(gdn_fwd_dplr), the decode step (gdn_fwd_dplr_step) and the pooled decode
+(gdn_fwd_dplr_decode), through the C ABI, against the
 fp64 oracle (oracle.fwd_dplr, the token recurrence).
 
 Metric: max |x - x_ref| / max |x_ref| per output tensor; 2e-2 for bf16 inputs, 1e-4
@@ -147,3 +148,46 @@ def test_dplr_steps_equal_forward(gdn, gate):
     o_ref, fs_ref = oracle.fwd_dplr(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], inp["log_alpha"],
                                     inp["initial_state"])
     assert relerr(torch.stack(outs, 1), o_ref) <= TOL["bf16"] and relerr(state, fs_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("gate", ["none", "head", "key", "const"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dplr_decode_pool(gdn, gate, dtype):
+    """Three tokens per stream against a pool: a padding stream, states stored after
+    chosen tokens (one back into the stream's own slot), untouched slots unchanged."""
+    N, L, H, dk, dv, P = 5, 3, 2, 128, 64, 12
+    inp = step_case(N, H, dk, dv, gate, dtype, seed=31 + len(gate), T=L)
+    g = torch.Generator().manual_seed(7)
+    pool = torch.randn(P, H, dk, dv, generator=g) * 0.3
+    src = torch.tensor([3, -1, 0, 7, 11], dtype=torch.int32)  # stream 1 is padding
+    dst = torch.full((N, L), -1, dtype=torch.int32)
+    dst[0] = torch.tensor([1, 2, 3], dtype=torch.int32)
+    dst[1, 0] = 8  # a padding stream stores nothing
+    dst[2, 2] = 0
+    dst[3, 0], dst[3, 2] = 4, 5
+    dst[4, 1] = 6
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    pool_d = pool.cuda()
+    o = gdn.dplr_decode(d["q"], d["k"], d["v"], d["a"], d["b"], d["log_alpha"], pool_d, src.cuda(), dst.cuda())
+    torch.cuda.synchronize()
+    la = oracle_la(inp, gate, N, L)
+    pool_ref = pool.clone().double().numpy()
+    tol = TOL[dtype]
+    for n in range(N):
+        s = int(src[n])
+        if not 0 <= s < P:
+            continue
+        s0 = pool[s][None].double()
+        for t in range(L):
+            sl = lambda x: None if x is None else x[n:n + 1, :t + 1]
+            o_ref, fs = oracle.fwd_dplr(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["a"]), sl(inp["b"]),
+                                        sl(la), s0)
+            assert relerr(o[n, t], o_ref[0, t]) <= tol, (n, t)
+            if 0 <= int(dst[n, t]) < P:
+                pool_ref[int(dst[n, t])] = fs[0]
+    got = pool_d.double().cpu().numpy()
+    for slot in range(P):
+        err = np.abs(got[slot] - pool_ref[slot]).max() / np.abs(pool_ref[slot]).max()
+        assert err <= 1e-5, (slot, err)
+    for slot in (7, 8, 9, 10, 11):  # never written: bit-identical
+        assert np.array_equal(got[slot], pool[slot].double().numpy())
