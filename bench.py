@@ -269,6 +269,42 @@ def time_pool_decode(gdn, N, L, H, dk, dv, store, steps=64):
             "hbm_gbs": nbytes / (ms / 1e3) / 1e9, "hbm_frac": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
 
 
+def time_dplr_pool_decode(gdn, N=256, L=4, H=16, dk=128, dv=128, steps=64):
+    """gdn_fwd_dplr_decode: L tokens for each of N streams per call, scalar gate, each
+    stream's state read from and written back to its own pool slot.  Algorithmic bytes:
+    the state read and written once per call in fp32, and per token q, k, a, b, v read
+    and o written in bf16 and log alpha read."""
+    import torch
+    import synth
+    inp = synth.dplr_inputs(N, L, H, dk, dv, "head", "bf16", seed=1207, state_std=0.02)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    pool = d["initial_state"].clone()
+    src = torch.arange(N, dtype=torch.int32, device="cuda")
+    dst = torch.full((N, L), -1, dtype=torch.int32, device="cuda")
+    dst[:, L - 1] = src
+    out = torch.empty((N, L, H, dv), dtype=torch.bfloat16, device="cuda")
+    args = (d["q"], d["k"], d["v"], d["a"], d["b"], d["log_alpha"], pool, src, dst)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    gdn.dplr_decode(*args, out=out)
+    torch.cuda.synchronize()
+    warm = max(4, int(SETTLE_MS / 1e3 / (time.perf_counter() - t)) + 1)
+    for _ in range(warm):
+        gdn.dplr_decode(*args, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        gdn.dplr_decode(*args, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = N * H * (2 * 4 * dk * dv + L * (2 * (4 * dk + 2 * dv) + 4))
+    return {"workload": "dplr-decode-pool-bf16-N%d-L%d-H%d-d%d-in-place" % (N, L, H, dk), "ms_per_step": ms,
+            "tokens_per_s": N * L / (ms / 1e3), "alg_bytes": nbytes, "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
+            "hbm_frac": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+
+
 def time_bwd(gdn, name, steps=20, cpu=False):
     """gdn_bwd_chunked on a workload: the gradients of o and of the final state are
     seeded N(0,1) and N(0, 0.1^2).  Algorithmic bytes: q, k, v, dout read and dq, dk,
@@ -506,6 +542,7 @@ def main():
             torch.cuda.empty_cache()
             extra.append(r)
         extra.append(time_dplr_step(gdn, cpu=not args.no_cpu))
+        extra.append(time_dplr_pool_decode(gdn))
         torch.cuda.empty_cache()
         extra.append(time_bwd(gdn, HEADLINE, cpu=not args.no_cpu))
         torch.cuda.empty_cache()
