@@ -530,6 +530,6 @@ const char *gdn_status_str(int status) {
   }
 }
 
-int gdn_version(void) { return 100; }
+int gdn_version(void) { return 200; }
 
 }  // extern "C"

@@ -1,5 +1,6 @@
 /*
- * gdn.h -- C ABI of the MI355X (gfx950) chunked gated delta-rule forward.
+ * gdn.h -- C ABI of the MI355X (gfx950) chunked gated delta rule: the forward, its
+ * gradients, decode steps for serving, and the diagonal-plus-low-rank transition.
  *
  * The method: a linear-attention layer keeps one fixed-size matrix state per
  * (sequence, head) ("Decoding Hybrid Linear Attention Architectures", sec. 1: a
