@@ -1,0 +1,70 @@
+"""Packed-sequence offsets that break the contract (cu_seqlens must be non-decreasing and
+end at T): the kernels validate each sequence's offsets on the device and leave the
+outputs of a malformed sequence unwritten, as include/gdn.h documents.  Offsets here:
+[0, 100, 400, 300] over 300 packed tokens; sequence 0 is valid, sequence 1 ends past T
+and sequence 2 ends before it starts.  Tokens 100 .. 299 belong to no valid sequence,
+so their output rows keep the caller's sentinel, and so do the final states of
+sequences 1 and 2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 7.0
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_20_amd as g
+    return g
+
+
+def relerr(x, ref):
+    x = x.detach().double().cpu().numpy()
+    return float(np.abs(x - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def malformed(inp):
+    cu = torch.tensor([0, 100, 400, 300], dtype=torch.int32)
+    return dict(inp, cu_seqlens=cu, N=3)
+
+
+def check_untouched(o, fs):
+    assert torch.all(o[0, 100:].float() == SENTINEL)
+    assert torch.all(fs[1:] == SENTINEL)
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_forward_leaves_malformed_sequences_untouched(gdn, dk):
+    inp = malformed(synth.random_inputs(1, 300, 2, dk, 128, "head", "bf16", seed=41))
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    o = torch.full((1, 300, 2, 128), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    fs = torch.full((3, 2, dk, 128), SENTINEL, device="cuda")
+    gdn.fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], None, d["cu_seqlens"], out=o, final_state=fs)
+    torch.cuda.synchronize()
+    check_untouched(o, fs)
+    o_ref, fs_ref = oracle.fwd(inp["q"][:, :100], inp["k"][:, :100], inp["v"][:, :100], inp["beta"][:, :100],
+                               inp["log_alpha"][:, :100])
+    assert relerr(o[:, :100], o_ref) <= 2e-2 and relerr(fs[:1], fs_ref) <= 2e-2
+
+
+def test_dplr_leaves_malformed_sequences_untouched(gdn):
+    inp = malformed(synth.dplr_inputs(1, 300, 2, 128, 128, "head", "bf16", seed=42))
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    o = torch.full((1, 300, 2, 128), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    fs = torch.full((3, 2, 128, 128), SENTINEL, device="cuda")
+    gdn.fwd_dplr(d["q"], d["k"], d["v"], d["a"], d["b"], d["log_alpha"], None, d["cu_seqlens"], out=o,
+                 final_state=fs)
+    torch.cuda.synchronize()
+    check_untouched(o, fs)
+    sl = lambda x: x[:, :100]
+    o_ref, fs_ref = oracle.fwd_dplr(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["a"]), sl(inp["b"]),
+                                    sl(inp["log_alpha"]))
+    assert relerr(o[:, :100], o_ref) <= 2e-2 and relerr(fs[:1], fs_ref) <= 2e-2
