@@ -4,7 +4,8 @@ outputs of a malformed sequence unwritten, as include/gdn.h documents.  Offsets 
 [0, 100, 400, 300] over 300 packed tokens; sequence 0 is valid, sequence 1 ends past T
 and sequence 2 ends before it starts.  Tokens 100 .. 299 belong to no valid sequence,
 so their output rows keep the caller's sentinel, and so do the final states of
-sequences 1 and 2.
+sequences 1 and 2.  The backward's kernels skip the malformed sequences the same way;
+its test checks the valid sequence's gradients.
 """
 import numpy as np
 import pytest
@@ -68,3 +69,25 @@ def test_dplr_leaves_malformed_sequences_untouched(gdn):
     o_ref, fs_ref = oracle.fwd_dplr(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["a"]), sl(inp["b"]),
                                     sl(inp["log_alpha"]))
     assert relerr(o[:, :100], o_ref) <= 2e-2 and relerr(fs[:1], fs_ref) <= 2e-2
+
+
+@pytest.mark.parametrize("write", ["delta", "add"])
+def test_backward_with_malformed_sequences(gdn, write):
+    """The valid sequence's gradients are exact; the malformed ones are skipped."""
+    inp = malformed(synth.random_inputs(1, 300, 2, 128, 128, "head", "bf16", seed=43))
+    if write == "add":
+        inp["beta"] = None
+    g = torch.Generator().manual_seed(44)
+    dout = torch.randn(1, 300, 2, 128, generator=g).to(torch.bfloat16)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    got = gdn.bwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], None, dout.cuda(), None,
+                          d["cu_seqlens"], write=write)
+    torch.cuda.synchronize()
+    sl = lambda x: None if x is None else x[:, :100]
+    ref = oracle.bwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["log_alpha"]), None,
+                     sl(dout), None, write=write)
+    for name, g_, r in zip(["dq", "dk", "dv", "dbeta", "dlog_alpha"], got[:5], ref[:5]):
+        if r is None:
+            continue
+        assert relerr(g_[:, :100], r) <= 2e-2, name
+    assert relerr(got[5][:1], ref[5]) <= 2e-2
