@@ -425,25 +425,23 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
     }
     gram(Ql, Kl, e_out, X1, 0, NWB);
     __syncthreads();
-    // ---- O += P_qk V
+    // ---- O += P_qk V; A_ab into X2
 #pragma unroll
     for (int q = 0; q < OQ; ++q) {
       int m0, n0;
       otile(q, m0, n0);
       Oacc[q] += tile_frag<DC>(rowf(X1, SX, m0 + lm), rowb(Vt, SVT, n0 + lm), kend(m0));
     }
+    gram(Al, Bl, e_in, X2, 0, NWB);
     __syncthreads();
-    // ---- A_ab into X1
-    gram(Al, Bl, e_in, X1, 0, NWB);
-    __syncthreads();
-    // ---- T = (I - A_ab)^-1 into Tb (waves 0-2) while the other waves form A_ak (into X2)
+    // ---- T = (I - A_ab)^-1 into Tb (waves 0-2) while the other waves form A_ak (into X1)
     // and then R = diag(e^{G_{j-1}}) A M0 + A_ak V (into R^T)
     if (wave == 0) {  // diagonal blocks: lane (lg, lm) solves column lm of block lg
       const int o = 16 * lg;
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float *arow = X1 + (o + r) * SX + o;
+        const float *arow = X2 + (o + r) * SX + o;
         float acc = r == lm ? 1.f : 0.f;
 #pragma unroll
         for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
@@ -457,7 +455,7 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) Tb[(o + r) * SX + o + lm] = x[r];
     } else {
-      gram(Al, Kl, e_in, X2, 1, NWB - 1);
+      gram(Al, Kl, e_in, X1, 1, NWB - 1);
     }
     __syncthreads();
     if (wave < 3) {  // off-diagonal blocks, block column b = wave: T[a][b] = T[a][a] sum_k A[a][k] T[k][b]
@@ -470,7 +468,7 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
           if (k0 + 32 <= 16 * b || k0 >= 16 * a) continue;  // wave-uniform
           const int kk = k0 + 8 * lg;                        // this lane's 8 k-slots
           const bool in = kk >= 16 * b && kk < 16 * a;
-          f32x8 af = ld8(X1 + (16 * a + lm) * SX + kk), bfv;
+          f32x8 af = ld8(X2 + (16 * a + lm) * SX + kk), bfv;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             if (!in) af[i] = 0.f;
@@ -492,7 +490,7 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
       for (int t = wave - 3; t < 8; t += NWB - 3) {  // the 8 tiles of R over waves 3 ..
         const int m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
         const f32x4 v = tile_frag<DK>(rowb(Al, SKE, m0 + lm), rowf(Mt, SM, n0 + lm));
-        const f32x4 w = tile_frag<DC>(rowf(X2, SX, m0 + lm), rowb(Vt, SVT, n0 + lm), kend(m0));
+        const f32x4 w = tile_frag<DC>(rowf(X1, SX, m0 + lm), rowb(Vt, SVT, n0 + lm), kend(m0));
         f32x4 res;
 #pragma unroll
         for (int u = 0; u < 4; ++u) res[u] = egp[m0 + 4 * lg + u] * v[u] + w[u];
