@@ -591,8 +591,15 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
     f32x4 sv = zero4(), rv = zero4();
     if (n0 <= m0) {
-      if (!ADD) sv = tile_g<E, DK, true, true>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
-      rv = tile_g<E, DK, true, true>(m0, n0, lg, lm, Q_, [&](int d, int i) { return K_(i, d); });
+      if constexpr (std::is_same<E, bf16>::value) {  // bf16 rows read whole
+        const E *kr = Kl + (m0 + lm) * SKE + 8 * lg, *qr = Ql + (m0 + lm) * SKE + 8 * lg;
+        const E *kc = Kl + (n0 + lm) * SKE + 8 * lg;
+        if (!ADD) sv = tile_frag<DK>([&](int k0) { return ld8(kr + k0); }, [&](int k0) { return ld8(kc + k0); });
+        rv = tile_frag<DK>([&](int k0) { return ld8(qr + k0); }, [&](int k0) { return ld8(kc + k0); });
+      } else {
+        if (!ADD) sv = tile_g<E, DK, true, true>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
+        rv = tile_g<E, DK, true, true>(m0, n0, lg, lm, Q_, [&](int d, int i) { return K_(i, d); });
+      }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
