@@ -365,11 +365,13 @@ def fwd_chunked(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=No
     args = make_fwd_args(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out,
                          final_state if output_final_state else None, chunk, write)
     need = fwd_workspace_size(args)
+    own = None
     if need:
         if workspace is None or workspace.numel() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = own = torch.empty(need, dtype=torch.uint8, device=q.device)
         args.workspace, args.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _check(_lib.gdn_fwd_chunked(ctypes.byref(args), _stream(stream)), "gdn_fwd_chunked")
+    _keep_for_stream(own, stream)
     return out, (final_state if output_final_state else None)
 
 
@@ -579,6 +581,14 @@ class PreparedBwd:
         return self.outs
 
 
+def _keep_for_stream(buf, stream):
+    """A scratch buffer allocated here on torch's current stream but used by work queued
+    on another stream: tell the caching allocator, so that the block is not handed out
+    again before that stream's work is done."""
+    if buf is not None and stream is not None:
+        buf.record_stream(stream)
+
+
 def _bwd_args(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state, cu_seqlens, output_dinitial,
               workspace, write="delta"):
     import torch
@@ -618,6 +628,7 @@ def bwd_chunked(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state=None
     args, outs, keep = _bwd_args(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state, cu_seqlens,
                                  output_dinitial, workspace, write)
     _check(_lib.gdn_bwd_chunked(ctypes.byref(args), _stream(stream)), "gdn_bwd_chunked")
+    _keep_for_stream(keep[-1] if keep[-1] is not workspace else None, stream)
     return outs
 
 

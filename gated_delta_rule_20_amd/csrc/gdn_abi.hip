@@ -25,9 +25,11 @@ bool operands_ok(int gate, int write, const void *beta, const void *log_alpha) {
   return (beta != nullptr) == (write == GDN_WRITE_DELTA) && (log_alpha != nullptr) == (gate != GDN_GATE_NONE);
 }
 
-// Value columns per workgroup: 64, or 32 when there are too few (sequence, head)
-// streams to give every compute unit a workgroup.
-int choose_dvb(int N, int H, int dv) {
+// Value columns per workgroup of the fused kernel: 64, or 32 when there are too few
+// (sequence, head) streams to give every compute unit a workgroup; always 32 for fp32
+// I/O with d_k = 128, whose tiles leave LDS room for 32 columns only.
+int choose_dvb(int N, int H, int dv, int dtype, int dk) {
+  if (dtype == GDN_F32 && dk == 128) return 32;
   const long wg64 = (long)N * H * (dv / 64);
   return wg64 >= 256 ? 64 : 32;
 }
@@ -39,7 +41,8 @@ int check_fwd(const gdn_fwd_args *a) {
   if (!gate_ok(a->gate) || !write_ok(a->write)) return GDN_ERR_INVALID_ARG;
   if (a->chunk != 64) return GDN_ERR_UNSUPPORTED;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
-  if (a->dtype == GDN_F32 && a->d_k != 64) return GDN_ERR_UNSUPPORTED;
+  // every offset inside one 64-token chunk of q, k or v must fit 32 bits
+  if ((long)a->H * 64 * 256 > (long)UINT32_MAX) return GDN_ERR_UNSUPPORTED;
   if (a->cu_seqlens) {
     if (a->B != 1 || a->N < 1) return GDN_ERR_INVALID_ARG;
   } else if (a->N != a->B) {
@@ -141,6 +144,7 @@ int check_bwd(const gdn_bwd_args *a) {
   const int st = check_fwd(&f);
   if (st != GDN_OK) return st;
   if (a->gate == GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
+  if (a->dtype == GDN_F32 && a->d_k != 64) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long)a->B * a->T > 0;
   if (tokens && (!a->dq || !a->dk || !a->dv)) return GDN_ERR_INVALID_ARG;
   // dbeta exactly for the delta write; dlog_alpha exactly for a gate (the constant
@@ -167,6 +171,7 @@ int check_dplr(const gdn_dplr_args *a) {
   const int st = check_fwd(&f);
   if (st != GDN_OK) return st;
   if (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD) return GDN_ERR_UNSUPPORTED;
+  if (a->dtype == GDN_F32 && a->d_k != 64) return GDN_ERR_UNSUPPORTED;
   if ((long)a->B * a->T > 0 && (!a->a || !a->b)) return GDN_ERR_INVALID_ARG;
   if ((a->a && !aligned(a->a, 16)) || (a->b && !aligned(a->b, 16))) return GDN_ERR_INVALID_ARG;
   return GDN_OK;
@@ -249,7 +254,7 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
       hipError_t e = a->dfinal_state
                          ? hipMemcpyAsync(a->dinitial_state, a->dfinal_state, bytes, hipMemcpyDeviceToDevice,
                                           (hipStream_t)hip_stream)
-                         : hipMemsetAsync(a->dinitial_state, 0, bytes, (hipStream_t)hip_stream);
+                         : gdn::launch_fill_zero(a->dinitial_state, bytes / 4, (hipStream_t)hip_stream);
       if (e != hipSuccess) return GDN_ERR_HIP;
     }
     return GDN_OK;
@@ -284,7 +289,7 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
     fp.nb = a->d_v / 64;
     if (gdn::launch_fwd_pipe(fp, (int)a->gate, add, stream) != hipSuccess) return GDN_ERR_HIP;
   } else {
-    const int dvb = choose_dvb(a->N, a->H, a->d_v);
+    const int dvb = choose_dvb(a->N, a->H, a->d_v, a->dtype, a->d_k);
     fp.nb = a->d_v / dvb;
     if (gdn::launch_fwd_fused(fp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, kernel_gate(a->gate), add, stream) !=
         hipSuccess)
@@ -316,6 +321,11 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   bp.T = a->T;
   bp.dv = a->d_v;
   bp.slots = L.slots;
+  // the constant decay's per-token gradients are summed over every token of the call:
+  // tokens that no valid sequence covers (outside [cu[0], cu[N]), or in a sequence
+  // skipped for malformed offsets) must contribute zero
+  if (a->gate == GDN_GATE_HEAD_CONST && gdn::launch_fill_zero(dla_tok, (size_t)tokens * a->H, stream) != hipSuccess)
+    return GDN_ERR_HIP;
   if (gdn::launch_bwd(bp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, kernel_gate(a->gate), add, stream) != hipSuccess)
     return GDN_ERR_HIP;
   if (a->gate == GDN_GATE_HEAD_CONST &&
@@ -392,7 +402,7 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
       return GDN_ERR_HIP;
     return GDN_OK;
   }
-  const int dvb = choose_dvb(a->N, a->H, a->d_v);
+  const int dvb = choose_dvb(a->N, a->H, a->d_v, a->dtype, a->d_k);
   p.nb = a->d_v / dvb;
   if (gdn::launch_fwd_fused(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, dvb, kernel_gate(a->gate),
                             a->write == GDN_WRITE_ADD, stream) != hipSuccess)

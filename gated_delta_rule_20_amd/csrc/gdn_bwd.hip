@@ -2,7 +2,8 @@
 //
 // Reverse mode through the chunk equations of the forward ("Decoding Hybrid Linear
 // Attention Architectures", sec. 5; the WY / UT form of "Linear Attention Variants",
-// DeltaNet section), for the delta write with no gate or one decay per (token, head).
+// DeltaNet section), for the delta write and the additive write, with no gate, one
+// decay per (token, head) or one constant decay per head.
 // Per chunk, with G the chunk-local decay prefix, Gamma[r,i] = e^{G_r - G_i} (i <= r),
 // Kt = e^G K, Qt = e^G Q, Kh = e^{G_C - G} K, gam = e^{G_C},
 // A = strict(diag(beta)(K K^T * Gamma)), T = (I + A)^-1, P = incl(Q K^T * Gamma),
@@ -16,7 +17,9 @@
 // the sum of dG_r over r >= t in the chunk plus dG_C.
 //
 // Three launches:
-//  1. the fused forward with chunk-state output: every chunk's entering state M0;
+//  1. a forward that stores every chunk's entering state M0 instead of o: the
+//     pipelined kernel's STATES variant for bf16 with d_k = 128, the fused kernel
+//     otherwise;
 //  2. bwd_state_kernel, one workgroup per (sequence, head, 32 value columns), walks the
 //     chunks in reverse carrying dM: it writes dV, the entering-state gradient and T,
 //     and per value block the partial sums of dP, dT, dQ, dK, dG, dbeta and dG_C
@@ -24,8 +27,12 @@
 //  3. bwd_chunk_kernel, one workgroup per (chunk, head), fully parallel: it sums the
 //     partials in a fixed order (deterministic), forms dA and the Gram / Gamma terms
 //     and writes dq, dk, dbeta and d log alpha.
-// All arithmetic is fp32 (inputs in bf16 or fp32): the products on the matrix cores
-// (v_mfma_f32_16x16x4f32) with operands gathered from LDS, the rest on the vector units.
+// All arithmetic is fp32 or its equivalent (inputs in bf16 or fp32).  With bf16 I/O the
+// products run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16): an operand whose
+// values are bf16 inputs (q, k, dO) is taken exactly, any other is split into a hi + lo
+// pair of bf16 terms (about 2^-17 relative error per product).  With fp32 I/O they run
+// on v_mfma_f32_16x16x4f32 with operands gathered from LDS.  The rest runs on the
+// vector units.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 #include "gdn_tile.h"
@@ -750,9 +757,23 @@ __global__ __launch_bounds__(1024) void sum_tokens_kernel(const float *x, long t
   if (tid == 0) out[h] = part[0];
 }
 
+// x[0 .. n) = 0 (a kernel rather than a memset, so that graph capture records no
+// memset node)
+__global__ void fill_zero_kernel(float *x, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    x[i] = 0.f;
+}
+
 }  // namespace
 
 size_t bwd_part_floats(int dk) { return dk == 128 ? Part<128>::SIZE : Part<64>::SIZE; }
+
+hipError_t launch_fill_zero(float *x, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream, x, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_sum_tokens(const float *x, long tokens, int H, float *out, hipStream_t stream) {
   if (H <= 0) return hipSuccess;

@@ -63,9 +63,14 @@ __device__ __forceinline__ void st_pack(E *dst, const E (&v)[R]) {
   *(T *)dst = u.t;
 }
 
+// LEAN (fp32 I/O with d_k = 128): no transposed copy of K (the state update gathers
+// its K^T operands from the row-major tile), no O staging tile (each lane stores its
+// outputs directly) and the diagonal blocks of A kept in the fp32 A tile, so that the
+// tiles fit the 160 KiB of LDS.
 template <typename E, int DK, int DVB, bool KG>
 struct Cfg {
   static constexpr int ES = sizeof(E);
+  static constexpr bool LEAN = sizeof(E) == 4 && DK == 128;
   static constexpr int VEC = 16 / ES;       // elements per 16-byte access
   static constexpr int SK = DK + VEC;       // row stride of K, Q (elements, padded)
   static constexpr int ST = C + VEC;        // row stride of 64-wide matrices
@@ -83,15 +88,16 @@ struct Cfg {
   static constexpr int OFF_K = 0;
   static constexpr int OFF_Q = OFF_K + C * SK * ES;
   static constexpr int OFF_KT = OFF_Q + C * SK * ES;
-  static constexpr int OFF_VT = OFF_KT + DK * ST * ES;
+  static constexpr int OFF_VT = OFF_KT + (LEAN ? 0 : DK * ST * ES);
   static constexpr int OFF_T = OFF_VT + DVB * ST * ES;
   static constexpr int OFF_P = OFF_T + C * ST * ES;
   static constexpr int OFF_A = OFF_P + C * ST * ES;
   static constexpr int OFF_O = OFF_A + C * ST * ES;
-  static constexpr int OFF_AD = OFF_O + C * SO * ES;
-  static constexpr int OFF_VEC = OFF_AD + 4 * 16 * 16 * 4;
+  static constexpr int OFF_AD = OFF_O + (LEAN ? 0 : C * SO * ES);
+  static constexpr int OFF_VEC = OFF_AD + (LEAN ? 0 : 4 * 16 * 16 * 4);
   static constexpr int OFF_G = OFF_VEC + (5 * C + 8) * 4;  // per-channel gate: g [C][SG], e^{g_C} [DK]
-  static constexpr int BYTES = OFF_G + (KG ? (C * SG + DK) * 4 : 0);
+  // (LEAN keeps e^{g_C} in the scalar gate's vectors, which the per-channel gate leaves unused)
+  static constexpr int BYTES = OFF_G + (KG ? (C * SG + (LEAN ? 0 : DK)) * 4 : 0);
   static_assert(RPT >= 1 && C * CH == RPT * NT, "K loader geometry");
   static_assert(!KG || C * CHG == RPTG * NT, "log-decay loader geometry");
   static_assert(RPTV >= 1 && C * CHV == RPTV * NT, "V loader geometry");
@@ -108,6 +114,7 @@ template <typename E, int DK, int DVB, int GATE, bool ADD>
 __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   constexpr bool KG = GATE == GATE_KEY;
   typedef Cfg<E, DK, DVB, KG> CF;
+  constexpr bool LEAN = CF::LEAN;
   typedef typename Frag<E>::type F;
   constexpr int SK = CF::SK, ST = CF::ST, SO = CF::SO, VEC = CF::VEC, SG = CF::SG;
   __shared__ __align__(16) char smem[CF::BYTES];
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   float *egcs = egs + C;
   float *misc = egcs + C;
   float *Gs = (float *)(smem + CF::OFF_G);  // KEY: chunk-local log-decay prefix per channel
-  float *egck = Gs + C * SG;                 // KEY: e^{g_C} per channel
+  float *egck = LEAN ? las : Gs + C * SG;    // KEY: e^{g_C} per channel (LEAN: las, gs)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
@@ -255,12 +262,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       *(u32x4 *)(Ks + row * SK + cc * VEC) = rk[u];
       *(u32x4 *)(Qs + row * SK + cc * VEC) = rq[u];
     }
+    if constexpr (!LEAN) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      E col[CF::RPT];
+      for (int e = 0; e < VEC; ++e) {
+        E col[CF::RPT];
 #pragma unroll
-      for (int u = 0; u < CF::RPT; ++u) col[u] = ((const E *)&rk[u])[e];
-      st_pack<E, CF::RPT>(KTs + (cc * VEC + e) * ST + rg * CF::RPT, col);
+        for (int u = 0; u < CF::RPT; ++u) col[u] = ((const E *)&rk[u])[e];
+        st_pack<E, CF::RPT>(KTs + (cc * VEC + e) * ST + rg * CF::RPT, col);
+      }
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
         const float pv = qk[j] * gam;
         if (!ADD) {
           const float av = (i < r) ? betas[r] * kk[j] * gam : 0.f;
-          if (a == b)
+          if (a == b && !LEAN)
             AD[(16 * a + 4 * lg + j) * 16 + lm] = av;
           else
             As[r * ST + i] = to_e<E>(av);
@@ -373,13 +382,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
     //     lane (lg, lm) solves column lm of block lg
     if (wave == 0) {
       if (!ADD) {
-      const float *ad = AD + lg * 256;
+      // diagonal block lg of A: the fp32 AD tiles, or (LEAN) the fp32 A tile itself
+      const float *ad = LEAN ? (const float *)As + 16 * lg * ST + 16 * lg : AD + lg * 256;
+      constexpr int ADS = LEAN ? ST : 16;
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float acc = (r == lm) ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < r; ++i) acc -= ad[r * 16 + i] * x[i];
+        for (int i = 0; i < r; ++i) acc -= ad[r * ADS + i] * x[i];
         x[r] = acc;
       }
 #pragma unroll
@@ -397,11 +408,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float e = __expf(g[j]);
-          kp[j] = to_e<E>(to_f(kp[j]) * e);
+          if (!LEAN) kp[j] = to_e<E>(to_f(kp[j]) * e);  // LEAN: applied as K is read
           qp[j] = to_e<E>(to_f(qp[j]) * e);
         }
       }
-      for (int idx = t3; idx < DK * (C / 4); idx += NT - 64) {
+      for (int idx = t3; !LEAN && idx < DK * (C / 4); idx += NT - 64) {
         const int ch = idx / (C / 4), i4 = (idx % (C / 4)) * 4;
         const float gc = Gs[(C - 1) * SG + ch];
         E *kt = KTs + ch * ST + i4;
@@ -462,7 +473,16 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
         for (int i = 0; i < 4; ++i) {
           if (!ADD) {
             const E *kr = Ks + (16 * i + lm) * SK + 32 * s + 4 * lg;
-            X[i] = mma(ld4x2(kr, kr + 16), MB[s], X[i]);
+            F kf = ld4x2(kr, kr + 16);
+            if constexpr (LEAN && KG) {  // K e^G, per channel
+              const float *gr = Gs + (16 * i + lm) * SG + 32 * s + 4 * lg;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                kf[j] *= __expf(gr[j]);
+                kf[4 + j] *= __expf(gr[16 + j]);
+              }
+            }
+            X[i] = mma(kf, MB[s], X[i]);
           }
           const E *qr = Qs + (16 * i + lm) * SK + 32 * s + 4 * lg;
           O[i] = mma(ld4x2(qr, qr + 16), MB[s], O[i]);
@@ -517,19 +537,54 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
         if (KG)
 #pragma unroll
           for (int j = 0; j < 4; ++j) M[t][j] *= egck[16 * t + 4 * lg + j];
-        const E *kt = KTs + (16 * t + lm) * ST + 4 * lg;
-        M[t] = mma(ld4x2(kt, kt + 16), DT0, M[t]);
-        M[t] = mma(ld4x2(kt + 32, kt + 48), DT1, M[t]);
+        if constexpr (LEAN) {
+          // K^T fragments gathered from the row-major K tile: entry (key 16t + lm,
+          // token i) is K[i][16t + lm] (times e^{g_C - g_i} per channel)
+          const int ch = 16 * t + lm;
+          const float gce = KG ? Gs[(C - 1) * SG + ch] : 0.f;
+          F k0, k1;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i0 = 4 * lg + j;
+            k0[j] = to_f(Ks[i0 * SK + ch]);
+            k0[4 + j] = to_f(Ks[(16 + i0) * SK + ch]);
+            k1[j] = to_f(Ks[(32 + i0) * SK + ch]);
+            k1[4 + j] = to_f(Ks[(48 + i0) * SK + ch]);
+            if (KG) {
+              k0[j] *= __expf(gce - Gs[i0 * SG + ch]);
+              k0[4 + j] *= __expf(gce - Gs[(16 + i0) * SG + ch]);
+              k1[j] *= __expf(gce - Gs[(32 + i0) * SG + ch]);
+              k1[4 + j] *= __expf(gce - Gs[(48 + i0) * SG + ch]);
+            }
+          }
+          M[t] = mma(k0, DT0, M[t]);
+          M[t] = mma(k1, DT1, M[t]);
+        } else {
+          const E *kt = KTs + (16 * t + lm) * ST + 4 * lg;
+          M[t] = mma(ld4x2(kt, kt + 16), DT0, M[t]);
+          M[t] = mma(ld4x2(kt + 32, kt + 48), DT1, M[t]);
+        }
       }
+      if constexpr (LEAN) {  // O straight to HBM: lane holds column n0 + lm of rows 16i + 4lg + j
+        const int nv = min(C, len - c * C);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Os[(16 * i + 4 * lg + j) * SO + n0 + lm] = to_e<E>(O[i][j]);
+          for (int j = 0; j < 4; ++j) {
+            const int r = 16 * i + 4 * lg + j;
+            if (r < nv && p.o) ob[(size_t)(c * C + r) * sv + n0 + lm] = to_e<E>(O[i][j]);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) Os[(16 * i + 4 * lg + j) * SO + n0 + lm] = to_e<E>(O[i][j]);
+      }
     }
     __syncthreads();
 
     // (6) O tile -> HBM (coalesced rows), next chunk's tiles -> LDS
-    for (int idx = tid; idx < C * CF::CHV; idx += NT) {
+    for (int idx = tid; !LEAN && idx < C * CF::CHV; idx += NT) {
       const int row = idx / CF::CHV, cq = idx % CF::CHV;
       if (row < nv && p.o)
         *(uint4 *)(ob + (size_t)(c * C + row) * sv + cq * VEC) = *(const uint4 *)(Os + row * SO + cq * VEC);
@@ -586,13 +641,12 @@ hipError_t launch_g(const FwdParams &p, int gate, bool add, hipStream_t stream) 
 hipError_t launch_fwd_fused(const FwdParams &p, int dtype, int dk, int dvb, int gate, bool add,
                             hipStream_t stream) {
   if (dtype == 1) {
-    if (dk == 128 && dvb == 64) return launch_g<bf16, 128, 64>(p, gate, add, stream);
-    if (dk == 128 && dvb == 32) return launch_g<bf16, 128, 32>(p, gate, add, stream);
     if (dk == 64 && dvb == 64) return launch_g<bf16, 64, 64>(p, gate, add, stream);
     if (dk == 64 && dvb == 32) return launch_g<bf16, 64, 32>(p, gate, add, stream);
   } else {
     if (dk == 64 && dvb == 64) return launch_g<float, 64, 64>(p, gate, add, stream);
     if (dk == 64 && dvb == 32) return launch_g<float, 64, 32>(p, gate, add, stream);
+    if (dk == 128 && dvb == 32) return launch_g<float, 128, 32>(p, gate, add, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -151,32 +151,43 @@ __device__ __forceinline__ float readlane(float x, int l) {
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Per-sequence tensor bases and extents.  Every load builds the buffer descriptor of
+// its chunk: based at the chunk's first row, with the bytes left in the sequence as
+// its range, so that every offset inside a chunk fits 32 bits however long the
+// sequence is, and rows past the sequence end read as zero (range check).
 struct Res {
-  __amdgpu_buffer_rsrc_t k, q, v, beta, la, kh;
+  const char *k, *q, *v, *beta, *la, *kh;
+  uint64_t span_qk, span_v, span_s, span_kh, span_beta, span_la;  // bytes from base to the end
   uint32_t row_qk, row_v, row_s;  // bytes between consecutive tokens
 };
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const char *base, uint64_t span, uint64_t off) {
+  const uint64_t left = span > off ? span - off : 0;
+  const uint32_t rec = left > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)left;
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(base + (span > off ? off : 0)), 0, (int)rec, 0x00020000);
+}
 
 // ---- loaders: chunk tiles straight into LDS
 // one [64][128] tile of K (q = false) or Q (q = true) of a chunk
 __device__ __forceinline__ void load_kq(const Res &rs, char *dst, int chunk, int lane, bool q) {
-  const uint32_t soff = (uint32_t)chunk * C * rs.row_qk;
+  const uint64_t off = (uint64_t)chunk * C * rs.row_qk;
+  const __amdgpu_buffer_rsrc_t r4 = chunk_rsrc(q ? rs.q : rs.k, rs.span_qk, off);
   char *d = dst + (q ? C * DK * 2 : 0);
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
     const int r = 4 * n + (lane >> 4);
     const int ch = (lane & 15) ^ kq_swz(r & 15);
     const uint32_t vo = r * rs.row_qk + ch * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(q ? rs.q : rs.k, (lds_void_t *)(d + n * 1024), 16, vo, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r4, (lds_void_t *)(d + n * 1024), 16, vo, 0, 0, 0);
   }
 }
 // K e^{g_C - G} of a chunk (per-key-channel gate), in the layout of K
 __device__ __forceinline__ void load_kh(const Res &rs, char *dst, int chunk, int lane) {
-  const uint32_t soff = (uint32_t)chunk * C * rs.row_qk;
+  const __amdgpu_buffer_rsrc_t r4 = chunk_rsrc(rs.kh, rs.span_kh, (uint64_t)chunk * C * rs.row_qk);
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
     const int r = 4 * n + (lane >> 4);
     const int ch = (lane & 15) ^ kq_swz(r & 15);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.kh, (lds_void_t *)(dst + n * 1024), 16, r * rs.row_qk + ch * 16, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r4, (lds_void_t *)(dst + n * 1024), 16, r * rs.row_qk + ch * 16, 0, 0, 0);
   }
 }
 // `bytes` (a multiple of 1 KiB) copied verbatim from `src` into LDS
@@ -194,22 +205,25 @@ __device__ __forceinline__ void load_egc(const float *src, float *dst, int lane)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + 64), 4, 256 + lane * 4, 0, 0, 0);
 }
 __device__ __forceinline__ void load_v(const Res &rs, char *dst, int chunk, int lane) {
-  const uint32_t soff = (uint32_t)chunk * C * rs.row_v;
+  const __amdgpu_buffer_rsrc_t r4 = chunk_rsrc(rs.v, rs.span_v, (uint64_t)chunk * C * rs.row_v);
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const int r = 8 * n + (lane >> 3);
     const int ch = (lane & 7) ^ (r & 7);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.v, (lds_void_t *)(dst + n * 1024), 16, r * rs.row_v + ch * 16, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r4, (lds_void_t *)(dst + n * 1024), 16, r * rs.row_v + ch * 16, 0, 0, 0);
   }
 }
 template <int GATE>
 __device__ __forceinline__ void load_bl(const Res &rs, char *dst, int chunk, int lane) {
-  const uint32_t soff = (uint32_t)chunk * C * rs.row_s;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.beta, (lds_void_t *)dst, 4, lane * rs.row_s, soff, 0, 0);
+  const uint64_t off = (uint64_t)chunk * C * rs.row_s;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(chunk_rsrc(rs.beta, rs.span_beta, off), (lds_void_t *)dst, 4,
+                                           lane * rs.row_s, 0, 0, 0);
   if (GATE == GATE_HEAD)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.la, (lds_void_t *)(dst + 256), 4, lane * rs.row_s, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(chunk_rsrc(rs.la, rs.span_la, off), (lds_void_t *)(dst + 256), 4,
+                                             lane * rs.row_s, 0, 0, 0);
   if (GATE == GATE_CONST)  // the head's one value, for every row
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.la, (lds_void_t *)(dst + 256), 4, 0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(chunk_rsrc(rs.la, rs.span_la, 0), (lds_void_t *)(dst + 256), 4, 0, 0, 0,
+                                             0);
 }
 
 // ---- decay prefix and the per-position factors of Gamma (loader wave, two chunks ahead).
@@ -368,25 +382,27 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   rs.row_v = (uint32_t)H * dv * 2;
   rs.row_s = (uint32_t)H * 4;
   {
-    const int lm1 = len > 0 ? len - 1 : 0;
-    const uint32_t nk = len > 0 ? (uint32_t)lm1 * rs.row_qk + DK * 2 : 0;
-    const uint32_t nvb = len > 0 ? (uint32_t)lm1 * rs.row_v + DVB * 2 : 0;
-    const uint32_t ns = len > 0 ? (uint32_t)lm1 * rs.row_s + 4 : 0;
-    rs.k = __builtin_amdgcn_make_buffer_rsrc((void *)((const bf16 *)p.k + ((size_t)tok0 * H + h) * DK), 0, nk, 0x00020000);
-    rs.q = __builtin_amdgcn_make_buffer_rsrc((void *)((const bf16 *)p.q + ((size_t)tok0 * H + h) * DK), 0, nk, 0x00020000);
-    rs.v = __builtin_amdgcn_make_buffer_rsrc((void *)((const bf16 *)p.v + ((size_t)tok0 * H + h) * dv + col0), 0, nvb, 0x00020000);
+    const uint64_t lm1 = len > 0 ? (uint64_t)(len - 1) : 0;
+    rs.span_qk = len > 0 ? lm1 * rs.row_qk + DK * 2 : 0;
+    rs.span_v = len > 0 ? lm1 * rs.row_v + DVB * 2 : 0;
+    const uint64_t ns = len > 0 ? lm1 * rs.row_s + 4 : 0;
+    rs.k = (const char *)((const bf16 *)p.k + ((size_t)tok0 * H + h) * DK);
+    rs.q = (const char *)((const bf16 *)p.q + ((size_t)tok0 * H + h) * DK);
+    rs.v = (const char *)((const bf16 *)p.v + ((size_t)tok0 * H + h) * dv + col0);
     // (the additive write reads no beta: zero records, so its loads return 0)
-    rs.beta = ADD ? __builtin_amdgcn_make_buffer_rsrc((void *)p.q, 0, 0, 0x00020000)
-                  : __builtin_amdgcn_make_buffer_rsrc((void *)(p.beta + (size_t)tok0 * H + h), 0, ns, 0x00020000);
-    if (GATE == GATE_CONST)
-      rs.la = __builtin_amdgcn_make_buffer_rsrc((void *)(p.log_alpha + h), 0, len > 0 ? 4 : 0, 0x00020000);
-    else
-      rs.la = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(GATE == GATE_HEAD ? p.log_alpha + (size_t)tok0 * H + h : (ADD ? p.q : p.beta)), 0,
-          GATE == GATE_HEAD ? ns : 0, 0x00020000);
-    rs.kh = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(GATE == GATE_KEY ? (const bf16 *)p.k_hat + ((size_t)tok0 * H + h) * DK : (const bf16 *)p.k), 0,
-        GATE == GATE_KEY ? nk : 0, 0x00020000);
+    rs.beta = ADD ? (const char *)p.q : (const char *)(p.beta + (size_t)tok0 * H + h);
+    rs.span_beta = ADD ? 0 : ns;
+    if (GATE == GATE_CONST) {
+      rs.la = (const char *)(p.log_alpha + h);
+      rs.span_la = len > 0 ? 4 : 0;
+    } else {
+      rs.la = GATE == GATE_HEAD ? (const char *)(p.log_alpha + (size_t)tok0 * H + h)
+                                : (const char *)(ADD ? (const void *)p.q : (const void *)p.beta);
+      rs.span_la = GATE == GATE_HEAD ? ns : 0;
+    }
+    rs.kh = GATE == GATE_KEY ? (const char *)((const bf16 *)p.k_hat + ((size_t)tok0 * H + h) * DK)
+                             : (const char *)p.k;
+    rs.span_kh = GATE == GATE_KEY ? rs.span_qk : 0;
   }
 
   auto KQ = [&](int i) { return smem + OFF_KQ + i * KQ_BYTES; };
@@ -671,13 +687,24 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
     // its own data before it waits for the other's, so neither wait can block.
     // (relaxed workgroup-scope atomics: a volatile access would make the compiler
     // wait for every outstanding memory operation of the wave first)
+    // Why each wait ends: between two workgroup barriers both builders run phase 1 of
+    // the same chunk and then reach this hand-off; each stores its own flag (cc + 1)
+    // before it reads the other's, and neither waits for anything else in between, so
+    // the later of the two finds the other's flag already set and the earlier one sees
+    // it as soon as the later one has stored.  The spin cap (2^22 sleeps of 64 clocks,
+    // about 0.1 s, against a wait of at most one phase 1, a few microseconds) is only a
+    // guard against an edit that breaks this order: the kernel then finishes with wrong
+    // results instead of hanging the GPU.
     int *flags = (int *)(smem + OFF_FLAGS);
     auto handoff = [&](int cc) {
       if (ADD || (wave != W_TA && wave != W_TB)) return;
       const int mine = wave == W_TA ? 0 : 1;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own LDS writes done
       if (lane == 0) __hip_atomic_store(flags + mine, cc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      while (__hip_atomic_load(flags + (mine ^ 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < cc + 1)
+      for (int spin = 0;
+           spin < (1 << 22) &&
+           __hip_atomic_load(flags + (mine ^ 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < cc + 1;
+           ++spin)
         __builtin_amdgcn_s_sleep(1);
       asm volatile("" ::: "memory");
     };

@@ -63,9 +63,10 @@ struct DecodeParams {
   int la_stride;  // scalar gate: elements of log_alpha between tokens (H, or 0: per head)
 };
 
-// Backward pass of the chunked delta rule (no gate or the scalar gate).  The chunk
-// states come from the fused forward with FwdParams::chunk_states; the slots of the
-// chunks are numbered as for key_slots.
+// Backward pass of the chunked delta rule and of the additive write (no gate, the
+// scalar gate or a constant per-head decay).  The chunk states come from a forward
+// launched with FwdParams::chunk_states; the slots of the chunks are numbered as for
+// key_slots.
 struct BwdParams {
   const void *q, *k, *v, *dout;  // [tokens, H, d_k] / [tokens, H, d_v], I/O dtype
   const float *beta, *log_alpha; // [tokens, H] (beta NULL for the additive write; log_alpha
@@ -85,6 +86,8 @@ struct BwdParams {
 };
 size_t bwd_part_floats(int dk);
 hipError_t launch_bwd(const BwdParams &p, int dtype, int dk, int gate, bool add, hipStream_t stream);
+// x[0 .. n) = 0
+hipError_t launch_fill_zero(float *x, size_t n, hipStream_t stream);
 // out[h] = sum over tokens of x[t, h] (deterministic order)
 hipError_t launch_sum_tokens(const float *x, long tokens, int H, float *out, hipStream_t stream);
 

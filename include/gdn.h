@@ -98,8 +98,9 @@ typedef enum { GDN_WRITE_DELTA = 0, GDN_WRITE_ADD = 1 } gdn_write;
  * result is the recurrence's, as if padded with beta = 0 and log_alpha = 0.
  */
 typedef struct {
-  int B, T, H;        /* batch, tokens per batch row (packed total in varlen), heads */
-  int d_k, d_v;       /* head dims: each 64 or 128                                   */
+  int B, T, H;        /* batch, tokens per batch row (packed total in varlen), heads
+                         (H <= 262143: offsets inside one chunk fit 32 bits)         */
+  int d_k, d_v;       /* head dims: each 64 or 128, in either dtype                  */
   int chunk;          /* chunk length: must be 64                                    */
   int N;              /* number of sequences: B, or len(cu_seqlens) - 1              */
   gdn_dtype dtype;    /* dtype of q, k, v, o                                         */
@@ -199,7 +200,7 @@ int gdn_fwd_decode(const gdn_decode_args *args, void *hip_stream);
  * write and the additive write (GDN_WRITE_ADD: gated linear attention / RetNet), each
  * with no gate, one decay per (token, head) or one constant decay per head
  * (GDN_GATE_NONE, GDN_GATE_HEAD, GDN_GATE_HEAD_CONST); the per-key-channel gate returns
- * GDN_ERR_UNSUPPORTED.  Inputs as for gdn_fwd_chunked (the same validation rules, which
+ * GDN_ERR_UNSUPPORTED, and so does fp32 I/O with d_k = 128.  Inputs as for gdn_fwd_chunked (the same validation rules, which
  * this call repeats), plus the gradients of its outputs;
  * the forward is recomputed inside the call (chunk-entering states into the
  * workspace), so nothing of the forward call needs to be kept.  All arithmetic is

@@ -85,7 +85,7 @@ def test_package_has_no_cpu_path():
     (dict(chunk=32), UNSUPPORTED),
     (dict(d_k=96), UNSUPPORTED),
     (dict(d_v=256), UNSUPPORTED),
-    (dict(dtype=0), UNSUPPORTED),          # fp32 I/O needs d_k = 64
+    (dict(H=262144), UNSUPPORTED),         # offsets inside a chunk would pass 32 bits
     (dict(dtype=7), INVALID),
     (dict(gate=4), INVALID),
     (dict(write=2), INVALID),
@@ -312,6 +312,8 @@ def bwd_args(g, **kw):
     (dict(dq=fake(6, 2)), INVALID),
     (dict(chunk=32), UNSUPPORTED),
     (dict(d_k=96), UNSUPPORTED),
+    (dict(dtype=0), UNSUPPORTED),              # fp32 gradients take d_k = 64 only
+    (dict(dtype=0, d_k=64), WORKSPACE),        # ... which is valid
     (dict(), WORKSPACE),
 ])
 def test_bwd_host_validation(g, change, status):

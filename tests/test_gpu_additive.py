@@ -63,9 +63,19 @@ def test_additive_bf16(gdn, gate, T, dk):
     check(gdn, inputs(2, T, 3, dk, 128, gate, "bf16", seed=T + dk))
 
 
+@pytest.mark.parametrize("dk", [64, 128])
 @pytest.mark.parametrize("gate", ["none", "head", "key", "const"])
-def test_additive_fp32(gdn, gate):
-    check(gdn, inputs(2, 150, 2, 64, 64, gate, "f32", seed=7))
+def test_additive_fp32(gdn, gate, dk):
+    check(gdn, inputs(2, 150, 2, dk, 64, gate, "f32", seed=7))
+
+
+@pytest.mark.parametrize("write", ["delta", "add"])
+@pytest.mark.parametrize("gate", ["none", "head", "key", "const"])
+@pytest.mark.parametrize("dtype,dv,B", [("f32", 64, 16), ("f32", 128, 8), ("bf16", 64, 16)])
+def test_fused_64_column_blocks(gdn, dtype, dv, B, gate, write):
+    """d_k = 64 with N H d_v / 64 = 256 (sequence, head, 64 columns) blocks: the fused
+    kernel then gives each workgroup 64 value columns instead of 32."""
+    check(gdn, inputs(B, 150, 16, 64, dv, gate, dtype, seed=41 + dv), write=write)
 
 
 @pytest.mark.parametrize("gate", ["key", "const"])

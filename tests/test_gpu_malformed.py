@@ -71,10 +71,15 @@ def test_dplr_leaves_malformed_sequences_untouched(gdn):
     assert relerr(o[:, :100], o_ref) <= 2e-2 and relerr(fs[:1], fs_ref) <= 2e-2
 
 
-@pytest.mark.parametrize("write", ["delta", "add"])
-def test_backward_with_malformed_sequences(gdn, write):
-    """The valid sequence's gradients are exact; the malformed ones are skipped."""
+@pytest.mark.parametrize("write,gate", [("delta", "head"), ("add", "head"), ("delta", "const"),
+                                        ("add", "const")])
+def test_backward_with_malformed_sequences(gdn, write, gate):
+    """The valid sequence's gradients are exact; the malformed ones are skipped.  With
+    the constant per-head decay the [H] gradient sums the valid sequence's tokens only
+    (tokens 100 .. 299 belong to no valid sequence and contribute nothing)."""
     inp = malformed(synth.random_inputs(1, 300, 2, 128, 128, "head", "bf16", seed=43))
+    if gate == "const":
+        inp["log_alpha"] = synth.retnet_log_gamma(2)
     if write == "add":
         inp["beta"] = None
     g = torch.Generator().manual_seed(44)
@@ -83,11 +88,15 @@ def test_backward_with_malformed_sequences(gdn, write):
     got = gdn.bwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], None, dout.cuda(), None,
                           d["cu_seqlens"], write=write)
     torch.cuda.synchronize()
-    sl = lambda x: None if x is None else x[:, :100]
-    ref = oracle.bwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["log_alpha"]), None,
+    sl = lambda x: None if x is None or x.dim() == 1 else x[:, :100]
+    if gate == "const":
+        sl_la = inp["log_alpha"]
+    else:
+        sl_la = sl(inp["log_alpha"])
+    ref = oracle.bwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl_la, None,
                      sl(dout), None, write=write)
     for name, g_, r in zip(["dq", "dk", "dv", "dbeta", "dlog_alpha"], got[:5], ref[:5]):
         if r is None:
             continue
-        assert relerr(g_[:, :100], r) <= 2e-2, name
+        assert relerr(g_ if g_.dim() == 1 else g_[:, :100], r) <= 2e-2, name
     assert relerr(got[5][:1], ref[5]) <= 2e-2

@@ -73,10 +73,19 @@ def test_bf16_head_dims(gdn, dk, dv, with_state, gate):
     check(gdn, inp)
 
 
+@pytest.mark.parametrize("dk", [64, 128])
 @pytest.mark.parametrize("dv", [64, 128])
 @pytest.mark.parametrize("gate", ["none", "head", "key"])
-def test_fp32_mode(gdn, dv, gate):
-    inp = synth.random_inputs(2, 190, 2, 64, dv, gate, "f32", seed=dv, state_std=0.1)
+def test_fp32_mode(gdn, dk, dv, gate):
+    inp = synth.random_inputs(2, 190, 2, dk, dv, gate, "f32", seed=dv + dk, state_std=0.1)
+    check(gdn, inp)
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_fp32_dk128_varlen(gdn, gate):
+    """fp32 I/O with d_k = 128 on packed sequences with partial chunks and an empty one."""
+    inp = synth.random_inputs(1, None, 3, 128, 128, gate, "f32", seed=19, state_std=0.1,
+                              lengths=[1, 64, 130, 0, 77])
     check(gdn, inp)
 
 
@@ -126,7 +135,7 @@ def test_key_prepared_call_repeats(gdn):
 
 
 @pytest.mark.parametrize("gate", ["head", "key"])
-@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
 def test_strong_decay(gdn, gate, dtype, dk):
     """Log decay of -5 per token (-320 per chunk): the per-position factors of every
     decay product must stay finite and the result match the recurrence."""
@@ -215,23 +224,56 @@ def test_workload_kda_long(gdn):
     check(gdn, synth.workload_inputs("kda-bf16-B2-T16384-H16-d128"))
 
 
-def test_workload_varlen_sampled(gdn):
-    """Full packed workload on the GPU; the oracle recomputes sampled sequences
-    (shortest, longest, one more) on two heads."""
-    name = "gdn-varlen-bf16-N32-H16-d128"
-    inp = synth.workload_inputs(name)
+@pytest.fixture(scope="module")
+def varlen_run(gdn):
+    """The packed workload (32 sequences, 283,220 tokens, 16 heads) on the GPU and in
+    the oracle, computed once for the tests below."""
+    inp = synth.workload_inputs("gdn-varlen-bf16-N32-H16-d128")
     o, fs = run_gpu(gdn, inp)
-    lengths = inp["lengths"]
+    o_ref, fs_ref = run_oracle(inp)
+    return inp, o, fs, o_ref, fs_ref
+
+
+def test_workload_varlen_full(varlen_run):
+    """Every sequence and every head of the packed workload against the oracle: the
+    whole tensors, and each sequence's rows and final state on their own (so that a
+    short sequence cannot hide behind a long one's larger values)."""
+    inp, o, fs, o_ref, fs_ref = varlen_run
+    assert np.isfinite(o.float().numpy()).all() and np.isfinite(fs.numpy()).all()
+    assert relerr(o, o_ref) <= 2e-2 and relerr(fs, fs_ref) <= 2e-2
     cu = inp["cu_seqlens"].tolist()
-    picks = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), 5})
-    heads = [0, 15]
-    for n in picks:
+    for n in range(len(cu) - 1):
         sl = slice(cu[n], cu[n + 1])
-        o_ref, f_ref = oracle.fwd(inp["q"][:, sl][:, :, heads], inp["k"][:, sl][:, :, heads],
-                                  inp["v"][:, sl][:, :, heads], inp["beta"][:, sl][:, :, heads],
-                                  inp["log_alpha"][:, sl][:, :, heads], None)
-        assert relerr(o[:, sl][:, :, heads], o_ref) <= 2e-2, n
-        assert relerr(fs[n, heads], f_ref[0]) <= 2e-2, n
+        assert relerr(o[:, sl], o_ref[:, sl]) <= 2e-2, n
+        assert relerr(fs[n], fs_ref[n]) <= 2e-2, n
+
+
+def test_workload_varlen_decode(gdn, varlen_run):
+    """The packed workload's decode leg: 64 single-token recurrent steps at batch 256 x
+    16 heads, from the 32 final states tiled 8 times (stream s starts from sequence
+    s mod 32), fresh seeded tokens per step.  The oracle steps from the same GPU
+    states, so each step's o is held to the bf16 bound and the fp32 pool to 1e-5;
+    the whole chain (prefill then decode) is also held end to end against the oracle
+    run from its own final states."""
+    inp, _, fs, _, fs_ref = varlen_run
+    spec = synth.WORKLOADS["gdn-varlen-bf16-N32-H16-d128"]
+    batch, steps = spec["decode_batch"], spec["decode_steps"]
+    dec = synth.decode_inputs(batch, spec["H"], spec["dk"], spec["dv"], steps, spec["gate"], spec["dtype"],
+                              seed=spec["seed"] + 1)
+    st = synth.decode_initial_states(fs, batch).cuda()
+    ref = synth.decode_initial_states(fs, batch).double().numpy()
+    chain = fs_ref[np.arange(batch) % fs_ref.shape[0]]
+    for s in range(steps):
+        o = gdn.recurrent_step(dec["q"][s].cuda(), dec["k"][s].cuda(), dec["v"][s].cuda(),
+                               dec["beta"][s].cuda(), dec["log_alpha"][s].cuda(), st)
+        torch.cuda.synchronize()
+        o_ref, ref = oracle.step(dec["q"][s], dec["k"][s], dec["v"][s], dec["beta"][s], dec["log_alpha"][s], ref)
+        o_chain, chain = oracle.step(dec["q"][s], dec["k"][s], dec["v"][s], dec["beta"][s], dec["log_alpha"][s],
+                                     chain)
+        assert relerr(o.cpu(), o_ref) <= 2e-2, s
+        assert relerr(o.cpu(), o_chain) <= 2e-2, s
+    assert relerr(st.cpu(), ref) <= 1e-5
+    assert relerr(st.cpu(), chain) <= 2e-2
 
 
 # ---------------------------------------------------------------- decode step
@@ -278,3 +320,22 @@ def test_prepared_call_matches_direct_call(gdn):
         o, fs = call.launch()
         torch.cuda.synchronize()
         assert torch.equal(o.cpu(), o_ref) and torch.equal(fs.cpu(), f_ref)
+
+
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_side_stream(gdn, gate):
+    """A call queued on a stream other than torch's current one: the workspace the
+    binding allocates (the per-key-channel gate's prepared operands) stays reserved for
+    that stream's work, and the results equal those of a call on the current stream."""
+    inp = synth.random_inputs(2, 200, 2, 128, 128, gate, "bf16", seed=29, state_std=0.05)
+    o_ref, f_ref = run_gpu(gdn, inp)
+    d = to_dev(inp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o, fs = gdn.fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"], None,
+                            stream=side)
+    junk = [torch.full((1 << 20,), 3.0, device="cuda") for _ in range(8)]  # reuses freed blocks, if any
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(o.cpu(), o_ref) and torch.equal(fs.cpu(), f_ref)
