@@ -7,7 +7,9 @@ current stream.  There is no fallback: if the library is missing this module
 raises on import.
 
 The names follow the C ABI: ``fwd_chunked`` wraps ``gdn_fwd_chunked``,
-``recurrent_step`` wraps ``gdn_fwd_recurrent_step``, ``decode`` wraps
+``fwd_chunked_static`` wraps ``gdn_fwd_chunked_static`` (the same forward with the
+library's own per-GPU scratch array instead of a workspace), ``recurrent_step`` wraps
+``gdn_fwd_recurrent_step``, ``decode`` wraps
 ``gdn_fwd_decode``, ``bwd_chunked`` wraps ``gdn_bwd_chunked``, ``fwd_dplr`` wraps
 ``gdn_fwd_dplr``, ``dplr_step`` wraps ``gdn_fwd_dplr_step`` and ``dplr_decode`` wraps
 ``gdn_fwd_dplr_decode``.
@@ -118,6 +120,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs)]
     lib.gdn_fwd_chunked.restype = ctypes.c_int
     lib.gdn_fwd_chunked.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+    lib.gdn_fwd_chunked_static.restype = ctypes.c_int
+    lib.gdn_fwd_chunked_static.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
     lib.gdn_fwd_recurrent_step.restype = ctypes.c_int
     lib.gdn_fwd_recurrent_step.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_void_p]
     lib.gdn_fwd_decode.restype = ctypes.c_int
@@ -373,6 +377,23 @@ def fwd_chunked(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=No
     _check(_lib.gdn_fwd_chunked(ctypes.byref(args), _stream(stream)), "gdn_fwd_chunked")
     _keep_for_stream(own, stream)
     return out, (final_state if output_final_state else None)
+
+
+STATIC_SCRATCH_BYTES = 128 << 20  # GDN_STATIC_SCRATCH_BYTES of include/gdn.h
+
+
+def fwd_chunked_static(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None,
+                       out=None, final_state=None, stream=None, write: str = "delta"):
+    """Chunked forward without a workspace (gdn_fwd_chunked_static): the library uses
+    its own scratch array on this GPU (at most STATIC_SCRATCH_BYTES; larger needs
+    raise) and allocates nothing.  The caller passes every output: ``out``
+    [B,T,H,d_v] and ``final_state`` None | [N,H,d_k,d_v] fp32.  Calls that may overlap
+    on one GPU race on the shared scratch.  Other arguments as for fwd_chunked."""
+    _require(out is not None, "out must be given (this entry point allocates nothing)")
+    check_fwd_tensors(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out, final_state, write)
+    args = make_fwd_args(q, k, v, beta, log_alpha, initial_state, cu_seqlens, out, final_state, CHUNK, write)
+    _check(_lib.gdn_fwd_chunked_static(ctypes.byref(args), _stream(stream)), "gdn_fwd_chunked_static")
+    return out, final_state
 
 
 class PreparedFwd:

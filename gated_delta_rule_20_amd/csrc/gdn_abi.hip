@@ -6,8 +6,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gdn.h"
 #include "gdn_kernels.h"
+
+// Scratch memory of gdn_fwd_chunked_static: one array per GPU, alive until the process
+// ends.  Its name is a host-side stand-in, never a device address: host code uses only
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[GDN_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -339,15 +346,67 @@ size_t gdn_fwd_workspace_size(const gdn_fwd_args *a) {
   return order_bytes(a) + key_layout(a).total();
 }
 
+}  // extern "C"
+
+namespace {
+
+// The forward on a checked argument set, with its scratch memory at `ws` (need bytes,
+// 256-aligned; may be NULL when need is 0).
+int fwd_chunked_launch(const gdn_fwd_args *a, void *ws_base, void *hip_stream);
+
+// Device address of this process's scratch array on the current device, looked up once
+// per device (NULL if the lookup fails).
+void *static_scratch() {
+  static std::mutex mu;
+  static void *ptr[256];
+  static bool done[256];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!done[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = p;
+    done[dev] = true;
+  }
+  return ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_fwd_chunked_static(const gdn_fwd_args *a, void *hip_stream) {
+  const int st = check_fwd(a);
+  if (st != GDN_OK) return st;
+  const size_t need = order_bytes(a) + key_layout(a).total();
+  if (need > GDN_STATIC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
+  if (a->N == 0) return GDN_OK;
+  void *ws = nullptr;
+  if (need) {
+    ws = static_scratch();
+    if (!ws) return GDN_ERR_HIP;
+  }
+  return fwd_chunked_launch(a, ws, hip_stream);
+}
+
 int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
   const int st = check_fwd(a);
   if (st != GDN_OK) return st;
-  const size_t obytes = order_bytes(a);
-  const KeyLayout L = key_layout(a);
-  const size_t need = obytes + L.total();
+  const size_t need = order_bytes(a) + key_layout(a).total();
   if (need && (!a->workspace || a->workspace_bytes < need || !aligned(a->workspace, 256)))
     return GDN_ERR_WORKSPACE;
   if (a->N == 0) return GDN_OK;
+  return fwd_chunked_launch(a, a->workspace, hip_stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int fwd_chunked_launch(const gdn_fwd_args *a, void *ws_base, void *hip_stream) {
+  const size_t obytes = order_bytes(a);
+  const KeyLayout L = key_layout(a);
   hipStream_t stream = (hipStream_t)hip_stream;
   gdn::FwdParams p;
   p.q = a->q;
@@ -359,7 +418,7 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
   p.final_state = a->final_state;
   p.o = a->o;
   p.cu_seqlens = a->cu_seqlens;
-  p.order = obytes ? (const int32_t *)a->workspace : nullptr;
+  p.order = obytes ? (const int32_t *)ws_base : nullptr;
   p.k_hat = nullptr;
   p.tp_img = nullptr;
   p.egc = nullptr;
@@ -370,11 +429,11 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
   p.la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
   p.chunk_states = nullptr;
   if (obytes) {
-    if (gdn::launch_seq_order(a->cu_seqlens, a->N, (int32_t *)a->workspace, stream) != hipSuccess)
+    if (gdn::launch_seq_order(a->cu_seqlens, a->N, (int32_t *)ws_base, stream) != hipSuccess)
       return GDN_ERR_HIP;
   }
   if (L.slots) {
-    char *ws = (char *)a->workspace + obytes;
+    char *ws = (char *)ws_base + obytes;
     gdn::KeyPrepParams kp;
     kp.q = a->q;
     kp.k = a->k;
@@ -409,6 +468,10 @@ int gdn_fwd_chunked(const gdn_fwd_args *a, void *hip_stream) {
     return GDN_ERR_HIP;
   return GDN_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int gdn_fwd_recurrent_step(const gdn_step_args *a, void *hip_stream) {
   const int st = check_step(a);

@@ -186,6 +186,20 @@ size_t gdn_fwd_workspace_size(const gdn_fwd_args *args);
 /* Chunked forward: writes o (and final_state when non-NULL). */
 int gdn_fwd_chunked(const gdn_fwd_args *args, void *hip_stream);
 
+/* The same forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): it takes no workspace
+ * (args->workspace and args->workspace_bytes are ignored) and allocates nothing.  Its
+ * scratch memory is one array of GDN_STATIC_SCRATCH_BYTES per GPU, part of the
+ * library's device code and held until the process ends.  Calls whose
+ * gdn_fwd_workspace_size() exceeds that return GDN_ERR_WORKSPACE and launch nothing
+ * (a call that needs no scratch, e.g. batch mode with a scalar gate, always fits).
+ * All calls on one GPU share that GPU's array: two such calls that can overlap on one
+ * GPU (different streams without ordering between them) race and give undefined
+ * results; calls ordered on one stream are safe.  The scratch needs no initialisation.
+ * Otherwise identical to gdn_fwd_chunked (same arguments, validation and results). */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+int gdn_fwd_chunked_static(const gdn_fwd_args *args, void *hip_stream);
+
 /* One decode token per stream: writes o and updates state in place. */
 int gdn_fwd_recurrent_step(const gdn_step_args *args, void *hip_stream);
 

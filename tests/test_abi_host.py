@@ -50,7 +50,7 @@ def fwd(g, a):
 
 def test_header_declares_the_boundary(g):
     assert g.header_functions() == ["gdn_bwd_chunked", "gdn_bwd_workspace_size", "gdn_fwd_chunked",
-                                    "gdn_fwd_decode", "gdn_fwd_dplr", "gdn_fwd_dplr_decode", "gdn_fwd_dplr_step",
+                                    "gdn_fwd_chunked_static", "gdn_fwd_decode", "gdn_fwd_dplr", "gdn_fwd_dplr_decode", "gdn_fwd_dplr_step",
                                     "gdn_fwd_recurrent_step",
                                     "gdn_fwd_workspace_size", "gdn_status_str", "gdn_version"]
 
@@ -115,6 +115,7 @@ def test_fwd_host_validation(g, change, status):
 
 def test_fwd_null_args(g):
     assert fwd(g, None) == INVALID
+    assert g._lib.gdn_fwd_chunked_static(None, None) == INVALID
     assert g._lib.gdn_fwd_workspace_size(None) == 0
 
 
@@ -428,3 +429,16 @@ def dplr_decode_args(g, **kw):
 def test_dplr_decode_host_validation(g, change, status):
     assert g._lib.gdn_fwd_dplr_decode(ctypes.byref(dplr_decode_args(g, **change)), None) == status
     assert g._lib.gdn_fwd_dplr_decode(None, None) == INVALID
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(q=None), INVALID),
+    (dict(gate=2, log_alpha=fake(4, 0), B=1, T=65536, N=1), WORKSPACE),  # ~270 MB of scratch
+    (dict(B=0, N=0), OK),
+])
+def test_static_entry_host_validation(g, change, status):
+    """gdn_fwd_chunked_static validates like gdn_fwd_chunked and refuses scratch needs
+    above its fixed array, launching nothing."""
+    a = base_args(g, **change)
+    assert g._lib.gdn_fwd_chunked_static(ctypes.byref(a), None) == status
