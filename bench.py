@@ -6,19 +6,27 @@ random fp32 initial state): every step of the chunked method runs in that call.
 Inputs are synthetic (seeded), resident in HBM before timing, and rotated over
 four copies so that no step finds its inputs in the 256 MB last-level cache.
 
-Warm-up: from idle, the GPU's power controller needs about 25-30 ms of continuous
-load to settle (launch durations first dip well below and then recover to the
-sustained rate, with socket power at its 1400 W limit). The default warm-up of 600
-headline launches (about 50 ms) covers that transient, so the timed steps measure
-the sustained rate a continuously running layer sees.
+Settle and warm-up: from idle, the GPU's power controller needs about 25-30 ms of
+continuous load to settle (launch durations first dip below and then rise above the
+sustained rate, with socket power at its 1400 W limit).  Before the W warm-up steps,
+the benchmark therefore runs untimed headline launches for --settle-ms (default 50 ms)
+of wall time, so that the timed steps measure the sustained rate a continuously
+running layer sees whatever W is; the line reports the settle phase ("settle").
 
-Prints ONE JSON line.  `roofline` relates the fused kernel's algorithmic bytes
-(q, k, v read and o written in bf16, beta and log alpha in fp32, initial and final
-fp32 state) to its average launch duration, measured with HIP events on the stream
-the kernel runs on.  `cpu_baseline` times the fp64 oracle on the host cores.
+Prints ONE JSON line.  `value`, `ms_per_step`, `tflops` and `mfma_peak_frac` all use
+the whole-job wall time of the K timed steps.  `roofline` relates the kernel's
+algorithmic bytes (q, k, v read and o written in bf16, beta and log alpha in fp32,
+initial and final fp32 state) to its average launch duration measured with HIP events
+on the stream the kernel runs on (`launch_ms`); `frac_at_ms_per_step` is the same
+fraction on the wall-clock step time.  `cpu_baseline` times the fp64 oracle on the
+host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
-                       [--calibrate-copy MIB]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--all]
+                       [--no-cpu] [--calibrate-copy MIB] [--only WORKLOAD[:bwd]]
+
+--only runs just one named workload's forward (or, with ":bwd", its backward) for the
+given steps and prints its measurement line instead of the headline: the form the
+per-kernel counter profiles use.
 """
 from __future__ import annotations
 
@@ -107,10 +115,12 @@ def make_device_inputs(inp, copies):
     return sets
 
 
-def time_chunked(gdn, sets, steps, warmup):
+def time_chunked(gdn, sets, steps, warmup, settle_ms=0.0):
     """Whole-job time of `steps` calls (barrier + synchronize on both sides) after
     `warmup` untimed calls (None: as many as fill SETTLE_MS), and the average
-    per-launch duration from HIP events on the launch stream."""
+    per-launch duration from HIP events on the launch stream.  With settle_ms > 0,
+    untimed calls run first until that much wall time has passed (reported as the
+    third value: the number of settle launches)."""
     import torch
     # one validated call per input copy: each timed step is a single library call
     stream = torch.cuda.current_stream()
@@ -122,6 +132,15 @@ def time_chunked(gdn, sets, steps, warmup):
     def call(i):
         calls[i % len(calls)].launch(stream)
 
+    settled = 0
+    if settle_ms > 0:
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + settle_ms / 1e3
+        while time.perf_counter() < t_end:
+            for _ in range(16):
+                call(settled)
+                settled += 1
+            torch.cuda.synchronize()
     if warmup is None:
         # enough launches for SETTLE_MS of continuous load, from one timed call
         call(0)
@@ -144,7 +163,7 @@ def time_chunked(gdn, sets, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, e0.elapsed_time(e1) / steps
+    return wall, e0.elapsed_time(e1) / steps, settled
 
 
 def time_decode(gdn, spec, final_states, steps=64, cpu=False):
@@ -433,14 +452,14 @@ def cpu_baseline_sample(inp, kind="fwd", max_tokens=32768):
             "sample": "%s (%d tokens x %d heads), one run (%.2f s)" % (text, tokens, H, dt)}
 
 
-def bench_workload(gdn, name, steps, warmup):
+def bench_workload(gdn, name, steps, warmup, settle_ms=0.0):
     import synth
     spec = synth.WORKLOADS[name]
     inp = synth.workload_inputs(name)
     B, T, H, dk = inp["q"].shape
     dv = inp["v"].shape[-1]
     sets = make_device_inputs(inp, ROTATE)
-    wall, launch_ms = time_chunked(gdn, sets, steps, warmup)
+    wall, launch_ms, settled = time_chunked(gdn, sets, steps, warmup, settle_ms)
     tokens = B * T
     esize = 2 if spec["dtype"] == "bf16" else 4
     flops, nbytes = alg_counts(tokens, H, dk, dv, inp["N"], spec["gate"], esize,
@@ -451,8 +470,21 @@ def bench_workload(gdn, name, steps, warmup):
            "mfma_frac": flops / (launch_ms / 1e3) / 1e12 / PEAK_MFMA["f32" if spec.get("write") == "dplr"
                                                                      else spec["dtype"]],
            "hbm_gbs": nbytes / (launch_ms / 1e3) / 1e9,
-           "hbm_frac": nbytes / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+           "hbm_frac": nbytes / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBS, "settle_launches": settled}
     return res, inp, sets
+
+
+def calibrate_copy(mib):
+    """Two launches of a plain elementwise kernel reading `mib` MiB once and writing them
+    once: the known-size reference for the HBM byte counters of a profile run."""
+    if not mib:
+        return
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -460,9 +492,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=600,
-                    help="untimed launches first; the default covers the power controller's settling")
+                    help="untimed launches before the timed ones (after the settle phase)")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed launches for this much wall time first, so that the power "
+                         "controller has settled before the warm-up and timed steps (0: none)")
     ap.add_argument("--all", action="store_true", help="also report every workload (extra lines on stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only", default=None, metavar="WORKLOAD[:bwd]",
+                    help="run only this workload (forward, or backward with ':bwd') and print its line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run twice a plain elementwise kernel that reads MIB MiB once "
                          "and writes them once: the known-size reference for HBM byte counters")
@@ -477,10 +514,23 @@ def main():
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    res, inp, sets = bench_workload(gdn, HEADLINE, args.steps, args.warmup)
+    if args.only:
+        name, _, part = args.only.partition(":")
+        if name not in synth.WORKLOADS:
+            sys.exit("unknown workload %r; known: %s" % (name, ", ".join(sorted(synth.WORKLOADS))))
+        if part == "bwd":
+            r = time_bwd(gdn, name, steps=args.steps)
+        else:
+            r, _, _ = bench_workload(gdn, name, args.steps, args.warmup, args.settle_ms)
+        calibrate_copy(args.calibrate_copy)
+        print(json.dumps(r))
+        return
+
+    res, inp, sets = bench_workload(gdn, HEADLINE, args.steps, args.warmup, args.settle_ms)
     spec = synth.WORKLOADS[HEADLINE]
     B, T, H, dk = inp["q"].shape
     achieved = res["alg_bytes"] / (res["launch_ms"] / 1e3) / 1e9
+    step_s = res["ms_per_step"] / 1e3
     traffic = read_traffic()
     line = {
         "metric": METRIC,
@@ -499,19 +549,17 @@ def main():
         "config": {"workload": HEADLINE, "B": B, "T": T, "H": H, "d_k": dk, "d_v": inp["v"].shape[-1],
                    "chunk": CHUNK, "gate": spec["gate"], "initial_state": True,
                    "rotated_input_copies": ROTATE},
-        "tflops": res["tflops"],
-        "mfma_peak_frac": res["mfma_frac"],
+        "settle": {"wall_ms": args.settle_ms, "launches": res["settle_launches"],
+                   "note": "untimed headline launches before the warm-up, so that the GPU's power "
+                           "controller has settled"},
+        "tflops": res["alg_flops"] / step_s / 1e12,
+        "mfma_peak_frac": res["alg_flops"] / step_s / 1e12 / PEAK_MFMA["bf16"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic},
+                     "frac": achieved / PEAK_HBM_GBS, "launch_ms": res["launch_ms"],
+                     "frac_at_ms_per_step": res["alg_bytes"] / step_s / 1e9 / PEAK_HBM_GBS,
+                     "alg_bytes": res["alg_bytes"], "traffic": traffic},
     }
-    if args.calibrate_copy:
-        src = torch.ones(args.calibrate_copy << 18, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    calibrate_copy(args.calibrate_copy)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(inp, H)
     if args.all:
