@@ -148,7 +148,8 @@ def fwd(q, k, v, beta, log_alpha=None, initial_state=None, cu_seqlens=None, gate
 def bwd(q, k, v, beta, log_alpha, initial_state, dout, dfinal=None, cu_seqlens=None, gate=None,
         nthreads: int = 0, lib=None, write: str = "delta"):
     """Gradients of the recurrence (the delta write, or the additive write with beta
-    None; no gate, one decay per (token, head), or one constant decay per head [H]) with
+    None; no gate, one decay per (token, head), one per (token, head, key channel), or one
+    constant decay per head [H]) with
     respect to q, k, v, beta, log_alpha and the initial state, given dout [B,T,H,d_v]
     (the gradient of o) and dfinal None | [N,H,d_k,d_v] (the gradient of the final
     state).  Shapes as for ``fwd``.  Returns (dq, dk, dv, dbeta or None, dlog_alpha or
@@ -173,7 +174,7 @@ def bwd(q, k, v, beta, log_alpha, initial_state, dout, dfinal=None, cu_seqlens=N
     dq, dk_ = np.zeros_like(q), np.zeros_like(k)
     dv_ = np.zeros_like(v)
     db = None if write == "add" else np.zeros_like(beta)
-    dla = np.zeros((B, T, H)) if gate == "head" else None
+    dla = np.zeros((B, T, H)) if gate == "head" else np.zeros((B, T, H, dk)) if gate == "key" else None
     dinit = np.zeros((N, H, dk, dv))
     lib = lib or load()
     rc = lib.oracle_bwd(N, start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),

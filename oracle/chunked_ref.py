@@ -211,13 +211,79 @@ def _chunk_step_bwd_add(q, k, v, G, Gam, R, M0, dO, dM):
     return dq, dk, dv, None, dg, dM0
 
 
+def chunk_step_bwd_key(q, k, v, beta, la, M0, dO, dM, write="delta"):
+    """Gradients of one chunk with one decay per key channel (la [C,dk], log decays),
+    for the delta write or the additive write (beta None).  The chunk equations are
+    those of the module docstring with per-channel Gamma[r,i,c] = e^{G[r,c] - G[i,c]}
+    inside the A and P contractions, Kt = K e^G, Qt = Q e^G, Khat = K e^{G_C - G} and
+    gam = e^{G_C} per channel.  Reverse mode, step by step:
+      dDelta, Y, dM0 (= Qt^T dO + diag(gam) dM - Kt^T diag(beta) Y), dV, dbeta, dKt, dT,
+      dA = -(T^T dT T^T) strictly lower, dP = dO Delta^T inclusive lower, dQt = dO M0^T,
+      dKhat = Delta dM^T, dgam_c = sum_j M0[c,j] dM[c,j]   (as for the scalar gate);
+    then with Z[r,c] = sum_i dA[r,i] K[i,c] Gamma[r,i,c] (the A rows),
+      Zc[i,c] = sum_r beta_r dA[r,i] K[r,c] Gamma[r,i,c] (the A columns),
+      Pr[r,c] = sum_i dP[r,i] K[i,c] Gamma[r,i,c] and Pc[i,c] = sum_r dP[r,i] Q[r,c] Gamma[r,i,c]:
+      dq = Pr + e^G dQt,   dk = beta Z + Zc + Pc + e^G dKt + e^{G_C - G} dKhat,
+      dbeta += sum_c K Z,
+      dG = beta K Z - K Zc + Q Pr - K Pc + Kt dKt + Qt dQt - Khat dKhat  (elementwise),
+      dG_C = sum_r Khat dKhat + gam dgam,
+    and d log alpha[t, c] = sum_{r >= t} dG[r, c] + dG_C[c].  Returns (dq, dk, dv, dbeta or
+    None, dlog_alpha [C,dk], dM0)."""
+    C, dk_ = q.shape
+    strict = np.tril(np.ones((C, C), dtype=bool), -1)
+    incl = np.tril(np.ones((C, C), dtype=bool), 0)
+    G = np.cumsum(la, axis=0)
+    gC = G[-1]
+    diff = G[:, None, :] - G[None, :, :]
+    Gam = np.exp(np.where(incl[:, :, None], diff, 0.0)) * incl[:, :, None]
+    eG, eT, gam = np.exp(G), np.exp(gC[None, :] - G), np.exp(gC)
+    Kt, Qt, Kh = eG * k, eG * q, eT * k
+    P = np.einsum("rc,ic,ric->ri", q, k, Gam)
+    dbeta = None
+    if write == "add":
+        Delta = v
+        dv = P.T @ dO + Kh @ dM
+        dM0 = Qt.T @ dO + gam[:, None] * dM
+        dKt = np.zeros_like(k)
+        Z = Zc = np.zeros_like(k)
+    else:
+        SG = np.einsum("rc,ic,ric->ri", k, k, Gam) * strict
+        T = forward_substitution_inverse(beta[:, None] * SG)
+        VmK = v - Kt @ M0
+        X = beta[:, None] * VmK
+        Delta = T @ X
+        dDelta = P.T @ dO + Kh @ dM
+        Y = T.T @ dDelta
+        dM0 = Qt.T @ dO + gam[:, None] * dM - Kt.T @ (beta[:, None] * Y)
+        dv = beta[:, None] * Y
+        dKt = -(beta[:, None] * Y) @ M0.T
+        dA = np.where(strict, -(T.T @ (dDelta @ X.T) @ T.T), 0.0)
+        Z = np.einsum("ri,ic,ric->rc", dA, k, Gam)
+        Zc = np.einsum("ri,rc,ric->ic", beta[:, None] * dA, k, Gam)
+        dbeta = np.sum(Y * VmK, axis=1) + np.sum(k * Z, axis=1)
+    dP = np.where(incl, dO @ Delta.T, 0.0)
+    dQt, dKh = dO @ M0.T, Delta @ dM.T
+    dgam = np.sum(M0 * dM, axis=1)
+    Pr = np.einsum("ri,ic,ric->rc", dP, k, Gam)
+    Pc = np.einsum("ri,rc,ric->ic", dP, q, Gam)
+    bz = 0.0 if beta is None or write == "add" else beta[:, None] * Z
+    dq = Pr + eG * dQt
+    dk = bz + Zc + Pc + eG * dKt + eT * dKh
+    dG = bz * k - k * Zc + q * Pr - k * Pc + Kt * dKt + Qt * dQt - Kh * dKh
+    dG[-1] += np.sum(Kh * dKh, axis=0) + gam * dgam
+    dla = np.cumsum(dG[::-1], axis=0)[::-1]
+    return dq, dk, dv, dbeta, dla, dM0
+
+
 def chunked_bwd(q, k, v, beta, log_alpha, M0, dO, dMT, C=64, write="delta"):
     """Gradients over one sequence by chunks: q,k [T,dk], v [T,dv], beta [T] (None with
-    write="add"), log_alpha None | [T], M0 [dk,dv], dO [T,dv], dMT None | [dk,dv].  The
-    chunk states are recomputed forward, then the chunks are walked in reverse.  A
-    partial last chunk is padded with zero rows (beta = 0, log alpha = 0)."""
+    write="add"), log_alpha None | [T] | [T,dk] (one decay per key channel), M0 [dk,dv],
+    dO [T,dv], dMT None | [dk,dv].  The chunk states are recomputed forward, then the
+    chunks are walked in reverse.  A partial last chunk is padded with zero rows (beta =
+    0, log alpha = 0)."""
     Tn, dk_ = q.shape
     dv_ = v.shape[1]
+    key = log_alpha is not None and np.ndim(log_alpha) == 2
     la = np.zeros(Tn) if log_alpha is None else log_alpha
     if beta is None:
         beta = np.zeros(Tn)
@@ -228,18 +294,19 @@ def chunked_bwd(q, k, v, beta, log_alpha, M0, dO, dMT, C=64, write="delta"):
     states = [M0]
     for c in range(nch):
         sl = slice(c * C, (c + 1) * C)
-        G = np.cumsum(lp[sl])
-        if write == "add":  # M_C = e^{G_C} M0 + (e^{G_C - G} K)^T V
-            states.append(np.exp(G[-1]) * states[-1] + (np.exp(G[-1] - G)[:, None] * kp[sl]).T @ vp[sl])
+        G = np.cumsum(lp[sl], axis=0)
+        Gk = G if key else np.repeat(G[:, None], dk_, axis=1)
+        if write == "add":  # M_C = diag(e^{G_C}) M0 + (e^{G_C - G} K)^T V
+            states.append(np.exp(Gk[-1])[:, None] * states[-1] + (np.exp(Gk[-1][None, :] - Gk) * kp[sl]).T @ vp[sl])
         else:
-            res = chunk_step(qp[sl], kp[sl], vp[sl], bp[sl], np.repeat(G[:, None], dk_, axis=1), states[-1])
+            res = chunk_step(qp[sl], kp[sl], vp[sl], bp[sl], Gk, states[-1])
             states.append(res["M"])
     dM = np.zeros((dk_, dv_)) if dMT is None else dMT
     out = [np.zeros_like(x) for x in (qp, kp, vp, bp, lp)]
     for c in reversed(range(nch)):
         sl = slice(c * C, (c + 1) * C)
-        dq, dk, dv, db, dg, dM = chunk_step_bwd(qp[sl], kp[sl], vp[sl], bp[sl], lp[sl], states[c], dOp[sl], dM,
-                                                write=write)
+        step = chunk_step_bwd_key if key else chunk_step_bwd
+        dq, dk, dv, db, dg, dM = step(qp[sl], kp[sl], vp[sl], bp[sl], lp[sl], states[c], dOp[sl], dM, write=write)
         for o_, x in zip(out, (dq, dk, dv, db, dg)):
             if x is not None:
                 o_[sl] = x

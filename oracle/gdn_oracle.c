@@ -154,8 +154,9 @@ int oracle_step(int N, int H, int dk, int dv, int gate, int write, const double 
 
 /*
  * Gradients of the token recurrence above (reverse mode, fp64), for the delta write and
- * the additive write with no gate or one decay per (token, head).  For one token of the
- * delta write, with M' = a M_{t-1},
+ * the additive write with no gate, one decay per (token, head) or one decay per (token,
+ * head, key channel).  For one token of the delta write, with M' = a M_{t-1} (row i
+ * scaled by a_i for the per-channel gate),
  * r = M'^T k, e = v - r, M_t = M' + beta k e^T, o = M_t^T q, and the gradient G of
  * the loss with respect to M_t (everything that later tokens and the final state
  * pass back) plus do:
@@ -166,12 +167,15 @@ int oracle_step(int N, int H, int dk, int dv, int gate, int write, const double 
  *   G'    = G - k de^T                (gradient with respect to M')
  *   dlog_alpha = sum(G' .* M')        (M' = a M_{t-1}, d a / d log a = a)
  *   G_{t-1} = a G'
+ * With one decay per key channel the last two lines hold row by row: dlog_alpha_i =
+ * sum_j G'[i][j] M'[i][j] and row i of G_{t-1} is a_i times row i of G'.
  * The additive write M_t = M' + k v^T passes G to M' unchanged, with dk = G v and
  * dv = G^T k (no beta: dbeta may be NULL).
  * Each sequence's states M_t are recomputed forward and kept, then swept in reverse.
  * dfinal (NULL: zeros) is the gradient with respect to the final state; the result
  * dinit is the gradient with respect to the initial state.  Arrays as for
- * oracle_fwd; dlog_alpha is [tokens][H] (or NULL without a gate).
+ * oracle_fwd; dlog_alpha is [tokens][H], [tokens][H][d_k] for the per-channel gate, or
+ * NULL without a gate.
  */
 int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, int dv, int gate,
                int write, const double *q, const double *k, const double *v, const double *beta,
@@ -183,8 +187,8 @@ int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
   if (N < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   if (write != ORACLE_WRITE_DELTA && write != ORACLE_WRITE_ADD) return -1;
   if (write == ORACLE_WRITE_DELTA && (beta == NULL || dbeta == NULL)) return -1;
-  if (gate != ORACLE_GATE_NONE && gate != ORACLE_GATE_HEAD) return -1;
-  if (gate == ORACLE_GATE_HEAD && (log_alpha == NULL || dlog_alpha == NULL)) return -1;
+  if (gate != ORACLE_GATE_NONE && gate != ORACLE_GATE_HEAD && gate != ORACLE_GATE_KEY) return -1;
+  if (gate != ORACLE_GATE_NONE && (log_alpha == NULL || dlog_alpha == NULL)) return -1;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
@@ -199,10 +203,11 @@ int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
     double *e = (double *)malloc(sizeof(double) * (size_t)dv);
     double *de = (double *)malloc(sizeof(double) * (size_t)dv);
     double *otmp = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *arow = (double *)malloc(sizeof(double) * (size_t)dk); /* decay of each key row */
     int64_t t;
     int i, j;
-    if (!Ms || !G || !Mp || !r || !e || !de || !otmp) {
-      free(Ms); free(G); free(Mp); free(r); free(e); free(de); free(otmp);
+    if (!Ms || !G || !Mp || !r || !e || !de || !otmp || !arow) {
+      free(Ms); free(G); free(Mp); free(r); free(e); free(de); free(otmp); free(arow);
       failed = 1;
       continue;
     }
@@ -215,7 +220,8 @@ int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
       size_t th = (size_t)(start[n] + t) * H + h;
       memcpy(Ms + (t + 1) * S, Ms + t * S, sizeof(double) * S);
       oracle_token(dk, dv, gate, write, q + th * dk, k + th * dk, v + th * dv, beta ? beta[th] : 0.0,
-                   gate == ORACLE_GATE_HEAD ? log_alpha + th : NULL, Ms + (t + 1) * S, r, otmp);
+                   gate == ORACLE_GATE_HEAD ? log_alpha + th : gate == ORACLE_GATE_KEY ? log_alpha + th * dk : NULL,
+                   Ms + (t + 1) * S, r, otmp);
     }
     /* reverse sweep */
     if (dfinal)
@@ -226,10 +232,12 @@ int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
       size_t th = (size_t)(start[n] + t) * H + h;
       const double *qt = q + th * dk, *kt = k + th * dk, *vt = v + th * dv, *dot = dout + th * dv;
       const double *Mt = Ms + (t + 1) * S, *Mprev = Ms + t * S;
-      const double a = gate == ORACLE_GATE_HEAD ? exp(log_alpha[th]) : 1.0;
       const double bt = beta ? beta[th] : 0.0;
       double db = 0.0, dla = 0.0;
-      for (i = 0; i < S; ++i) Mp[i] = a * Mprev[i];
+      for (i = 0; i < dk; ++i)
+        arow[i] = gate == ORACLE_GATE_HEAD ? exp(log_alpha[th]) : gate == ORACLE_GATE_KEY ? exp(log_alpha[th * dk + i]) : 1.0;
+      for (i = 0; i < dk; ++i)
+        for (j = 0; j < dv; ++j) Mp[i * dv + j] = arow[i] * Mprev[i * dv + j];
       for (j = 0; j < dv; ++j) r[j] = 0.0;
       for (i = 0; i < dk; ++i)
         for (j = 0; j < dv; ++j) r[j] += Mp[i * dv + j] * kt[i];
@@ -255,9 +263,14 @@ int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
           for (i = 0; i < dk; ++i) acc += G[i * dv + j] * kt[i];
           dv_out[th * dv + j] = acc;
         }
-        for (i = 0; i < S; ++i) {
-          dla += G[i] * Mp[i];
-          G[i] *= a;
+        for (i = 0; i < dk; ++i) {
+          double dli = 0.0;
+          for (j = 0; j < dv; ++j) {
+            dli += G[i * dv + j] * Mp[i * dv + j];
+            G[i * dv + j] *= arow[i];
+          }
+          if (gate == ORACLE_GATE_KEY) dlog_alpha[th * dk + i] = dli;
+          dla += dli;
         }
         if (gate == ORACLE_GATE_HEAD) dlog_alpha[th] = dla;
         continue;
@@ -281,16 +294,20 @@ int oracle_bwd(int N, const int64_t *start, const int64_t *len, int H, int dk, i
       for (j = 0; j < dv; ++j) dv_out[th * dv + j] = de[j];
       dbeta[th] = db;
       /* gradient with respect to M', then M_{t-1} */
-      for (i = 0; i < dk; ++i)
+      for (i = 0; i < dk; ++i) {
+        double dli = 0.0;
         for (j = 0; j < dv; ++j) {
           G[i * dv + j] -= kt[i] * de[j];
-          dla += G[i * dv + j] * Mp[i * dv + j];
-          G[i * dv + j] *= a;
+          dli += G[i * dv + j] * Mp[i * dv + j];
+          G[i * dv + j] *= arow[i];
         }
+        if (gate == ORACLE_GATE_KEY) dlog_alpha[th * dk + i] = dli;
+        dla += dli;
+      }
       if (gate == ORACLE_GATE_HEAD) dlog_alpha[th] = dla;
     }
     if (dinit) memcpy(dinit + ((size_t)n * H + h) * S, G, sizeof(double) * S);
-    free(Ms); free(G); free(Mp); free(r); free(e); free(de); free(otmp);
+    free(Ms); free(G); free(Mp); free(r); free(e); free(de); free(otmp); free(arow);
   }
   return failed ? -1 : 0;
 }
