@@ -99,13 +99,13 @@ def test_additive_gradients_match_torch_autograd():
 def test_planted_mistake_in_additive_adjoint_is_caught():
     path = os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")
     src = open(path).read()
-    old = """          dla += G[i] * Mp[i];
-          G[i] *= a;"""
+    old = """            dli += G[i * dv + j] * Mp[i * dv + j];
+            G[i * dv + j] *= arow[i];"""
     assert src.count(old) == 1
     q, k, v, la, s0, wo, ws = case(1, 6, 1, 3, 2, "head", seed=17)
     with tempfile.TemporaryDirectory() as d:
         mpath = os.path.join(d, "mut.c")
-        open(mpath, "w").write(src.replace(old, "          dla += G[i] * Mp[i];"))
+        open(mpath, "w").write(src.replace(old, "            dli += G[i * dv + j] * Mp[i * dv + j];"))
         lib = oracle.load(oracle.build(force=True, src=mpath, out=os.path.join(d, "mut.so")))
         got = oracle.bwd(q, k, v, None, la, s0, wo, ws, lib=lib, write="add")
     grads = dict(q=got[0], k=got[1], v=got[2], la=got[4], s0=got[5])
