@@ -365,8 +365,10 @@ def time_bwd(gdn, name, steps=20, cpu=False):
     tokens = B * T
     esize = 2 if spec["dtype"] == "bf16" else 4
     th = tokens * H
-    per_tok = (8 if write == "delta" else 0) + (8 if spec["gate"] == "head" else 0)
-    nbytes = th * (esize * (4 * dk + 3 * dv) + per_tok) + 3 * 4 * dk * dv * inp["N"] * H
+    per_tok = (8 if write == "delta" else 0) + (8 if spec["gate"] == "head" else 8 * dk if spec["gate"] == "key" else 0)
+    # dfinal read, dinit written, and the initial state read when there is one
+    nstate = (2 + (1 if inp["initial_state"] is not None else 0)) * 4 * dk * dv * inp["N"] * H
+    nbytes = th * (esize * (4 * dk + 3 * dv) + per_tok) + nstate
     fwd_flops, _ = alg_counts(tokens, H, dk, dv, inp["N"], spec["gate"], esize, True, write=write)
     if write == "add":
         flops = fwd_flops + th * (6 * CHUNK * dk + 4 * CHUNK * dv + 8 * dk * dv)
@@ -595,6 +597,9 @@ def main():
         extra.append(time_bwd(gdn, HEADLINE, cpu=not args.no_cpu))
         torch.cuda.empty_cache()
         extra.append(time_bwd(gdn, "retnet-bf16-B16-T2048-H8-d128", cpu=not args.no_cpu))
+        torch.cuda.empty_cache()
+        # (no CPU line: the oracle's reverse sweep keeps 2 GB of states per sequence and head here)
+        extra.append(time_bwd(gdn, "kda-bf16-B2-T16384-H16-d128", steps=5))
         torch.cuda.empty_cache()
         for e in extra:
             print(json.dumps(e), file=sys.stderr)

@@ -614,9 +614,9 @@ def _bwd_args(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state, cu_se
               workspace, write="delta"):
     import torch
     N = check_fwd_tensors(q, k, v, beta, log_alpha, initial_state, cu_seqlens, dout, dfinal_state, write)
-    _require(log_alpha is None or log_alpha.dim() in (1, 3),
-             "the backward supports no gate, log_alpha [B, T, H] (one decay per token and head) or [H] "
-             "(one constant decay per head)")
+    _require(log_alpha is None or log_alpha.dim() in (1, 3, 4),
+             "log_alpha must be None, [H] (one constant decay per head), [B, T, H] (one decay per token "
+             "and head) or [B, T, H, d_k] (one decay per key channel)")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -642,7 +642,8 @@ def bwd_chunked(q, k, v, beta, log_alpha, initial_state, dout, dfinal_state=None
                 output_dinitial: bool = True, workspace=None, stream=None, write: str = "delta"):
     """Gradients of fwd_chunked (gdn_bwd_chunked) for the delta write (beta [B,T,H]) or
     the additive write (write="add", beta None), with no gate, one decay per (token,
-    head) ([B,T,H]) or one constant decay per head ([H]).  Inputs as for fwd_chunked,
+    head) ([B,T,H]), one per key channel ([B,T,H,d_k]) or one constant decay per head
+    ([H]).  Inputs as for fwd_chunked,
     plus dout [B,T,H,d_v] (dtype of q) and dfinal_state None | [N,H,d_k,d_v] fp32.
     Returns (dq, dk, dv, dbeta or None, dlog_alpha or None (shaped like log_alpha),
     dinitial_state or None)."""

@@ -150,8 +150,8 @@ int check_bwd(const gdn_bwd_args *a) {
   const gdn_fwd_args f = fwd_of(a);
   const int st = check_fwd(&f);
   if (st != GDN_OK) return st;
-  if (a->gate == GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
-  if (a->dtype == GDN_F32 && a->d_k != 64) return GDN_ERR_UNSUPPORTED;
+  // fp32 I/O at d_k = 128 has gradients only with the per-key-channel gate
+  if (a->dtype == GDN_F32 && a->d_k != 64 && a->gate != GDN_GATE_KEY) return GDN_ERR_UNSUPPORTED;
   const bool tokens = (long)a->B * a->T > 0;
   if (tokens && (!a->dq || !a->dk || !a->dv)) return GDN_ERR_INVALID_ARG;
   // dbeta exactly for the delta write; dlog_alpha exactly for a gate (the constant
@@ -223,6 +223,38 @@ struct BwdLayout {
   size_t states, tmat, part, dla;
   size_t total() const { return states + tmat + part + dla; }
 };
+// The per-key-channel gate: the fp32 arrays of BwdKeyParams, in this order
+struct BwdKeyLayout {
+  long slots;
+  size_t sz[12];
+  size_t total() const {
+    size_t t = 0;
+    for (size_t x : sz) t += x;
+    return t;
+  }
+};
+BwdKeyLayout bwd_key_layout(const gdn_bwd_args *a) {
+  BwdKeyLayout L{};
+  const long tokens = (long)a->B * a->T;
+  L.slots = gdn::key_slots(tokens, a->N);
+  const size_t sh = (size_t)L.slots * a->H, dk = a->d_k, dv = a->d_v;
+  const bool delta = a->write == GDN_WRITE_DELTA;
+  const size_t sizes[12] = {
+      sh * dk * dv * 4,          // states
+      sh * dk * dv * 4,          // chunk-end state gradients
+      sh * 64 * dv * 4,          // dDelta
+      delta ? sh * 4096 * 4 : 0, // T
+      delta ? sh * 4096 * 4 : 0, // T^T
+      sh * 4096 * 4,             // P^T
+      delta ? sh * 64 * dk * 4 : 0,  // K e^G
+      sh * 64 * dk * 4,          // K e^{g_C - G}
+      delta ? sh * dk * 64 * 4 : 0,  // (K e^G)^T
+      sh * dk * 64 * 4,          // (Q e^G)^T
+      sh * dk * 64 * 4,          // (K e^{g_C - G})^T
+      sh * dk * 4};              // e^{g_C}
+  for (int i = 0; i < 12; ++i) L.sz[i] = align256(sizes[i]);
+  return L;
+}
 BwdLayout bwd_layout(const gdn_bwd_args *a) {
   BwdLayout L{0, 0, 0, 0, 0};
   const long tokens = (long)a->B * a->T;
@@ -241,14 +273,15 @@ extern "C" {
 
 size_t gdn_bwd_workspace_size(const gdn_bwd_args *a) {
   if (check_bwd(a) != GDN_OK) return 0;
-  return bwd_layout(a).total();
+  return a->gate == GDN_GATE_KEY ? bwd_key_layout(a).total() : bwd_layout(a).total();
 }
 
 int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   const int st = check_bwd(a);
   if (st != GDN_OK) return st;
   const BwdLayout L = bwd_layout(a);
-  if (!a->workspace || a->workspace_bytes < L.total() || !aligned(a->workspace, 256)) return GDN_ERR_WORKSPACE;
+  const size_t need = a->gate == GDN_GATE_KEY ? bwd_key_layout(a).total() : L.total();
+  if (!a->workspace || a->workspace_bytes < need || !aligned(a->workspace, 256)) return GDN_ERR_WORKSPACE;
   const long tokens = (long)a->B * a->T;
   if (a->N == 0 || tokens == 0) {
     // no tokens: the initial-state gradient is the final-state gradient (or zero), and a
@@ -268,6 +301,52 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   }
   hipStream_t stream = (hipStream_t)hip_stream;
   char *ws = (char *)a->workspace;
+  if (a->gate == GDN_GATE_KEY) {
+    const BwdKeyLayout KL = bwd_key_layout(a);
+    float *arr[12];
+    size_t off = 0;
+    for (int i = 0; i < 12; ++i) {
+      arr[i] = (float *)(ws + off);
+      off += KL.sz[i];
+    }
+    gdn::BwdKeyParams kp;
+    kp.q = a->q;
+    kp.k = a->k;
+    kp.v = a->v;
+    kp.dout = a->dout;
+    kp.beta = a->beta;
+    kp.log_alpha = a->log_alpha;
+    kp.init_state = a->initial_state;
+    kp.dfinal = a->dfinal_state;
+    kp.cu_seqlens = a->cu_seqlens;
+    kp.states = arr[0];
+    kp.dmc = arr[1];
+    kp.dd = arr[2];
+    kp.tm = arr[3];
+    kp.tmT = arr[4];
+    kp.pmT = arr[5];
+    kp.kt = arr[6];
+    kp.kh = arr[7];
+    kp.ktT = arr[8];
+    kp.qtT = arr[9];
+    kp.khT = arr[10];
+    kp.gam = arr[11];
+    kp.dq = a->dq;
+    kp.dk = a->dk;
+    kp.dv_out = a->dv;
+    kp.dbeta = a->dbeta;
+    kp.dlog_alpha = a->dlog_alpha;
+    kp.dinit = a->dinitial_state;
+    kp.N = a->N;
+    kp.H = a->H;
+    kp.T = a->T;
+    kp.dv = a->d_v;
+    kp.slots = KL.slots;
+    if (gdn::launch_bwd_key(kp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->write == GDN_WRITE_ADD, stream) !=
+        hipSuccess)
+      return GDN_ERR_HIP;
+    return GDN_OK;
+  }
   // 1. forward recomputation: every chunk's entering state
   gdn::FwdParams fp;
   fp.q = a->q;

@@ -1,0 +1,800 @@
+// gdn_bwd_key.hip -- gradients of the chunked forward with one decay per key channel
+// (the channel-wise gate of "Decoding Hybrid Linear Attention Architectures", sec. 3
+// item 6, and with the additive write gated linear attention's gate, item 4).
+//
+// Reverse mode through the chunk equations of sec. 5 with the per-channel decay inside
+// the contractions.  Per chunk, with G[r][c] the chunk-local prefix of log alpha of key
+// channel c, Gamma[r][i][c] = e^{G[r][c] - G[i][c]} (i <= r),
+//   A[r][i] = beta_r sum_c K[r][c] K[i][c] Gamma[r][i][c] (i < r),  T = (I + A)^-1,
+//   P[r][i] = sum_c Q[r][c] K[i][c] Gamma[r][i][c] (i <= r),
+//   Kt = K e^G, Qt = Q e^G, Kh = K e^{G_C - G}, gam = e^{G_C} (per channel),
+//   X' = V - Kt M0, Delta = T diag(beta) X' (the additive write: Delta = V),
+//   O = Qt M0 + P Delta,  M_C = diag(gam) M0 + Kh^T Delta.
+// Given dO and dM (the gradient of M_C):
+//   dDelta = P^T dO + Kh dM,  Y = T^T dDelta,  dV = diag(beta) Y,
+//   dM0 = Qt^T dO + diag(gam) dM - Kt^T diag(beta) Y,
+//   dP = incl(dO Delta^T), dT = dDelta (diag(beta) X')^T, dA = -strict(T^T dT T^T),
+//   dQt = dO M0^T, dKt = -diag(beta) Y M0^T, dKh = Delta dM^T, dgam_c = <M0[c], dM[c]>;
+// with Z = sum_i dA[r][i] K[i] Gamma[r][i], Zc = sum_r beta_r dA[r][i] K[r] Gamma[r][i],
+// Pr = sum_i dP[r][i] K[i] Gamma[r][i], Pc = sum_r dP[r][i] Q[r] Gamma[r][i] (per channel):
+//   dq = Pr + e^G dQt,  dk = beta Z + Zc + Pc + e^G dKt + e^{G_C - G} dKh,
+//   dbeta = rowsum(Y * X') + rowsum(K * Z),
+//   dG = beta K Z - K Zc + Q Pr - K Pc + Kt dKt + Qt dQt - Kh dKh,
+//   dG_C = colsum(Kh * dKh) + gam dgam,  dlog alpha[t] = sum_{r >= t} dG[r] + dG_C.
+// Every pairwise factor is split at row m = 16a + 7 of a 16-row block a: e^{G[r] - G[m]}
+// on one side, e^{G[m] - G[i]} on the other, so that no factor exceeds the decay
+// accumulated over eight tokens (the forward's reading of the decay range).
+//
+// Four launches, everything in between in the caller's workspace (fp32):
+//  1. bwdk_prep_kernel, one workgroup per (chunk, head), fully parallel: Kt, Kh (row-major),
+//     Kt^T, Qt^T, Kh^T (channel-major), gam, T and T^T (delta write), P^T;
+//  2. bwdk_fwd_kernel, one workgroup per (sequence, head, 32 value columns), chunks in
+//     order: the chunk-entering states;
+//  3. bwdk_rev_kernel, the same grid, chunks in reverse: the chunk-end state gradient dM
+//     and dDelta of every chunk, dV, and the initial-state gradient;
+//  4. bwdk_chunk_kernel, one workgroup per (chunk, head), fully parallel: everything
+//     else (dq, dk, dbeta, dlog alpha).
+// Products run on the bf16 matrix cores with every fp32 operand split into hi + lo bf16
+// terms (three MFMAs per 32-deep step, about 2^-17 relative error per product); sums
+// are in fp32 and in a fixed order (deterministic, no atomics).
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+#include "gdn_tile.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int KC = 64;        // chunk length
+constexpr int KBV = 32;       // value columns per workgroup of the serial passes
+constexpr int SV = KBV + 4;   // fp32 pitch of 32-column tiles (rows 16-byte aligned)
+constexpr int SC = KC + 1;    // fp32 pitch of 64-column tiles
+
+template <typename E> __device__ __forceinline__ f32x8 ldrow8(const E *p);
+template <> __device__ __forceinline__ f32x8 ldrow8<float>(const float *p) { return ld8(p); }
+template <> __device__ __forceinline__ f32x8 ldrow8<bf16>(const bf16 *p) { return widen8(ld8(p)); }
+
+__device__ __forceinline__ f32x8 zero8() {
+  f32x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = 0.f;
+  return z;
+}
+
+// One 16x16 tile of C = A B over k in [0, K): fa(k0) and fb(k0) give this lane's fp32
+// fragments (A: its row, B: its column, at k = k0 + 8 lg .. + 7).  32-deep steps
+// outside [kbeg, kend) are skipped (known zeros; wave-uniform bounds).
+template <int K, class FA, class FB>
+__device__ __forceinline__ f32x4 kprod(FA fa, FB fb, int kbeg = 0, int kend = K) {
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32)
+    if (k0 + 32 > kbeg && k0 < kend) acc = mm(split8(fa(k0)), split8(fb(k0)), acc);
+  return acc;
+}
+
+__device__ __forceinline__ bool seq_extent_k(const BwdKeyParams &p, int n, long &tok0, int &len) {
+  if (p.cu_seqlens) {
+    const int a = p.cu_seqlens[n], b = p.cu_seqlens[n + 1];
+    if (a < 0 || b < a || b > p.T) return false;
+    tok0 = a;
+    len = b - a;
+  } else {
+    tok0 = (long)n * p.T;
+    len = p.T;
+  }
+  return true;
+}
+
+// The chunk that owns a slot: its first token and valid rows (false: no chunk owns it)
+__device__ __forceinline__ bool slot_chunk(const BwdKeyParams &p, long slot, long &tb, int &nv) {
+  auto tok_start = [&](int sq) -> long { return p.cu_seqlens ? (long)p.cu_seqlens[sq] : (long)sq * p.T; };
+  int lo = 0, hi = p.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((tok_start(mid) >> 6) + mid <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  long tok0;
+  int len;
+  if (!seq_extent_k(p, lo, tok0, len)) return false;
+  const long c = slot - ((tok0 >> 6) + lo);
+  if (c < 0 || 64 * c >= len) return false;
+  tb = tok0 + 64 * c;
+  nv = (int)min(64L, (long)len - 64 * c);
+  return true;
+}
+
+// ---------------------------------------------------------------- 1. operands per chunk
+template <typename E, int DK, bool ADD>
+__global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
+  constexpr int SG = DK + 4;
+  __shared__ __align__(16) float Ks[KC * SG];
+  __shared__ __align__(16) float Qs[KC * SG];
+  __shared__ __align__(16) float Gs[KC * SG];
+  __shared__ float As[KC * SC];
+  __shared__ float Ps[KC * SC];
+  __shared__ float bsh[KC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lm = lane & 15;
+  const int H = p.H;
+  const long slot = blockIdx.x / H;
+  const int h = blockIdx.x % H;
+  long tb;
+  int nv;
+  if (!slot_chunk(p, slot, tb, nv)) return;
+  const size_t sh = (size_t)slot * H + h;
+  for (int i = tid; i < KC * DK; i += 256) {
+    const int r = i / DK, d = i % DK;
+    const size_t o = ((size_t)(tb + r) * H + h) * DK + d;
+    const bool in = r < nv;
+    Ks[r * SG + d] = in ? to_f(((const E *)p.k)[o]) : 0.f;
+    Qs[r * SG + d] = in ? to_f(((const E *)p.q)[o]) : 0.f;
+    Gs[r * SG + d] = in ? p.log_alpha[o] : 0.f;
+  }
+  if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? p.beta[(size_t)(tb + tid) * H + h] : 0.f;
+  for (int i = tid; i < KC * SC; i += 256) As[i] = Ps[i] = 0.f;
+  __syncthreads();
+  if (tid < DK) {  // inclusive prefix over the chunk, per channel
+    float g = 0.f;
+    for (int r = 0; r < KC; ++r) {
+      g += Gs[r * SG + tid];
+      Gs[r * SG + tid] = g;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < KC * DK; i += 256) {
+    const int r = i / DK, d = i % DK;
+    const float g = Gs[r * SG + d], gC = Gs[(KC - 1) * SG + d];
+    const float e = __expf(g), et = __expf(gC - g), kv = Ks[r * SG + d];
+    if (!ADD) {
+      p.kt[(sh * KC + r) * DK + d] = kv * e;
+      p.ktT[(sh * DK + d) * KC + r] = kv * e;
+    }
+    p.kh[(sh * KC + r) * DK + d] = kv * et;
+    p.khT[(sh * DK + d) * KC + r] = kv * et;
+    p.qtT[(sh * DK + d) * KC + r] = Qs[r * SG + d] * e;
+  }
+  if (tid < DK) p.gam[sh * DK + tid] = __expf(Gs[(KC - 1) * SG + tid]);
+  // the ten lower 16x16 tiles of P (and of A): row operand x[r] e^{G[r] - G[m]}, column
+  // operand K[i] e^{G[m] - G[i]}, m = 16a + 7 of the row block a
+  for (int t = wave; t < (ADD ? 10 : 20); t += 4) {
+    const int tt = t % 10, a = tt < 1 ? 0 : tt < 3 ? 1 : tt < 6 ? 2 : 3;
+    const int b = tt - a * (a + 1) / 2, m = 16 * a + 7;
+    const float *X = t < 10 ? Qs : Ks;
+    const f32x4 acc = kprod<DK>(
+        [&](int k0) {
+          f32x8 f;
+          const int r = 16 * a + lm;
+#pragma unroll
+          for (int ii = 0; ii < 8; ++ii) {
+            const int c = k0 + 8 * lg + ii;
+            f[ii] = X[r * SG + c] * __expf(Gs[r * SG + c] - Gs[m * SG + c]);
+          }
+          return f;
+        },
+        [&](int k0) {
+          f32x8 f;
+          const int i = 16 * b + lm;
+#pragma unroll
+          for (int ii = 0; ii < 8; ++ii) {
+            const int c = k0 + 8 * lg + ii;
+            f[ii] = Ks[i * SG + c] * __expf(Gs[m * SG + c] - Gs[i * SG + c]);
+          }
+          return f;
+        });
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * a + 4 * lg + j, i = 16 * b + lm;
+      if (t < 10)
+        Ps[r * SC + i] = i <= r ? acc[j] : 0.f;
+      else
+        As[r * SC + i] = i < r ? bsh[r] * acc[j] : 0.f;
+    }
+  }
+  __syncthreads();
+  if (!ADD && tid < KC) {
+    // T = (I + A)^-1, column c per thread: T[r][c] = [r == c] - sum_{i<r} A[r][i] T[i][c]
+    const int c = tid;
+    float x[KC];
+#pragma unroll
+    for (int r = 0; r < KC; ++r) {
+      float acc = r == c ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc -= As[r * SC + i] * x[i];
+      x[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < KC; ++r) {
+      p.tm[(sh * KC + r) * KC + c] = x[r];
+      p.tmT[(sh * KC + c) * KC + r] = x[r];
+    }
+  }
+  for (int i = tid; i < KC * KC; i += 256) {
+    const int r = i / KC, c = i % KC;
+    p.pmT[sh * KC * KC + i] = Ps[c * SC + r];
+  }
+}
+
+// ---------------------------------------------------------------- 2. chunk-entering states
+template <typename E, int DK, bool ADD>
+__global__ __launch_bounds__(256, 1) void bwdk_fwd_kernel(BwdKeyParams p) {
+  __shared__ __align__(16) float Ms[DK * SV];
+  __shared__ __align__(16) float Xs[KC * SV];
+  __shared__ __align__(16) float Ds[KC * SV];
+  __shared__ __align__(16) float Vs[KC * SV];
+  __shared__ float bsh[KC], gsh[DK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lm = lane & 15;
+  const int H = p.H, dv = p.dv, nb = dv / KBV;
+  const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
+  const int n = pair / H, h = pair % H, col0 = jb * KBV;
+  long tok0;
+  int len;
+  if (!seq_extent_k(p, n, tok0, len)) return;
+  const int nchunks = (len + KC - 1) / KC;
+  const long slot0 = (tok0 >> 6) + n;
+  const size_t sbase = ((size_t)n * H + h) * DK * dv + col0;
+  for (int i = tid; i < DK * KBV; i += 256) {
+    const int d = i / KBV, j = i % KBV;
+    Ms[d * SV + j] = p.init_state ? p.init_state[sbase + (size_t)d * dv + j] : 0.f;
+  }
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const size_t sh = (size_t)(slot0 + c) * H + h;
+    const int nv = min(KC, len - c * KC);
+    const size_t tbase = (size_t)tok0 + (size_t)c * KC;
+    for (int i = tid; i < DK * KBV; i += 256) {
+      const int d = i / KBV, j = i % KBV;
+      p.states[(sh * DK + d) * dv + col0 + j] = Ms[d * SV + j];
+    }
+    for (int i = tid; i < KC * KBV; i += 256) {
+      const int r = i / KBV, j = i % KBV;
+      Vs[r * SV + j] = r < nv ? to_f(((const E *)p.v)[((tbase + r) * H + h) * dv + col0 + j]) : 0.f;
+    }
+    if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? p.beta[(tbase + tid) * H + h] : 0.f;
+    if (tid < DK) gsh[tid] = p.gam[sh * DK + tid];
+    __syncthreads();
+    if constexpr (!ADD) {
+      // X' = V - Kt M  (eight 16x16 tiles, two per wave)
+      for (int t = wave; t < 8; t += 4) {
+        const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
+        const f32x4 acc = kprod<DK>([&](int k0) { return ld8(p.kt + (sh * KC + m0 + lm) * DK + k0 + 8 * lg); },
+                                    [&](int k0) {
+                                      f32x8 f;
+#pragma unroll
+                                      for (int ii = 0; ii < 8; ++ii) f[ii] = Ms[(k0 + 8 * lg + ii) * SV + n0 + lm];
+                                      return f;
+                                    });
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = m0 + 4 * lg + j;
+          Xs[r * SV + n0 + lm] = Vs[r * SV + n0 + lm] - acc[j];
+        }
+      }
+      __syncthreads();
+      // Delta = T diag(beta) X'  (T lower triangular)
+      for (int t = wave; t < 8; t += 4) {
+        const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
+        const f32x4 acc = kprod<KC>([&](int k0) { return ld8(p.tm + (sh * KC + m0 + lm) * KC + k0 + 8 * lg); },
+                                    [&](int k0) {
+                                      f32x8 f;
+#pragma unroll
+                                      for (int ii = 0; ii < 8; ++ii) {
+                                        const int k = k0 + 8 * lg + ii;
+                                        f[ii] = bsh[k] * Xs[k * SV + n0 + lm];
+                                      }
+                                      return f;
+                                    },
+                                    0, m0 + 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Ds[(m0 + 4 * lg + j) * SV + n0 + lm] = acc[j];
+      }
+      __syncthreads();
+    }
+    const float *D = ADD ? Vs : Ds;
+    // M = diag(gam) M + Kh^T Delta
+    for (int t = wave; t < (DK / 16) * 2; t += 4) {
+      const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
+      const f32x4 acc = kprod<KC>([&](int k0) { return ld8(p.khT + (sh * DK + m0 + lm) * KC + k0 + 8 * lg); },
+                                  [&](int k0) {
+                                    f32x8 f;
+#pragma unroll
+                                    for (int ii = 0; ii < 8; ++ii) f[ii] = D[(k0 + 8 * lg + ii) * SV + n0 + lm];
+                                    return f;
+                                  });
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = m0 + 4 * lg + j;
+        Ms[d * SV + n0 + lm] = gsh[d] * Ms[d * SV + n0 + lm] + acc[j];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- 3. reverse state pass
+template <typename E, int DK, bool ADD>
+__global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
+  __shared__ __align__(16) float dMs[DK * SV];
+  __shared__ __align__(16) float dOs[KC * SV];
+  __shared__ __align__(16) float dDs[KC * SV];
+  __shared__ __align__(16) float Ys[KC * SV];
+  __shared__ float bsh[KC], gsh[DK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lm = lane & 15;
+  const int H = p.H, dv = p.dv, nb = dv / KBV;
+  const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
+  const int n = pair / H, h = pair % H, col0 = jb * KBV;
+  long tok0;
+  int len;
+  if (!seq_extent_k(p, n, tok0, len)) return;
+  const int nchunks = (len + KC - 1) / KC;
+  const long slot0 = (tok0 >> 6) + n;
+  const size_t sbase = ((size_t)n * H + h) * DK * dv + col0;
+  for (int i = tid; i < DK * KBV; i += 256) {
+    const int d = i / KBV, j = i % KBV;
+    dMs[d * SV + j] = p.dfinal ? p.dfinal[sbase + (size_t)d * dv + j] : 0.f;
+  }
+  __syncthreads();
+  for (int c = nchunks - 1; c >= 0; --c) {
+    const size_t sh = (size_t)(slot0 + c) * H + h;
+    const int nv = min(KC, len - c * KC);
+    const size_t tbase = (size_t)tok0 + (size_t)c * KC;
+    for (int i = tid; i < DK * KBV; i += 256) {
+      const int d = i / KBV, j = i % KBV;
+      p.dmc[(sh * DK + d) * dv + col0 + j] = dMs[d * SV + j];
+    }
+    for (int i = tid; i < KC * KBV; i += 256) {
+      const int r = i / KBV, j = i % KBV;
+      dOs[r * SV + j] = r < nv ? to_f(((const E *)p.dout)[((tbase + r) * H + h) * dv + col0 + j]) : 0.f;
+    }
+    if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? p.beta[(tbase + tid) * H + h] : 0.f;
+    if (tid < DK) gsh[tid] = p.gam[sh * DK + tid];
+    __syncthreads();
+    // dDelta = P^T dO + Kh dM  (P^T[r][i] = P[i][r] is zero for i < r)
+    for (int t = wave; t < 8; t += 4) {
+      const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
+      const f32x4 a1 = kprod<KC>([&](int k0) { return ld8(p.pmT + (sh * KC + m0 + lm) * KC + k0 + 8 * lg); },
+                                 [&](int k0) {
+                                   f32x8 f;
+#pragma unroll
+                                   for (int ii = 0; ii < 8; ++ii) f[ii] = dOs[(k0 + 8 * lg + ii) * SV + n0 + lm];
+                                   return f;
+                                 },
+                                 m0, KC);
+      const f32x4 a2 = kprod<DK>([&](int k0) { return ld8(p.kh + (sh * KC + m0 + lm) * DK + k0 + 8 * lg); },
+                                 [&](int k0) {
+                                   f32x8 f;
+#pragma unroll
+                                   for (int ii = 0; ii < 8; ++ii) f[ii] = dMs[(k0 + 8 * lg + ii) * SV + n0 + lm];
+                                   return f;
+                                 });
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = m0 + 4 * lg + j;
+        const float x = a1[j] + a2[j];
+        dDs[r * SV + n0 + lm] = x;
+        p.dd[(sh * KC + r) * dv + col0 + n0 + lm] = x;
+      }
+    }
+    __syncthreads();
+    if constexpr (!ADD) {
+      // Y = T^T dDelta  (T^T[r][i] = T[i][r] is zero for i < r)
+      for (int t = wave; t < 8; t += 4) {
+        const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
+        const f32x4 acc = kprod<KC>([&](int k0) { return ld8(p.tmT + (sh * KC + m0 + lm) * KC + k0 + 8 * lg); },
+                                    [&](int k0) {
+                                      f32x8 f;
+#pragma unroll
+                                      for (int ii = 0; ii < 8; ++ii) f[ii] = dDs[(k0 + 8 * lg + ii) * SV + n0 + lm];
+                                      return f;
+                                    },
+                                    m0, KC);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Ys[(m0 + 4 * lg + j) * SV + n0 + lm] = acc[j];
+      }
+      __syncthreads();
+    }
+    const float *Y = ADD ? dDs : Ys;
+    for (int i = tid; i < KC * KBV; i += 256) {
+      const int r = i / KBV, j = i % KBV;
+      if (r < nv)
+        ((E *)p.dv_out)[((tbase + r) * H + h) * dv + col0 + j] = to_e<E>(ADD ? Y[r * SV + j] : bsh[r] * Y[r * SV + j]);
+    }
+    // dM <- diag(gam) dM + Qt^T dO - Kt^T diag(beta) Y
+    for (int t = wave; t < (DK / 16) * 2; t += 4) {
+      const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
+      const f32x4 a1 = kprod<KC>([&](int k0) { return ld8(p.qtT + (sh * DK + m0 + lm) * KC + k0 + 8 * lg); },
+                                 [&](int k0) {
+                                   f32x8 f;
+#pragma unroll
+                                   for (int ii = 0; ii < 8; ++ii) f[ii] = dOs[(k0 + 8 * lg + ii) * SV + n0 + lm];
+                                   return f;
+                                 });
+      f32x4 a2 = zero4();
+      if constexpr (!ADD)
+        a2 = kprod<KC>([&](int k0) { return ld8(p.ktT + (sh * DK + m0 + lm) * KC + k0 + 8 * lg); },
+                       [&](int k0) {
+                         f32x8 f;
+#pragma unroll
+                         for (int ii = 0; ii < 8; ++ii) {
+                           const int k = k0 + 8 * lg + ii;
+                           f[ii] = bsh[k] * Y[k * SV + n0 + lm];
+                         }
+                         return f;
+                       });
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = m0 + 4 * lg + j;
+        dMs[d * SV + n0 + lm] = gsh[d] * dMs[d * SV + n0 + lm] + a1[j] - a2[j];
+      }
+    }
+    __syncthreads();
+  }
+  if (p.dinit)
+    for (int i = tid; i < DK * KBV; i += 256) {
+      const int d = i / KBV, j = i % KBV;
+      p.dinit[sbase + (size_t)d * dv + j] = dMs[d * SV + j];
+    }
+}
+
+// ---------------------------------------------------------------- 4. per-chunk gradients
+template <typename E, int DK, bool ADD>
+__global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
+  constexpr int SG = DK + 4;
+  constexpr int NCT = DK / 32;  // 16-column channel tiles per wave
+  __shared__ __align__(16) float Gs[KC * SG];  // G, then dG
+  __shared__ float Tl[KC * SC];
+  __shared__ float dTl[KC * SC];               // dT, then dA
+  __shared__ float dPl[KC * SC];
+  __shared__ __align__(16) float scr[3 * KC * SV];  // X', Delta, Y of a value slice; then W
+  __shared__ float bsh[KC], gcl[DK], rb[2][KC], gcp[4][DK], dbys[KC];
+  float *Xs = scr, *Ds = scr + KC * SV, *Ys = scr + 2 * KC * SV, *Wl = scr;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lm = lane & 15;
+  const int H = p.H, dv = p.dv;
+  const long slot = blockIdx.x / H;
+  const int h = blockIdx.x % H;
+  long tb;
+  int nv;
+  if (!slot_chunk(p, slot, tb, nv)) return;
+  const size_t sh = (size_t)slot * H + h;
+  const E *kin = (const E *)p.k, *qin = (const E *)p.q, *vin = (const E *)p.v, *doin = (const E *)p.dout;
+  auto K_ = [&](int r, int c) { return r < nv ? to_f(kin[((size_t)(tb + r) * H + h) * DK + c]) : 0.f; };
+  auto Q_ = [&](int r, int c) { return r < nv ? to_f(qin[((size_t)(tb + r) * H + h) * DK + c]) : 0.f; };
+  for (int i = tid; i < KC * DK; i += 512) {
+    const int r = i / DK, d = i % DK;
+    Gs[r * SG + d] = r < nv ? p.log_alpha[((size_t)(tb + r) * H + h) * DK + d] : 0.f;
+  }
+  if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? p.beta[(size_t)(tb + tid) * H + h] : 0.f;
+  if (!ADD)
+    for (int i = tid; i < KC * KC; i += 512) Tl[(i / KC) * SC + i % KC] = p.tm[sh * KC * KC + i];
+  __syncthreads();
+  if (tid < DK) {
+    float g = 0.f;
+    for (int r = 0; r < KC; ++r) {
+      g += Gs[r * SG + tid];
+      Gs[r * SG + tid] = g;
+    }
+    gcl[tid] = g;
+  }
+  __syncthreads();
+
+  // ---- value slices: X', Delta, Y, and the sums over value columns
+  const int wa = wave & 3, wc = wave >> 2;
+  f32x4 aP[2], aT[2], aQ[NCT], aK[NCT], aH[NCT];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) aP[u] = aT[u] = zero4();
+#pragma unroll
+  for (int u = 0; u < NCT; ++u) aQ[u] = aK[u] = aH[u] = zero4();
+  float dby = 0.f, dgm = 0.f;
+  const float *st = p.states + sh * DK * dv, *dmc = p.dmc + sh * DK * dv, *dd = p.dd + sh * KC * dv;
+  for (int col0 = 0; col0 < dv; col0 += KBV) {
+    {  // X' = V - Kt M0 (delta write) or Delta = V (additive write): eight tiles, one per wave
+      const int m0 = 16 * (wave >> 1), n0 = 16 * (wave & 1);
+      f32x4 acc = zero4();
+      if constexpr (!ADD)
+        acc = kprod<DK>([&](int k0) { return ld8(p.kt + (sh * KC + m0 + lm) * DK + k0 + 8 * lg); },
+                        [&](int k0) {
+                          f32x8 f;
+#pragma unroll
+                          for (int ii = 0; ii < 8; ++ii) f[ii] = st[(size_t)(k0 + 8 * lg + ii) * dv + col0 + n0 + lm];
+                          return f;
+                        });
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = m0 + 4 * lg + j;
+        const float vv = r < nv ? to_f(vin[((size_t)(tb + r) * H + h) * dv + col0 + n0 + lm]) : 0.f;
+        (ADD ? Ds : Xs)[r * SV + n0 + lm] = vv - acc[j];
+      }
+    }
+    __syncthreads();
+    if constexpr (!ADD) {
+      const int m0 = 16 * (wave >> 1), n0 = 16 * (wave & 1);
+      const f32x4 dl = kprod<KC>(
+          [&](int k0) {
+            f32x8 f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) f[ii] = Tl[(m0 + lm) * SC + k0 + 8 * lg + ii];
+            return f;
+          },
+          [&](int k0) {
+            f32x8 f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) {
+              const int k = k0 + 8 * lg + ii;
+              f[ii] = bsh[k] * Xs[k * SV + n0 + lm];
+            }
+            return f;
+          },
+          0, m0 + 16);
+      const f32x4 y = kprod<KC>(
+          [&](int k0) {
+            f32x8 f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) f[ii] = Tl[(k0 + 8 * lg + ii) * SC + m0 + lm];
+            return f;
+          },
+          [&](int k0) {
+            f32x8 f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) f[ii] = dd[(size_t)(k0 + 8 * lg + ii) * dv + col0 + n0 + lm];
+            return f;
+          },
+          m0, KC);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Ds[(m0 + 4 * lg + j) * SV + n0 + lm] = dl[j];
+        Ys[(m0 + 4 * lg + j) * SV + n0 + lm] = y[j];
+      }
+      __syncthreads();
+      if (tid < KC)
+        for (int j = 0; j < KBV; ++j) dby += Ys[tid * SV + j] * Xs[tid * SV + j];
+    }
+    if (tid < DK)
+      for (int j = 0; j < KBV; ++j) dgm += st[(size_t)tid * dv + col0 + j] * dmc[(size_t)tid * dv + col0 + j];
+    auto dorow = [&](int r, int k0) {
+      return r < nv ? ldrow8<E>(doin + ((size_t)(tb + r) * H + h) * dv + col0 + k0 + 8 * lg) : zero8();
+    };
+    // dP += dO Delta^T, dT += dDelta (diag(beta) X')^T  (64 x 64: tiles wave, wave + 8)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = wave + 8 * u, m0 = 16 * (t >> 2), n0 = 16 * (t & 3);
+      aP[u] += kprod<KBV>([&](int k0) { return dorow(m0 + lm, k0); },
+                          [&](int k0) { return ld8(Ds + (n0 + lm) * SV + k0 + 8 * lg); });
+      if constexpr (!ADD)
+        aT[u] += kprod<KBV>([&](int k0) { return ld8(dd + (size_t)(m0 + lm) * dv + col0 + k0 + 8 * lg); },
+                            [&](int k0) { return ld8(Xs + (n0 + lm) * SV + k0 + 8 * lg) * bsh[n0 + lm]; });
+    }
+    // dQt += dO M0^T, dKt -= diag(beta) Y M0^T, dKh += Delta dM^T  (64 x DK)
+#pragma unroll
+    for (int u = 0; u < NCT; ++u) {
+      const int m0 = 16 * wa, n0 = 16 * (wc + 2 * u);
+      auto fm = [&](int k0) { return ld8(st + (size_t)(n0 + lm) * dv + col0 + k0 + 8 * lg); };
+      aQ[u] += kprod<KBV>([&](int k0) { return dorow(m0 + lm, k0); }, fm);
+      if constexpr (!ADD)
+        aK[u] -= kprod<KBV>([&](int k0) { return ld8(Ys + (m0 + lm) * SV + k0 + 8 * lg) * bsh[m0 + lm]; }, fm);
+      aH[u] += kprod<KBV>([&](int k0) { return ld8(Ds + (m0 + lm) * SV + k0 + 8 * lg); },
+                          [&](int k0) { return ld8(dmc + (size_t)(n0 + lm) * dv + col0 + k0 + 8 * lg); });
+    }
+    __syncthreads();  // the slice buffers are rewritten by the next slice
+  }
+
+  // ---- dP (inclusive lower) and dT into LDS; dA = -strict(T^T dT T^T)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = wave + 8 * u, m0 = 16 * (t >> 2), n0 = 16 * (t & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = m0 + 4 * lg + j, i = n0 + lm;
+      dPl[r * SC + i] = i <= r ? aP[u][j] : 0.f;
+      if (!ADD) dTl[r * SC + i] = aT[u][j];
+    }
+  }
+  if (tid < KC) dbys[tid] = dby;
+  __syncthreads();
+  if constexpr (!ADD) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // W = dT T^T
+      const int t = wave + 8 * u, m0 = 16 * (t >> 2), n0 = 16 * (t & 3);
+      const f32x4 w = kprod<KC>(
+          [&](int k0) {
+            f32x8 f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) f[ii] = dTl[(m0 + lm) * SC + k0 + 8 * lg + ii];
+            return f;
+          },
+          [&](int k0) {
+            f32x8 f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) f[ii] = Tl[(n0 + lm) * SC + k0 + 8 * lg + ii];
+            return f;
+          },
+          0, n0 + 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Wl[(m0 + 4 * lg + j) * SC + n0 + lm] = w[j];
+    }
+    __syncthreads();
+    f32x4 da[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // dA = -T^T W
+      const int t = wave + 8 * u, m0 = 16 * (t >> 2), n0 = 16 * (t & 3);
+      da[u] = kprod<KC>(
+          [&](int k0) {
+            f32x8 f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) f[ii] = Tl[(k0 + 8 * lg + ii) * SC + m0 + lm];
+            return f;
+          },
+          [&](int k0) {
+            f32x8 f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) f[ii] = Wl[(k0 + 8 * lg + ii) * SC + n0 + lm];
+            return f;
+          },
+          m0, KC);
+    }
+    __syncthreads();  // every read of dT is done
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = wave + 8 * u, m0 = 16 * (t >> 2), n0 = 16 * (t & 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = m0 + 4 * lg + j, i = n0 + lm;
+        dTl[r * SC + i] = i < r ? -da[u][j] : 0.f;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- per-channel terms, tiles (row block wa, channel blocks wc + 2u)
+  const int a = wa, mref = 16 * a + 7;
+  float rbs[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 dgt[NCT];
+#pragma unroll
+  for (int u = 0; u < NCT; ++u) {
+    const int c = 16 * (wc + 2 * u) + lm;
+    const float gm = Gs[mref * SG + c];
+    // rows i of the column operand K[i] e^{G[m] - G[i]}, i < 16 (a + 1)
+    auto kcol = [&](int k0) {
+      f32x8 f;
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        const int i = k0 + 8 * lg + ii;
+        f[ii] = i < 16 * (a + 1) ? K_(i, c) * __expf(gm - Gs[i * SG + c]) : 0.f;
+      }
+      return f;
+    };
+    // rows r >= 16 a of x[r] e^{G[r] - G[m]}
+    auto rrow = [&](auto X, int k0) {
+      f32x8 f;
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        const int r = k0 + 8 * lg + ii;
+        f[ii] = r >= 16 * a ? X(r, c) * __expf(Gs[r * SG + c] - gm) : 0.f;
+      }
+      return f;
+    };
+    const f32x4 Pr = kprod<KC>(
+        [&](int k0) {
+          f32x8 f;
+#pragma unroll
+          for (int ii = 0; ii < 8; ++ii) f[ii] = dPl[(16 * a + lm) * SC + k0 + 8 * lg + ii];
+          return f;
+        },
+        kcol, 0, 16 * (a + 1));
+    const f32x4 Pc = kprod<KC>(
+        [&](int k0) {
+          f32x8 f;
+#pragma unroll
+          for (int ii = 0; ii < 8; ++ii) f[ii] = dPl[(k0 + 8 * lg + ii) * SC + 16 * a + lm];
+          return f;
+        },
+        [&](int k0) { return rrow(Q_, k0); }, 16 * a, KC);
+    f32x4 Z = zero4(), Zc = zero4();
+    if constexpr (!ADD) {
+      Z = kprod<KC>(
+          [&](int k0) {
+            f32x8 f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) f[ii] = dTl[(16 * a + lm) * SC + k0 + 8 * lg + ii];
+            return f;
+          },
+          kcol, 0, 16 * (a + 1));
+      Zc = kprod<KC>(
+          [&](int k0) {
+            f32x8 f;
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) {
+              const int r = k0 + 8 * lg + ii;
+              f[ii] = bsh[r] * dTl[r * SC + 16 * a + lm];
+            }
+            return f;
+          },
+          [&](int k0) { return rrow(K_, k0); }, 16 * a, KC);
+    }
+    float gcs = 0.f;
+    const float gC = gcl[c];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * a + 4 * lg + j;
+      const float g = Gs[r * SG + c];
+      const float eg = __expf(g), et = __expf(gC - g), fr = __expf(g - gm), fc = __expf(gm - g);
+      const float kv = K_(r, c), qv = Q_(r, c), br = bsh[r];
+      const float z = Z[j] * fr, pr = Pr[j] * fr, zc = Zc[j] * fc, pc = Pc[j] * fc;
+      const float dq = pr + eg * aQ[u][j];
+      const float dk = br * z + zc + pc + eg * aK[u][j] + et * aH[u][j];
+      dgt[u][j] = br * kv * z - kv * zc + qv * pr - kv * pc + kv * eg * aK[u][j] + qv * eg * aQ[u][j] -
+                  kv * et * aH[u][j];
+      rbs[j] += kv * z;
+      gcs += kv * et * aH[u][j];
+      if (r < nv) {
+        const size_t o = ((size_t)(tb + r) * H + h) * DK + c;
+        ((E *)p.dq)[o] = to_e<E>(dq);
+        ((E *)p.dk)[o] = to_e<E>(dk);
+      }
+    }
+    gcs += __shfl_xor(gcs, 16);
+    gcs += __shfl_xor(gcs, 32);
+    if (lg == 0) gcp[a][c] = gcs;
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rbs[j] += __shfl_xor(rbs[j], off);
+  __syncthreads();  // every read of G is done
+#pragma unroll
+  for (int u = 0; u < NCT; ++u) {
+    const int c = 16 * (wc + 2 * u) + lm;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Gs[(16 * a + 4 * lg + j) * SG + c] = dgt[u][j];
+  }
+  if (lm == 0)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rb[wc][16 * a + 4 * lg + j] = rbs[j];
+  __syncthreads();
+  if (tid < DK) {  // d log alpha: reverse prefix of dG plus dG_C, per channel
+    const int c = tid;
+    const float dgc = ((gcp[0][c] + gcp[1][c]) + (gcp[2][c] + gcp[3][c])) + __expf(gcl[c]) * dgm;
+    float acc = 0.f;
+    for (int r = KC - 1; r >= 0; --r) {
+      acc += Gs[r * SG + c];
+      if (r < nv) p.dlog_alpha[((size_t)(tb + r) * H + h) * DK + c] = acc + dgc;
+    }
+  }
+  if (!ADD && tid < nv) p.dbeta[(size_t)(tb + tid) * H + h] = dbys[tid] + (rb[0][tid] + rb[1][tid]);
+}
+
+template <typename E, int DK>
+hipError_t launch_k(const BwdKeyParams &p, bool add, hipStream_t stream) {
+  const unsigned items = (unsigned)(p.slots * p.H), serial = (unsigned)(p.N * p.H * (p.dv / KBV));
+  if (items == 0 || serial == 0) return hipSuccess;
+  if (add) {
+    hipLaunchKernelGGL((bwdk_prep_kernel<E, DK, true>), dim3(items), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwdk_fwd_kernel<E, DK, true>), dim3(serial), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, true>), dim3(serial), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwdk_chunk_kernel<E, DK, true>), dim3(items), dim3(512), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((bwdk_prep_kernel<E, DK, false>), dim3(items), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwdk_fwd_kernel<E, DK, false>), dim3(serial), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, false>), dim3(serial), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwdk_chunk_kernel<E, DK, false>), dim3(items), dim3(512), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_key(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream) {
+  if (dtype == 1) {
+    if (dk == 128) return launch_k<bf16, 128>(p, add, stream);
+    if (dk == 64) return launch_k<bf16, 64>(p, add, stream);
+  } else {
+    if (dk == 128) return launch_k<float, 128>(p, add, stream);
+    if (dk == 64) return launch_k<float, 64>(p, add, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -91,6 +91,29 @@ hipError_t launch_fill_zero(float *x, size_t n, hipStream_t stream);
 // out[h] = sum over tokens of x[t, h] (deterministic order)
 hipError_t launch_sum_tokens(const float *x, long tokens, int H, float *out, hipStream_t stream);
 
+// Backward pass with one decay per key channel: four launches over a workspace of
+// per-chunk operands (every array indexed by chunk slot, as for key_slots, then head).
+struct BwdKeyParams {
+  const void *q, *k, *v, *dout;  // [tokens, H, d_k] / [tokens, H, d_v], I/O dtype
+  const float *beta;             // [tokens, H]; NULL for the additive write
+  const float *log_alpha;        // [tokens, H, d_k]
+  const float *init_state;       // NULL | [N, H, d_k, d_v]
+  const float *dfinal;           // NULL | [N, H, d_k, d_v]
+  const int32_t *cu_seqlens;     // NULL (batch) | [N + 1]
+  // workspace (fp32): chunk-entering states and chunk-end state gradients [S, H, d_k, d_v],
+  // dDelta [S, H, 64, d_v], T and T^T [S, H, 64, 64] (delta write), P^T [S, H, 64, 64],
+  // K e^G and K e^{g_C - G} [S, H, 64, d_k], their transposes and (Q e^G)^T [S, H, d_k, 64],
+  // e^{g_C} [S, H, d_k]
+  float *states, *dmc, *dd, *tm, *tmT, *pmT, *kt, *kh, *ktT, *qtT, *khT, *gam;
+  void *dq, *dk, *dv_out;        // outputs, I/O dtype
+  float *dbeta;                  // [tokens, H]; NULL for the additive write
+  float *dlog_alpha;             // [tokens, H, d_k]
+  float *dinit;                  // NULL | [N, H, d_k, d_v]
+  int N, H, T, dv;
+  long slots;
+};
+hipError_t launch_bwd_key(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream);
+
 // Forward of the diagonal-plus-low-rank transition (no gate or the scalar gate).
 struct DplrParams {
   const void *q, *k, *v, *a, *b;  // [tokens, H, d_k] (v: d_v), I/O dtype

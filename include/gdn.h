@@ -212,9 +212,9 @@ int gdn_fwd_decode(const gdn_decode_args *args, void *hip_stream);
  * equations of "Decoding Hybrid Linear Attention Architectures", sec. 5, written out
  * in this library's kernels (the pages give the forward only).  Supported: the delta
  * write and the additive write (GDN_WRITE_ADD: gated linear attention / RetNet), each
- * with no gate, one decay per (token, head) or one constant decay per head
- * (GDN_GATE_NONE, GDN_GATE_HEAD, GDN_GATE_HEAD_CONST); the per-key-channel gate returns
- * GDN_ERR_UNSUPPORTED, and so does fp32 I/O with d_k = 128.  Inputs as for gdn_fwd_chunked (the same validation rules, which
+ * with every gate (GDN_GATE_NONE, GDN_GATE_HEAD, GDN_GATE_KEY, GDN_GATE_HEAD_CONST);
+ * fp32 I/O with d_k = 128 only with the per-key-channel gate (GDN_ERR_UNSUPPORTED
+ * otherwise).  Inputs as for gdn_fwd_chunked (the same validation rules, which
  * this call repeats), plus the gradients of its outputs;
  * the forward is recomputed inside the call (chunk-entering states into the
  * workspace), so nothing of the forward call needs to be kept.  All arithmetic is
@@ -227,7 +227,8 @@ typedef struct {
   gdn_write write;
   const void *q, *k, *v;           /* as in gdn_fwd_args                          */
   const float *beta;               /* DELTA: [B, T, H]; ADD: NULL                 */
-  const float *log_alpha;          /* NONE: NULL; HEAD: [B, T, H]; HEAD_CONST: [H] */
+  const float *log_alpha;          /* NONE: NULL; HEAD: [B, T, H]; KEY: [B, T, H, d_k];
+                                      HEAD_CONST: [H]                             */
   const float *initial_state;      /* NULL (zeros) or [N, H, d_k, d_v]            */
   const int32_t *cu_seqlens;       /* NULL or [N + 1] int32 (device)              */
   const void *dout;                /* [B, T, H, d_v], dtype: gradient of o        */
@@ -235,7 +236,8 @@ typedef struct {
                                       the final state                             */
   void *dq, *dk, *dv;              /* out: [B, T, H, d_k] / [B, T, H, d_v], dtype */
   float *dbeta;                    /* out: DELTA: [B, T, H]; ADD: NULL            */
-  float *dlog_alpha;               /* out: HEAD: [B, T, H]; HEAD_CONST: [H] (the
+  float *dlog_alpha;               /* out: HEAD: [B, T, H]; KEY: [B, T, H, d_k];
+                                      HEAD_CONST: [H] (the
                                       sum over all tokens, written also when there
                                       are none); NONE: NULL                       */
   float *dinitial_state;           /* out: NULL or [N, H, d_k, d_v]               */
@@ -243,13 +245,18 @@ typedef struct {
   size_t workspace_bytes;
 } gdn_bwd_args;
 
-/* Bytes of device workspace gdn_bwd_chunked needs (0 for arguments it would reject):
- * with S = floor(B T / 64) + N chunk slots, the chunk-entering states (4 d_k d_v
- * bytes per slot and head), T of every chunk (delta write only: 16 KiB per slot and
- * head), the partial sums over value columns (d_v / 32 records of 4 (8192 + 128 d_k +
- * 192) bytes per slot and head) and, for the constant per-head decay, the per-token
- * decay gradients (4 bytes per token and head), each rounded up to 256 bytes.  Owned
- * by the caller; no initialisation needed. */
+/* Bytes of device workspace gdn_bwd_chunked needs (0 for arguments it would reject),
+ * with S = floor(B T / 64) + N chunk slots, each part rounded up to 256 bytes:
+ *  - no gate, one decay per (token, head), one constant decay per head: the chunk-
+ *    entering states (4 d_k d_v bytes per slot and head), T of every chunk (delta write
+ *    only: 16 KiB per slot and head), the partial sums over value columns (d_v / 32
+ *    records of 4 (8192 + 128 d_k + 192) bytes per slot and head) and, for the constant
+ *    per-head decay, the per-token decay gradients (4 bytes per token and head);
+ *  - one decay per key channel, per slot and head in fp32: the chunk-entering states and
+ *    chunk-end state gradients (d_k d_v each), dDelta (64 d_v), T and T^T (delta write)
+ *    and P^T (64 x 64 each), K e^G (delta write), K e^{g_C - G}, their transposes and
+ *    (Q e^G)^T (64 d_k each; K e^G's transpose for the delta write only), e^{g_C} (d_k).
+ * Owned by the caller; no initialisation needed. */
 size_t gdn_bwd_workspace_size(const gdn_bwd_args *args);
 
 /* Gradients: writes dq, dk, dv, dbeta (DELTA), dlog_alpha (a gate) and dinitial_state

@@ -298,7 +298,9 @@ def bwd_args(g, **kw):
 
 
 @pytest.mark.parametrize("change,status", [
-    (dict(gate=2, log_alpha=fake(4, 0), dlog_alpha=fake(10)), UNSUPPORTED),  # per-key gate
+    (dict(gate=2, log_alpha=fake(4, 0), dlog_alpha=fake(10)), WORKSPACE),    # per-key gate: valid
+    (dict(gate=2, log_alpha=fake(4, 0), dlog_alpha=fake(10), dtype=0), WORKSPACE),  # ... also fp32 at d_k 128
+    (dict(gate=2, log_alpha=fake(4, 0), dlog_alpha=None), INVALID),          # ... needs its gradient buffer
     (dict(gate=3, dlog_alpha=fake(10)), WORKSPACE),                           # constant gate: valid
     (dict(gate=3, dlog_alpha=None), INVALID),                                 # ... needs its [H] gradient
     (dict(write=1, beta=None, dbeta=None), WORKSPACE),                        # additive write: valid
@@ -334,6 +336,23 @@ def test_bwd_workspace_size(g):
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(add)) == expect - slots * 4 * 4096 * 4
     const = bwd_args(g, gate=3)
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(const)) == expect + 2 * 128 * 4 * 4
+
+
+def test_bwd_workspace_size_key_gate(g):
+    """The per-key-channel gate's backward workspace: with S = floor(B T / 64) + N chunk
+    slots, fp32 chunk states and chunk-end state gradients (d_k d_v per slot and head),
+    dDelta (64 d_v), T and T^T (delta write), P^T (64 x 64 each), K e^G (delta write), K
+    e^{g_C - G} and the three transposed operands (64 d_k each, K e^G's transpose only for
+    the delta write) and e^{g_C} (d_k), each rounded up to 256 bytes."""
+    up = lambda x: (x + 255) // 256 * 256
+    a = bwd_args(g, gate=2, log_alpha=fake(4, 0))
+    sh = ((2 * 128) // 64 + 2) * 4
+    dk = dv = 128
+    delta = [sh * dk * dv * 4] * 2 + [sh * 64 * dv * 4] + [sh * 4096 * 4] * 3 + [sh * 64 * dk * 4] * 5 + [sh * dk * 4]
+    assert g._lib.gdn_bwd_workspace_size(ctypes.byref(a)) == sum(up(x) for x in delta)
+    add = bwd_args(g, gate=2, log_alpha=fake(4, 0), write=1, beta=None, dbeta=None)
+    add_sizes = [sh * dk * dv * 4] * 2 + [sh * 64 * dv * 4] + [sh * 4096 * 4] + [sh * 64 * dk * 4] * 3 + [sh * dk * 4]
+    assert g._lib.gdn_bwd_workspace_size(ctypes.byref(add)) == sum(up(x) for x in add_sizes)
 
 
 def dplr_args(g, **kw):
