@@ -193,14 +193,17 @@ def fwd_dplr(q, k, v, a, b, log_alpha=None, initial_state=None, cu_seqlens=None,
              nthreads: int = 0, lib=None):
     """The diagonal-plus-low-rank transition M_t = Diag(alpha_t) M_{t-1} + b_t (a_t^T
     M_{t-1}) + k_t v_t^T, o_t = M_t^T q_t, over whole sequences.  q, k, a, b
-    [B,T,H,d_k], v [B,T,H,d_v], log_alpha None | [B,T,H] | [B,T,H,d_k]; other
-    arguments as for ``fwd``.  Returns (o, final_state) in fp64."""
+    [B,T,H,d_k], v [B,T,H,d_v], log_alpha None | [H] (one constant decay per head) |
+    [B,T,H] | [B,T,H,d_k]; other arguments as for ``fwd``.  Returns (o, final_state) in
+    fp64."""
     q, k, v, a, b = _f64(q), _f64(k), _f64(v), _f64(a), _f64(b)
     log_alpha, initial_state = _f64(log_alpha), _f64(initial_state)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if gate is None:
         gate = infer_gate(log_alpha, 3)
+    if gate == "const":
+        log_alpha, gate = _per_token(log_alpha, (B, T)), "head"
     if cu_seqlens is not None:
         cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64)
         start, lens = cu[:-1].copy(), np.diff(cu)

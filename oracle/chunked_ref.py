@@ -315,8 +315,10 @@ def chunked_bwd(q, k, v, beta, log_alpha, M0, dO, dMT, C=64, write="delta"):
 
 def chunk_step_dplr(q, k, v, a, b, g, M0):
     """One chunk of the diagonal-plus-low-rank transition with one decay per position
-    (g [C] log decays; zeros without a gate).  With u_j = a_j^T M_{j-1} (the rows U),
-    G the inclusive prefix of g and G_{-1} = 0:
+    (g [C] log decays; zeros without a gate) or one per position and key channel (g
+    [C,dk]: every exponential below is then per channel, inside the contractions over
+    the key channels).  With u_j = a_j^T M_{j-1} (the rows U), G the inclusive prefix of
+    g and G_{-1} = 0:
       (I - A_ab) U = diag(e^{G_{j-1}}) A M0 + A_ak V,
       A_ab[j,i] = (a_j . b_i) e^{G_{j-1} - G_i},  A_ak[j,i] = (a_j . k_i) e^{G_{j-1} - G_i}  (i < j)
       O   = diag(e^G) Q M0 + P_qb U + P_qk V,
@@ -326,6 +328,8 @@ def chunk_step_dplr(q, k, v, a, b, g, M0):
     C = q.shape[0]
     strict = np.tril(np.ones((C, C), dtype=bool), -1)
     incl = np.tril(np.ones((C, C), dtype=bool), 0)
+    if np.ndim(g) == 2:
+        return _chunk_step_dplr_key(q, k, v, a, b, np.asarray(g, dtype=np.float64), M0, strict, incl)
     G = np.cumsum(g)
     Gp = np.concatenate([[0.0], G[:-1]])  # G_{j-1}
     E1 = np.where(strict, np.exp(np.where(strict, Gp[:, None] - G[None, :], 0.0)), 0.0)
@@ -338,9 +342,30 @@ def chunk_step_dplr(q, k, v, a, b, g, M0):
     return O, MC
 
 
+def _chunk_step_dplr_key(q, k, v, a, b, g, M0, strict, incl):
+    """chunk_step_dplr with one decay per key channel: G [C,dk] the per-channel prefix,
+    Gp its shift (G_{j-1}, G_{-1} = 0), and with E1[j,i,c] = e^{Gp[j,c] - G[i,c]} (i < j)
+    and E2[r,i,c] = e^{G[r,c] - G[i,c]} (i <= r):
+      A_ab[j,i] = sum_c a_j[c] b_i[c] E1[j,i,c],  A_ak likewise with k,
+      (I - A_ab) U = (A * e^{Gp}) M0 + A_ak V,
+      O = (Q * e^G) M0 + P_qb U + P_qk V,  P_qb[r,i] = sum_c q_r[c] b_i[c] E2[r,i,c],
+      M_C = diag(e^{G_C}) M0 + (B * e^{G_C - G})^T U + (K * e^{G_C - G})^T V."""
+    G = np.cumsum(g, axis=0)
+    Gp = np.concatenate([np.zeros((1, G.shape[1])), G[:-1]])
+    E1 = np.exp(np.where(strict[:, :, None], Gp[:, None, :] - G[None, :, :], 0.0)) * strict[:, :, None]
+    E2 = np.exp(np.where(incl[:, :, None], G[:, None, :] - G[None, :, :], 0.0)) * incl[:, :, None]
+    Aab = np.einsum("jc,ic,jic->ji", a, b, E1)
+    Aak = np.einsum("jc,ic,jic->ji", a, k, E1)
+    U = np.linalg.solve(np.eye(q.shape[0]) - Aab, (a * np.exp(Gp)) @ M0 + Aak @ v)
+    O = (q * np.exp(G)) @ M0 + np.einsum("rc,ic,ric->ri", q, b, E2) @ U + np.einsum("rc,ic,ric->ri", q, k, E2) @ v
+    w = np.exp(G[-1][None, :] - G)
+    MC = np.exp(G[-1])[:, None] * M0 + (w * b).T @ U + (w * k).T @ v
+    return O, MC
+
+
 def chunked_dplr(q, k, v, a, b, log_alpha, M0, C=64):
     """The chunked form over one sequence (q, k, a, b [T,dk], v [T,dv], log_alpha None
-    | [T]); a partial last chunk is padded with zero rows and log alpha = 0."""
+    | [T] | [T,dk]); a partial last chunk is padded with zero rows and log alpha = 0."""
     Tn, dk_ = q.shape
     la = np.zeros(Tn) if log_alpha is None else log_alpha
     O = np.zeros((Tn, v.shape[1]))

@@ -71,8 +71,20 @@ def test_equals_dense_transition_products(gate):
     np.testing.assert_allclose(fs[0, 0], S.T, atol=1e-12, rtol=0)
 
 
+def test_constant_gate_is_per_token_broadcast():
+    """One constant decay per head ([H]) equals the same value given at every token."""
+    q, k, v, beta, la, s0 = case(2, 21, 3, 5, 4, "none", seed=11)
+    r = np.random.default_rng(12)
+    a, b = r.standard_normal(q.shape) * 0.4, r.standard_normal(q.shape) * 0.4
+    g = np.log(np.array([0.9, 0.75, 0.99]))
+    o1, f1 = oracle.fwd_dplr(q, k, v, a, b, g, s0)
+    o2, f2 = oracle.fwd_dplr(q, k, v, a, b, np.broadcast_to(g, (2, 21, 3)).copy(), s0)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(f1, f2)
+
+
 @pytest.mark.parametrize("C", [1, 5, 16, 64])
-@pytest.mark.parametrize("gate", ["none", "head"])
+@pytest.mark.parametrize("gate", ["none", "head", "key"])
 def test_chunked_form_equals_recurrence(C, gate):
     """The chunk equations (oracle/chunked_ref.py: chunk_step_dplr) that the GPU kernel
     implements, against the token recurrence."""
