@@ -89,7 +89,8 @@ class DplrArgs(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("a", ctypes.c_void_p),
                 ("b", ctypes.c_void_p), ("v", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
                 ("initial_state", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
-                ("o", ctypes.c_void_p), ("final_state", ctypes.c_void_p)]
+                ("o", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class DplrStepArgs(ctypes.Structure):
@@ -134,6 +135,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_fwd_dplr_decode.argtypes = [ctypes.POINTER(DplrDecodeArgs), ctypes.c_void_p]
     lib.gdn_fwd_dplr_step.restype = ctypes.c_int
     lib.gdn_fwd_dplr_step.argtypes = [ctypes.POINTER(DplrStepArgs), ctypes.c_void_p]
+    lib.gdn_dplr_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_dplr_workspace_size.argtypes = [ctypes.POINTER(DplrArgs)]
     lib.gdn_fwd_dplr.restype = ctypes.c_int
     lib.gdn_fwd_dplr.argtypes = [ctypes.POINTER(DplrArgs), ctypes.c_void_p]
     lib.gdn_status_str.restype = ctypes.c_char_p
@@ -453,14 +456,19 @@ def make_dplr_args(q, k, v, a, b, log_alpha, initial_state, cu_seqlens, o, final
     return DplrArgs(B=B, T=T, H=H, d_k=dk, d_v=v.shape[-1], chunk=chunk, N=N, dtype=_dtype_code(q),
                     gate=gate_code(log_alpha, 3), q=_ptr(q), k=_ptr(k), a=_ptr(a), b=_ptr(b), v=_ptr(v),
                     log_alpha=_ptr(log_alpha), initial_state=_ptr(initial_state),
-                    cu_seqlens=_ptr(cu_seqlens), o=_ptr(o), final_state=_ptr(final_state))
+                    cu_seqlens=_ptr(cu_seqlens), o=_ptr(o), final_state=_ptr(final_state),
+                    workspace=None, workspace_bytes=0)
+
+
+def dplr_workspace_size(args: DplrArgs) -> int:
+    return int(_lib.gdn_dplr_workspace_size(ctypes.byref(args)))
 
 
 class PreparedDplr:
     """A validated gdn_fwd_dplr call on fixed buffers (see PreparedFwd)."""
 
     def __init__(self, q, k, v, a, b, log_alpha=None, initial_state=None, cu_seqlens=None, out=None,
-                 final_state=None, output_final_state: bool = True, chunk: int = CHUNK):
+                 final_state=None, output_final_state: bool = True, chunk: int = CHUNK, workspace=None):
         import torch
         B, T, H, dk = q.shape
         N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
@@ -471,7 +479,13 @@ class PreparedDplr:
         fs = final_state if output_final_state else None
         check_dplr_tensors(q, k, v, a, b, log_alpha, initial_state, cu_seqlens, out, fs)
         self.args = make_dplr_args(q, k, v, a, b, log_alpha, initial_state, cu_seqlens, out, fs, chunk)
-        self._keep = (q, k, v, a, b, log_alpha, initial_state, cu_seqlens)
+        need = dplr_workspace_size(self.args)
+        self.own_workspace = None
+        if need:
+            if workspace is None or workspace.numel() < need:
+                workspace = self.own_workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            self.args.workspace, self.args.workspace_bytes = workspace.data_ptr(), workspace.numel()
+        self._keep = (q, k, v, a, b, log_alpha, initial_state, cu_seqlens, workspace)
         self.out, self.final_state = out, fs
         self._ref = ctypes.byref(self.args)
 
@@ -481,16 +495,21 @@ class PreparedDplr:
 
 
 def fwd_dplr(q, k, v, a, b, log_alpha=None, initial_state=None, cu_seqlens=None,
-             output_final_state: bool = True, chunk: int = CHUNK, out=None, final_state=None, stream=None):
+             output_final_state: bool = True, chunk: int = CHUNK, out=None, final_state=None, stream=None,
+             workspace=None):
     """Chunked forward of the diagonal-plus-low-rank transition (gdn_fwd_dplr):
     M_t = Diag(alpha_t) M_{t-1} + b_t (a_t^T M_{t-1}) + k_t v_t^T, o_t = M_t^T q_t.
 
     q, k, a, b [B,T,H,d_k] and v [B,T,H,d_v] (one dtype, bf16 or fp32); log_alpha None
-    | [B,T,H] fp32; initial_state, cu_seqlens as for fwd_chunked.  Returns (o,
-    final_state or None), asynchronous on the current (or given) stream."""
+    | [H] (constant per head) | [B,T,H] | [B,T,H,d_k] (one decay per key channel) fp32;
+    initial_state, cu_seqlens as for fwd_chunked; workspace (uint8, per-channel gate
+    only) allocated here when not given.  Returns (o, final_state or None),
+    asynchronous on the current (or given) stream."""
     p = PreparedDplr(q, k, v, a, b, log_alpha, initial_state, cu_seqlens, out, final_state,
-                     output_final_state, chunk)
-    return p.launch(stream)
+                     output_final_state, chunk, workspace)
+    res = p.launch(stream)
+    _keep_for_stream(p.own_workspace, stream)
+    return res
 
 
 def dplr_step(q, k, v, a, b, log_alpha, state, out=None, stream=None):

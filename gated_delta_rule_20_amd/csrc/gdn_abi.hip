@@ -177,7 +177,6 @@ int check_dplr(const gdn_dplr_args *a) {
   f.initial_state = a->initial_state; f.cu_seqlens = a->cu_seqlens; f.o = a->o; f.final_state = a->final_state;
   const int st = check_fwd(&f);
   if (st != GDN_OK) return st;
-  if (a->gate != GDN_GATE_NONE && a->gate != GDN_GATE_HEAD) return GDN_ERR_UNSUPPORTED;
   if (a->dtype == GDN_F32 && a->d_k != 64) return GDN_ERR_UNSUPPORTED;
   if ((long)a->B * a->T > 0 && (!a->a || !a->b)) return GDN_ERR_INVALID_ARG;
   if ((a->a && !aligned(a->a, 16)) || (a->b && !aligned(a->b, 16))) return GDN_ERR_INVALID_ARG;
@@ -216,6 +215,28 @@ int check_dplr_decode(const gdn_dplr_decode_args *a) {
     if (p && !aligned(p, 4)) return GDN_ERR_INVALID_ARG;
   if (!aligned(a->state_pool, 16)) return GDN_ERR_INVALID_ARG;
   return GDN_OK;
+}
+
+// The per-key-channel gate of the diagonal-plus-low-rank forward: the fp32 arrays of
+// DplrKeyParams, in this order (tm, aak, pqb, pqk, at, qg, bhT, khT, gam)
+struct DplrKeyLayout {
+  long slots;
+  size_t sz[9];
+  size_t total() const {
+    size_t t = 0;
+    for (size_t x : sz) t += x;
+    return t;
+  }
+};
+DplrKeyLayout dplr_key_layout(const gdn_dplr_args *a) {
+  DplrKeyLayout L{};
+  if (a->gate != GDN_GATE_KEY) return L;
+  L.slots = gdn::key_slots((long)a->B * a->T, a->N);
+  const size_t sh = (size_t)L.slots * a->H, dk = a->d_k;
+  const size_t sizes[9] = {sh * 4096 * 4, sh * 4096 * 4, sh * 4096 * 4, sh * 4096 * 4, sh * 64 * dk * 4,
+                           sh * 64 * dk * 4, sh * dk * 64 * 4, sh * dk * 64 * 4, sh * dk * 4};
+  for (int i = 0; i < 9; ++i) L.sz[i] = align256(sizes[i]);
+  return L;
 }
 
 struct BwdLayout {
@@ -598,9 +619,46 @@ int gdn_fwd_decode(const gdn_decode_args *a, void *hip_stream) {
   return GDN_OK;
 }
 
+size_t gdn_dplr_workspace_size(const gdn_dplr_args *a) {
+  if (check_dplr(a) != GDN_OK) return 0;
+  return dplr_key_layout(a).total();
+}
+
 int gdn_fwd_dplr(const gdn_dplr_args *a, void *hip_stream) {
   const int st = check_dplr(a);
   if (st != GDN_OK) return st;
+  if (a->gate == GDN_GATE_KEY) {
+    const DplrKeyLayout L = dplr_key_layout(a);
+    const size_t need = L.total();
+    if (need && (!a->workspace || a->workspace_bytes < need || !aligned(a->workspace, 256)))
+      return GDN_ERR_WORKSPACE;
+    if (a->N == 0) return GDN_OK;
+    gdn::DplrKeyParams p;
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.a = a->a;
+    p.b = a->b;
+    p.log_alpha = a->log_alpha;
+    p.init_state = a->initial_state;
+    p.final_state = a->final_state;
+    p.o = a->o;
+    p.cu_seqlens = a->cu_seqlens;
+    float **arr[9] = {&p.tm, &p.aak, &p.pqb, &p.pqk, &p.at, &p.qg, &p.bhT, &p.khT, &p.gam};
+    char *ws = (char *)a->workspace;
+    for (int i = 0; i < 9; ++i) {
+      *arr[i] = (float *)ws;
+      ws += L.sz[i];
+    }
+    p.N = a->N;
+    p.H = a->H;
+    p.T = a->T;
+    p.dv = a->d_v;
+    p.slots = (long)a->B * a->T > 0 ? L.slots : 0;
+    if (gdn::launch_dplr_key(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, (hipStream_t)hip_stream) != hipSuccess)
+      return GDN_ERR_HIP;
+    return GDN_OK;
+  }
   if (a->N == 0) return GDN_OK;
   gdn::DplrParams p;
   p.q = a->q;
@@ -617,7 +675,8 @@ int gdn_fwd_dplr(const gdn_dplr_args *a, void *hip_stream) {
   p.H = a->H;
   p.T = a->T;
   p.dv = a->d_v;
-  if (gdn::launch_dplr(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, (int)a->gate, (hipStream_t)hip_stream) !=
+  p.la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
+  if (gdn::launch_dplr(p, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, kernel_gate(a->gate), (hipStream_t)hip_stream) !=
       hipSuccess)
     return GDN_ERR_HIP;
   return GDN_OK;

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(DNT, 1) void dplr_fwd_kernel(DplrParams p) {
       const int r = i / DVB, j = i % DVB;
       Vb[r * DSV + j] = r < nv ? to_f(((const E *)p.v)[((tb + r) * H + h) * dv + col0 + j]) : 0.f;
     }
-    if (tid < DC) gs[tid] = (GATE == GATE_HEAD && tid < nv) ? p.log_alpha[(tb + tid) * H + h] : 0.f;
+    if (tid < DC) gs[tid] = (GATE == GATE_HEAD && tid < nv) ? p.log_alpha[(tb + tid) * p.la_stride + h] : 0.f;
     __syncthreads();
     if (wave == 0) {  // decay prefix: e^G, e^{G_{j-1}}, e^{G_C - G}, e^{G_C}
       float g = gs[lane];
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
       const int r = min(tid / 4, last), g = tid % 4;
       pv = *(const u32x4 *)((const bf16 *)p.v + ((tbc + r) * H + h) * dv + col0 + 8 * g);
     }
-    if (GATE == GATE_HEAD && tid < DC) pl = p.log_alpha[(tbc + min(tid, last)) * H + h];
+    if (GATE == GATE_HEAD && tid < DC) pl = p.log_alpha[(tbc + min(tid, last)) * p.la_stride + h];
   };
   if (nchunks > 0) fetch(0);
 

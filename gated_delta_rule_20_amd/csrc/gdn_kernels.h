@@ -117,14 +117,32 @@ hipError_t launch_bwd_key(const BwdKeyParams &p, int dtype, int dk, bool add, hi
 // Forward of the diagonal-plus-low-rank transition (no gate or the scalar gate).
 struct DplrParams {
   const void *q, *k, *v, *a, *b;  // [tokens, H, d_k] (v: d_v), I/O dtype
-  const float *log_alpha;         // NULL | [tokens, H]
+  const float *log_alpha;         // NULL | [tokens, H] (read at token * la_stride + h)
   const float *init_state;        // NULL | [N, H, d_k, d_v]
   float *final_state;             // NULL | [N, H, d_k, d_v]
   void *o;                        // [tokens, H, d_v]
   const int32_t *cu_seqlens;      // NULL (batch) | [N + 1]
-  int N, H, T, dv;
+  int N, H, T, dv, la_stride;
 };
 hipError_t launch_dplr(const DplrParams &p, int dtype, int dk, int gate, hipStream_t stream);
+// The same transition with one decay per key channel: a parallel preparation per
+// (chunk, head) into the fp32 workspace arrays below (slot of chunk c as for key_slots),
+// then one serial pass per (sequence, head, 32 value columns).
+struct DplrKeyParams {
+  const void *q, *k, *v, *a, *b;  // [tokens, H, d_k] (v: d_v), I/O dtype
+  const float *log_alpha;         // [tokens, H, d_k]
+  const float *init_state;        // NULL | [N, H, d_k, d_v]
+  float *final_state;             // NULL | [N, H, d_k, d_v]
+  void *o;                        // [tokens, H, d_v]
+  const int32_t *cu_seqlens;      // NULL (batch) | [N + 1]
+  float *tm, *aak, *pqb, *pqk;    // [slots, H, 64, 64] each
+  float *at, *qg;                 // [slots, H, 64, d_k]
+  float *bhT, *khT;               // [slots, H, d_k, 64]
+  float *gam;                     // [slots, H, d_k]
+  int N, H, T, dv;
+  long slots;
+};
+hipError_t launch_dplr_key(const DplrKeyParams &p, int dtype, int dk, hipStream_t stream);
 // One decode token per stream of the diagonal-plus-low-rank transition, state in place.
 struct DplrStepParams {
   const void *q, *k, *v, *a, *b;  // [N, H, d_k] (v: d_v), I/O dtype

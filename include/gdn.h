@@ -274,26 +274,40 @@ int gdn_bwd_chunked(const gdn_bwd_args *args, void *hip_stream);
  * a_t = -alpha_t beta_t k_t and v scaled by beta_t it is the (gated) delta rule of
  * gdn_fwd_chunked; with a_t = 0 it is its additive write.  Computed chunk by chunk
  * (C = 64; the pages' chunkwise algorithm of sec. 5, with the within-chunk low-rank
- * products solved in UT form as for the delta rule).  Supported: GDN_GATE_NONE and
- * GDN_GATE_HEAD (other gates return GDN_ERR_UNSUPPORTED); bf16 with d_k 64 or 128,
- * fp32 with d_k 64; d_v 64 or 128.  Batch and varlen modes, partial chunks, empty
- * sequences, alignment and validation as for gdn_fwd_chunked.  No workspace.
+ * products solved in UT form as for the delta rule).  Every gate: GDN_GATE_NONE,
+ * GDN_GATE_HEAD, GDN_GATE_HEAD_CONST (one log alpha per head for every token) and
+ * GDN_GATE_KEY (one log alpha per key channel, alpha_t a vector as in sec. 3 item 5);
+ * bf16 with d_k 64 or 128, fp32 with d_k 64 (GDN_ERR_UNSUPPORTED otherwise); d_v 64
+ * or 128.  Batch and varlen modes, partial chunks, empty sequences, alignment and
+ * validation as for gdn_fwd_chunked.  GDN_GATE_KEY needs a workspace of
+ * gdn_dplr_workspace_size bytes (256-byte aligned, else GDN_ERR_WORKSPACE); the other
+ * gates need none and ignore the two workspace fields.
  * The recurrence is stable only when the transitions are (e.g. a = -kappa,
  * b = kappa * w with |kappa| = 1 and 0 <= w <= 1); the library does not check this.
  */
 typedef struct {
   int B, T, H, d_k, d_v, chunk, N; /* as in gdn_fwd_args                          */
   gdn_dtype dtype;                 /* dtype of q, k, v, a, b, o                   */
-  gdn_gate gate;                   /* GDN_GATE_NONE or GDN_GATE_HEAD              */
+  gdn_gate gate;                   /* any gdn_gate                                */
   const void *q, *k, *a, *b;       /* [B, T, H, d_k], dtype                       */
   const void *v;                   /* [B, T, H, d_v], dtype                       */
-  const float *log_alpha;          /* NONE: NULL; HEAD: [B, T, H] fp32            */
+  const float *log_alpha;          /* NONE: NULL; HEAD: [B, T, H]; HEAD_CONST: [H];
+                                      KEY: [B, T, H, d_k]; fp32                   */
   const float *initial_state;      /* NULL (zeros) or [N, H, d_k, d_v] fp32       */
   const int32_t *cu_seqlens;       /* NULL or [N + 1] int32 (device)              */
   void *o;                         /* out: [B, T, H, d_v], dtype                  */
   float *final_state;              /* out: NULL or [N, H, d_k, d_v]; may alias
                                       initial_state                               */
+  void *workspace;                 /* GDN_GATE_KEY: device scratch, see below     */
+  size_t workspace_bytes;
 } gdn_dplr_args;
+
+/* Workspace bytes gdn_fwd_dplr needs: 0 for every gate but GDN_GATE_KEY (and for
+ * invalid arguments).  With the per-channel gate, per chunk slot (floor(B T / 64) + N
+ * slots) and head: (I - A_ab)^-1, A_ak, P_qb, P_qk (64 x 64 each), A e^{G_{j-1}} and
+ * Q e^G (64 d_k each), (B e^{G_C - G})^T and (K e^{G_C - G})^T (d_k 64 each) and
+ * e^{G_C} (d_k), fp32.  Owned by the caller; no initialisation needed. */
+size_t gdn_dplr_workspace_size(const gdn_dplr_args *args);
 
 /* Diagonal-plus-low-rank forward: writes o (and final_state when non-NULL). */
 int gdn_fwd_dplr(const gdn_dplr_args *args, void *hip_stream);

@@ -49,9 +49,9 @@ def fwd(g, a):
 
 
 def test_header_declares_the_boundary(g):
-    assert g.header_functions() == ["gdn_bwd_chunked", "gdn_bwd_workspace_size", "gdn_fwd_chunked",
-                                    "gdn_fwd_chunked_static", "gdn_fwd_decode", "gdn_fwd_dplr", "gdn_fwd_dplr_decode", "gdn_fwd_dplr_step",
-                                    "gdn_fwd_recurrent_step",
+    assert g.header_functions() == ["gdn_bwd_chunked", "gdn_bwd_workspace_size",
+                                    "gdn_dplr_workspace_size", "gdn_fwd_chunked", "gdn_fwd_chunked_static", "gdn_fwd_decode",
+                                    "gdn_fwd_dplr", "gdn_fwd_dplr_decode", "gdn_fwd_dplr_step", "gdn_fwd_recurrent_step",
                                     "gdn_fwd_workspace_size", "gdn_status_str", "gdn_version"]
 
 
@@ -364,8 +364,13 @@ def dplr_args(g, **kw):
 
 
 @pytest.mark.parametrize("change,status", [
-    (dict(gate=2), UNSUPPORTED),                  # per-key-channel gate
-    (dict(gate=3), UNSUPPORTED),                  # constant per-head gate
+    (dict(gate=2), WORKSPACE),                    # per-key-channel gate: needs a workspace
+    (dict(gate=2, workspace=fake(8), workspace_bytes=4096), WORKSPACE),   # too small
+    (dict(gate=2, workspace=fake(8, 16), workspace_bytes=1 << 30), WORKSPACE),  # 256-byte alignment
+    (dict(gate=2, dtype=0, d_k=128), UNSUPPORTED),  # fp32 takes d_k = 64 only, every gate
+    (dict(gate=2, log_alpha=fake(4, 4)), INVALID),  # per-channel decays: 16-byte alignment
+    (dict(gate=3, B=0, N=0), OK),                 # constant per-head gate, nothing to do
+    (dict(gate=2, B=0, N=0), OK),                 # per-channel gate, nothing to do: no workspace
     (dict(gate=7), INVALID),
     (dict(a=None), INVALID),
     (dict(b=None), INVALID),
@@ -381,6 +386,17 @@ def dplr_args(g, **kw):
 def test_dplr_host_validation(g, change, status):
     assert g._lib.gdn_fwd_dplr(ctypes.byref(dplr_args(g, **change)), None) == status
     assert g._lib.gdn_fwd_dplr(None, None) == INVALID
+
+
+def test_dplr_workspace_size(g):
+    # per chunk slot (floor(B T / 64) + N = 6 slots) and head: four 64 x 64 fp32 tiles,
+    # four 64 x d_k arrays and e^{g_C} (d_k); no workspace for the scalar gates
+    sh = (2 * 128 // 64 + 2) * 4
+    key = dplr_args(g, gate=g.GDN_GATE_KEY)
+    assert g._lib.gdn_dplr_workspace_size(ctypes.byref(key)) == sh * (4 * 4096 + 4 * 64 * 128 + 128) * 4
+    for gate in (g.GDN_GATE_HEAD, g.GDN_GATE_HEAD_CONST):
+        assert g._lib.gdn_dplr_workspace_size(ctypes.byref(dplr_args(g, gate=gate))) == 0
+    assert g._lib.gdn_dplr_workspace_size(ctypes.byref(dplr_args(g, gate=g.GDN_GATE_KEY, chunk=32))) == 0
 
 
 def test_binding_rejects_bad_dplr_tensors(g):

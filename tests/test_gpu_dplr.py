@@ -1,7 +1,8 @@
 """GPU parity of the diagonal-plus-low-rank transition, the chunked forward
 (gdn_fwd_dplr), the decode step (gdn_fwd_dplr_step) and the pooled decode
 (gdn_fwd_dplr_decode), through the C ABI, against the
-fp64 oracle (oracle.fwd_dplr, the token recurrence).
+fp64 oracle (oracle.fwd_dplr, the token recurrence), for every gate: none, one decay
+per token and head, one per key channel and a constant one per head.
 
 Metric: max |x - x_ref| / max |x_ref| per output tensor; 2e-2 for bf16 inputs, 1e-4
 for the fp32 mode.  The oracle sees the same (rounded) inputs.  Inputs: synth's
@@ -50,24 +51,68 @@ def run(gdn, inp, tol=None, **kw):
     return o, fs
 
 
+def chunk_case(B, T, H, dk, dv, gate, dtype, seed, lengths=None):
+    """dplr_inputs for gate none | head | key | const (RetNet's per-head decays)."""
+    inp = synth.dplr_inputs(B, T, H, dk, dv, "head" if gate == "const" else gate, dtype, seed=seed,
+                            state_std=0.05, lengths=lengths)
+    if gate == "const":
+        inp["log_alpha"] = synth.retnet_log_gamma(H)
+    return inp
+
+
+GATES = ["none", "head", "key", "const"]
+
+
 @pytest.mark.parametrize("T", [1, 64, 130])
-@pytest.mark.parametrize("gate", ["none", "head"])
+@pytest.mark.parametrize("gate", GATES)
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64)])
 def test_dplr_bf16(gdn, gate, T, dk, dv):
-    run(gdn, synth.dplr_inputs(2, T, 3, dk, dv, gate, "bf16", seed=T + dk + dv, state_std=0.05))
+    run(gdn, chunk_case(2, T, 3, dk, dv, gate, "bf16", seed=T + dk + dv))
 
 
-@pytest.mark.parametrize("gate", ["none", "head"])
+@pytest.mark.parametrize("gate", GATES)
 @pytest.mark.parametrize("dv", [64, 128])
 def test_dplr_fp32(gdn, gate, dv):
-    run(gdn, synth.dplr_inputs(2, 150, 2, 64, dv, gate, "f32", seed=7 + dv, state_std=0.05))
+    run(gdn, chunk_case(2, 150, 2, 64, dv, gate, "f32", seed=7 + dv))
 
 
-@pytest.mark.parametrize("gate", ["none", "head"])
+@pytest.mark.parametrize("gate", GATES)
 def test_dplr_varlen(gdn, gate):
     """Packed sequences with an empty one and ragged tails."""
-    run(gdn, synth.dplr_inputs(1, None, 4, 128, 128, gate, "bf16", seed=8, state_std=0.05,
-                               lengths=[1, 200, 64, 0, 77, 129]))
+    run(gdn, chunk_case(1, None, 4, 128, 128, gate, "bf16", seed=8, lengths=[1, 200, 64, 0, 77, 129]))
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_dplr_key_strong_decay(gdn, dtype, dk):
+    """Per-channel log decays near -5 per token (about -350 per chunk) on half the
+    channels, near 0 on the rest: every split decay factor stays finite and the
+    result matches the recurrence."""
+    inp = chunk_case(2, 200, 2, dk, 128, "key", dtype, seed=41)
+    la = inp["log_alpha"]
+    g = torch.Generator().manual_seed(3)
+    strong = torch.full_like(la, -5.0) + 0.5 * torch.rand(la.shape, generator=g)
+    inp["log_alpha"] = torch.where(torch.arange(dk) % 2 == 0, strong, -0.01 * torch.rand(la.shape, generator=g))
+    run(gdn, inp)
+
+
+def test_dplr_key_varlen_equals_separate_runs(gdn):
+    """Each packed sequence gives bit for bit what it gives alone, with a caller
+    workspace reused across the calls."""
+    lengths = [70, 5, 129]
+    inp = chunk_case(1, None, 2, 128, 128, "key", "bf16", seed=9, lengths=lengths)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    o, fs = gdn.fwd_dplr(d["q"], d["k"], d["v"], d["a"], d["b"], d["log_alpha"], d["initial_state"],
+                         d["cu_seqlens"], workspace=ws)
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(len(lengths)):
+        sl = slice(cu[n], cu[n + 1])
+        cut = lambda x: x[:, sl].contiguous()
+        o1, f1 = gdn.fwd_dplr(cut(d["q"]), cut(d["k"]), cut(d["v"]), cut(d["a"]), cut(d["b"]),
+                              cut(d["log_alpha"]), d["initial_state"][n:n + 1].contiguous(), workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o[:, sl]), n
+        assert torch.equal(f1[0], fs[n]), n
 
 
 def test_dplr_full_replace(gdn):
@@ -98,6 +143,13 @@ def test_dplr_empty_and_aliased_state(gdn):
 def test_dplr_workload_full_size(gdn):
     """The 350M-class shape (B16, T2048, H8, d128), every output against the oracle."""
     run(gdn, synth.workload_inputs("dplr-bf16-B16-T2048-H8-d128"))
+
+
+@pytest.mark.parametrize("gate", ["key", "const"])
+def test_dplr_full_size_other_gates(gdn, gate):
+    """The same shape with one decay per key channel and with a constant decay per
+    head, every output against the oracle."""
+    run(gdn, chunk_case(16, 2048, 8, 128, 128, gate, "bf16", seed=1009 + len(gate)))
 
 
 def step_case(N, H, dk, dv, gate, dtype, seed, T=1):
