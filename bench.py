@@ -571,7 +571,7 @@ def main():
         for name in ["gdn-bf16-B4-T2048-H8-d128", "kda-bf16-B2-T16384-H16-d128",
                      "gdn-varlen-bf16-N32-H16-d128", "deltanet-fp32-B1-T256-H2-d64",
                      "retnet-bf16-B16-T2048-H8-d128", "gla-bf16-B2-T16384-H16-d128",
-                     "dplr-bf16-B16-T2048-H8-d128"]:
+                     "dplr-bf16-B16-T2048-H8-d128", "dplr-key-bf16-B16-T2048-H8-d128"]:
             try:
                 r, winp, wsets = bench_workload(gdn, name, max(5, args.steps // 5), None)
                 if not args.no_cpu:

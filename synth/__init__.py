@@ -52,6 +52,10 @@ WORKLOADS = {
     "dplr-bf16-B16-T2048-H8-d128": dict(
         B=16, T=2048, H=8, dk=128, dv=128, gate="head", write="dplr", dtype="bf16", state_std=0.02,
         seed=1007),
+    # ... and with one decay per key channel (the page's Diag(alpha_t) + a b^T)
+    "dplr-key-bf16-B16-T2048-H8-d128": dict(
+        B=16, T=2048, H=8, dk=128, dv=128, gate="key", write="dplr", dtype="bf16", state_std=0.02,
+        seed=1008),
 }
 
 CHUNK = 64
