@@ -217,7 +217,7 @@ int check_dplr_decode(const gdn_dplr_decode_args *a) {
   return GDN_OK;
 }
 
-// The per-key-channel gate of the diagonal-plus-low-rank forward: the fp32 arrays of
+// The per-key-channel gate of the diagonal-plus-low-rank forward: the arrays of
 // DplrKeyParams, in this order (tm, aak, pqb, pqk, at, qg, bhT, khT, gam)
 struct DplrKeyLayout {
   long slots;
@@ -644,12 +644,13 @@ int gdn_fwd_dplr(const gdn_dplr_args *a, void *hip_stream) {
     p.final_state = a->final_state;
     p.o = a->o;
     p.cu_seqlens = a->cu_seqlens;
-    float **arr[9] = {&p.tm, &p.aak, &p.pqb, &p.pqk, &p.at, &p.qg, &p.bhT, &p.khT, &p.gam};
+    __bf16 **arr[8] = {&p.tm, &p.aak, &p.pqb, &p.pqk, &p.at, &p.qg, &p.bhT, &p.khT};
     char *ws = (char *)a->workspace;
-    for (int i = 0; i < 9; ++i) {
-      *arr[i] = (float *)ws;
+    for (int i = 0; i < 8; ++i) {
+      *arr[i] = (__bf16 *)ws;
       ws += L.sz[i];
     }
+    p.gam = (float *)ws;
     p.N = a->N;
     p.H = a->H;
     p.T = a->T;

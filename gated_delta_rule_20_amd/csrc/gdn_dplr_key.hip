@@ -16,13 +16,21 @@
 // block a (e^{x[r] - G[m]} on the row operand, e^{G[m] - G[i]} on the column operand):
 // no factor exceeds the decay accumulated over eight tokens.
 //
-// Two launches: dplrk_prep_kernel (one workgroup per (chunk, head), fully parallel)
-// writes the chunk's fp32 operands to the caller's workspace -- (I - A_ab)^-1, A_ak,
-// P_qb, P_qk, A e^{Gp}, Q e^G (row-major), (B e^{G_C - G})^T, (K e^{G_C - G})^T
-// (channel-major) and e^{G_C}; dplrk_state_kernel (one workgroup per (sequence, head,
-// 32 value columns)) walks the chunks in order with the fp32 state block in LDS.
-// Products run on the bf16 matrix cores with every fp32 operand split into hi + lo bf16
-// terms (about 2^-17 relative error per product); accumulation in fp32.
+// Two launches:
+//  1. dplrk_prep_kernel, one workgroup per (chunk, head), fully parallel: the Gram
+//     tiles, T = (I - A_ab)^-1 (blocked: substitution of the diagonal blocks, block
+//     substitution of the rest on the matrix cores), and every state-independent
+//     operand of the chunk into the caller's workspace, each already split into a hi
+//     and a lo bf16 half (row-major, so that a matrix-core A fragment is two 16-byte
+//     loads and needs no arithmetic): T, A_ak, P_qb, P_qk (64 x 64), A e^{Gp} and
+//     Q e^G (64 x d_k), (B e^{G_C - G})^T and (K e^{G_C - G})^T (d_k x 64); e^{G_C} in fp32.
+//  2. dplrk_state_kernel, one workgroup per (sequence, head, 32 value columns), chunks
+//     in order.  The fp32 state block stays in the matrix-core accumulators of its four
+//     waves (d_k / 4 key rows each) for the whole sequence; its split bf16 copy, V, R
+//     and U sit transposed in LDS so that every B fragment is two 16-byte reads.
+// Products run on the bf16 matrix cores with every fp32 operand a hi + lo pair (about
+// 2^-17 relative error per product); bf16 inputs (v) are taken exactly; accumulation
+// in fp32.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 #include "gdn_tile.h"
@@ -32,16 +40,18 @@ namespace gdn {
 namespace {
 
 constexpr int KC = 64;
-constexpr int KBV = 32;
-constexpr int SV = KBV + 4;
-constexpr int SC = KC + 1;
+constexpr int KBV = 32;     // value columns per workgroup of the state pass
+constexpr int SC = KC + 1;  // fp32 pitch of 64-column tiles in LDS
+constexpr int PV = KC + 8;  // bf16 pitch of the transposed 64-row operands (V, R, U)
 
+// One 16x16 tile over k in [0, K) from fragment loaders (steps from k0 = kend on are
+// known zeros of a triangular operand and skipped; kend wave-uniform).
 template <int K, class FA, class FB>
-__device__ __forceinline__ f32x4 dprod(FA fa, FB fb, int kbeg = 0, int kend = K) {
+__device__ __forceinline__ f32x4 dprod(FA fa, FB fb, int kend = K) {
   f32x4 acc = zero4();
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += 32)
-    if (k0 + 32 > kbeg && k0 < kend) acc = mm(split8(fa(k0)), split8(fb(k0)), acc);
+    if (k0 < kend) acc = mm(fa(k0), fb(k0), acc);
   return acc;
 }
 
@@ -76,16 +86,26 @@ __device__ __forceinline__ bool slot_chunk_d(const DplrKeyParams &p, long slot, 
   return true;
 }
 
+// The hi half of slot-head sh's copy of a (rows x cols) split matrix; its lo half
+// follows at + rows * cols.
+__device__ __forceinline__ bf16 *split_hi(bf16 *base, size_t sh, int rows, int cols) {
+  return base + sh * 2 * (size_t)rows * cols;
+}
+
 template <typename E, int DK>
 __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
   constexpr int SE = DK + 8;  // element pitch of the staged inputs (rows 16-byte aligned)
   constexpr int SG = DK + 4;
+  constexpr int NP = 256 / DK, RP = KC / NP;  // prefix: parts per channel, rows per part
   __shared__ __align__(16) E As[KC * SE];
   __shared__ __align__(16) E Bs[KC * SE];
   __shared__ __align__(16) E Ks[KC * SE];
   __shared__ __align__(16) E Qs[KC * SE];
   __shared__ __align__(16) float Gs[KC * SG];
   __shared__ float Ab[KC * SC];  // A_ab
+  __shared__ float Tb[KC * SC];  // T
+  __shared__ float ys[3 * 16 * 17];
+  __shared__ float tot[NP][DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H;
@@ -95,38 +115,92 @@ __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
   int nv;
   if (!slot_chunk_d(p, slot, tb, nv)) return;
   const size_t sh = (size_t)slot * H + h;
-  for (int i = tid; i < KC * DK; i += 256) {
-    const int r = i / DK, d = i % DK;
-    const size_t o = ((size_t)(tb + r) * H + h) * DK + d;
-    const bool in = r < nv;
-    As[r * SE + d] = in ? ((const E *)p.a)[o] : to_e<E>(0.f);
-    Bs[r * SE + d] = in ? ((const E *)p.b)[o] : to_e<E>(0.f);
-    Ks[r * SE + d] = in ? ((const E *)p.k)[o] : to_e<E>(0.f);
-    Qs[r * SE + d] = in ? ((const E *)p.q)[o] : to_e<E>(0.f);
-    Gs[r * SG + d] = in ? p.log_alpha[o] : 0.f;
-  }
-  for (int i = tid; i < KC * SC; i += 256) Ab[i] = 0.f;
-  __syncthreads();
-  if (tid < DK) {
-    float g = 0.f;
-    for (int r = 0; r < KC; ++r) {
-      g += Gs[r * SG + tid];
-      Gs[r * SG + tid] = g;
+  {  // 16-byte loads, all in flight before the LDS stores (rows past the end are zero)
+    constexpr int VE = 16 / (int)sizeof(E), PR = DK / VE, NI = KC * PR / 256;  // inputs
+    constexpr int PG = DK / 4, NG = KC * PG / 256;                             // log alpha
+    const E *src[4] = {(const E *)p.a, (const E *)p.b, (const E *)p.k, (const E *)p.q};
+    E *dst[4] = {As, Bs, Ks, Qs};
+    u32x4 x[4][NI], y[NG];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int pc = tid + 256 * u, r = pc / PR, g = pc % PR;
+      const size_t o = ((size_t)(tb + r) * H + h) * DK + g * VE;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) x[a][u] = r < nv ? *(const u32x4 *)(src[a] + o) : (u32x4){0u, 0u, 0u, 0u};
     }
-    p.gam[sh * DK + tid] = __expf(g);
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int pc = tid + 256 * u, r = pc / PG, g = pc % PG;
+      y[u] = r < nv ? *(const u32x4 *)(p.log_alpha + ((size_t)(tb + r) * H + h) * DK + 4 * g)
+                    : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int pc = tid + 256 * u, r = pc / PR, g = pc % PR;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) *(u32x4 *)(dst[a] + r * SE + g * VE) = x[a][u];
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int pc = tid + 256 * u, r = pc / PG, g = pc % PG;
+      *(u32x4 *)(Gs + r * SG + 4 * g) = y[u];
+    }
+  }
+  __syncthreads();
+  {  // per-channel inclusive prefix: NP parts of RP rows per channel, then the offsets
+    const int d = tid % DK, q = tid / DK;
+    float g = 0.f;
+    for (int r = q * RP; r < (q + 1) * RP; ++r) {
+      g += Gs[r * SG + d];
+      Gs[r * SG + d] = g;
+    }
+    tot[q][d] = g;
+    __syncthreads();
+    float off = 0.f;
+    for (int u = 0; u < q; ++u) off += tot[u][d];
+    if (q > 0)
+      for (int r = q * RP; r < (q + 1) * RP; ++r) Gs[r * SG + d] += off;
   }
   __syncthreads();
   auto gp = [&](int j, int c) { return j > 0 ? Gs[(j - 1) * SG + c] : 0.f; };
-  for (int i = tid; i < KC * DK; i += 256) {
-    const int r = i / DK, d = i % DK;
-    const float g = Gs[r * SG + d], gC = Gs[(KC - 1) * SG + d], et = __expf(gC - g);
-    p.at[(sh * KC + r) * DK + d] = to_f(As[r * SE + d]) * __expf(gp(r, d));
-    p.qg[(sh * KC + r) * DK + d] = to_f(Qs[r * SE + d]) * __expf(g);
-    p.bhT[(sh * DK + d) * KC + r] = to_f(Bs[r * SE + d]) * et;
-    p.khT[(sh * DK + d) * KC + r] = to_f(Ks[r * SE + d]) * et;
+  if (tid < DK) p.gam[sh * DK + tid] = __expf(Gs[(KC - 1) * SG + tid]);
+  {  // A e^{Gp} and Q e^G (row-major), the write weights (channel-major), split; each
+     // thread forms 8 consecutive elements and stores each half with one 16-byte store
+    bf16 *ath = split_hi(p.at, sh, KC, DK), *qgh = split_hi(p.qg, sh, KC, DK);
+    for (int i = 8 * tid; i < KC * DK; i += 8 * 256) {
+      const int r = i / DK, d = i % DK;
+      f32x8 fa, fq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        fa[e] = to_f(As[r * SE + d + e]) * __expf(gp(r, d + e));
+        fq[e] = to_f(Qs[r * SE + d + e]) * __expf(Gs[r * SG + d + e]);
+      }
+      const Split sa = split8(fa), sq = split8(fq);
+      *(bf16x8 *)(ath + i) = sa.hi;
+      *(bf16x8 *)(ath + KC * DK + i) = sa.lo;
+      *(bf16x8 *)(qgh + i) = sq.hi;
+      *(bf16x8 *)(qgh + KC * DK + i) = sq.lo;
+    }
+    bf16 *bhh = split_hi(p.bhT, sh, DK, KC), *khh = split_hi(p.khT, sh, DK, KC);
+    for (int i = 8 * tid; i < DK * KC; i += 8 * 256) {
+      const int d = i / KC, r = i % KC;
+      const float gC = Gs[(KC - 1) * SG + d];
+      f32x8 fb, fk;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float et = __expf(gC - Gs[(r + e) * SG + d]);
+        fb[e] = to_f(Bs[(r + e) * SE + d]) * et;
+        fk[e] = to_f(Ks[(r + e) * SE + d]) * et;
+      }
+      const Split sb = split8(fb), sk = split8(fk);
+      *(bf16x8 *)(bhh + i) = sb.hi;
+      *(bf16x8 *)(bhh + DK * KC + i) = sb.lo;
+      *(bf16x8 *)(khh + i) = sk.hi;
+      *(bf16x8 *)(khh + DK * KC + i) = sk.lo;
+    }
   }
-  // the Gram matrices: 16 tiles of each (upper ones zero), ten lower ones computed
-  float *const outs[4] = {nullptr, p.aak + sh * KC * KC, p.pqb + sh * KC * KC, p.pqk + sh * KC * KC};
+  // the Gram matrices: the ten lower 16x16 tiles of each (the upper ones are zero)
+  bf16 *outs[4] = {nullptr, split_hi(p.aak, sh, KC, KC), split_hi(p.pqb, sh, KC, KC), split_hi(p.pqk, sh, KC, KC)};
   for (int t = wave; t < 64; t += 4) {
     const int w = t >> 4, tt = t & 15, a = tt >> 2, b = tt & 3;  // matrix w, tile (a, b)
     const int m = 16 * a + 7;
@@ -145,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
               const float x = strict ? gp(r, c) : Gs[r * SG + c];
               f[ii] = to_f(X[r * SE + c]) * __expf(x - Gs[m * SG + c]);
             }
-            return f;
+            return split8(f);
           },
           [&](int k0) {
             f32x8 f;
@@ -155,7 +229,7 @@ __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
               const int c = k0 + 8 * lg + ii;
               f[ii] = to_f(Y[i * SE + c]) * __expf(Gs[m * SG + c] - Gs[i * SG + c]);
             }
-            return f;
+            return split8(f);
           });
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -164,123 +238,274 @@ __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
       if (w == 0)
         Ab[r * SC + i] = v;
       else
-        outs[w][r * KC + i] = v;
+        store_split(outs[w], outs[w] + KC * KC, r * KC + i, v);
     }
   }
   __syncthreads();
-  if (tid < KC) {
-    // (I - A_ab)^-1, column c per thread: T[r][c] = [r == c] + sum_{i<r} A_ab[r][i] T[i][c]
-    const int c = tid;
-    float x[KC];
+  tri_inv64<-1>(Ab, SC, Tb, SC, ys);  // T = (I - A_ab)^-1
+  bf16 *tmh = split_hi(p.tm, sh, KC, KC);
+  for (int i = 8 * tid; i < KC * KC; i += 8 * 256) {
+    f32x8 f;
 #pragma unroll
-    for (int r = 0; r < KC; ++r) {
-      float acc = r == c ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 0; i < r; ++i) acc += Ab[r * SC + i] * x[i];
-      x[r] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < KC; ++r) p.tm[(sh * KC + r) * KC + c] = x[r];
+    for (int e = 0; e < 8; ++e) f[e] = Tb[(i / KC) * SC + i % KC + e];
+    const Split st = split8(f);
+    *(bf16x8 *)(tmh + i) = st.hi;
+    *(bf16x8 *)(tmh + KC * KC + i) = st.lo;
   }
 }
 
-template <typename E, int DK>
+template <typename E, int DK, int NCT>
 __global__ __launch_bounds__(256, 1) void dplrk_state_kernel(DplrKeyParams p) {
-  __shared__ __align__(16) float Ms[DK * SV];
-  __shared__ __align__(16) float Vs[KC * SV];
-  __shared__ __align__(16) float Rs[KC * SV];
-  __shared__ __align__(16) float Us[KC * SV];
+  constexpr int BV = 16 * NCT;  // value columns of this workgroup
+  constexpr int PM = DK + 8;    // bf16 pitch of the transposed state (one row per value column)
+  constexpr int SK = DK / 32;   // 32-deep steps over the key channels
+  __shared__ __align__(16) bf16 MTh[BV * PM];
+  __shared__ __align__(16) bf16 MTl[BV * PM];
+  __shared__ __align__(16) bf16 VTh[BV * PV];
+  __shared__ __align__(16) bf16 VTl[BV * PV];
+  __shared__ __align__(16) bf16 RTh[BV * PV];
+  __shared__ __align__(16) bf16 RTl[BV * PV];
+  __shared__ __align__(16) bf16 UTh[BV * PV];
+  __shared__ __align__(16) bf16 UTl[BV * PV];
   __shared__ float gsh[DK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr bool VX = std::is_same<E, bf16>::value;  // v exact in bf16: no lo half needed
+  constexpr int RB = DK / 64;                         // 16-row state blocks per wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lm = lane & 15;
-  const int H = p.H, dv = p.dv, nb = dv / KBV;
+  const int H = p.H, dv = p.dv, nb = dv / BV;
   const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
-  const int n = pair / H, h = pair % H, col0 = jb * KBV;
+  const int n = pair / H, h = pair % H, col0 = jb * BV;
   long tok0;
   int len;
   if (!seq_extent_d(p, n, tok0, len)) return;  // malformed offsets: leave untouched
   const int nchunks = (len + KC - 1) / KC;
   const long slot0 = (tok0 >> 6) + n;
   const size_t sbase = ((size_t)n * H + h) * DK * dv + col0;
-  for (int i = tid; i < DK * KBV; i += 256) {
-    const int d = i / KBV, j = i % KBV;
-    Ms[d * SV + j] = p.init_state ? p.init_state[sbase + (size_t)d * dv + j] : 0.f;
-  }
-  auto colB = [&](const float *X, int n0) {
-    return [=](int k0) {
-      f32x8 f;
+  // the state: wave w holds key rows 16 (RB w + rb) + 4 lg + j, value columns 16 ct + lm
+  f32x4 Mc[RB][NCT];
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) f[ii] = X[(k0 + 8 * lg + ii) * SV + n0 + lm];
-      return f;
-    };
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 16 * (RB * wave + rb) + 4 * lg + j;
+        Mc[rb][ct][j] = p.init_state ? p.init_state[sbase + (size_t)d * dv + 16 * ct + lm] : 0.f;
+      }
+  // a C tile (rows r0 + 4 lg + j, column 16 ct + lm) into a transposed split LDS matrix
+  auto put_t = [&](bf16 *Xh, bf16 *Xl, int pitch, int r0, int ct, const f32x4 &v) {
+    bf16x4 hv, lv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hv[j] = (bf16)v[j];
+      lv[j] = (bf16)(v[j] - (float)hv[j]);
+    }
+    const int o = (16 * ct + lm) * pitch + r0 + 4 * lg;
+    *(bf16x4 *)(Xh + o) = hv;
+    *(bf16x4 *)(Xl + o) = lv;
   };
+  auto put_state = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) put_t(MTh, MTl, PM, 16 * (RB * wave + rb), ct, Mc[rb][ct]);
+  };
+  put_state();
+  // B fragment (column 16 ct + lm, k = k0 + 8 lg ..) of a transposed split LDS matrix
+  auto bfrag = [&](const bf16 *Xh, const bf16 *Xl, int pitch, int ct, int k0) {
+    const int o = (16 * ct + lm) * pitch + k0 + 8 * lg;
+    return Split{ld8(Xh + o), ld8(Xl + o)};
+  };
+  auto vfrag = [&](int ct, int k0) {
+    if constexpr (VX) {
+      return ld8(VTh + (16 * ct + lm) * PV + k0 + 8 * lg);
+    } else {
+      return bfrag(VTh, VTl, PV, ct, k0);
+    }
+  };
+  const int r0 = 16 * wave + lm;    // this lane's A row of the 64-row products
+  const int kend = 16 * wave + 16;  // triangular 64 x 64 operands: columns below kend
+  const int ks = (kend + 31) / 32;  // ... their 32-deep steps
+  // A fragments of a split matrix (rows x cols) in the workspace, row `row`: the loads
+  // of each phase are issued one phase ahead and consumed from registers
+  auto ldrow = [&](const bf16 *Xh, int rows, int cols, int row, int k0) {
+    const bf16 *x = Xh + (size_t)row * cols + k0 + 8 * lg;
+    return Split{ld8(x), ld8(x + (size_t)rows * cols)};
+  };
+  Split f_at[SK], f_aak[2], f_tm[2], f_qg[SK], f_pqb[2], f_pqk[2], f_bh[RB][2], f_kh[RB][2];
+  auto load_r = [&](size_t sh) {
+    const bf16 *ath = split_hi(p.at, sh, KC, DK), *aakh = split_hi(p.aak, sh, KC, KC);
+#pragma unroll
+    for (int s = 0; s < SK; ++s) f_at[s] = ldrow(ath, KC, DK, r0, 32 * s);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s < ks) f_aak[s] = ldrow(aakh, KC, KC, r0, 32 * s);
+  };
+  auto load_u = [&](size_t sh) {
+    const bf16 *tmh = split_hi(p.tm, sh, KC, KC);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s < ks) f_tm[s] = ldrow(tmh, KC, KC, r0, 32 * s);
+  };
+  auto load_o = [&](size_t sh) {
+    const bf16 *qgh = split_hi(p.qg, sh, KC, DK), *pqbh = split_hi(p.pqb, sh, KC, KC);
+    const bf16 *pqkh = split_hi(p.pqk, sh, KC, KC);
+#pragma unroll
+    for (int s = 0; s < SK; ++s) f_qg[s] = ldrow(qgh, KC, DK, r0, 32 * s);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s < ks) {
+        f_pqb[s] = ldrow(pqbh, KC, KC, r0, 32 * s);
+        f_pqk[s] = ldrow(pqkh, KC, KC, r0, 32 * s);
+      }
+  };
+  auto load_m = [&](size_t sh) {
+    const bf16 *bhh = split_hi(p.bhT, sh, DK, KC), *khh = split_hi(p.khT, sh, DK, KC);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int d = 16 * (RB * wave + rb) + lm;
+        f_bh[rb][s] = ldrow(bhh, DK, KC, d, 32 * s);
+        f_kh[rb][s] = ldrow(khh, DK, KC, d, 32 * s);
+      }
+  };
+  // V of a chunk and its e^{G_C}, loaded one chunk ahead with no branch around a load
+  // (rows past the end read the last row and are zeroed when staged): thread = (token,
+  // a quarter of the columns); every thread reads the e^{G_C} of channel tid % DK
+  constexpr int VC = BV / 4, VL = VC * (int)sizeof(E) / 16;  // columns, 16-byte loads
+  u32x4 vraw[VL];
+  float gnext = 0.f;
+  auto load_v = [&](size_t tbase, int nvc, size_t shn) {
+    const int r = min(tid >> 2, nvc - 1), g = tid & 3;
+    const E *src = (const E *)p.v + ((tbase + r) * H + h) * dv + col0 + VC * g;
+#pragma unroll
+    for (int u = 0; u < VL; ++u) vraw[u] = *(const u32x4 *)(src + u * (16 / (int)sizeof(E)));
+    gnext = p.gam[shn * DK + tid % DK];
+  };
+  if (nchunks > 0) {
+    load_r((size_t)slot0 * H + h);
+    load_v((size_t)tok0, min(KC, len), (size_t)slot0 * H + h);
+  }
+  typedef decltype(vfrag(0, 0)) VF;
   for (int c = 0; c < nchunks; ++c) {
     const size_t sh = (size_t)(slot0 + c) * H + h;
     const int nv = min(KC, len - c * KC);
     const size_t tbase = (size_t)tok0 + (size_t)c * KC;
-    for (int i = tid; i < KC * KBV; i += 256) {
-      const int r = i / KBV, j = i % KBV;
-      Vs[r * SV + j] = r < nv ? to_f(((const E *)p.v)[((tbase + r) * H + h) * dv + col0 + j]) : 0.f;
+    {
+      const int r = tid >> 2, g = tid & 3;
+      const bool in = r < nv;
+#pragma unroll
+      for (int u = 0; u < VL; ++u) {
+        typedef E EV __attribute__((ext_vector_type(16 / sizeof(E))));
+        const EV ev = __builtin_bit_cast(EV, vraw[u]);
+#pragma unroll
+        for (int e = 0; e < 16 / (int)sizeof(E); ++e) {
+          const float x = in ? to_f(ev[e]) : 0.f;
+          const int col = VC * g + u * (16 / (int)sizeof(E)) + e;
+          const bf16 hv = (bf16)x;
+          VTh[col * PV + r] = hv;
+          if constexpr (!VX) VTl[col * PV + r] = (bf16)(x - (float)hv);
+        }
+      }
+      if (tid < DK) gsh[tid] = gnext;
     }
-    if (tid < DK) gsh[tid] = p.gam[sh * DK + tid];
     __syncthreads();
-    const float *at = p.at + sh * KC * DK, *qg = p.qg + sh * KC * DK;
-    const float *tm = p.tm + sh * KC * KC, *aak = p.aak + sh * KC * KC, *pqb = p.pqb + sh * KC * KC,
-                *pqk = p.pqk + sh * KC * KC;
+    load_u(sh);
+    // this chunk's B fragments of M0 and V (read once, used by R, O and the update)
+    Split bm[NCT][SK];
+    VF bv[NCT][2];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int s = 0; s < SK; ++s) bm[ct][s] = bfrag(MTh, MTl, PM, ct, 32 * s);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) bv[ct][s] = vfrag(ct, 32 * s);
+    }
     // R = (A e^{Gp}) M0 + A_ak V
-    for (int t = wave; t < 8; t += 4) {
-      const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
-      const f32x4 r1 = dprod<DK>([&](int k0) { return ld8(at + (m0 + lm) * DK + k0 + 8 * lg); }, colB(Ms, n0));
-      const f32x4 r2 = dprod<KC>([&](int k0) { return ld8(aak + (m0 + lm) * KC + k0 + 8 * lg); }, colB(Vs, n0),
-                                 0, m0 + 16);
+    {
+      f32x4 R[NCT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Rs[(m0 + 4 * lg + j) * SV + n0 + lm] = r1[j] + r2[j];
+      for (int ct = 0; ct < NCT; ++ct) {
+        R[ct] = zero4();
+#pragma unroll
+        for (int s = 0; s < SK; ++s) R[ct] = mm(f_at[s], bm[ct][s], R[ct]);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          if (s < ks) R[ct] = mm(f_aak[s], bv[ct][s], R[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) put_t(RTh, RTl, PV, 16 * wave, ct, R[ct]);
     }
     __syncthreads();
+    load_o(sh);
     // U = (I - A_ab)^-1 R
-    for (int t = wave; t < 8; t += 4) {
-      const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
-      const f32x4 u = dprod<KC>([&](int k0) { return ld8(tm + (m0 + lm) * KC + k0 + 8 * lg); }, colB(Rs, n0), 0,
-                                m0 + 16);
+    {
+      Split br[NCT][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Us[(m0 + 4 * lg + j) * SV + n0 + lm] = u[j];
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) br[ct][s] = bfrag(RTh, RTl, PV, ct, 32 * s);
+      f32x4 U[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        U[ct] = zero4();
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          if (s < ks) U[ct] = mm(f_tm[s], br[ct][s], U[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) put_t(UTh, UTl, PV, 16 * wave, ct, U[ct]);
     }
     __syncthreads();
+    load_m(sh);
+    if (c + 1 < nchunks) load_v(tbase + KC, min(KC, len - (c + 1) * KC), sh + H);
+    Split bu[NCT][2];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) bu[ct][s] = bfrag(UTh, UTl, PV, ct, 32 * s);
     // O = (Q e^G) M0 + P_qb U + P_qk V
-    for (int t = wave; t < 8; t += 4) {
-      const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
-      const f32x4 o1 = dprod<DK>([&](int k0) { return ld8(qg + (m0 + lm) * DK + k0 + 8 * lg); }, colB(Ms, n0));
-      const f32x4 o2 = dprod<KC>([&](int k0) { return ld8(pqb + (m0 + lm) * KC + k0 + 8 * lg); }, colB(Us, n0), 0,
-                                 m0 + 16);
-      const f32x4 o3 = dprod<KC>([&](int k0) { return ld8(pqk + (m0 + lm) * KC + k0 + 8 * lg); }, colB(Vs, n0), 0,
-                                 m0 + 16);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 O = zero4();
+#pragma unroll
+      for (int s = 0; s < SK; ++s) O = mm(f_qg[s], bm[ct][s], O);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (s < ks) O = mm(f_pqk[s], bv[ct][s], mm(f_pqb[s], bu[ct][s], O));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = m0 + 4 * lg + j;
-        if (r < nv && p.o) ((E *)p.o)[((tbase + r) * H + h) * dv + col0 + n0 + lm] = to_e<E>(o1[j] + o2[j] + o3[j]);
+        const int r = 16 * wave + 4 * lg + j;
+        if (r < nv && p.o) ((E *)p.o)[((tbase + r) * H + h) * dv + col0 + 16 * ct + lm] = to_e<E>(O[j]);
       }
     }
-    __syncthreads();  // every read of M0 is done
+    if (c + 1 < nchunks) load_r(sh + H);
     // M = diag(e^{G_C}) M0 + (B e^{G_C - G})^T U + (K e^{G_C - G})^T V
-    for (int t = wave; t < (DK / 16) * 2; t += 4) {
-      const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
-      const f32x4 a1 =
-          dprod<KC>([&](int k0) { return ld8(p.bhT + (sh * DK + m0 + lm) * KC + k0 + 8 * lg); }, colB(Us, n0));
-      const f32x4 a2 =
-          dprod<KC>([&](int k0) { return ld8(p.khT + (sh * DK + m0 + lm) * KC + k0 + 8 * lg); }, colB(Vs, n0));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = m0 + 4 * lg + j;
-        Ms[d * SV + n0 + lm] = gsh[d] * Ms[d * SV + n0 + lm] + a1[j] + a2[j];
+    for (int rb = 0; rb < RB; ++rb) {
+      const int d0 = 16 * (RB * wave + rb);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Mc[rb][ct][j] *= gsh[d0 + 4 * lg + j];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) Mc[rb][ct] = mm(f_kh[rb][s], bv[ct][s], mm(f_bh[rb][s], bu[ct][s], Mc[rb][ct]));
       }
     }
-    __syncthreads();
+    __syncthreads();  // every read of M0, V and gam is done
+    put_state();
   }
   if (p.final_state)
-    for (int i = tid; i < DK * KBV; i += 256) {
-      const int d = i / KBV, j = i % KBV;
-      p.final_state[sbase + (size_t)d * dv + j] = Ms[d * SV + j];
-    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 16 * (RB * wave + rb) + 4 * lg + j;
+          p.final_state[sbase + (size_t)d * dv + 16 * ct + lm] = Mc[rb][ct][j];
+        }
 }
 
 template <typename E, int DK>
@@ -288,7 +513,7 @@ hipError_t launch_dk(const DplrKeyParams &p, hipStream_t stream) {
   const unsigned items = (unsigned)(p.slots * p.H), serial = (unsigned)(p.N * p.H * (p.dv / KBV));
   if (serial == 0) return hipSuccess;
   if (items) hipLaunchKernelGGL((dplrk_prep_kernel<E, DK>), dim3(items), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((dplrk_state_kernel<E, DK>), dim3(serial), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((dplrk_state_kernel<E, DK, KBV / 16>), dim3(serial), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -135,9 +135,11 @@ struct DplrKeyParams {
   float *final_state;             // NULL | [N, H, d_k, d_v]
   void *o;                        // [tokens, H, d_v]
   const int32_t *cu_seqlens;      // NULL (batch) | [N + 1]
-  float *tm, *aak, *pqb, *pqk;    // [slots, H, 64, 64] each
-  float *at, *qg;                 // [slots, H, 64, d_k]
-  float *bhT, *khT;               // [slots, H, d_k, 64]
+  // per slot-head, each matrix as a bf16 hi half then a bf16 lo half (hi + lo = the
+  // fp32 value), row-major
+  __bf16 *tm, *aak, *pqb, *pqk;   // [slots, H, 2, 64, 64]
+  __bf16 *at, *qg;                // [slots, H, 2, 64, d_k]
+  __bf16 *bhT, *khT;              // [slots, H, 2, d_k, 64]
   float *gam;                     // [slots, H, d_k]
   int N, H, T, dv;
   long slots;

@@ -144,4 +144,84 @@ __device__ __forceinline__ bf16x8 col_frag(const bf16 *X, int pitch, int k0, int
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// x as a hi + lo pair of bf16 (see Split) stored at hi[i] and lo[i].
+__device__ __forceinline__ void store_split(bf16 *hi, bf16 *lo, size_t i, float x) {
+  const bf16 h = (bf16)x;
+  hi[i] = h;
+  lo[i] = (bf16)(x - (float)h);
+}
+// The fragment (8 contiguous elements) of a matrix stored as hi and lo bf16 halves.
+__device__ __forceinline__ Split ld_split(const bf16 *hi, const bf16 *lo) { return Split{ld8(hi), ld8(lo)}; }
+
+// T = (I + s A)^-1 (s = SGN, +1 or -1) of a strictly lower triangular 64 x 64 fp32
+// matrix A in LDS (row pitch sa), written to LDS T (row pitch st; every entry).
+// Blocked: wave 0 solves the four 16 x 16 diagonal blocks by forward substitution
+// (lane (lg, lm) takes column lm of block lg); then waves 0-2 each walk down one block
+// column b, T[a][b] = -s T[a][a] sum_{b <= k < a} A[a][k] T[k][b] for a = b+1 .. 3, on
+// the bf16 matrix cores with split operands (the inner sum passes through the wave's
+// 16 x 17 slice of ys).  Every thread of the workgroup (at least four waves) calls it;
+// it ends with a barrier.
+template <int SGN>
+__device__ __forceinline__ void tri_inv64(const float *A, int sa, float *T, int st, float *ys) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lm = lane & 15;
+  for (int i = tid; i < 64 * 64; i += blockDim.x) {
+    const int r = i >> 6, c = i & 63;
+    if ((c >> 4) > (r >> 4)) T[r * st + c] = 0.f;
+  }
+  if (wave == 0) {
+    const int o = 16 * lg;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc += A[(o + r) * sa + o + i] * x[i];
+      x[r] = (r == lm ? 1.f : 0.f) - (float)SGN * acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) T[(o + r) * st + o + lm] = x[r];
+  }
+  __syncthreads();
+  if (wave < 3) {
+    const int b = wave;
+    float *y = ys + wave * (16 * 17);
+    for (int a = b + 1; a < 4; ++a) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < 64; k0 += 32) {
+        if (k0 + 32 <= 16 * b || k0 >= 16 * a) continue;
+        f32x8 fa, fb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int k = k0 + 8 * lg + i;
+          const bool in = k >= 16 * b && k < 16 * a;
+          fa[i] = in ? A[(16 * a + lm) * sa + k] : 0.f;
+          fb[i] = in ? T[k * st + 16 * b + lm] : 0.f;
+        }
+        acc = mm(split8(fa), split8(fb), acc);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[(4 * lg + j) * 17 + lm] = acc[j];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      f32x8 fa, fb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = 8 * lg + i;
+        fa[i] = k < 16 ? T[(16 * a + lm) * st + 16 * a + k] : 0.f;
+        fb[i] = k < 16 ? y[k * 17 + lm] : 0.f;
+      }
+      const f32x4 z = mm(split8(fa), split8(fb), zero4());
+#pragma unroll
+      for (int j = 0; j < 4; ++j) T[(16 * a + 4 * lg + j) * st + 16 * b + lm] = -(float)SGN * z[j];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  __syncthreads();
+}
+
 }  // namespace gdn
