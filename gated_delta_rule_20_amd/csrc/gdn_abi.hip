@@ -241,8 +241,8 @@ DplrKeyLayout dplr_key_layout(const gdn_dplr_args *a) {
 
 struct BwdLayout {
   long slots;
-  size_t states, tmat, part, dla;
-  size_t total() const { return states + tmat + part + dla; }
+  size_t states, tmat, pmat, part, dla;
+  size_t total() const { return states + tmat + pmat + part + dla; }
 };
 // The per-key-channel gate: the fp32 arrays of BwdKeyParams, in this order
 struct BwdKeyLayout {
@@ -277,11 +277,12 @@ BwdKeyLayout bwd_key_layout(const gdn_bwd_args *a) {
   return L;
 }
 BwdLayout bwd_layout(const gdn_bwd_args *a) {
-  BwdLayout L{0, 0, 0, 0, 0};
+  BwdLayout L{0, 0, 0, 0, 0, 0};
   const long tokens = (long)a->B * a->T;
   L.slots = gdn::key_slots(tokens, a->N);
   L.states = align256((size_t)L.slots * a->H * a->d_k * a->d_v * 4);
   if (a->write == GDN_WRITE_DELTA) L.tmat = align256((size_t)L.slots * a->H * 64 * 64 * 4);  // T per chunk
+  L.pmat = align256((size_t)L.slots * a->H * 64 * 64 * 4);  // P per chunk
   L.part = align256((size_t)L.slots * a->H * (a->d_v / 32) * gdn::bwd_part_floats(a->d_k) * 4);
   // the constant per-head decay: per-token gradients, summed per head afterwards
   if (a->gate == GDN_GATE_HEAD_CONST) L.dla = align256((size_t)tokens * a->H * 4);
@@ -414,12 +415,13 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   bp.cu_seqlens = a->cu_seqlens;
   bp.states = (const float *)ws;
   bp.tmat = (float *)(ws + L.states);
-  bp.part = (float *)(ws + L.states + L.tmat);
+  bp.pmat = (float *)(ws + L.states + L.tmat);
+  bp.part = (float *)(ws + L.states + L.tmat + L.pmat);
   bp.dq = a->dq;
   bp.dk = a->dk;
   bp.dv_out = a->dv;
   bp.dbeta = a->dbeta;
-  float *const dla_tok = (float *)(ws + L.states + L.tmat + L.part);
+  float *const dla_tok = (float *)(ws + L.states + L.tmat + L.pmat + L.part);
   bp.dlog_alpha = a->gate == GDN_GATE_HEAD_CONST ? dla_tok : a->dlog_alpha;
   bp.la_stride = la_stride;
   bp.dinit = a->dinitial_state;

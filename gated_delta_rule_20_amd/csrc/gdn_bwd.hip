@@ -16,15 +16,17 @@
 // then A, P, Gamma, Kt, Qt, Kh and gam give dq, dk, dbeta and dG, and d log alpha_t is
 // the sum of dG_r over r >= t in the chunk plus dG_C.
 //
-// Three launches:
+// Four launches:
 //  1. a forward that stores every chunk's entering state M0 instead of o: the
 //     pipelined kernel's STATES variant for bf16 with d_k = 128, the fused kernel
 //     otherwise;
-//  2. bwd_state_kernel, one workgroup per (sequence, head, 32 value columns), walks the
-//     chunks in reverse carrying dM: it writes dV, the entering-state gradient and T,
-//     and per value block the partial sums of dP, dT, dQ, dK, dG, dbeta and dG_C
-//     (the terms that sum over value columns);
-//  3. bwd_chunk_kernel, one workgroup per (chunk, head), fully parallel: it sums the
+//  2. bwd_prep_kernel, one workgroup per (chunk, head), fully parallel: P and T of every
+//     chunk (the parts of the chunk that depend on neither state nor value columns);
+//  3. bwd_state_kernel, one workgroup per (sequence, head, 32 value columns), walks the
+//     chunks in reverse carrying dM: it writes dV and the entering-state gradient, and
+//     per value block the partial sums of dP, dT, dQ, dK, dG, dbeta and dG_C (the terms
+//     that sum over value columns);
+//  4. bwd_chunk_kernel, one workgroup per (chunk, head), fully parallel: it sums the
 //     partials in a fixed order (deterministic), forms dA and the Gram / Gamma terms
 //     and writes dq, dk, dbeta and d log alpha.
 // All arithmetic is fp32 or its equivalent (inputs in bf16 or fp32).  With bf16 I/O the
@@ -42,7 +44,8 @@ namespace gdn {
 namespace {
 
 constexpr int BC = 64;    // chunk length
-constexpr int BNT = 256;  // threads per workgroup of the per-chunk kernel
+constexpr int BNT = 1024;  // threads per workgroup of the per-chunk kernel (four waves per SIMD)
+constexpr int BNW = BNT / 64;
 // threads per workgroup of the reverse-state kernel: the additive write's variant runs
 // two waves per SIMD; the delta write's needs more registers than that leaves (256 per
 // wave) and runs one
@@ -72,6 +75,114 @@ __device__ __forceinline__ bool seq_extent(const BwdParams &p, int n, long &tok0
   return true;
 }
 
+// the chunk of a slot: (first token, valid rows), or false when no chunk owns it
+__device__ __forceinline__ bool slot_chunk(const BwdParams &p, long slot, size_t &tb, int &nv) {
+  auto tok_start = [&](int sq) -> long { return p.cu_seqlens ? (long)p.cu_seqlens[sq] : (long)sq * p.T; };
+  int lo = 0, hi = p.N - 1;  // the last n with floor(tok0_n / 64) + n <= slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((tok_start(mid) >> 6) + mid <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  long tok0;
+  int len;
+  if (!seq_extent(p, lo, tok0, len)) return false;
+  const long c = slot - ((tok0 >> 6) + lo);
+  if (c < 0 || 64 * c >= len) return false;
+  nv = (int)min(64L, (long)len - 64 * c);
+  tb = (size_t)tok0 + (size_t)c * BC;
+  return true;
+}
+
+// One workgroup per (chunk slot, head), fully parallel: P = incl(Q K^T * Gamma) and, for
+// the delta write, T = (I + A)^-1 with A = strict(diag(beta) K K^T * Gamma), both fp32
+// row-major into the workspace (the blocks above the diagonal zero).  The Gram tiles
+// take the bf16 inputs exactly; T is the blocked inverse (tri_inv64).
+template <typename E, int DK, int GATE, bool ADD>
+__global__ __launch_bounds__(256, 2) void bwd_prep_kernel(BwdParams p) {
+  constexpr int SKE = DK + 8;
+  __shared__ __align__(16) E Kl[BC * SKE];
+  __shared__ __align__(16) E Ql[BC * SKE];
+  __shared__ float Al[BC * ST], Tl[BC * ST];
+  __shared__ float ys[3 * 16 * 17];
+  __shared__ float bs[BC], gs[BC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lm = lane & 15;
+  const int H = p.H;
+  const long slot = blockIdx.x / H;
+  const int h = blockIdx.x % H;
+  size_t tb;
+  int nv;
+  if (!slot_chunk(p, slot, tb, nv)) return;
+  auto K_ = [&](int r, int d) { return to_f(Kl[r * SKE + d]); };
+  auto Q_ = [&](int r, int d) { return to_f(Ql[r * SKE + d]); };
+  {  // K, Q: 16-byte loads, all in flight before the LDS stores (rows past the end zero)
+    constexpr int VE = 16 / (int)sizeof(E), RK = BC * (DK / VE) / 256;
+    u32x4 kv[RK], qv[RK];
+#pragma unroll
+    for (int u = 0; u < RK; ++u) {
+      const int pc = tid + 256 * u, r = pc / (DK / VE), g = pc % (DK / VE);
+      const size_t o = ((tb + r) * H + h) * DK + g * VE;
+      kv[u] = r < nv ? *(const u32x4 *)((const E *)p.k + o) : (u32x4){0u, 0u, 0u, 0u};
+      qv[u] = r < nv ? *(const u32x4 *)((const E *)p.q + o) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < RK; ++u) {
+      const int pc = tid + 256 * u, r = pc / (DK / VE), g = pc % (DK / VE);
+      *(u32x4 *)(Kl + r * SKE + g * VE) = kv[u];
+      *(u32x4 *)(Ql + r * SKE + g * VE) = qv[u];
+    }
+  }
+  if (tid < BC) {
+    const bool ok = tid < nv;
+    bs[tid] = (!ADD && ok) ? p.beta[(tb + tid) * H + h] : 0.f;
+    gs[tid] = (GATE == GATE_HEAD && ok) ? p.log_alpha[(tb + tid) * p.la_stride + h] : 0.f;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float g = gs[lane];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(g, off);
+      if (lane >= off) g += y;
+    }
+    gs[lane] = g;
+  }
+  __syncthreads();
+  float *pm = p.pmat + ((size_t)slot * H + h) * BC * BC;
+  for (int t = wave; t < 16; t += 4) {
+    const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
+    f32x4 av = zero4(), pv = zero4();
+    if (n0 <= m0) {
+      if constexpr (std::is_same<E, bf16>::value) {  // bf16 rows read whole
+        const E *kr = Kl + (m0 + lm) * SKE + 8 * lg, *qr = Ql + (m0 + lm) * SKE + 8 * lg;
+        const E *kc = Kl + (n0 + lm) * SKE + 8 * lg;
+        if (!ADD) av = tile_frag<DK>([&](int k0) { return ld8(kr + k0); }, [&](int k0) { return ld8(kc + k0); });
+        pv = tile_frag<DK>([&](int k0) { return ld8(qr + k0); }, [&](int k0) { return ld8(kc + k0); });
+      } else {
+        if (!ADD) av = tile_g<E, DK, true, true>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
+        pv = tile_g<E, DK, true, true>(m0, n0, lg, lm, Q_, [&](int d, int i) { return K_(i, d); });
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = m0 + 4 * lg + u, i = n0 + lm;
+      const float gam = i <= r ? (GATE == GATE_HEAD ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
+      if (!ADD) Al[r * ST + i] = i < r ? bs[r] * av[u] * gam : 0.f;
+      pm[r * BC + i] = pv[u] * gam;
+    }
+  }
+  if constexpr (!ADD) {
+    __syncthreads();
+    tri_inv64<1>(Al, ST, Tl, ST, ys);
+    float *tm = p.tmat + ((size_t)slot * H + h) * BC * BC;
+    for (int i4 = 4 * tid; i4 < BC * BC; i4 += 4 * 256) {
+      const int r = i4 / BC, i = i4 % BC;
+      *(f32x4 *)(tm + i4) = (f32x4){Tl[r * ST + i], Tl[r * ST + i + 1], Tl[r * ST + i + 2], Tl[r * ST + i + 3]};
+    }
+  }
+}
+
 template <typename E, int DK, int GATE, bool ADD>
 __global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdParams p) {
   constexpr int SNT = state_threads<ADD>(), NWS = SNT / 64;
@@ -82,6 +193,7 @@ __global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdP
   constexpr int NPV = BC * (BVB / VE);           // V / dO pieces
   constexpr int RV = (NPV + SNT - 1) / SNT;      // ... per thread (the first NPV threads)
   constexpr int RM = DK * (BVB / 4) / SNT;       // entering-state pieces per thread
+  constexpr int RT = BC * BC / 4 / SNT;          // T / P pieces per thread
   typedef E EV __attribute__((ext_vector_type(VE)));
   typedef Part<DK> PT;
   __shared__ __align__(16) E Kl[BC * SKE];
@@ -97,11 +209,9 @@ __global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdP
   __shared__ __align__(16) float dDl[BC * SV];
   __shared__ float bs[BC], gs[BC], eg[BC], et[BC], wsum[NWS], misc[4];
   __shared__ float rsum[NH][3][BC];  // row sums of the dQ / dK products, per column part
-  // delta write: V is dead once X is formed and A once T is; additive write: Delta = V
-  // and Y = dDelta
+  // delta write: V is dead once X is formed; additive write: Delta = V and Y = dDelta
   float *const Yl = ADD ? dDl : Vb;
   float *const Dl = ADD ? Vb : Tl;
-  float *const Ys = dDl;  // scratch of the block substitution, before dDelta exists
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = p.H, dv = p.dv, nb = dv / BVB;
@@ -120,16 +230,21 @@ __global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdP
     const int d = i / BVB, j = i % BVB;
     dM[d * SV + j] = p.dfinal ? p.dfinal[sstate + (size_t)d * dv + j] : 0.f;
   }
-  for (int i = tid; i < BC * ST; i += SNT) Tb[i] = Pl[i] = 0.f;  // upper blocks stay zero
 
   // ---- a chunk's inputs: 16-byte loads into registers one chunk ahead (rows past the
   // sequence end re-read its last row and are zeroed when staged)
   u32x4 pk[RK], pq[RK], pv[RV], pd[RV];
-  f32x4 pm[RM];
+  f32x4 pm[RM], pt[RT], pp[RT];
   float pb = 0.f, pl = 0.f;
   auto fetch = [&](int cc) {
     const int last = min(BC, len - cc * BC) - 1;
     const size_t tbc = (size_t)tok0 + (size_t)cc * BC;
+    const size_t tp = (((size_t)slot0 + cc) * H + h) * BC * BC;  // T and P of the chunk
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      if (!ADD) pt[u] = *(const f32x4 *)(p.tmat + tp + 4 * (tid + SNT * u));
+      pp[u] = *(const f32x4 *)(p.pmat + tp + 4 * (tid + SNT * u));
+    }
 #pragma unroll
     for (int u = 0; u < RK; ++u) {
       const int pc = tid + SNT * u, r = min(pc / (DK / VE), last), g = pc % (DK / VE);
@@ -186,6 +301,17 @@ __global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdP
 #pragma unroll
       for (int e = 0; e < 4; ++e) M0[d * SV + 4 * g + e] = pm[u][e];
     }
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      const int i4 = 4 * (tid + SNT * u), r = i4 / BC, i = i4 % BC;
+      if (!ADD) opaque(pt[u]);
+      opaque(pp[u]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!ADD) Tb[r * ST + i + e] = pt[u][e];
+        Pl[r * ST + i + e] = pp[u][e];
+      }
+    }
     if (tid < BC) {
       opaque(pb);
       opaque(pl);
@@ -217,81 +343,15 @@ __global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdP
       if (lane == 0) misc[0] = __expf(gC);
     }
     __syncthreads();
-    // ---- A (strictly lower) into Tl and P (lower inclusive) into Pl; tiles above the
-    // diagonal are zero
-    auto gam_at = [&](int r, int i) {
-      return i <= r ? (GATE == GATE_HEAD ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
-    };
-    {
-      // the ten lower tiles, 3/3/2/2 per wave (the upper ones were zeroed once)
-      const int lg = lane >> 4, lm = lane & 15;
-      for (int t = wave; t < 10; t += NWS) {
-        const int mb = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-        const int m0 = 16 * mb, n0 = 16 * (t - mb * (mb + 1) / 2);
-        f32x4 av = zero4(), pv4;
-        if constexpr (std::is_same<E, bf16>::value) {
-          const E *kr = Kl + (m0 + lm) * SKE + 8 * lg, *qr = Ql + (m0 + lm) * SKE + 8 * lg;
-          const E *kc = Kl + (n0 + lm) * SKE + 8 * lg;
-          if (!ADD) av = tile_frag<DK>([&](int k0) { return ld8(kr + k0); }, [&](int k0) { return ld8(kc + k0); });
-          pv4 = tile_frag<DK>([&](int k0) { return ld8(qr + k0); }, [&](int k0) { return ld8(kc + k0); });
-        } else {
-          if (!ADD) av = tile<DK>(m0, n0, lg, lm, K_, [&](int d, int i) { return K_(i, d); });
-          pv4 = tile<DK>(m0, n0, lg, lm, Q_, [&](int d, int i) { return K_(i, d); });
-        }
+    // ---- V - Kt M0 into Xl (64 x 32; the delta write only)
+    if constexpr (!ADD)
+      mm_g<E, BC, BVB, DK, NWS, true, false>(wave, lane, K_, [&](int d, int j) { return M0[d * SV + j]; },
+                                             [&](int r, int j, f32x4 v) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = m0 + 4 * lg + u, i = n0 + lm;
-          if (!ADD) Tl[r * ST + i] = i < r ? bs[r] * av[u] * gam_at(r, i) : 0.f;
-          Pl[r * ST + i] = pv4[u] * gam_at(r, i);
-        }
-      }
-    }
+                                               for (int u = 0; u < 4; ++u)
+                                                 Xl[(r + u) * SV + j] = Vb[(r + u) * SV + j] - eg[r + u] * v[u];
+                                             });
     __syncthreads();
-    if (ADD) {
-      // the additive write has no A, T or X
-    } else if (wave == 0) {
-      // diagonal 16x16 blocks of T = (I + A)^-1: lane (lg, lm) solves column lm of block lg
-      const int lg = lane >> 4, lm = lane & 15, o = 16 * lg;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = r == lm ? 1.f : 0.f;
-#pragma unroll
-        for (int i = 0; i < r; ++i) acc -= Tl[(o + r) * ST + o + i] * x[i];
-        x[r] = acc;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Tb[(o + r) * ST + o + lm] = x[r];
-    } else {
-      // V - Kt M0 into Xl (64 x 32, the other waves)
-      mm_g<E, BC, BVB, DK, NWS - 1, true, false>(wave - 1, lane, K_, [&](int d, int j) { return M0[d * SV + j]; },
-                              [&](int r, int j, f32x4 v) {
-#pragma unroll
-                                for (int u = 0; u < 4; ++u) Xl[(r + u) * SV + j] = Vb[(r + u) * SV + j] - eg[r + u] * v[u];
-                              });
-    }
-    __syncthreads();
-    if (!ADD && wave < 3) {
-      // off-diagonal blocks, block column b = wave, downwards:
-      // T[a][b] = -T[a][a] sum_{k=b}^{a-1} A[a][k] T[k][b]
-      const int lg = lane >> 4, lm = lane & 15, b = wave;
-      float *ys = Ys + wave * (16 * 17);
-      for (int a = b + 1; a < 4; ++a) {
-        const f32x4 y = tile_g<E, BC, false, false>(16 * a, 16 * b, lg, lm,
-                                 [&](int r, int k) { return (k >= 16 * b && k < 16 * a) ? Tl[r * ST + k] : 0.f; },
-                                 [&](int k, int col) { return Tb[k * ST + col]; }, 16 * b, 16 * a);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ys[(4 * lg + u) * 17 + lm] = y[u];
-        const f32x4 z = tile_g<E, 32, false, false>(16 * a, 16 * b, lg, lm,
-                                 [&](int r, int k) { return k < 16 ? Tb[r * ST + 16 * a + k] : 0.f; },
-                                 [&](int k, int col) { return k < 16 ? ys[k * 17 + col - 16 * b] : 0.f; });
-#pragma unroll
-        for (int u = 0; u < 4; ++u) Tb[(16 * a + 4 * lg + u) * ST + 16 * b + lm] = -z[u];
-      }
-    }
-    __syncthreads();
-    if (!ADD && jb == 0)  // T for the per-chunk kernel
-      for (int i = tid; i < BC * BC; i += SNT) p.tmat[(slot * H + h) * BC * BC + i] = Tb[(i / BC) * ST + i % BC];
     // ---- Delta = T diag(beta) (V - Kt M0) (the additive write: Delta = V, already in Vb);
     // dDelta = P^T dO + diag(e^{G_C - G}) K dM  (8 tiles each)
     {
@@ -529,10 +589,11 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   auto Q_ = [&](int r, int d) { return to_f(Ql[r * SKE + d]); };
 
   // K, Q: 16-byte loads (rows past the sequence end are zero)
-  constexpr int VE = 16 / (int)sizeof(E), RK = BC * (DK / VE) / BNT;
+  constexpr int VE = 16 / (int)sizeof(E), NPC = BC * (DK / VE);  // 16-byte pieces
 #pragma unroll
-  for (int u = 0; u < RK; ++u) {
+  for (int u = 0; u < (NPC + BNT - 1) / BNT; ++u) {
     const int pc = tid + BNT * u, r = pc / (DK / VE), g = pc % (DK / VE);
+    if (pc >= NPC) break;
     u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
     if (r < nv) {
       const size_t o = ((tb + r) * H + h) * DK + g * VE;
@@ -594,7 +655,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   __syncthreads();
   // S = K K^T, R = Q K^T (only their lower tiles are used: the upper ones are set to
   // zero);  Z = dT T^T
-  for (int t = wave; t < 16; t += 4) {
+  for (int t = wave; t < 16; t += BNW) {
     const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
     f32x4 sv = zero4(), rv = zero4();
     if (n0 <= m0) {
@@ -624,13 +685,13 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   }
   __syncthreads();
   // dA = -strict(T^T Z), then per entry: Gamma, Ea = dA beta_r Gamma, Ep = dP Gamma,
-  // wG = (dA beta_r S + dP R) Gamma, and dA S Gamma (for dbeta).  Each wave's 4 tiles
+  // wG = (dA beta_r S + dP R) Gamma, and dA S Gamma (for dbeta).  Each wave's tiles
   // are computed first (Zl is read), then written after a barrier.
   {
-    f32x4 da[4];
+    f32x4 da[16 / BNW];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = wave + 4 * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
+    for (int q = 0; q < 16 / BNW; ++q) {
+      const int t = wave + BNW * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
       da[q] = zero4();  // only the strictly lower part is kept (none for the additive write)
       if (!ADD && n0 <= m0)
         da[q] = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int k) { return Tl[k * ST + r]; },
@@ -638,8 +699,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = wave + 4 * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
+    for (int q = 0; q < 16 / BNW; ++q) {
+      const int t = wave + BNW * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = m0 + 4 * lg + u, i = n0 + lm;
@@ -687,7 +748,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   }
   // dq = Ep K + (partials), dk = (Ea + Ea^T) K + Ep^T Q + (partials); the partials of a
   // tile are loaded before its products, so the loads overlap them
-  for (int t = wave; t < (DK / 16) * 4; t += 4) {
+  for (int t = wave; t < (DK / 16) * 4; t += BNW) {
     const int m0 = (t / (DK / 16)) * 16, n0 = (t % (DK / 16)) * 16;
     f32x4 pq_ = zero4(), pk_ = zero4();  // partials stored [d][r]: this lane's 4 rows are contiguous
     for (int b = 0; b < nb; ++b) {
@@ -717,6 +778,7 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
 template <typename E, int DK, int GATE, bool ADD>
 void launch_bg(const BwdParams &p, hipStream_t stream) {
   const int nb = p.dv / BVB;
+  hipLaunchKernelGGL((bwd_prep_kernel<E, DK, GATE, ADD>), dim3((unsigned)(p.slots * p.H)), dim3(256), 0, stream, p);
   hipLaunchKernelGGL((bwd_state_kernel<E, DK, GATE, ADD>), dim3(p.N * p.H * nb), dim3(state_threads<ADD>()), 0,
                      stream, p);
   hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, GATE, ADD>), dim3((unsigned)(p.slots * p.H)), dim3(BNT), 0, stream, p);

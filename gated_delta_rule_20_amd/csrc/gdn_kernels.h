@@ -74,7 +74,8 @@ struct BwdParams {
   const float *dfinal;           // NULL | [N, H, d_k, d_v]
   const int32_t *cu_seqlens;     // NULL (batch) | [N + 1]
   const float *states;           // [slots, H, d_k, d_v] chunk-entering states
-  float *tmat;                   // [slots, H, 64, 64] T of every chunk (written, then read)
+  float *tmat;                   // [slots, H, 64, 64] T of every chunk (delta write)
+  float *pmat;                   // [slots, H, 64, 64] P of every chunk
   float *part;                   // [slots, H, d_v / 32, bwd_part_floats(d_k)] partial sums
   void *dq, *dk, *dv_out;        // outputs, I/O dtype
   float *dbeta, *dlog_alpha;     // [tokens, H]; dbeta NULL for the additive write, dlog_alpha

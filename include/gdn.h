@@ -249,7 +249,8 @@ typedef struct {
  * with S = floor(B T / 64) + N chunk slots, each part rounded up to 256 bytes:
  *  - no gate, one decay per (token, head), one constant decay per head: the chunk-
  *    entering states (4 d_k d_v bytes per slot and head), T of every chunk (delta write
- *    only: 16 KiB per slot and head), the partial sums over value columns (d_v / 32
+ *    only: 16 KiB per slot and head), P of every chunk (16 KiB per slot and head), the
+ *    partial sums over value columns (d_v / 32
  *    records of 4 (8192 + 128 d_k + 192) bytes per slot and head) and, for the constant
  *    per-head decay, the per-token decay gradients (4 bytes per token and head);
  *  - one decay per key channel, per slot and head in fp32: the chunk-entering states and

@@ -328,10 +328,11 @@ def test_bwd_workspace_size(g):
     slots = (2 * 128) // 64 + 2
     part = 8192 + 128 * 128 + 192
     expect = sum((x + 255) // 256 * 256 for x in (slots * 4 * 128 * 128 * 4, slots * 4 * 4096 * 4,
-                                                   slots * 4 * 4 * part * 4))
+                                                   slots * 4 * 4096 * 4, slots * 4 * 4 * part * 4))
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(a)) == expect
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(bwd_args(g, dq=None))) == 0
-    # the additive write keeps no T; the constant gate adds the per-token decay gradients
+    # states, T (delta write only), P, the partials; the constant gate adds the
+    # per-token decay gradients
     add = bwd_args(g, write=1, beta=None, dbeta=None)
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(add)) == expect - slots * 4 * 4096 * 4
     const = bwd_args(g, gate=3)
