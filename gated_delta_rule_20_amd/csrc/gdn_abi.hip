@@ -5,6 +5,7 @@
 // allocates, copies or synchronises.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -24,6 +25,16 @@ bool gate_ok(int g) {
   return g == GDN_GATE_NONE || g == GDN_GATE_HEAD || g == GDN_GATE_KEY || g == GDN_GATE_HEAD_CONST;
 }
 bool write_ok(int w) { return w == GDN_WRITE_DELTA || w == GDN_WRITE_ADD; }
+// The integer a caller stored in an enum field, read without loading the enum type (a
+// value outside the enumerators must be rejected, not loaded: that load is undefined
+// in C++).
+template <class En> int raw(const En &e) {
+  static_assert(sizeof(En) == sizeof(int), "enum fields are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+bool dtype_ok(int t) { return t == GDN_F32 || t == GDN_BF16; }
 // Kernel gate of an ABI gate: the constant per-head gate is the scalar gate read
 // with a token stride of 0.
 int kernel_gate(int g) { return g == GDN_GATE_HEAD_CONST ? gdn::GATE_HEAD : g; }
@@ -44,8 +55,7 @@ int choose_dvb(int N, int H, int dv, int dtype, int dk) {
 int check_fwd(const gdn_fwd_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
   if (a->B < 0 || a->T < 0 || a->H <= 0 || a->N < 0) return GDN_ERR_INVALID_ARG;
-  if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (!gate_ok(a->gate) || !write_ok(a->write)) return GDN_ERR_INVALID_ARG;
+  if (!dtype_ok(raw(a->dtype)) || !gate_ok(raw(a->gate)) || !write_ok(raw(a->write))) return GDN_ERR_INVALID_ARG;
   if (a->chunk != 64) return GDN_ERR_UNSUPPORTED;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   // every offset inside one 64-token chunk of q, k or v must fit 32 bits
@@ -103,8 +113,7 @@ KeyLayout key_layout(const gdn_fwd_args *a) {
 int check_step(const gdn_step_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
   if (a->N < 0 || a->H <= 0) return GDN_ERR_INVALID_ARG;
-  if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (!gate_ok(a->gate) || !write_ok(a->write)) return GDN_ERR_INVALID_ARG;
+  if (!dtype_ok(raw(a->dtype)) || !gate_ok(raw(a->gate)) || !write_ok(raw(a->write))) return GDN_ERR_INVALID_ARG;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   if (a->N == 0) return GDN_OK;
   if (!a->q || !a->k || !a->v || !a->state || !a->o) return GDN_ERR_INVALID_ARG;
@@ -119,8 +128,7 @@ int check_decode(const gdn_decode_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
   if (a->N < 0 || a->L < 1 || a->H <= 0 || a->pool_size < 1) return GDN_ERR_INVALID_ARG;
   if ((long long)a->N * a->H > INT32_MAX || (long long)a->N * a->L > INT32_MAX) return GDN_ERR_UNSUPPORTED;
-  if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (!gate_ok(a->gate) || !write_ok(a->write)) return GDN_ERR_INVALID_ARG;
+  if (!dtype_ok(raw(a->dtype)) || !gate_ok(raw(a->gate)) || !write_ok(raw(a->write))) return GDN_ERR_INVALID_ARG;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   if (a->N == 0) return GDN_OK;
   if (!a->q || !a->k || !a->v || !a->state_pool || !a->src_slots || !a->dst_slots || !a->o)
@@ -147,6 +155,7 @@ gdn_fwd_args fwd_of(const gdn_bwd_args *a) {
 
 int check_bwd(const gdn_bwd_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
+  if (!dtype_ok(raw(a->dtype)) || !gate_ok(raw(a->gate)) || !write_ok(raw(a->write))) return GDN_ERR_INVALID_ARG;
   const gdn_fwd_args f = fwd_of(a);
   const int st = check_fwd(&f);
   if (st != GDN_OK) return st;
@@ -170,6 +179,7 @@ int check_bwd(const gdn_bwd_args *a) {
 
 int check_dplr(const gdn_dplr_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
+  if (!dtype_ok(raw(a->dtype)) || !gate_ok(raw(a->gate))) return GDN_ERR_INVALID_ARG;
   gdn_fwd_args f{};
   f.B = a->B; f.T = a->T; f.H = a->H; f.d_k = a->d_k; f.d_v = a->d_v; f.chunk = a->chunk; f.N = a->N;
   f.dtype = a->dtype; f.gate = a->gate; f.write = GDN_WRITE_ADD;
@@ -186,8 +196,7 @@ int check_dplr(const gdn_dplr_args *a) {
 int check_dplr_step(const gdn_dplr_step_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
   if (a->N < 0 || a->H <= 0) return GDN_ERR_INVALID_ARG;
-  if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (!gate_ok(a->gate)) return GDN_ERR_INVALID_ARG;
+  if (!dtype_ok(raw(a->dtype)) || !gate_ok(raw(a->gate))) return GDN_ERR_INVALID_ARG;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   if (a->N == 0) return GDN_OK;
   if (!a->q || !a->k || !a->a || !a->b || !a->v || !a->state || !a->o) return GDN_ERR_INVALID_ARG;
@@ -203,8 +212,7 @@ int check_dplr_decode(const gdn_dplr_decode_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
   if (a->N < 0 || a->L < 1 || a->H <= 0 || a->pool_size < 1) return GDN_ERR_INVALID_ARG;
   if ((long long)a->N * a->H > INT32_MAX || (long long)a->N * a->L > INT32_MAX) return GDN_ERR_UNSUPPORTED;
-  if (a->dtype != GDN_F32 && a->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (!gate_ok(a->gate)) return GDN_ERR_INVALID_ARG;
+  if (!dtype_ok(raw(a->dtype)) || !gate_ok(raw(a->gate))) return GDN_ERR_INVALID_ARG;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   if (a->N == 0) return GDN_OK;
   if (!a->q || !a->k || !a->a || !a->b || !a->v || !a->state_pool || !a->src_slots || !a->dst_slots || !a->o)

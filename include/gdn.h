@@ -40,8 +40,10 @@
  *    return means nothing was launched and nothing was written.  Launch failures
  *    return GDN_ERR_HIP.  No C++ exception crosses this boundary.
  *  - Results are deterministic: no atomics, fixed reduction order.
- *  - Thread safety: the library holds no mutable global state; concurrent calls
- *    on different streams are independent.
+ *  - Thread safety: the only mutable global state is the per-device address of the
+ *    scratch array of gdn_fwd_chunked_static, looked up once per device under a lock.
+ *    Concurrent calls on different streams are independent, except calls of
+ *    gdn_fwd_chunked_static that overlap on one GPU: they share that array and race.
  */
 #ifndef GDN_H_
 #define GDN_H_
