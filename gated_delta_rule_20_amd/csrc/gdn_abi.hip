@@ -372,6 +372,54 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
     kp.T = a->T;
     kp.dv = a->d_v;
     kp.slots = KL.slots;
+    kp.states_ready = 0;
+    const gdn_fwd_args f = fwd_of(a);
+    const KeyLayout FL = key_layout(&f);
+    if (FL.slots && FL.total() <= KL.sz[1] + KL.sz[2]) {
+      // bf16 with d_k = 128: the forward's own per-channel path recomputes the chunk
+      // states (its preparation's operands go to the chunk-end-gradient and dDelta
+      // arrays, which the reverse pass writes only afterwards)
+      char *fw = (char *)arr[1];
+      gdn::KeyPrepParams pp;
+      pp.q = a->q;
+      pp.k = a->k;
+      pp.beta = a->beta;
+      pp.log_alpha = a->log_alpha;
+      pp.cu_seqlens = a->cu_seqlens;
+      pp.k_g = fw;
+      pp.q_g = fw + FL.kq;
+      pp.k_hat = fw + 2 * FL.kq;
+      pp.tp_img = fw + 3 * FL.kq;
+      pp.egc = (float *)(fw + 3 * FL.kq + FL.tp);
+      pp.N = a->N;
+      pp.H = a->H;
+      pp.T = a->T;
+      if (gdn::launch_key_prep(pp, FL.slots, a->write == GDN_WRITE_ADD, stream) != hipSuccess) return GDN_ERR_HIP;
+      gdn::FwdParams fp;
+      fp.q = pp.q_g;
+      fp.k = pp.k_g;
+      fp.v = a->v;
+      fp.beta = a->beta;
+      fp.log_alpha = a->log_alpha;
+      fp.init_state = a->initial_state;
+      fp.final_state = nullptr;
+      fp.o = nullptr;
+      fp.cu_seqlens = a->cu_seqlens;
+      fp.order = nullptr;
+      fp.k_hat = pp.k_hat;
+      fp.tp_img = pp.tp_img;
+      fp.egc = pp.egc;
+      fp.N = a->N;
+      fp.H = a->H;
+      fp.T = a->T;
+      fp.dv = a->d_v;
+      fp.nb = a->d_v / 64;
+      fp.la_stride = a->H;
+      fp.chunk_states = arr[0];
+      if (gdn::launch_fwd_pipe(fp, gdn::GATE_KEY, a->write == GDN_WRITE_ADD, stream) != hipSuccess)
+        return GDN_ERR_HIP;
+      kp.states_ready = 1;
+    }
     if (gdn::launch_bwd_key(kp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->write == GDN_WRITE_ADD, stream) !=
         hipSuccess)
       return GDN_ERR_HIP;

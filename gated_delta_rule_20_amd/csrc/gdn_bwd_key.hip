@@ -114,6 +114,8 @@ __global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
   __shared__ __align__(16) float Gs[KC * SG];
   __shared__ float As[KC * SC];
   __shared__ float Ps[KC * SC];
+  __shared__ float Ts[KC * SC];
+  __shared__ float ys[3 * 16 * 17];
   __shared__ float bsh[KC];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
@@ -124,36 +126,97 @@ __global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
   int nv;
   if (!slot_chunk(p, slot, tb, nv)) return;
   const size_t sh = (size_t)slot * H + h;
-  for (int i = tid; i < KC * DK; i += 256) {
-    const int r = i / DK, d = i % DK;
-    const size_t o = ((size_t)(tb + r) * H + h) * DK + d;
-    const bool in = r < nv;
-    Ks[r * SG + d] = in ? to_f(((const E *)p.k)[o]) : 0.f;
-    Qs[r * SG + d] = in ? to_f(((const E *)p.q)[o]) : 0.f;
-    Gs[r * SG + d] = in ? p.log_alpha[o] : 0.f;
+  {  // 16-byte loads, all in flight before the LDS stores (rows past the end are zero)
+    constexpr int VE = 16 / (int)sizeof(E), PR = DK / VE, NI = KC * PR / 256;  // k, q
+    constexpr int PG = DK / 4, NG = KC * PG / 256;                             // log alpha
+    typedef E EV __attribute__((ext_vector_type(16 / sizeof(E))));
+    u32x4 xk[NI], xq[NI], y[NG];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int pc = tid + 256 * u, r = pc / PR, g = pc % PR;
+      const size_t o = ((size_t)(tb + r) * H + h) * DK + g * VE;
+      xk[u] = r < nv ? *(const u32x4 *)((const E *)p.k + o) : (u32x4){0u, 0u, 0u, 0u};
+      xq[u] = r < nv ? *(const u32x4 *)((const E *)p.q + o) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int pc = tid + 256 * u, r = pc / PG, g = pc % PG;
+      y[u] = r < nv ? *(const u32x4 *)(p.log_alpha + ((size_t)(tb + r) * H + h) * DK + 4 * g)
+                    : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int pc = tid + 256 * u, r = pc / PR, g = pc % PR;
+      const EV ek = __builtin_bit_cast(EV, xk[u]), eq = __builtin_bit_cast(EV, xq[u]);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        Ks[r * SG + g * VE + e] = to_f(ek[e]);
+        Qs[r * SG + g * VE + e] = to_f(eq[e]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int pc = tid + 256 * u, r = pc / PG, g = pc % PG;
+      *(u32x4 *)(Gs + r * SG + 4 * g) = y[u];
+    }
   }
   if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? p.beta[(size_t)(tb + tid) * H + h] : 0.f;
   for (int i = tid; i < KC * SC; i += 256) As[i] = Ps[i] = 0.f;
   __syncthreads();
-  if (tid < DK) {  // inclusive prefix over the chunk, per channel
+  {  // per-channel inclusive prefix: 256 / DK parts of rows per channel, then the offsets
+    constexpr int NP = 256 / DK, RP = KC / NP;
+    const int d = tid % DK, q = tid / DK;
     float g = 0.f;
-    for (int r = 0; r < KC; ++r) {
-      g += Gs[r * SG + tid];
-      Gs[r * SG + tid] = g;
+    for (int r = q * RP; r < (q + 1) * RP; ++r) {
+      g += Gs[r * SG + d];
+      Gs[r * SG + d] = g;
     }
+    Ts[q * DK + d] = g;  // part totals (Ts is free until T is formed)
+    __syncthreads();
+    float off = 0.f;
+    for (int u = 0; u < q; ++u) off += Ts[u * DK + d];
+    if (q > 0)
+      for (int r = q * RP; r < (q + 1) * RP; ++r) Gs[r * SG + d] += off;
   }
   __syncthreads();
-  for (int i = tid; i < KC * DK; i += 256) {
+  // row-major Kt, Kh: 8 consecutive channels per thread (two 16-byte stores each)
+  for (int i = 8 * tid; i < KC * DK; i += 8 * 256) {
     const int r = i / DK, d = i % DK;
-    const float g = Gs[r * SG + d], gC = Gs[(KC - 1) * SG + d];
-    const float e = __expf(g), et = __expf(gC - g), kv = Ks[r * SG + d];
-    if (!ADD) {
-      p.kt[(sh * KC + r) * DK + d] = kv * e;
-      p.ktT[(sh * DK + d) * KC + r] = kv * e;
+    f32x4 kt0, kt1, kh0, kh1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float g = Gs[r * SG + d + e], gC = Gs[(KC - 1) * SG + d + e], kv = Ks[r * SG + d + e];
+      const float a = kv * __expf(g), b = kv * __expf(gC - g);
+      if (e < 4) kt0[e] = a, kh0[e] = b;
+      else kt1[e - 4] = a, kh1[e - 4] = b;
     }
-    p.kh[(sh * KC + r) * DK + d] = kv * et;
-    p.khT[(sh * DK + d) * KC + r] = kv * et;
-    p.qtT[(sh * DK + d) * KC + r] = Qs[r * SG + d] * e;
+    if (!ADD) {
+      *(f32x4 *)(p.kt + sh * KC * DK + i) = kt0;
+      *(f32x4 *)(p.kt + sh * KC * DK + i + 4) = kt1;
+    }
+    *(f32x4 *)(p.kh + sh * KC * DK + i) = kh0;
+    *(f32x4 *)(p.kh + sh * KC * DK + i + 4) = kh1;
+  }
+  // channel-major Kt^T, Kh^T, Qt^T: 8 consecutive rows per thread
+  for (int i = 8 * tid; i < DK * KC; i += 8 * 256) {
+    const int d = i / KC, r = i % KC;
+    const float gC = Gs[(KC - 1) * SG + d];
+    f32x4 a0, a1, b0, b1, c0, c1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float g = Gs[(r + e) * SG + d], kv = Ks[(r + e) * SG + d], eg = __expf(g);
+      const float a = kv * eg, b = kv * __expf(gC - g), c = Qs[(r + e) * SG + d] * eg;
+      if (e < 4) a0[e] = a, b0[e] = b, c0[e] = c;
+      else a1[e - 4] = a, b1[e - 4] = b, c1[e - 4] = c;
+    }
+    if (!ADD) {
+      *(f32x4 *)(p.ktT + sh * DK * KC + i) = a0;
+      *(f32x4 *)(p.ktT + sh * DK * KC + i + 4) = a1;
+    }
+    *(f32x4 *)(p.khT + sh * DK * KC + i) = b0;
+    *(f32x4 *)(p.khT + sh * DK * KC + i + 4) = b1;
+    *(f32x4 *)(p.qtT + sh * DK * KC + i) = c0;
+    *(f32x4 *)(p.qtT + sh * DK * KC + i + 4) = c1;
   }
   if (tid < DK) p.gam[sh * DK + tid] = __expf(Gs[(KC - 1) * SG + tid]);
   // the ten lower 16x16 tiles of P (and of A): row operand x[r] e^{G[r] - G[m]}, column
@@ -193,21 +256,12 @@ __global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
     }
   }
   __syncthreads();
-  if (!ADD && tid < KC) {
-    // T = (I + A)^-1, column c per thread: T[r][c] = [r == c] - sum_{i<r} A[r][i] T[i][c]
-    const int c = tid;
-    float x[KC];
-#pragma unroll
-    for (int r = 0; r < KC; ++r) {
-      float acc = r == c ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 0; i < r; ++i) acc -= As[r * SC + i] * x[i];
-      x[r] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < KC; ++r) {
-      p.tm[(sh * KC + r) * KC + c] = x[r];
-      p.tmT[(sh * KC + c) * KC + r] = x[r];
+  if constexpr (!ADD) {
+    tri_inv64<1>(As, SC, Ts, SC, ys);  // T = (I + A)^-1
+    for (int i = tid; i < KC * KC; i += 256) {
+      const int r = i / KC, c = i % KC;
+      p.tm[sh * KC * KC + i] = Ts[r * SC + c];
+      p.tmT[sh * KC * KC + i] = Ts[c * SC + r];
     }
   }
   for (int i = tid; i < KC * KC; i += 256) {
@@ -772,12 +826,14 @@ hipError_t launch_k(const BwdKeyParams &p, bool add, hipStream_t stream) {
   if (items == 0 || serial == 0) return hipSuccess;
   if (add) {
     hipLaunchKernelGGL((bwdk_prep_kernel<E, DK, true>), dim3(items), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL((bwdk_fwd_kernel<E, DK, true>), dim3(serial), dim3(256), 0, stream, p);
+    if (!p.states_ready)
+      hipLaunchKernelGGL((bwdk_fwd_kernel<E, DK, true>), dim3(serial), dim3(256), 0, stream, p);
     hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, true>), dim3(serial), dim3(256), 0, stream, p);
     hipLaunchKernelGGL((bwdk_chunk_kernel<E, DK, true>), dim3(items), dim3(512), 0, stream, p);
   } else {
     hipLaunchKernelGGL((bwdk_prep_kernel<E, DK, false>), dim3(items), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL((bwdk_fwd_kernel<E, DK, false>), dim3(serial), dim3(256), 0, stream, p);
+    if (!p.states_ready)
+      hipLaunchKernelGGL((bwdk_fwd_kernel<E, DK, false>), dim3(serial), dim3(256), 0, stream, p);
     hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, false>), dim3(serial), dim3(256), 0, stream, p);
     hipLaunchKernelGGL((bwdk_chunk_kernel<E, DK, false>), dim3(items), dim3(512), 0, stream, p);
   }

@@ -1372,6 +1372,8 @@ hipError_t launch_fwd_pipe(const FwdParams &p, int gate, bool add, hipStream_t s
       case 2 * GATE_HEAD + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_HEAD, true, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
       case 2 * GATE_CONST: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_CONST, false, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
       case 2 * GATE_CONST + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_CONST, true, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+      case 2 * GATE_KEY: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_KEY, false, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
+      case 2 * GATE_KEY + 1: hipLaunchKernelGGL((fwd_pipe_kernel<GATE_KEY, true, true>), dim3(blocks), dim3(NT), 0, stream, p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

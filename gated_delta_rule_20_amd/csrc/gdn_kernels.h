@@ -112,6 +112,7 @@ struct BwdKeyParams {
   float *dinit;                  // NULL | [N, H, d_k, d_v]
   int N, H, T, dv;
   long slots;
+  int states_ready;              // the chunk-entering states are already in `states`
 };
 hipError_t launch_bwd_key(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream);
 
@@ -175,6 +176,7 @@ hipError_t launch_fwd_fused(const FwdParams &p, int dtype, int dk, int dvb, int 
 // gate: GATE_NONE, GATE_HEAD, GATE_CONST or GATE_KEY (the latter with the prepared
 // operands, delta write only); add: the additive write.
 // Gate NONE or HEAD; gate KEY after launch_key_prep, with the k_hat, tp_img, egc fields.
+// With chunk_states set (every gate): the chunk-entering states instead of o.
 hipError_t launch_fwd_pipe(const FwdParams &p, int gate, bool add, hipStream_t stream);
 // Per-key-channel gate, bf16, d_k = 128: for every chunk (all in parallel) the
 // pre-scaled operands K e^G, Q e^G, K e^{g_C - G}, e^{g_C}, and T diag(beta) and P as
