@@ -368,14 +368,28 @@ __global__ __launch_bounds__(256, 1) void bwdk_fwd_kernel(BwdKeyParams p) {
 }
 
 // ---------------------------------------------------------------- 3. reverse state pass
+// The gradient dM of the chunk-end state stays in the matrix-core accumulators of the
+// four waves (d_k / 4 key rows each, 32 value columns) for the whole sequence.  Per
+// chunk (in reverse): dDelta = P^T dO + Kh dM, Y = T^T dDelta, dV = diag(beta) Y,
+// dM <- diag(gam) dM + Qt^T dO - Kt^T diag(beta) Y.  The B operands (dM, dO, dDelta,
+// -diag(beta) Y) are staged once per chunk in LDS, transposed and split into hi and lo
+// bf16 halves, so that every fragment is two 16-byte reads; the A operands are read
+// from the workspace one phase ahead of their products.
 template <typename E, int DK, bool ADD>
 __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
-  __shared__ __align__(16) float dMs[DK * SV];
-  __shared__ __align__(16) float dOs[KC * SV];
-  __shared__ __align__(16) float dDs[KC * SV];
-  __shared__ __align__(16) float Ys[KC * SV];
+  constexpr int PM = DK + 8, PV = KC + 8;  // bf16 pitches of the transposed operands
+  constexpr int NCT = KBV / 16, RB = DK / 64, SK = DK / 32;
+  constexpr bool VX = std::is_same<E, bf16>::value;  // dO exact in bf16: no lo half
+  __shared__ __align__(16) bf16 dMh[KBV * PM];
+  __shared__ __align__(16) bf16 dMl[KBV * PM];
+  __shared__ __align__(16) bf16 dOh[KBV * PV];
+  __shared__ __align__(16) bf16 dOl[KBV * PV];
+  __shared__ __align__(16) bf16 dDh[KBV * PV];
+  __shared__ __align__(16) bf16 dDl[KBV * PV];
+  __shared__ __align__(16) bf16 bYh[KBV * PV];
+  __shared__ __align__(16) bf16 bYl[KBV * PV];
   __shared__ float bsh[KC], gsh[DK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H, dv = p.dv, nb = dv / KBV;
   const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
@@ -386,111 +400,208 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
   const int nchunks = (len + KC - 1) / KC;
   const long slot0 = (tok0 >> 6) + n;
   const size_t sbase = ((size_t)n * H + h) * DK * dv + col0;
-  for (int i = tid; i < DK * KBV; i += 256) {
-    const int d = i / KBV, j = i % KBV;
-    dMs[d * SV + j] = p.dfinal ? p.dfinal[sbase + (size_t)d * dv + j] : 0.f;
+  // dM: wave w holds key rows 16 (RB w + rb) + 4 lg + j, value columns 16 ct + lm
+  f32x4 dM[RB][NCT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 16 * (RB * wave + rb) + 4 * lg + j;
+        dM[rb][ct][j] = p.dfinal ? p.dfinal[sbase + (size_t)d * dv + 16 * ct + lm] : 0.f;
+      }
+  auto put_t = [&](bf16 *Xh, bf16 *Xl, int pitch, int r0, int ct, const f32x4 &v) {
+    bf16x4 hv, lv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hv[j] = (bf16)v[j];
+      lv[j] = (bf16)(v[j] - (float)hv[j]);
+    }
+    const int o = (16 * ct + lm) * pitch + r0 + 4 * lg;
+    *(bf16x4 *)(Xh + o) = hv;
+    *(bf16x4 *)(Xl + o) = lv;
+  };
+  auto bfrag = [&](const bf16 *Xh, const bf16 *Xl, int pitch, int ct, int k0) {
+    const int o = (16 * ct + lm) * pitch + k0 + 8 * lg;
+    return Split{ld8(Xh + o), ld8(Xl + o)};
+  };
+  auto ofrag = [&](int ct, int k0) {
+    if constexpr (VX) {
+      return ld8(dOh + (16 * ct + lm) * PV + k0 + 8 * lg);
+    } else {
+      return bfrag(dOh, dOl, PV, ct, k0);
+    }
+  };
+  typedef decltype(ofrag(0, 0)) OF;
+  const int r0 = 16 * wave + lm;  // this lane's A row of the 64-row products
+  const int s0 = wave >> 1;       // P^T and T^T rows of block w vanish below column 16 w
+  // A fragments (fp32 rows of the workspace), loaded one phase ahead, split when used
+  f32x8 f_pm[2], f_kh[SK], f_tm[2], f_qt[RB][2], f_kt[RB][2];
+  auto load_1 = [&](size_t sh) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s >= s0) f_pm[s] = ld8(p.pmT + (sh * KC + r0) * KC + 32 * s + 8 * lg);
+#pragma unroll
+    for (int s = 0; s < SK; ++s) f_kh[s] = ld8(p.kh + (sh * KC + r0) * DK + 32 * s + 8 * lg);
+  };
+  auto load_2 = [&](size_t sh) {
+    if constexpr (!ADD)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        if (s >= s0) f_tm[s] = ld8(p.tmT + (sh * KC + r0) * KC + 32 * s + 8 * lg);
+  };
+  auto load_3 = [&](size_t sh) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int d = 16 * (RB * wave + rb) + lm;
+        f_qt[rb][s] = ld8(p.qtT + (sh * DK + d) * KC + 32 * s + 8 * lg);
+        if (!ADD) f_kt[rb][s] = ld8(p.ktT + (sh * DK + d) * KC + 32 * s + 8 * lg);
+      }
+  };
+  // dO of a chunk, beta and e^{g_C} (no branch around a load: rows past the end read
+  // the last row and are zeroed when staged)
+  constexpr int VC = KBV / 4, VL = VC * (int)sizeof(E) / 16;
+  u32x4 oraw[VL];
+  float bnext = 0.f, gnext = 0.f;
+  auto load_o = [&](int cc) {
+    const int nvc = min(KC, len - cc * KC);
+    const size_t tbc = (size_t)tok0 + (size_t)cc * KC;
+    const int r = min(tid >> 2, nvc - 1), g = tid & 3;
+    const E *src = (const E *)p.dout + ((tbc + r) * H + h) * dv + col0 + VC * g;
+#pragma unroll
+    for (int u = 0; u < VL; ++u) oraw[u] = *(const u32x4 *)(src + u * (16 / (int)sizeof(E)));
+    if (!ADD) bnext = p.beta[(tbc + min(tid % KC, nvc - 1)) * H + h];
+    gnext = p.gam[((size_t)(slot0 + cc) * H + h) * DK + tid % DK];
+  };
+  if (nchunks > 0) {
+    load_1((size_t)(slot0 + nchunks - 1) * H + h);
+    load_o(nchunks - 1);
   }
-  __syncthreads();
   for (int c = nchunks - 1; c >= 0; --c) {
     const size_t sh = (size_t)(slot0 + c) * H + h;
     const int nv = min(KC, len - c * KC);
     const size_t tbase = (size_t)tok0 + (size_t)c * KC;
-    for (int i = tid; i < DK * KBV; i += 256) {
-      const int d = i / KBV, j = i % KBV;
-      p.dmc[(sh * DK + d) * dv + col0 + j] = dMs[d * SV + j];
+    // the chunk-end gradient: to the workspace and, split, to LDS
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 16 * (RB * wave + rb) + 4 * lg + j;
+          p.dmc[(sh * DK + d) * dv + col0 + 16 * ct + lm] = dM[rb][ct][j];
+        }
+        put_t(dMh, dMl, PM, 16 * (RB * wave + rb), ct, dM[rb][ct]);
+      }
+    {
+      const int r = tid >> 2, g = tid & 3;
+      const bool in = r < nv;
+#pragma unroll
+      for (int u = 0; u < VL; ++u) {
+        typedef E EV __attribute__((ext_vector_type(16 / sizeof(E))));
+        const EV ev = __builtin_bit_cast(EV, oraw[u]);
+#pragma unroll
+        for (int e = 0; e < 16 / (int)sizeof(E); ++e) {
+          const float x = in ? to_f(ev[e]) : 0.f;
+          const int col = VC * g + u * (16 / (int)sizeof(E)) + e;
+          const bf16 hv = (bf16)x;
+          dOh[col * PV + r] = hv;
+          if constexpr (!VX) dOl[col * PV + r] = (bf16)(x - (float)hv);
+        }
+      }
+      if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? bnext : 0.f;
+      if (tid < DK) gsh[tid] = gnext;
     }
-    for (int i = tid; i < KC * KBV; i += 256) {
-      const int r = i / KBV, j = i % KBV;
-      dOs[r * SV + j] = r < nv ? to_f(((const E *)p.dout)[((tbase + r) * H + h) * dv + col0 + j]) : 0.f;
-    }
-    if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? p.beta[(tbase + tid) * H + h] : 0.f;
-    if (tid < DK) gsh[tid] = p.gam[sh * DK + tid];
     __syncthreads();
-    // dDelta = P^T dO + Kh dM  (P^T[r][i] = P[i][r] is zero for i < r)
-    for (int t = wave; t < 8; t += 4) {
-      const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
-      const f32x4 a1 = kprod<KC>([&](int k0) { return ld8(p.pmT + (sh * KC + m0 + lm) * KC + k0 + 8 * lg); },
-                                 [&](int k0) {
-                                   f32x8 f;
+    load_2(sh);
+    OF fo[NCT][2];
 #pragma unroll
-                                   for (int ii = 0; ii < 8; ++ii) f[ii] = dOs[(k0 + 8 * lg + ii) * SV + n0 + lm];
-                                   return f;
-                                 },
-                                 m0, KC);
-      const f32x4 a2 = kprod<DK>([&](int k0) { return ld8(p.kh + (sh * KC + m0 + lm) * DK + k0 + 8 * lg); },
-                                 [&](int k0) {
-                                   f32x8 f;
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                                   for (int ii = 0; ii < 8; ++ii) f[ii] = dMs[(k0 + 8 * lg + ii) * SV + n0 + lm];
-                                   return f;
-                                 });
+      for (int s = 0; s < 2; ++s) fo[ct][s] = ofrag(ct, 32 * s);
+    // dDelta = P^T dO + Kh dM
+    {
+      f32x4 D[NCT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = m0 + 4 * lg + j;
-        const float x = a1[j] + a2[j];
-        dDs[r * SV + n0 + lm] = x;
-        p.dd[(sh * KC + r) * dv + col0 + n0 + lm] = x;
+      for (int ct = 0; ct < NCT; ++ct) {
+        D[ct] = zero4();
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          if (s >= s0) D[ct] = mm(split8(f_pm[s]), fo[ct][s], D[ct]);
+#pragma unroll
+        for (int s = 0; s < SK; ++s) D[ct] = mm(split8(f_kh[s]), bfrag(dMh, dMl, PM, ct, 32 * s), D[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * wave + 4 * lg + j;
+          p.dd[(sh * KC + r) * dv + col0 + 16 * ct + lm] = D[ct][j];
+          if (ADD && r < nv) ((E *)p.dv_out)[((tbase + r) * H + h) * dv + col0 + 16 * ct + lm] = to_e<E>(D[ct][j]);
+        }
+        if constexpr (!ADD) put_t(dDh, dDl, PV, 16 * wave, ct, D[ct]);
       }
     }
     __syncthreads();
+    load_3(sh);
     if constexpr (!ADD) {
-      // Y = T^T dDelta  (T^T[r][i] = T[i][r] is zero for i < r)
-      for (int t = wave; t < 8; t += 4) {
-        const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
-        const f32x4 acc = kprod<KC>([&](int k0) { return ld8(p.tmT + (sh * KC + m0 + lm) * KC + k0 + 8 * lg); },
-                                    [&](int k0) {
-                                      f32x8 f;
+      // Y = T^T dDelta;  dV = diag(beta) Y;  -diag(beta) Y into LDS for the dM update
+      f32x4 Y[NCT];
 #pragma unroll
-                                      for (int ii = 0; ii < 8; ++ii) f[ii] = dDs[(k0 + 8 * lg + ii) * SV + n0 + lm];
-                                      return f;
-                                    },
-                                    m0, KC);
+      for (int ct = 0; ct < NCT; ++ct) {
+        Y[ct] = zero4();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Ys[(m0 + 4 * lg + j) * SV + n0 + lm] = acc[j];
+        for (int s = 0; s < 2; ++s)
+          if (s >= s0) Y[ct] = mm(split8(f_tm[s]), bfrag(dDh, dDl, PV, ct, 32 * s), Y[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 nb4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * wave + 4 * lg + j;
+          const float by = bsh[r] * Y[ct][j];
+          nb4[j] = -by;
+          if (r < nv) ((E *)p.dv_out)[((tbase + r) * H + h) * dv + col0 + 16 * ct + lm] = to_e<E>(by);
+        }
+        put_t(bYh, bYl, PV, 16 * wave, ct, nb4);
       }
       __syncthreads();
     }
-    const float *Y = ADD ? dDs : Ys;
-    for (int i = tid; i < KC * KBV; i += 256) {
-      const int r = i / KBV, j = i % KBV;
-      if (r < nv)
-        ((E *)p.dv_out)[((tbase + r) * H + h) * dv + col0 + j] = to_e<E>(ADD ? Y[r * SV + j] : bsh[r] * Y[r * SV + j]);
+    if (c > 0) {
+      load_1(sh - H);
+      load_o(c - 1);
     }
     // dM <- diag(gam) dM + Qt^T dO - Kt^T diag(beta) Y
-    for (int t = wave; t < (DK / 16) * 2; t += 4) {
-      const int m0 = 16 * (t >> 1), n0 = 16 * (t & 1);
-      const f32x4 a1 = kprod<KC>([&](int k0) { return ld8(p.qtT + (sh * DK + m0 + lm) * KC + k0 + 8 * lg); },
-                                 [&](int k0) {
-                                   f32x8 f;
 #pragma unroll
-                                   for (int ii = 0; ii < 8; ++ii) f[ii] = dOs[(k0 + 8 * lg + ii) * SV + n0 + lm];
-                                   return f;
-                                 });
-      f32x4 a2 = zero4();
-      if constexpr (!ADD)
-        a2 = kprod<KC>([&](int k0) { return ld8(p.ktT + (sh * DK + m0 + lm) * KC + k0 + 8 * lg); },
-                       [&](int k0) {
-                         f32x8 f;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int d0 = 16 * (RB * wave + rb);
 #pragma unroll
-                         for (int ii = 0; ii < 8; ++ii) {
-                           const int k = k0 + 8 * lg + ii;
-                           f[ii] = bsh[k] * Y[k * SV + n0 + lm];
-                         }
-                         return f;
-                       });
+      for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = m0 + 4 * lg + j;
-        dMs[d * SV + n0 + lm] = gsh[d] * dMs[d * SV + n0 + lm] + a1[j] - a2[j];
+        for (int j = 0; j < 4; ++j) dM[rb][ct][j] *= gsh[d0 + 4 * lg + j];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          dM[rb][ct] = mm(split8(f_qt[rb][s]), fo[ct][s], dM[rb][ct]);
+          if constexpr (!ADD) dM[rb][ct] = mm(split8(f_kt[rb][s]), bfrag(bYh, bYl, PV, ct, 32 * s), dM[rb][ct]);
+        }
       }
     }
-    __syncthreads();
+    __syncthreads();  // every read of this chunk's dO, dM and -diag(beta) Y is done
   }
   if (p.dinit)
-    for (int i = tid; i < DK * KBV; i += 256) {
-      const int d = i / KBV, j = i % KBV;
-      p.dinit[sbase + (size_t)d * dv + j] = dMs[d * SV + j];
-    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 16 * (RB * wave + rb) + 4 * lg + j;
+          p.dinit[sbase + (size_t)d * dv + 16 * ct + lm] = dM[rb][ct][j];
+        }
 }
 
 // ---------------------------------------------------------------- 4. per-chunk gradients
