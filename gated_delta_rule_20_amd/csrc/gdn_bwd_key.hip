@@ -614,6 +614,9 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
   __shared__ float dTl[KC * SC];               // dT, then dA
   __shared__ float dPl[KC * SC];
   __shared__ __align__(16) float scr[3 * KC * SV];  // X', Delta, Y of a value slice; then W
+  __shared__ __align__(16) float Ms[DK * SV];       // the value slice of M0, dM and dDelta
+  __shared__ __align__(16) float dMs[DK * SV];
+  __shared__ __align__(16) float dDs[KC * SV];
   __shared__ float bsh[KC], gcl[DK], rb[2][KC], gcp[4][DK], dbys[KC];
   float *Xs = scr, *Ds = scr + KC * SV, *Ys = scr + 2 * KC * SV, *Wl = scr;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -656,6 +659,26 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
   float dby = 0.f, dgm = 0.f;
   const float *st = p.states + sh * DK * dv, *dmc = p.dmc + sh * DK * dv, *dd = p.dd + sh * KC * dv;
   for (int col0 = 0; col0 < dv; col0 += KBV) {
+    {  // the slice of M0, dM and dDelta: 16-byte loads, all in flight before the stores
+      constexpr int PS = KBV / 4, NS = DK * PS / 512;  // pieces per row, per thread
+      f32x4 xm[NS], xd[NS], xe;
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int pc = tid + 512 * u, d = pc / PS, g = pc % PS;
+        xm[u] = *(const f32x4 *)(st + (size_t)d * dv + col0 + 4 * g);
+        xd[u] = *(const f32x4 *)(dmc + (size_t)d * dv + col0 + 4 * g);
+      }
+      const int er = tid / PS, eg = tid % PS;  // KC * PS = 512 pieces of dDelta
+      xe = *(const f32x4 *)(dd + (size_t)er * dv + col0 + 4 * eg);
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int pc = tid + 512 * u, d = pc / PS, g = pc % PS;
+        *(f32x4 *)(Ms + d * SV + 4 * g) = xm[u];
+        *(f32x4 *)(dMs + d * SV + 4 * g) = xd[u];
+      }
+      *(f32x4 *)(dDs + er * SV + 4 * eg) = xe;
+    }
+    __syncthreads();
     {  // X' = V - Kt M0 (delta write) or Delta = V (additive write): eight tiles, one per wave
       const int m0 = 16 * (wave >> 1), n0 = 16 * (wave & 1);
       f32x4 acc = zero4();
@@ -664,7 +687,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
                         [&](int k0) {
                           f32x8 f;
 #pragma unroll
-                          for (int ii = 0; ii < 8; ++ii) f[ii] = st[(size_t)(k0 + 8 * lg + ii) * dv + col0 + n0 + lm];
+                          for (int ii = 0; ii < 8; ++ii) f[ii] = Ms[(k0 + 8 * lg + ii) * SV + n0 + lm];
                           return f;
                         });
 #pragma unroll
@@ -704,7 +727,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
           [&](int k0) {
             f32x8 f;
 #pragma unroll
-            for (int ii = 0; ii < 8; ++ii) f[ii] = dd[(size_t)(k0 + 8 * lg + ii) * dv + col0 + n0 + lm];
+            for (int ii = 0; ii < 8; ++ii) f[ii] = dDs[(k0 + 8 * lg + ii) * SV + n0 + lm];
             return f;
           },
           m0, KC);
@@ -718,7 +741,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
         for (int j = 0; j < KBV; ++j) dby += Ys[tid * SV + j] * Xs[tid * SV + j];
     }
     if (tid < DK)
-      for (int j = 0; j < KBV; ++j) dgm += st[(size_t)tid * dv + col0 + j] * dmc[(size_t)tid * dv + col0 + j];
+      for (int j = 0; j < KBV; ++j) dgm += Ms[tid * SV + j] * dMs[tid * SV + j];
     auto dorow = [&](int r, int k0) {
       return r < nv ? ldrow8<E>(doin + ((size_t)(tb + r) * H + h) * dv + col0 + k0 + 8 * lg) : zero8();
     };
@@ -729,19 +752,19 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
       aP[u] += kprod<KBV>([&](int k0) { return dorow(m0 + lm, k0); },
                           [&](int k0) { return ld8(Ds + (n0 + lm) * SV + k0 + 8 * lg); });
       if constexpr (!ADD)
-        aT[u] += kprod<KBV>([&](int k0) { return ld8(dd + (size_t)(m0 + lm) * dv + col0 + k0 + 8 * lg); },
+        aT[u] += kprod<KBV>([&](int k0) { return ld8(dDs + (m0 + lm) * SV + k0 + 8 * lg); },
                             [&](int k0) { return ld8(Xs + (n0 + lm) * SV + k0 + 8 * lg) * bsh[n0 + lm]; });
     }
     // dQt += dO M0^T, dKt -= diag(beta) Y M0^T, dKh += Delta dM^T  (64 x DK)
 #pragma unroll
     for (int u = 0; u < NCT; ++u) {
       const int m0 = 16 * wa, n0 = 16 * (wc + 2 * u);
-      auto fm = [&](int k0) { return ld8(st + (size_t)(n0 + lm) * dv + col0 + k0 + 8 * lg); };
+      auto fm = [&](int k0) { return ld8(Ms + (n0 + lm) * SV + k0 + 8 * lg); };
       aQ[u] += kprod<KBV>([&](int k0) { return dorow(m0 + lm, k0); }, fm);
       if constexpr (!ADD)
         aK[u] -= kprod<KBV>([&](int k0) { return ld8(Ys + (m0 + lm) * SV + k0 + 8 * lg) * bsh[m0 + lm]; }, fm);
       aH[u] += kprod<KBV>([&](int k0) { return ld8(Ds + (m0 + lm) * SV + k0 + 8 * lg); },
-                          [&](int k0) { return ld8(dmc + (size_t)(n0 + lm) * dv + col0 + k0 + 8 * lg); });
+                          [&](int k0) { return ld8(dMs + (n0 + lm) * SV + k0 + 8 * lg); });
     }
     __syncthreads();  // the slice buffers are rewritten by the next slice
   }
