@@ -613,12 +613,18 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
   __shared__ float Tl[KC * SC];
   __shared__ float dTl[KC * SC];               // dT, then dA
   __shared__ float dPl[KC * SC];
-  __shared__ __align__(16) float scr[3 * KC * SV];  // X', Delta, Y of a value slice; then W
-  __shared__ __align__(16) float Ms[DK * SV];       // the value slice of M0, dM and dDelta
-  __shared__ __align__(16) float dMs[DK * SV];
-  __shared__ __align__(16) float dDs[KC * SV];
+  // One region, three lives: the value slice of M0, dM and dDelta with the slice's X',
+  // Delta and Y; then W (in the second part); then K and Q of the chunk (the I/O dtype,
+  // rows of DK + 2 elements, so that a column read is free of bank conflicts).
+  constexpr int SLICE = (2 * DK + KC) * SV, PK = DK + 2;
+  constexpr int STG = SLICE + 3 * KC * SV;
+  static_assert(2 * KC * PK * (int)sizeof(E) <= STG * 4, "K and Q fit the staging region");
+  __shared__ __align__(16) float stg[STG];
   __shared__ float bsh[KC], gcl[DK], rb[2][KC], gcp[4][DK], dbys[KC];
+  float *Ms = stg, *dMs = stg + DK * SV, *dDs = stg + 2 * DK * SV;
+  float *scr = stg + SLICE;
   float *Xs = scr, *Ds = scr + KC * SV, *Ys = scr + 2 * KC * SV, *Wl = scr;
+  E *Kst = (E *)stg, *Qst = (E *)stg + KC * PK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H, dv = p.dv;
@@ -629,8 +635,9 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
   if (!slot_chunk(p, slot, tb, nv)) return;
   const size_t sh = (size_t)slot * H + h;
   const E *kin = (const E *)p.k, *qin = (const E *)p.q, *vin = (const E *)p.v, *doin = (const E *)p.dout;
-  auto K_ = [&](int r, int c) { return r < nv ? to_f(kin[((size_t)(tb + r) * H + h) * DK + c]) : 0.f; };
-  auto Q_ = [&](int r, int c) { return r < nv ? to_f(qin[((size_t)(tb + r) * H + h) * DK + c]) : 0.f; };
+  // K and Q from the staging region (after the value slices; rows past the end zero)
+  auto K_ = [&](int r, int c) { return to_f(Kst[r * PK + c]); };
+  auto Q_ = [&](int r, int c) { return to_f(Qst[r * PK + c]); };
   for (int i = tid; i < KC * DK; i += 512) {
     const int r = i / DK, d = i % DK;
     Gs[r * SG + d] = r < nv ? p.log_alpha[((size_t)(tb + r) * H + h) * DK + d] : 0.f;
@@ -836,6 +843,25 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
     __syncthreads();
   }
 
+  {  // K and Q of the chunk into the staging region (W and the slices are dead)
+    constexpr int VE = 16 / (int)sizeof(E), PR = DK / VE, NI = (KC * PR + 511) / 512;
+    typedef E EV __attribute__((ext_vector_type(16 / sizeof(E))));
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int pc = tid + 512 * u, r = pc / PR, g = pc % PR;
+      if (pc >= KC * PR) break;
+      const size_t o = ((size_t)(tb + r) * H + h) * DK + g * VE;
+      const u32x4 xk = r < nv ? *(const u32x4 *)(kin + o) : (u32x4){0u, 0u, 0u, 0u};
+      const u32x4 xq = r < nv ? *(const u32x4 *)(qin + o) : (u32x4){0u, 0u, 0u, 0u};
+      const EV ek = __builtin_bit_cast(EV, xk), eq = __builtin_bit_cast(EV, xq);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        Kst[r * PK + g * VE + e] = ek[e];
+        Qst[r * PK + g * VE + e] = eq[e];
+      }
+    }
+    __syncthreads();
+  }
   // ---- per-channel terms, tiles (row block wa, channel blocks wc + 2u)
   const int a = wa, mref = 16 * a + 7;
   float rbs[4] = {0.f, 0.f, 0.f, 0.f};
