@@ -94,19 +94,29 @@ bool use_pipe(const gdn_fwd_args *a) { return a->dtype == GDN_BF16 && a->d_k == 
 // The per-key-channel gate on the pipelined kernel: a first pass prepares every
 // chunk's operands in the workspace.
 bool key_pipe(const gdn_fwd_args *a) { return a->gate == GDN_GATE_KEY && use_pipe(a); }
+// Chunks per window of the windowed per-key-channel forward: long batch-mode sequences
+// run as consecutive windows, each launch preparing the next window's operands on the
+// CUs that the state pass of the current one leaves free.
+constexpr int KEY_WINDOW = 32;
+int key_windows(const gdn_fwd_args *a) {
+  const int nchunks = (a->T + 63) / 64;
+  return (!a->cu_seqlens && nchunks >= 2 * KEY_WINDOW) ? (nchunks + KEY_WINDOW - 1) / KEY_WINDOW : 1;
+}
 struct KeyLayout {
   long slots;
-  size_t kq, tp, eg;  // bytes of one pre-scaled K/Q array, the T/P images, e^{g_C}
-  size_t total() const { return 3 * kq + tp + eg; }
+  size_t kq, tp, eg, carry;  // bytes of one pre-scaled K/Q array, the T/P images, e^{g_C},
+                             // the state between windows
+  size_t total() const { return 3 * kq + tp + eg + carry; }
 };
 KeyLayout key_layout(const gdn_fwd_args *a) {
-  KeyLayout L{0, 0, 0, 0};
+  KeyLayout L{0, 0, 0, 0, 0};
   if (!key_pipe(a)) return L;
   const long tokens = (long)a->B * a->T;
   L.slots = gdn::key_slots(tokens, a->N);
   L.kq = align256((size_t)tokens * a->H * 128 * 2);
   L.tp = align256((size_t)L.slots * a->H * 16384);
   L.eg = align256((size_t)L.slots * a->H * 128 * 4);
+  if (key_windows(a) > 1) L.carry = align256((size_t)a->N * a->H * 128 * a->d_v * 4);
   return L;
 }
 
@@ -606,12 +616,33 @@ int fwd_chunked_launch(const gdn_fwd_args *a, void *ws_base, void *hip_stream) {
     kp.N = a->N;
     kp.H = a->H;
     kp.T = a->T;
-    if (gdn::launch_key_prep(kp, L.slots, a->write == GDN_WRITE_ADD, stream) != hipSuccess) return GDN_ERR_HIP;
     p.k = kp.k_g;  // the pipelined kernel then reads the pre-scaled operands
     p.q = kp.q_g;
     p.k_hat = kp.k_hat;
     p.tp_img = kp.tp_img;
     p.egc = kp.egc;
+    const bool add = a->write == GDN_WRITE_ADD;
+    const int windows = key_windows(a), ns = a->N * a->H * (a->d_v / 64), free_cus = gdn::device_cus() - ns;
+    if (windows > 1 && free_cus > 0) {
+      // window w's state pass shares a launch with window w + 1's preparation
+      float *carry = (float *)(ws + 3 * L.kq + L.tp + L.eg);
+      p.nb = a->d_v / 64;
+      kp.c_lo = 0;
+      kp.c_hi = KEY_WINDOW;
+      if (gdn::launch_key_prep(kp, L.slots, add, stream) != hipSuccess) return GDN_ERR_HIP;
+      for (int w = 0; w < windows; ++w) {
+        p.c_lo = w * KEY_WINDOW;
+        p.c_hi = (w + 1) * KEY_WINDOW;
+        p.init_state = w == 0 ? a->initial_state : carry;
+        p.final_state = w == windows - 1 ? a->final_state : carry;
+        kp.c_lo = (w + 1) * KEY_WINDOW;
+        kp.c_hi = (w + 2) * KEY_WINDOW;
+        if (gdn::launch_key_window(p, kp, L.slots, w + 1 < windows ? free_cus : 0, add, stream) != hipSuccess)
+          return GDN_ERR_HIP;
+      }
+      return GDN_OK;
+    }
+    if (gdn::launch_key_prep(kp, L.slots, add, stream) != hipSuccess) return GDN_ERR_HIP;
   }
   if (use_pipe(a)) {
     p.nb = a->d_v / 64;

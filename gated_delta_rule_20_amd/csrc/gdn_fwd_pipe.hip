@@ -338,9 +338,8 @@ __device__ __forceinline__ f32x4 gamma_tile(const GammaRegs &G, int a, int b, in
 
 // STATES: instead of o, store every chunk's entering state into p.chunk_states
 // ([slot, H, d_k, d_v], slot floor(tok0 / 64) + n + c), for the gradient pass.
-template <int GATE, bool ADD, bool STATES = false>
-__global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
-  __shared__ __align__(16) char smem[LDS_TOTAL];
+template <int GATE, bool ADD, bool STATES = false, bool WIN = false>
+__device__ __forceinline__ void fwd_pipe_body(const FwdParams &p, char *smem, const int bid) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lm = lane & 15;
@@ -349,7 +348,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   // head) get ids equal mod 8 (same XCD, shared L2 for K and Q).
   const int nb = p.nb;
   const int total = p.N * p.H * nb;
-  const int bid = blockIdx.x;
   const int grp = 8 * nb;
   const int full = (total / grp) * grp;
   int pair, jb;
@@ -373,6 +371,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
   } else {
     tok0 = (long)n * p.T;
     len = p.T;
+  }
+  if constexpr (WIN) {  // the chunk window [c_lo, c_hi) of the sequence (state in from
+    // init_state, out to final_state); a whole number of chunks, so slot
+    // floor(tok0 / 64) + n + c of the window's chunk c is the sequence's own slot of it
+    const int all = (len + C - 1) / C, cb = min(p.c_lo, all), ce = min(p.c_hi, all);
+    tok0 += (long)C * cb;
+    len = ce > cb ? min(len, C * ce) - C * cb : 0;
   }
   const int H = p.H, dv = p.dv, col0 = jb * DVB;
   const int nchunks = (len + C - 1) / C;
@@ -1017,6 +1022,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
 // decay over the rows between them); T = (I + A)^-1 by forward substitution of the
 // diagonal blocks in fp32 and block substitution on MFMA; T diag(beta) and P leave as
 // the 16 KiB LDS images the pipelined kernel loads (tp_off layout).
+template <int GATE, bool ADD, bool STATES = false>
+__global__ __launch_bounds__(NT, 1) void fwd_pipe_kernel(FwdParams p) {
+  __shared__ __align__(16) char smem[LDS_TOTAL];
+  fwd_pipe_body<GATE, ADD, STATES>(p, smem, blockIdx.x);
+}
+
 constexpr int KP_NT = 512;  // 8 waves
 constexpr int KP_SG = 132;  // row stride of the fp32 [64][128] tables (floats)
 constexpr int KP_SK = 136;  // row stride of the bf16 [64][128] operands
@@ -1056,8 +1067,8 @@ __device__ __forceinline__ void kp_barrier() {  // LDS-only barrier: loads stay 
 }
 
 template <bool ADD>
-__global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, long items) {
-  __shared__ __align__(16) char smem[KP_BYTES];
+__device__ __forceinline__ void key_prep_body(const KeyPrepParams &p, long items, char *smem, const int wg,
+                                              const int nwg) {
   float *Gs = (float *)(smem + KP_OFF_G);
   float *Et = Gs;  // e^{G[e] - G}, after the prefix is no longer read
   bf16 *Ks = (bf16 *)(smem + KP_OFF_K), *QA = (bf16 *)(smem + KP_OFF_QA);
@@ -1097,6 +1108,7 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
     if (tok0 < 0 || tend < tok0 || (p.cu_seqlens && tend > p.T)) return it;  // malformed offsets
     const long c = it.slot - ((tok0 >> 6) + lo);
     if (c < 0 || 64 * c >= tend - tok0) return it;
+    if (c < p.c_lo || c >= p.c_hi) return it;  // outside this pass's chunk window
     it.ok = true;
     it.nv = (int)min(64L, tend - tok0 - 64 * c);
     it.t0 = tok0 + 64 * c;
@@ -1125,10 +1137,10 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
     b_r = (!ADD && it.ok && tid < it.nv) ? p.beta[(size_t)(it.t0 + tid) * H + it.h] : 0.f;
   };
 
-  long w = blockIdx.x;
+  long w = wg;
   Item cur = decode(w);
   prefetch(cur);
-  for (; w < items; w += gridDim.x) {
+  for (; w < items; w += nwg) {
     const Item it = cur;
     const int nv = it.nv, h = it.h;
     const long t0 = it.t0, slot = it.slot;
@@ -1151,7 +1163,7 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
       for (int i = tid; i < PRE_BYTES / 16; i += KP_NT) ((uint4 *)img)[i] = make_uint4(0, 0, 0, 0);
       for (int i = tid; i < C * KP_ST * 2 / 16; i += KP_NT) ((uint4 *)As)[i] = make_uint4(0, 0, 0, 0);
     }
-    cur = decode(w + gridDim.x);
+    cur = decode(w + nwg);
     prefetch(cur);  // in flight while this item is computed
     if (!it.ok) continue;  // uniform over the workgroup
     kp_barrier();
@@ -1361,6 +1373,27 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
 
 }  // namespace
 
+template <bool ADD>
+__global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, long items) {
+  __shared__ __align__(16) char smem[KP_BYTES];
+  key_prep_body<ADD>(p, items, smem, blockIdx.x, gridDim.x);
+}
+
+// One pass of the windowed per-key-channel forward: workgroups [0, ns) run the state
+// pass over the chunk window of fp, the rest prepare the operands of kp's window (the
+// next one) in the same launch, on the CUs the state pass leaves free.  The two roles
+// touch disjoint chunk slots, so nothing in the launch waits for anything else.
+static_assert(NT == KP_NT, "both roles run with one block size");
+constexpr int WIN_LDS = LDS_TOTAL > KP_BYTES ? LDS_TOTAL : KP_BYTES;
+template <bool ADD>
+__global__ __launch_bounds__(NT, 1) void key_window_kernel(FwdParams fp, KeyPrepParams kp, long items, int ns) {
+  __shared__ __align__(16) char smem[WIN_LDS];
+  if ((int)blockIdx.x < ns)
+    fwd_pipe_body<GATE_KEY, ADD, false, true>(fp, smem, blockIdx.x);
+  else
+    key_prep_body<ADD>(kp, items, smem, (int)blockIdx.x - ns, (int)gridDim.x - ns);
+}
+
 hipError_t launch_fwd_pipe(const FwdParams &p, int gate, bool add, hipStream_t stream) {
   const int blocks = p.N * p.H * p.nb;
   if (blocks == 0) return hipSuccess;
@@ -1392,13 +1425,31 @@ hipError_t launch_fwd_pipe(const FwdParams &p, int gate, bool add, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_key_prep(const KeyPrepParams &p, long slots, bool add, hipStream_t stream) {
-  if (slots <= 0 || p.N <= 0 || p.H <= 0) return hipSuccess;
-  const long items = slots * p.H;
+int device_cus() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
+  return cus;
+}
+
+hipError_t launch_key_window(const FwdParams &fp, const KeyPrepParams &kp, long slots, int nprep, bool add,
+                             hipStream_t stream) {
+  const int ns = fp.N * fp.H * fp.nb;
+  const long items = slots * kp.H;
+  if (ns <= 0 || nprep < 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(ns + nprep));
+  if (add)
+    hipLaunchKernelGGL(key_window_kernel<true>, grid, dim3(NT), 0, stream, fp, kp, items, ns);
+  else
+    hipLaunchKernelGGL(key_window_kernel<false>, grid, dim3(NT), 0, stream, fp, kp, items, ns);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_prep(const KeyPrepParams &p, long slots, bool add, hipStream_t stream) {
+  if (slots <= 0 || p.N <= 0 || p.H <= 0) return hipSuccess;
+  const long items = slots * p.H;
+  const int cus = device_cus();
   const long grid = items < cus ? items : cus;  // persistent: one workgroup per CU
   if (add)
     hipLaunchKernelGGL(key_prep_kernel<true>, dim3((unsigned)grid), dim3(KP_NT), 0, stream, p, items);

@@ -36,6 +36,10 @@ struct FwdParams {
   // stored here ([slots, H, d_k, d_v], slot of chunk c as for key_slots) and o may be
   // NULL (not written).
   float *chunk_states;
+  // launch_key_window only: process the chunk window [c_lo, c_hi) of every sequence,
+  // the state entering the window read from init_state and the state leaving it
+  // written to final_state.
+  int c_lo = 0, c_hi = 1 << 30;
 };
 
 // Chunk slots of the per-key-channel preparation: chunk c of sequence n (first token
@@ -190,9 +194,15 @@ struct KeyPrepParams {
   void *tp_img;                  // [slots, H, 16384 B]
   float *egc;                    // [slots, H, 128]
   int N, H, T;
+  int c_lo = 0, c_hi = 1 << 30;  // prepare only chunks c_lo <= c < c_hi of each sequence
 };
 // add: operands for the additive write (no beta, no T, no K e^G).
 hipError_t launch_key_prep(const KeyPrepParams &p, long slots, bool add, hipStream_t stream);
+// One launch: the state pass over fp's chunk window (fp.N * fp.H * fp.nb workgroups)
+// and, on nprep more workgroups, the preparation of kp's chunk window.
+hipError_t launch_key_window(const FwdParams &fp, const KeyPrepParams &kp, long slots, int nprep, bool add,
+                             hipStream_t stream);
+int device_cus();
 hipError_t launch_seq_order(const int32_t *cu_seqlens, int N, int32_t *order, hipStream_t stream);
 hipError_t launch_recurrent_step(const StepParams &p, int dtype, int dk, int dv, int gate, bool add,
                                  hipStream_t stream);

@@ -224,6 +224,30 @@ def test_workload_kda_long(gdn):
     check(gdn, synth.workload_inputs("kda-bf16-B2-T16384-H16-d128"))
 
 
+@pytest.mark.parametrize("write", ["delta", "add"])
+@pytest.mark.parametrize("dv", [64, 128])
+def test_key_gate_windows(gdn, write, dv):
+    """Long batch sequences with one decay per key channel run as windows of 32 chunks
+    (the state carried between launches).  65 chunks and a ragged tail give three
+    windows, the last of one partial chunk.  Against the oracle, and bit for bit against
+    the same sequences packed (a packed call runs without windows)."""
+    T = 64 * 64 + 37
+    inp = synth.random_inputs(2, T, 2, 128, dv, "key", "bf16", seed=61 + dv, state_std=0.05)
+    if write == "add":
+        inp["beta"] = None
+    d = to_dev(inp)
+    o, fs = gdn.fwd_chunked(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["initial_state"], write=write)
+    cu = torch.tensor([0, T, 2 * T], dtype=torch.int32, device="cuda")
+    flat = lambda x: None if x is None else x.reshape(1, 2 * T, *x.shape[2:]).contiguous()
+    o2, fs2 = gdn.fwd_chunked(flat(d["q"]), flat(d["k"]), flat(d["v"]), flat(d["beta"]), flat(d["log_alpha"]),
+                              d["initial_state"], cu, write=write)
+    torch.cuda.synchronize()
+    assert torch.equal(o.reshape(1, 2 * T, 2, dv), o2) and torch.equal(fs, fs2)
+    o_ref, fs_ref = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], inp["initial_state"],
+                               gate="key", write=write)
+    assert relerr(o.cpu(), o_ref) <= TOL["bf16"] and relerr(fs.cpu(), fs_ref) <= TOL["bf16"]
+
+
 @pytest.fixture(scope="module")
 def varlen_run(gdn):
     """The packed workload (32 sequences, 283,220 tokens, 16 heads) on the GPU and in
