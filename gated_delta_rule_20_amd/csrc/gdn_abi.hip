@@ -629,6 +629,7 @@ int fwd_chunked_launch(const gdn_fwd_args *a, void *ws_base, void *hip_stream) {
       p.nb = a->d_v / 64;
       kp.c_lo = 0;
       kp.c_hi = KEY_WINDOW;
+      kp.win_items = 1;
       if (gdn::launch_key_prep(kp, L.slots, add, stream) != hipSuccess) return GDN_ERR_HIP;
       for (int w = 0; w < windows; ++w) {
         p.c_lo = w * KEY_WINDOW;

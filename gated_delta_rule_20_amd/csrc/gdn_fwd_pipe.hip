@@ -1094,6 +1094,18 @@ __device__ __forceinline__ void key_prep_body(const KeyPrepParams &p, long items
   auto decode = [&](long w) {
     Item it{false, 0, 0, 0, 0};
     if (w >= items) return it;
+    if (p.win_items) {  // batch mode, item = (sequence, chunk of the window, head)
+      const int wn = p.c_hi - p.c_lo;
+      const long sq = w / ((long)wn * H), rem = w % ((long)wn * H);
+      const long c = p.c_lo + rem / H, tok0 = sq * p.T;
+      it.h = (int)(rem % H);
+      if (64 * c >= p.T) return it;
+      it.slot = (tok0 >> 6) + sq + c;
+      it.ok = true;
+      it.nv = (int)min(64L, (long)p.T - 64 * c);
+      it.t0 = tok0 + 64 * c;
+      return it;
+    }
     it.slot = w / H;
     it.h = (int)(w % H);
     auto tok_start = [&](int sq) -> long { return p.cu_seqlens ? (long)p.cu_seqlens[sq] : (long)sq * p.T; };
@@ -1436,7 +1448,7 @@ int device_cus() {
 hipError_t launch_key_window(const FwdParams &fp, const KeyPrepParams &kp, long slots, int nprep, bool add,
                              hipStream_t stream) {
   const int ns = fp.N * fp.H * fp.nb;
-  const long items = slots * kp.H;
+  const long items = kp.win_items ? (long)kp.N * (kp.c_hi - kp.c_lo) * kp.H : slots * kp.H;
   if (ns <= 0 || nprep < 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(ns + nprep));
   if (add)
@@ -1448,7 +1460,7 @@ hipError_t launch_key_window(const FwdParams &fp, const KeyPrepParams &kp, long 
 
 hipError_t launch_key_prep(const KeyPrepParams &p, long slots, bool add, hipStream_t stream) {
   if (slots <= 0 || p.N <= 0 || p.H <= 0) return hipSuccess;
-  const long items = slots * p.H;
+  const long items = p.win_items ? (long)p.N * (p.c_hi - p.c_lo) * p.H : slots * p.H;
   const int cus = device_cus();
   const long grid = items < cus ? items : cus;  // persistent: one workgroup per CU
   if (add)

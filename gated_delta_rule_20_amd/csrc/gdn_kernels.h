@@ -195,6 +195,7 @@ struct KeyPrepParams {
   float *egc;                    // [slots, H, 128]
   int N, H, T;
   int c_lo = 0, c_hi = 1 << 30;  // prepare only chunks c_lo <= c < c_hi of each sequence
+  int win_items = 0;             // batch mode: walk only the window's (sequence, chunk, head)
 };
 // add: operands for the additive write (no beta, no T, no K e^G).
 hipError_t launch_key_prep(const KeyPrepParams &p, long slots, bool add, hipStream_t stream);
