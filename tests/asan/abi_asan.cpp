@@ -28,6 +28,8 @@ STUB(launch_dplr_decode(const DplrDecodeParams &, int, int, int, int, hipStream_
 STUB(launch_fwd_fused(const FwdParams &, int, int, int, int, bool, hipStream_t))
 STUB(launch_fwd_pipe(const FwdParams &, int, bool, hipStream_t))
 STUB(launch_key_prep(const KeyPrepParams &, long, bool, hipStream_t))
+STUB(launch_key_window(const FwdParams &, const KeyPrepParams &, long, int, bool, hipStream_t))
+int device_cus() { return 256; }
 STUB(launch_seq_order(const int32_t *, int, int32_t *, hipStream_t))
 STUB(launch_recurrent_step(const StepParams &, int, int, int, int, bool, hipStream_t))
 STUB(launch_decode(const DecodeParams &, int, int, int, int, bool, hipStream_t))
