@@ -215,7 +215,8 @@ __global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdP
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = p.H, dv = p.dv, nb = dv / BVB;
-  const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
+  int pair, jb;
+  xcd_pair_block(blockIdx.x, p.N * p.H, nb, pair, jb);
   const int n = pair / H, h = pair % H, col0 = jb * BVB;
   long tok0;
   int len;

@@ -281,7 +281,8 @@ __global__ __launch_bounds__(256, 1) void bwdk_fwd_kernel(BwdKeyParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H, dv = p.dv, nb = dv / KBV;
-  const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
+  int pair, jb;
+  xcd_pair_block(blockIdx.x, p.N * p.H, nb, pair, jb);
   const int n = pair / H, h = pair % H, col0 = jb * KBV;
   long tok0;
   int len;
@@ -392,7 +393,8 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H, dv = p.dv, nb = dv / KBV;
-  const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
+  int pair, jb;
+  xcd_pair_block(blockIdx.x, p.N * p.H, nb, pair, jb);
   const int n = pair / H, h = pair % H, col0 = jb * KBV;
   long tok0;
   int len;

@@ -50,7 +50,8 @@ __global__ __launch_bounds__(DNT, 1) void dplr_fwd_kernel(DplrParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H, dv = p.dv, nb = dv / DVB;
-  const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
+  int pair, jb;
+  xcd_pair_block(blockIdx.x, p.N * p.H, nb, pair, jb);
   const int n = pair / H, h = pair % H, col0 = jb * DVB;
   long tok0;
   int len;
@@ -288,7 +289,8 @@ __global__ __launch_bounds__(DNB, 1) void dplr_bf16_kernel(DplrParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H, dv = p.dv, nb = dv / DVB;
-  const int jb = blockIdx.x % nb, pair = blockIdx.x / nb;
+  int pair, jb;
+  xcd_pair_block(blockIdx.x, p.N * p.H, nb, pair, jb);
   const int n = pair / H, h = pair % H, col0 = jb * DVB;
   long tok0;
   int len;

@@ -144,6 +144,22 @@ __device__ __forceinline__ bf16x8 col_frag(const bf16 *X, int pitch, int k0, int
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Workgroup bid of a grid of `pairs` (sequence, head) pairs x nb value blocks -> (pair,
+// value block), such that the nb blocks of one pair get ids equal mod 8: consecutive
+// ids go to the eight XCDs in turn, so the blocks of a pair run on one XCD and share its
+// L2 for the operands that every block of the pair reads.
+__device__ __forceinline__ void xcd_pair_block(int bid, int pairs, int nb, int &pair, int &jb) {
+  const int grp = 8 * nb, full = (pairs * nb / grp) * grp;
+  if (bid < full) {
+    const int slot = bid >> 3;
+    pair = (slot / nb) * 8 + (bid & 7);
+    jb = slot % nb;
+  } else {
+    pair = bid / nb;
+    jb = bid % nb;
+  }
+}
+
 // x as a hi + lo pair of bf16 (see Split) stored at hi[i] and lo[i].
 __device__ __forceinline__ void store_split(bf16 *hi, bf16 *lo, size_t i, float x) {
   const bf16 h = (bf16)x;
