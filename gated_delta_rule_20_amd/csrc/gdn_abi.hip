@@ -257,53 +257,38 @@ DplrKeyLayout dplr_key_layout(const gdn_dplr_args *a) {
   return L;
 }
 
+// The backward's workspace: the fp32 arrays of BwdKeyParams / BwdParams, in this order,
+// then the constant decay's per-token gradients
 struct BwdLayout {
   long slots;
-  size_t states, tmat, pmat, part, dla;
-  size_t total() const { return states + tmat + pmat + part + dla; }
-};
-// The per-key-channel gate: the fp32 arrays of BwdKeyParams, in this order
-struct BwdKeyLayout {
-  long slots;
-  size_t sz[12];
+  size_t sz[13];
   size_t total() const {
     size_t t = 0;
     for (size_t x : sz) t += x;
     return t;
   }
 };
-BwdKeyLayout bwd_key_layout(const gdn_bwd_args *a) {
-  BwdKeyLayout L{};
+BwdLayout bwd_layout(const gdn_bwd_args *a) {
+  BwdLayout L{};
   const long tokens = (long)a->B * a->T;
   L.slots = gdn::key_slots(tokens, a->N);
   const size_t sh = (size_t)L.slots * a->H, dk = a->d_k, dv = a->d_v;
-  const bool delta = a->write == GDN_WRITE_DELTA;
-  const size_t sizes[12] = {
-      sh * dk * dv * 4,          // states
-      sh * dk * dv * 4,          // chunk-end state gradients
-      sh * 64 * dv * 4,          // dDelta
-      delta ? sh * 4096 * 4 : 0, // T
-      delta ? sh * 4096 * 4 : 0, // T^T
-      sh * 4096 * 4,             // P^T
-      delta ? sh * 64 * dk * 4 : 0,  // K e^G
-      sh * 64 * dk * 4,          // K e^{g_C - G}
-      delta ? sh * dk * 64 * 4 : 0,  // (K e^G)^T
-      sh * dk * 64 * 4,          // (Q e^G)^T
-      sh * dk * 64 * 4,          // (K e^{g_C - G})^T
-      sh * dk * 4};              // e^{g_C}
-  for (int i = 0; i < 12; ++i) L.sz[i] = align256(sizes[i]);
-  return L;
-}
-BwdLayout bwd_layout(const gdn_bwd_args *a) {
-  BwdLayout L{0, 0, 0, 0, 0, 0};
-  const long tokens = (long)a->B * a->T;
-  L.slots = gdn::key_slots(tokens, a->N);
-  L.states = align256((size_t)L.slots * a->H * a->d_k * a->d_v * 4);
-  if (a->write == GDN_WRITE_DELTA) L.tmat = align256((size_t)L.slots * a->H * 64 * 64 * 4);  // T per chunk
-  L.pmat = align256((size_t)L.slots * a->H * 64 * 64 * 4);  // P per chunk
-  L.part = align256((size_t)L.slots * a->H * (a->d_v / 32) * gdn::bwd_part_floats(a->d_k) * 4);
-  // the constant per-head decay: per-token gradients, summed per head afterwards
-  if (a->gate == GDN_GATE_HEAD_CONST) L.dla = align256((size_t)tokens * a->H * 4);
+  const bool delta = a->write == GDN_WRITE_DELTA, key = a->gate == GDN_GATE_KEY;
+  const size_t sizes[13] = {
+      sh * dk * dv * 4,                    // states
+      sh * dk * dv * 4,                    // chunk-end state gradients
+      sh * 64 * dv * 4,                    // dDelta
+      delta ? sh * 4096 * 4 : 0,           // T
+      delta ? sh * 4096 * 4 : 0,           // T^T
+      sh * 4096 * 4,                       // P^T
+      key && delta ? sh * 64 * dk * 4 : 0, // K e^G (per key channel)
+      sh * 64 * dk * 4,                    // K e^{g_C - G}
+      delta ? sh * dk * 64 * 4 : 0,        // (K e^G)^T
+      sh * dk * 64 * 4,                    // (Q e^G)^T
+      key ? sh * dk * 64 * 4 : 0,          // (K e^{g_C - G})^T (per key channel)
+      sh * dk * 4,                         // e^{g_C}
+      a->gate == GDN_GATE_HEAD_CONST ? (size_t)tokens * a->H * 4 : 0};  // per-token decay gradients
+  for (int i = 0; i < 13; ++i) L.sz[i] = align256(sizes[i]);
   return L;
 }
 
@@ -313,14 +298,14 @@ extern "C" {
 
 size_t gdn_bwd_workspace_size(const gdn_bwd_args *a) {
   if (check_bwd(a) != GDN_OK) return 0;
-  return a->gate == GDN_GATE_KEY ? bwd_key_layout(a).total() : bwd_layout(a).total();
+  return bwd_layout(a).total();
 }
 
 int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   const int st = check_bwd(a);
   if (st != GDN_OK) return st;
   const BwdLayout L = bwd_layout(a);
-  const size_t need = a->gate == GDN_GATE_KEY ? bwd_key_layout(a).total() : L.total();
+  const size_t need = L.total();
   if (!a->workspace || a->workspace_bytes < need || !aligned(a->workspace, 256)) return GDN_ERR_WORKSPACE;
   const long tokens = (long)a->B * a->T;
   if (a->N == 0 || tokens == 0) {
@@ -341,14 +326,15 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   }
   hipStream_t stream = (hipStream_t)hip_stream;
   char *ws = (char *)a->workspace;
-  if (a->gate == GDN_GATE_KEY) {
-    const BwdKeyLayout KL = bwd_key_layout(a);
-    float *arr[12];
+  float *arr[13];
+  {
     size_t off = 0;
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < 13; ++i) {
       arr[i] = (float *)(ws + off);
-      off += KL.sz[i];
+      off += L.sz[i];
     }
+  }
+  if (a->gate == GDN_GATE_KEY) {
     gdn::BwdKeyParams kp;
     kp.q = a->q;
     kp.k = a->k;
@@ -381,11 +367,11 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
     kp.H = a->H;
     kp.T = a->T;
     kp.dv = a->d_v;
-    kp.slots = KL.slots;
+    kp.slots = L.slots;
     kp.states_ready = 0;
     const gdn_fwd_args f = fwd_of(a);
     const KeyLayout FL = key_layout(&f);
-    if (FL.slots && FL.total() <= KL.sz[1] + KL.sz[2]) {
+    if (FL.slots && FL.total() <= L.sz[1] + L.sz[2]) {
       // bf16 with d_k = 128: the forward's own per-channel path recomputes the chunk
       // states (its preparation's operands go to the chunk-end-gradient and dDelta
       // arrays, which the reverse pass writes only afterwards)
@@ -457,7 +443,7 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   const bool add = a->write == GDN_WRITE_ADD;
   const int la_stride = a->gate == GDN_GATE_HEAD_CONST ? 0 : a->H;
   fp.la_stride = la_stride;
-  fp.chunk_states = (float *)ws;
+  fp.chunk_states = arr[0];
   const gdn_fwd_args f = fwd_of(a);
   if (use_pipe(&f)) {  // bf16, d_k = 128: the pipelined kernel, chunk states instead of o
     fp.nb = a->d_v / 64;
@@ -469,7 +455,7 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
         hipSuccess)
       return GDN_ERR_HIP;
   }
-  // 2. reverse state pass and 3. per-chunk gradients
+  // 2. operands, 3. reverse state pass, 4. per-chunk gradients
   gdn::BwdParams bp;
   bp.q = a->q;
   bp.k = a->k;
@@ -479,15 +465,21 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   bp.log_alpha = a->log_alpha;
   bp.dfinal = a->dfinal_state;
   bp.cu_seqlens = a->cu_seqlens;
-  bp.states = (const float *)ws;
-  bp.tmat = (float *)(ws + L.states);
-  bp.pmat = (float *)(ws + L.states + L.tmat);
-  bp.part = (float *)(ws + L.states + L.tmat + L.pmat);
+  bp.states = arr[0];
+  bp.dmc = arr[1];
+  bp.dd = arr[2];
+  bp.tm = arr[3];
+  bp.tmT = arr[4];
+  bp.pmT = arr[5];
+  bp.kh = arr[7];
+  bp.ktT = arr[8];
+  bp.qtT = arr[9];
+  bp.gam = arr[11];
   bp.dq = a->dq;
   bp.dk = a->dk;
   bp.dv_out = a->dv;
   bp.dbeta = a->dbeta;
-  float *const dla_tok = (float *)(ws + L.states + L.tmat + L.pmat + L.part);
+  float *const dla_tok = arr[12];
   bp.dlog_alpha = a->gate == GDN_GATE_HEAD_CONST ? dla_tok : a->dlog_alpha;
   bp.la_stride = la_stride;
   bp.dinit = a->dinitial_state;

@@ -16,25 +16,26 @@
 // then A, P, Gamma, Kt, Qt, Kh and gam give dq, dk, dbeta and dG, and d log alpha_t is
 // the sum of dG_r over r >= t in the chunk plus dG_C.
 //
-// Four launches:
+// Four launches, everything in between in the caller's workspace (fp32):
 //  1. a forward that stores every chunk's entering state M0 instead of o: the
 //     pipelined kernel's STATES variant for bf16 with d_k = 128, the fused kernel
 //     otherwise;
-//  2. bwd_prep_kernel, one workgroup per (chunk, head), fully parallel: P and T of every
-//     chunk (the parts of the chunk that depend on neither state nor value columns);
-//  3. bwd_state_kernel, one workgroup per (sequence, head, 32 value columns), walks the
-//     chunks in reverse carrying dM: it writes dV and the entering-state gradient, and
-//     per value block the partial sums of dP, dT, dQ, dK, dG, dbeta and dG_C (the terms
-//     that sum over value columns);
-//  4. bwd_chunk_kernel, one workgroup per (chunk, head), fully parallel: it sums the
-//     partials in a fixed order (deterministic), forms dA and the Gram / Gamma terms
-//     and writes dq, dk, dbeta and d log alpha.
-// All arithmetic is fp32 or its equivalent (inputs in bf16 or fp32).  With bf16 I/O the
-// products run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16): an operand whose
-// values are bf16 inputs (q, k, dO) is taken exactly, any other is split into a hi + lo
-// pair of bf16 terms (about 2^-17 relative error per product).  With fp32 I/O they run
-// on v_mfma_f32_16x16x4f32 with operands gathered from LDS.  The rest runs on the
-// vector units.
+//  2. bwd_prep_kernel, one workgroup per (chunk, head), fully parallel: T, T^T and P^T of
+//     every chunk, and the operands of the reverse pass (Kh, Qt^T, Kt^T, gam);
+//  3. the reverse state pass of the per-key-channel gradients (launch_bwdk_rev), which
+//     these operands fit unchanged: one workgroup per (sequence, head, 32 value columns)
+//     walks the chunks in reverse with dM in matrix-core accumulators and writes dM and
+//     dDelta of every chunk, dV and the initial-state gradient;
+//  4. bwd_chunk_kernel, one workgroup per (chunk, head), fully parallel: every product
+//     over the value columns at full width (X, Delta, Y, dP, dT, dQt, dKt, dKh) from the
+//     stored M0, dM and dDelta, 32 columns at a time, then dA, the Gram and Gamma terms,
+//     dq, dk, dbeta and d log alpha.  Nothing sums across workgroups: the result is
+//     deterministic.
+// All arithmetic is fp32 or its equivalent (inputs in bf16 or fp32).  The products run
+// on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16): an operand whose values are bf16
+// inputs (q, k, v, dO) is taken exactly, any other (and every fp32 input) is split into
+// a hi + lo pair of bf16 terms (about 2^-17 relative error per product).  The Gram and
+// Gamma phase of the per-chunk kernel runs on v_mfma_f32_16x16x4f32 for fp32 I/O.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 #include "gdn_tile.h"
@@ -43,23 +44,8 @@ namespace gdn {
 
 namespace {
 
-constexpr int BC = 64;    // chunk length
-constexpr int BNT = 1024;  // threads per workgroup of the per-chunk kernel (four waves per SIMD)
-constexpr int BNW = BNT / 64;
-// threads per workgroup of the reverse-state kernel: the additive write's variant runs
-// two waves per SIMD; the delta write's needs more registers than that leaves (256 per
-// wave) and runs one
-template <bool ADD> constexpr int state_threads() { return ADD ? 512 : 256; }
-constexpr int BVB = 32;   // value columns per workgroup of the reverse-state kernel
-constexpr int SV = BVB + 4, ST = BC + 1;  // fp32 row strides (padded; SV rows 16-byte aligned)
-
-// floats of one partial record (per chunk slot, head and value block); dP, dT (64 x 64)
-// and dQ, dK (64 x d_k) are stored transposed, [column][row], so that a lane's four
-// rows of a matrix-core tile are one 16-byte store and one 16-byte load
-template <int DK> struct Part {
-  static constexpr int DP = 0, DT = BC * BC, DQ = 2 * BC * BC, DKO = DQ + BC * DK, DG = DKO + BC * DK,
-                       DB = DG + BC, GC = DB + BC, SIZE = GC + BC;
-};
+constexpr int BC = 64;      // chunk length
+constexpr int ST = BC + 1;  // fp32 pitch of 64-column tiles
 
 // sequence extent of stream n (false: malformed offsets)
 __device__ __forceinline__ bool seq_extent(const BwdParams &p, int n, long &tok0, int &len) {
@@ -94,10 +80,27 @@ __device__ __forceinline__ bool slot_chunk(const BwdParams &p, long slot, size_t
   return true;
 }
 
+// decay prefix of a chunk (wave 0, lane = row): gs <- G, eg <- e^G, et <- e^{G_C - G},
+// *gC <- e^{G_C}
+__device__ __forceinline__ void decay_prefix(float *gs, float *eg, float *et, float *gC, int lane) {
+  float g = gs[lane];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(g, off);
+    if (lane >= off) g += y;
+  }
+  const float gc = __shfl(g, 63);
+  gs[lane] = g;
+  eg[lane] = __expf(g);
+  et[lane] = __expf(gc - g);
+  if (lane == 0) *gC = __expf(gc);
+}
+
 // One workgroup per (chunk slot, head), fully parallel: P = incl(Q K^T * Gamma) and, for
-// the delta write, T = (I + A)^-1 with A = strict(diag(beta) K K^T * Gamma), both fp32
-// row-major into the workspace (the blocks above the diagonal zero).  The Gram tiles
-// take the bf16 inputs exactly; T is the blocked inverse (tri_inv64).
+// the delta write, T = (I + A)^-1 with A = strict(diag(beta) K K^T * Gamma) (blocked
+// inverse, tri_inv64); into the workspace P^T, T, T^T, Kh = e^{G_C - G} K (row-major),
+// (e^G Q)^T, (e^G K)^T (channel-major) and gam = e^{G_C} repeated over the key channels,
+// the operands of the reverse pass.  The Gram tiles take the bf16 inputs exactly.
 template <typename E, int DK, int GATE, bool ADD>
 __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(BwdParams p) {
   constexpr int SKE = DK + 8;
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(BwdParams p) {
   __shared__ __align__(16) E Ql[BC * SKE];
   __shared__ float Al[BC * ST], Tl[BC * ST];
   __shared__ float ys[3 * 16 * 17];
-  __shared__ float bs[BC], gs[BC];
+  __shared__ float bs[BC], gs[BC], eg[BC], et[BC], gcs[1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H;
@@ -114,6 +117,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(BwdParams p) {
   size_t tb;
   int nv;
   if (!slot_chunk(p, slot, tb, nv)) return;
+  const size_t sh = (size_t)slot * H + h;
   auto K_ = [&](int r, int d) { return to_f(Kl[r * SKE + d]); };
   auto Q_ = [&](int r, int d) { return to_f(Ql[r * SKE + d]); };
   {  // K, Q: 16-byte loads, all in flight before the LDS stores (rows past the end zero)
@@ -139,17 +143,11 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(BwdParams p) {
     gs[tid] = (GATE == GATE_HEAD && ok) ? p.log_alpha[(tb + tid) * p.la_stride + h] : 0.f;
   }
   __syncthreads();
-  if (wave == 0) {
-    float g = gs[lane];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(g, off);
-      if (lane >= off) g += y;
-    }
-    gs[lane] = g;
-  }
+  if (wave == 0) decay_prefix(gs, eg, et, gcs, lane);
   __syncthreads();
-  float *pm = p.pmat + ((size_t)slot * H + h) * BC * BC;
+  // Gram tiles: P^T straight to the workspace (a lane's four rows of a tile are four
+  // consecutive floats of the transpose), A into LDS
+  float *pmT = p.pmT + sh * BC * BC;
   for (int t = wave; t < 16; t += 4) {
     const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
     f32x4 av = zero4(), pv = zero4();
@@ -164,499 +162,417 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(BwdParams p) {
         pv = tile_g<E, DK, true, true>(m0, n0, lg, lm, Q_, [&](int d, int i) { return K_(i, d); });
       }
     }
+    f32x4 pt;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int r = m0 + 4 * lg + u, i = n0 + lm;
       const float gam = i <= r ? (GATE == GATE_HEAD ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
       if (!ADD) Al[r * ST + i] = i < r ? bs[r] * av[u] * gam : 0.f;
-      pm[r * BC + i] = pv[u] * gam;
+      pt[u] = pv[u] * gam;
+    }
+    *(f32x4 *)(pmT + (n0 + lm) * BC + m0 + 4 * lg) = pt;
+  }
+  // Kh rows (8 consecutive channels per thread), then (e^G Q)^T and (e^G K)^T (8
+  // consecutive rows per thread) and gam
+  for (int i = 8 * tid; i < BC * DK; i += 8 * 256) {
+    const int r = i / DK, d = i % DK;
+    const float s = et[r];
+    f32x4 a0, a1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a0[e] = K_(r, d + e) * s;
+      a1[e] = K_(r, d + 4 + e) * s;
+    }
+    *(f32x4 *)(p.kh + sh * BC * DK + i) = a0;
+    *(f32x4 *)(p.kh + sh * BC * DK + i + 4) = a1;
+  }
+  for (int i = 8 * tid; i < DK * BC; i += 8 * 256) {
+    const int d = i / BC, r = i % BC;
+    f32x4 q0, q1, k0, k1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q0[e] = Q_(r + e, d) * eg[r + e];
+      q1[e] = Q_(r + 4 + e, d) * eg[r + 4 + e];
+      k0[e] = K_(r + e, d) * eg[r + e];
+      k1[e] = K_(r + 4 + e, d) * eg[r + 4 + e];
+    }
+    *(f32x4 *)(p.qtT + sh * DK * BC + i) = q0;
+    *(f32x4 *)(p.qtT + sh * DK * BC + i + 4) = q1;
+    if (!ADD) {
+      *(f32x4 *)(p.ktT + sh * DK * BC + i) = k0;
+      *(f32x4 *)(p.ktT + sh * DK * BC + i + 4) = k1;
     }
   }
+  if (tid < DK) p.gam[sh * DK + tid] = gcs[0];
   if constexpr (!ADD) {
     __syncthreads();
     tri_inv64<1>(Al, ST, Tl, ST, ys);
-    float *tm = p.tmat + ((size_t)slot * H + h) * BC * BC;
+    float *tm = p.tm + sh * BC * BC, *tmT = p.tmT + sh * BC * BC;
     for (int i4 = 4 * tid; i4 < BC * BC; i4 += 4 * 256) {
       const int r = i4 / BC, i = i4 % BC;
       *(f32x4 *)(tm + i4) = (f32x4){Tl[r * ST + i], Tl[r * ST + i + 1], Tl[r * ST + i + 2], Tl[r * ST + i + 3]};
+      *(f32x4 *)(tmT + i4) =
+          (f32x4){Tl[i * ST + r], Tl[(i + 1) * ST + r], Tl[(i + 2) * ST + r], Tl[(i + 3) * ST + r]};
     }
   }
 }
 
-template <typename E, int DK, int GATE, bool ADD>
-__global__ __launch_bounds__(state_threads<ADD>(), 1) void bwd_state_kernel(BwdParams p) {
-  constexpr int SNT = state_threads<ADD>(), NWS = SNT / 64;
-  constexpr int NH = NWS / 4;  // column parts of the dQ / dK phase
-  constexpr int SKE = DK + 8;
-  constexpr int VE = 16 / (int)sizeof(E);        // elements per 16-byte piece
-  constexpr int RK = BC * (DK / VE) / SNT;       // K / Q pieces per thread
-  constexpr int NPV = BC * (BVB / VE);           // V / dO pieces
-  constexpr int RV = (NPV + SNT - 1) / SNT;      // ... per thread (the first NPV threads)
-  constexpr int RM = DK * (BVB / 4) / SNT;       // entering-state pieces per thread
-  constexpr int RT = BC * BC / 4 / SNT;          // T / P pieces per thread
-  typedef E EV __attribute__((ext_vector_type(VE)));
-  typedef Part<DK> PT;
-  __shared__ __align__(16) E Kl[BC * SKE];
-  __shared__ __align__(16) E Ql[BC * SKE];
-  __shared__ __align__(16) float Vb[BC * SV];
-  __shared__ __align__(16) float dOb[BC * SV];
-  __shared__ __align__(16) float M0[DK * SV];
-  __shared__ __align__(16) float dM[DK * SV];
-  __shared__ __align__(16) float Tl[BC * ST];
-  __shared__ __align__(16) float Pl[BC * ST];
-  __shared__ __align__(16) float Tb[BC * ST];
-  __shared__ __align__(16) float Xl[BC * SV];
-  __shared__ __align__(16) float dDl[BC * SV];
-  __shared__ float bs[BC], gs[BC], eg[BC], et[BC], wsum[NWS], misc[4];
-  __shared__ float rsum[NH][3][BC];  // row sums of the dQ / dK products, per column part
-  // delta write: V is dead once X is formed; additive write: Delta = V and Y = dDelta
-  float *const Yl = ADD ? dDl : Vb;
-  float *const Dl = ADD ? Vb : Tl;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H = p.H, dv = p.dv, nb = dv / BVB;
-  int pair, jb;
-  xcd_pair_block(blockIdx.x, p.N * p.H, nb, pair, jb);
-  const int n = pair / H, h = pair % H, col0 = jb * BVB;
-  long tok0;
-  int len;
-  if (!seq_extent(p, n, tok0, len)) return;
-  const int nchunks = (len + BC - 1) / BC;
-  const long slot0 = (tok0 >> 6) + n;
-  const size_t sstate = ((size_t)n * H + h) * DK * dv + col0;
-  auto K_ = [&](int r, int d) { return to_f(Kl[r * SKE + d]); };
-  auto Q_ = [&](int r, int d) { return to_f(Ql[r * SKE + d]); };
-
-  for (int i = tid; i < DK * BVB; i += SNT) {
-    const int d = i / BVB, j = i % BVB;
-    dM[d * SV + j] = p.dfinal ? p.dfinal[sstate + (size_t)d * dv + j] : 0.f;
+// ---- operand fragments for the per-chunk kernel
+// an input row piece: exact in bf16, split into hi + lo from fp32
+__device__ __forceinline__ bf16x8 in8(const bf16 *p) { return ld8(p); }
+__device__ __forceinline__ Split in8(const float *p) { return split8(ld8(p)); }
+// an fp32 array kept in LDS as two bf16 arrays (hi, lo)
+struct Halves {
+  bf16 *h, *l;
+};
+__device__ __forceinline__ Split sfrag(const Halves &x, int o) { return Split{ld8(x.h + o), ld8(x.l + o)}; }
+__device__ __forceinline__ void sput(const Halves &x, int o, float v) {
+  const bf16 hv = (bf16)v;
+  x.h[o] = hv;
+  x.l[o] = (bf16)(v - (float)hv);
+}
+__device__ __forceinline__ void sput4(const Halves &x, int o, const f32x4 &v) {
+  bf16x4 hv, lv;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hv[j] = (bf16)v[j];
+    lv[j] = (bf16)(v[j] - (float)hv[j]);
   }
-
-  // ---- a chunk's inputs: 16-byte loads into registers one chunk ahead (rows past the
-  // sequence end re-read its last row and are zeroed when staged)
-  u32x4 pk[RK], pq[RK], pv[RV], pd[RV];
-  f32x4 pm[RM], pt[RT], pp[RT];
-  float pb = 0.f, pl = 0.f;
-  auto fetch = [&](int cc) {
-    const int last = min(BC, len - cc * BC) - 1;
-    const size_t tbc = (size_t)tok0 + (size_t)cc * BC;
-    const size_t tp = (((size_t)slot0 + cc) * H + h) * BC * BC;  // T and P of the chunk
-#pragma unroll
-    for (int u = 0; u < RT; ++u) {
-      if (!ADD) pt[u] = *(const f32x4 *)(p.tmat + tp + 4 * (tid + SNT * u));
-      pp[u] = *(const f32x4 *)(p.pmat + tp + 4 * (tid + SNT * u));
-    }
-#pragma unroll
-    for (int u = 0; u < RK; ++u) {
-      const int pc = tid + SNT * u, r = min(pc / (DK / VE), last), g = pc % (DK / VE);
-      const size_t o = ((tbc + r) * H + h) * DK + g * VE;
-      pk[u] = *(const u32x4 *)((const E *)p.k + o);
-      pq[u] = *(const u32x4 *)((const E *)p.q + o);
-    }
-#pragma unroll
-    for (int u = 0; u < RV; ++u) {
-      const int pc = tid + SNT * u, r = min(pc / (BVB / VE), last), g = pc % (BVB / VE);
-      if (pc >= NPV) break;
-      const size_t o = ((tbc + r) * H + h) * dv + col0 + g * VE;
-      pv[u] = *(const u32x4 *)((const E *)p.v + o);
-      pd[u] = *(const u32x4 *)((const E *)p.dout + o);
-    }
-#pragma unroll
-    for (int u = 0; u < RM; ++u) {
-      const int pc = tid + SNT * u, d = pc / (BVB / 4), g = pc % (BVB / 4);
-      pm[u] = *(const f32x4 *)(p.states + ((((size_t)slot0 + cc) * H + h) * DK + d) * dv + col0 + 4 * g);
-    }
-    if (tid < BC) {
-      const size_t t = tbc + min(tid, last);
-      pb = ADD ? 0.f : p.beta[t * H + h];
-      pl = GATE == GATE_HEAD ? p.log_alpha[t * p.la_stride + h] : 0.f;
-    }
-  };
-  auto stage = [&](int nvc) {
-#pragma unroll
-    for (int u = 0; u < RK; ++u) {
-      opaque(pk[u]);
-      opaque(pq[u]);
-      const int pc = tid + SNT * u, r = pc / (DK / VE), g = pc % (DK / VE);
-      if (r >= nvc) pk[u] = pq[u] = (u32x4){0u, 0u, 0u, 0u};
-      *(u32x4 *)(Kl + r * SKE + g * VE) = pk[u];
-      *(u32x4 *)(Ql + r * SKE + g * VE) = pq[u];
-    }
-#pragma unroll
-    for (int u = 0; u < RV; ++u) {
-      const int pc = tid + SNT * u, r = pc / (BVB / VE), g = pc % (BVB / VE);
-      if (pc >= NPV) break;
-      opaque(pv[u]);
-      opaque(pd[u]);
-      const EV ev = __builtin_bit_cast(EV, pv[u]), ed = __builtin_bit_cast(EV, pd[u]);
-#pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        Vb[r * SV + g * VE + e] = r < nvc ? to_f(ev[e]) : 0.f;
-        dOb[r * SV + g * VE + e] = r < nvc ? to_f(ed[e]) : 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < RM; ++u) {
-      opaque(pm[u]);
-      const int pc = tid + SNT * u, d = pc / (BVB / 4), g = pc % (BVB / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) M0[d * SV + 4 * g + e] = pm[u][e];
-    }
-#pragma unroll
-    for (int u = 0; u < RT; ++u) {
-      const int i4 = 4 * (tid + SNT * u), r = i4 / BC, i = i4 % BC;
-      if (!ADD) opaque(pt[u]);
-      opaque(pp[u]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (!ADD) Tb[r * ST + i + e] = pt[u][e];
-        Pl[r * ST + i + e] = pp[u][e];
-      }
-    }
-    if (tid < BC) {
-      opaque(pb);
-      opaque(pl);
-      bs[tid] = tid < nvc ? pb : 0.f;
-      gs[tid] = tid < nvc ? pl : 0.f;
-    }
-  };
-  if (nchunks > 0) fetch(nchunks - 1);
-
-  for (int c = nchunks - 1; c >= 0; --c) {
-    const int nv = min(BC, len - c * BC);
-    const size_t tb = (size_t)tok0 + (size_t)c * BC;  // token of row 0
-    const size_t slot = (size_t)(slot0 + c);
-    __syncthreads();  // the previous chunk is done with every buffer
-    stage(nv);
-    if (c > 0) fetch(c - 1);  // in flight during this chunk's compute
-    __syncthreads();
-    if (wave == 0) {  // decay prefix
-      float g = gs[lane];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(g, off);
-        if (lane >= off) g += y;
-      }
-      const float gC = __shfl(g, 63);
-      gs[lane] = g;
-      eg[lane] = __expf(g);
-      et[lane] = __expf(gC - g);
-      if (lane == 0) misc[0] = __expf(gC);
-    }
-    __syncthreads();
-    // ---- V - Kt M0 into Xl (64 x 32; the delta write only)
-    if constexpr (!ADD)
-      mm_g<E, BC, BVB, DK, NWS, true, false>(wave, lane, K_, [&](int d, int j) { return M0[d * SV + j]; },
-                                             [&](int r, int j, f32x4 v) {
-#pragma unroll
-                                               for (int u = 0; u < 4; ++u)
-                                                 Xl[(r + u) * SV + j] = Vb[(r + u) * SV + j] - eg[r + u] * v[u];
-                                             });
-    __syncthreads();
-    // ---- Delta = T diag(beta) (V - Kt M0) (the additive write: Delta = V, already in Vb);
-    // dDelta = P^T dO + diag(e^{G_C - G}) K dM  (8 tiles each)
-    {
-      const int lg = lane >> 4, lm = lane & 15;
-      for (int t = wave; t < 8; t += NWS) {
-        const int m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
-        f32x4 dd = zero4();
-        if (!ADD)
-          dd = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int i) { return Tb[r * ST + i]; },
-                                           [&](int i, int j) { return bs[i] * Xl[i * SV + j]; }, 0, m0 + 16);
-        const f32x4 d1 = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int r, int i) { return Pl[i * ST + r]; },
-                                                    [&](int i, int j) { return dOb[i * SV + j]; }, m0);
-        const f32x4 d2 =
-            tile_g<E, DK, true, false>(m0, n0, lg, lm, K_, [&](int d, int j) { return dM[d * SV + j]; });
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = m0 + 4 * lg + u, j = n0 + lm;
-          if (!ADD) Dl[r * SV + j] = dd[u];
-          dDl[r * SV + j] = d1[u] + et[r] * d2[u];
-        }
-      }
-    }
-    __syncthreads();
-    // ---- Y = T^T dDelta (the additive write: Y = dDelta, already in dDl)
-    if constexpr (!ADD)
-      mm_g<E, BC, BVB, BC, NWS, false, false>(wave, lane, [&](int r, int i) { return Tb[i * ST + r]; },
-                              [&](int i, int j) { return dDl[i * SV + j]; }, [&](int r, int j, f32x4 v) {
-#pragma unroll
-                                for (int u = 0; u < 4; ++u) Yl[(r + u) * SV + j] = v[u];
-                              });
-    __syncthreads();
-    // ---- dV (complete for this value block)
-    for (int i = tid; i < BC * BVB; i += SNT) {
-      const int r = i / BVB, j = i % BVB;
-      if (r < nv) ((E *)p.dv_out)[((tb + r) * H + h) * dv + col0 + j] = to_e<E>(ADD ? Yl[r * SV + j] : bs[r] * Yl[r * SV + j]);
-    }
-    float *pr = p.part + ((slot * H + h) * nb + jb) * (size_t)PT::SIZE;
-    // ---- dP = incl(dO Delta^T), dT = dDelta (diag(beta) X)^T  (partial over value columns;
-    // no dT for the additive write)
-    if constexpr (std::is_same<E, bf16>::value) {
-      // these contract over the 32 value columns: every fragment is a row piece
-      const int lg = lane >> 4, lm = lane & 15;
-      for (int t = wave; t < 16; t += NWS) {
-        const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16, i = n0 + lm;
-        f32x4 vp = zero4();
-        if (n0 <= m0)
-          vp = tile_frag<BVB>([&](int k0) { return to_bf8(ld8(dOb + (m0 + lm) * SV + 8 * lg + k0)); },
-                              [&](int k0) { return split8(ld8(Dl + i * SV + 8 * lg + k0)); });
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (i > m0 + 4 * lg + u) vp[u] = 0.f;
-        *(f32x4 *)(pr + PT::DP + i * BC + m0 + 4 * lg) = vp;
-        if (!ADD) {
-          const float bi = bs[i];
-          const f32x4 vt = tile_frag<BVB>([&](int k0) { return split8(ld8(dDl + (m0 + lm) * SV + 8 * lg + k0)); },
-                                          [&](int k0) { return split8(ld8(Xl + i * SV + 8 * lg + k0) * bi); });
-          *(f32x4 *)(pr + PT::DT + i * BC + m0 + 4 * lg) = vt;
-        }
-      }
-    } else {
-      mm_g<E, BC, BC, BVB, NWS, true, false>(wave, lane, [&](int r, int j) { return dOb[r * SV + j]; },
-                              [&](int j, int i) { return Dl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
-#pragma unroll
-                                for (int u = 0; u < 4; ++u) pr[PT::DP + i * BC + r + u] = i <= r + u ? v[u] : 0.f;
-                              });
-      if constexpr (!ADD)
-        mm_g<E, BC, BC, BVB, NWS, false, false>(wave, lane, [&](int r, int j) { return dDl[r * SV + j]; },
-                                [&](int j, int i) { return bs[i] * Xl[i * SV + j]; }, [&](int r, int i, f32x4 v) {
-#pragma unroll
-                                  for (int u = 0; u < 4; ++u) pr[PT::DT + i * BC + r + u] = v[u];
-                                });
-    }
-    // ---- dQ = e^G dO M0^T, dK = -e^G beta Y M0^T + e^{G_C - G} Delta dM^T, and the rows of
-    // dG: e^G (dO M0^T).Q - e^G beta (Y M0^T).K - e^{G_C - G} (Delta dM^T).K.  A wave takes
-    // one 16-row block and one of NH parts of the DK columns; the row sums of the parts
-    // meet in LDS.
-    {
-      const int lg = lane >> 4, lm = lane & 15;
-      const int m0 = 16 * (wave & 3), half = wave >> 2;
-      float gq[4] = {0.f, 0.f, 0.f, 0.f}, gk[4] = {0.f, 0.f, 0.f, 0.f}, gz[4] = {0.f, 0.f, 0.f, 0.f};
-      // this wave's rows of dO, Y and Delta as A fragments (the contraction is over the
-      // 32 value columns: one 32-deep step)
-      [[maybe_unused]] bf16x8 fdo;
-      [[maybe_unused]] Split fy, fd;
-      if constexpr (std::is_same<E, bf16>::value) {
-        fdo = to_bf8(ld8(dOb + (m0 + lm) * SV + 8 * lg));
-        fy = split8(ld8(Yl + (m0 + lm) * SV + 8 * lg));
-        fd = split8(ld8(Dl + (m0 + lm) * SV + 8 * lg));
-      }
-      for (int n0 = half * (DK / NH); n0 < (half + 1) * (DK / NH); n0 += 16) {
-        f32x4 w, uu, z;
-        if constexpr (std::is_same<E, bf16>::value) {
-          const Split fm = split8(ld8(M0 + (n0 + lm) * SV + 8 * lg));
-          const Split fdm = split8(ld8(dM + (n0 + lm) * SV + 8 * lg));
-          w = mm(fdo, fm, zero4());
-          uu = ADD ? zero4() : mm(fy, fm, zero4());
-          z = mm(fd, fdm, zero4());
-        } else {
-          w = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return dOb[r * SV + j]; },
-                        [&](int j, int d) { return M0[d * SV + j]; });
-          uu = zero4();
-          if (!ADD)
-            uu = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Yl[r * SV + j]; },
-                           [&](int j, int d) { return M0[d * SV + j]; });
-          z = tile<BVB>(m0, n0, lg, lm, [&](int r, int j) { return Dl[r * SV + j]; },
-                        [&](int j, int d) { return dM[d * SV + j]; });
-        }
-        const int d = n0 + lm;
-        f32x4 sq, sk;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = m0 + 4 * lg + u;
-          const float qv = Q_(r, d), kv = K_(r, d);
-          sq[u] = eg[r] * w[u];
-          sk[u] = -eg[r] * bs[r] * uu[u] + et[r] * z[u];
-          gq[u] += w[u] * qv;
-          gk[u] += uu[u] * kv;
-          gz[u] += z[u] * kv;
-        }
-        *(f32x4 *)(pr + PT::DQ + d * BC + m0 + 4 * lg) = sq;
-        *(f32x4 *)(pr + PT::DKO + d * BC + m0 + 4 * lg) = sk;
-      }
-      // a row's columns are spread over the 16 lanes lm of its lane group
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          gq[u] += __shfl_xor(gq[u], off);
-          gk[u] += __shfl_xor(gk[u], off);
-          gz[u] += __shfl_xor(gz[u], off);
-        }
-      if (lm == 0)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = m0 + 4 * lg + u;
-          rsum[half][0][r] = gq[u];
-          rsum[half][1][r] = gk[u];
-          rsum[half][2][r] = gz[u];
-        }
-    }
-    // ---- dM <- gam dM + Qt^T dO - Kt^T diag(beta) Y (no last term for the additive write)
-    // (DK x 32: DK / 8 tiles), into registers: written after the next barrier
-    const int lgm = lane >> 4, lmm = lane & 15;
-    constexpr int TILES = (DK / 16) * 2;
-    f32x4 nm[TILES / NWS];
-    {
-      const float gam = misc[0];
-#pragma unroll
-      for (int q = 0; q < TILES / NWS; ++q) {
-        const int t = wave + NWS * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
-        const f32x4 n1 = tile_g<E, BC, false, true>(m0, n0, lgm, lmm, [&](int d, int r) { return eg[r] * Q_(r, d); },
-                                  [&](int r, int j) { return dOb[r * SV + j]; });
-        f32x4 n2 = zero4();
-        if (!ADD)
-          n2 = tile_g<E, BC, false, false>(m0, n0, lgm, lmm, [&](int d, int r) { return eg[r] * bs[r] * K_(r, d); },
-                                           [&](int r, int j) { return Yl[r * SV + j]; });
-#pragma unroll
-        for (int u = 0; u < 4; ++u) nm[q][u] = gam * dM[(m0 + 4 * lgm + u) * SV + n0 + lmm] + n1[u] - n2[u];
-      }
-    }
-    // ---- dbeta rows: Y . (V - Kt M0);  dG_C: the e^{G_C - G} terms plus gam <M0, dM>
-    float part_m = 0.f;
-    for (int i = tid; i < DK * BVB; i += SNT) part_m += M0[(i / BVB) * SV + i % BVB] * dM[(i / BVB) * SV + i % BVB];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part_m += __shfl_xor(part_m, off);
-    if (lane == 0) wsum[wave] = part_m;
-    if (!ADD && tid < BC) {
-      float sb = 0.f;
-      for (int j = 0; j < BVB; ++j) sb += Yl[tid * SV + j] * Xl[tid * SV + j];
-      pr[PT::DB + tid] = sb;
-    }
-    __syncthreads();  // every read of the old dM is done; the row sums are in LDS
-    if (wave == 0) {  // lane = row: the dG rows, and dG_C (their e^{G_C - G} terms plus gam <M0, dM>)
-      const int r = lane;
-      float gq = 0.f, gk = 0.f, gz = 0.f;
-#pragma unroll
-      for (int c = 0; c < NH; ++c) {
-        gq += rsum[c][0][r];
-        gk += rsum[c][1][r];
-        gz += rsum[c][2][r];
-      }
-      pr[PT::DG + r] = eg[r] * gq - eg[r] * bs[r] * gk - et[r] * gz;
-      float sg = et[r] * gz;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) sg += __shfl_xor(sg, off);
-      float wm = 0.f;
-#pragma unroll
-      for (int w = 0; w < NWS; ++w) wm += wsum[w];
-      if (lane == 0) pr[PT::GC] = sg + misc[0] * wm;
-    }
-#pragma unroll
-    for (int q = 0; q < TILES / NWS; ++q) {
-      const int t = wave + NWS * q, m0 = (t >> 1) * 16, n0 = (t & 1) * 16;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) dM[(m0 + 4 * lgm + u) * SV + n0 + lmm] = nm[q][u];
-    }
-  }
-  __syncthreads();
-  if (p.dinit)
-    for (int i = tid; i < DK * BVB; i += SNT) {
-      const int d = i / BVB, j = i % BVB;
-      p.dinit[sstate + (size_t)d * dv + j] = dM[d * SV + j];
-    }
+  *(bf16x4 *)(x.h + o) = hv;
+  *(bf16x4 *)(x.l + o) = lv;
 }
 
+// LDS bytes of the per-chunk kernel's staging region: the first part (value slices)
+// and the second (Gram and Gamma terms) share it
+template <typename E, int DK, bool ADD> struct ChunkLds {
+  static constexpr int PK = DK + 8, PMT = DK + 8, PC = 40, PR = BC + 8;
+  static constexpr int HM = 32 * PMT, HR = DK * PC, H6 = BC * PC, HT = 32 * PR;  // elements of one half
+  // M0^T, M0, dM, Delta (bf16 halves); dO and V (I/O dtype); dDelta, dDelta^T,
+  // (beta X)^T, beta X, -beta Y (bf16 halves; the delta write only)
+  static constexpr int A_BYTES = 4 * ((ADD ? 0 : HM) + 2 * HR + H6) + 2 * H6 * (int)sizeof(E) +
+                                 (ADD ? 0 : 4 * (3 * H6 + 2 * HT));
+  // Q (I/O dtype) and six fp32 64 x 64 tiles
+  static constexpr int B_BYTES = BC * PK * (int)sizeof(E) + 6 * BC * ST * 4;
+  static constexpr int BYTES = A_BYTES > B_BYTES ? A_BYTES : B_BYTES;
+};
+
+// One workgroup of eight waves per (chunk slot, head), fully parallel.
+// First part, 32 value columns at a time (the slice of M0, dM, dDelta, dO and V staged
+// in LDS, the next slice's loads in flight meanwhile):
+//   X = V - e^G (K M0), Delta = T diag(beta) X, Y = T^T dDelta,
+//   dP += dO Delta^T, dT += dDelta (diag(beta) X)^T,
+//   dQt += dO M0^T, dKt -= diag(beta) Y M0^T, dKh += Delta dM^T,
+//   dbeta_r += Y_r . X_r, <M0, dM>;
+// the sums stay in matrix-core accumulators.  Every B operand and every computed A
+// operand is staged once per slice as split bf16 halves in the layout its fragments
+// read (two 16-byte reads); K and dO are taken exactly.
+// Second part: dA = -strict(T^T dT T^T), the Gram and Gamma terms, dq, dk, dbeta and
+// d log alpha (the reverse prefix of dG plus dG_C).
 template <typename E, int DK, int GATE, bool ADD>
-__global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
-  constexpr int SKE = DK + 8;
-  typedef Part<DK> PT;
-  __shared__ __align__(16) E Kl[BC * SKE];
-  __shared__ __align__(16) E Ql[BC * SKE];
-  __shared__ float Tl[BC * ST], Pl[BC * ST], Dt[BC * ST], Zl[BC * ST], Sl[BC * ST], Rl[BC * ST];
-  __shared__ float bs[BC], gs[BC], dGs[BC], dBs[BC], misc[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(512, 1) void bwd_chunk_kernel(BwdParams p) {
+  constexpr int NT = 512, NW = 8;
+  typedef ChunkLds<E, DK, ADD> L;
+  constexpr int PK = L::PK, PMT = L::PMT, PC = L::PC, PR = L::PR;
+  constexpr int SKE = PK;
+  __shared__ __align__(16) E Kl[BC * PK];
+  __shared__ __align__(16) char U[L::BYTES];
+  __shared__ float bs[BC], gs[BC], eg[BC], et[BC], dGs[BC], dBs[BC], misc[4];
+  __shared__ float rq[2][3][BC], dbp[2][BC], wsum[NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lm = lane & 15;
-  const int H = p.H, nb = p.dv / BVB;
+  const int H = p.H, dv = p.dv;
   const long slot = blockIdx.x / H;
   const int h = blockIdx.x % H;
-  // the sequence that owns the slot: the last n with floor(tok0_n / 64) + n <= slot
-  auto tok_start = [&](int sq) -> long { return p.cu_seqlens ? (long)p.cu_seqlens[sq] : (long)sq * p.T; };
-  int lo = 0, hi = p.N - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((tok_start(mid) >> 6) + mid <= slot) lo = mid;
-    else hi = mid - 1;
-  }
-  long tok0;
-  int len;
-  if (!seq_extent(p, lo, tok0, len)) return;
-  const long c = slot - ((tok0 >> 6) + lo);
-  if (c < 0 || 64 * c >= len) return;  // no chunk owns this slot
-  const int nv = (int)min(64L, (long)len - 64 * c);
-  const size_t tb = (size_t)tok0 + (size_t)c * BC;
-  auto K_ = [&](int r, int d) { return to_f(Kl[r * SKE + d]); };
-  auto Q_ = [&](int r, int d) { return to_f(Ql[r * SKE + d]); };
+  size_t tb;
+  int nv;
+  if (!slot_chunk(p, slot, tb, nv)) return;
+  const size_t sh = (size_t)slot * H + h;
+  auto K_ = [&](int r, int d) { return to_f(Kl[r * PK + d]); };
 
-  // K, Q: 16-byte loads (rows past the sequence end are zero)
-  constexpr int VE = 16 / (int)sizeof(E), NPC = BC * (DK / VE);  // 16-byte pieces
-#pragma unroll
-  for (int u = 0; u < (NPC + BNT - 1) / BNT; ++u) {
-    const int pc = tid + BNT * u, r = pc / (DK / VE), g = pc % (DK / VE);
-    if (pc >= NPC) break;
-    u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-    if (r < nv) {
-      const size_t o = ((tb + r) * H + h) * DK + g * VE;
-      kv = *(const u32x4 *)((const E *)p.k + o);
-      qv = *(const u32x4 *)((const E *)p.q + o);
-    }
-    *(u32x4 *)(Kl + r * SKE + g * VE) = kv;
-    *(u32x4 *)(Ql + r * SKE + g * VE) = qv;
+  // ---- first part's LDS: carve the staging region
+  char *u = U;
+  auto halves = [&](int n) {
+    Halves x{(bf16 *)u, (bf16 *)u + n};
+    u += 4 * n;
+    return x;
+  };
+  const Halves M0T = ADD ? Halves{nullptr, nullptr} : halves(L::HM);
+  const Halves M0r = halves(L::HR), dMr = halves(L::HR), Dr = halves(L::H6);
+  E *const dOr = (E *)u;
+  u += L::H6 * sizeof(E);
+  E *const Vr = (E *)u;
+  u += L::H6 * sizeof(E);
+  Halves dDr{nullptr, nullptr}, dDT{nullptr, nullptr}, XbT{nullptr, nullptr}, Xbr{nullptr, nullptr},
+      nYr{nullptr, nullptr};
+  if constexpr (!ADD) {
+    dDr = halves(L::H6);
+    dDT = halves(L::HT);
+    XbT = halves(L::HT);
+    Xbr = halves(L::H6);
+    nYr = halves(L::H6);
   }
-  // dP and dT summed over the value blocks in a fixed order, and T: 16-byte loads
-  const float *pr0 = p.part + ((size_t)slot * H + h) * nb * (size_t)PT::SIZE;
-  const float *tm = p.tmat + ((size_t)slot * H + h) * BC * BC;
+
+  {  // K (16-byte loads, rows past the end zero), beta and the decay prefix
+    constexpr int VE = 16 / (int)sizeof(E), NPC = BC * (DK / VE);
 #pragma unroll
-  for (int u = 0; u < BC * BC / 4 / BNT; ++u) {
-    // T is row-major; the partials are stored transposed (column i, rows r0 .. r0+3)
-    const int i4 = 4 * (tid + BNT * u), r = i4 / BC, col = i4 % BC;
-    f32x4 sp = zero4(), st = zero4(), tv = zero4();
-    for (int b = 0; b < nb; ++b) {
-      sp += *(const f32x4 *)(pr0 + (size_t)b * PT::SIZE + PT::DP + i4);
-      if (!ADD) st += *(const f32x4 *)(pr0 + (size_t)b * PT::SIZE + PT::DT + i4);
+    for (int q = 0; q < (NPC + NT - 1) / NT; ++q) {
+      const int pc = tid + NT * q, r = pc / (DK / VE), g = pc % (DK / VE);
+      if (pc >= NPC) break;
+      u32x4 kv = {0u, 0u, 0u, 0u};
+      if (r < nv) kv = *(const u32x4 *)((const E *)p.k + ((tb + r) * H + h) * DK + g * VE);
+      *(u32x4 *)(Kl + r * PK + g * VE) = kv;
     }
-    if (!ADD) tv = *(const f32x4 *)(tm + i4);
+    if (tid < BC) {
+      const bool ok = tid < nv;
+      bs[tid] = (!ADD && ok) ? p.beta[(tb + tid) * H + h] : 0.f;
+      gs[tid] = (GATE == GATE_HEAD && ok) ? p.log_alpha[(tb + tid) * p.la_stride + h] : 0.f;
+    }
+    __syncthreads();
+    if (wave == 0) decay_prefix(gs, eg, et, misc + 1, lane);
+  }
+
+  // ---- first part
+  const int a = wave >> 1, ct = wave & 1;  // X, Delta, Y tiles: row block a, column tile ct
+  const int wa = wave & 3, wc = wave >> 2;  // dQt / dKt / dKh tiles: row block wa, channel tiles wc + 2 u
+  constexpr int NCT = DK / 32;
+  // T (rows of block a, k-steps 0 .. a / 2) and T^T (k-steps a / 2 .. 1) as A fragments,
+  // split once
+  Split fT[2], fTt[2];
+  if constexpr (!ADD) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Pl[(col + e) * ST + r] = sp[e];
-      if (!ADD) {  // no T for the additive write (its LDS then goes unused)
-        Dt[(col + e) * ST + r] = st[e];
-        Tl[r * ST + col + e] = tv[e];
+    for (int s = 0; s < 2; ++s) {
+      const size_t o = (sh * BC + 16 * a + lm) * BC + 32 * s + 8 * lg;
+      if (s <= (a >> 1)) fT[s] = split8(ld8(p.tm + o));
+      if (s >= (a >> 1)) fTt[s] = split8(ld8(p.tmT + o));
+    }
+  }
+  f32x4 aP[2], aT[2], aQ[NCT], aK[NCT], aH[NCT];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) aP[q] = aT[q] = zero4();
+#pragma unroll
+  for (int q = 0; q < NCT; ++q) aQ[q] = aK[q] = aH[q] = zero4();
+  f32x4 dby = zero4();
+  float dgm = 0.f;
+  // a slice's loads: 16-byte pieces of M0, dM (DK x 32 fp32), dDelta (64 x 32 fp32),
+  // dO and V (64 x 32, I/O dtype; rows past the end re-read the last row, zeroed when
+  // staged).  No branch around a load but the thread-count guard.
+  constexpr int NM = DK * 8 / NT;                              // M0 / dM pieces per thread
+  constexpr int VE = 16 / (int)sizeof(E), NVP = BC * 32 / VE;  // dO / V pieces
+  const float *st = p.states + sh * DK * dv, *dmc = p.dmc + sh * DK * dv, *dd = p.dd + sh * BC * dv;
+  f32x4 rm[NM], rdm[NM], rdd;
+  u32x4 rv, ro;
+  auto fetch = [&](int col0) {
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      const int pc = tid + NT * q, d = pc >> 3, g = pc & 7;
+      rm[q] = *(const f32x4 *)(st + (size_t)d * dv + col0 + 4 * g);
+      rdm[q] = *(const f32x4 *)(dmc + (size_t)d * dv + col0 + 4 * g);
+    }
+    if constexpr (!ADD) rdd = *(const f32x4 *)(dd + (size_t)(tid >> 3) * dv + col0 + 4 * (tid & 7));
+    if (tid < NVP) {
+      const int r = min(tid / (32 / VE), nv - 1), g = tid % (32 / VE);
+      const size_t o = ((tb + r) * H + h) * dv + col0 + g * VE;
+      rv = *(const u32x4 *)((const E *)p.v + o);
+      ro = *(const u32x4 *)((const E *)p.dout + o);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      const int pc = tid + NT * q, d = pc >> 3, g = pc & 7;
+      sput4(M0r, d * PC + 4 * g, rm[q]);
+      sput4(dMr, d * PC + 4 * g, rdm[q]);
+      if constexpr (!ADD)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sput(M0T, (4 * g + e) * PMT + d, rm[q][e]);
+      dgm += rm[q][0] * rdm[q][0] + rm[q][1] * rdm[q][1] + rm[q][2] * rdm[q][2] + rm[q][3] * rdm[q][3];
+    }
+    if constexpr (!ADD) {
+      const int r = tid >> 3, g = tid & 7;
+      sput4(dDr, r * PC + 4 * g, rdd);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sput(dDT, (4 * g + e) * PR + r, rdd[e]);
+    }
+    if (tid < NVP) {
+      const int r = tid / (32 / VE), g = tid % (32 / VE);
+      const bool in = r < nv;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *(u32x4 *)(dOr + r * PC + g * VE) = in ? ro : z;
+      if constexpr (ADD) {  // Delta = V
+        typedef E EV __attribute__((ext_vector_type(16 / sizeof(E))));
+        const EV ev = __builtin_bit_cast(EV, rv);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) sput(Dr, r * PC + g * VE + e, in ? to_f(ev[e]) : 0.f);
+      } else {
+        *(u32x4 *)(Vr + r * PC + g * VE) = in ? rv : z;
+      }
+    }
+  };
+  fetch(0);
+  for (int col0 = 0; col0 < dv; col0 += 32) {
+    if (col0) __syncthreads();  // every read of the previous slice is done
+    stage();
+    if (col0 + 32 < dv) fetch(col0 + 32);
+    __syncthreads();
+    f32x4 xv = zero4();
+    if constexpr (!ADD) {
+      // X = V - e^G (K M0): tile (a, ct), K exact
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < DK; k0 += 32)
+        acc = mm(in8(Kl + (16 * a + lm) * PK + k0 + 8 * lg), sfrag(M0T, (16 * ct + lm) * PMT + k0 + 8 * lg), acc);
+      const int col = 16 * ct + lm;
+      f32x4 bx;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * a + 4 * lg + j;
+        xv[j] = to_f(Vr[r * PC + col]) - eg[r] * acc[j];
+        bx[j] = bs[r] * xv[j];
+        sput(Xbr, r * PC + col, bx[j]);
+      }
+      sput4(XbT, col * PR + 16 * a + 4 * lg, bx);
+      __syncthreads();
+      // Delta = T (beta X), Y = T^T dDelta: tile (a, ct)
+      f32x4 D = zero4(), Y = zero4();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (s <= (a >> 1)) D = mm(fT[s], sfrag(XbT, col * PR + 32 * s + 8 * lg), D);
+        if (s >= (a >> 1)) Y = mm(fTt[s], sfrag(dDT, col * PR + 32 * s + 8 * lg), Y);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * a + 4 * lg + j;
+        sput(Dr, r * PC + col, D[j]);
+        sput(nYr, r * PC + col, -bs[r] * Y[j]);
+        dby[j] += Y[j] * xv[j];
+      }
+      __syncthreads();
+    }
+    // dP (lower tiles) and dT: tiles wave and wave + 8 of the 4 x 4
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int t = wave + 8 * q, m0 = 16 * (t >> 2), n0 = 16 * (t & 3);
+      if (n0 <= m0) aP[q] = mm(in8(dOr + (m0 + lm) * PC + 8 * lg), sfrag(Dr, (n0 + lm) * PC + 8 * lg), aP[q]);
+      if constexpr (!ADD)
+        aT[q] = mm(sfrag(dDr, (m0 + lm) * PC + 8 * lg), sfrag(Xbr, (n0 + lm) * PC + 8 * lg), aT[q]);
+    }
+    // dQt, dKt, dKh: row block wa, channel tiles wc + 2 q
+    {
+      const auto fo = in8(dOr + (16 * wa + lm) * PC + 8 * lg);
+      const Split fd = sfrag(Dr, (16 * wa + lm) * PC + 8 * lg);
+      Split fy;
+      if constexpr (!ADD) fy = sfrag(nYr, (16 * wa + lm) * PC + 8 * lg);
+#pragma unroll
+      for (int q = 0; q < NCT; ++q) {
+        const int n0 = 16 * (wc + 2 * q);
+        const Split fm = sfrag(M0r, (n0 + lm) * PC + 8 * lg);
+        aQ[q] = mm(fo, fm, aQ[q]);
+        if constexpr (!ADD) aK[q] = mm(fy, fm, aK[q]);
+        aH[q] = mm(fd, sfrag(dMr, (n0 + lm) * PC + 8 * lg), aH[q]);
       }
     }
   }
-  if (tid < BC) {
-    const bool ok = tid < nv;
-    bs[tid] = (!ADD && ok) ? p.beta[(tb + tid) * H + h] : 0.f;
-    gs[tid] = (GATE == GATE_HEAD && ok) ? p.log_alpha[(tb + tid) * p.la_stride + h] : 0.f;
-    float sg = 0.f, sb = 0.f;
-    for (int b = 0; b < nb; ++b) {
-      sg += pr0[(size_t)b * PT::SIZE + PT::DG + tid];
-      if (!ADD) sb += pr0[(size_t)b * PT::SIZE + PT::DB + tid];
+  __syncthreads();  // the staging region is free
+
+  // ---- second part's LDS
+  E *const Ql = (E *)U;
+  float *const Tl = (float *)(U + BC * PK * sizeof(E));
+  float *const Pl = Tl + BC * ST, *const Dt = Pl + BC * ST, *const Zl = Dt + BC * ST, *const Sl = Zl + BC * ST,
+               *const Rl = Sl + BC * ST;
+  auto Q_ = [&](int r, int d) { return to_f(Ql[r * PK + d]); };
+  {  // Q and T, and dP (inclusive lower) / dT from the accumulators
+    constexpr int NPC = BC * (DK / VE);
+#pragma unroll
+    for (int q = 0; q < (NPC + NT - 1) / NT; ++q) {
+      const int pc = tid + NT * q, r = pc / (DK / VE), g = pc % (DK / VE);
+      if (pc >= NPC) break;
+      u32x4 qv = {0u, 0u, 0u, 0u};
+      if (r < nv) qv = *(const u32x4 *)((const E *)p.q + ((tb + r) * H + h) * DK + g * VE);
+      *(u32x4 *)(Ql + r * PK + g * VE) = qv;
     }
-    dGs[tid] = sg;
-    dBs[tid] = sb;
+    if constexpr (!ADD) {
+      const float *tm = p.tm + sh * BC * BC;
+      for (int i4 = 4 * tid; i4 < BC * BC; i4 += 4 * NT) {
+        const f32x4 tv = *(const f32x4 *)(tm + i4);
+        const int r = i4 / BC, c = i4 % BC;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Tl[r * ST + c + e] = tv[e];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int t = wave + 8 * q, m0 = 16 * (t >> 2), n0 = 16 * (t & 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = m0 + 4 * lg + j, i = n0 + lm;
+        Pl[r * ST + i] = i <= r ? aP[q][j] : 0.f;
+        if (!ADD) Dt[r * ST + i] = aT[q][j];
+      }
+    }
   }
-  if (tid == 0) {
-    float sc = 0.f;
-    for (int b = 0; b < nb; ++b) sc += pr0[(size_t)b * PT::SIZE + PT::GC];
-    misc[0] = sc;
+  // <M0, dM> over the workgroup
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dgm += __shfl_xor(dgm, off);
+  if (lane == 0) wsum[wave] = dgm;
+  // dbeta rows: Y . X over the tile's 16 columns, the two column tiles meet in LDS
+  if constexpr (!ADD) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dby[j] += __shfl_xor(dby[j], off);
+    if (lm == 0)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dbp[ct][16 * a + 4 * lg + j] = dby[j];
   }
   __syncthreads();
-  if (wave == 0) {
-    float g = gs[lane];
+  {  // the rows of dG from the value-width sums: dQt . Q, dKt . K, dKh . K
+    float gq[4] = {0.f, 0.f, 0.f, 0.f}, gk[4] = {0.f, 0.f, 0.f, 0.f}, gz[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(g, off);
-      if (lane >= off) g += y;
+    for (int q = 0; q < NCT; ++q) {
+      const int c = 16 * (wc + 2 * q) + lm;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * wa + 4 * lg + j;
+        gq[j] += aQ[q][j] * Q_(r, c);
+        gk[j] += aK[q][j] * K_(r, c);
+        gz[j] += aH[q][j] * K_(r, c);
+      }
     }
-    gs[lane] = g;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gq[j] += __shfl_xor(gq[j], off);
+        gk[j] += __shfl_xor(gk[j], off);
+        gz[j] += __shfl_xor(gz[j], off);
+      }
+    if (lm == 0)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * wa + 4 * lg + j;
+        rq[wc][0][r] = gq[j];
+        rq[wc][1][r] = gk[j];
+        rq[wc][2][r] = gz[j];
+      }
+  }
+  __syncthreads();
+  if (wave == 0) {  // lane = row: dG and dbeta rows, and dG_C = sum of e^{G_C - G} dKh . K + gam <M0, dM>
+    const int r = lane;
+    const float gq = rq[0][0][r] + rq[1][0][r], gk = rq[0][1][r] + rq[1][1][r], gz = rq[0][2][r] + rq[1][2][r];
+    dGs[r] = eg[r] * (gq + gk) - et[r] * gz;
+    dBs[r] = ADD ? 0.f : dbp[0][r] + dbp[1][r];
+    float sg = et[r] * gz;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sg += __shfl_xor(sg, off);
+    float wm = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) wm += wsum[w];
+    if (lane == 0) misc[0] = sg + misc[1] * wm;
   }
   __syncthreads();
   // S = K K^T, R = Q K^T (only their lower tiles are used: the upper ones are set to
   // zero);  Z = dT T^T
-  for (int t = wave; t < 16; t += BNW) {
+  for (int t = wave; t < 16; t += NW) {
     const int m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
     f32x4 sv = zero4(), rv = zero4();
     if (n0 <= m0) {
@@ -689,10 +605,10 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
   // wG = (dA beta_r S + dP R) Gamma, and dA S Gamma (for dbeta).  Each wave's tiles
   // are computed first (Zl is read), then written after a barrier.
   {
-    f32x4 da[16 / BNW];
+    f32x4 da[16 / NW];
 #pragma unroll
-    for (int q = 0; q < 16 / BNW; ++q) {
-      const int t = wave + BNW * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
+    for (int q = 0; q < 16 / NW; ++q) {
+      const int t = wave + NW * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
       da[q] = zero4();  // only the strictly lower part is kept (none for the additive write)
       if (!ADD && n0 <= m0)
         da[q] = tile_g<E, BC, false, false>(m0, n0, lg, lm, [&](int r, int k) { return Tl[k * ST + r]; },
@@ -700,8 +616,8 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 16 / BNW; ++q) {
-      const int t = wave + BNW * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
+    for (int q = 0; q < 16 / NW; ++q) {
+      const int t = wave + NW * q, m0 = (t >> 2) * 16, n0 = (t & 3) * 16;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = m0 + 4 * lg + u, i = n0 + lm;
@@ -747,16 +663,11 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
       if (GATE == GATE_HEAD) p.dlog_alpha[(tb + t) * H + h] = g;
     }
   }
-  // dq = Ep K + (partials), dk = (Ea + Ea^T) K + Ep^T Q + (partials); the partials of a
-  // tile are loaded before its products, so the loads overlap them
-  for (int t = wave; t < (DK / 16) * 4; t += BNW) {
-    const int m0 = (t / (DK / 16)) * 16, n0 = (t % (DK / 16)) * 16;
-    f32x4 pq_ = zero4(), pk_ = zero4();  // partials stored [d][r]: this lane's 4 rows are contiguous
-    for (int b = 0; b < nb; ++b) {
-      const size_t o = (size_t)b * PT::SIZE + (size_t)(n0 + lm) * BC + m0 + 4 * lg;
-      pq_ += *(const f32x4 *)(pr0 + PT::DQ + o);
-      pk_ += *(const f32x4 *)(pr0 + PT::DKO + o);
-    }
+  // dq = Ep K + e^G dQt, dk = (Ea + Ea^T) K + Ep^T Q + e^G dKt + e^{G_C - G} dKh: the
+  // tiles whose value-width sums this wave holds
+#pragma unroll
+  for (int q = 0; q < NCT; ++q) {
+    const int m0 = 16 * wa, n0 = 16 * (wc + 2 * q);
     const f32x4 q_ = tile_g<E, BC, false, true>(m0, n0, lg, lm, [&](int r, int i) { return Pl[r * ST + i]; },
                                                 [&](int i, int d) { return K_(i, d); }, 0, m0 + 16);
     f32x4 k_ = zero4();
@@ -767,34 +678,57 @@ __global__ __launch_bounds__(BNT, 1) void bwd_chunk_kernel(BwdParams p) {
                                      [&](int i, int d) { return Q_(i, d); }, m0);
     const int d = n0 + lm;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = m0 + 4 * lg + u;
+    for (int j = 0; j < 4; ++j) {
+      const int r = m0 + 4 * lg + j;
       if (r >= nv) continue;
-      ((E *)p.dq)[((tb + r) * H + h) * DK + d] = to_e<E>(q_[u] + pq_[u]);
-      ((E *)p.dk)[((tb + r) * H + h) * DK + d] = to_e<E>(k_[u] + pk_[u]);
+      ((E *)p.dq)[((tb + r) * H + h) * DK + d] = to_e<E>(q_[j] + eg[r] * aQ[q][j]);
+      ((E *)p.dk)[((tb + r) * H + h) * DK + d] = to_e<E>(k_[j] + eg[r] * aK[q][j] + et[r] * aH[q][j]);
     }
   }
 }
 
 template <typename E, int DK, int GATE, bool ADD>
-void launch_bg(const BwdParams &p, hipStream_t stream) {
-  const int nb = p.dv / BVB;
+hipError_t launch_bg(const BwdParams &p, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_prep_kernel<E, DK, GATE, ADD>), dim3((unsigned)(p.slots * p.H)), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((bwd_state_kernel<E, DK, GATE, ADD>), dim3(p.N * p.H * nb), dim3(state_threads<ADD>()), 0,
-                     stream, p);
-  hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, GATE, ADD>), dim3((unsigned)(p.slots * p.H)), dim3(BNT), 0, stream, p);
+  BwdKeyParams kp{};
+  kp.q = p.q;
+  kp.k = p.k;
+  kp.v = p.v;
+  kp.dout = p.dout;
+  kp.beta = p.beta;
+  kp.dfinal = p.dfinal;
+  kp.cu_seqlens = p.cu_seqlens;
+  kp.states = const_cast<float *>(p.states);
+  kp.dmc = p.dmc;
+  kp.dd = p.dd;
+  kp.tmT = p.tmT;
+  kp.pmT = p.pmT;
+  kp.kh = p.kh;
+  kp.ktT = p.ktT;
+  kp.qtT = p.qtT;
+  kp.gam = p.gam;
+  kp.dv_out = p.dv_out;
+  kp.dinit = p.dinit;
+  kp.N = p.N;
+  kp.H = p.H;
+  kp.T = p.T;
+  kp.dv = p.dv;
+  kp.slots = p.slots;
+  kp.states_ready = 1;
+  const hipError_t e = launch_bwdk_rev(kp, std::is_same<E, bf16>::value ? 1 : 0, DK, ADD, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_chunk_kernel<E, DK, GATE, ADD>), dim3((unsigned)(p.slots * p.H)), dim3(512), 0, stream, p);
+  return hipGetLastError();
 }
 
 template <typename E, int DK>
 hipError_t launch_b(const BwdParams &p, int gate, bool add, hipStream_t stream) {
   if (p.N == 0 || p.slots * p.H == 0) return hipSuccess;
   if (gate == GATE_HEAD)
-    add ? launch_bg<E, DK, GATE_HEAD, true>(p, stream) : launch_bg<E, DK, GATE_HEAD, false>(p, stream);
-  else if (gate == GATE_NONE)
-    add ? launch_bg<E, DK, GATE_NONE, true>(p, stream) : launch_bg<E, DK, GATE_NONE, false>(p, stream);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+    return add ? launch_bg<E, DK, GATE_HEAD, true>(p, stream) : launch_bg<E, DK, GATE_HEAD, false>(p, stream);
+  if (gate == GATE_NONE)
+    return add ? launch_bg<E, DK, GATE_NONE, true>(p, stream) : launch_bg<E, DK, GATE_NONE, false>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 // out[h] = sum over t of x[t * H + h], in a fixed order (deterministic): one workgroup
@@ -828,8 +762,6 @@ __global__ void fill_zero_kernel(float *x, size_t n) {
 }
 
 }  // namespace
-
-size_t bwd_part_floats(int dk) { return dk == 128 ? Part<128>::SIZE : Part<64>::SIZE; }
 
 hipError_t launch_fill_zero(float *x, size_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;

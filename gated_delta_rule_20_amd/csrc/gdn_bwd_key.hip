@@ -1004,6 +1004,18 @@ hipError_t launch_k(const BwdKeyParams &p, bool add, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_bwdk_rev(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream) {
+  const unsigned serial = (unsigned)(p.N * p.H * (p.dv / KBV));
+  if (serial == 0) return hipSuccess;
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(serial), dim3(256), 0, stream, p); };
+  if (dtype == 1 && dk == 128) add ? go(bwdk_rev_kernel<bf16, 128, true>) : go(bwdk_rev_kernel<bf16, 128, false>);
+  else if (dtype == 1 && dk == 64) add ? go(bwdk_rev_kernel<bf16, 64, true>) : go(bwdk_rev_kernel<bf16, 64, false>);
+  else if (dtype == 0 && dk == 128) add ? go(bwdk_rev_kernel<float, 128, true>) : go(bwdk_rev_kernel<float, 128, false>);
+  else if (dtype == 0 && dk == 64) add ? go(bwdk_rev_kernel<float, 64, true>) : go(bwdk_rev_kernel<float, 64, false>);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_key(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream) {
   if (dtype == 1) {
     if (dk == 128) return launch_k<bf16, 128>(p, add, stream);

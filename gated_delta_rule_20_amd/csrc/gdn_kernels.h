@@ -77,10 +77,12 @@ struct BwdParams {
                                  // NULL without a gate, read at t * la_stride + h)
   const float *dfinal;           // NULL | [N, H, d_k, d_v]
   const int32_t *cu_seqlens;     // NULL (batch) | [N + 1]
-  const float *states;           // [slots, H, d_k, d_v] chunk-entering states
-  float *tmat;                   // [slots, H, 64, 64] T of every chunk (delta write)
-  float *pmat;                   // [slots, H, 64, 64] P of every chunk
-  float *part;                   // [slots, H, d_v / 32, bwd_part_floats(d_k)] partial sums
+  // workspace (fp32): chunk-entering states and chunk-end state gradients [slots, H, d_k,
+  // d_v], dDelta [slots, H, 64, d_v], T and T^T (delta write) and P^T [slots, H, 64, 64],
+  // e^{G_C - G} K [slots, H, 64, d_k], (e^G Q)^T and (e^G K)^T (delta write) [slots, H,
+  // d_k, 64], e^{G_C} [slots, H, d_k]
+  const float *states;
+  float *dmc, *dd, *tm, *tmT, *pmT, *kh, *qtT, *ktT, *gam;
   void *dq, *dk, *dv_out;        // outputs, I/O dtype
   float *dbeta, *dlog_alpha;     // [tokens, H]; dbeta NULL for the additive write, dlog_alpha
                                  // NULL without a gate (per token also for a constant decay)
@@ -89,7 +91,6 @@ struct BwdParams {
   int la_stride;                 // H, or 0 for one constant decay per head
   long slots;
 };
-size_t bwd_part_floats(int dk);
 hipError_t launch_bwd(const BwdParams &p, int dtype, int dk, int gate, bool add, hipStream_t stream);
 // x[0 .. n) = 0
 hipError_t launch_fill_zero(float *x, size_t n, hipStream_t stream);
@@ -119,6 +120,9 @@ struct BwdKeyParams {
   int states_ready;              // the chunk-entering states are already in `states`
 };
 hipError_t launch_bwd_key(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream);
+// the reverse state pass alone (chunk-end state gradients, dDelta, dV, initial-state
+// gradient), from operands already in the workspace; also the scalar-gate path's
+hipError_t launch_bwdk_rev(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream);
 
 // Forward of the diagonal-plus-low-rank transition (no gate or the scalar gate).
 struct DplrParams {

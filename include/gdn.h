@@ -249,16 +249,14 @@ typedef struct {
 
 /* Bytes of device workspace gdn_bwd_chunked needs (0 for arguments it would reject),
  * with S = floor(B T / 64) + N chunk slots, each part rounded up to 256 bytes:
- *  - no gate, one decay per (token, head), one constant decay per head: the chunk-
- *    entering states (4 d_k d_v bytes per slot and head), T of every chunk (delta write
- *    only: 16 KiB per slot and head), P of every chunk (16 KiB per slot and head), the
- *    partial sums over value columns (d_v / 32
- *    records of 4 (8192 + 128 d_k + 192) bytes per slot and head) and, for the constant
- *    per-head decay, the per-token decay gradients (4 bytes per token and head);
- *  - one decay per key channel, per slot and head in fp32: the chunk-entering states and
- *    chunk-end state gradients (d_k d_v each), dDelta (64 d_v), T and T^T (delta write)
- *    and P^T (64 x 64 each), K e^G (delta write), K e^{g_C - G}, their transposes and
- *    (Q e^G)^T (64 d_k each; K e^G's transpose for the delta write only), e^{g_C} (d_k).
+ *  - every gate, per slot and head in fp32: the chunk-entering states and chunk-end
+ *    state gradients (d_k d_v each), dDelta (64 d_v), T and T^T (delta write) and P^T
+ *    (64 x 64 each), K e^{g_C - G} (64 d_k), (K e^G)^T (delta write) and (Q e^G)^T
+ *    (d_k 64 each), e^{g_C} (d_k);
+ *  - one decay per key channel adds K e^G (delta write) and (K e^{g_C - G})^T (64 d_k
+ *    each per slot and head);
+ *  - one constant decay per head adds the per-token decay gradients (4 bytes per token
+ *    and head).
  * Owned by the caller; no initialisation needed. */
 size_t gdn_bwd_workspace_size(const gdn_bwd_args *args);
 

@@ -11,7 +11,7 @@
 
 static int launches = 0;
 namespace gdn {
-size_t bwd_part_floats(int dk) { return 2 * 64 * 64 + 2 * 64 * (size_t)dk + 3 * 64; }
+
 #define STUB(sig) \
   hipError_t sig { \
     ++launches; \

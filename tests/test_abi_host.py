@@ -324,19 +324,24 @@ def test_bwd_host_validation(g, change, status):
 
 
 def test_bwd_workspace_size(g):
+    """The scalar gates' backward workspace: with S = floor(B T / 64) + N chunk slots,
+    fp32 chunk states and chunk-end state gradients (d_k d_v per slot and head), dDelta
+    (64 d_v), T and T^T (delta write), P^T (64 x 64 each), e^{g_C - g} K (64 d_k), the
+    transposes of e^g K (delta write) and e^g Q (d_k 64 each) and e^{g_C} (d_k), each
+    rounded up to 256 bytes; the constant gate adds the per-token decay gradients."""
+    up = lambda x: (x + 255) // 256 * 256
     a = bwd_args(g)
-    slots = (2 * 128) // 64 + 2
-    part = 8192 + 128 * 128 + 192
-    expect = sum((x + 255) // 256 * 256 for x in (slots * 4 * 128 * 128 * 4, slots * 4 * 4096 * 4,
-                                                   slots * 4 * 4096 * 4, slots * 4 * 4 * part * 4))
+    sh = ((2 * 128) // 64 + 2) * 4
+    dk = dv = 128
+    delta = [sh * dk * dv * 4] * 2 + [sh * 64 * dv * 4] + [sh * 4096 * 4] * 3 + [sh * 64 * dk * 4] * 3 + [sh * dk * 4]
+    expect = sum(up(x) for x in delta)
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(a)) == expect
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(bwd_args(g, dq=None))) == 0
-    # states, T (delta write only), P, the partials; the constant gate adds the
-    # per-token decay gradients
     add = bwd_args(g, write=1, beta=None, dbeta=None)
-    assert g._lib.gdn_bwd_workspace_size(ctypes.byref(add)) == expect - slots * 4 * 4096 * 4
+    add_sizes = [sh * dk * dv * 4] * 2 + [sh * 64 * dv * 4] + [sh * 4096 * 4] + [sh * 64 * dk * 4] * 2 + [sh * dk * 4]
+    assert g._lib.gdn_bwd_workspace_size(ctypes.byref(add)) == sum(up(x) for x in add_sizes)
     const = bwd_args(g, gate=3)
-    assert g._lib.gdn_bwd_workspace_size(ctypes.byref(const)) == expect + 2 * 128 * 4 * 4
+    assert g._lib.gdn_bwd_workspace_size(ctypes.byref(const)) == expect + up(2 * 128 * 4 * 4)
 
 
 def test_bwd_workspace_size_key_gate(g):
