@@ -376,26 +376,26 @@ __global__ __launch_bounds__(256, 1) void bwdk_fwd_kernel(BwdKeyParams p) {
 // -diag(beta) Y) are staged once per chunk in LDS, transposed and split into hi and lo
 // bf16 halves, so that every fragment is two 16-byte reads; the A operands are read
 // from the workspace one phase ahead of their products.
-template <typename E, int DK, bool ADD>
+template <typename E, int DK, bool ADD, int VB>
 __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
   constexpr int PM = DK + 8, PV = KC + 8;  // bf16 pitches of the transposed operands
-  constexpr int NCT = KBV / 16, RB = DK / 64, SK = DK / 32;
+  constexpr int NCT = VB / 16, RB = DK / 64, SK = DK / 32;
   constexpr bool VX = std::is_same<E, bf16>::value;  // dO exact in bf16: no lo half
-  __shared__ __align__(16) bf16 dMh[KBV * PM];
-  __shared__ __align__(16) bf16 dMl[KBV * PM];
-  __shared__ __align__(16) bf16 dOh[KBV * PV];
-  __shared__ __align__(16) bf16 dOl[KBV * PV];
-  __shared__ __align__(16) bf16 dDh[KBV * PV];
-  __shared__ __align__(16) bf16 dDl[KBV * PV];
-  __shared__ __align__(16) bf16 bYh[KBV * PV];
-  __shared__ __align__(16) bf16 bYl[KBV * PV];
+  __shared__ __align__(16) bf16 dMh[VB * PM];
+  __shared__ __align__(16) bf16 dMl[VB * PM];
+  __shared__ __align__(16) bf16 dOh[VB * PV];
+  __shared__ __align__(16) bf16 dOl[VB * PV];
+  __shared__ __align__(16) bf16 dDh[VB * PV];
+  __shared__ __align__(16) bf16 dDl[VB * PV];
+  __shared__ __align__(16) bf16 bYh[VB * PV];
+  __shared__ __align__(16) bf16 bYl[VB * PV];
   __shared__ float bsh[KC], gsh[DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lm = lane & 15;
-  const int H = p.H, dv = p.dv, nb = dv / KBV;
+  const int H = p.H, dv = p.dv, nb = dv / VB;
   int pair, jb;
   xcd_pair_block(blockIdx.x, p.N * p.H, nb, pair, jb);
-  const int n = pair / H, h = pair % H, col0 = jb * KBV;
+  const int n = pair / H, h = pair % H, col0 = jb * VB;
   long tok0;
   int len;
   if (!seq_extent_k(p, n, tok0, len)) return;
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
   };
   // dO of a chunk, beta and e^{g_C} (no branch around a load: rows past the end read
   // the last row and are zeroed when staged)
-  constexpr int VC = KBV / 4, VL = VC * (int)sizeof(E) / 16;
+  constexpr int VC = VB / 4, VL = VC * (int)sizeof(E) / 16;
   u32x4 oraw[VL];
   float bnext = 0.f, gnext = 0.f;
   auto load_o = [&](int cc) {
@@ -982,6 +982,20 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
   if (!ADD && tid < nv) p.dbeta[(size_t)(tb + tid) * H + h] = dbys[tid] + (rb[0][tid] + rb[1][tid]);
 }
 
+// The reverse pass takes 64 value columns per workgroup when that still gives one
+// workgroup per compute unit (the A operands are then read once for twice the columns),
+// else 32
+template <typename E, int DK, bool ADD>
+void launch_rev(const BwdKeyParams &p, hipStream_t stream) {
+  const long pairs = (long)p.N * p.H;
+  if (p.dv % 64 == 0 && pairs * (p.dv / 64) >= 256)
+    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, 64>), dim3((unsigned)(pairs * (p.dv / 64))), dim3(256), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, KBV>), dim3((unsigned)(pairs * (p.dv / KBV))), dim3(256), 0,
+                       stream, p);
+}
+
 template <typename E, int DK>
 hipError_t launch_k(const BwdKeyParams &p, bool add, hipStream_t stream) {
   const unsigned items = (unsigned)(p.slots * p.H), serial = (unsigned)(p.N * p.H * (p.dv / KBV));
@@ -990,13 +1004,13 @@ hipError_t launch_k(const BwdKeyParams &p, bool add, hipStream_t stream) {
     hipLaunchKernelGGL((bwdk_prep_kernel<E, DK, true>), dim3(items), dim3(256), 0, stream, p);
     if (!p.states_ready)
       hipLaunchKernelGGL((bwdk_fwd_kernel<E, DK, true>), dim3(serial), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, true>), dim3(serial), dim3(256), 0, stream, p);
+    launch_rev<E, DK, true>(p, stream);
     hipLaunchKernelGGL((bwdk_chunk_kernel<E, DK, true>), dim3(items), dim3(512), 0, stream, p);
   } else {
     hipLaunchKernelGGL((bwdk_prep_kernel<E, DK, false>), dim3(items), dim3(256), 0, stream, p);
     if (!p.states_ready)
       hipLaunchKernelGGL((bwdk_fwd_kernel<E, DK, false>), dim3(serial), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, false>), dim3(serial), dim3(256), 0, stream, p);
+    launch_rev<E, DK, false>(p, stream);
     hipLaunchKernelGGL((bwdk_chunk_kernel<E, DK, false>), dim3(items), dim3(512), 0, stream, p);
   }
   return hipGetLastError();
@@ -1005,13 +1019,11 @@ hipError_t launch_k(const BwdKeyParams &p, bool add, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwdk_rev(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream) {
-  const unsigned serial = (unsigned)(p.N * p.H * (p.dv / KBV));
-  if (serial == 0) return hipSuccess;
-  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(serial), dim3(256), 0, stream, p); };
-  if (dtype == 1 && dk == 128) add ? go(bwdk_rev_kernel<bf16, 128, true>) : go(bwdk_rev_kernel<bf16, 128, false>);
-  else if (dtype == 1 && dk == 64) add ? go(bwdk_rev_kernel<bf16, 64, true>) : go(bwdk_rev_kernel<bf16, 64, false>);
-  else if (dtype == 0 && dk == 128) add ? go(bwdk_rev_kernel<float, 128, true>) : go(bwdk_rev_kernel<float, 128, false>);
-  else if (dtype == 0 && dk == 64) add ? go(bwdk_rev_kernel<float, 64, true>) : go(bwdk_rev_kernel<float, 64, false>);
+  if (p.N * p.H * (p.dv / KBV) == 0) return hipSuccess;
+  if (dtype == 1 && dk == 128) add ? launch_rev<bf16, 128, true>(p, stream) : launch_rev<bf16, 128, false>(p, stream);
+  else if (dtype == 1 && dk == 64) add ? launch_rev<bf16, 64, true>(p, stream) : launch_rev<bf16, 64, false>(p, stream);
+  else if (dtype == 0 && dk == 128) add ? launch_rev<float, 128, true>(p, stream) : launch_rev<float, 128, false>(p, stream);
+  else if (dtype == 0 && dk == 64) add ? launch_rev<float, 64, true>(p, stream) : launch_rev<float, 64, false>(p, stream);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
