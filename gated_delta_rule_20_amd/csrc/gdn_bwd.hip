@@ -39,6 +39,7 @@
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 #include "gdn_tile.h"
+#include "gdn_bwd_slices.h"
 
 namespace gdn {
 
@@ -217,45 +218,6 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
-// ---- operand fragments for the per-chunk kernel
-// an input row piece: exact in bf16, split into hi + lo from fp32
-__device__ __forceinline__ bf16x8 in8(const bf16 *p) { return ld8(p); }
-__device__ __forceinline__ Split in8(const float *p) { return split8(ld8(p)); }
-// an fp32 array kept in LDS as two bf16 arrays (hi, lo)
-struct Halves {
-  bf16 *h, *l;
-};
-__device__ __forceinline__ Split sfrag(const Halves &x, int o) { return Split{ld8(x.h + o), ld8(x.l + o)}; }
-__device__ __forceinline__ void sput(const Halves &x, int o, float v) {
-  const bf16 hv = (bf16)v;
-  x.h[o] = hv;
-  x.l[o] = (bf16)(v - (float)hv);
-}
-__device__ __forceinline__ void sput4(const Halves &x, int o, const f32x4 &v) {
-  bf16x4 hv, lv;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    hv[j] = (bf16)v[j];
-    lv[j] = (bf16)(v[j] - (float)hv[j]);
-  }
-  *(bf16x4 *)(x.h + o) = hv;
-  *(bf16x4 *)(x.l + o) = lv;
-}
-
-// LDS bytes of the per-chunk kernel's staging region: the first part (value slices)
-// and the second (Gram and Gamma terms) share it
-template <typename E, int DK, bool ADD> struct ChunkLds {
-  static constexpr int PK = DK + 8, PMT = DK + 8, PC = 40, PR = BC + 8;
-  static constexpr int HM = 32 * PMT, HR = DK * PC, H6 = BC * PC, HT = 32 * PR;  // elements of one half
-  // M0^T, M0, dM, Delta (bf16 halves); dO and V (I/O dtype); dDelta, dDelta^T,
-  // (beta X)^T, beta X, -beta Y (bf16 halves; the delta write only)
-  static constexpr int A_BYTES = 4 * ((ADD ? 0 : HM) + 2 * HR + H6) + 2 * H6 * (int)sizeof(E) +
-                                 (ADD ? 0 : 4 * (3 * H6 + 2 * HT));
-  // Q (I/O dtype) and six fp32 64 x 64 tiles
-  static constexpr int B_BYTES = BC * PK * (int)sizeof(E) + 6 * BC * ST * 4;
-  static constexpr int BYTES = A_BYTES > B_BYTES ? A_BYTES : B_BYTES;
-};
-
 // One workgroup of eight waves per (chunk slot, head), fully parallel.
 // First part, 32 value columns at a time (the slice of M0, dM, dDelta, dO and V staged
 // in LDS, the next slice's loads in flight meanwhile):
@@ -270,12 +232,11 @@ template <typename E, int DK, bool ADD> struct ChunkLds {
 // d log alpha (the reverse prefix of dG plus dG_C).
 template <typename E, int DK, int GATE, bool ADD>
 __global__ __launch_bounds__(512, 1) void bwd_chunk_kernel(BwdParams p) {
-  constexpr int NT = 512, NW = 8;
-  typedef ChunkLds<E, DK, ADD> L;
-  constexpr int PK = L::PK, PMT = L::PMT, PC = L::PC, PR = L::PR;
-  constexpr int SKE = PK;
+  constexpr int NT = 512, NW = 8, PK = DK + 8, SKE = PK;
+  // the second part's LDS (Q and six fp32 64 x 64 tiles) shares U with the first's
+  constexpr int B_BYTES = BC * PK * (int)sizeof(E) + 6 * BC * ST * 4, A_BYTES = SliceLds<E, DK, ADD>::BYTES;
   __shared__ __align__(16) E Kl[BC * PK];
-  __shared__ __align__(16) char U[L::BYTES];
+  __shared__ __align__(16) char U[A_BYTES > B_BYTES ? A_BYTES : B_BYTES];
   __shared__ float bs[BC], gs[BC], eg[BC], et[BC], dGs[BC], dBs[BC], misc[4];
   __shared__ float rq[2][3][BC], dbp[2][BC], wsum[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -288,29 +249,6 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kernel(BwdParams p) {
   if (!slot_chunk(p, slot, tb, nv)) return;
   const size_t sh = (size_t)slot * H + h;
   auto K_ = [&](int r, int d) { return to_f(Kl[r * PK + d]); };
-
-  // ---- first part's LDS: carve the staging region
-  char *u = U;
-  auto halves = [&](int n) {
-    Halves x{(bf16 *)u, (bf16 *)u + n};
-    u += 4 * n;
-    return x;
-  };
-  const Halves M0T = ADD ? Halves{nullptr, nullptr} : halves(L::HM);
-  const Halves M0r = halves(L::HR), dMr = halves(L::HR), Dr = halves(L::H6);
-  E *const dOr = (E *)u;
-  u += L::H6 * sizeof(E);
-  E *const Vr = (E *)u;
-  u += L::H6 * sizeof(E);
-  Halves dDr{nullptr, nullptr}, dDT{nullptr, nullptr}, XbT{nullptr, nullptr}, Xbr{nullptr, nullptr},
-      nYr{nullptr, nullptr};
-  if constexpr (!ADD) {
-    dDr = halves(L::H6);
-    dDT = halves(L::HT);
-    XbT = halves(L::HT);
-    Xbr = halves(L::H6);
-    nYr = halves(L::H6);
-  }
 
   {  // K (16-byte loads, rows past the end zero), beta and the decay prefix
     constexpr int VE = 16 / (int)sizeof(E), NPC = BC * (DK / VE);
@@ -331,148 +269,32 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kernel(BwdParams p) {
     if (wave == 0) decay_prefix(gs, eg, et, misc + 1, lane);
   }
 
-  // ---- first part
-  const int a = wave >> 1, ct = wave & 1;  // X, Delta, Y tiles: row block a, column tile ct
-  const int wa = wave & 3, wc = wave >> 2;  // dQt / dKt / dKh tiles: row block wa, channel tiles wc + 2 u
+  // ---- first part: the sums over the value columns
   constexpr int NCT = DK / 32;
-  // T (rows of block a, k-steps 0 .. a / 2) and T^T (k-steps a / 2 .. 1) as A fragments,
-  // split once
-  Split fT[2], fTt[2];
-  if constexpr (!ADD) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const size_t o = (sh * BC + 16 * a + lm) * BC + 32 * s + 8 * lg;
-      if (s <= (a >> 1)) fT[s] = split8(ld8(p.tm + o));
-      if (s >= (a >> 1)) fTt[s] = split8(ld8(p.tmT + o));
-    }
+  const int a = wave >> 1, ct = wave & 1, wa = wave & 3, wc = wave >> 2;
+  SliceSums<DK> S;
+  {
+    SliceIn in;
+    in.st = p.states + sh * DK * dv;
+    in.dmc = p.dmc + sh * DK * dv;
+    in.dd = p.dd + sh * BC * dv;
+    in.tm = p.tm + sh * BC * BC;
+    in.tmT = p.tmT + sh * BC * BC;
+    in.kt = nullptr;
+    in.v = p.v;
+    in.dout = p.dout;
+    in.tb = tb;
+    in.nv = nv;
+    in.H = H;
+    in.h = h;
+    in.dv = dv;
+    slice_sums<E, DK, ADD, false>(in, U, Kl, eg, bs, S);
   }
-  f32x4 aP[2], aT[2], aQ[NCT], aK[NCT], aH[NCT];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) aP[q] = aT[q] = zero4();
-#pragma unroll
-  for (int q = 0; q < NCT; ++q) aQ[q] = aK[q] = aH[q] = zero4();
-  f32x4 dby = zero4();
+  f32x4 *const aP = S.aP, *const aT = S.aT, *const aQ = S.aQ, *const aK = S.aK, *const aH = S.aH;
+  f32x4 dby = S.dby;
   float dgm = 0.f;
-  // a slice's loads: 16-byte pieces of M0, dM (DK x 32 fp32), dDelta (64 x 32 fp32),
-  // dO and V (64 x 32, I/O dtype; rows past the end re-read the last row, zeroed when
-  // staged).  No branch around a load but the thread-count guard.
-  constexpr int NM = DK * 8 / NT;                              // M0 / dM pieces per thread
-  constexpr int VE = 16 / (int)sizeof(E), NVP = BC * 32 / VE;  // dO / V pieces
-  const float *st = p.states + sh * DK * dv, *dmc = p.dmc + sh * DK * dv, *dd = p.dd + sh * BC * dv;
-  f32x4 rm[NM], rdm[NM], rdd;
-  u32x4 rv, ro;
-  auto fetch = [&](int col0) {
 #pragma unroll
-    for (int q = 0; q < NM; ++q) {
-      const int pc = tid + NT * q, d = pc >> 3, g = pc & 7;
-      rm[q] = *(const f32x4 *)(st + (size_t)d * dv + col0 + 4 * g);
-      rdm[q] = *(const f32x4 *)(dmc + (size_t)d * dv + col0 + 4 * g);
-    }
-    if constexpr (!ADD) rdd = *(const f32x4 *)(dd + (size_t)(tid >> 3) * dv + col0 + 4 * (tid & 7));
-    if (tid < NVP) {
-      const int r = min(tid / (32 / VE), nv - 1), g = tid % (32 / VE);
-      const size_t o = ((tb + r) * H + h) * dv + col0 + g * VE;
-      rv = *(const u32x4 *)((const E *)p.v + o);
-      ro = *(const u32x4 *)((const E *)p.dout + o);
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int q = 0; q < NM; ++q) {
-      const int pc = tid + NT * q, d = pc >> 3, g = pc & 7;
-      sput4(M0r, d * PC + 4 * g, rm[q]);
-      sput4(dMr, d * PC + 4 * g, rdm[q]);
-      if constexpr (!ADD)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sput(M0T, (4 * g + e) * PMT + d, rm[q][e]);
-      dgm += rm[q][0] * rdm[q][0] + rm[q][1] * rdm[q][1] + rm[q][2] * rdm[q][2] + rm[q][3] * rdm[q][3];
-    }
-    if constexpr (!ADD) {
-      const int r = tid >> 3, g = tid & 7;
-      sput4(dDr, r * PC + 4 * g, rdd);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sput(dDT, (4 * g + e) * PR + r, rdd[e]);
-    }
-    if (tid < NVP) {
-      const int r = tid / (32 / VE), g = tid % (32 / VE);
-      const bool in = r < nv;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *(u32x4 *)(dOr + r * PC + g * VE) = in ? ro : z;
-      if constexpr (ADD) {  // Delta = V
-        typedef E EV __attribute__((ext_vector_type(16 / sizeof(E))));
-        const EV ev = __builtin_bit_cast(EV, rv);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) sput(Dr, r * PC + g * VE + e, in ? to_f(ev[e]) : 0.f);
-      } else {
-        *(u32x4 *)(Vr + r * PC + g * VE) = in ? rv : z;
-      }
-    }
-  };
-  fetch(0);
-  for (int col0 = 0; col0 < dv; col0 += 32) {
-    if (col0) __syncthreads();  // every read of the previous slice is done
-    stage();
-    if (col0 + 32 < dv) fetch(col0 + 32);
-    __syncthreads();
-    f32x4 xv = zero4();
-    if constexpr (!ADD) {
-      // X = V - e^G (K M0): tile (a, ct), K exact
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int k0 = 0; k0 < DK; k0 += 32)
-        acc = mm(in8(Kl + (16 * a + lm) * PK + k0 + 8 * lg), sfrag(M0T, (16 * ct + lm) * PMT + k0 + 8 * lg), acc);
-      const int col = 16 * ct + lm;
-      f32x4 bx;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * a + 4 * lg + j;
-        xv[j] = to_f(Vr[r * PC + col]) - eg[r] * acc[j];
-        bx[j] = bs[r] * xv[j];
-        sput(Xbr, r * PC + col, bx[j]);
-      }
-      sput4(XbT, col * PR + 16 * a + 4 * lg, bx);
-      __syncthreads();
-      // Delta = T (beta X), Y = T^T dDelta: tile (a, ct)
-      f32x4 D = zero4(), Y = zero4();
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s <= (a >> 1)) D = mm(fT[s], sfrag(XbT, col * PR + 32 * s + 8 * lg), D);
-        if (s >= (a >> 1)) Y = mm(fTt[s], sfrag(dDT, col * PR + 32 * s + 8 * lg), Y);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * a + 4 * lg + j;
-        sput(Dr, r * PC + col, D[j]);
-        sput(nYr, r * PC + col, -bs[r] * Y[j]);
-        dby[j] += Y[j] * xv[j];
-      }
-      __syncthreads();
-    }
-    // dP (lower tiles) and dT: tiles wave and wave + 8 of the 4 x 4
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int t = wave + 8 * q, m0 = 16 * (t >> 2), n0 = 16 * (t & 3);
-      if (n0 <= m0) aP[q] = mm(in8(dOr + (m0 + lm) * PC + 8 * lg), sfrag(Dr, (n0 + lm) * PC + 8 * lg), aP[q]);
-      if constexpr (!ADD)
-        aT[q] = mm(sfrag(dDr, (m0 + lm) * PC + 8 * lg), sfrag(Xbr, (n0 + lm) * PC + 8 * lg), aT[q]);
-    }
-    // dQt, dKt, dKh: row block wa, channel tiles wc + 2 q
-    {
-      const auto fo = in8(dOr + (16 * wa + lm) * PC + 8 * lg);
-      const Split fd = sfrag(Dr, (16 * wa + lm) * PC + 8 * lg);
-      Split fy;
-      if constexpr (!ADD) fy = sfrag(nYr, (16 * wa + lm) * PC + 8 * lg);
-#pragma unroll
-      for (int q = 0; q < NCT; ++q) {
-        const int n0 = 16 * (wc + 2 * q);
-        const Split fm = sfrag(M0r, (n0 + lm) * PC + 8 * lg);
-        aQ[q] = mm(fo, fm, aQ[q]);
-        if constexpr (!ADD) aK[q] = mm(fy, fm, aK[q]);
-        aH[q] = mm(fd, sfrag(dMr, (n0 + lm) * PC + 8 * lg), aH[q]);
-      }
-    }
-  }
-  __syncthreads();  // the staging region is free
+  for (int q = 0; q < SliceSums<DK>::NM; ++q) dgm += S.dgm[q];
 
   // ---- second part's LDS
   E *const Ql = (E *)U;
@@ -481,7 +303,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kernel(BwdParams p) {
                *const Rl = Sl + BC * ST;
   auto Q_ = [&](int r, int d) { return to_f(Ql[r * PK + d]); };
   {  // Q and T, and dP (inclusive lower) / dT from the accumulators
-    constexpr int NPC = BC * (DK / VE);
+    constexpr int VE = 16 / (int)sizeof(E), NPC = BC * (DK / VE);
 #pragma unroll
     for (int q = 0; q < (NPC + NT - 1) / NT; ++q) {
       const int pc = tid + NT * q, r = pc / (DK / VE), g = pc % (DK / VE);

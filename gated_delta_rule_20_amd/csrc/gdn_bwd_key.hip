@@ -40,6 +40,7 @@
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 #include "gdn_tile.h"
+#include "gdn_bwd_slices.h"
 
 namespace gdn {
 
@@ -611,22 +612,17 @@ template <typename E, int DK, bool ADD>
 __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
   constexpr int SG = DK + 4;
   constexpr int NCT = DK / 32;  // 16-column channel tiles per wave
-  __shared__ __align__(16) float Gs[KC * SG];  // G, then dG
-  __shared__ float Tl[KC * SC];
-  __shared__ float dTl[KC * SC];               // dT, then dA
-  __shared__ float dPl[KC * SC];
-  // One region, three lives: the value slice of M0, dM and dDelta with the slice's X',
-  // Delta and Y; then W (in the second part); then K and Q of the chunk (the I/O dtype,
-  // rows of DK + 2 elements, so that a column read is free of bank conflicts).
-  constexpr int SLICE = (2 * DK + KC) * SV, PK = DK + 2;
-  constexpr int STG = SLICE + 3 * KC * SV;
-  static_assert(2 * KC * PK * (int)sizeof(E) <= STG * 4, "K and Q fit the staging region");
-  __shared__ __align__(16) float stg[STG];
-  __shared__ float bsh[KC], gcl[DK], rb[2][KC], gcp[4][DK], dbys[KC];
-  float *Ms = stg, *dMs = stg + DK * SV, *dDs = stg + 2 * DK * SV;
-  float *scr = stg + SLICE;
-  float *Xs = scr, *Ds = scr + KC * SV, *Ys = scr + 2 * KC * SV, *Wl = scr;
-  E *Kst = (E *)stg, *Qst = (E *)stg + KC * PK;
+  // One region, two lives: the value slices (slice_sums); then G (then dG), T, dT (then
+  // dA), dP and a last part holding W, then K and Q of the chunk (the I/O dtype, rows of
+  // DK + 2 elements, so that a column read is free of bank conflicts)
+  constexpr int PK = DK + 2;
+  constexpr int LAST = 2 * KC * PK * (int)sizeof(E) > KC * SC * 4 ? 2 * KC * PK * (int)sizeof(E) : KC * SC * 4;
+  constexpr int B_BYTES = (KC * SG + 3 * KC * SC) * 4 + LAST, A_BYTES = SliceLds<E, DK, ADD>::BYTES;
+  __shared__ __align__(16) char U[A_BYTES > B_BYTES ? A_BYTES : B_BYTES];
+  __shared__ float bsh[KC], gcl[DK], rb[2][KC], gcp[4][DK], dbys[KC], dbp[2][KC], dgmc[DK];
+  float *const Gs = (float *)U, *const Tl = Gs + KC * SG, *const dTl = Tl + KC * SC, *const dPl = dTl + KC * SC;
+  float *const Wl = dPl + KC * SC;
+  E *const Kst = (E *)Wl, *const Qst = (E *)Wl + KC * PK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H, dv = p.dv;
@@ -636,17 +632,60 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
   int nv;
   if (!slot_chunk(p, slot, tb, nv)) return;
   const size_t sh = (size_t)slot * H + h;
-  const E *kin = (const E *)p.k, *qin = (const E *)p.q, *vin = (const E *)p.v, *doin = (const E *)p.dout;
-  // K and Q from the staging region (after the value slices; rows past the end zero)
+  const E *kin = (const E *)p.k, *qin = (const E *)p.q;
+  // K and Q from the last part (rows past the end zero)
   auto K_ = [&](int r, int c) { return to_f(Kst[r * PK + c]); };
   auto Q_ = [&](int r, int c) { return to_f(Qst[r * PK + c]); };
+  if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? p.beta[(size_t)(tb + tid) * H + h] : 0.f;
+  __syncthreads();
+
+  // ---- the sums over the value columns (dP, dT, dQt, dKt, dKh, the dbeta rows and
+  // <M0[c], dM[c]>)
+  SliceSums<DK> S;
+  {
+    SliceIn in;
+    in.st = p.states + sh * DK * dv;
+    in.dmc = p.dmc + sh * DK * dv;
+    in.dd = p.dd + sh * KC * dv;
+    in.tm = p.tm + sh * KC * KC;
+    in.tmT = p.tmT + sh * KC * KC;
+    in.kt = p.kt + sh * KC * DK;
+    in.v = p.v;
+    in.dout = p.dout;
+    in.tb = (size_t)tb;
+    in.nv = nv;
+    in.H = H;
+    in.h = h;
+    in.dv = dv;
+    slice_sums<E, DK, ADD, true>(in, U, (const E *)nullptr, nullptr, bsh, S);
+  }
+  const int wa = wave & 3, wc = wave >> 2;
+  f32x4 *const aP = S.aP, *const aT = S.aT, *const aQ = S.aQ, *const aK = S.aK, *const aH = S.aH;
+  // G per channel and T into the region
   for (int i = tid; i < KC * DK; i += 512) {
     const int r = i / DK, d = i % DK;
     Gs[r * SG + d] = r < nv ? p.log_alpha[((size_t)(tb + r) * H + h) * DK + d] : 0.f;
   }
-  if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? p.beta[(size_t)(tb + tid) * H + h] : 0.f;
   if (!ADD)
     for (int i = tid; i < KC * KC; i += 512) Tl[(i / KC) * SC + i % KC] = p.tm[sh * KC * KC + i];
+  if constexpr (!ADD) {  // dbeta rows: the lanes' columns, then the two column blocks
+    f32x4 dby = S.dby;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dby[j] += __shfl_xor(dby[j], off);
+    if (lm == 0)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dbp[wave & 1][16 * (wave >> 1) + 4 * lg + j] = dby[j];
+  }
+#pragma unroll
+  for (int q = 0; q < SliceSums<DK>::NM; ++q) {  // <M0[d], dM[d]>: eight threads per key row
+    float x = S.dgm[q];
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    if ((tid & 7) == 0) dgmc[(tid + 512 * q) >> 3] = x;
+  }
   __syncthreads();
   if (tid < DK) {
     float g = 0.f;
@@ -656,128 +695,6 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
     }
     gcl[tid] = g;
   }
-  __syncthreads();
-
-  // ---- value slices: X', Delta, Y, and the sums over value columns
-  const int wa = wave & 3, wc = wave >> 2;
-  f32x4 aP[2], aT[2], aQ[NCT], aK[NCT], aH[NCT];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) aP[u] = aT[u] = zero4();
-#pragma unroll
-  for (int u = 0; u < NCT; ++u) aQ[u] = aK[u] = aH[u] = zero4();
-  float dby = 0.f, dgm = 0.f;
-  const float *st = p.states + sh * DK * dv, *dmc = p.dmc + sh * DK * dv, *dd = p.dd + sh * KC * dv;
-  for (int col0 = 0; col0 < dv; col0 += KBV) {
-    {  // the slice of M0, dM and dDelta: 16-byte loads, all in flight before the stores
-      constexpr int PS = KBV / 4, NS = DK * PS / 512;  // pieces per row, per thread
-      f32x4 xm[NS], xd[NS], xe;
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const int pc = tid + 512 * u, d = pc / PS, g = pc % PS;
-        xm[u] = *(const f32x4 *)(st + (size_t)d * dv + col0 + 4 * g);
-        xd[u] = *(const f32x4 *)(dmc + (size_t)d * dv + col0 + 4 * g);
-      }
-      const int er = tid / PS, eg = tid % PS;  // KC * PS = 512 pieces of dDelta
-      xe = *(const f32x4 *)(dd + (size_t)er * dv + col0 + 4 * eg);
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const int pc = tid + 512 * u, d = pc / PS, g = pc % PS;
-        *(f32x4 *)(Ms + d * SV + 4 * g) = xm[u];
-        *(f32x4 *)(dMs + d * SV + 4 * g) = xd[u];
-      }
-      *(f32x4 *)(dDs + er * SV + 4 * eg) = xe;
-    }
-    __syncthreads();
-    {  // X' = V - Kt M0 (delta write) or Delta = V (additive write): eight tiles, one per wave
-      const int m0 = 16 * (wave >> 1), n0 = 16 * (wave & 1);
-      f32x4 acc = zero4();
-      if constexpr (!ADD)
-        acc = kprod<DK>([&](int k0) { return ld8(p.kt + (sh * KC + m0 + lm) * DK + k0 + 8 * lg); },
-                        [&](int k0) {
-                          f32x8 f;
-#pragma unroll
-                          for (int ii = 0; ii < 8; ++ii) f[ii] = Ms[(k0 + 8 * lg + ii) * SV + n0 + lm];
-                          return f;
-                        });
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = m0 + 4 * lg + j;
-        const float vv = r < nv ? to_f(vin[((size_t)(tb + r) * H + h) * dv + col0 + n0 + lm]) : 0.f;
-        (ADD ? Ds : Xs)[r * SV + n0 + lm] = vv - acc[j];
-      }
-    }
-    __syncthreads();
-    if constexpr (!ADD) {
-      const int m0 = 16 * (wave >> 1), n0 = 16 * (wave & 1);
-      const f32x4 dl = kprod<KC>(
-          [&](int k0) {
-            f32x8 f;
-#pragma unroll
-            for (int ii = 0; ii < 8; ++ii) f[ii] = Tl[(m0 + lm) * SC + k0 + 8 * lg + ii];
-            return f;
-          },
-          [&](int k0) {
-            f32x8 f;
-#pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
-              const int k = k0 + 8 * lg + ii;
-              f[ii] = bsh[k] * Xs[k * SV + n0 + lm];
-            }
-            return f;
-          },
-          0, m0 + 16);
-      const f32x4 y = kprod<KC>(
-          [&](int k0) {
-            f32x8 f;
-#pragma unroll
-            for (int ii = 0; ii < 8; ++ii) f[ii] = Tl[(k0 + 8 * lg + ii) * SC + m0 + lm];
-            return f;
-          },
-          [&](int k0) {
-            f32x8 f;
-#pragma unroll
-            for (int ii = 0; ii < 8; ++ii) f[ii] = dDs[(k0 + 8 * lg + ii) * SV + n0 + lm];
-            return f;
-          },
-          m0, KC);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Ds[(m0 + 4 * lg + j) * SV + n0 + lm] = dl[j];
-        Ys[(m0 + 4 * lg + j) * SV + n0 + lm] = y[j];
-      }
-      __syncthreads();
-      if (tid < KC)
-        for (int j = 0; j < KBV; ++j) dby += Ys[tid * SV + j] * Xs[tid * SV + j];
-    }
-    if (tid < DK)
-      for (int j = 0; j < KBV; ++j) dgm += Ms[tid * SV + j] * dMs[tid * SV + j];
-    auto dorow = [&](int r, int k0) {
-      return r < nv ? ldrow8<E>(doin + ((size_t)(tb + r) * H + h) * dv + col0 + k0 + 8 * lg) : zero8();
-    };
-    // dP += dO Delta^T, dT += dDelta (diag(beta) X')^T  (64 x 64: tiles wave, wave + 8)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = wave + 8 * u, m0 = 16 * (t >> 2), n0 = 16 * (t & 3);
-      aP[u] += kprod<KBV>([&](int k0) { return dorow(m0 + lm, k0); },
-                          [&](int k0) { return ld8(Ds + (n0 + lm) * SV + k0 + 8 * lg); });
-      if constexpr (!ADD)
-        aT[u] += kprod<KBV>([&](int k0) { return ld8(dDs + (m0 + lm) * SV + k0 + 8 * lg); },
-                            [&](int k0) { return ld8(Xs + (n0 + lm) * SV + k0 + 8 * lg) * bsh[n0 + lm]; });
-    }
-    // dQt += dO M0^T, dKt -= diag(beta) Y M0^T, dKh += Delta dM^T  (64 x DK)
-#pragma unroll
-    for (int u = 0; u < NCT; ++u) {
-      const int m0 = 16 * wa, n0 = 16 * (wc + 2 * u);
-      auto fm = [&](int k0) { return ld8(Ms + (n0 + lm) * SV + k0 + 8 * lg); };
-      aQ[u] += kprod<KBV>([&](int k0) { return dorow(m0 + lm, k0); }, fm);
-      if constexpr (!ADD)
-        aK[u] -= kprod<KBV>([&](int k0) { return ld8(Ys + (m0 + lm) * SV + k0 + 8 * lg) * bsh[m0 + lm]; }, fm);
-      aH[u] += kprod<KBV>([&](int k0) { return ld8(Ds + (m0 + lm) * SV + k0 + 8 * lg); },
-                          [&](int k0) { return ld8(dMs + (n0 + lm) * SV + k0 + 8 * lg); });
-    }
-    __syncthreads();  // the slice buffers are rewritten by the next slice
-  }
-
   // ---- dP (inclusive lower) and dT into LDS; dA = -strict(T^T dT T^T)
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -789,7 +706,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
       if (!ADD) dTl[r * SC + i] = aT[u][j];
     }
   }
-  if (tid < KC) dbys[tid] = dby;
+  if (!ADD && tid < KC) dbys[tid] = dbp[0][tid] + dbp[1][tid];
   __syncthreads();
   if constexpr (!ADD) {
 #pragma unroll
@@ -972,7 +889,7 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
   __syncthreads();
   if (tid < DK) {  // d log alpha: reverse prefix of dG plus dG_C, per channel
     const int c = tid;
-    const float dgc = ((gcp[0][c] + gcp[1][c]) + (gcp[2][c] + gcp[3][c])) + __expf(gcl[c]) * dgm;
+    const float dgc = ((gcp[0][c] + gcp[1][c]) + (gcp[2][c] + gcp[3][c])) + __expf(gcl[c]) * dgmc[c];
     float acc = 0.f;
     for (int r = KC - 1; r >= 0; --r) {
       acc += Gs[r * SG + c];
