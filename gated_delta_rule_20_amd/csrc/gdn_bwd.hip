@@ -238,7 +238,7 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kernel(BwdParams p) {
   __shared__ __align__(16) E Kl[BC * PK];
   __shared__ __align__(16) char U[A_BYTES > B_BYTES ? A_BYTES : B_BYTES];
   __shared__ float bs[BC], gs[BC], eg[BC], et[BC], dGs[BC], dBs[BC], misc[4];
-  __shared__ float rq[2][3][BC], dbp[2][BC], wsum[NW];
+  __shared__ float rq[2][3][BC], dbp[2][BC], wsum[NW], rsp[2][NW][BC];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H, dv = p.dv;
@@ -459,17 +459,31 @@ __global__ __launch_bounds__(512, 1) void bwd_chunk_kernel(BwdParams p) {
     }
   }
   __syncthreads();
-  // row / column sums: dG and dbeta; then d log alpha = reverse prefix of dG (+ dG_C)
-  if (tid < BC) {
+  // row / column sums: dG and dbeta (eight parts of eight columns, then the parts in a
+  // fixed order); then d log alpha = reverse prefix of dG (+ dG_C)
+  {
+    const int r = tid & (BC - 1), part = tid >> 6;
+    const float *Wl = ADD ? Rl : Sl;  // wG
     float rs = 0.f, cs = 0.f, bsum = 0.f;
-    for (int i = 0; i < BC; ++i) {
-      const float *Wl = ADD ? Rl : Sl;  // wG
-      rs += Wl[tid * ST + i];
-      cs += Wl[i * ST + tid];
-      if (!ADD) bsum += Rl[tid * ST + i];
+#pragma unroll
+    for (int i = 8 * part; i < 8 * part + 8; ++i) {
+      rs += Wl[r * ST + i];
+      cs += Wl[i * ST + r];
+      if (!ADD) bsum += Rl[r * ST + i];
     }
-    dGs[tid] += rs - cs + (tid == BC - 1 ? misc[0] : 0.f);
-    dBs[tid] += bsum;
+    rsp[0][part][r] = rs - cs;
+    rsp[1][part][r] = bsum;
+  }
+  __syncthreads();
+  if (tid < BC) {
+    float g = 0.f, b = 0.f;
+#pragma unroll
+    for (int part = 0; part < NW; ++part) {
+      g += rsp[0][part][tid];
+      b += rsp[1][part][tid];
+    }
+    dGs[tid] += g + (tid == BC - 1 ? misc[0] : 0.f);
+    dBs[tid] += b;
   }
   __syncthreads();
   if (wave == 0) {
