@@ -92,11 +92,23 @@ __device__ __forceinline__ bf16 *split_hi(bf16 *base, size_t sh, int rows, int c
   return base + sh * 2 * (size_t)rows * cols;
 }
 
+// eight consecutive input elements as fp32 (one 16-byte read for bf16)
+__device__ __forceinline__ f32x8 rowf8(const bf16 *x) { return widen8(ld8(x)); }
+__device__ __forceinline__ f32x8 rowf8(const float *x) { return ld8(x); }
+__device__ __forceinline__ f32x8 zero8() {
+  f32x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = 0.f;
+  return z;
+}
+
+constexpr int PNT = 512;  // threads of the preparation (eight waves)
+
 template <typename E, int DK>
-__global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
+__global__ __launch_bounds__(PNT, 1) void dplrk_prep_kernel(DplrKeyParams p) {
   constexpr int SE = DK + 8;  // element pitch of the staged inputs (rows 16-byte aligned)
   constexpr int SG = DK + 4;
-  constexpr int NP = 256 / DK, RP = KC / NP;  // prefix: parts per channel, rows per part
+  constexpr int NP = PNT / DK, RP = KC / NP;  // prefix: parts per channel, rows per part
   __shared__ __align__(16) E As[KC * SE];
   __shared__ __align__(16) E Bs[KC * SE];
   __shared__ __align__(16) E Ks[KC * SE];
@@ -116,33 +128,33 @@ __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
   if (!slot_chunk_d(p, slot, tb, nv)) return;
   const size_t sh = (size_t)slot * H + h;
   {  // 16-byte loads, all in flight before the LDS stores (rows past the end are zero)
-    constexpr int VE = 16 / (int)sizeof(E), PR = DK / VE, NI = KC * PR / 256;  // inputs
-    constexpr int PG = DK / 4, NG = KC * PG / 256;                             // log alpha
+    constexpr int VE = 16 / (int)sizeof(E), PR = DK / VE, NI = KC * PR / PNT;  // inputs
+    constexpr int PG = DK / 4, NG = KC * PG / PNT;                             // log alpha
     const E *src[4] = {(const E *)p.a, (const E *)p.b, (const E *)p.k, (const E *)p.q};
     E *dst[4] = {As, Bs, Ks, Qs};
     u32x4 x[4][NI], y[NG];
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      const int pc = tid + 256 * u, r = pc / PR, g = pc % PR;
+      const int pc = tid + PNT * u, r = pc / PR, g = pc % PR;
       const size_t o = ((size_t)(tb + r) * H + h) * DK + g * VE;
 #pragma unroll
       for (int a = 0; a < 4; ++a) x[a][u] = r < nv ? *(const u32x4 *)(src[a] + o) : (u32x4){0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      const int pc = tid + 256 * u, r = pc / PG, g = pc % PG;
+      const int pc = tid + PNT * u, r = pc / PG, g = pc % PG;
       y[u] = r < nv ? *(const u32x4 *)(p.log_alpha + ((size_t)(tb + r) * H + h) * DK + 4 * g)
                     : (u32x4){0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      const int pc = tid + 256 * u, r = pc / PR, g = pc % PR;
+      const int pc = tid + PNT * u, r = pc / PR, g = pc % PR;
 #pragma unroll
       for (int a = 0; a < 4; ++a) *(u32x4 *)(dst[a] + r * SE + g * VE) = x[a][u];
     }
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      const int pc = tid + 256 * u, r = pc / PG, g = pc % PG;
+      const int pc = tid + PNT * u, r = pc / PG, g = pc % PG;
       *(u32x4 *)(Gs + r * SG + 4 * g) = y[u];
     }
   }
@@ -162,18 +174,19 @@ __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
       for (int r = q * RP; r < (q + 1) * RP; ++r) Gs[r * SG + d] += off;
   }
   __syncthreads();
-  auto gp = [&](int j, int c) { return j > 0 ? Gs[(j - 1) * SG + c] : 0.f; };
   if (tid < DK) p.gam[sh * DK + tid] = __expf(Gs[(KC - 1) * SG + tid]);
   {  // A e^{Gp} and Q e^G (row-major), the write weights (channel-major), split; each
      // thread forms 8 consecutive elements and stores each half with one 16-byte store
     bf16 *ath = split_hi(p.at, sh, KC, DK), *qgh = split_hi(p.qg, sh, KC, DK);
-    for (int i = 8 * tid; i < KC * DK; i += 8 * 256) {
+    for (int i = 8 * tid; i < KC * DK; i += 8 * PNT) {
       const int r = i / DK, d = i % DK;
+      const f32x8 av = rowf8(As + r * SE + d), qv = rowf8(Qs + r * SE + d), gr = ld8(Gs + r * SG + d);
+      const f32x8 gq = r > 0 ? ld8(Gs + (r - 1) * SG + d) : zero8();
       f32x8 fa, fq;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        fa[e] = to_f(As[r * SE + d + e]) * __expf(gp(r, d + e));
-        fq[e] = to_f(Qs[r * SE + d + e]) * __expf(Gs[r * SG + d + e]);
+        fa[e] = av[e] * __expf(gq[e]);
+        fq[e] = qv[e] * __expf(gr[e]);
       }
       const Split sa = split8(fa), sq = split8(fq);
       *(bf16x8 *)(ath + i) = sa.hi;
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
       *(bf16x8 *)(qgh + KC * DK + i) = sq.lo;
     }
     bf16 *bhh = split_hi(p.bhT, sh, DK, KC), *khh = split_hi(p.khT, sh, DK, KC);
-    for (int i = 8 * tid; i < DK * KC; i += 8 * 256) {
+    for (int i = 8 * tid; i < DK * KC; i += 8 * PNT) {
       const int d = i / KC, r = i % KC;
       const float gC = Gs[(KC - 1) * SG + d];
       f32x8 fb, fk;
@@ -201,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
   }
   // the Gram matrices: the ten lower 16x16 tiles of each (the upper ones are zero)
   bf16 *outs[4] = {nullptr, split_hi(p.aak, sh, KC, KC), split_hi(p.pqb, sh, KC, KC), split_hi(p.pqk, sh, KC, KC)};
-  for (int t = wave; t < 64; t += 4) {
+  for (int t = wave; t < 64; t += PNT / 64) {
     const int w = t >> 4, tt = t & 15, a = tt >> 2, b = tt & 3;  // matrix w, tile (a, b)
     const int m = 16 * a + 7;
     const bool strict = w < 2;  // A_ab, A_ak: i < j; P_qb, P_qk: i <= r
@@ -210,25 +223,22 @@ __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
     f32x4 acc = zero4();
     if (b <= a)
       acc = dprod<DK>(
-          [&](int k0) {
+          [&](int k0) {  // row r of X e^{G[r] - G[m]} (A rows: e^{G[r-1] - G[m]}), vector reads
+            const int r = 16 * a + lm, c0 = k0 + 8 * lg;
+            const int rg = strict ? r - 1 : r;
+            const f32x8 xv = rowf8(X + r * SE + c0), gm = ld8(Gs + m * SG + c0);
+            const f32x8 gx = rg >= 0 ? ld8(Gs + rg * SG + c0) : zero8();
             f32x8 f;
-            const int r = 16 * a + lm;
 #pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
-              const int c = k0 + 8 * lg + ii;
-              const float x = strict ? gp(r, c) : Gs[r * SG + c];
-              f[ii] = to_f(X[r * SE + c]) * __expf(x - Gs[m * SG + c]);
-            }
+            for (int ii = 0; ii < 8; ++ii) f[ii] = xv[ii] * __expf(gx[ii] - gm[ii]);
             return split8(f);
           },
-          [&](int k0) {
+          [&](int k0) {  // row i of Y e^{G[m] - G[i]}
+            const int i = 16 * b + lm, c0 = k0 + 8 * lg;
+            const f32x8 yv = rowf8(Y + i * SE + c0), gm = ld8(Gs + m * SG + c0), gi = ld8(Gs + i * SG + c0);
             f32x8 f;
-            const int i = 16 * b + lm;
 #pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
-              const int c = k0 + 8 * lg + ii;
-              f[ii] = to_f(Y[i * SE + c]) * __expf(Gs[m * SG + c] - Gs[i * SG + c]);
-            }
+            for (int ii = 0; ii < 8; ++ii) f[ii] = yv[ii] * __expf(gm[ii] - gi[ii]);
             return split8(f);
           });
 #pragma unroll
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(256, 1) void dplrk_prep_kernel(DplrKeyParams p) {
   __syncthreads();
   tri_inv64<-1>(Ab, SC, Tb, SC, ys);  // T = (I - A_ab)^-1
   bf16 *tmh = split_hi(p.tm, sh, KC, KC);
-  for (int i = 8 * tid; i < KC * KC; i += 8 * 256) {
+  for (int i = 8 * tid; i < KC * KC; i += 8 * PNT) {
     f32x8 f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = Tb[(i / KC) * SC + i % KC + e];
@@ -513,7 +523,7 @@ template <typename E, int DK>
 hipError_t launch_dk(const DplrKeyParams &p, hipStream_t stream) {
   const unsigned items = (unsigned)(p.slots * p.H), serial = (unsigned)(p.N * p.H * (p.dv / KBV));
   if (serial == 0) return hipSuccess;
-  if (items) hipLaunchKernelGGL((dplrk_prep_kernel<E, DK>), dim3(items), dim3(256), 0, stream, p);
+  if (items) hipLaunchKernelGGL((dplrk_prep_kernel<E, DK>), dim3(items), dim3(PNT), 0, stream, p);
   hipLaunchKernelGGL((dplrk_state_kernel<E, DK, KBV / 16>), dim3(serial), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
