@@ -106,9 +106,11 @@ __device__ __forceinline__ bool slot_chunk(const BwdKeyParams &p, long slot, lon
   return true;
 }
 
+constexpr int PNT = 512;  // threads of the preparation (eight waves)
+
 // ---------------------------------------------------------------- 1. operands per chunk
 template <typename E, int DK, bool ADD>
-__global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
+__global__ __launch_bounds__(PNT, 1) void bwdk_prep_kernel(BwdKeyParams p) {
   constexpr int SG = DK + 4;
   __shared__ __align__(16) float Ks[KC * SG];
   __shared__ __align__(16) float Qs[KC * SG];
@@ -128,26 +130,26 @@ __global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
   if (!slot_chunk(p, slot, tb, nv)) return;
   const size_t sh = (size_t)slot * H + h;
   {  // 16-byte loads, all in flight before the LDS stores (rows past the end are zero)
-    constexpr int VE = 16 / (int)sizeof(E), PR = DK / VE, NI = KC * PR / 256;  // k, q
-    constexpr int PG = DK / 4, NG = KC * PG / 256;                             // log alpha
+    constexpr int VE = 16 / (int)sizeof(E), PR = DK / VE, NI = KC * PR / PNT;  // k, q
+    constexpr int PG = DK / 4, NG = KC * PG / PNT;                             // log alpha
     typedef E EV __attribute__((ext_vector_type(16 / sizeof(E))));
     u32x4 xk[NI], xq[NI], y[NG];
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      const int pc = tid + 256 * u, r = pc / PR, g = pc % PR;
+      const int pc = tid + PNT * u, r = pc / PR, g = pc % PR;
       const size_t o = ((size_t)(tb + r) * H + h) * DK + g * VE;
       xk[u] = r < nv ? *(const u32x4 *)((const E *)p.k + o) : (u32x4){0u, 0u, 0u, 0u};
       xq[u] = r < nv ? *(const u32x4 *)((const E *)p.q + o) : (u32x4){0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      const int pc = tid + 256 * u, r = pc / PG, g = pc % PG;
+      const int pc = tid + PNT * u, r = pc / PG, g = pc % PG;
       y[u] = r < nv ? *(const u32x4 *)(p.log_alpha + ((size_t)(tb + r) * H + h) * DK + 4 * g)
                     : (u32x4){0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      const int pc = tid + 256 * u, r = pc / PR, g = pc % PR;
+      const int pc = tid + PNT * u, r = pc / PR, g = pc % PR;
       const EV ek = __builtin_bit_cast(EV, xk[u]), eq = __builtin_bit_cast(EV, xq[u]);
 #pragma unroll
       for (int e = 0; e < VE; ++e) {
@@ -157,15 +159,15 @@ __global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
     }
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      const int pc = tid + 256 * u, r = pc / PG, g = pc % PG;
+      const int pc = tid + PNT * u, r = pc / PG, g = pc % PG;
       *(u32x4 *)(Gs + r * SG + 4 * g) = y[u];
     }
   }
   if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? p.beta[(size_t)(tb + tid) * H + h] : 0.f;
-  for (int i = tid; i < KC * SC; i += 256) As[i] = Ps[i] = 0.f;
+  for (int i = tid; i < KC * SC; i += PNT) As[i] = Ps[i] = 0.f;
   __syncthreads();
-  {  // per-channel inclusive prefix: 256 / DK parts of rows per channel, then the offsets
-    constexpr int NP = 256 / DK, RP = KC / NP;
+  {  // per-channel inclusive prefix: PNT / DK parts of rows per channel, then the offsets
+    constexpr int NP = PNT / DK, RP = KC / NP;
     const int d = tid % DK, q = tid / DK;
     float g = 0.f;
     for (int r = q * RP; r < (q + 1) * RP; ++r) {
@@ -181,12 +183,13 @@ __global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
   }
   __syncthreads();
   // row-major Kt, Kh: 8 consecutive channels per thread (two 16-byte stores each)
-  for (int i = 8 * tid; i < KC * DK; i += 8 * 256) {
+  for (int i = 8 * tid; i < KC * DK; i += 8 * PNT) {
     const int r = i / DK, d = i % DK;
+    const f32x8 gv = ld8(Gs + r * SG + d), gc = ld8(Gs + (KC - 1) * SG + d), kk = ld8(Ks + r * SG + d);
     f32x4 kt0, kt1, kh0, kh1;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float g = Gs[r * SG + d + e], gC = Gs[(KC - 1) * SG + d + e], kv = Ks[r * SG + d + e];
+      const float g = gv[e], gC = gc[e], kv = kk[e];
       const float a = kv * __expf(g), b = kv * __expf(gC - g);
       if (e < 4) kt0[e] = a, kh0[e] = b;
       else kt1[e - 4] = a, kh1[e - 4] = b;
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
     *(f32x4 *)(p.kh + sh * KC * DK + i + 4) = kh1;
   }
   // channel-major Kt^T, Kh^T, Qt^T: 8 consecutive rows per thread
-  for (int i = 8 * tid; i < DK * KC; i += 8 * 256) {
+  for (int i = 8 * tid; i < DK * KC; i += 8 * PNT) {
     const int d = i / KC, r = i % KC;
     const float gC = Gs[(KC - 1) * SG + d];
     f32x4 a0, a1, b0, b1, c0, c1;
@@ -222,29 +225,25 @@ __global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
   if (tid < DK) p.gam[sh * DK + tid] = __expf(Gs[(KC - 1) * SG + tid]);
   // the ten lower 16x16 tiles of P (and of A): row operand x[r] e^{G[r] - G[m]}, column
   // operand K[i] e^{G[m] - G[i]}, m = 16a + 7 of the row block a
-  for (int t = wave; t < (ADD ? 10 : 20); t += 4) {
+  for (int t = wave; t < (ADD ? 10 : 20); t += PNT / 64) {
     const int tt = t % 10, a = tt < 1 ? 0 : tt < 3 ? 1 : tt < 6 ? 2 : 3;
     const int b = tt - a * (a + 1) / 2, m = 16 * a + 7;
     const float *X = t < 10 ? Qs : Ks;
     const f32x4 acc = kprod<DK>(
-        [&](int k0) {
+        [&](int k0) {  // row r of x e^{G[r] - G[m]} (16-byte reads)
+          const int r = 16 * a + lm, c0 = k0 + 8 * lg;
+          const f32x8 xv = ld8(X + r * SG + c0), gr = ld8(Gs + r * SG + c0), gm = ld8(Gs + m * SG + c0);
           f32x8 f;
-          const int r = 16 * a + lm;
 #pragma unroll
-          for (int ii = 0; ii < 8; ++ii) {
-            const int c = k0 + 8 * lg + ii;
-            f[ii] = X[r * SG + c] * __expf(Gs[r * SG + c] - Gs[m * SG + c]);
-          }
+          for (int ii = 0; ii < 8; ++ii) f[ii] = xv[ii] * __expf(gr[ii] - gm[ii]);
           return f;
         },
-        [&](int k0) {
+        [&](int k0) {  // row i of K e^{G[m] - G[i]}
+          const int i = 16 * b + lm, c0 = k0 + 8 * lg;
+          const f32x8 kv = ld8(Ks + i * SG + c0), gi = ld8(Gs + i * SG + c0), gm = ld8(Gs + m * SG + c0);
           f32x8 f;
-          const int i = 16 * b + lm;
 #pragma unroll
-          for (int ii = 0; ii < 8; ++ii) {
-            const int c = k0 + 8 * lg + ii;
-            f[ii] = Ks[i * SG + c] * __expf(Gs[m * SG + c] - Gs[i * SG + c]);
-          }
+          for (int ii = 0; ii < 8; ++ii) f[ii] = kv[ii] * __expf(gm[ii] - gi[ii]);
           return f;
         });
 #pragma unroll
@@ -259,13 +258,13 @@ __global__ __launch_bounds__(256, 1) void bwdk_prep_kernel(BwdKeyParams p) {
   __syncthreads();
   if constexpr (!ADD) {
     tri_inv64<1>(As, SC, Ts, SC, ys);  // T = (I + A)^-1
-    for (int i = tid; i < KC * KC; i += 256) {
+    for (int i = tid; i < KC * KC; i += PNT) {
       const int r = i / KC, c = i % KC;
       p.tm[sh * KC * KC + i] = Ts[r * SC + c];
       p.tmT[sh * KC * KC + i] = Ts[c * SC + r];
     }
   }
-  for (int i = tid; i < KC * KC; i += 256) {
+  for (int i = tid; i < KC * KC; i += PNT) {
     const int r = i / KC, c = i % KC;
     p.pmT[sh * KC * KC + i] = Ps[c * SC + r];
   }
@@ -918,13 +917,13 @@ hipError_t launch_k(const BwdKeyParams &p, bool add, hipStream_t stream) {
   const unsigned items = (unsigned)(p.slots * p.H), serial = (unsigned)(p.N * p.H * (p.dv / KBV));
   if (items == 0 || serial == 0) return hipSuccess;
   if (add) {
-    hipLaunchKernelGGL((bwdk_prep_kernel<E, DK, true>), dim3(items), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwdk_prep_kernel<E, DK, true>), dim3(items), dim3(PNT), 0, stream, p);
     if (!p.states_ready)
       hipLaunchKernelGGL((bwdk_fwd_kernel<E, DK, true>), dim3(serial), dim3(256), 0, stream, p);
     launch_rev<E, DK, true>(p, stream);
     hipLaunchKernelGGL((bwdk_chunk_kernel<E, DK, true>), dim3(items), dim3(512), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((bwdk_prep_kernel<E, DK, false>), dim3(items), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwdk_prep_kernel<E, DK, false>), dim3(items), dim3(PNT), 0, stream, p);
     if (!p.states_ready)
       hipLaunchKernelGGL((bwdk_fwd_kernel<E, DK, false>), dim3(serial), dim3(256), 0, stream, p);
     launch_rev<E, DK, false>(p, stream);
