@@ -465,16 +465,19 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
   };
   // dO of a chunk, beta and e^{g_C} (no branch around a load: rows past the end read
   // the last row and are zeroed when staged)
-  constexpr int VC = VB / 4, VL = VC * (int)sizeof(E) / 16;
-  u32x4 oraw[VL];
+  // 16-byte pieces of a chunk's dO slice: NPR per row, PPT per thread (a thread-count
+  // guard when there are fewer pieces than threads, uniform over each wave)
+  constexpr int VE = 16 / (int)sizeof(E), NPR = VB / VE, NPO = KC * NPR, PPT = (NPO + 255) / 256;
+  u32x4 oraw[PPT];
   float bnext = 0.f, gnext = 0.f;
   auto load_o = [&](int cc) {
     const int nvc = min(KC, len - cc * KC);
     const size_t tbc = (size_t)tok0 + (size_t)cc * KC;
-    const int r = min(tid >> 2, nvc - 1), g = tid & 3;
-    const E *src = (const E *)p.dout + ((tbc + r) * H + h) * dv + col0 + VC * g;
 #pragma unroll
-    for (int u = 0; u < VL; ++u) oraw[u] = *(const u32x4 *)(src + u * (16 / (int)sizeof(E)));
+    for (int u = 0; u < PPT; ++u) {
+      const int pc = tid + 256 * u, r = min(pc / NPR, nvc - 1), g = pc % NPR;
+      if (pc < NPO) oraw[u] = *(const u32x4 *)((const E *)p.dout + ((tbc + r) * H + h) * dv + col0 + VE * g);
+    }
     if (!ADD) bnext = p.beta[(tbc + min(tid % KC, nvc - 1)) * H + h];
     gnext = p.gam[((size_t)(slot0 + cc) * H + h) * DK + tid % DK];
   };
@@ -499,16 +502,17 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
         put_t(dMh, dMl, PM, 16 * (RB * wave + rb), ct, dM[rb][ct]);
       }
     {
-      const int r = tid >> 2, g = tid & 3;
-      const bool in = r < nv;
 #pragma unroll
-      for (int u = 0; u < VL; ++u) {
+      for (int u = 0; u < PPT; ++u) {
+        const int pc = tid + 256 * u, r = pc / NPR, g = pc % NPR;
+        if (pc >= NPO) break;
+        const bool in = r < nv;
         typedef E EV __attribute__((ext_vector_type(16 / sizeof(E))));
         const EV ev = __builtin_bit_cast(EV, oraw[u]);
 #pragma unroll
-        for (int e = 0; e < 16 / (int)sizeof(E); ++e) {
+        for (int e = 0; e < VE; ++e) {
           const float x = in ? to_f(ev[e]) : 0.f;
-          const int col = VC * g + u * (16 / (int)sizeof(E)) + e;
+          const int col = VE * g + e;
           const bf16 hv = (bf16)x;
           dOh[col * PV + r] = hv;
           if constexpr (!VX) dOl[col * PV + r] = (bf16)(x - (float)hv);
@@ -898,17 +902,20 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
   if (!ADD && tid < nv) p.dbeta[(size_t)(tb + tid) * H + h] = dbys[tid] + (rb[0][tid] + rb[1][tid]);
 }
 
-// The reverse pass takes 64 value columns per workgroup when that still gives one
-// workgroup per compute unit (the A operands are then read once for twice the columns),
-// else 32
+// The reverse pass takes the widest value block (64, 32 or 16 columns) that still gives
+// one workgroup per compute unit: a wider block reads the A operands once for more
+// columns, a narrower one puts more of the chip to work on few long sequences
 template <typename E, int DK, bool ADD>
 void launch_rev(const BwdKeyParams &p, hipStream_t stream) {
   const long pairs = (long)p.N * p.H;
-  if (p.dv % 64 == 0 && pairs * (p.dv / 64) >= 256)
+  if (pairs * (p.dv / 64) >= 256)
     hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, 64>), dim3((unsigned)(pairs * (p.dv / 64))), dim3(256), 0,
                        stream, p);
+  else if (pairs * (p.dv / 32) >= 256)
+    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, 32>), dim3((unsigned)(pairs * (p.dv / 32))), dim3(256), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, KBV>), dim3((unsigned)(pairs * (p.dv / KBV))), dim3(256), 0,
+    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, 16>), dim3((unsigned)(pairs * (p.dv / 16))), dim3(256), 0,
                        stream, p);
 }
 

@@ -74,6 +74,17 @@ def test_bwd_head_dims(gdn, dk, dv, gate):
     check(gdn, synth.random_inputs(2, 150, 2, dk, dv, gate, "bf16", seed=dk + dv, state_std=0.05), seed=1)
 
 
+@pytest.mark.parametrize("B,H,dv,width", [(2, 2, 128, 16), (16, 8, 64, 32), (32, 8, 128, 64)])
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_bwd_reverse_pass_widths(gdn, B, H, dv, width, gate):
+    """The reverse pass takes the widest value block of 64, 32 or 16 columns that still
+    gives N H d_v / width >= 256 workgroups (else 16); these shapes select each width."""
+    pairs = B * H
+    assert (pairs * dv // 64 >= 256) == (width == 64)
+    assert (pairs * dv // 64 < 256 <= pairs * dv // 32) == (width == 32)
+    check(gdn, synth.random_inputs(B, 130, H, 128, dv, gate, "bf16", seed=width, state_std=0.05), seed=width)
+
+
 @pytest.mark.parametrize("dv", [64, 128])
 @pytest.mark.parametrize("gate", ["none", "head"])
 def test_bwd_fp32(gdn, dv, gate):
