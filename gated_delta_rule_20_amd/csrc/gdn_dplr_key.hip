@@ -524,7 +524,13 @@ hipError_t launch_dk(const DplrKeyParams &p, hipStream_t stream) {
   const unsigned items = (unsigned)(p.slots * p.H), serial = (unsigned)(p.N * p.H * (p.dv / KBV));
   if (serial == 0) return hipSuccess;
   if (items) hipLaunchKernelGGL((dplrk_prep_kernel<E, DK>), dim3(items), dim3(PNT), 0, stream, p);
-  hipLaunchKernelGGL((dplrk_state_kernel<E, DK, KBV / 16>), dim3(serial), dim3(256), 0, stream, p);
+  // 64 value columns per workgroup when that still gives one per compute unit (the A
+  // operands are then read once for twice the columns; the full-size per-channel test
+  // takes this path), else 32
+  if ((long)p.N * p.H * (p.dv / 64) >= 256)
+    hipLaunchKernelGGL((dplrk_state_kernel<E, DK, 4>), dim3(serial / 2), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((dplrk_state_kernel<E, DK, KBV / 16>), dim3(serial), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
