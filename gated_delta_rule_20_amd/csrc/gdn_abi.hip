@@ -390,7 +390,15 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
       pp.N = a->N;
       pp.H = a->H;
       pp.T = a->T;
-      if (gdn::launch_key_prep(pp, FL.slots, a->write == GDN_WRITE_ADD, stream) != hipSuccess) return GDN_ERR_HIP;
+      const bool add = a->write == GDN_WRITE_ADD;
+      const int windows = key_windows(&f), ns = a->N * a->H * (a->d_v / 64), free_cus = gdn::device_cus() - ns;
+      const bool windowed = windows > 1 && free_cus > 0;
+      if (windowed) {  // this launch prepares window 0 only
+        pp.c_lo = 0;
+        pp.c_hi = KEY_WINDOW;
+        pp.win_items = 1;
+      }
+      if (gdn::launch_key_prep(pp, FL.slots, add, stream) != hipSuccess) return GDN_ERR_HIP;
       gdn::FwdParams fp;
       fp.q = pp.q_g;
       fp.k = pp.k_g;
@@ -412,8 +420,23 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
       fp.nb = a->d_v / 64;
       fp.la_stride = a->H;
       fp.chunk_states = arr[0];
-      if (gdn::launch_fwd_pipe(fp, gdn::GATE_KEY, a->write == GDN_WRITE_ADD, stream) != hipSuccess)
+      if (windowed) {
+        // as in the forward: window w's state pass shares a launch with window w + 1's
+        // preparation
+        float *carry = (float *)(fw + 3 * FL.kq + FL.tp + FL.eg);
+        for (int w = 0; w < windows; ++w) {
+          fp.c_lo = w * KEY_WINDOW;
+          fp.c_hi = (w + 1) * KEY_WINDOW;
+          fp.init_state = w == 0 ? a->initial_state : carry;
+          fp.final_state = w == windows - 1 ? nullptr : carry;
+          pp.c_lo = (w + 1) * KEY_WINDOW;
+          pp.c_hi = (w + 2) * KEY_WINDOW;
+          if (gdn::launch_key_window(fp, pp, FL.slots, w + 1 < windows ? free_cus : 0, add, stream) != hipSuccess)
+            return GDN_ERR_HIP;
+        }
+      } else if (gdn::launch_fwd_pipe(fp, gdn::GATE_KEY, add, stream) != hipSuccess) {
         return GDN_ERR_HIP;
+      }
       kp.states_ready = 1;
     }
     if (gdn::launch_bwd_key(kp, a->dtype == GDN_BF16 ? 1 : 0, a->d_k, a->write == GDN_WRITE_ADD, stream) !=

@@ -1397,11 +1397,12 @@ __global__ __launch_bounds__(KP_NT, 1) void key_prep_kernel(KeyPrepParams p, lon
 // touch disjoint chunk slots, so nothing in the launch waits for anything else.
 static_assert(NT == KP_NT, "both roles run with one block size");
 constexpr int WIN_LDS = LDS_TOTAL > KP_BYTES ? LDS_TOTAL : KP_BYTES;
-template <bool ADD>
+// (STATES: the gradient pass's recomputation, chunk states instead of o)
+template <bool ADD, bool STATES>
 __global__ __launch_bounds__(NT, 1) void key_window_kernel(FwdParams fp, KeyPrepParams kp, long items, int ns) {
   __shared__ __align__(16) char smem[WIN_LDS];
   if ((int)blockIdx.x < ns)
-    fwd_pipe_body<GATE_KEY, ADD, false, true>(fp, smem, blockIdx.x);
+    fwd_pipe_body<GATE_KEY, ADD, STATES, true>(fp, smem, blockIdx.x);
   else
     key_prep_body<ADD>(kp, items, smem, (int)blockIdx.x - ns, (int)gridDim.x - ns);
 }
@@ -1451,10 +1452,17 @@ hipError_t launch_key_window(const FwdParams &fp, const KeyPrepParams &kp, long 
   const long items = kp.win_items ? (long)kp.N * (kp.c_hi - kp.c_lo) * kp.H : slots * kp.H;
   if (ns <= 0 || nprep < 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(ns + nprep));
-  if (add)
-    hipLaunchKernelGGL(key_window_kernel<true>, grid, dim3(NT), 0, stream, fp, kp, items, ns);
-  else
-    hipLaunchKernelGGL(key_window_kernel<false>, grid, dim3(NT), 0, stream, fp, kp, items, ns);
+  if (fp.chunk_states) {
+    if (add)
+      hipLaunchKernelGGL((key_window_kernel<true, true>), grid, dim3(NT), 0, stream, fp, kp, items, ns);
+    else
+      hipLaunchKernelGGL((key_window_kernel<false, true>), grid, dim3(NT), 0, stream, fp, kp, items, ns);
+  } else {
+    if (add)
+      hipLaunchKernelGGL((key_window_kernel<true, false>), grid, dim3(NT), 0, stream, fp, kp, items, ns);
+    else
+      hipLaunchKernelGGL((key_window_kernel<false, false>), grid, dim3(NT), 0, stream, fp, kp, items, ns);
+  }
   return hipGetLastError();
 }
 
