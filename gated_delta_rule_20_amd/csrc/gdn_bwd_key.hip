@@ -802,53 +802,45 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
       }
       return f;
     };
-    // rows r >= 16 a of x[r] e^{G[r] - G[m]}
-    auto rrow = [&](auto X, int k0) {
-      f32x8 f;
+    // Pr and Z share their column operand, Pc and Zc their row factors: each is formed
+    // once per 32-deep step
+    f32x4 Pr = zero4(), Z = zero4(), Pc = zero4(), Zc = zero4();
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int r = k0 + 8 * lg + ii;
-        f[ii] = r >= 16 * a ? X(r, c) * __expf(Gs[r * SG + c] - gm) : 0.f;
+    for (int k0 = 0; k0 < KC; k0 += 32) {
+      if (k0 < 16 * (a + 1)) {  // columns i < 16 (a + 1)
+        const Split bk = split8(kcol(k0));
+        f32x8 fp;
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) fp[ii] = dPl[(16 * a + lm) * SC + k0 + 8 * lg + ii];
+        Pr = mm(split8(fp), bk, Pr);
+        if constexpr (!ADD) {
+          f32x8 ft;
+#pragma unroll
+          for (int ii = 0; ii < 8; ++ii) ft[ii] = dTl[(16 * a + lm) * SC + k0 + 8 * lg + ii];
+          Z = mm(split8(ft), bk, Z);
+        }
       }
-      return f;
-    };
-    const f32x4 Pr = kprod<KC>(
-        [&](int k0) {
-          f32x8 f;
+      if (k0 + 32 > 16 * a) {  // rows r >= 16 a
+        f32x8 fq, fk, fp;
 #pragma unroll
-          for (int ii = 0; ii < 8; ++ii) f[ii] = dPl[(16 * a + lm) * SC + k0 + 8 * lg + ii];
-          return f;
-        },
-        kcol, 0, 16 * (a + 1));
-    const f32x4 Pc = kprod<KC>(
-        [&](int k0) {
-          f32x8 f;
+        for (int ii = 0; ii < 8; ++ii) {
+          const int r = k0 + 8 * lg + ii;
+          const float e = r >= 16 * a ? __expf(Gs[r * SG + c] - gm) : 0.f;
+          fq[ii] = Q_(r, c) * e;
+          fk[ii] = K_(r, c) * e;
+          fp[ii] = dPl[r * SC + 16 * a + lm];
+        }
+        Pc = mm(split8(fp), split8(fq), Pc);
+        if constexpr (!ADD) {
+          f32x8 ft;
 #pragma unroll
-          for (int ii = 0; ii < 8; ++ii) f[ii] = dPl[(k0 + 8 * lg + ii) * SC + 16 * a + lm];
-          return f;
-        },
-        [&](int k0) { return rrow(Q_, k0); }, 16 * a, KC);
-    f32x4 Z = zero4(), Zc = zero4();
-    if constexpr (!ADD) {
-      Z = kprod<KC>(
-          [&](int k0) {
-            f32x8 f;
-#pragma unroll
-            for (int ii = 0; ii < 8; ++ii) f[ii] = dTl[(16 * a + lm) * SC + k0 + 8 * lg + ii];
-            return f;
-          },
-          kcol, 0, 16 * (a + 1));
-      Zc = kprod<KC>(
-          [&](int k0) {
-            f32x8 f;
-#pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
-              const int r = k0 + 8 * lg + ii;
-              f[ii] = bsh[r] * dTl[r * SC + 16 * a + lm];
-            }
-            return f;
-          },
-          [&](int k0) { return rrow(K_, k0); }, 16 * a, KC);
+          for (int ii = 0; ii < 8; ++ii) {
+            const int r = k0 + 8 * lg + ii;
+            ft[ii] = bsh[r] * dTl[r * SC + 16 * a + lm];
+          }
+          Zc = mm(split8(ft), split8(fk), Zc);
+        }
+      }
     }
     float gcs = 0.f;
     const float gC = gcl[c];
