@@ -274,19 +274,20 @@ BwdLayout bwd_layout(const gdn_bwd_args *a) {
   L.slots = gdn::key_slots(tokens, a->N);
   const size_t sh = (size_t)L.slots * a->H, dk = a->d_k, dv = a->d_v;
   const bool delta = a->write == GDN_WRITE_DELTA, key = a->gate == GDN_GATE_KEY;
+  const size_t es = a->dtype == GDN_BF16 ? 2 : 4;  // the scalar gates' Q^T and K^T: I/O dtype
   const size_t sizes[13] = {
-      sh * dk * dv * 4,                    // states
-      sh * dk * dv * 4,                    // chunk-end state gradients
-      sh * 64 * dv * 4,                    // dDelta
-      delta ? sh * 4096 * 4 : 0,           // T
-      delta ? sh * 4096 * 4 : 0,           // T^T
-      sh * 4096 * 4,                       // P^T
-      key && delta ? sh * 64 * dk * 4 : 0, // K e^G (per key channel)
-      sh * 64 * dk * 4,                    // K e^{g_C - G}
-      delta ? sh * dk * 64 * 4 : 0,        // (K e^G)^T
-      sh * dk * 64 * 4,                    // (Q e^G)^T
-      key ? sh * dk * 64 * 4 : 0,          // (K e^{g_C - G})^T (per key channel)
-      sh * dk * 4,                         // e^{g_C}
+      sh * dk * dv * 4,                              // states
+      sh * dk * dv * 4,                              // chunk-end state gradients
+      sh * 64 * dv * 4,                              // dDelta
+      delta ? sh * 4096 * 4 : 0,                     // T
+      delta ? sh * 4096 * 4 : 0,                     // T^T
+      sh * 4096 * 4,                                 // P^T
+      key && delta ? sh * 64 * dk * 4 : 0,           // K e^G (per key channel)
+      key ? sh * 64 * dk * 4 : sh * 128 * 4,         // K e^{g_C - G}; scalar gates: e^g, e^{g_C - g} rows
+      delta ? sh * dk * 64 * (key ? 4 : es) : 0,     // (K e^G)^T; scalar gates: K^T
+      sh * dk * 64 * (key ? 4 : es),                 // (Q e^G)^T; scalar gates: Q^T
+      key ? sh * dk * 64 * 4 : 0,                    // (K e^{g_C - G})^T (per key channel)
+      sh * dk * 4,                                   // e^{g_C}
       a->gate == GDN_GATE_HEAD_CONST ? (size_t)tokens * a->H * 4 : 0};  // per-token decay gradients
   for (int i = 0; i < 13; ++i) L.sz[i] = align256(sizes[i]);
   return L;
@@ -494,9 +495,10 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
   bp.tm = arr[3];
   bp.tmT = arr[4];
   bp.pmT = arr[5];
-  bp.kh = arr[7];
-  bp.ktT = arr[8];
-  bp.qtT = arr[9];
+  bp.egr = arr[7];
+  bp.etr = arr[7] + (size_t)L.slots * a->H * 64;
+  bp.kT = arr[8];
+  bp.qT = arr[9];
   bp.gam = arr[11];
   bp.dq = a->dq;
   bp.dk = a->dk;

@@ -21,11 +21,12 @@
 //     pipelined kernel's STATES variant for bf16 with d_k = 128, the fused kernel
 //     otherwise;
 //  2. bwd_prep_kernel, one workgroup per (chunk, head), fully parallel: T, T^T and P^T of
-//     every chunk, and the operands of the reverse pass (Kh, Qt^T, Kt^T, gam);
-//  3. the reverse state pass of the per-key-channel gradients (launch_bwdk_rev), which
-//     these operands fit unchanged: one workgroup per (sequence, head, 32 value columns)
-//     walks the chunks in reverse with dM in matrix-core accumulators and writes dM and
-//     dDelta of every chunk, dV and the initial-state gradient;
+//     every chunk, and the other operands of the reverse pass (Q^T, K^T, e^G and e^{G_C -
+//     G} per row, gam);
+//  3. the reverse state pass of the per-key-channel gradients in its scalar-gate form
+//     (launch_bwdk_rev): one workgroup per (sequence, head, value block) walks the chunks
+//     in reverse with dM in matrix-core accumulators and writes dM and dDelta of every
+//     chunk, dV and the initial-state gradient;
 //  4. bwd_chunk_kernel, one workgroup per (chunk, head), fully parallel: every product
 //     over the value columns at full width (X, Delta, Y, dP, dT, dQt, dKt, dKh) from the
 //     stored M0, dM and dDelta, 32 columns at a time, then dA, the Gram and Gamma terms,
@@ -99,9 +100,9 @@ __device__ __forceinline__ void decay_prefix(float *gs, float *eg, float *et, fl
 
 // One workgroup per (chunk slot, head), fully parallel: P = incl(Q K^T * Gamma) and, for
 // the delta write, T = (I + A)^-1 with A = strict(diag(beta) K K^T * Gamma) (blocked
-// inverse, tri_inv64); into the workspace P^T, T, T^T, Kh = e^{G_C - G} K (row-major),
-// (e^G Q)^T, (e^G K)^T (channel-major) and gam = e^{G_C} repeated over the key channels,
-// the operands of the reverse pass.  The Gram tiles take the bf16 inputs exactly.
+// inverse, tri_inv64); into the workspace P^T, T, T^T, and for the reverse pass Q^T, K^T
+// (channel-major copies of the inputs), e^G and e^{G_C - G} per row and gam = e^{G_C}
+// repeated over the key channels.  The Gram tiles take the bf16 inputs exactly.
 template <typename E, int DK, int GATE, bool ADD>
 __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(BwdParams p) {
   constexpr int SKE = DK + 8;
@@ -173,36 +174,29 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(BwdParams p) {
     }
     *(f32x4 *)(pmT + (n0 + lm) * BC + m0 + 4 * lg) = pt;
   }
-  // Kh rows (8 consecutive channels per thread), then (e^G Q)^T and (e^G K)^T (8
-  // consecutive rows per thread) and gam
-  for (int i = 8 * tid; i < BC * DK; i += 8 * 256) {
-    const int r = i / DK, d = i % DK;
-    const float s = et[r];
-    f32x4 a0, a1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a0[e] = K_(r, d + e) * s;
-      a1[e] = K_(r, d + 4 + e) * s;
-    }
-    *(f32x4 *)(p.kh + sh * BC * DK + i) = a0;
-    *(f32x4 *)(p.kh + sh * BC * DK + i + 4) = a1;
-  }
+  // Q^T and K^T (channel-major, the I/O dtype; 8 consecutive rows per thread), the row
+  // factors e^G and e^{G_C - G} (0 past the sequence end) and gam
   for (int i = 8 * tid; i < DK * BC; i += 8 * 256) {
     const int d = i / BC, r = i % BC;
-    f32x4 q0, q1, k0, k1;
+    E q8[8], k8[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      q0[e] = Q_(r + e, d) * eg[r + e];
-      q1[e] = Q_(r + 4 + e, d) * eg[r + 4 + e];
-      k0[e] = K_(r + e, d) * eg[r + e];
-      k1[e] = K_(r + 4 + e, d) * eg[r + 4 + e];
+    for (int e = 0; e < 8; ++e) {
+      q8[e] = Ql[(r + e) * SKE + d];
+      k8[e] = Kl[(r + e) * SKE + d];
     }
-    *(f32x4 *)(p.qtT + sh * DK * BC + i) = q0;
-    *(f32x4 *)(p.qtT + sh * DK * BC + i + 4) = q1;
-    if (!ADD) {
-      *(f32x4 *)(p.ktT + sh * DK * BC + i) = k0;
-      *(f32x4 *)(p.ktT + sh * DK * BC + i + 4) = k1;
+    E *qt = (E *)p.qT + sh * DK * BC + i, *kt = (E *)p.kT + sh * DK * BC + i;
+#pragma unroll
+    for (int e = 0; e < 8; e += 16 / (int)sizeof(E)) {
+      u32x4 wq, wk;
+      __builtin_memcpy(&wq, q8 + e, 16);
+      __builtin_memcpy(&wk, k8 + e, 16);
+      *(u32x4 *)(qt + e) = wq;
+      if (!ADD) *(u32x4 *)(kt + e) = wk;
     }
+  }
+  if (tid < BC) {
+    p.egr[sh * BC + tid] = tid < nv ? eg[tid] : 0.f;
+    p.etr[sh * BC + tid] = tid < nv ? et[tid] : 0.f;
   }
   if (tid < DK) p.gam[sh * DK + tid] = gcs[0];
   if constexpr (!ADD) {
@@ -539,9 +533,10 @@ hipError_t launch_bg(const BwdParams &p, hipStream_t stream) {
   kp.dd = p.dd;
   kp.tmT = p.tmT;
   kp.pmT = p.pmT;
-  kp.kh = p.kh;
-  kp.ktT = p.ktT;
-  kp.qtT = p.qtT;
+  kp.qT = p.qT;
+  kp.kT = p.kT;
+  kp.egr = p.egr;
+  kp.etr = p.etr;
   kp.gam = p.gam;
   kp.dv_out = p.dv_out;
   kp.dinit = p.dinit;

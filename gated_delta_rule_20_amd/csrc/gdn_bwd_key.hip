@@ -376,11 +376,18 @@ __global__ __launch_bounds__(256, 1) void bwdk_fwd_kernel(BwdKeyParams p) {
 // -diag(beta) Y) are staged once per chunk in LDS, transposed and split into hi and lo
 // bf16 halves, so that every fragment is two 16-byte reads; the A operands are read
 // from the workspace one phase ahead of their products.
-template <typename E, int DK, bool ADD, int VB>
+// SCAL (no gate or a scalar gate): K, Q^T and K^T are the inputs themselves (exact in
+// bf16) and the row factors move to the other side: dDelta = P^T dO + diag(e^{g_C - g})
+// (K dM), and e^g scales the staged B operands of the dM update (e^g dO, -e^g beta Y).
+template <typename E, int DK, bool ADD, int VB, bool SCAL>
 __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
   constexpr int PM = DK + 8, PV = KC + 8;  // bf16 pitches of the transposed operands
   constexpr int NCT = VB / 16, RB = DK / 64, SK = DK / 32;
   constexpr bool VX = std::is_same<E, bf16>::value;  // dO exact in bf16: no lo half
+  typedef decltype(in8((const E *)nullptr)) KF;      // an input fragment (exact or split)
+  __shared__ __align__(16) bf16 dGh[SCAL ? VB * PV : 8];  // e^g dO (SCAL)
+  __shared__ __align__(16) bf16 dGl[SCAL ? VB * PV : 8];
+  __shared__ float egs[KC], ets[KC];                      // e^g, e^{g_C - g} (SCAL)
   __shared__ __align__(16) bf16 dMh[VB * PM];
   __shared__ __align__(16) bf16 dMl[VB * PM];
   __shared__ __align__(16) bf16 dOh[VB * PV];
@@ -438,14 +445,25 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
   typedef decltype(ofrag(0, 0)) OF;
   const int r0 = 16 * wave + lm;  // this lane's A row of the 64-row products
   const int s0 = wave >> 1;       // P^T and T^T rows of block w vanish below column 16 w
-  // A fragments (fp32 rows of the workspace), loaded one phase ahead, split when used
-  f32x8 f_pm[2], f_kh[SK], f_tm[2], f_qt[RB][2], f_kt[RB][2];
-  auto load_1 = [&](size_t sh) {
+  // A fragments (fp32 rows of the workspace, split when used; SCAL: the inputs), loaded
+  // one phase ahead
+  f32x8 f_pm[2], f_kh[SCAL ? 1 : SK], f_tm[2], f_qt[SCAL ? 1 : RB][2], f_kt[SCAL ? 1 : RB][2];
+  KF k_r[SCAL ? SK : 1], q_t[SCAL ? RB : 1][2], k_t[SCAL ? RB : 1][2];
+  auto load_1 = [&](int cc) {
+    const size_t sh = (size_t)(slot0 + cc) * H + h;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       if (s >= s0) f_pm[s] = ld8(p.pmT + (sh * KC + r0) * KC + 32 * s + 8 * lg);
+    if constexpr (SCAL) {  // K row r0 of the chunk (rows past the end re-read the last row:
+                           // their e^{g_C - g} is 0)
+      const int nvc = min(KC, len - cc * KC);
+      const size_t t = (size_t)tok0 + (size_t)cc * KC + min(r0, nvc - 1);
 #pragma unroll
-    for (int s = 0; s < SK; ++s) f_kh[s] = ld8(p.kh + (sh * KC + r0) * DK + 32 * s + 8 * lg);
+      for (int s = 0; s < SK; ++s) k_r[s] = in8((const E *)p.k + (t * H + h) * DK + 32 * s + 8 * lg);
+    } else {
+#pragma unroll
+      for (int s = 0; s < SK; ++s) f_kh[s] = ld8(p.kh + (sh * KC + r0) * DK + 32 * s + 8 * lg);
+    }
   };
   auto load_2 = [&](size_t sh) {
     if constexpr (!ADD)
@@ -459,8 +477,14 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int d = 16 * (RB * wave + rb) + lm;
-        f_qt[rb][s] = ld8(p.qtT + (sh * DK + d) * KC + 32 * s + 8 * lg);
-        if (!ADD) f_kt[rb][s] = ld8(p.ktT + (sh * DK + d) * KC + 32 * s + 8 * lg);
+        const size_t o = (sh * DK + d) * KC + 32 * s + 8 * lg;
+        if constexpr (SCAL) {
+          q_t[rb][s] = in8((const E *)p.qT + o);
+          if (!ADD) k_t[rb][s] = in8((const E *)p.kT + o);
+        } else {
+          f_qt[rb][s] = ld8(p.qtT + o);
+          if (!ADD) f_kt[rb][s] = ld8(p.ktT + o);
+        }
       }
   };
   // dO of a chunk, beta and e^{g_C} (no branch around a load: rows past the end read
@@ -469,20 +493,28 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
   // guard when there are fewer pieces than threads, uniform over each wave)
   constexpr int VE = 16 / (int)sizeof(E), NPR = VB / VE, NPO = KC * NPR, PPT = (NPO + 255) / 256;
   u32x4 oraw[PPT];
-  float bnext = 0.f, gnext = 0.f;
+  float onext[SCAL ? PPT : 1];  // SCAL: e^g of each staged dO piece's row
+  float bnext = 0.f, gnext = 0.f, enext = 0.f, tnext = 0.f;
   auto load_o = [&](int cc) {
     const int nvc = min(KC, len - cc * KC);
-    const size_t tbc = (size_t)tok0 + (size_t)cc * KC;
+    const size_t tbc = (size_t)tok0 + (size_t)cc * KC, shc = (size_t)(slot0 + cc) * H + h;
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
       const int pc = tid + 256 * u, r = min(pc / NPR, nvc - 1), g = pc % NPR;
-      if (pc < NPO) oraw[u] = *(const u32x4 *)((const E *)p.dout + ((tbc + r) * H + h) * dv + col0 + VE * g);
+      if (pc < NPO) {
+        oraw[u] = *(const u32x4 *)((const E *)p.dout + ((tbc + r) * H + h) * dv + col0 + VE * g);
+        if constexpr (SCAL) onext[u] = p.egr[shc * KC + r];
+      }
     }
     if (!ADD) bnext = p.beta[(tbc + min(tid % KC, nvc - 1)) * H + h];
-    gnext = p.gam[((size_t)(slot0 + cc) * H + h) * DK + tid % DK];
+    gnext = p.gam[shc * DK + tid % DK];
+    if constexpr (SCAL) {
+      enext = p.egr[shc * KC + tid % KC];
+      tnext = p.etr[shc * KC + tid % KC];
+    }
   };
   if (nchunks > 0) {
-    load_1((size_t)(slot0 + nchunks - 1) * H + h);
+    load_1(nchunks - 1);
     load_o(nchunks - 1);
   }
   for (int c = nchunks - 1; c >= 0; --c) {
@@ -516,10 +548,20 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
           const bf16 hv = (bf16)x;
           dOh[col * PV + r] = hv;
           if constexpr (!VX) dOl[col * PV + r] = (bf16)(x - (float)hv);
+          if constexpr (SCAL) {
+            const float xg = x * onext[u];
+            const bf16 hg = (bf16)xg;
+            dGh[col * PV + r] = hg;
+            dGl[col * PV + r] = (bf16)(xg - (float)hg);
+          }
         }
       }
       if (tid < KC) bsh[tid] = (!ADD && tid < nv) ? bnext : 0.f;
       if (tid < DK) gsh[tid] = gnext;
+      if (SCAL && tid < KC) {
+        egs[tid] = enext;
+        ets[tid] = tnext;
+      }
     }
     __syncthreads();
     load_2(sh);
@@ -537,8 +579,16 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
           if (s >= s0) D[ct] = mm(split8(f_pm[s]), fo[ct][s], D[ct]);
+        if constexpr (SCAL) {
+          f32x4 D2 = zero4();
 #pragma unroll
-        for (int s = 0; s < SK; ++s) D[ct] = mm(split8(f_kh[s]), bfrag(dMh, dMl, PM, ct, 32 * s), D[ct]);
+          for (int s = 0; s < SK; ++s) D2 = mm(k_r[s], bfrag(dMh, dMl, PM, ct, 32 * s), D2);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) D[ct][j] += ets[16 * wave + 4 * lg + j] * D2[j];
+        } else {
+#pragma unroll
+          for (int s = 0; s < SK; ++s) D[ct] = mm(split8(f_kh[s]), bfrag(dMh, dMl, PM, ct, 32 * s), D[ct]);
+        }
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -570,7 +620,7 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
         for (int j = 0; j < 4; ++j) {
           const int r = 16 * wave + 4 * lg + j;
           const float by = bsh[r] * Y[ct][j];
-          nb4[j] = -by;
+          nb4[j] = SCAL ? -by * egs[r] : -by;
           if (r < nv) ((E *)p.dv_out)[((tbase + r) * H + h) * dv + col0 + 16 * ct + lm] = to_e<E>(by);
         }
         put_t(bYh, bYl, PV, 16 * wave, ct, nb4);
@@ -578,7 +628,7 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
       __syncthreads();
     }
     if (c > 0) {
-      load_1(sh - H);
+      load_1(c - 1);
       load_o(c - 1);
     }
     // dM <- diag(gam) dM + Qt^T dO - Kt^T diag(beta) Y
@@ -591,8 +641,13 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
         for (int j = 0; j < 4; ++j) dM[rb][ct][j] *= gsh[d0 + 4 * lg + j];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          dM[rb][ct] = mm(split8(f_qt[rb][s]), fo[ct][s], dM[rb][ct]);
-          if constexpr (!ADD) dM[rb][ct] = mm(split8(f_kt[rb][s]), bfrag(bYh, bYl, PV, ct, 32 * s), dM[rb][ct]);
+          if constexpr (SCAL) {
+            dM[rb][ct] = mm(q_t[rb][s], bfrag(dGh, dGl, PV, ct, 32 * s), dM[rb][ct]);
+            if constexpr (!ADD) dM[rb][ct] = mm(k_t[rb][s], bfrag(bYh, bYl, PV, ct, 32 * s), dM[rb][ct]);
+          } else {
+            dM[rb][ct] = mm(split8(f_qt[rb][s]), fo[ct][s], dM[rb][ct]);
+            if constexpr (!ADD) dM[rb][ct] = mm(split8(f_kt[rb][s]), bfrag(bYh, bYl, PV, ct, 32 * s), dM[rb][ct]);
+          }
         }
       }
     }
@@ -897,17 +952,17 @@ __global__ __launch_bounds__(512, 1) void bwdk_chunk_kernel(BwdKeyParams p) {
 // The reverse pass takes the widest value block (64, 32 or 16 columns) that still gives
 // one workgroup per compute unit: a wider block reads the A operands once for more
 // columns, a narrower one puts more of the chip to work on few long sequences
-template <typename E, int DK, bool ADD>
+template <typename E, int DK, bool ADD, bool SCAL = false>
 void launch_rev(const BwdKeyParams &p, hipStream_t stream) {
   const long pairs = (long)p.N * p.H;
   if (pairs * (p.dv / 64) >= 256)
-    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, 64>), dim3((unsigned)(pairs * (p.dv / 64))), dim3(256), 0,
+    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, 64, SCAL>), dim3((unsigned)(pairs * (p.dv / 64))), dim3(256), 0,
                        stream, p);
   else if (pairs * (p.dv / 32) >= 256)
-    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, 32>), dim3((unsigned)(pairs * (p.dv / 32))), dim3(256), 0,
+    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, 32, SCAL>), dim3((unsigned)(pairs * (p.dv / 32))), dim3(256), 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, 16>), dim3((unsigned)(pairs * (p.dv / 16))), dim3(256), 0,
+    hipLaunchKernelGGL((bwdk_rev_kernel<E, DK, ADD, 16, SCAL>), dim3((unsigned)(pairs * (p.dv / 16))), dim3(256), 0,
                        stream, p);
 }
 
@@ -934,11 +989,12 @@ hipError_t launch_k(const BwdKeyParams &p, bool add, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwdk_rev(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream) {
+  // (the scalar-gate path's reverse pass: the SCAL operands, bf16 with d_k 64 or 128 or
+  // fp32 with d_k 64)
   if (p.N * p.H * (p.dv / KBV) == 0) return hipSuccess;
-  if (dtype == 1 && dk == 128) add ? launch_rev<bf16, 128, true>(p, stream) : launch_rev<bf16, 128, false>(p, stream);
-  else if (dtype == 1 && dk == 64) add ? launch_rev<bf16, 64, true>(p, stream) : launch_rev<bf16, 64, false>(p, stream);
-  else if (dtype == 0 && dk == 128) add ? launch_rev<float, 128, true>(p, stream) : launch_rev<float, 128, false>(p, stream);
-  else if (dtype == 0 && dk == 64) add ? launch_rev<float, 64, true>(p, stream) : launch_rev<float, 64, false>(p, stream);
+  if (dtype == 1 && dk == 128) add ? launch_rev<bf16, 128, true, true>(p, stream) : launch_rev<bf16, 128, false, true>(p, stream);
+  else if (dtype == 1 && dk == 64) add ? launch_rev<bf16, 64, true, true>(p, stream) : launch_rev<bf16, 64, false, true>(p, stream);
+  else if (dtype == 0 && dk == 64) add ? launch_rev<float, 64, true, true>(p, stream) : launch_rev<float, 64, false, true>(p, stream);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

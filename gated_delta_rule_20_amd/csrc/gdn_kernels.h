@@ -77,12 +77,13 @@ struct BwdParams {
                                  // NULL without a gate, read at t * la_stride + h)
   const float *dfinal;           // NULL | [N, H, d_k, d_v]
   const int32_t *cu_seqlens;     // NULL (batch) | [N + 1]
-  // workspace (fp32): chunk-entering states and chunk-end state gradients [slots, H, d_k,
-  // d_v], dDelta [slots, H, 64, d_v], T and T^T (delta write) and P^T [slots, H, 64, 64],
-  // e^{G_C - G} K [slots, H, 64, d_k], (e^G Q)^T and (e^G K)^T (delta write) [slots, H,
-  // d_k, 64], e^{G_C} [slots, H, d_k]
+  // workspace: chunk-entering states and chunk-end state gradients [slots, H, d_k, d_v],
+  // dDelta [slots, H, 64, d_v], T and T^T (delta write) and P^T [slots, H, 64, 64],
+  // e^{G_C} [slots, H, d_k] (fp32); Q^T and K^T (delta write) [slots, H, d_k, 64] in the
+  // I/O dtype; e^G and e^{G_C - G} per row [slots, H, 64] (fp32, 0 past the sequence end)
   const float *states;
-  float *dmc, *dd, *tm, *tmT, *pmT, *kh, *qtT, *ktT, *gam;
+  float *dmc, *dd, *tm, *tmT, *pmT, *gam, *egr, *etr;
+  void *qT, *kT;
   void *dq, *dk, *dv_out;        // outputs, I/O dtype
   float *dbeta, *dlog_alpha;     // [tokens, H]; dbeta NULL for the additive write, dlog_alpha
                                  // NULL without a gate (per token also for a constant decay)
@@ -111,6 +112,10 @@ struct BwdKeyParams {
   // K e^G and K e^{g_C - G} [S, H, 64, d_k], their transposes and (Q e^G)^T [S, H, d_k, 64],
   // e^{g_C} [S, H, d_k]
   float *states, *dmc, *dd, *tm, *tmT, *pmT, *kt, *kh, *ktT, *qtT, *khT, *gam;
+  // the scalar gates' reverse pass (launch_bwdk_rev) reads instead of kh, qtT and ktT:
+  // Q^T and K^T [S, H, d_k, 64] (I/O dtype), e^G and e^{G_C - G} per row [S, H, 64]
+  const void *qT, *kT;
+  const float *egr, *etr;
   void *dq, *dk, *dv_out;        // outputs, I/O dtype
   float *dbeta;                  // [tokens, H]; NULL for the additive write
   float *dlog_alpha;             // [tokens, H, d_k]
@@ -120,8 +125,8 @@ struct BwdKeyParams {
   int states_ready;              // the chunk-entering states are already in `states`
 };
 hipError_t launch_bwd_key(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream);
-// the reverse state pass alone (chunk-end state gradients, dDelta, dV, initial-state
-// gradient), from operands already in the workspace; also the scalar-gate path's
+// the scalar gates' reverse state pass (chunk-end state gradients, dDelta, dV, initial-
+// state gradient) from P^T, T^T, Q^T, K^T and the row factors already in the workspace
 hipError_t launch_bwdk_rev(const BwdKeyParams &p, int dtype, int dk, bool add, hipStream_t stream);
 
 // Forward of the diagonal-plus-low-rank transition (no gate or the scalar gate).

@@ -326,19 +326,20 @@ def test_bwd_host_validation(g, change, status):
 def test_bwd_workspace_size(g):
     """The scalar gates' backward workspace: with S = floor(B T / 64) + N chunk slots,
     fp32 chunk states and chunk-end state gradients (d_k d_v per slot and head), dDelta
-    (64 d_v), T and T^T (delta write), P^T (64 x 64 each), e^{g_C - g} K (64 d_k), the
-    transposes of e^g K (delta write) and e^g Q (d_k 64 each) and e^{g_C} (d_k), each
-    rounded up to 256 bytes; the constant gate adds the per-token decay gradients."""
+    (64 d_v), T and T^T (delta write), P^T (64 x 64 each), e^g and e^{g_C - g} per row
+    (2 x 64), K^T (delta write) and Q^T in the I/O dtype (d_k 64 each) and e^{g_C} (d_k),
+    each rounded up to 256 bytes; the constant gate adds the per-token decay gradients."""
     up = lambda x: (x + 255) // 256 * 256
     a = bwd_args(g)
     sh = ((2 * 128) // 64 + 2) * 4
     dk = dv = 128
-    delta = [sh * dk * dv * 4] * 2 + [sh * 64 * dv * 4] + [sh * 4096 * 4] * 3 + [sh * 64 * dk * 4] * 3 + [sh * dk * 4]
+    rows, qkt = sh * 128 * 4, sh * dk * 64 * 2  # e^g and e^{g_C - g} rows; bf16 Q^T / K^T
+    delta = [sh * dk * dv * 4] * 2 + [sh * 64 * dv * 4] + [sh * 4096 * 4] * 3 + [rows, qkt, qkt] + [sh * dk * 4]
     expect = sum(up(x) for x in delta)
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(a)) == expect
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(bwd_args(g, dq=None))) == 0
     add = bwd_args(g, write=1, beta=None, dbeta=None)
-    add_sizes = [sh * dk * dv * 4] * 2 + [sh * 64 * dv * 4] + [sh * 4096 * 4] + [sh * 64 * dk * 4] * 2 + [sh * dk * 4]
+    add_sizes = [sh * dk * dv * 4] * 2 + [sh * 64 * dv * 4] + [sh * 4096 * 4] + [rows, qkt] + [sh * dk * 4]
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(add)) == sum(up(x) for x in add_sizes)
     const = bwd_args(g, gate=3)
     assert g._lib.gdn_bwd_workspace_size(ctypes.byref(const)) == expect + up(2 * 128 * 4 * 4)
