@@ -251,10 +251,12 @@ typedef struct {
  * with S = floor(B T / 64) + N chunk slots, each part rounded up to 256 bytes:
  *  - every gate, per slot and head in fp32: the chunk-entering states and chunk-end
  *    state gradients (d_k d_v each), dDelta (64 d_v), T and T^T (delta write) and P^T
- *    (64 x 64 each), K e^{g_C - G} (64 d_k), (K e^G)^T (delta write) and (Q e^G)^T
- *    (d_k 64 each), e^{g_C} (d_k);
- *  - one decay per key channel adds K e^G (delta write) and (K e^{g_C - G})^T (64 d_k
- *    each per slot and head);
+ *    (64 x 64 each), e^{g_C} (d_k);
+ *  - no gate or a scalar gate adds Q^T and K^T (delta write) in the I/O dtype (d_k 64
+ *    elements each) and e^g, e^{g_C - g} per row (2 x 64 fp32);
+ *  - one decay per key channel adds instead K e^G (delta write), K e^{g_C - G} (64 d_k
+ *    each), their transposes and (Q e^G)^T (d_k 64 each; K e^G's transpose for the
+ *    delta write only), fp32;
  *  - one constant decay per head adds the per-token decay gradients (4 bytes per token
  *    and head).
  * Owned by the caller; no initialisation needed. */
