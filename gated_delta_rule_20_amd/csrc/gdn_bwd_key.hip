@@ -217,8 +217,10 @@ __global__ __launch_bounds__(PNT, 1) void bwdk_prep_kernel(BwdKeyParams p) {
       *(f32x4 *)(p.ktT + sh * DK * KC + i) = a0;
       *(f32x4 *)(p.ktT + sh * DK * KC + i + 4) = a1;
     }
-    *(f32x4 *)(p.khT + sh * DK * KC + i) = b0;
-    *(f32x4 *)(p.khT + sh * DK * KC + i + 4) = b1;
+    if (!p.states_ready) {  // read only by the chunk-state kernel (bwdk_fwd_kernel)
+      *(f32x4 *)(p.khT + sh * DK * KC + i) = b0;
+      *(f32x4 *)(p.khT + sh * DK * KC + i + 4) = b1;
+    }
     *(f32x4 *)(p.qtT + sh * DK * KC + i) = c0;
     *(f32x4 *)(p.qtT + sh * DK * KC + i + 4) = c1;
   }
