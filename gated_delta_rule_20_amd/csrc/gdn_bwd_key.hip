@@ -30,8 +30,10 @@
 //     Kt^T, Qt^T, Kh^T (channel-major), gam, T and T^T (delta write), P^T;
 //  2. bwdk_fwd_kernel, one workgroup per (sequence, head, 32 value columns), chunks in
 //     order: the chunk-entering states;
-//  3. bwdk_rev_kernel, the same grid, chunks in reverse: the chunk-end state gradient dM
-//     and dDelta of every chunk, dV, and the initial-state gradient;
+//  3. bwdk_rev_kernel, one workgroup per (sequence, head, value block of 64, 32 or 16
+//     columns, the widest that fills the chip), chunks in reverse: the chunk-end state
+//     gradient dM and dDelta of every chunk, dV, and the initial-state gradient (also the
+//     scalar gates' reverse pass, in its SCAL form);
 //  4. bwdk_chunk_kernel, one workgroup per (chunk, head), fully parallel: everything
 //     else (dq, dk, dbeta, dlog alpha).
 // Products run on the bf16 matrix cores with every fp32 operand split into hi + lo bf16
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(256, 1) void bwdk_fwd_kernel(BwdKeyParams p) {
 
 // ---------------------------------------------------------------- 3. reverse state pass
 // The gradient dM of the chunk-end state stays in the matrix-core accumulators of the
-// four waves (d_k / 4 key rows each, 32 value columns) for the whole sequence.  Per
+// four waves (d_k / 4 key rows each, VB value columns) for the whole sequence.  Per
 // chunk (in reverse): dDelta = P^T dO + Kh dM, Y = T^T dDelta, dV = diag(beta) Y,
 // dM <- diag(gam) dM + Qt^T dO - Kt^T diag(beta) Y.  The B operands (dM, dO, dDelta,
 // -diag(beta) Y) are staged once per chunk in LDS, transposed and split into hi and lo

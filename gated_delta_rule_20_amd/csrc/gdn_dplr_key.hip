@@ -24,8 +24,8 @@
 //     and a lo bf16 half (row-major, so that a matrix-core A fragment is two 16-byte
 //     loads and needs no arithmetic): T, A_ak, P_qb, P_qk (64 x 64), A e^{Gp} and
 //     Q e^G (64 x d_k), (B e^{G_C - G})^T and (K e^{G_C - G})^T (d_k x 64); e^{G_C} in fp32.
-//  2. dplrk_state_kernel, one workgroup per (sequence, head, 32 value columns), chunks
-//     in order.  The fp32 state block stays in the matrix-core accumulators of its four
+//  2. dplrk_state_kernel, one workgroup per (sequence, head, 64 or 32 value columns: 64
+//     when that still gives one workgroup per compute unit), chunks in order.  The fp32 state block stays in the matrix-core accumulators of its four
 //     waves (d_k / 4 key rows each) for the whole sequence; its split bf16 copy, V, R
 //     and U sit transposed in LDS so that every B fragment is two 16-byte reads.
 // Products run on the bf16 matrix cores with every fp32 operand a hi + lo pair (about

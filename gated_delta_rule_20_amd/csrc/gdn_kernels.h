@@ -142,7 +142,7 @@ struct DplrParams {
 hipError_t launch_dplr(const DplrParams &p, int dtype, int dk, int gate, hipStream_t stream);
 // The same transition with one decay per key channel: a parallel preparation per
 // (chunk, head) into the fp32 workspace arrays below (slot of chunk c as for key_slots),
-// then one serial pass per (sequence, head, 32 value columns).
+// then one serial pass per (sequence, head, 64 or 32 value columns).
 struct DplrKeyParams {
   const void *q, *k, *v, *a, *b;  // [tokens, H, d_k] (v: d_v), I/O dtype
   const float *log_alpha;         // [tokens, H, d_k]
