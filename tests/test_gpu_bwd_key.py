@@ -125,6 +125,27 @@ def test_bwd_key_deterministic(gdn):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("write", ["delta", "add"])
+def test_bwd_key_windowed_states_ragged(gdn, write):
+    """Batch sequences of 71 chunks with a ragged last chunk (T = 64 * 70 + 29): the
+    chunk states are recomputed in three windows of 32, 32 and 7 chunks, the state
+    carried between them; two (sequence, head) pairs against the oracle in full."""
+    inp = synth.random_inputs(2, 64 * 70 + 29, 2, 128, 128, "key", "bf16", seed=77, state_std=0.05)
+    inp["write"] = write
+    if write == "add":
+        inp["beta"] = None
+    dout, dfs = grads_inputs(inp, 23)
+    got = run_gpu(gdn, inp, dout, dfs)
+    for n, h in [(0, 1), (1, 0)]:
+        sl = lambda x: None if x is None else x[n:n + 1, :, h:h + 1].contiguous()
+        ref = oracle.bwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["log_alpha"]),
+                         inp["initial_state"][n:n + 1, h:h + 1], sl(dout), dfs[n:n + 1, h:h + 1], write=write,
+                         nthreads=1)
+        part = [None if g_ is None else (g_[n:n + 1, h:h + 1] if i == 5 else g_[n:n + 1, :, h:h + 1])
+                for i, g_ in enumerate(got)]
+        compare(part, ref, TOL["bf16"])
+
+
 @pytest.mark.parametrize("name,pairs", [("kda-bf16-B2-T16384-H16-d128", [(0, 0), (1, 15)]),
                                         ("gla-bf16-B2-T16384-H16-d128", [(1, 3)])])
 def test_bwd_key_long_workload(gdn, name, pairs):
