@@ -111,6 +111,16 @@ def test_constant_decay_gradient_without_tokens(gdn):
     assert torch.equal(got[5], dfs)
 
 
+@pytest.mark.parametrize("B,H,dv,width", [(2, 2, 128, 16), (16, 8, 64, 32), (32, 8, 128, 64)])
+def test_additive_bwd_reverse_pass_widths(gdn, B, H, dv, width):
+    """The additive write at each value-block width of the reverse pass (the widest of
+    64, 32 or 16 columns that gives N H d_v / width >= 256 workgroups, else 16)."""
+    pairs = B * H
+    assert (pairs * dv // 64 >= 256) == (width == 64)
+    assert (pairs * dv // 64 < 256 <= pairs * dv // 32) == (width == 32)
+    check(gdn, inputs(B, 130, H, 128, dv, "head", "bf16", seed=width + 1, write="add"), seed=width)
+
+
 def test_retnet_backward_full_size(gdn):
     """The RetNet workload (B16, T2048, H8, d128, fixed decays, additive write)."""
     check(gdn, synth.workload_inputs("retnet-bf16-B16-T2048-H8-d128"), seed=13)
