@@ -401,6 +401,23 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
   __shared__ __align__(16) bf16 bYh[VB * PV];
   __shared__ __align__(16) bf16 bYl[VB * PV];
   __shared__ float bsh[KC], gsh[DK];
+  // Staged A operands (the additive write with the per-key-channel gate at 16 value
+  // columns): the next chunk's P^T, Kh and Qt^T are fetched into registers at the top of
+  // a chunk, a whole chunk ahead of their use, and written to LDS at the top of the next;
+  // the fragments are then read from LDS.  Fetched one phase ahead instead (the other
+  // path), their latency is exposed between the short products of a 16-column block
+  // (3.37 -> 3.20 ms for the whole backward of B=2, T=16384, H=16, d=128).  With the
+  // delta write the same staging measured no faster: there the 128 KB of operands per
+  // chunk and workgroup bound the pass, not their latency.  Each operand is rows of
+  // 16-byte pieces with piece c of row r stored at c ^ (r & 15), so a fragment read by
+  // 16 lanes of 16 rows touches 16 bank groups.
+  constexpr int O_TM = KC * KC / 4, O_KH = O_TM + (ADD ? 0 : KC * KC / 4), O_QT = O_KH + KC * DK / 4;
+  constexpr int O_KT = O_QT + DK * KC / 4, N_PC = O_KT + (ADD ? 0 : DK * KC / 4);  // piece offsets
+  constexpr int BASE_LDS = (2 * (SCAL ? VB * PV : 8) + 2 * VB * PM + 6 * VB * PV) * 2 + (3 * KC + DK) * 4 + 256;
+  constexpr bool STG = !SCAL && ADD && VB == 16;
+  static_assert(!STG || BASE_LDS + 16 * N_PC <= 160 * 1024, "LDS budget of the staged operands");
+  static_assert(N_PC % 256 == 0 && O_KH % 256 == 0 && O_QT % 256 == 0 && O_KT % 256 == 0, "whole steps per operand");
+  __shared__ __align__(16) float stg[STG ? 4 * N_PC : 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, lm = lane & 15;
   const int H = p.H, dv = p.dv, nb = dv / VB;
@@ -491,6 +508,50 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
         }
       }
   };
+  // the staged path: step u of a thread covers pieces 256 u .. 256 u + 255 of the
+  // concatenated operands (each operand holds whole steps), the thread's piece is
+  // 256 u + tid; kh rows hold DK / 4 pieces, the others 16
+  constexpr int NPC = STG ? N_PC / 256 : 1;
+  u32x4 pre[NPC];
+  auto stg_fetch = [&](int cc) {
+    const size_t sh = (size_t)(slot0 + cc) * H + h;
+#pragma unroll
+    for (int u = 0; u < NPC; ++u) {
+      const int i = 256 * u, o = i < O_TM ? 0 : i < O_KH ? O_TM : i < O_QT ? O_KH : i < O_KT ? O_QT : O_KT;
+      const float *src = i < O_TM   ? p.pmT + sh * KC * KC
+                         : i < O_KH ? p.tmT + sh * KC * KC
+                         : i < O_QT ? p.kh + sh * KC * DK
+                         : i < O_KT ? p.qtT + sh * DK * KC
+                                    : p.ktT + sh * DK * KC;
+      pre[u] = *(const u32x4 *)(src + 4 * (i - o + tid));
+    }
+  };
+  auto stg_put = [&]() {
+#pragma unroll
+    for (int u = 0; u < NPC; ++u) {
+      const int i = 256 * u, o = i < O_TM ? 0 : i < O_KH ? O_TM : i < O_QT ? O_KH : i < O_KT ? O_QT : O_KT;
+      const int rp = (i >= O_KH && i < O_QT) ? DK / 4 : 16, q = i - o + tid, r = q / rp, c = q % rp;
+      *(u32x4 *)(stg + 4 * (o + r * rp + (c ^ (r & 15)))) = pre[u];
+    }
+  };
+  // the 8 floats at columns col .. col + 7 (col a multiple of 8) of row r of the staged
+  // operand at piece offset o with rp pieces per row
+  auto sfr = [&](int o, int rp, int r, int col) {
+    const int c = col >> 2, x = r & 15;
+    const f32x4 a = *(const f32x4 *)(stg + 4 * (o + r * rp + (c ^ x)));
+    const f32x4 b = *(const f32x4 *)(stg + 4 * (o + r * rp + ((c + 1) ^ x)));
+    return (f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  };
+  // the A fragments, from LDS (staged) or from the registers loaded a phase ahead
+  auto A_pm = [&](int s) { return STG ? sfr(0, 16, r0, 32 * s + 8 * lg) : f_pm[s]; };
+  auto A_kh = [&](int s) { return STG ? sfr(O_KH, DK / 4, r0, 32 * s + 8 * lg) : f_kh[SCAL ? 0 : s]; };
+  auto A_tm = [&](int s) { return STG ? sfr(O_TM, 16, r0, 32 * s + 8 * lg) : f_tm[s]; };
+  auto A_qt = [&](int rb, int s) {
+    return STG ? sfr(O_QT, 16, 16 * (RB * wave + rb) + lm, 32 * s + 8 * lg) : f_qt[SCAL ? 0 : rb][s];
+  };
+  auto A_kt = [&](int rb, int s) {
+    return STG ? sfr(O_KT, 16, 16 * (RB * wave + rb) + lm, 32 * s + 8 * lg) : f_kt[SCAL ? 0 : rb][s];
+  };
   // dO of a chunk, beta and e^{g_C} (no branch around a load: rows past the end read
   // the last row and are zeroed when staged)
   // 16-byte pieces of a chunk's dO slice: NPR per row, PPT per thread (a thread-count
@@ -518,13 +579,15 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
     }
   };
   if (nchunks > 0) {
-    load_1(nchunks - 1);
+    if constexpr (STG) stg_fetch(nchunks - 1);
+    else load_1(nchunks - 1);
     load_o(nchunks - 1);
   }
   for (int c = nchunks - 1; c >= 0; --c) {
     const size_t sh = (size_t)(slot0 + c) * H + h;
     const int nv = min(KC, len - c * KC);
     const size_t tbase = (size_t)tok0 + (size_t)c * KC;
+    if constexpr (STG) stg_put();  // every read of the last chunk's operands is done
     // the chunk-end gradient: to the workspace and, split, to LDS
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -567,8 +630,12 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
         ets[tid] = tnext;
       }
     }
+    if (STG && c > 0) {  // the next chunk's operands, in flight for a whole chunk
+      stg_fetch(c - 1);
+      load_o(c - 1);
+    }
     __syncthreads();
-    load_2(sh);
+    if constexpr (!STG) load_2(sh);
     OF fo[NCT][2];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -582,7 +649,7 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
         D[ct] = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          if (s >= s0) D[ct] = mm(split8(f_pm[s]), fo[ct][s], D[ct]);
+          if (s >= s0) D[ct] = mm(split8(A_pm(s)), fo[ct][s], D[ct]);
         if constexpr (SCAL) {
           f32x4 D2 = zero4();
 #pragma unroll
@@ -591,7 +658,7 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
           for (int j = 0; j < 4; ++j) D[ct][j] += ets[16 * wave + 4 * lg + j] * D2[j];
         } else {
 #pragma unroll
-          for (int s = 0; s < SK; ++s) D[ct] = mm(split8(f_kh[s]), bfrag(dMh, dMl, PM, ct, 32 * s), D[ct]);
+          for (int s = 0; s < SK; ++s) D[ct] = mm(split8(A_kh(s)), bfrag(dMh, dMl, PM, ct, 32 * s), D[ct]);
         }
       }
 #pragma unroll
@@ -606,7 +673,7 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
       }
     }
     __syncthreads();
-    load_3(sh);
+    if constexpr (!STG) load_3(sh);
     if constexpr (!ADD) {
       // Y = T^T dDelta;  dV = diag(beta) Y;  -diag(beta) Y into LDS for the dM update
       f32x4 Y[NCT];
@@ -615,7 +682,7 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
         Y[ct] = zero4();
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          if (s >= s0) Y[ct] = mm(split8(f_tm[s]), bfrag(dDh, dDl, PV, ct, 32 * s), Y[ct]);
+          if (s >= s0) Y[ct] = mm(split8(A_tm(s)), bfrag(dDh, dDl, PV, ct, 32 * s), Y[ct]);
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -631,7 +698,7 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
       }
       __syncthreads();
     }
-    if (c > 0) {
+    if (!STG && c > 0) {
       load_1(c - 1);
       load_o(c - 1);
     }
@@ -649,8 +716,8 @@ __global__ __launch_bounds__(256, 1) void bwdk_rev_kernel(BwdKeyParams p) {
             dM[rb][ct] = mm(q_t[rb][s], bfrag(dGh, dGl, PV, ct, 32 * s), dM[rb][ct]);
             if constexpr (!ADD) dM[rb][ct] = mm(k_t[rb][s], bfrag(bYh, bYl, PV, ct, 32 * s), dM[rb][ct]);
           } else {
-            dM[rb][ct] = mm(split8(f_qt[rb][s]), fo[ct][s], dM[rb][ct]);
-            if constexpr (!ADD) dM[rb][ct] = mm(split8(f_kt[rb][s]), bfrag(bYh, bYl, PV, ct, 32 * s), dM[rb][ct]);
+            dM[rb][ct] = mm(split8(A_qt(rb, s)), fo[ct][s], dM[rb][ct]);
+            if constexpr (!ADD) dM[rb][ct] = mm(split8(A_kt(rb, s)), bfrag(bYh, bYl, PV, ct, 32 * s), dM[rb][ct]);
           }
         }
       }

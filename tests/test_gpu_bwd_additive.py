@@ -112,13 +112,15 @@ def test_constant_decay_gradient_without_tokens(gdn):
 
 
 @pytest.mark.parametrize("B,H,dv,width", [(2, 2, 128, 16), (16, 8, 64, 32), (32, 8, 128, 64)])
-def test_additive_bwd_reverse_pass_widths(gdn, B, H, dv, width):
+@pytest.mark.parametrize("gate", ["head", "key"])
+def test_additive_bwd_reverse_pass_widths(gdn, B, H, dv, width, gate):
     """The additive write at each value-block width of the reverse pass (the widest of
-    64, 32 or 16 columns that gives N H d_v / width >= 256 workgroups, else 16)."""
+    64, 32 or 16 columns that gives N H d_v / width >= 256 workgroups, else 16); with one
+    decay per key channel the 16-column block reads its operands through LDS staging."""
     pairs = B * H
     assert (pairs * dv // 64 >= 256) == (width == 64)
     assert (pairs * dv // 64 < 256 <= pairs * dv // 32) == (width == 32)
-    check(gdn, inputs(B, 130, H, 128, dv, "head", "bf16", seed=width + 1, write="add"), seed=width)
+    check(gdn, inputs(B, 130, H, 128, dv, gate, "bf16", seed=width + 1, write="add"), seed=width)
 
 
 def test_retnet_backward_full_size(gdn):
