@@ -601,6 +601,8 @@ def main():
         # (no CPU line: the oracle's reverse sweep keeps 2 GB of states per sequence and head here)
         extra.append(time_bwd(gdn, "kda-bf16-B2-T16384-H16-d128", steps=5))
         torch.cuda.empty_cache()
+        extra.append(time_bwd(gdn, "gla-bf16-B2-T16384-H16-d128", steps=5))
+        torch.cuda.empty_cache()
         for e in extra:
             print(json.dumps(e), file=sys.stderr)
     print(json.dumps(line))
