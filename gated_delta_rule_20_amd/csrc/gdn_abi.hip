@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
 #include <mutex>
 
 #include "gdn.h"
@@ -94,13 +96,23 @@ bool use_pipe(const gdn_fwd_args *a) { return a->dtype == GDN_BF16 && a->d_k == 
 // The per-key-channel gate on the pipelined kernel: a first pass prepares every
 // chunk's operands in the workspace.
 bool key_pipe(const gdn_fwd_args *a) { return a->gate == GDN_GATE_KEY && use_pipe(a); }
-// Chunks per window of the windowed per-key-channel forward: long batch-mode sequences
-// run as consecutive windows, each launch preparing the next window's operands on the
-// CUs that the state pass of the current one leaves free.
-constexpr int KEY_WINDOW = 32;
-int key_windows(const gdn_fwd_args *a) {
+// The windowed per-key-channel forward: long batch-mode sequences run as consecutive
+// windows of chunks, each launch preparing the next window's operands (N H items per
+// chunk, one item at a time per CU) on the CUs that the state pass of the current one
+// leaves free.  A window is the shortest of at least 16 chunks whose items fill whole
+// rounds of those CUs (as nearly as whole chunks allow): a last, partial round would
+// leave the state pass waiting for a few CUs.  At N = 2, H = 16, d_v = 128 (192 free
+// CUs, 6 chunks per round) that is 18 chunks: 0.64 ms per forward call, against 0.66
+// at 24 chunks, 0.69 at 20 and 0.78 at 32.
+constexpr int KEY_WINDOW_MIN = 16;
+int key_window_len(const gdn_fwd_args *a, int free_cus) {
+  const double per_round = (double)free_cus / ((double)a->N * a->H);  // chunks per round
+  const double rounds = std::ceil(KEY_WINDOW_MIN / per_round);
+  return std::max(KEY_WINDOW_MIN, (int)std::floor(rounds * per_round));
+}
+int key_windows(const gdn_fwd_args *a, int len) {
   const int nchunks = (a->T + 63) / 64;
-  return (!a->cu_seqlens && nchunks >= 2 * KEY_WINDOW) ? (nchunks + KEY_WINDOW - 1) / KEY_WINDOW : 1;
+  return (!a->cu_seqlens && nchunks >= 2 * len) ? (nchunks + len - 1) / len : 1;
 }
 struct KeyLayout {
   long slots;
@@ -116,7 +128,8 @@ KeyLayout key_layout(const gdn_fwd_args *a) {
   L.kq = align256((size_t)tokens * a->H * 128 * 2);
   L.tp = align256((size_t)L.slots * a->H * 16384);
   L.eg = align256((size_t)L.slots * a->H * 128 * 4);
-  if (key_windows(a) > 1) L.carry = align256((size_t)a->N * a->H * 128 * a->d_v * 4);
+  if (key_windows(a, KEY_WINDOW_MIN) > 1)  // every window length is at least the minimum
+    L.carry = align256((size_t)a->N * a->H * 128 * a->d_v * 4);
   return L;
 }
 
@@ -392,11 +405,13 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
       pp.H = a->H;
       pp.T = a->T;
       const bool add = a->write == GDN_WRITE_ADD;
-      const int windows = key_windows(&f), ns = a->N * a->H * (a->d_v / 64), free_cus = gdn::device_cus() - ns;
-      const bool windowed = windows > 1 && free_cus > 0;
+      const int ns = a->N * a->H * (a->d_v / 64), free_cus = gdn::device_cus() - ns;
+      const int wlen = free_cus > 0 ? key_window_len(&f, free_cus) : 0;
+      const int windows = free_cus > 0 ? key_windows(&f, wlen) : 1;
+      const bool windowed = windows > 1;
       if (windowed) {  // this launch prepares window 0 only
         pp.c_lo = 0;
-        pp.c_hi = KEY_WINDOW;
+        pp.c_hi = wlen;
         pp.win_items = 1;
       }
       if (gdn::launch_key_prep(pp, FL.slots, add, stream) != hipSuccess) return GDN_ERR_HIP;
@@ -426,12 +441,12 @@ int gdn_bwd_chunked(const gdn_bwd_args *a, void *hip_stream) {
         // preparation
         float *carry = (float *)(fw + 3 * FL.kq + FL.tp + FL.eg);
         for (int w = 0; w < windows; ++w) {
-          fp.c_lo = w * KEY_WINDOW;
-          fp.c_hi = (w + 1) * KEY_WINDOW;
+          fp.c_lo = w * wlen;
+          fp.c_hi = (w + 1) * wlen;
           fp.init_state = w == 0 ? a->initial_state : carry;
           fp.final_state = w == windows - 1 ? nullptr : carry;
-          pp.c_lo = (w + 1) * KEY_WINDOW;
-          pp.c_hi = (w + 2) * KEY_WINDOW;
+          pp.c_lo = (w + 1) * wlen;
+          pp.c_hi = (w + 2) * wlen;
           if (gdn::launch_key_window(fp, pp, FL.slots, w + 1 < windows ? free_cus : 0, add, stream) != hipSuccess)
             return GDN_ERR_HIP;
         }
@@ -639,22 +654,24 @@ int fwd_chunked_launch(const gdn_fwd_args *a, void *ws_base, void *hip_stream) {
     p.tp_img = kp.tp_img;
     p.egc = kp.egc;
     const bool add = a->write == GDN_WRITE_ADD;
-    const int windows = key_windows(a), ns = a->N * a->H * (a->d_v / 64), free_cus = gdn::device_cus() - ns;
-    if (windows > 1 && free_cus > 0) {
+    const int ns = a->N * a->H * (a->d_v / 64), free_cus = gdn::device_cus() - ns;
+    const int wlen = free_cus > 0 ? key_window_len(a, free_cus) : 0;
+    const int windows = free_cus > 0 ? key_windows(a, wlen) : 1;
+    if (windows > 1) {
       // window w's state pass shares a launch with window w + 1's preparation
       float *carry = (float *)(ws + 3 * L.kq + L.tp + L.eg);
       p.nb = a->d_v / 64;
       kp.c_lo = 0;
-      kp.c_hi = KEY_WINDOW;
+      kp.c_hi = wlen;
       kp.win_items = 1;
       if (gdn::launch_key_prep(kp, L.slots, add, stream) != hipSuccess) return GDN_ERR_HIP;
       for (int w = 0; w < windows; ++w) {
-        p.c_lo = w * KEY_WINDOW;
-        p.c_hi = (w + 1) * KEY_WINDOW;
+        p.c_lo = w * wlen;
+        p.c_hi = (w + 1) * wlen;
         p.init_state = w == 0 ? a->initial_state : carry;
         p.final_state = w == windows - 1 ? a->final_state : carry;
-        kp.c_lo = (w + 1) * KEY_WINDOW;
-        kp.c_hi = (w + 2) * KEY_WINDOW;
+        kp.c_lo = (w + 1) * wlen;
+        kp.c_hi = (w + 2) * wlen;
         if (gdn::launch_key_window(p, kp, L.slots, w + 1 < windows ? free_cus : 0, add, stream) != hipSuccess)
           return GDN_ERR_HIP;
       }

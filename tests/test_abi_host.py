@@ -140,6 +140,13 @@ def test_workspace_size_key_gate(g):
     assert g.fwd_workspace_size(a) == expect(300, 1, 3)
     a = base_args(g, gate=g.GDN_GATE_KEY, B=1, T=1000, N=7, cu_seqlens=fake(7))
     assert g.fwd_workspace_size(a) == expect(1000, 4, 7, order=256)
+    # batch sequences of at least 32 chunks (two windows of the shortest window length)
+    # may run windowed: the state carried between windows adds N H 128 d_v fp32
+    carry = (2 * 4 * 128 * 128 * 4 + 255) // 256 * 256
+    a = base_args(g, gate=g.GDN_GATE_KEY, T=64 * 31 + 1)
+    assert g.fwd_workspace_size(a) == expect(2 * (64 * 31 + 1), 4, 2) + carry
+    a = base_args(g, gate=g.GDN_GATE_KEY, T=64 * 31)
+    assert g.fwd_workspace_size(a) == expect(2 * 64 * 31, 4, 2)
     # the other modes that take the per-key-channel gate need no prepared operands
     assert g.fwd_workspace_size(base_args(g, gate=g.GDN_GATE_KEY, d_k=64)) == 0
     # and the pass needs that workspace: without it the call is rejected, nothing launched

@@ -33,6 +33,22 @@ def relerr(x, ref):
     return float(np.abs(x - ref).max() / (den if den > 0 else 1.0))
 
 
+def key_window_plan(N, H, dv, T):
+    """Window lengths of the windowed per-key-channel path on this GPU: the shortest
+    window of at least 16 chunks whose N H preparation items per chunk fill whole rounds
+    of the CUs the state pass leaves free (batch mode, at least two windows)."""
+    import math
+    free = torch.cuda.get_device_properties(0).multi_processor_count - N * H * (dv // 64)
+    nchunks = (T + 63) // 64
+    if free <= 0:
+        return []
+    per_round = free / (N * H)
+    wlen = max(16, int(math.floor(math.ceil(16 / per_round) * per_round)))
+    if nchunks < 2 * wlen:
+        return []
+    return [min(wlen, nchunks - w * wlen) for w in range((nchunks + wlen - 1) // wlen)]
+
+
 def inputs(B, T, H, dk, dv, dtype, seed, write="delta", state=True, lengths=None):
     inp = synth.random_inputs(B, T, H, dk, dv, "key", dtype, seed=seed, state_std=0.05 if state else None,
                               lengths=lengths)
@@ -127,16 +143,19 @@ def test_bwd_key_deterministic(gdn):
 
 @pytest.mark.parametrize("write", ["delta", "add"])
 def test_bwd_key_windowed_states_ragged(gdn, write):
-    """Batch sequences of 71 chunks with a ragged last chunk (T = 64 * 70 + 29): the
-    chunk states are recomputed in three windows of 32, 32 and 7 chunks, the state
-    carried between them; two (sequence, head) pairs against the oracle in full."""
-    inp = synth.random_inputs(2, 64 * 70 + 29, 2, 128, 128, "key", "bf16", seed=77, state_std=0.05)
+    """Batch sequences of 45 chunks with a ragged last chunk (T = 64 * 44 + 29) at N = 2,
+    H = 16: the chunk states are recomputed in windows (18, 18 and 9 chunks on 256 CUs),
+    the state carried between them; two (sequence, head) pairs against the oracle in full."""
+    T = 64 * 44 + 29
+    plan = key_window_plan(2, 16, 128, T)
+    assert len(plan) >= 3 and plan[-1] < plan[0], plan
+    inp = synth.random_inputs(2, T, 16, 128, 128, "key", "bf16", seed=77, state_std=0.05)
     inp["write"] = write
     if write == "add":
         inp["beta"] = None
     dout, dfs = grads_inputs(inp, 23)
     got = run_gpu(gdn, inp, dout, dfs)
-    for n, h in [(0, 1), (1, 0)]:
+    for n, h in [(0, 1), (1, 14)]:
         sl = lambda x: None if x is None else x[n:n + 1, :, h:h + 1].contiguous()
         ref = oracle.bwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["log_alpha"]),
                          inp["initial_state"][n:n + 1, h:h + 1], sl(dout), dfs[n:n + 1, h:h + 1], write=write,

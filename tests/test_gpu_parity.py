@@ -29,6 +29,22 @@ def relerr(x, ref):
     return float(np.abs(x - ref).max() / (den if den > 0 else 1.0))
 
 
+def key_window_plan(N, H, dv, T):
+    """Window lengths of the windowed per-key-channel path on this GPU: the shortest
+    window of at least 16 chunks whose N H preparation items per chunk fill whole rounds
+    of the CUs the state pass leaves free (batch mode, at least two windows)."""
+    import math
+    free = torch.cuda.get_device_properties(0).multi_processor_count - N * H * (dv // 64)
+    nchunks = (T + 63) // 64
+    if free <= 0:
+        return []
+    per_round = free / (N * H)
+    wlen = max(16, int(math.floor(math.ceil(16 / per_round) * per_round)))
+    if nchunks < 2 * wlen:
+        return []
+    return [min(wlen, nchunks - w * wlen) for w in range((nchunks + wlen - 1) // wlen)]
+
+
 def to_dev(inp):
     return {k: (v.cuda() if hasattr(v, "cuda") else v) for k, v in inp.items()}
 
@@ -227,12 +243,15 @@ def test_workload_kda_long(gdn):
 @pytest.mark.parametrize("write", ["delta", "add"])
 @pytest.mark.parametrize("dv", [64, 128])
 def test_key_gate_windows(gdn, write, dv):
-    """Long batch sequences with one decay per key channel run as windows of 32 chunks
-    (the state carried between launches).  65 chunks and a ragged tail give three
-    windows, the last of one partial chunk.  Against the oracle, and bit for bit against
-    the same sequences packed (a packed call runs without windows)."""
-    T = 64 * 64 + 37
-    inp = synth.random_inputs(2, T, 2, 128, dv, "key", "bf16", seed=61 + dv, state_std=0.05)
+    """Long batch sequences with one decay per key channel run as windows of chunks (the
+    state carried between launches).  45 chunks with a ragged tail at N = 2, H = 16 give
+    three windows on 256 CUs (18, 18 and 9 chunks at d_v = 128; 21, 21 and 3 at 64).
+    Against the oracle, and bit for bit against the same sequences packed (a packed call
+    runs without windows)."""
+    T = 64 * 44 + 37
+    plan = key_window_plan(2, 16, dv, T)
+    assert len(plan) >= 3 and plan[-1] < plan[0], plan
+    inp = synth.random_inputs(2, T, 16, 128, dv, "key", "bf16", seed=61 + dv, state_std=0.05)
     if write == "add":
         inp["beta"] = None
     d = to_dev(inp)
@@ -242,7 +261,7 @@ def test_key_gate_windows(gdn, write, dv):
     o2, fs2 = gdn.fwd_chunked(flat(d["q"]), flat(d["k"]), flat(d["v"]), flat(d["beta"]), flat(d["log_alpha"]),
                               d["initial_state"], cu, write=write)
     torch.cuda.synchronize()
-    assert torch.equal(o.reshape(1, 2 * T, 2, dv), o2) and torch.equal(fs, fs2)
+    assert torch.equal(o.reshape(1, 2 * T, 16, dv), o2) and torch.equal(fs, fs2)
     o_ref, fs_ref = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], inp["initial_state"],
                                gate="key", write=write)
     assert relerr(o.cpu(), o_ref) <= TOL["bf16"] and relerr(fs.cpu(), fs_ref) <= TOL["bf16"]
