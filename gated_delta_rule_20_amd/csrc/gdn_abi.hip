@@ -68,6 +68,14 @@ int check_fwd(const gdn_fwd_args *a) {
     return GDN_ERR_INVALID_ARG;
   }
   if ((long)a->B * a->T > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+  // every launch grid must fit a signed 32-bit count: per-stream grids have at most
+  // d_v / 16 workgroups per (sequence, head); per-chunk grids one per (chunk slot, head),
+  // with fewer than B T / 64 + N + 1 slots
+  {
+    const long long streams = (long long)a->N * a->H;
+    const long long slots = ((long long)a->B * a->T + 63) / 64 + a->N + 1;
+    if (streams * (a->d_v / 16) > INT32_MAX || slots * a->H > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+  }
   const bool tokens = (long)a->B * a->T > 0;
   if (tokens && (!a->q || !a->k || !a->v || !a->o)) return GDN_ERR_INVALID_ARG;
   if (tokens && !operands_ok(a->gate, a->write, a->beta, a->log_alpha)) return GDN_ERR_INVALID_ARG;
@@ -136,6 +144,7 @@ KeyLayout key_layout(const gdn_fwd_args *a) {
 int check_step(const gdn_step_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
   if (a->N < 0 || a->H <= 0) return GDN_ERR_INVALID_ARG;
+  if ((long long)a->N * a->H > INT32_MAX) return GDN_ERR_UNSUPPORTED;  // one workgroup per (stream, head)
   if (!dtype_ok(raw(a->dtype)) || !gate_ok(raw(a->gate)) || !write_ok(raw(a->write))) return GDN_ERR_INVALID_ARG;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   if (a->N == 0) return GDN_OK;
@@ -219,6 +228,7 @@ int check_dplr(const gdn_dplr_args *a) {
 int check_dplr_step(const gdn_dplr_step_args *a) {
   if (!a) return GDN_ERR_INVALID_ARG;
   if (a->N < 0 || a->H <= 0) return GDN_ERR_INVALID_ARG;
+  if ((long long)a->N * a->H > INT32_MAX) return GDN_ERR_UNSUPPORTED;  // one workgroup per (stream, head)
   if (!dtype_ok(raw(a->dtype)) || !gate_ok(raw(a->gate))) return GDN_ERR_INVALID_ARG;
   if (!head_dim_ok(a->d_k) || !head_dim_ok(a->d_v)) return GDN_ERR_UNSUPPORTED;
   if (a->N == 0) return GDN_OK;

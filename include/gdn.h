@@ -104,7 +104,9 @@ typedef struct {
                          (H <= 262143: offsets inside one chunk fit 32 bits)         */
   int d_k, d_v;       /* head dims: each 64 or 128, in either dtype                  */
   int chunk;          /* chunk length: must be 64                                    */
-  int N;              /* number of sequences: B, or len(cu_seqlens) - 1              */
+  int N;              /* number of sequences: B, or len(cu_seqlens) - 1
+                         (N H d_v / 16 and (B T / 64 + N + 1) H at most 2^31 - 1,
+                         the launch grids; GDN_ERR_UNSUPPORTED otherwise)           */
   gdn_dtype dtype;    /* dtype of q, k, v, o                                         */
   gdn_gate gate;      /* gate mode                                                   */
   gdn_write write;    /* write rule                                                  */
@@ -127,7 +129,8 @@ typedef struct {
  * "Decoding Hybrid Linear Attention Architectures", sec. 6; the recurrent mode of
  * "Linear Attention Variants", RetNet section). */
 typedef struct {
-  int N, H, d_k, d_v; /* streams, heads, head dims (each 64 or 128)                  */
+  int N, H, d_k, d_v; /* streams, heads, head dims (each 64 or 128); N H at most
+                         2^31 - 1 (GDN_ERR_UNSUPPORTED otherwise)                  */
   gdn_dtype dtype;    /* dtype of q, k, v, o                                         */
   gdn_gate gate;
   gdn_write write;
@@ -323,7 +326,8 @@ int gdn_fwd_dplr(const gdn_dplr_args *args, void *hip_stream);
  * per key channel); any dtype; d_k, d_v in {64, 128}.  Validation as for
  * gdn_fwd_recurrent_step. */
 typedef struct {
-  int N, H, d_k, d_v;     /* streams, heads, head dims (each 64 or 128)                */
+  int N, H, d_k, d_v;     /* streams, heads, head dims (each 64 or 128); N H at most
+                             2^31 - 1 (GDN_ERR_UNSUPPORTED otherwise)              */
   gdn_dtype dtype;        /* dtype of q, k, a, b, v, o                                 */
   gdn_gate gate;
   const void *q, *k, *a, *b; /* [N, H, d_k]                                            */

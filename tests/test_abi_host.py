@@ -104,6 +104,7 @@ def test_package_has_no_cpu_path():
     (dict(H=0), INVALID),
     (dict(T=-1), INVALID),
     (dict(B=65536, T=65536, N=65536), UNSUPPORTED),  # more than 2^31 - 1 tokens
+    (dict(B=1 << 20, T=1, N=1 << 20, H=1 << 12), UNSUPPORTED),  # launch grids past 2^31 - 1 workgroups
     (dict(B=1, N=3, cu_seqlens=fake(7)), WORKSPACE),  # varlen needs its order table
     (dict(B=1, N=3, cu_seqlens=fake(7), workspace=fake(8, 16), workspace_bytes=4096), WORKSPACE),
     (dict(B=1, N=3, cu_seqlens=fake(7), workspace=fake(8), workspace_bytes=8), WORKSPACE),
@@ -175,6 +176,7 @@ def step_args(g, **kw):
     (dict(beta=None), INVALID),
     (dict(dtype=5), INVALID),
     (dict(H=0), INVALID),
+    (dict(N=1 << 20, H=1 << 12), UNSUPPORTED),  # one workgroup per (stream, head): past 2^31 - 1
 ])
 def test_step_host_validation(g, change, status):
     assert g._lib.gdn_fwd_recurrent_step(ctypes.byref(step_args(g, **change)), None) == status
@@ -440,6 +442,7 @@ def dplr_step_args(g, **kw):
     (dict(gate=0), INVALID),                 # no gate: no decays either
     (dict(state=fake(6, 8)), INVALID),       # the state needs 16-byte alignment
     (dict(d_v=96), UNSUPPORTED),
+    (dict(N=1 << 20, H=1 << 12), UNSUPPORTED),  # one workgroup per (stream, head): past 2^31 - 1
     (dict(N=0), OK),                         # nothing to do, nothing launched
 ])
 def test_dplr_step_host_validation(g, change, status):
