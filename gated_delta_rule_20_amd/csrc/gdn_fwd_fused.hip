@@ -37,6 +37,7 @@
 //    is written once; no intermediate (W, U, per-chunk states, Delta) reaches HBM.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
+#include "gdn_tile.h"
 
 namespace gdn {
 
@@ -379,22 +380,30 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
     __syncthreads();
 
     // (3) diagonal 16x16 blocks of T = (I + A)^-1: forward substitution in fp32,
-    //     lane (lg, lm) solves column lm of block lg
+    //     lane (lg, lm) solves row lm of block lg (lower_solve16: the rows reach the
+    //     other lanes by DPP broadcast)
     if (wave == 0) {
       if (!ADD) {
-      // diagonal block lg of A: the fp32 AD tiles, or (LEAN) the fp32 A tile itself
-      const float *ad = LEAN ? (const float *)As + 16 * lg * ST + 16 * lg : AD + lg * 256;
+      // row lm of diagonal block lg of A: the fp32 AD tiles, or (LEAN) the fp32 A tile
       constexpr int ADS = LEAN ? ST : 16;
-      float x[16];
+      const float *ad = (LEAN ? (const float *)As + 16 * lg * ST + 16 * lg : AD + lg * 256) + lm * ADS;
+      float nl[16], t[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == lm) ? 1.f : 0.f;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v4 = *(const f32x4 *)(ad + 4 * q4);
 #pragma unroll
-        for (int i = 0; i < r; ++i) acc -= ad[r * ADS + i] * x[i];
-        x[r] = acc;
+        for (int j = 0; j < 4; ++j) nl[4 * q4 + j] = -v4[j];
       }
+      lower_solve16(t, nl);
+      constexpr int PK = 16 / CF::ES;  // elements per 16-byte store
+      E *trow = Ts + (16 * lg + lm) * ST + 16 * lg;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Ts[(16 * lg + r) * ST + 16 * lg + lm] = to_e<E>(x[r]);
+      for (int c0 = 0; c0 < 16; c0 += PK) {
+        E pk[PK];
+#pragma unroll
+        for (int j = 0; j < PK; ++j) pk[j] = to_e<E>(t[c0 + j]);
+        st_pack<E, PK>(trow + c0, pk);
+      }
       }
     } else if (KG) {
       // per-channel decay folded into the state-phase operands (waves 1-3, while

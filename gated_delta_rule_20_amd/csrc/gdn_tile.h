@@ -169,6 +169,59 @@ __device__ __forceinline__ void store_split(bf16 *hi, bf16 *lo, size_t i, float 
 // The fragment (8 contiguous elements) of a matrix stored as hi and lo bf16 halves.
 __device__ __forceinline__ Split ld_split(const bf16 *hi, const bf16 *lo) { return Split{ld8(hi), ld8(lo)}; }
 
+// Forward substitution of one unit lower triangular 16 x 16 system per 16-lane row of
+// a wave, in fp32: on entry lane lm holds nl[i] = -L[lm][i] (zero for i >= lm); on
+// return t[0..15] is row lm of (I + L)^-1.  Step i adds nl[i] times row i of the result
+// to every later row; row i is final once steps 0 .. i-1 are done, and it reaches the
+// other lanes of its 16-lane row by DPP broadcast (row_newbcast), so no LDS round trip
+// sits in the dependent chain.  Each step is one asm block that starts with the two
+// wait states a DPP read needs after a VALU write of the same register.
+__device__ __forceinline__ void lower_solve16(float (&t)[16], const float (&nl)[16]) {
+  const int lm = threadIdx.x & 15;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) t[c] = (c == lm) ? 1.f : 0.f;
+#define GDN_LS_FMA(I, C) "v_fmac_f32_dpp %" #C ", %" #C ", %16 row_newbcast:" #I " row_mask:0xf bank_mask:0xf\n"
+#define GDN_LS_STEP(I, BODY)                                                                        \
+  asm volatile("s_nop 1\n" BODY                                                                    \
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), \
+                 "+v"(t[7]), "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]),           \
+                 "+v"(t[13]), "+v"(t[14]), "+v"(t[15])                                               \
+               : "v"(nl[I]))
+  GDN_LS_STEP(0, GDN_LS_FMA(0, 0));
+  GDN_LS_STEP(1, GDN_LS_FMA(1, 0) GDN_LS_FMA(1, 1));
+  GDN_LS_STEP(2, GDN_LS_FMA(2, 0) GDN_LS_FMA(2, 1) GDN_LS_FMA(2, 2));
+  GDN_LS_STEP(3, GDN_LS_FMA(3, 0) GDN_LS_FMA(3, 1) GDN_LS_FMA(3, 2) GDN_LS_FMA(3, 3));
+  GDN_LS_STEP(4, GDN_LS_FMA(4, 0) GDN_LS_FMA(4, 1) GDN_LS_FMA(4, 2) GDN_LS_FMA(4, 3) GDN_LS_FMA(4, 4));
+  GDN_LS_STEP(5, GDN_LS_FMA(5, 0) GDN_LS_FMA(5, 1) GDN_LS_FMA(5, 2) GDN_LS_FMA(5, 3) GDN_LS_FMA(5, 4)
+                     GDN_LS_FMA(5, 5));
+  GDN_LS_STEP(6, GDN_LS_FMA(6, 0) GDN_LS_FMA(6, 1) GDN_LS_FMA(6, 2) GDN_LS_FMA(6, 3) GDN_LS_FMA(6, 4)
+                     GDN_LS_FMA(6, 5) GDN_LS_FMA(6, 6));
+  GDN_LS_STEP(7, GDN_LS_FMA(7, 0) GDN_LS_FMA(7, 1) GDN_LS_FMA(7, 2) GDN_LS_FMA(7, 3) GDN_LS_FMA(7, 4)
+                     GDN_LS_FMA(7, 5) GDN_LS_FMA(7, 6) GDN_LS_FMA(7, 7));
+  GDN_LS_STEP(8, GDN_LS_FMA(8, 0) GDN_LS_FMA(8, 1) GDN_LS_FMA(8, 2) GDN_LS_FMA(8, 3) GDN_LS_FMA(8, 4)
+                     GDN_LS_FMA(8, 5) GDN_LS_FMA(8, 6) GDN_LS_FMA(8, 7) GDN_LS_FMA(8, 8));
+  GDN_LS_STEP(9, GDN_LS_FMA(9, 0) GDN_LS_FMA(9, 1) GDN_LS_FMA(9, 2) GDN_LS_FMA(9, 3) GDN_LS_FMA(9, 4)
+                     GDN_LS_FMA(9, 5) GDN_LS_FMA(9, 6) GDN_LS_FMA(9, 7) GDN_LS_FMA(9, 8) GDN_LS_FMA(9, 9));
+  GDN_LS_STEP(10, GDN_LS_FMA(10, 0) GDN_LS_FMA(10, 1) GDN_LS_FMA(10, 2) GDN_LS_FMA(10, 3) GDN_LS_FMA(10, 4)
+                      GDN_LS_FMA(10, 5) GDN_LS_FMA(10, 6) GDN_LS_FMA(10, 7) GDN_LS_FMA(10, 8) GDN_LS_FMA(10, 9)
+                          GDN_LS_FMA(10, 10));
+  GDN_LS_STEP(11, GDN_LS_FMA(11, 0) GDN_LS_FMA(11, 1) GDN_LS_FMA(11, 2) GDN_LS_FMA(11, 3) GDN_LS_FMA(11, 4)
+                      GDN_LS_FMA(11, 5) GDN_LS_FMA(11, 6) GDN_LS_FMA(11, 7) GDN_LS_FMA(11, 8) GDN_LS_FMA(11, 9)
+                          GDN_LS_FMA(11, 10) GDN_LS_FMA(11, 11));
+  GDN_LS_STEP(12, GDN_LS_FMA(12, 0) GDN_LS_FMA(12, 1) GDN_LS_FMA(12, 2) GDN_LS_FMA(12, 3) GDN_LS_FMA(12, 4)
+                      GDN_LS_FMA(12, 5) GDN_LS_FMA(12, 6) GDN_LS_FMA(12, 7) GDN_LS_FMA(12, 8) GDN_LS_FMA(12, 9)
+                          GDN_LS_FMA(12, 10) GDN_LS_FMA(12, 11) GDN_LS_FMA(12, 12));
+  GDN_LS_STEP(13, GDN_LS_FMA(13, 0) GDN_LS_FMA(13, 1) GDN_LS_FMA(13, 2) GDN_LS_FMA(13, 3) GDN_LS_FMA(13, 4)
+                      GDN_LS_FMA(13, 5) GDN_LS_FMA(13, 6) GDN_LS_FMA(13, 7) GDN_LS_FMA(13, 8) GDN_LS_FMA(13, 9)
+                          GDN_LS_FMA(13, 10) GDN_LS_FMA(13, 11) GDN_LS_FMA(13, 12) GDN_LS_FMA(13, 13));
+  GDN_LS_STEP(14, GDN_LS_FMA(14, 0) GDN_LS_FMA(14, 1) GDN_LS_FMA(14, 2) GDN_LS_FMA(14, 3) GDN_LS_FMA(14, 4)
+                      GDN_LS_FMA(14, 5) GDN_LS_FMA(14, 6) GDN_LS_FMA(14, 7) GDN_LS_FMA(14, 8) GDN_LS_FMA(14, 9)
+                          GDN_LS_FMA(14, 10) GDN_LS_FMA(14, 11) GDN_LS_FMA(14, 12) GDN_LS_FMA(14, 13)
+                              GDN_LS_FMA(14, 14));
+#undef GDN_LS_STEP
+#undef GDN_LS_FMA
+}
+
 // T = (I + s A)^-1 (s = SGN, +1 or -1) of a strictly lower triangular 64 x 64 fp32
 // matrix A in LDS (row pitch sa), written to LDS T (row pitch st; every entry).
 // Blocked: wave 0 solves the four 16 x 16 diagonal blocks by forward substitution
