@@ -35,6 +35,8 @@
 //  * Every HBM byte of q, k, v is read once per d_v block (d_v / 64 blocks share
 //    the K/Q tiles through L2: their workgroups are placed on the same XCD) and o
 //    is written once; no intermediate (W, U, per-chunk states, Delta) reaches HBM.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 #include "gdn_tile.h"
@@ -109,7 +111,9 @@ struct Cfg {
 // computes each: w0 (0,0) (3,0) (3,1); w1 (1,0) (1,1) (3,2); w2 (2,0) (2,1); w3 (2,2) (3,3).
 constexpr int GT_A[10] = {0, 3, 3, 1, 1, 3, 2, 2, 2, 3};
 constexpr int GT_B[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-constexpr int GT_W[10] = {0, 0, 0, 1, 1, 1, 2, 2, 3, 3};
+// wave w takes the GT_N[w] consecutive tiles from GT_T0[w]
+constexpr int GT_T0[4] = {0, 3, 6, 8};
+constexpr int GT_N[4] = {3, 3, 2, 2};
 
 template <typename E, int DK, int DVB, int GATE, bool ADD>
 __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
@@ -280,7 +284,22 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       st_pack<E, CF::RPTV>(VTs + (cv * VEC + e) * ST + rgv * CF::RPTV, col);
     }
     if (tid < C) betas[tid] = rbeta;
-    if (GATE == GATE_HEAD && tid >= C && tid < 2 * C) las[tid - C] = rla;
+    if (GATE == GATE_HEAD && tid >= C && tid < 2 * C) {
+      // the chunk's decay prefix, from the log decays this wave holds (lane = token):
+      // g = inclusive cumsum of log alpha over the chunk, e^g, e^{g_C - g}, e^{g_C}
+      const int tk = tid - C;
+      float g = rla;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(g, off);
+        if (tk >= off) g += y;
+      }
+      const float gC = __shfl(g, 63);
+      gs[tk] = g;
+      egs[tk] = __expf(g);
+      egcs[tk] = __expf(gC - g);
+      if (tk == 0) misc[0] = __expf(gC);
+    }
   };
 
   const int nchunks = (len + C - 1) / C;
@@ -304,20 +323,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
         for (int j = 0; j < 4; ++j) dst[(size_t)(16 * t + 4 * lg + j) * dv] = M[t][j];
     }
 
-    // (1) gate prefix: g = inclusive cumsum of log alpha over the chunk
-    if (GATE == GATE_HEAD && wave == 0) {
-      float g = las[lane];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(g, off);
-        if (lane >= off) g += y;
-      }
-      const float gC = __shfl(g, 63);
-      gs[lane] = g;
-      egs[lane] = __expf(g);
-      egcs[lane] = __expf(gC - g);
-      if (lane == 0) misc[0] = __expf(gC);
-    }
+    // (1) gate prefix (the per-head gate's was formed when the chunk was staged)
     if (KG && tid < DK) {
       // per channel: inclusive prefix over the chunk's rows, in place
       float x[C];
@@ -331,52 +337,81 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       }
       egck[tid] = __expf(g);
     }
-    __syncthreads();
+    if constexpr (KG) __syncthreads();
 
-    // (2) Gram tiles -> A (strictly lower, beta- and decay-weighted) and P
+    // (2) Gram tiles -> A (strictly lower, beta- and decay-weighted) and P.  Wave w
+    // takes tiles GT_T0[w] .. + GT_N[w] - 1 (compile-time per wave, the 32-deep steps
+    // outermost, so the wave's independent tiles issue their reads and products together).
+    // Each tile (a, b) is formed transposed, as the product of block b's rows with block
+    // a's, so lane (lg, lm) holds row 16a + lm, columns 16b + 4lg .. +3: one prefix value
+    // and one 16-byte read per row and column side, and one store per matrix.
+    auto gram_wave = [&](auto wc) {
+      constexpr int w = decltype(wc)::value, T0 = GT_T0[w], NTL = GT_N[w];
+      f32x4 kk[NTL], qk[NTL];
 #pragma unroll
-    for (int ti = 0; ti < 10; ++ti) {
-      if (wave != GT_W[ti]) continue;
-      const int a = GT_A[ti], b = GT_B[ti];
-      f32x4 kk = zero4(), qk = zero4();
+      for (int u = 0; u < NTL; ++u) kk[u] = qk[u] = zero4();
 #pragma unroll
-      for (int s = 0; s < CF::KB; ++s) {
-        F bk = ld8(Ks + (16 * b + lm) * SK + 32 * s + 8 * lg);
-        F ak = ld8(Ks + (16 * a + lm) * SK + 32 * s + 8 * lg);
-        F aq = ld8(Qs + (16 * a + lm) * SK + 32 * s + 8 * lg);
-        if (KG) {
-          // exp(g_r - g_i) per channel = exp(g_r - m_a) * exp(m_a - g_i), m_a = g at row 16a+7
-          const float *gr = Gs + (16 * a + lm) * SG + 32 * s + 8 * lg;
-          const float *gi = Gs + (16 * b + lm) * SG + 32 * s + 8 * lg;
-          const float *gm = Gs + (16 * a + 7) * SG + 32 * s + 8 * lg;
+      for (int s = 0; s < CF::KB; ++s)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float ea = __expf(gr[j] - gm[j]), eb = __expf(gm[j] - gi[j]);
-            ak[j] = to_e<E>(to_f(ak[j]) * ea);
-            aq[j] = to_e<E>(to_f(aq[j]) * ea);
-            bk[j] = to_e<E>(to_f(bk[j]) * eb);
+        for (int u = 0; u < NTL; ++u) {
+          const int a = GT_A[T0 + u], b = GT_B[T0 + u];
+          F bk = ld8(Ks + (16 * b + lm) * SK + 32 * s + 8 * lg);
+          F ak = ld8(Ks + (16 * a + lm) * SK + 32 * s + 8 * lg);
+          F aq = ld8(Qs + (16 * a + lm) * SK + 32 * s + 8 * lg);
+          if (KG) {
+            // exp(g_r - g_i) per channel = exp(g_r - m_a) * exp(m_a - g_i), m_a = g at row 16a+7
+            const float *gr = Gs + (16 * a + lm) * SG + 32 * s + 8 * lg;
+            const float *gi = Gs + (16 * b + lm) * SG + 32 * s + 8 * lg;
+            const float *gm = Gs + (16 * a + 7) * SG + 32 * s + 8 * lg;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float ea = __expf(gr[j] - gm[j]), eb = __expf(gm[j] - gi[j]);
+              ak[j] = to_e<E>(to_f(ak[j]) * ea);
+              aq[j] = to_e<E>(to_f(aq[j]) * ea);
+              bk[j] = to_e<E>(to_f(bk[j]) * eb);
+            }
+          }
+          if (!ADD) kk[u] = mma(bk, ak, kk[u]);
+          qk[u] = mma(bk, aq, qk[u]);
+        }
+#pragma unroll
+      for (int u = 0; u < NTL; ++u) {
+        const int a = GT_A[T0 + u], b = GT_B[T0 + u];
+        const int r = 16 * a + lm, i0 = 16 * b + 4 * lg;
+        f32x4 gam;
+        if (GATE == GATE_HEAD) {
+          const float gr = gs[r];
+          const f32x4 gi = *(const f32x4 *)(gs + i0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) gam[j] = (i0 + j <= r) ? __expf(gr - gi[j]) : 0.f;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) gam[j] = (i0 + j <= r) ? 1.f : 0.f;
+        }
+        E pv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[j] = to_e<E>(qk[u][j] * gam[j]);
+        st_pack<E, 4>(Ps + r * ST + i0, pv);
+        if (!ADD) {
+          const float br = betas[r];
+          f32x4 av;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) av[j] = (i0 + j < r) ? br * kk[u][j] * gam[j] : 0.f;
+          if (a == b && !LEAN) {
+            *(f32x4 *)(AD + r * 16 + 4 * lg) = av;
+          } else {
+            E ae[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ae[j] = to_e<E>(av[j]);
+            st_pack<E, 4>(As + r * ST + i0, ae);
           }
         }
-        if (!ADD) kk = mma(ak, bk, kk);
-        qk = mma(aq, bk, qk);
       }
-      const int i = 16 * b + lm;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * a + 4 * lg + j;
-        float gam = (i <= r) ? 1.f : 0.f;
-        if (GATE == GATE_HEAD) gam = (i <= r) ? __expf(gs[r] - gs[i]) : 0.f;
-        const float pv = qk[j] * gam;
-        if (!ADD) {
-          const float av = (i < r) ? betas[r] * kk[j] * gam : 0.f;
-          if (a == b && !LEAN)
-            AD[(16 * a + 4 * lg + j) * 16 + lm] = av;
-          else
-            As[r * ST + i] = to_e<E>(av);
-        }
-        Ps[r * ST + i] = to_e<E>(pv);
-      }
-    }
+    };
+    if (wave == 0) gram_wave(std::integral_constant<int, 0>());
+    else if (wave == 1) gram_wave(std::integral_constant<int, 1>());
+    else if (wave == 2) gram_wave(std::integral_constant<int, 2>());
+    else gram_wave(std::integral_constant<int, 3>());
     __syncthreads();
 
     // (3) diagonal 16x16 blocks of T = (I + A)^-1: forward substitution in fp32,
