@@ -467,39 +467,57 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
     __syncthreads();
 
     // (4) off-diagonal blocks: T[a][b] = -T[a][a] * sum_{k=b}^{a-1} A[a][k] T[k][b];
-    //     wave b walks block column b downwards, keeping T[k][b] in C tiles
-    if (!ADD && wave < 3) {
-      const int b = wave;
+    //     wave b walks block column b downwards, keeping T[k][b] in C tiles.  The column
+    //     is a compile-time constant; with bf16 operands every A and T[a][a] fragment of
+    //     it is read before the dependent MFMA chain starts (the twice wider fp32
+    //     fragments are read where they are used: holding them all costs more than it saves).
+    auto tcolumn = [&](auto bcol) {
+      constexpr int b = decltype(bcol)::value;
+      constexpr bool HOIST = sizeof(E) == 2;
+      F af[4][2], tf[4];
+#pragma unroll
+      for (int a = b + 1; a < 4 && HOIST; ++a) {
+#pragma unroll
+        for (int k0 = 0; k0 < 4; k0 += 2)
+          if ((k0 >= b && k0 < a) || (k0 + 1 >= b && k0 + 1 < a)) {
+            const E *ar = As + (16 * a + lm) * ST + 16 * k0 + 4 * lg;
+            af[a][k0 >> 1] = ld4x2(ar, ar + 16);
+          }
+        tf[a] = ld4z(Ts + (16 * a + lm) * ST + 16 * a + 4 * lg);
+      }
       f32x4 Tc[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        Tc[k] = zero4();
-        if (k == b)
+      for (int k = 0; k < 4; ++k) Tc[k] = zero4();
 #pragma unroll
-          for (int j = 0; j < 4; ++j) Tc[k][j] = to_f(Ts[(16 * k + 4 * lg + j) * ST + 16 * k + lm]);
-      }
+      for (int j = 0; j < 4; ++j) Tc[b][j] = to_f(Ts[(16 * b + 4 * lg + j) * ST + 16 * b + lm]);
 #pragma unroll
-      for (int a = 1; a < 4; ++a) {
-        if (a > b) {
-          f32x4 y = zero4();
+      for (int a = b + 1; a < 4; ++a) {
+        f32x4 y = zero4();
 #pragma unroll
-          for (int k0 = 0; k0 < 4; k0 += 2) {
-            const bool in0 = (k0 >= b && k0 < a), in1 = (k0 + 1 >= b && k0 + 1 < a);
-            if (in0 || in1) {
-              const F bf = frag_from_c<E>(in0 ? Tc[k0] : zero4(), in1 ? Tc[k0 + 1] : zero4());
+        for (int k0 = 0; k0 < 4; k0 += 2) {
+          const bool in0 = (k0 >= b && k0 < a), in1 = (k0 + 1 >= b && k0 + 1 < a);
+          if (in0 || in1) {
+            const F bf = frag_from_c<E>(in0 ? Tc[k0] : zero4(), in1 ? Tc[k0 + 1] : zero4());
+            if (!HOIST) {
               const E *ar = As + (16 * a + lm) * ST + 16 * k0 + 4 * lg;
-              y = mma(ld4x2(ar, ar + 16), bf, y);
+              af[a][k0 >> 1] = ld4x2(ar, ar + 16);
             }
-          }
-          const F tf = ld4z(Ts + (16 * a + lm) * ST + 16 * a + 4 * lg);
-          const f32x4 z = mma(tf, frag_from_c_half<E>(y), zero4());
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            Tc[a][j] = -z[j];
-            Ts[(16 * a + 4 * lg + j) * ST + 16 * b + lm] = to_e<E>(-z[j]);
+            y = mma(af[a][k0 >> 1], bf, y);
           }
         }
+        if (!HOIST) tf[a] = ld4z(Ts + (16 * a + lm) * ST + 16 * a + 4 * lg);
+        const f32x4 z = mma(tf[a], frag_from_c_half<E>(y), zero4());
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Tc[a][j] = -z[j];
+          Ts[(16 * a + 4 * lg + j) * ST + 16 * b + lm] = to_e<E>(-z[j]);
+        }
       }
+    };
+    if (!ADD) {
+      if (wave == 0) tcolumn(std::integral_constant<int, 0>());
+      else if (wave == 1) tcolumn(std::integral_constant<int, 1>());
+      else if (wave == 2) tcolumn(std::integral_constant<int, 2>());
     }
     __syncthreads();
 
