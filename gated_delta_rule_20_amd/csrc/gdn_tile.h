@@ -225,7 +225,7 @@ __device__ __forceinline__ void lower_solve16(float (&t)[16], const float (&nl)[
 // T = (I + s A)^-1 (s = SGN, +1 or -1) of a strictly lower triangular 64 x 64 fp32
 // matrix A in LDS (row pitch sa), written to LDS T (row pitch st; every entry).
 // Blocked: wave 0 solves the four 16 x 16 diagonal blocks by forward substitution
-// (lane (lg, lm) takes column lm of block lg); then waves 0-2 each walk down one block
+// (lane (lg, lm) takes row lm of block lg, lower_solve16); then waves 0-2 each walk down one block
 // column b, T[a][b] = -s T[a][a] sum_{b <= k < a} A[a][k] T[k][b] for a = b+1 .. 3, on
 // the bf16 matrix cores with split operands (the inner sum passes through the wave's
 // 16 x 17 slice of ys).  Every thread of the workgroup (at least four waves) calls it;
@@ -239,17 +239,17 @@ __device__ __forceinline__ void tri_inv64(const float *A, int sa, float *T, int 
     if ((c >> 4) > (r >> 4)) T[r * st + c] = 0.f;
   }
   if (wave == 0) {
+    // lane (lg, lm) solves row lm of diagonal block lg (entries of A on or above the
+    // diagonal are not read as zeros: they are masked)
     const int o = 16 * lg;
-    float x[16];
+    const float *ar = A + (o + lm) * sa + o;
+    float nl[16], t[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = 0.f;
+    for (int i = 0; i < 16; ++i) nl[i] = i < lm ? -(float)SGN * ar[i] : 0.f;
+    lower_solve16(t, nl);
+    float *tr = T + (o + lm) * st + o;
 #pragma unroll
-      for (int i = 0; i < r; ++i) acc += A[(o + r) * sa + o + i] * x[i];
-      x[r] = (r == lm ? 1.f : 0.f) - (float)SGN * acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) T[(o + r) * st + o + lm] = x[r];
+    for (int c = 0; c < 16; ++c) tr[c] = t[c];
   }
   __syncthreads();
   if (wave < 3) {
