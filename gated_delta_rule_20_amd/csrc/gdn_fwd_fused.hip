@@ -288,13 +288,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       // the chunk's decay prefix, from the log decays this wave holds (lane = token):
       // g = inclusive cumsum of log alpha over the chunk, e^g, e^{g_C - g}, e^{g_C}
       const int tk = tid - C;
-      float g = rla;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(g, off);
-        if (tk >= off) g += y;
-      }
-      const float gC = __shfl(g, 63);
+      const float g = wave_scan64(rla);
+      const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 63));
       gs[tk] = g;
       egs[tk] = __expf(g);
       egcs[tk] = __expf(gC - g);

@@ -169,6 +169,22 @@ __device__ __forceinline__ void store_split(bf16 *hi, bf16 *lo, size_t i, float 
 // The fragment (8 contiguous elements) of a matrix stored as hi and lo bf16 halves.
 __device__ __forceinline__ Split ld_split(const bf16 *hi, const bf16 *lo) { return Split{ld8(hi), ld8(lo)}; }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in fp32: within each 16-lane row
+// by four DPP row shifts (1, 2, 4, 8; lanes without a source add 0), then the totals
+// of the earlier rows, read from their last lanes.  Every lane of the wave must be
+// active.
+__device__ __forceinline__ float wave_scan64(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
+}
+
 // Forward substitution of one unit lower triangular 16 x 16 system per 16-lane row of
 // a wave, in fp32: on entry lane lm holds nl[i] = -L[lm][i] (zero for i >= lm); on
 // return t[0..15] is row lm of (I + L)^-1.  Step i adds nl[i] times row i of the result
