@@ -127,6 +127,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   E *Qs = (E *)(smem + CF::OFF_Q);
   E *KTs = (E *)(smem + CF::OFF_KT);
   E *VTs = (E *)(smem + CF::OFF_VT);
+  // bf16 without the per-key gate: K^T and V^T fragments come from the row-major K and V
+  // tiles through the transposing LDS read (lds_tr4), so no transposed copies are
+  // stored; the row-major V tile takes the K^T tile's place
+  constexpr bool TRR = sizeof(E) == 2 && !LEAN && !KG;
+  constexpr int SVR = DVB + VEC;  // row pitch of the row-major V tile (elements)
+  static_assert(!TRR || C * SVR <= DK * ST, "row-major V fits the K^T tile");
+  E *Vr = KTs;
   E *Ts = (E *)(smem + CF::OFF_T);
   E *Ps = (E *)(smem + CF::OFF_P);
   E *As = (E *)(smem + CF::OFF_A);
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       *(u32x4 *)(Ks + row * SK + cc * VEC) = rk[u];
       *(u32x4 *)(Qs + row * SK + cc * VEC) = rq[u];
     }
-    if constexpr (!LEAN) {
+    if constexpr (!LEAN && !TRR) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         E col[CF::RPT];
@@ -276,12 +283,17 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
         st_pack<E, CF::RPT>(KTs + (cc * VEC + e) * ST + rg * CF::RPT, col);
       }
     }
+    if constexpr (TRR) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      E col[CF::RPTV];
+      for (int u = 0; u < CF::RPTV; ++u) *(u32x4 *)(Vr + (rgv * CF::RPTV + u) * SVR + cv * VEC) = rv[u];
+    } else {
 #pragma unroll
-      for (int u = 0; u < CF::RPTV; ++u) col[u] = ((const E *)&rv[u])[e];
-      st_pack<E, CF::RPTV>(VTs + (cv * VEC + e) * ST + rgv * CF::RPTV, col);
+      for (int e = 0; e < VEC; ++e) {
+        E col[CF::RPTV];
+#pragma unroll
+        for (int u = 0; u < CF::RPTV; ++u) col[u] = ((const E *)&rv[u])[e];
+        st_pack<E, CF::RPTV>(VTs + (cv * VEC + e) * ST + rgv * CF::RPTV, col);
+      }
     }
     if (tid < C) betas[tid] = rbeta;
     if (GATE == GATE_HEAD && tid >= C && tid < 2 * C) {
@@ -547,7 +559,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
       // X <- beta * (V - e^g * K M0);  O <- e^g * Q M0  (additive write: X <- V)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 vv = ld4f(VTs + (n0 + lm) * ST + 16 * i + 4 * lg);
+        f32x4 vv;
+        if constexpr (TRR) {  // V[16i + 4lg + j][n0 + lm], j = 0..3
+          const bf16x4 v4 = lds_tr4((const bf16 *)Vr + (16 * i + 4 * lg + (lm >> 2)) * SVR + n0 + 4 * (lm & 3));
+          vv = (f32x4){(float)v4[0], (float)v4[1], (float)v4[2], (float)v4[3]};
+        } else {
+          vv = ld4f(VTs + (n0 + lm) * ST + 16 * i + 4 * lg);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = 16 * i + 4 * lg + j;
@@ -617,9 +635,19 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
           M[t] = mma(k0, DT0, M[t]);
           M[t] = mma(k1, DT1, M[t]);
         } else {
-          const E *kt = KTs + (16 * t + lm) * ST + 4 * lg;
-          M[t] = mma(ld4x2(kt, kt + 16), DT0, M[t]);
-          M[t] = mma(ld4x2(kt + 32, kt + 48), DT1, M[t]);
+          if constexpr (TRR) {
+            // K^T[16t + lm][token] for tokens 4lg + j and 16 + 4lg + j (+ 32 for DT1),
+            // read transposed from the row-major K tile
+            const bf16 *kb = (const bf16 *)Ks + (4 * lg + (lm >> 2)) * SK + 16 * t + 4 * (lm & 3);
+            const bf16x4 a0 = lds_tr4(kb), a1 = lds_tr4(kb + 16 * SK);
+            const bf16x4 b0 = lds_tr4(kb + 32 * SK), b1 = lds_tr4(kb + 48 * SK);
+            M[t] = mma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), DT0, M[t]);
+            M[t] = mma(__builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), DT1, M[t]);
+          } else {
+            const E *kt = KTs + (16 * t + lm) * ST + 4 * lg;
+            M[t] = mma(ld4x2(kt, kt + 16), DT0, M[t]);
+            M[t] = mma(ld4x2(kt + 32, kt + 48), DT1, M[t]);
+          }
         }
       }
       if constexpr (LEAN) {  // O straight to HBM: lane holds column n0 + lm of rows 16i + 4lg + j
