@@ -134,6 +134,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
   constexpr int SVR = DVB + VEC;  // row pitch of the row-major V tile (elements)
   static_assert(!TRR || C * SVR <= DK * ST, "row-major V fits the K^T tile");
   E *Vr = KTs;
+  // O formed transposed (each lane one row, four consecutive columns: vector stores, one
+  // decay scale per row) for bf16 and for fp32 with d_k = 128; fp32 with d_k = 64 keeps
+  // O = Q M, which measured faster there
+  constexpr bool OTR = sizeof(E) == 2 || LEAN;
   E *Ts = (E *)(smem + CF::OFF_T);
   E *Ps = (E *)(smem + CF::OFF_P);
   E *As = (E *)(smem + CF::OFF_A);
@@ -554,7 +558,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
             X[i] = mma(kf, MB[s], X[i]);
           }
           const E *qr = Qs + (16 * i + lm) * SK + 32 * s + 4 * lg;
-          O[i] = mma(ld4x2(qr, qr + 16), MB[s], O[i]);
+          // OTR: O^T = M^T Q^T (lane holds a row of O); else O = Q M (lane holds a column)
+          O[i] = OTR ? mma(MB[s], ld4x2(qr, qr + 16), O[i]) : mma(ld4x2(qr, qr + 16), MB[s], O[i]);
         }
       // X <- beta * (V - e^g * K M0);  O <- e^g * Q M0  (additive write: X <- V)
 #pragma unroll
@@ -571,8 +576,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
           const int r = 16 * i + 4 * lg + j;
           const float e = (GATE == GATE_HEAD) ? egs[r] : 1.f;
           X[i][j] = ADD ? vv[j] : betas[r] * (vv[j] - e * X[i][j]);
-          O[i][j] *= e;
+          if (!OTR) O[i][j] *= e;
         }
+        if (OTR && GATE == GATE_HEAD) O[i] *= egs[16 * i + lm];  // row 16i + lm of O
       }
       // Delta = T X  (T lower triangular: tiles 0,1 need k-block 0 only); Delta = V
       // for the additive write
@@ -601,8 +607,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const E *pr = Ps + (16 * i + lm) * ST + 4 * lg;
-        O[i] = mma(ld4x2(pr, pr + 16), DB0, O[i]);
-        if (i >= 2) O[i] = mma(ld4x2(pr + 32, pr + 48), DB1, O[i]);
+        if constexpr (OTR) {  // O^T += Delta^T P^T
+          O[i] = mma(DB0, ld4x2(pr, pr + 16), O[i]);
+          if (i >= 2) O[i] = mma(DB1, ld4x2(pr + 32, pr + 48), O[i]);
+        } else {
+          O[i] = mma(ld4x2(pr, pr + 16), DB0, O[i]);
+          if (i >= 2) O[i] = mma(ld4x2(pr + 32, pr + 48), DB1, O[i]);
+        }
       }
       // M <- e^{g_C} M + K^T diag(e^{g_C - g}) Delta
       const float gam = (GATE == GATE_HEAD) ? misc[0] : 1.f;
@@ -650,16 +661,26 @@ __global__ __launch_bounds__(NT, 1) void fwd_fused_kernel(FwdParams p) {
           }
         }
       }
-      if constexpr (LEAN) {  // O straight to HBM: lane holds column n0 + lm of rows 16i + 4lg + j
+      // OTR: lane holds row 16i + lm of O, columns n0 + 4lg .. +3 (O^T was formed)
+      if constexpr (LEAN) {  // O straight to HBM, one 16-byte store per row block
         const int nv = min(C, len - c * C);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * i + lm;
+          E ov[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 16 * i + 4 * lg + j;
-            if (r < nv && p.o) ob[(size_t)(c * C + r) * sv + n0 + lm] = to_e<E>(O[i][j]);
-          }
-      } else {
+          for (int j = 0; j < 4; ++j) ov[j] = to_e<E>(O[i][j]);
+          if (r < nv && p.o) st_pack<E, 4>(ob + (size_t)(c * C + r) * sv + n0 + 4 * lg, ov);
+        }
+      } else if constexpr (OTR) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          E ov[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ov[j] = to_e<E>(O[i][j]);
+          st_pack<E, 4>(Os + (16 * i + lm) * SO + n0 + 4 * lg, ov);
+        }
+      } else {  // lane holds column n0 + lm of rows 16i + 4lg + j
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
