@@ -27,11 +27,14 @@
 //    the matrix-core accumulators: wave w owns 16 value columns of M, as eight
 //    16x16 C tiles (d_k = 128), and feeds them back as B operands (B from C), so
 //    the serial inter-chunk recursion needs no LDS or HBM round trip.
-//  * Per chunk, K, Q (row-major and K transposed) and the V block are staged in LDS;
-//    the next chunk's tiles are loaded into registers while this chunk computes.
-//  * Gram tiles K K^T and Q K^T (lower 16x16 tiles) on MFMA; the UT inverse by
-//    forward substitution of the four 16x16 diagonal blocks (fp32, one lane per
-//    column) and block forward substitution of the off-diagonal blocks on MFMA.
+//  * Per chunk, K, Q and the V block are staged in LDS, row-major, with transposed
+//    copies of K and V where the transposing LDS read cannot serve (fp32, or the
+//    per-key gate, which rescales K^T per channel); the next chunk's tiles are
+//    loaded into registers while this chunk computes.
+//  * Gram tiles K K^T and Q K^T (lower 16x16 tiles, each formed transposed so a lane
+//    holds one row) on MFMA; the UT inverse by forward substitution of the four
+//    16x16 diagonal blocks (fp32, one lane per row, rows broadcast by DPP) and
+//    block forward substitution of the off-diagonal blocks on MFMA.
 //  * Every HBM byte of q, k, v is read once per d_v block (d_v / 64 blocks share
 //    the K/Q tiles through L2: their workgroups are placed on the same XCD) and o
 //    is written once; no intermediate (W, U, per-chunk states, Delta) reaches HBM.
